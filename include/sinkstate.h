@@ -1,0 +1,192 @@
+/*
+ * sinkstate.h -- C-ABI of libsinkstate.so: a pool of linear-attention
+ * recurrent states held in factored (low-rank) form on one AMD Instinct
+ * MI355X (gfx950), with buffered decode, factored readout, Brand-style
+ * compaction and a dense fallback.
+ *
+ * The operations follow "SinkState: On-the-Fly SVD of Recurrent States for
+ * Efficient Hybrid LLM Serving" (arXiv 2611.14246), cited below as [SS], and
+ * the gated delta rule as written in "Shallow Encoding Emits Deep Memories"
+ * (arXiv 2611.06084) section 2, eq. (2), cited as [SEED].
+ *
+ * Orientation.  A state is S (d_k x d_v) with o = S^T q.  [SS] 2.1 writes the
+ * transpose H = S^T (d_v x d_k); the two are the same object.  Factored form:
+ *   S = Gamma * ( sum_i sigma_i u_i v_i^T  +  sum_j c_j k_j w_j^T )
+ * where (u_i in R^{d_k}, v_i in R^{d_v}, sigma_i) are the components ([SS]
+ * 3.2 Design 1: the first min(r, R) by sigma are "active", the rest
+ * "frozen"), (k_j, w_j, c_j) are the pad slots ([SS] 4.2 "(i) Buffering"),
+ * and Gamma is the decay accumulated since the last compaction ([SS] 4.4:
+ * the decode kernel applies the accumulated decay on the fly).
+ *
+ * Conventions for every entry point:
+ *  - Every call returns ss_status.  Argument and shape checks run on the host
+ *    before any HIP call; a failing check changes nothing.
+ *  - Device pointers (q, k, v, alpha, beta, o) are caller-owned fp32 device
+ *    memory, contiguous, row-major [n_states][d]; they must stay valid until
+ *    the enqueued work completes.  Host pointers are only read during the call.
+ *  - All device work is enqueued on the given stream (NULL = the null stream);
+ *    calls return without waiting unless stated.  A pool is used by one stream
+ *    at a time and is not reentrant.
+ *  - A failure detected by a kernel (capacity exhausted, pad overflow) is
+ *    sticky: the pool records it and every later call returns it.
+ *  - ss_last_error() returns a thread-local message for the last failure.
+ *  - No C++ exception crosses the ABI.
+ */
+#ifndef SINKSTATE_H_
+#define SINKSTATE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SS_OK = 0,
+  SS_ERR_ARG = 1,      /* NULL pointer, bad enum, negative size */
+  SS_ERR_SHAPE = 2,    /* unsupported d_k / d_v / K / r combination */
+  SS_ERR_OOM = 3,      /* device or host allocation failed */
+  SS_ERR_CAPACITY = 4, /* a region of the pool is full */
+  SS_ERR_HIP = 5,      /* a HIP runtime call failed */
+  SS_ERR_STATE = 6     /* the pool is poisoned by an earlier kernel-side failure */
+} ss_status;
+
+/* Update rule of a state ([SS] 4.2, "the same procedure also applies to GDN").
+ *  SCALAR (Mamba-2):       S_t = alpha S_{t-1} + k v^T                ([SS] 2.1)
+ *  DELTA  (Gated DeltaNet): S_t = alpha (I - beta k k^T) S_{t-1} + beta k v^T
+ *                          = alpha S_{t-1} + k w^T,  w = beta (v - alpha S_{t-1}^T k)
+ *                          ([SEED] eq. (2) with g = alpha), S_{t-1}^T k read
+ *                          from the factors. */
+typedef enum { SS_RULE_SCALAR = 0, SS_RULE_DELTA = 1 } ss_rule;
+
+typedef struct ss_pool ss_pool; /* opaque; owns all of its device memory */
+
+typedef struct {
+  int64_t n_states;           /* N >= 1 */
+  int32_t d_k, d_v;           /* each a multiple of 4, 4..256 */
+  int32_t pad_slots;          /* K, 1..8 ([SS] 5.1 uses 8) */
+  int32_t r_active;           /* r, 1..8 ([SS] 5.1 uses 8); r + K <= 16 */
+  int32_t dense_rank_limit;   /* L; < 0 selects floor(d_k d_v / (d_k + d_v)) ([SS] 4.4) */
+  int32_t promote_on_compact; /* 1: re-apply the dense test after every compaction */
+  int32_t max_frozen;         /* frozen components per state when promotion is off, 1..255; 0 = 255 */
+  int32_t force_dense;        /* 1: every state is held dense (the dense baseline) */
+  int32_t n_groups;           /* compaction groups (stagger groups), >= 1 */
+  const int32_t *group_of_state; /* host [N] in [0, n_groups), or NULL: all in group 0 */
+  const int32_t *group_offset;   /* host [n_groups] step offsets in [0, K), or NULL: all 0 */
+  const uint8_t *rule;        /* host [N] ss_rule, or NULL: all SS_RULE_SCALAR */
+  const float *eps;           /* host [N] truncation threshold eps >= 0, or NULL: eps_default */
+  float eps_default;
+  int64_t dense_capacity;     /* dense slots; 0 = N */
+} ss_pool_desc;
+
+/* Initial states, host memory, copied during create.  Components of state s
+ * are rows comp_off[s] .. comp_off[s+1]-1 of u / v / sigma and must be sorted
+ * by sigma, descending.  A state with more than L components is stored dense
+ * ([SS] 4.4: the fallback is decided after initialization).  The pad starts
+ * empty and Gamma = 1.  A NULL ss_init (or NULL comp_off) creates empty
+ * states (S = 0). */
+typedef struct {
+  const int64_t *comp_off; /* [N+1], comp_off[0] = 0 */
+  const float *u;          /* [comp_off[N]][d_k] */
+  const float *v;          /* [comp_off[N]][d_v] */
+  const float *sigma;      /* [comp_off[N]] */
+} ss_init;
+
+typedef struct {
+  int64_t n_states, n_dense, n_factored;
+  int64_t active_components, frozen_components, pad_entries;
+  int64_t live_bytes;       /* bytes of live factors, pads, dense states and metadata */
+  int64_t reserved_bytes;   /* device bytes held by the pool */
+  int64_t max_rank;         /* largest components count of a factored state */
+  int64_t rank_hist[65];    /* factored states by total components; [64] = 64 or more */
+  int64_t decode_calls, compact_calls, readout_calls;
+  uint64_t decode_bytes;    /* algorithmic bytes moved by all decode_step calls so far */
+  uint64_t compact_states;  /* states compacted (non-empty pad) so far */
+  uint64_t compact_flops;   /* algorithmic flops of all compactions so far */
+  int64_t promotions;       /* factored -> dense conversions after create */
+} ss_stats;
+
+/* Create a pool ([SS] 4.4 "Memory layout"): per state a 16-byte metadata
+ * record; an active region and a separate frozen region of components, each
+ * split per compaction group into two segments that alternate at every
+ * compaction of the group; a pad of K slots per state kept apart from the
+ * factors; and a dense region.  Initial data is uploaded on `stream`, and
+ * the call waits for it.  Errors: SS_ERR_ARG, SS_ERR_SHAPE, SS_ERR_OOM,
+ * SS_ERR_HIP.  On success *out owns the pool; release it with
+ * ss_state_pool_destroy. */
+ss_status ss_state_pool_create(const ss_pool_desc *desc, const ss_init *init, hipStream_t stream, ss_pool **out);
+
+/* Waits for the pool's streams and frees all of its memory.  NULL is a no-op. */
+ss_status ss_state_pool_destroy(ss_pool *pool);
+
+/* One decode step of every state ([SS] 4.2 "(i) Buffering", 4.4 fused decode
+ * kernel): Gamma <- alpha Gamma; w = v (scalar) or beta (v - alpha S_{t-1}^T k)
+ * (delta); append (k, w, 1/Gamma) to the pad; o = S_t^T q, read after the
+ * update.  Dense states run S <- alpha S + k w^T, o = S^T q.
+ * q, k: [N][d_k]; v, o: [N][d_v]; alpha: [N] in (0, 1]; beta: [N], may be
+ * NULL when no state uses the delta rule.  A factored state whose pad is
+ * already full poisons the pool (SS_ERR_STATE on the next call): compact its
+ * group first. */
+ss_status ss_decode_step(ss_pool *pool, const float *q, const float *k, const float *v, const float *alpha,
+                         const float *beta, float *o, hipStream_t stream);
+
+/* Read-only readout o = S^T q of every state from factors, pad and dense
+ * region, without changing the pool ([SS] 4.2 "(i) Buffering": the output is
+ * computed from the extended factors; 4.4: without materializing the state). */
+ss_status ss_readout(ss_pool *pool, const float *q, float *o, hipStream_t stream);
+
+/* Compact every state of compaction group `group` (or of all groups when
+ * group < 0) whose pad is not empty ([SS] 4.2 "(ii) Top-subspace SVD" and
+ * 3.2 Design 1): U_C = [U_active | pad keys], V_C = [V_active | pad w],
+ * Sigma_C = Gamma diag(sigma_active, c); thin QR of both; SVD of the core
+ * C = R_L Sigma_C R_R^T; rotate back; merge with the frozen components (whose
+ * sigma are scaled by Gamma); drop sigma < eps * sigma_max; the first r of
+ * the merged list become active, the rest frozen; the pad empties and Gamma
+ * resets to 1.  The result is written to the group's other segment.  With
+ * promote_on_compact, a state left with more than L components moves to the
+ * dense region ([SS] 4.4). */
+ss_status ss_compact(ss_pool *pool, int32_t group, hipStream_t stream);
+
+/* Staggered schedule ([SS] 4.2 "Staggered compaction across layers"): the
+ * groups due after decode step `step` (counted from 1) are those with
+ * (step + group_offset[g]) mod K == 0.  Writes up to `cap` group ids to out
+ * and returns their count in *n_due.  Host only. */
+ss_status ss_schedule_due(const ss_pool *pool, int64_t step, int32_t *out, int32_t cap, int32_t *n_due);
+
+/* Test hook: copy states `ids` (host array) to host memory in the canonical
+ * form, effective weights (Gamma folded in).  Waits on `stream`.  Layout per
+ * state, packed in id order:
+ *   int32 header[8] = {id_lo, dense, n_components, n_active, n_pad, rule, 0, 0}
+ *   then, if dense: float S[d_k][d_v];
+ *   else: float sigma[n_components], u[n_components][d_k], v[n_components][d_v],
+ *         c[n_pad], k[n_pad][d_k], w[n_pad][d_v]
+ * Components are in stored order: the n_active active ones first, then the
+ * frozen ones.  *needed receives the byte size; if cap is too small nothing
+ * is written and SS_ERR_CAPACITY is returned. */
+ss_status ss_state_export(ss_pool *pool, const int64_t *ids, int64_t n, void *host_buf, size_t cap, size_t *needed,
+                          hipStream_t stream);
+
+/* Pool statistics; waits on `stream`. */
+ss_status ss_pool_stats(ss_pool *pool, ss_stats *out, hipStream_t stream);
+
+/* L = floor(d_k d_v / (d_k + d_v)): above this many components the factored
+ * form (d_k + d_v + 1 values each) is larger than the dense d_k d_v ([SS] 4.4). */
+int32_t ss_dense_rank_limit(int32_t d_k, int32_t d_v);
+
+/* Algorithmic bytes one decode_step moves for one state: a factored state
+ * with n_comp components and n_pad filled slots reads its 16-byte record,
+ * all components and slots (4 (d_k + d_v + 1) bytes each), q, k, v, alpha
+ * (and beta for the delta rule), and writes the record, one slot and o.  A
+ * dense state reads and writes d_k d_v floats instead of the factors. */
+uint64_t ss_decode_bytes_per_state(int32_t d_k, int32_t d_v, int32_t n_comp, int32_t n_pad, int32_t rule,
+                                   int32_t dense);
+
+const char *ss_status_string(ss_status status);
+const char *ss_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SINKSTATE_H_ */
