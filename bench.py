@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Benchmark of the factored recurrent-state decode path on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic inputs:
+decode_step on every state (decay, append, read after update, delta rule
+where configured) followed by the compaction of the groups the staggered
+schedule makes due (Brand update, truncation, re-split, dense promotion).
+
+Default workload: 258,048 Mamba-2-shaped states (128 requests x 21 layers x
+96 heads, d_k = 128, d_v = 80, fp32), rank-8 start, 4 stagger groups, the
+whole 1,024-step job.  Inputs are generated on the GPU in chunks before each
+timed chunk (not timed).  W warmup steps first run on a scratch pool of the
+same workload.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
+METRIC = "state-steps/sec and achieved HBM GB/s (% peak) for decode_step, 258k states"
+
+
+def _pool(ss, w, init, **kw):
+    return ss.state_pool_create(w.n_states, w.d_k, w.d_v, w.K, w.r, group_of_state=init["group_of_state"],
+                                group_offset=init["group_offset"], rule=init["rule"], eps=init["eps"],
+                                comp_off=init["comp_off"], u=init["u"], v=init["v"], sigma=init["sigma"], **kw)
+
+
+def _run_steps(ss, torch, pool, xs, t0, o, ev=None):
+    """Run len(xs) steps starting after step t0; optional per-step events."""
+    for i, x in enumerate(xs):
+        t = t0 + i + 1
+        if ev is not None:
+            ev[i].record()
+        ss.decode_step(pool, x["q"], x["k"], x["v"], x["alpha"], x["beta"], o)
+        for g in ss.schedule_due(pool, t):
+            ss.compact(pool, g)
+    if ev is not None:
+        ev[len(xs)].record()
+
+
+def cpu_baseline(w, init, n_sample, n_steps):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload, all host cores."""
+    import numpy as np
+    from oracle import OraclePool, schedule_due
+    from oracle.oracle import OracleState, max_threads
+    from rank_recurrent_state_amd import workloads as W
+
+    rng = np.random.default_rng(7)
+    ids = np.sort(rng.choice(w.n_states, size=min(n_sample, w.n_states), replace=False))
+    P = OraclePool(len(ids), w.d_k, w.d_v, w.K, w.r, -1, True)
+    off = init["comp_off"]
+    for j, s in enumerate(ids):
+        a, b = off[s], off[s + 1]
+        P.set_state(j, OracleState(init["u"][a:b].astype(np.float64), init["v"][a:b].astype(np.float64),
+                                   init["sigma"][a:b].astype(np.float64), rule=int(init["rule"][s]),
+                                   eps=float(init["eps"][s])))
+    gen = W.StepInputs(w, device="cpu")
+    xs = []
+    for t in range(1, n_steps + 1):
+        x = gen.generate(t, states=ids)
+        xs.append({k: v.numpy().astype(np.float64) for k, v in x.items()})
+    grp = init["group_of_state"][ids]
+    nthreads = max_threads()
+    t_dec = t_cmp = 0.0
+    for t, x in enumerate(xs, start=1):
+        a = time.perf_counter()
+        P.decode(x["q"], x["k"], x["v"], x["alpha"], x["beta"], nthreads=nthreads)
+        b = time.perf_counter()
+        due = schedule_due(t, w.K, init["group_offset"])
+        if due:
+            P.compact(np.nonzero(np.isin(grp, due))[0], nthreads=nthreads)
+        t_dec += b - a
+        t_cmp += time.perf_counter() - b
+    tot = t_dec + t_cmp
+    return {"value": len(ids) * n_steps / tot, "unit": "state-steps/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"{len(ids)} states drawn from the same {w.n_states}-state workload, steps 1-{n_steps} "
+                      f"(decode + staggered compaction), fp64, OpenMP over states",
+            "decode_state_steps_per_s": len(ids) * n_steps / t_dec, "seconds": tot,
+            "cpu": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default: the workload's job length)")
+    ap.add_argument("--warmup", type=int, default=16, help="untimed steps on a scratch pool first")
+    ap.add_argument("--workload", default="mamba2_258k")
+    ap.add_argument("--requests", type=int, default=None, help="override the number of requests")
+    ap.add_argument("--chunk", type=int, default=64, help="steps whose inputs are generated at once")
+    ap.add_argument("--dense-steps", type=int, default=64, help="steps of the dense HIP baseline (0: skip)")
+    ap.add_argument("--cpu-sample", type=int, default=16384)
+    ap.add_argument("--cpu-steps", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (the path shards by request "
+                                   "with no exchange step, see DESIGN.md)"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from rank_recurrent_state_amd import sinkstate as ss
+    from rank_recurrent_state_amd import workloads as W
+
+    torch.cuda.set_device(0)
+    w = W.get(args.workload, n_requests=args.requests)
+    K_steps = args.steps if args.steps is not None else w.steps
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)  # noqa: E731
+    log(f"[bench] workload {w.name}: {w.n_states} states {w.d_k}x{w.d_v}, {K_steps} timed steps")
+    t_init = time.time()
+    init = W.initial_state(w)
+    log(f"[bench] initial states built in {time.time() - t_init:.1f}s")
+    gen = W.StepInputs(w, device="cuda")
+    o = torch.empty(w.n_states, w.d_v, device="cuda")
+
+    # warmup on a scratch pool of the same workload
+    if args.warmup > 0:
+        pool = _pool(ss, w, init)
+        for c0 in range(0, args.warmup, args.chunk):
+            xs = [gen.generate(t) for t in range(c0 + 1, min(args.warmup, c0 + args.chunk) + 1)]
+            _run_steps(ss, torch, pool, xs, c0, o)
+        torch.cuda.synchronize()
+        pool.close()
+        del xs
+        log(f"[bench] warmup {args.warmup} steps done")
+
+    # the timed job
+    pool = _pool(ss, w, init)
+    st0 = ss.pool_stats(pool)
+    ss.pool_timing(pool, True)
+    step_ms = []
+    hist_marks = {}
+    t = 0
+    while t < K_steps:
+        n = min(args.chunk, K_steps - t)
+        xs = [gen.generate(s) for s in range(t + 1, t + n + 1)]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        torch.cuda.synchronize()
+        _run_steps(ss, torch, pool, xs, t, o, ev)
+        torch.cuda.synchronize()
+        step_ms += [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
+        t += n
+        del xs
+        st = ss.pool_stats(pool)
+        hist_marks[t] = {"dense_fraction": st["n_dense"] / w.n_states,
+                         "mean_rank_factored": (st["active_components"] + st["frozen_components"])
+                         / max(1, st["n_factored"])}
+        log(f"[bench] {t}/{K_steps} steps, dense fraction {hist_marks[t]['dense_fraction']:.3f}, "
+            f"mean factored rank {hist_marks[t]['mean_rank_factored']:.1f}, "
+            f"chunk {sum(step_ms[-n:]):.1f} ms")
+    st1 = ss.pool_stats(pool)
+    pool.close()
+    total_ms = float(sum(step_ms))
+    value = w.n_states * K_steps / (total_ms / 1e3)
+
+    kms = {k: st1["kernel_ms"][k] - st0["kernel_ms"][k] for k in st1["kernel_ms"]}
+    kn = {k: st1["kernel_launches"][k] - st0["kernel_launches"][k] for k in st1["kernel_launches"]}
+    bytes_k = {"decode_factored": st1["decode_bytes_factored"] - st0["decode_bytes_factored"],
+               "decode_dense": st1["decode_bytes_dense"] - st0["decode_bytes_dense"]}
+    decode_ms = kms["decode_factored"] + kms["decode_dense"]
+    decode_bytes = bytes_k["decode_factored"] + bytes_k["decode_dense"]
+    dom = max(("decode_factored", "decode_dense"), key=lambda k: kms[k])
+    ach = bytes_k[dom] / (kms[dom] / 1e3) / 1e9 if kms[dom] > 0 else 0.0
+    per_kernel = {}
+    for k in ("decode_factored", "decode_dense"):
+        if kn[k]:
+            gbs = bytes_k[k] / (kms[k] / 1e3) / 1e9
+            per_kernel[k] = {"launches": kn[k], "avg_us": 1e3 * kms[k] / kn[k], "bytes_per_launch": bytes_k[k] / kn[k],
+                             "achieved_GBs": gbs, "frac": gbs / HBM_PEAK_GBS}
+    cflops = st1["compact_flops"] - st0["compact_flops"]
+    cstates = st1["compact_states"] - st0["compact_states"]
+    compaction = {"launches": kn["compact"], "ms_total": kms["compact"], "states": cstates,
+                  "states_per_s": cstates / (kms["compact"] / 1e3) if kms["compact"] else None,
+                  "algorithmic_TFLOPs": cflops / (kms["compact"] / 1e3) / 1e12 if kms["compact"] else None,
+                  "materialize_ms_total": kms["materialize"], "promotions": st1["promotions"] - st0["promotions"]}
+    sm = np.array(step_ms)
+    first = min(64, K_steps)
+    phases = {"steps_1_%d_ms_per_step" % first: float(sm[:first].mean()),
+              "steps_%d_%d_ms_per_step" % (first + 1, K_steps): float(sm[first:].mean()) if K_steps > first else None,
+              "p50_step_ms": float(np.percentile(sm, 50)), "p99_step_ms": float(np.percentile(sm, 99)),
+              "state_mix": hist_marks}
+
+    # dense HIP baseline on the same inputs
+    dense = None
+    if args.dense_steps > 0:
+        dp = _pool(ss, w, init, force_dense=True)
+        xs = [gen.generate(s) for s in range(1, args.dense_steps + 1)]
+        ss.pool_timing(dp, True)
+        s0 = ss.pool_stats(dp)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for x in xs:
+            ss.decode_step(dp, x["q"], x["k"], x["v"], x["alpha"], x["beta"], o)
+        e1.record()
+        torch.cuda.synchronize()
+        s1 = ss.pool_stats(dp)
+        dp.close()
+        del xs
+        dms = e0.elapsed_time(e1)
+        kd = s1["kernel_ms"]["decode_dense"] - s0["kernel_ms"]["decode_dense"]
+        bd = s1["decode_bytes_dense"] - s0["decode_bytes_dense"]
+        dense = {"value": w.n_states * args.dense_steps / (dms / 1e3), "unit": "state-steps/s",
+                 "ms_per_step": dms / args.dense_steps, "steps": args.dense_steps,
+                 "achieved_GBs": bd / (kd / 1e3) / 1e9, "frac": bd / (kd / 1e3) / 1e9 / HBM_PEAK_GBS,
+                 "kernel_avg_us": 1e3 * kd / args.dense_steps, "bytes_per_step": bd / args.dense_steps}
+        log(f"[bench] dense baseline {dense['ms_per_step']:.3f} ms/step, {dense['achieved_GBs']:.0f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, init, args.cpu_sample, args.cpu_steps)
+        log(f"[bench] cpu baseline {cpu['value']:.3e} state-steps/s on {cpu['cores']} threads ({cpu['seconds']:.1f}s)")
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "state-steps/s",
+        "n_gpus": 1,
+        "steps": K_steps,
+        "warmup": args.warmup,
+        "ms_per_step": total_ms / K_steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.description}; {w.n_requests} requests x {w.n_layers} layers x "
+                               f"{w.n_heads} heads, K={w.K}, r={w.r}, stagger={w.stagger}, whole {K_steps}-step job",
+                   "n_states": w.n_states, "d_k": w.d_k, "d_v": w.d_v},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": ach / HBM_PEAK_GBS, "traffic": None},
+        "cpu_baseline": cpu,
+        "decode_step": {"state_steps_per_s": w.n_states * K_steps / (decode_ms / 1e3) if decode_ms else None,
+                        "achieved_GBs": decode_bytes / (decode_ms / 1e3) / 1e9 if decode_ms else None,
+                        "kernels": per_kernel},
+        "compaction": compaction,
+        "phases": phases,
+        "dense_baseline": dense,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

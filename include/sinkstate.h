@@ -94,6 +94,17 @@ typedef struct {
   const float *sigma;      /* [comp_off[N]] */
 } ss_init;
 
+/* kernels timed by ss_pool_timing */
+enum {
+  SS_KERNEL_DECODE_FACTORED = 0,
+  SS_KERNEL_DECODE_DENSE = 1,
+  SS_KERNEL_READOUT_FACTORED = 2,
+  SS_KERNEL_READOUT_DENSE = 3,
+  SS_KERNEL_COMPACT = 4,
+  SS_KERNEL_MATERIALIZE = 5,
+  SS_KERNEL_COUNT = 8
+};
+
 typedef struct {
   int64_t n_states, n_dense, n_factored;
   int64_t active_components, frozen_components, pad_entries;
@@ -103,9 +114,14 @@ typedef struct {
   int64_t rank_hist[65];    /* factored states by total components; [64] = 64 or more */
   int64_t decode_calls, compact_calls, readout_calls;
   uint64_t decode_bytes;    /* algorithmic bytes moved by all decode_step calls so far */
+  uint64_t decode_bytes_factored; /* ... by the factored-state kernel */
+  uint64_t decode_bytes_dense;    /* ... by the dense-region kernel */
   uint64_t compact_states;  /* states compacted (non-empty pad) so far */
   uint64_t compact_flops;   /* algorithmic flops of all compactions so far */
   int64_t promotions;       /* factored -> dense conversions after create */
+  int64_t cap_truncations;  /* frozen components dropped because max_frozen was reached */
+  double kernel_ms[SS_KERNEL_COUNT];       /* summed HIP-event durations while timing is on */
+  int64_t kernel_launches[SS_KERNEL_COUNT];
 } ss_stats;
 
 /* Create a pool ([SS] 4.4 "Memory layout"): per state a 16-byte metadata
@@ -168,8 +184,15 @@ ss_status ss_schedule_due(const ss_pool *pool, int64_t step, int32_t *out, int32
 ss_status ss_state_export(ss_pool *pool, const int64_t *ids, int64_t n, void *host_buf, size_t cap, size_t *needed,
                           hipStream_t stream);
 
-/* Pool statistics; waits on `stream`. */
+/* Pool statistics; waits on `stream`.  Reading the statistics also collects
+ * the kernel durations recorded since the previous call. */
 ss_status ss_pool_stats(ss_pool *pool, ss_stats *out, hipStream_t stream);
+
+/* Measurement hook: with enable = 1 every later kernel launch of the pool is
+ * bracketed by a pair of HIP events recorded on the launch stream, and
+ * ss_pool_stats adds their elapsed times to kernel_ms / kernel_launches.
+ * enable = 0 stops recording.  Costs two event records per launch. */
+ss_status ss_pool_timing(ss_pool *pool, int32_t enable);
 
 /* L = floor(d_k d_v / (d_k + d_v)): above this many components the factored
  * form (d_k + d_v + 1 values each) is larger than the dense d_k d_v ([SS] 4.4). */

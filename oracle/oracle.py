@@ -50,7 +50,7 @@ def _load():
     lib.orc_destroy.argtypes = [ctypes.c_void_p]
     lib.orc_dense_limit.argtypes = [ctypes.c_void_p]
     lib.orc_set_state.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_int,
-                                  _dp, _dp, _dp, ctypes.c_int, _dp, _dp, _dp, ctypes.c_int, _dp]
+                                  _dp, _dp, _dp, ctypes.c_int, _dp, _dp, _dp, ctypes.c_int, _dp, ctypes.c_int]
     lib.orc_get_sizes.argtypes = [ctypes.c_void_p, ctypes.c_int64] + [ctypes.POINTER(ctypes.c_int)] * 4 + [_dp]
     lib.orc_get_state.argtypes = [ctypes.c_void_p, ctypes.c_int64] + [_dp] * 7
     lib.orc_get_bound.restype = ctypes.c_double
@@ -182,12 +182,14 @@ class OraclePool:
             pass
 
     # -- state access ------------------------------------------------------
-    def set_state(self, s, st: OracleState):
+    def set_state(self, s, st: OracleState, as_init: bool = True):
+        """Load a state.  as_init=True applies the create-time dense fallback (R > L);
+        as_init=False loads a mid-run state exactly as given."""
         dk, dv = self.d_k, self.d_v
         if st.S is not None:
             S = _f64(st.S).reshape(dk, dv)
             rc = self._lib.orc_set_state(self._p, int(s), int(st.rule), float(st.eps), 0, None, None, None, 0, None,
-                                         None, None, 1, _ptr(S))
+                                         None, None, 1, _ptr(S), int(as_init))
         else:
             sig = _f64(st.sigma if st.sigma is not None else np.zeros(0))
             R = sig.shape[0]
@@ -198,7 +200,7 @@ class OraclePool:
             PK = _f64(st.PK if n else np.zeros((0, dk))).reshape(n, dk)
             PW = _f64(st.PW if n else np.zeros((0, dv))).reshape(n, dv)
             rc = self._lib.orc_set_state(self._p, int(s), int(st.rule), float(st.eps), R, _ptr(U), _ptr(V), _ptr(sig),
-                                         n, _ptr(PK), _ptr(PW), _ptr(pc), 0, None)
+                                         n, _ptr(PK), _ptr(PW), _ptr(pc), 0, None, int(as_init))
         if rc != 0:
             raise ValueError(f"orc_set_state failed for state {s}")
 

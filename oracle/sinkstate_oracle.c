@@ -312,12 +312,13 @@ static int make_dense(orc_pool *p, orc_state *x) {
 }
 
 /* Set one state.  Components are given as rows and are sorted here by
- * sigma (descending, stable).  A factored state given with R > L falls back
- * to the dense form (SinkState 4.4: the fallback is decided after
- * initialization). */
+ * sigma (descending, stable).  With as_init set, a factored state given with
+ * R > L falls back to the dense form (SinkState 4.4: the fallback is decided
+ * after initialization); without it the state is loaded as given, e.g. to
+ * continue from a state taken in the middle of a run. */
 int orc_set_state(orc_pool *p, int64_t s, int rule, double eps, int R, const double *U, const double *V,
                   const double *sig, int n, const double *PK, const double *PW, const double *pc, int dense,
-                  const double *S) {
+                  const double *S, int as_init) {
   if (!p || s < 0 || s >= p->N || R < 0 || n < 0 || n > p->K) return -1;
   int dk = p->d_k, dv = p->d_v;
   orc_state *x = &p->st[s];
@@ -359,7 +360,7 @@ int orc_set_state(orc_pool *p, int64_t s, int rule, double eps, int R, const dou
     x->pc[j] = pc[j];
   }
   x->n = n;
-  if (x->R > p->L) return make_dense(p, x);
+  if (as_init && x->R > p->L) return make_dense(p, x);
   return 0;
 }
 

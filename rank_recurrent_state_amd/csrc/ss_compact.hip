@@ -1,0 +1,586 @@
+// ss_compact.hip -- Brand compaction, dense materialization, pool scatter.
+//
+// Compaction (SinkState 3.2 Design 1 and 4.2 "(ii) Top-subspace SVD"): one
+// 64-lane wavefront per state of the group, four states per workgroup.
+//   1. U_C = [U_active | pad keys] (d_k x m), V_C = [V_active | pad w]
+//      (d_v x m), weights Gamma * (sigma_active, c); m = r_a + n <= 16.
+//      Element e of a column lives in lane e % 64, register e / 64.
+//   2. Thin QR of both sides by classical Gram-Schmidt with one
+//      re-orthogonalization pass (CGS2); a column whose residual is at most
+//      1e-5 of its own norm is taken as dependent and zeroed (its R row is
+//      then zero too, so it cannot create a spurious component).
+//   3. Core C = R_L diag(w) R_R^T (m x m) in LDS.
+//   4. One-sided (Hestenes) Jacobi SVD of C: 8 lanes per column pair, pairs
+//      in round-robin (circle) order so that m/2 disjoint pairs rotate at
+//      once; sweeps until no pair is off-orthogonal by more than 1e-6.
+//   5. Sort the local singular values; merge them with the frozen ones
+//      (scaled by Gamma) in descending order, local first on ties; drop
+//      sigma < eps * sigma_max and sigma = 0 (SinkState 4.1, 4.2 example).
+//   6. U' = Q_L U_hat, V' = Q_R V_hat for the kept local components; kept
+//      frozen components are copied.  The first r of the merged list go to
+//      the group's other active segment, the rest to its other frozen segment.
+//   7. With promotion on, a state left with more than L components is queued
+//      for the dense region (SinkState 4.4).
+// No global-memory intermediates: QR factors live in registers, the small
+// matrices in LDS (SinkState 4.4: fused chains of factor algebra).
+#include "ss_internal.h"
+#include "ss_wave.h"
+
+namespace ss {
+
+namespace {
+
+constexpr float kTau2 = 1e-10f;  // (1e-5)^2: CGS2 dependent-column test on squared norms
+constexpr float kTolJ = 1e-6f;   // Jacobi: rotate while |a_i.a_j| > tol |a_i| |a_j|
+constexpr int kMaxSweeps = 16;
+constexpr int kLdsPerWave = 1152;
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// In-place CGS2 thin QR of the register-resident columns a[0..m).  R goes to
+// LDS, column-major 16 x 16: Rm[j * 16 + i] = R(i, j).
+template <int NS>
+__device__ __forceinline__ void cgs2(float (&a)[kMaxM][NS], int m, int lane, float *Rm) {
+#pragma unroll
+  for (int j = 0; j < kMaxM; ++j) {
+    if (j < m) {
+      float n0 = 0.f;
+#pragma unroll
+      for (int t = 0; t < NS; ++t) n0 = fmaf(a[j][t], a[j][t], n0);
+      n0 = wave_sum(n0);
+      float rc[kMaxM];
+#pragma unroll
+      for (int i = 0; i < kMaxM; ++i) rc[i] = 0.f;
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass) {
+        float d[kMaxM];
+#pragma unroll
+        for (int i = 0; i < j; ++i) {
+          float x = 0.f;
+#pragma unroll
+          for (int t = 0; t < NS; ++t) x = fmaf(a[i][t], a[j][t], x);
+          d[i] = wave_sum(x);
+        }
+#pragma unroll
+        for (int i = 0; i < j; ++i) {
+          rc[i] += d[i];
+#pragma unroll
+          for (int t = 0; t < NS; ++t) a[j][t] = fmaf(-d[i], a[i][t], a[j][t]);
+        }
+      }
+      float nn = 0.f;
+#pragma unroll
+      for (int t = 0; t < NS; ++t) nn = fmaf(a[j][t], a[j][t], nn);
+      nn = wave_sum(nn);
+      const bool keep = nn > 0.f && nn > kTau2 * n0;
+      const float nrm = sqrtf(nn);
+      const float inv = keep ? 1.0f / nrm : 0.f;
+#pragma unroll
+      for (int t = 0; t < NS; ++t) a[j][t] *= inv;
+      if (lane == 0) {
+#pragma unroll
+        for (int i = 0; i < kMaxM; ++i) Rm[j * 16 + i] = (i < j) ? rc[i] : ((i == j && keep) ? nrm : 0.f);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < NS; ++t) a[j][t] = 0.f;
+      if (lane == 0) {
+#pragma unroll
+        for (int i = 0; i < kMaxM; ++i) Rm[j * 16 + i] = 0.f;
+      }
+    }
+  }
+}
+
+// One-sided Jacobi on the 16 x 16 column-major C (columns >= m are zero),
+// accumulating the rotations into Vh.  Returns the number of sweeps run.
+__device__ int jacobi16(float *Cm, float *Vh, int m, int lane) {
+  const int M = (m + 1) & ~1;
+  if (M < 2) return 0;
+  const int np = M >> 1, rounds = M - 1;
+  const int p = lane >> 3, sub = lane & 7;
+  const bool act = p < np;
+  int sweep = 0;
+  while (sweep < kMaxSweeps) {
+    ++sweep;
+    bool any = false;
+    for (int k = 0; k < rounds; ++k) {
+      int ci, cj;
+      if (p == 0) {
+        ci = k;
+        cj = M - 1;
+      } else {
+        ci = (k + p) % (M - 1);
+        cj = (k - p + (M - 1)) % (M - 1);
+      }
+      float x0 = 0.f, x1 = 0.f, y0 = 0.f, y1 = 0.f;
+      if (act) {
+        x0 = Cm[ci * 16 + sub];
+        x1 = Cm[ci * 16 + sub + 8];
+        y0 = Cm[cj * 16 + sub];
+        y1 = Cm[cj * 16 + sub + 8];
+      }
+      float aa = fmaf(x0, x0, x1 * x1), bb = fmaf(y0, y0, y1 * y1), gg = fmaf(x0, y0, x1 * y1);
+      aa = group_sum<8>(aa);
+      bb = group_sum<8>(bb);
+      gg = group_sum<8>(gg);
+      const bool rot = act && gg != 0.f && fabsf(gg) > kTolJ * sqrtf(aa * bb);
+      if (rot) {
+        const float zeta = (bb - aa) / (2.f * gg);
+        const float az = fabsf(zeta);
+        const float t = az > 1e10f ? 0.5f / zeta : copysignf(1.f, zeta) / (az + sqrtf(fmaf(zeta, zeta, 1.f)));
+        const float c = 1.0f / sqrtf(fmaf(t, t, 1.f)), sn = c * t;
+        Cm[ci * 16 + sub] = c * x0 - sn * y0;
+        Cm[ci * 16 + sub + 8] = c * x1 - sn * y1;
+        Cm[cj * 16 + sub] = sn * x0 + c * y0;
+        Cm[cj * 16 + sub + 8] = sn * x1 + c * y1;
+        const float vx0 = Vh[ci * 16 + sub], vx1 = Vh[ci * 16 + sub + 8];
+        const float vy0 = Vh[cj * 16 + sub], vy1 = Vh[cj * 16 + sub + 8];
+        Vh[ci * 16 + sub] = c * vx0 - sn * vy0;
+        Vh[ci * 16 + sub + 8] = c * vx1 - sn * vy1;
+        Vh[cj * 16 + sub] = sn * vx0 + c * vy0;
+        Vh[cj * 16 + sub + 8] = sn * vx1 + c * vy1;
+      }
+      any = any || (__builtin_amdgcn_ballot_w64(rot) != 0ull);
+      wave_sync();
+    }
+    if (!any) break;
+  }
+  return sweep;
+}
+
+// copy one component (u, v) between arenas with float4 lanes
+__device__ __forceinline__ void copy_comp(const float *su, const float *sv, float *du, float *dv_, int dk, int dv,
+                                          int lane) {
+  const int dk4 = dk >> 2, tot = dk4 + (dv >> 2);
+  for (int e = lane; e < tot; e += 64) {
+    if (e < dk4) st4(du + 4 * e, ld4(su + 4 * e));
+    else st4(dv_ + 4 * (e - dk4), ld4(sv + 4 * (e - dk4)));
+  }
+}
+
+// number of frozen sigma (descending, scaled by g) that are >= thr and > 0
+__device__ __forceinline__ int frozen_kept(const float *fs, int rf, float g, float thr) {
+  int lo = 0, hi = rf;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    const float x = fs[mid] * g;
+    if (x >= thr && x > 0.f) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// number of the first kf frozen sigma (descending, scaled by g) that are > x
+__device__ __forceinline__ int frozen_greater(const float *fs, int kf, float g, float x) {
+  int lo = 0, hi = kf;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (fs[mid] * g > x) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+template <int NS>
+__global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
+  __shared__ float lds[4][kLdsPerWave];
+  const int w = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int mi = blockIdx.x * 4 + w;
+  if (mi >= a.n_members) return;
+  float *Rl = lds[w];
+  float *Rr = Rl + 256;
+  float *Cm = Rl + 512;
+  float *Vh = Rl + 768;
+  float *scw = Rl + 1024;
+  float *sgs = Rl + 1040;
+  float *sraw = Rl + 1056;
+  int *perm = reinterpret_cast<int *>(Rl + 1072);
+
+  const int s = uniform(a.members[mi]);
+  const Meta m = a.meta[s];
+  const uint32_t packed = (uint32_t)uniform((int)m.packed);
+  const uint32_t flags = meta_flags(packed);
+  if (flags & FLAG_DENSE) return;
+  const int ra = meta_ra(packed), rf = meta_rf(packed), n = meta_n(packed);
+  const int off_a = uniform(m.off_a), off_f = uniform(m.off_f);
+  const float gamma = uniformf(m.gamma);
+  const int dk = a.dk, dv = a.dv, K = a.K, r = a.r;
+  const int64_t dst_a = a.dst_base_a + (int64_t)mi * r;
+  const int64_t dst_f = a.dst_base_f + (int64_t)mi * a.fcap;
+
+  if (n == 0) {  // nothing buffered: move the components to the other segments unchanged
+    for (int j = 0; j < ra; ++j) {
+      copy_comp(a.act.u + (int64_t)(off_a + j) * dk, a.act.v + (int64_t)(off_a + j) * dv,
+                a.act.u + (dst_a + j) * dk, a.act.v + (dst_a + j) * dv, dk, dv, lane);
+      if (lane == 0) a.act.s[dst_a + j] = a.act.s[off_a + j] * gamma;
+    }
+    for (int j = 0; j < rf; ++j) {
+      copy_comp(a.frz.u + (int64_t)(off_f + j) * dk, a.frz.v + (int64_t)(off_f + j) * dv,
+                a.frz.u + (dst_f + j) * dk, a.frz.v + (dst_f + j) * dv, dk, dv, lane);
+      if (lane == 0) a.frz.s[dst_f + j] = a.frz.s[off_f + j] * gamma;
+    }
+    if (lane == 0) {
+      Meta nm;
+      nm.off_a = (int32_t)dst_a;
+      nm.off_f = (int32_t)dst_f;
+      nm.gamma = 1.0f;
+      nm.packed = meta_pack(ra, rf, 0, flags);
+      a.meta[s] = nm;
+    }
+    return;
+  }
+
+  const int mcol = ra + n;
+  float uc[kMaxM][NS], vc[kMaxM][NS];
+#pragma unroll
+  for (int j = 0; j < kMaxM; ++j) {
+    const bool valid = j < mcol;
+    const bool isact = j < ra;
+    const float *su = isact ? a.act.u + (int64_t)(off_a + j) * dk : a.pk + ((int64_t)s * K + (j - ra)) * dk;
+    const float *sv = isact ? a.act.v + (int64_t)(off_a + j) * dv : a.pw + ((int64_t)s * K + (j - ra)) * dv;
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+      const int row = lane + 64 * t;
+      uc[j][t] = (valid && row < dk) ? su[row] : 0.f;
+      vc[j][t] = (valid && row < dv) ? sv[row] : 0.f;
+    }
+  }
+  if (lane < kMaxM) {
+    float wgt = 0.f;
+    if (lane < ra) wgt = a.act.s[off_a + lane] * gamma;
+    else if (lane < mcol) wgt = a.pc[(int64_t)s * K + (lane - ra)] * gamma;
+    scw[lane] = wgt;
+  }
+  cgs2<NS>(uc, mcol, lane, Rl);
+  cgs2<NS>(vc, mcol, lane, Rr);
+  wave_sync();
+  for (int e = lane; e < 256; e += 64) {
+    const int i = e & 15, j = e >> 4;
+    float acc = 0.f;
+    if (i < mcol && j < mcol) {
+      for (int t = (i > j ? i : j); t < mcol; ++t) acc = fmaf(Rl[t * 16 + i] * scw[t], Rr[t * 16 + j], acc);
+    }
+    Cm[j * 16 + i] = acc;
+    Vh[j * 16 + i] = (i == j) ? 1.f : 0.f;
+  }
+  wave_sync();
+  const int sweeps = jacobi16(Cm, Vh, mcol, lane);
+  if (lane < 16) {
+    float x = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x = fmaf(Cm[lane * 16 + i], Cm[lane * 16 + i], x);
+    sraw[lane] = lane < mcol ? sqrtf(x) : -1.f;
+  }
+  wave_sync();
+  if (lane < mcol) {
+    const float my = sraw[lane];
+    int rank = 0;
+    for (int i = 0; i < mcol; ++i) {
+      const float o = sraw[i];
+      rank += (o > my) || (o == my && i < lane);
+    }
+    perm[rank] = lane;
+    sgs[rank] = my;
+  }
+  wave_sync();
+
+  // merge with the frozen part and truncate
+  const float *fs = a.frz.s + off_f;
+  const float eps = a.eps[s];
+  const float fs0 = rf > 0 ? fs[0] * gamma : 0.f;
+  const float smax = fmaxf(sgs[0], fs0);
+  const float thr = eps * smax;
+  int kl = 0;
+  for (int i = 0; i < mcol; ++i) kl += (sgs[i] >= thr && sgs[i] > 0.f) ? 1 : 0;
+  const int kf = frozen_kept(fs, rf, gamma, thr);
+  int total = kl + kf;
+  const int cap_total = r + a.fcap;
+  if (total > cap_total) {
+    if (lane == 0)
+      __hip_atomic_fetch_add(&a.counters[C_CAP_TRUNC], (uint32_t)(total - cap_total), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    total = cap_total;
+  }
+  const int ra2 = total < r ? total : r, rf2 = total - ra2;
+
+  // kept local components: U' = Q_L U_hat, V' = Q_R V_hat
+  for (int i = 0; i < kl; ++i) {
+    const int pos = i + frozen_greater(fs, kf, gamma, sgs[i]);
+    if (pos >= total) continue;
+    const int j = perm[i];
+    const float inv = 1.0f / sgs[i];
+    float ou[NS], ov[NS];
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+      ou[t] = 0.f;
+      ov[t] = 0.f;
+    }
+#pragma unroll
+    for (int tt = 0; tt < kMaxM; ++tt) {
+      const float cu = Cm[j * 16 + tt] * inv;
+      const float cv = Vh[j * 16 + tt];
+#pragma unroll
+      for (int t = 0; t < NS; ++t) {
+        ou[t] = fmaf(uc[tt][t], cu, ou[t]);
+        ov[t] = fmaf(vc[tt][t], cv, ov[t]);
+      }
+    }
+    float *du = pos < r ? a.act.u + (dst_a + pos) * dk : a.frz.u + (dst_f + pos - r) * dk;
+    float *dvv = pos < r ? a.act.v + (dst_a + pos) * dv : a.frz.v + (dst_f + pos - r) * dv;
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+      const int row = lane + 64 * t;
+      if (row < dk) du[row] = ou[t];
+      if (row < dv) dvv[row] = ov[t];
+    }
+    if (lane == 0) (pos < r ? a.act.s[dst_a + pos] : a.frz.s[dst_f + pos - r]) = sgs[i];
+  }
+  // kept frozen components: copied, sigma scaled by Gamma
+  for (int f = 0; f < kf; ++f) {
+    const float sf = fs[f] * gamma;
+    int pos = f;
+    for (int i = 0; i < kl; ++i) pos += (sgs[i] >= sf) ? 1 : 0;
+    if (pos >= total) continue;
+    float *du = pos < r ? a.act.u + (dst_a + pos) * dk : a.frz.u + (dst_f + pos - r) * dk;
+    float *dvv = pos < r ? a.act.v + (dst_a + pos) * dv : a.frz.v + (dst_f + pos - r) * dv;
+    copy_comp(a.frz.u + (int64_t)(off_f + f) * dk, a.frz.v + (int64_t)(off_f + f) * dv, du, dvv, dk, dv, lane);
+    if (lane == 0) (pos < r ? a.act.s[dst_a + pos] : a.frz.s[dst_f + pos - r]) = sf;
+  }
+  if (lane == 0) {
+    Meta nm;
+    nm.off_a = (int32_t)dst_a;
+    nm.off_f = (int32_t)dst_f;
+    nm.gamma = 1.0f;
+    nm.packed = meta_pack(ra2, rf2, 0, flags);
+    a.meta[s] = nm;
+    if (a.promote && total > a.L) {
+      const uint32_t idx =
+          __hip_atomic_fetch_add(&a.counters[C_PROMOTE_COUNT], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      a.promote_list[idx] = s;
+    }
+    const unsigned long long D = (unsigned long long)(dk + dv), mm = (unsigned long long)mcol;
+    const unsigned long long flops = 4ull * D * mm * (mm - 1) + 2ull * mm * mm * mm +
+                                     9ull * mm * mm * (mm - 1) * (unsigned long long)sweeps +
+                                     2ull * D * mm * (unsigned long long)kl;
+    __hip_atomic_fetch_add(&a.acct_flops[s & (kAcctSlots - 1)], flops, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(&a.acct_states[s & (kAcctSlots - 1)], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Materialize S = sum_c sigma_c u_c v_c^T into a new dense slot (256 threads
+// per state, components staged through LDS in chunks of CH).
+constexpr int kMatCH = 16;
+
+template <int NR>
+__global__ __launch_bounds__(256) void k_materialize(MaterializeArgs a) {
+  extern __shared__ float smem[];
+  __shared__ int s_slot;
+  const int t = threadIdx.x;
+  const int dk = a.dk, dv = a.dv;
+  const int C4 = dv >> 2, RG = 256 / C4;
+  const int c = t % C4, g = t / C4;
+  const bool act = t < RG * C4;
+  float *su = smem;                 // [CH][dk]
+  float *sv = smem + kMatCH * dk;   // [CH][dv]
+  float *ss = sv + kMatCH * dv;     // [CH]
+  const uint32_t cnt = a.count ? *a.count : (uint32_t)a.fixed_count;
+  for (uint32_t li = blockIdx.x; li < cnt; li += gridDim.x) {
+    const int s = a.list[li];
+    const Meta m = a.meta[s];
+    const uint32_t flags = meta_flags(m.packed) & FLAG_DELTA;
+    int n1, n2;
+    const float *u1, *v1, *s1, *u2, *v2, *s2;
+    float scale = 1.0f;
+    if (a.csr_off) {
+      const int64_t o0 = a.csr_off[s], o1 = a.csr_off[s + 1];
+      n1 = (int)(o1 - o0);
+      u1 = a.csr_u + o0 * dk;
+      v1 = a.csr_v + o0 * dv;
+      s1 = a.csr_s + o0;
+      n2 = 0;
+      u2 = u1;
+      v2 = v1;
+      s2 = s1;
+    } else {
+      n1 = (int)meta_ra(m.packed);
+      n2 = (int)meta_rf(m.packed);
+      u1 = a.act.u + (int64_t)m.off_a * dk;
+      v1 = a.act.v + (int64_t)m.off_a * dv;
+      s1 = a.act.s + m.off_a;
+      u2 = a.frz.u + (int64_t)m.off_f * dk;
+      v2 = a.frz.v + (int64_t)m.off_f * dv;
+      s2 = a.frz.s + m.off_f;
+      scale = m.gamma;
+    }
+    __syncthreads();
+    if (t == 0) {
+      const uint32_t slot =
+          __hip_atomic_fetch_add(&a.counters[C_DENSE_COUNT], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (slot < (uint32_t)a.cap_d) {
+        s_slot = (int)slot;
+      } else {
+        s_slot = -1;
+        __hip_atomic_fetch_add(&a.counters[C_ERR_DENSE_CAP], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *a.hflag = 1u;
+      }
+    }
+    __syncthreads();
+    const int slot = s_slot;
+    if (slot < 0) continue;
+    const int total = n1 + n2;
+    float4 acc[NR];
+#pragma unroll
+    for (int j = 0; j < NR; ++j) acc[j] = zero4();
+    for (int c0 = 0; c0 < total; c0 += kMatCH) {
+      __syncthreads();
+      for (int e = t; e < kMatCH * dk; e += 256) {
+        const int cc = e / dk, row = e - cc * dk, comp = c0 + cc;
+        su[e] = comp < total ? (comp < n1 ? u1[(int64_t)comp * dk + row] : u2[(int64_t)(comp - n1) * dk + row]) : 0.f;
+      }
+      for (int e = t; e < kMatCH * dv; e += 256) {
+        const int cc = e / dv, col = e - cc * dv, comp = c0 + cc;
+        sv[e] = comp < total ? (comp < n1 ? v1[(int64_t)comp * dv + col] : v2[(int64_t)(comp - n1) * dv + col]) : 0.f;
+      }
+      if (t < kMatCH) {
+        const int comp = c0 + t;
+        ss[t] = comp < total ? scale * (comp < n1 ? s1[comp] : s2[comp - n1]) : 0.f;
+      }
+      __syncthreads();
+      if (act) {
+        const int lim = (total - c0) < kMatCH ? (total - c0) : kMatCH;
+        for (int cc = 0; cc < lim; ++cc) {
+          const float4 v4 = scale4(ss[cc], *reinterpret_cast<const float4 *>(sv + cc * dv + 4 * c));
+#pragma unroll
+          for (int j = 0; j < NR; ++j) {
+            const int row = g + j * RG;
+            if (row < dk) acc[j] = fma4(su[cc * dk + row], v4, acc[j]);
+          }
+        }
+      }
+    }
+    float *S = a.dense + (int64_t)slot * dk * dv;
+    if (act) {
+#pragma unroll
+      for (int j = 0; j < NR; ++j) {
+        const int row = g + j * RG;
+        if (row < dk) st4(S + (int64_t)row * dv + 4 * c, acc[j]);
+      }
+    }
+    if (t == 0) {
+      Meta nm;
+      nm.off_a = slot;
+      nm.off_f = 0;
+      nm.gamma = 1.0f;
+      nm.packed = meta_pack(0, 0, 0, flags | FLAG_DENSE);
+      a.meta[s] = nm;
+      a.dense_ids[slot] = s;
+      if (!a.csr_off)
+        __hip_atomic_fetch_add(&a.counters[C_PROMOTIONS], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// Pool creation: place the CSR components of every state into its slice of
+// the group's first segments, or queue it for the dense region.
+__global__ __launch_bounds__(256) void k_scatter(ScatterArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t s = (int64_t)blockIdx.x * 4 + uniform(threadIdx.x >> 6);
+  if (s >= a.N) return;
+  const int64_t o0 = a.csr_off[s], o1 = a.csr_off[s + 1];
+  const int R = (int)(o1 - o0);
+  const uint32_t flags = a.rule[s] ? FLAG_DELTA : 0u;
+  if (a.force_dense || R > a.L) {
+    if (lane == 0) {
+      const uint32_t idx =
+          __hip_atomic_fetch_add(&a.counters[C_PROMOTE_COUNT], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      a.dense_list[idx] = (int32_t)s;
+      Meta nm;
+      nm.off_a = -1;
+      nm.off_f = -1;
+      nm.gamma = 1.0f;
+      nm.packed = meta_pack(0, 0, 0, flags);
+      a.meta[s] = nm;
+    }
+    return;
+  }
+  const int g = a.group_of_state[s];
+  const int64_t mi = a.member_index[s];
+  const int64_t dst_a = a.base_a[g] + mi * a.r, dst_f = a.base_f[g] + mi * a.fcap;
+  const int ra = R < a.r ? R : a.r, rf = R - ra;
+  const int dk = a.dk, dv = a.dv;
+  for (int c = 0; c < R; ++c) {
+    const float *su = a.csr_u + (o0 + c) * dk, *sv = a.csr_v + (o0 + c) * dv;
+    const bool isa = c < ra;
+    float *du = isa ? a.act.u + (dst_a + c) * dk : a.frz.u + (dst_f + c - ra) * dk;
+    float *dvv = isa ? a.act.v + (dst_a + c) * dv : a.frz.v + (dst_f + c - ra) * dv;
+    copy_comp(su, sv, du, dvv, dk, dv, lane);
+    if (lane == 0) (isa ? a.act.s[dst_a + c] : a.frz.s[dst_f + c - ra]) = a.csr_s[o0 + c];
+  }
+  if (lane == 0) {
+    Meta nm;
+    nm.off_a = (int32_t)dst_a;
+    nm.off_f = (int32_t)dst_f;
+    nm.gamma = 1.0f;
+    nm.packed = meta_pack(ra, rf, 0, flags);
+    a.meta[s] = nm;
+  }
+}
+
+__global__ void k_zero_u32(uint32_t *p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+template <int NR>
+hipError_t materialize_nr(const MaterializeArgs &a, unsigned grid, hipStream_t st) {
+  const size_t sh = sizeof(float) * (size_t)kMatCH * (a.dk + a.dv + 1);
+  hipLaunchKernelGGL((k_materialize<NR>), dim3(grid), dim3(256), sh, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int dense_rows_per_thread(int dk, int dv);
+
+hipError_t launch_compact(const CompactArgs &a, hipStream_t st) {
+  if (a.n_members <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((a.n_members + 3) / 4)), block(256);
+  const int d = a.dk > a.dv ? a.dk : a.dv;
+  if (d <= 64) hipLaunchKernelGGL((k_compact<1>), grid, block, 0, st, a);
+  else if (d <= 128) hipLaunchKernelGGL((k_compact<2>), grid, block, 0, st, a);
+  else if (d <= 256) hipLaunchKernelGGL((k_compact<4>), grid, block, 0, st, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_materialize(const MaterializeArgs &a, int64_t grid_upper, hipStream_t st) {
+  if (grid_upper <= 0) return hipSuccess;
+  const unsigned grid = (unsigned)(grid_upper < 2048 ? grid_upper : 2048);
+  const int nr = dense_rows_per_thread(a.dk, a.dv);
+  if (nr <= 1) return materialize_nr<1>(a, grid, st);
+  if (nr <= 2) return materialize_nr<2>(a, grid, st);
+  if (nr <= 4) return materialize_nr<4>(a, grid, st);
+  if (nr <= 8) return materialize_nr<8>(a, grid, st);
+  if (nr <= 12) return materialize_nr<12>(a, grid, st);
+  if (nr <= 16) return materialize_nr<16>(a, grid, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_scatter(const ScatterArgs &a, hipStream_t st) {
+  if (a.N <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_scatter, dim3((unsigned)((a.N + 3) / 4)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_u32(uint32_t *p, int n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
+
+}  // namespace ss

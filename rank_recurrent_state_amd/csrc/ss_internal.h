@@ -1,0 +1,153 @@
+// ss_internal.h -- device-side layout and kernel launchers shared by the
+// HIP sources of libsinkstate.so (not part of the public ABI).
+//
+// Layout in HBM (SinkState, 4.4 "Memory layout": buffer apart from the
+// factors, active and frozen parts in separate contiguous regions, offsets
+// per state, a separate dense region):
+//   meta   [N]                16-byte record per state (offsets, Gamma, counts)
+//   active arena              components: u [cap][d_k], v [cap][d_v], sigma [cap]
+//   frozen arena              same shape, separate allocation
+//   pad    [N][K]             k [N][K][d_k], w [N][K][d_v], c [N][K] (c = 1/Gamma at insertion)
+//   dense  [cap_d][d_k][d_v]  row-major states of the dense region, ids [cap_d]
+// Each compaction group owns two segments in each arena; a compaction reads
+// the group's current segment and writes the other one.  A state's slice of
+// a segment starts at (segment base + its index within the group * per-state
+// capacity); the record holds the start of the live components.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ss {
+
+constexpr uint32_t FLAG_DELTA = 1u;
+constexpr uint32_t FLAG_DENSE = 2u;
+constexpr int kMaxM = 16;      // r + K
+constexpr int kAcctSlots = 256;
+// accounting arrays, kAcctSlots entries each
+enum Acct : int { A_DECODE_FACTORED = 0, A_DECODE_DENSE = 1, A_COMPACT_FLOPS = 2, A_COMPACT_STATES = 3, A_N = 4 };
+
+// 16-byte per-state record.  packed: ra | rf << 8 | n << 16 | flags << 24.
+struct __attribute__((aligned(16))) Meta {
+  int32_t off_a;   // factored: first active component; dense: dense slot
+  int32_t off_f;   // first frozen component
+  float gamma;     // decay accumulated since the last compaction
+  uint32_t packed;
+};
+
+__host__ __device__ inline uint32_t meta_ra(uint32_t p) { return p & 0xffu; }
+__host__ __device__ inline uint32_t meta_rf(uint32_t p) { return (p >> 8) & 0xffu; }
+__host__ __device__ inline uint32_t meta_n(uint32_t p) { return (p >> 16) & 0xffu; }
+__host__ __device__ inline uint32_t meta_flags(uint32_t p) { return p >> 24; }
+__host__ __device__ inline uint32_t meta_pack(uint32_t ra, uint32_t rf, uint32_t n, uint32_t flags) {
+  return (ra & 0xffu) | ((rf & 0xffu) << 8) | ((n & 0xffu) << 16) | (flags << 24);
+}
+
+// Device-side counters (uint32 unless noted).
+enum Counter : int {
+  C_DENSE_COUNT = 0,   // dense slots in use
+  C_PROMOTE_COUNT = 1, // states queued for promotion by the running compaction
+  C_ERR_PAD = 2,       // decode found a full pad (also raised on a host-mapped flag)
+  C_ERR_DENSE_CAP = 3, // promotion found the dense region full (also host-mapped)
+  C_CAP_TRUNC = 4,     // frozen components dropped because max_frozen was reached
+  C_PROMOTIONS = 5,    // total promotions
+  C_N = 8
+};
+
+struct Arena {
+  float *u, *v, *s;
+};
+
+struct DecodeArgs {
+  int64_t N;
+  int dk, dv, K;
+  Meta *meta;
+  Arena act, frz;
+  float *pk, *pw, *pc;
+  const float *q, *k, *v, *alpha, *beta;
+  float *o;
+  uint32_t *counters;
+  unsigned long long *acct;   // [kAcctSlots] algorithmic bytes
+  uint32_t *hflag;            // host-mapped flag raised when a pad is found full
+};
+
+struct DenseArgs {
+  int dk, dv;
+  uint32_t cap_d;
+  Meta *meta;
+  float *dense;
+  const int32_t *dense_ids;
+  const float *q, *k, *v, *alpha, *beta;
+  float *o;
+  uint32_t *counters;
+  unsigned long long *acct;
+};
+
+struct CompactArgs {
+  int dk, dv, K, r, L, promote, fcap;
+  int32_t n_members;
+  const int32_t *members;      // state ids of the group, in member order
+  const float *eps;
+  Meta *meta;
+  Arena act, frz;              // arenas (segments addressed through bases)
+  int64_t src_base_a, dst_base_a, src_base_f, dst_base_f;   // segment bases (components); src only informative
+  float *pk, *pw, *pc;
+  int32_t *promote_list;
+  uint32_t *counters;
+  unsigned long long *acct_flops;
+  unsigned long long *acct_states;
+};
+
+struct MaterializeArgs {
+  int dk, dv, cap_d;
+  const int32_t *list;         // state ids
+  const uint32_t *count;       // number of entries in list (device)
+  int32_t fixed_count;         // used when count == nullptr
+  Meta *meta;
+  const Meta *src_meta;        // where the components are (meta after compaction), or nullptr
+  const int64_t *csr_off;      // alternative source: CSR offsets per state (init)
+  const float *csr_u, *csr_v, *csr_s;
+  Arena act, frz;
+  float *dense;
+  int32_t *dense_ids;
+  uint32_t *counters;
+  uint32_t *hflag;             // host-mapped flag raised when the dense region is full
+};
+
+struct ScatterArgs {
+  int64_t N;
+  int dk, dv, r, L, fcap, force_dense;
+  const int64_t *csr_off;
+  const float *csr_u, *csr_v, *csr_s;
+  const int32_t *member_index;   // index of each state within its group
+  const int32_t *group_of_state;
+  const int64_t *base_a, *base_f;  // per group: segment base (components) for parity 0
+  const uint8_t *rule;
+  Meta *meta;
+  Arena act, frz;
+  int32_t *dense_list;           // states to materialize
+  uint32_t *counters;            // uses C_PROMOTE_COUNT as the list length
+};
+
+// launchers (return hipError_t of the launch)
+hipError_t launch_decode_factored(const DecodeArgs &a, bool readonly, bool any_delta, hipStream_t st);
+hipError_t launch_decode_dense(const DenseArgs &a, int64_t grid_upper, bool readonly, hipStream_t st);
+hipError_t launch_compact(const CompactArgs &a, hipStream_t st);
+hipError_t launch_materialize(const MaterializeArgs &a, int64_t grid_upper, hipStream_t st);
+hipError_t launch_scatter(const ScatterArgs &a, hipStream_t st);
+hipError_t launch_zero_u32(uint32_t *p, int n, hipStream_t st);
+
+// algorithmic bytes of one decode step of one state (kept identical to the
+// in-kernel accounting)
+__host__ __device__ inline unsigned long long decode_bytes(int dk, int dv, int ncomp, int npad, bool delta,
+                                                           bool dense) {
+  unsigned long long in = 4ull * (2ull * dk + dv + 1 + (delta ? 1 : 0));
+  if (dense) {
+    // record + slot id, state read and written, inputs, output
+    return 16ull + 4ull + 8ull * (unsigned long long)dk * dv + in + 4ull * dv;
+  }
+  unsigned long long comp = 4ull * (unsigned long long)(dk + dv + 1);
+  // record read+write, components and pad slots read, inputs, one slot written, output
+  return 32ull + comp * (unsigned long long)(ncomp + npad) + in + comp + 4ull * dv;
+}
+
+}  // namespace ss

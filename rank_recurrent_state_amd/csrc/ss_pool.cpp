@@ -1,0 +1,650 @@
+// ss_pool.cpp -- host side of libsinkstate.so: argument checks, pool layout
+// and device allocation, launch orchestration, export and statistics.
+//
+// Pool layout (SinkState 4.4 "Memory layout"): the states are listed by
+// compaction group; group g with n_g states owns, in each of the active and
+// frozen arenas, two segments of n_g * cap components (cap = r for the
+// active arena; L + K - r, or max_frozen when promotion is off, for the
+// frozen arena).  A compaction of g reads its current segment and writes the
+// other one, so the group's storage is rewritten to fit the new ranks and the
+// per-state offsets in the 16-byte records are updated; nothing is ever
+// written in place while it may still be read.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/sinkstate.h"
+#include "ss_internal.h"
+
+namespace ss {
+int dense_rows_per_thread(int dk, int dv);
+}
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ss_status fail(ss_status st, const std::string &msg) {
+  g_last_error = msg;
+  return st;
+}
+
+enum HostFlag { HF_PAD = 0, HF_DENSE_CAP = 1, HF_N = 4 };
+
+}  // namespace
+
+struct ss_pool {
+  int64_t N = 0;
+  int dk = 0, dv = 0, K = 0, r = 0, L = 0, promote = 0, force_dense = 0, fcap = 0, G = 0;
+  bool any_delta = false;
+  std::vector<int32_t> group_offset;
+  std::vector<int64_t> group_start, group_size;
+  std::vector<int> parity;
+  int64_t cap_d = 0;
+  int64_t dense_upper = 0;
+  // device memory
+  ss::Meta *meta = nullptr;
+  int32_t *members = nullptr;
+  float *eps = nullptr;
+  ss::Arena act{nullptr, nullptr, nullptr}, frz{nullptr, nullptr, nullptr};
+  float *pk = nullptr, *pw = nullptr, *pc = nullptr;
+  float *dense = nullptr;
+  int32_t *dense_ids = nullptr;
+  int32_t *promote_list = nullptr;
+  uint32_t *counters = nullptr;
+  unsigned long long *acct = nullptr;  // [A_N][kAcctSlots] accounting (see ss::Acct)
+  uint32_t *hflags = nullptr;          // host-mapped error flags
+  uint32_t *hflags_dev = nullptr;
+  std::vector<void *> dev_allocs;
+  int64_t reserved = 0;
+  int64_t decode_calls = 0, compact_calls = 0, readout_calls = 0;
+  ss_status sticky = SS_OK;
+  std::string sticky_msg;
+  // measurement hook: event pairs around kernel launches
+  struct EvPair {
+    hipEvent_t a, b;
+    int kernel;
+  };
+  bool timing = false;
+  std::vector<EvPair> pending;
+  std::vector<hipEvent_t> spare;
+  double kernel_ms[SS_KERNEL_COUNT] = {0};
+  int64_t kernel_launches[SS_KERNEL_COUNT] = {0};
+
+  int64_t base_a(int g, int p) const { return 2 * r * group_start[g] + (int64_t)p * r * group_size[g]; }
+  int64_t base_f(int g, int p) const { return 2 * (int64_t)fcap * group_start[g] + (int64_t)p * fcap * group_size[g]; }
+};
+
+namespace {
+
+template <typename T>
+hipError_t dalloc(ss_pool *p, T **ptr, size_t count) {
+  *ptr = nullptr;
+  if (count == 0) return hipSuccess;
+  void *q = nullptr;
+  hipError_t e = hipMalloc(&q, count * sizeof(T));
+  if (e != hipSuccess) return e;
+  p->dev_allocs.push_back(q);
+  p->reserved += (int64_t)(count * sizeof(T));
+  *ptr = static_cast<T *>(q);
+  return hipSuccess;
+}
+
+void free_all(ss_pool *p) {
+  for (auto &e : p->pending) {
+    (void)hipEventDestroy(e.a);
+    (void)hipEventDestroy(e.b);
+  }
+  p->pending.clear();
+  for (hipEvent_t e : p->spare) (void)hipEventDestroy(e);
+  p->spare.clear();
+  for (void *q : p->dev_allocs) (void)hipFree(q);
+  p->dev_allocs.clear();
+  if (p->hflags) (void)hipHostFree(p->hflags);
+  p->hflags = nullptr;
+}
+
+hipError_t take_event(ss_pool *p, hipEvent_t *e) {
+  if (!p->spare.empty()) {
+    *e = p->spare.back();
+    p->spare.pop_back();
+    return hipSuccess;
+  }
+  return hipEventCreate(e);
+}
+
+// launch through `fn`, bracketed by events on `st` while timing is on
+template <typename F>
+hipError_t timed(ss_pool *p, int kernel, hipStream_t st, F fn) {
+  if (!p->timing) return fn();
+  ss_pool::EvPair ev{nullptr, nullptr, kernel};
+  hipError_t e = take_event(p, &ev.a);
+  if (e == hipSuccess) e = take_event(p, &ev.b);
+  if (e == hipSuccess) e = hipEventRecord(ev.a, st);
+  if (e != hipSuccess) return e;
+  e = fn();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(ev.b, st);
+  if (e == hipSuccess) p->pending.push_back(ev);
+  return e;
+}
+
+ss_status hip_fail(hipError_t e, const char *what) {
+  return fail(SS_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// check the host-visible error flags that kernels raise
+ss_status poll(ss_pool *p) {
+  if (p->sticky != SS_OK) return fail(p->sticky, p->sticky_msg);
+  if (p->hflags) {
+    const volatile uint32_t *f = p->hflags;
+    if (f[HF_PAD]) {
+      p->sticky = SS_ERR_STATE;
+      p->sticky_msg = "decode_step found a full pad: a compaction of the state's group was skipped";
+    } else if (f[HF_DENSE_CAP]) {
+      p->sticky = SS_ERR_CAPACITY;
+      p->sticky_msg = "the dense region is full; raise dense_capacity";
+    }
+  }
+  if (p->sticky != SS_OK) return fail(p->sticky, p->sticky_msg);
+  return SS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ss_dense_rank_limit(int32_t d_k, int32_t d_v) {
+  if (d_k <= 0 || d_v <= 0) return 0;
+  return (int32_t)(((int64_t)d_k * d_v) / ((int64_t)d_k + d_v));
+}
+
+uint64_t ss_decode_bytes_per_state(int32_t d_k, int32_t d_v, int32_t n_comp, int32_t n_pad, int32_t rule,
+                                   int32_t dense) {
+  return ss::decode_bytes(d_k, d_v, n_comp, n_pad, rule == SS_RULE_DELTA, dense != 0);
+}
+
+const char *ss_status_string(ss_status st) {
+  switch (st) {
+    case SS_OK: return "ok";
+    case SS_ERR_ARG: return "invalid argument";
+    case SS_ERR_SHAPE: return "unsupported shape";
+    case SS_ERR_OOM: return "out of memory";
+    case SS_ERR_CAPACITY: return "capacity exhausted";
+    case SS_ERR_HIP: return "HIP runtime error";
+    case SS_ERR_STATE: return "pool poisoned by an earlier failure";
+  }
+  return "unknown status";
+}
+
+const char *ss_last_error(void) { return g_last_error.c_str(); }
+
+ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipStream_t stream, ss_pool **out) {
+  if (!out) return fail(SS_ERR_ARG, "out is NULL");
+  *out = nullptr;
+  if (!d) return fail(SS_ERR_ARG, "desc is NULL");
+  const int64_t N = d->n_states;
+  if (N < 1) return fail(SS_ERR_ARG, "n_states must be >= 1");
+  if (d->d_k < 4 || d->d_v < 4 || d->d_k > 256 || d->d_v > 256 || (d->d_k & 3) || (d->d_v & 3))
+    return fail(SS_ERR_SHAPE, "d_k and d_v must be multiples of 4 in [4, 256]");
+  if (d->pad_slots < 1 || d->pad_slots > 8) return fail(SS_ERR_SHAPE, "pad_slots must be in [1, 8]");
+  if (d->r_active < 1 || d->r_active > 8) return fail(SS_ERR_SHAPE, "r_active must be in [1, 8]");
+  if (d->r_active + d->pad_slots > ss::kMaxM) return fail(SS_ERR_SHAPE, "r_active + pad_slots must be <= 16");
+  if (ss::dense_rows_per_thread(d->d_k, d->d_v) > 16)
+    return fail(SS_ERR_SHAPE, "dense region: d_k / floor(1024 / d_v) rows per thread must be <= 16");
+  if (d->n_groups < 1) return fail(SS_ERR_ARG, "n_groups must be >= 1");
+  if (d->max_frozen < 0 || d->max_frozen > 255) return fail(SS_ERR_ARG, "max_frozen must be in [0, 255]");
+  if (d->dense_capacity < 0 || d->dense_capacity > N) return fail(SS_ERR_ARG, "dense_capacity must be in [0, N]");
+  const int dk = d->d_k, dv = d->d_v, K = d->pad_slots, r = d->r_active, G = d->n_groups;
+  const int L = d->dense_rank_limit < 0 ? ss_dense_rank_limit(dk, dv) : d->dense_rank_limit;
+  if (L > 255 + r) return fail(SS_ERR_ARG, "dense_rank_limit too large (frozen part is limited to 255)");
+  const int promote = d->promote_on_compact ? 1 : 0;
+  int fcap = promote ? std::max(1, std::min(255, L + K - r)) : (d->max_frozen ? d->max_frozen : 255);
+  if (d->group_offset)
+    for (int g = 0; g < G; ++g)
+      if (d->group_offset[g] < 0 || d->group_offset[g] >= K) return fail(SS_ERR_ARG, "group_offset out of [0, K)");
+  std::vector<int32_t> grp(N, 0);
+  if (d->group_of_state) {
+    for (int64_t s = 0; s < N; ++s) {
+      if (d->group_of_state[s] < 0 || d->group_of_state[s] >= G) return fail(SS_ERR_ARG, "group_of_state out of range");
+      grp[s] = d->group_of_state[s];
+    }
+  }
+  bool any_delta = false;
+  if (d->rule)
+    for (int64_t s = 0; s < N; ++s) {
+      if (d->rule[s] > 1) return fail(SS_ERR_ARG, "rule must be 0 (scalar) or 1 (delta)");
+      any_delta |= d->rule[s] == 1;
+    }
+  if (d->eps) {
+    for (int64_t s = 0; s < N; ++s)
+      if (!(d->eps[s] >= 0.f) || !std::isfinite(d->eps[s])) return fail(SS_ERR_ARG, "eps must be finite and >= 0");
+  } else if (!(d->eps_default >= 0.f) || !std::isfinite(d->eps_default)) {
+    return fail(SS_ERR_ARG, "eps_default must be finite and >= 0");
+  }
+  // initial components
+  const int64_t *off = (init && init->comp_off) ? init->comp_off : nullptr;
+  int64_t total = 0, n_dense0 = 0;
+  if (off) {
+    if (off[0] != 0) return fail(SS_ERR_ARG, "comp_off[0] must be 0");
+    for (int64_t s = 0; s < N; ++s) {
+      const int64_t R = off[s + 1] - off[s];
+      if (R < 0) return fail(SS_ERR_ARG, "comp_off must be non-decreasing");
+      if (!d->force_dense && R <= L && R - std::min<int64_t>(R, r) > fcap)
+        return fail(SS_ERR_CAPACITY, "initial frozen part exceeds max_frozen");
+      if (d->force_dense || R > L) ++n_dense0;
+    }
+    total = off[N];
+    if (total > 0 && (!init->u || !init->v || !init->sigma)) return fail(SS_ERR_ARG, "u, v and sigma are required");
+    for (int64_t s = 0; s < N; ++s)
+      for (int64_t c = off[s] + 1; c < off[s + 1]; ++c)
+        if (!(init->sigma[c] <= init->sigma[c - 1])) return fail(SS_ERR_ARG, "sigma must be sorted descending per state");
+    for (int64_t c = 0; c < total; ++c)
+      if (!std::isfinite(init->sigma[c]) || init->sigma[c] < 0.f) return fail(SS_ERR_ARG, "sigma must be finite, >= 0");
+  } else if (d->force_dense) {
+    n_dense0 = N;
+  }
+  const int64_t cap_d = d->force_dense ? N : (d->dense_capacity ? d->dense_capacity : N);
+  if (n_dense0 > cap_d) return fail(SS_ERR_CAPACITY, "more initial dense states than dense_capacity");
+  const bool factored = !d->force_dense;
+  if (factored && (2 * (int64_t)fcap * N >= (int64_t)INT32_MAX || 2 * (int64_t)r * N >= (int64_t)INT32_MAX))
+    return fail(SS_ERR_CAPACITY, "too many states for 32-bit component offsets");
+
+  ss_pool *p = new (std::nothrow) ss_pool();
+  if (!p) return fail(SS_ERR_OOM, "host allocation failed");
+  p->N = N; p->dk = dk; p->dv = dv; p->K = K; p->r = r; p->L = L; p->promote = promote;
+  p->force_dense = d->force_dense ? 1 : 0; p->fcap = fcap; p->G = G; p->any_delta = any_delta; p->cap_d = cap_d;
+  p->group_offset.assign(G, 0);
+  if (d->group_offset) for (int g = 0; g < G; ++g) p->group_offset[g] = d->group_offset[g];
+  p->group_size.assign(G, 0);
+  p->group_start.assign(G, 0);
+  p->parity.assign(G, 0);
+  for (int64_t s = 0; s < N; ++s) p->group_size[grp[s]]++;
+  for (int g = 1; g < G; ++g) p->group_start[g] = p->group_start[g - 1] + p->group_size[g - 1];
+  std::vector<int32_t> members(N), member_index(N);
+  {
+    std::vector<int64_t> fill(p->group_start);
+    for (int64_t s = 0; s < N; ++s) {
+      const int64_t i = fill[grp[s]]++;
+      members[i] = (int32_t)s;
+      member_index[s] = (int32_t)(i - p->group_start[grp[s]]);
+    }
+  }
+  std::vector<int64_t> base_a(G), base_f(G);
+  for (int g = 0; g < G; ++g) {
+    base_a[g] = p->base_a(g, 0);
+    base_f[g] = p->base_f(g, 0);
+  }
+  std::vector<float> epsv(N);
+  for (int64_t s = 0; s < N; ++s) epsv[s] = d->eps ? d->eps[s] : d->eps_default;
+  std::vector<uint8_t> rulev(N, 0);
+  if (d->rule) std::memcpy(rulev.data(), d->rule, N);
+
+  // device allocations
+  const int64_t cap_a = factored ? 2 * r * N : 0, cap_f = factored ? 2 * (int64_t)fcap * N : 0;
+  hipError_t e = hipSuccess;
+  auto chk = [&](hipError_t x) { if (e == hipSuccess) e = x; };
+  chk(dalloc(p, &p->meta, N));
+  chk(dalloc(p, &p->members, N));
+  chk(dalloc(p, &p->eps, N));
+  chk(dalloc(p, &p->act.u, cap_a * dk));
+  chk(dalloc(p, &p->act.v, cap_a * dv));
+  chk(dalloc(p, &p->act.s, cap_a));
+  chk(dalloc(p, &p->frz.u, cap_f * dk));
+  chk(dalloc(p, &p->frz.v, cap_f * dv));
+  chk(dalloc(p, &p->frz.s, cap_f));
+  if (factored) {
+    chk(dalloc(p, &p->pk, (size_t)N * K * dk));
+    chk(dalloc(p, &p->pw, (size_t)N * K * dv));
+    chk(dalloc(p, &p->pc, (size_t)N * K));
+    chk(dalloc(p, &p->promote_list, N));
+  }
+  chk(dalloc(p, &p->dense, (size_t)cap_d * dk * dv));
+  chk(dalloc(p, &p->dense_ids, cap_d));
+  chk(dalloc(p, &p->counters, ss::C_N));
+  chk(dalloc(p, &p->acct, ss::A_N * ss::kAcctSlots));
+  if (e == hipSuccess) {
+    void *h = nullptr;
+    e = hipHostMalloc(&h, HF_N * sizeof(uint32_t), hipHostMallocMapped | hipHostMallocCoherent);
+    if (e == hipSuccess) {
+      p->hflags = static_cast<uint32_t *>(h);
+      std::memset(p->hflags, 0, HF_N * sizeof(uint32_t));
+      void *dp = nullptr;
+      e = hipHostGetDevicePointer(&dp, h, 0);
+      p->hflags_dev = static_cast<uint32_t *>(dp);
+    }
+  }
+  if (e != hipSuccess) {
+    const bool oom = e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation;
+    free_all(p);
+    delete p;
+    return oom ? fail(SS_ERR_OOM, "device allocation failed") : hip_fail(e, "allocation");
+  }
+  // temporaries for the initial upload
+  int64_t *d_off = nullptr;
+  float *d_u = nullptr, *d_v = nullptr, *d_s = nullptr;
+  int32_t *d_midx = nullptr, *d_grp = nullptr, *d_dlist = nullptr;
+  int64_t *d_ba = nullptr, *d_bf = nullptr;
+  uint8_t *d_rule = nullptr;
+  std::vector<void *> tmp;
+  auto talloc = [&](void **q, size_t bytes) {
+    if (e != hipSuccess || bytes == 0) return;
+    e = hipMalloc(q, bytes);
+    if (e == hipSuccess) tmp.push_back(*q);
+  };
+  std::vector<int64_t> zero_off;
+  if (!off) zero_off.assign(N + 1, 0);
+  const int64_t *offp = off ? off : zero_off.data();
+  talloc((void **)&d_off, (N + 1) * sizeof(int64_t));
+  talloc((void **)&d_u, total * dk * sizeof(float));
+  talloc((void **)&d_v, total * dv * sizeof(float));
+  talloc((void **)&d_s, total * sizeof(float));
+  talloc((void **)&d_midx, N * sizeof(int32_t));
+  talloc((void **)&d_grp, N * sizeof(int32_t));
+  talloc((void **)&d_dlist, N * sizeof(int32_t));
+  talloc((void **)&d_ba, G * sizeof(int64_t));
+  talloc((void **)&d_bf, G * sizeof(int64_t));
+  talloc((void **)&d_rule, N);
+  auto up = [&](void *dst, const void *src, size_t bytes) {
+    if (e == hipSuccess && bytes) e = hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, stream);
+  };
+  up(d_off, offp, (N + 1) * sizeof(int64_t));
+  if (total) {
+    up(d_u, init->u, total * dk * sizeof(float));
+    up(d_v, init->v, total * dv * sizeof(float));
+    up(d_s, init->sigma, total * sizeof(float));
+  }
+  up(d_midx, member_index.data(), N * sizeof(int32_t));
+  up(d_grp, grp.data(), N * sizeof(int32_t));
+  up(d_ba, base_a.data(), G * sizeof(int64_t));
+  up(d_bf, base_f.data(), G * sizeof(int64_t));
+  up(d_rule, rulev.data(), N);
+  up(p->members, members.data(), N * sizeof(int32_t));
+  up(p->eps, epsv.data(), N * sizeof(float));
+  if (e == hipSuccess) e = hipMemsetAsync(p->counters, 0, ss::C_N * sizeof(uint32_t), stream);
+  if (e == hipSuccess) e = hipMemsetAsync(p->acct, 0, ss::A_N * ss::kAcctSlots * sizeof(unsigned long long), stream);
+  if (e == hipSuccess) {
+    ss::ScatterArgs sa{};
+    sa.N = N; sa.dk = dk; sa.dv = dv; sa.r = r; sa.L = L; sa.fcap = fcap; sa.force_dense = p->force_dense;
+    sa.csr_off = d_off; sa.csr_u = d_u; sa.csr_v = d_v; sa.csr_s = d_s;
+    sa.member_index = d_midx; sa.group_of_state = d_grp; sa.base_a = d_ba; sa.base_f = d_bf; sa.rule = d_rule;
+    sa.meta = p->meta; sa.act = p->act; sa.frz = p->frz; sa.dense_list = d_dlist; sa.counters = p->counters;
+    e = ss::launch_scatter(sa, stream);
+  }
+  if (e == hipSuccess && n_dense0 > 0) {
+    ss::MaterializeArgs ma{};
+    ma.dk = dk; ma.dv = dv; ma.cap_d = (int)cap_d; ma.list = d_dlist; ma.count = p->counters + ss::C_PROMOTE_COUNT;
+    ma.meta = p->meta; ma.csr_off = d_off; ma.csr_u = d_u; ma.csr_v = d_v; ma.csr_s = d_s;
+    ma.act = p->act; ma.frz = p->frz; ma.dense = p->dense; ma.dense_ids = p->dense_ids; ma.counters = p->counters;
+    ma.hflag = p->hflags_dev + HF_DENSE_CAP;
+    e = ss::launch_materialize(ma, n_dense0, stream);
+  }
+  if (e == hipSuccess) e = ss::launch_zero_u32(p->counters + ss::C_PROMOTE_COUNT, 1, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  for (void *q : tmp) (void)hipFree(q);
+  if (e != hipSuccess) {
+    free_all(p);
+    delete p;
+    return hip_fail(e, "pool upload");
+  }
+  p->dense_upper = n_dense0;
+  *out = p;
+  return SS_OK;
+}
+
+ss_status ss_state_pool_destroy(ss_pool *p) {
+  if (!p) return SS_OK;
+  (void)hipDeviceSynchronize();
+  free_all(p);
+  delete p;
+  return SS_OK;
+}
+
+static ss_status run_decode(ss_pool *p, const float *q, const float *k, const float *v, const float *alpha,
+                            const float *beta, float *o, bool readonly, hipStream_t stream) {
+  if (!p) return fail(SS_ERR_ARG, "pool is NULL");
+  ss_status st = poll(p);
+  if (st != SS_OK) return st;
+  if (!q || !o) return fail(SS_ERR_ARG, "q and o are required");
+  if (!readonly && (!k || !v || !alpha)) return fail(SS_ERR_ARG, "k, v and alpha are required");
+  if (!readonly && p->any_delta && !beta) return fail(SS_ERR_ARG, "beta is required: the pool has delta-rule states");
+  hipError_t e = hipSuccess;
+  if (!p->force_dense) {
+    ss::DecodeArgs a{};
+    a.N = p->N; a.dk = p->dk; a.dv = p->dv; a.K = p->K; a.meta = p->meta; a.act = p->act; a.frz = p->frz;
+    a.pk = p->pk; a.pw = p->pw; a.pc = p->pc; a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.o = o;
+    a.counters = p->counters; a.acct = p->acct + ss::A_DECODE_FACTORED * ss::kAcctSlots;
+    a.hflag = p->hflags_dev + HF_PAD;
+    e = timed(p, readonly ? SS_KERNEL_READOUT_FACTORED : SS_KERNEL_DECODE_FACTORED, stream,
+              [&] { return ss::launch_decode_factored(a, readonly, p->any_delta, stream); });
+    if (e != hipSuccess) return hip_fail(e, "decode (factored) launch");
+  }
+  if (p->dense_upper > 0) {
+    ss::DenseArgs a{};
+    a.dk = p->dk; a.dv = p->dv; a.cap_d = (uint32_t)p->cap_d; a.meta = p->meta; a.dense = p->dense;
+    a.dense_ids = p->dense_ids; a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.o = o;
+    a.counters = p->counters; a.acct = p->acct + ss::A_DECODE_DENSE * ss::kAcctSlots;
+    e = timed(p, readonly ? SS_KERNEL_READOUT_DENSE : SS_KERNEL_DECODE_DENSE, stream,
+              [&] { return ss::launch_decode_dense(a, p->dense_upper, readonly, stream); });
+    if (e != hipSuccess) return hip_fail(e, "decode (dense) launch");
+  }
+  return SS_OK;
+}
+
+ss_status ss_decode_step(ss_pool *p, const float *q, const float *k, const float *v, const float *alpha,
+                         const float *beta, float *o, hipStream_t stream) {
+  ss_status st = run_decode(p, q, k, v, alpha, beta, o, false, stream);
+  if (st == SS_OK) p->decode_calls++;
+  return st;
+}
+
+ss_status ss_readout(ss_pool *p, const float *q, float *o, hipStream_t stream) {
+  ss_status st = run_decode(p, q, nullptr, nullptr, nullptr, nullptr, o, true, stream);
+  if (st == SS_OK) p->readout_calls++;
+  return st;
+}
+
+ss_status ss_compact(ss_pool *p, int32_t group, hipStream_t stream) {
+  if (!p) return fail(SS_ERR_ARG, "pool is NULL");
+  ss_status st = poll(p);
+  if (st != SS_OK) return st;
+  if (group >= p->G) return fail(SS_ERR_ARG, "group out of range");
+  if (p->force_dense) return SS_OK;  // dense states have no pad to compact
+  const int g0 = group < 0 ? 0 : group, g1 = group < 0 ? p->G : group + 1;
+  for (int g = g0; g < g1; ++g) {
+    if (p->group_size[g] == 0) continue;
+    hipError_t e = ss::launch_zero_u32(p->counters + ss::C_PROMOTE_COUNT, 1, stream);
+    if (e != hipSuccess) return hip_fail(e, "compact launch");
+    const int src = p->parity[g], dst = 1 - src;
+    ss::CompactArgs a{};
+    a.dk = p->dk; a.dv = p->dv; a.K = p->K; a.r = p->r; a.L = p->L; a.promote = p->promote; a.fcap = p->fcap;
+    a.n_members = (int32_t)p->group_size[g];
+    a.members = p->members + p->group_start[g];
+    a.eps = p->eps; a.meta = p->meta; a.act = p->act; a.frz = p->frz;
+    a.src_base_a = p->base_a(g, src); a.dst_base_a = p->base_a(g, dst);
+    a.src_base_f = p->base_f(g, src); a.dst_base_f = p->base_f(g, dst);
+    a.pk = p->pk; a.pw = p->pw; a.pc = p->pc; a.promote_list = p->promote_list; a.counters = p->counters;
+    a.acct_flops = p->acct + ss::A_COMPACT_FLOPS * ss::kAcctSlots;
+    a.acct_states = p->acct + ss::A_COMPACT_STATES * ss::kAcctSlots;
+    e = timed(p, SS_KERNEL_COMPACT, stream, [&] { return ss::launch_compact(a, stream); });
+    if (e != hipSuccess) return hip_fail(e, "compact launch");
+    if (p->promote) {
+      ss::MaterializeArgs ma{};
+      ma.dk = p->dk; ma.dv = p->dv; ma.cap_d = (int)p->cap_d; ma.list = p->promote_list;
+      ma.count = p->counters + ss::C_PROMOTE_COUNT; ma.meta = p->meta; ma.act = p->act; ma.frz = p->frz;
+      ma.dense = p->dense; ma.dense_ids = p->dense_ids; ma.counters = p->counters;
+      ma.hflag = p->hflags_dev + HF_DENSE_CAP;
+      const int64_t gsz = p->group_size[g];
+      e = timed(p, SS_KERNEL_MATERIALIZE, stream, [&] { return ss::launch_materialize(ma, gsz, stream); });
+      if (e != hipSuccess) return hip_fail(e, "promote launch");
+      p->dense_upper = std::min<int64_t>(p->cap_d, p->dense_upper + p->group_size[g]);
+    }
+    p->parity[g] = dst;
+  }
+  p->compact_calls++;
+  return SS_OK;
+}
+
+ss_status ss_schedule_due(const ss_pool *p, int64_t step, int32_t *out, int32_t cap, int32_t *n_due) {
+  if (!p || !n_due || (cap > 0 && !out) || cap < 0) return fail(SS_ERR_ARG, "bad arguments");
+  int32_t c = 0;
+  for (int g = 0; g < p->G; ++g) {
+    int64_t x = (step + p->group_offset[g]) % p->K;
+    if (x < 0) x += p->K;
+    if (x == 0) {
+      if (c < cap) out[c] = g;
+      ++c;
+    }
+  }
+  *n_due = c;
+  return c > cap ? fail(SS_ERR_CAPACITY, "out is too small") : SS_OK;
+}
+
+ss_status ss_state_export(ss_pool *p, const int64_t *ids, int64_t n, void *host_buf, size_t cap, size_t *needed,
+                          hipStream_t stream) {
+  if (!p || (n > 0 && !ids) || n < 0 || !needed) return fail(SS_ERR_ARG, "bad arguments");
+  for (int64_t i = 0; i < n; ++i)
+    if (ids[i] < 0 || ids[i] >= p->N) return fail(SS_ERR_ARG, "state id out of range");
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "export sync");
+  ss_status st = poll(p);
+  if (st != SS_OK) return st;
+  const int dk = p->dk, dv = p->dv, K = p->K;
+  std::vector<ss::Meta> metas(n);
+  for (int64_t i = 0; i < n; ++i) {
+    e = hipMemcpy(&metas[i], p->meta + ids[i], sizeof(ss::Meta), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "export meta");
+  }
+  size_t need = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    const uint32_t pk = metas[i].packed;
+    need += 8 * sizeof(int32_t);
+    if (ss::meta_flags(pk) & ss::FLAG_DENSE) {
+      need += sizeof(float) * (size_t)dk * dv;
+    } else {
+      const size_t R = ss::meta_ra(pk) + ss::meta_rf(pk), nn = ss::meta_n(pk);
+      need += sizeof(float) * (R * (1 + dk + dv) + nn * (1 + dk + dv));
+    }
+  }
+  *needed = need;
+  if (!host_buf || cap < need) return fail(SS_ERR_CAPACITY, "export buffer too small");
+  char *w = static_cast<char *>(host_buf);
+  for (int64_t i = 0; i < n; ++i) {
+    const ss::Meta m = metas[i];
+    const uint32_t pkd = m.packed;
+    const bool dense = ss::meta_flags(pkd) & ss::FLAG_DENSE;
+    const int ra = dense ? 0 : ss::meta_ra(pkd), rf = dense ? 0 : ss::meta_rf(pkd), nn = dense ? 0 : ss::meta_n(pkd);
+    int32_t hdr[8] = {(int32_t)ids[i], dense ? 1 : 0, ra + rf, ra, nn,
+                      (ss::meta_flags(pkd) & ss::FLAG_DELTA) ? 1 : 0, 0, 0};
+    std::memcpy(w, hdr, sizeof(hdr));
+    w += sizeof(hdr);
+    auto dl = [&](void *dst, const void *src, size_t bytes) {
+      if (e == hipSuccess && bytes) e = hipMemcpy(dst, src, bytes, hipMemcpyDeviceToHost);
+    };
+    if (dense) {
+      dl(w, p->dense + (size_t)m.off_a * dk * dv, sizeof(float) * (size_t)dk * dv);
+      w += sizeof(float) * (size_t)dk * dv;
+      continue;
+    }
+    const int R = ra + rf;
+    float *sig = reinterpret_cast<float *>(w);
+    float *u = sig + R;
+    float *v = u + (size_t)R * dk;
+    float *c = v + (size_t)R * dv;
+    float *kk = c + nn;
+    float *ww = kk + (size_t)nn * dk;
+    dl(sig, p->act.s + m.off_a, sizeof(float) * ra);
+    dl(sig + ra, p->frz.s + m.off_f, sizeof(float) * rf);
+    dl(u, p->act.u + (size_t)m.off_a * dk, sizeof(float) * (size_t)ra * dk);
+    dl(u + (size_t)ra * dk, p->frz.u + (size_t)m.off_f * dk, sizeof(float) * (size_t)rf * dk);
+    dl(v, p->act.v + (size_t)m.off_a * dv, sizeof(float) * (size_t)ra * dv);
+    dl(v + (size_t)ra * dv, p->frz.v + (size_t)m.off_f * dv, sizeof(float) * (size_t)rf * dv);
+    dl(c, p->pc + (size_t)ids[i] * K, sizeof(float) * nn);
+    dl(kk, p->pk + (size_t)ids[i] * K * dk, sizeof(float) * (size_t)nn * dk);
+    dl(ww, p->pw + (size_t)ids[i] * K * dv, sizeof(float) * (size_t)nn * dv);
+    if (e != hipSuccess) return hip_fail(e, "export copy");
+    for (int j = 0; j < R; ++j) sig[j] *= m.gamma;
+    for (int j = 0; j < nn; ++j) c[j] *= m.gamma;
+    w = reinterpret_cast<char *>(ww + (size_t)nn * dv);
+  }
+  if (e != hipSuccess) return hip_fail(e, "export copy");
+  return SS_OK;
+}
+
+ss_status ss_pool_stats(ss_pool *p, ss_stats *out, hipStream_t stream) {
+  if (!p || !out) return fail(SS_ERR_ARG, "bad arguments");
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "stats sync");
+  ss_status st = poll(p);
+  if (st != SS_OK) return st;
+  std::vector<ss::Meta> meta(p->N);
+  e = hipMemcpy(meta.data(), p->meta, sizeof(ss::Meta) * p->N, hipMemcpyDeviceToHost);
+  uint32_t ctr[ss::C_N];
+  if (e == hipSuccess) e = hipMemcpy(ctr, p->counters, sizeof(ctr), hipMemcpyDeviceToHost);
+  std::vector<unsigned long long> acct(ss::A_N * ss::kAcctSlots);
+  if (e == hipSuccess) e = hipMemcpy(acct.data(), p->acct, acct.size() * sizeof(unsigned long long), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "stats copy");
+  std::memset(out, 0, sizeof(*out));
+  out->n_states = p->N;
+  const int64_t comp = 4ll * (p->dk + p->dv + 1);
+  int64_t live = 16ll * p->N;
+  for (int64_t s = 0; s < p->N; ++s) {
+    const uint32_t pk = meta[s].packed;
+    if (ss::meta_flags(pk) & ss::FLAG_DENSE) {
+      out->n_dense++;
+      live += 4ll * p->dk * p->dv + 4;
+      continue;
+    }
+    out->n_factored++;
+    const int64_t ra = ss::meta_ra(pk), rf = ss::meta_rf(pk), nn = ss::meta_n(pk);
+    out->active_components += ra;
+    out->frozen_components += rf;
+    out->pad_entries += nn;
+    live += comp * (ra + rf + nn);
+    out->max_rank = std::max<int64_t>(out->max_rank, ra + rf);
+    out->rank_hist[std::min<int64_t>(64, ra + rf)]++;
+  }
+  out->live_bytes = live;
+  out->reserved_bytes = p->reserved;
+  out->decode_calls = p->decode_calls;
+  out->compact_calls = p->compact_calls;
+  out->readout_calls = p->readout_calls;
+  for (int i = 0; i < ss::kAcctSlots; ++i) {
+    out->decode_bytes_factored += acct[ss::A_DECODE_FACTORED * ss::kAcctSlots + i];
+    out->decode_bytes_dense += acct[ss::A_DECODE_DENSE * ss::kAcctSlots + i];
+    out->compact_flops += acct[ss::A_COMPACT_FLOPS * ss::kAcctSlots + i];
+    out->compact_states += acct[ss::A_COMPACT_STATES * ss::kAcctSlots + i];
+  }
+  out->decode_bytes = out->decode_bytes_factored + out->decode_bytes_dense;
+  out->promotions = ctr[ss::C_PROMOTIONS];
+  out->cap_truncations = ctr[ss::C_CAP_TRUNC];
+  for (auto &ev : p->pending) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, ev.a, ev.b) == hipSuccess) {
+      p->kernel_ms[ev.kernel] += ms;
+      p->kernel_launches[ev.kernel] += 1;
+    }
+    p->spare.push_back(ev.a);
+    p->spare.push_back(ev.b);
+  }
+  p->pending.clear();
+  for (int k = 0; k < SS_KERNEL_COUNT; ++k) {
+    out->kernel_ms[k] = p->kernel_ms[k];
+    out->kernel_launches[k] = p->kernel_launches[k];
+  }
+  p->dense_upper = std::min<int64_t>(p->cap_d, ctr[ss::C_DENSE_COUNT]);
+  return SS_OK;
+}
+
+ss_status ss_pool_timing(ss_pool *p, int32_t enable) {
+  if (!p) return fail(SS_ERR_ARG, "pool is NULL");
+  p->timing = enable != 0;
+  return SS_OK;
+}
+
+}  // extern "C"

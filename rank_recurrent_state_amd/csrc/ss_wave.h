@@ -1,0 +1,86 @@
+// ss_wave.h -- wavefront (64-lane) reductions for gfx950.
+//
+// Sums over aligned groups of P lanes use DPP inside a row of 16 lanes
+// (quad permutes, half-row and row mirrors: each step folds two aligned
+// halves of a 2^j block, so every lane of the block ends with the block sum),
+// ds_swizzle for the 16-lane stride inside a half-wave and ds_bpermute for
+// the 32-lane stride.
+#pragma once
+#include <hip/hip_runtime.h>
+
+namespace ss {
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// lane i reads lane i ^ MASK inside each 32-lane half (MASK < 32)
+template <int MASK>
+__device__ __forceinline__ float swz_xor(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), (MASK << 10) | 0x1F));
+}
+
+__device__ __forceinline__ float xor32(float x) {
+  const int lane = __lane_id();
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __builtin_bit_cast(int, x)));
+}
+
+// sum over each aligned block of P lanes (P a power of two, 1..64)
+template <int P>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (P >= 2) x += dpp<0xB1>(x);    // quad_perm [1,0,3,2]
+  if constexpr (P >= 4) x += dpp<0x4E>(x);    // quad_perm [2,3,0,1]
+  if constexpr (P >= 8) x += dpp<0x141>(x);   // row_half_mirror
+  if constexpr (P >= 16) x += dpp<0x140>(x);  // row_mirror
+  if constexpr (P >= 32) x += swz_xor<16>(x);
+  if constexpr (P >= 64) x += xor32(x);
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) { return group_sum<64>(x); }
+
+// lane i reads lane i ^ S (S a power of two < 64)
+template <int S>
+__device__ __forceinline__ float lane_xor(float x) {
+  if constexpr (S >= 32) return xor32(x);
+  else return swz_xor<S>(x);
+}
+
+// sum over lanes that differ only in bits >= log2(P): lanes with the same
+// position inside their P-block end with the same total
+template <int P>
+__device__ __forceinline__ float cross_group_sum(float x) {
+  if constexpr (P <= 1) x += lane_xor<1>(x);
+  if constexpr (P <= 2) x += lane_xor<2>(x);
+  if constexpr (P <= 4) x += lane_xor<4>(x);
+  if constexpr (P <= 8) x += lane_xor<8>(x);
+  if constexpr (P <= 16) x += lane_xor<16>(x);
+  if constexpr (P <= 32) x += lane_xor<32>(x);
+  return x;
+}
+
+__device__ __forceinline__ float4 add4(float4 a, float4 b) { return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w); }
+__device__ __forceinline__ float4 sub4(float4 a, float4 b) { return make_float4(a.x - b.x, a.y - b.y, a.z - b.z, a.w - b.w); }
+__device__ __forceinline__ float4 scale4(float s, float4 a) { return make_float4(s * a.x, s * a.y, s * a.z, s * a.w); }
+__device__ __forceinline__ float dot4(float4 a, float4 b) { return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w; }
+__device__ __forceinline__ float4 zero4() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+__device__ __forceinline__ float4 fma4(float s, float4 a, float4 c) {
+  return make_float4(fmaf(s, a.x, c.x), fmaf(s, a.y, c.y), fmaf(s, a.z, c.z), fmaf(s, a.w, c.w));
+}
+
+template <int P>
+__device__ __forceinline__ float4 cross_group_sum4(float4 a) {
+  return make_float4(cross_group_sum<P>(a.x), cross_group_sum<P>(a.y), cross_group_sum<P>(a.z),
+                     cross_group_sum<P>(a.w));
+}
+
+__device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+__device__ __forceinline__ void st4(float *p, float4 v) { *reinterpret_cast<float4 *>(p) = v; }
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ float uniformf(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+
+}  // namespace ss

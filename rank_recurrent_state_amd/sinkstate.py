@@ -1,0 +1,265 @@
+"""ctypes binding of libsinkstate.so (argument marshalling only).
+
+Every function keeps the name of the C entry point it wraps, without the
+``ss_`` prefix.  Tensors are torch fp32 tensors on the GPU; only their data
+pointers and the current HIP stream cross the boundary.  There is no CPU
+fallback: if the library is missing, loading fails with an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch  # loaded first so that the library binds to the same HIP runtime
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsinkstate.so")
+
+SS_OK, SS_ERR_ARG, SS_ERR_SHAPE, SS_ERR_OOM, SS_ERR_CAPACITY, SS_ERR_HIP, SS_ERR_STATE = range(7)
+RULE_SCALAR, RULE_DELTA = 0, 1
+
+_c_i32p = ctypes.POINTER(ctypes.c_int32)
+_c_i64p = ctypes.POINTER(ctypes.c_int64)
+_c_u8p = ctypes.POINTER(ctypes.c_uint8)
+_c_f32p = ctypes.POINTER(ctypes.c_float)
+
+
+class PoolDesc(ctypes.Structure):
+    _fields_ = [
+        ("n_states", ctypes.c_int64),
+        ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+        ("pad_slots", ctypes.c_int32), ("r_active", ctypes.c_int32),
+        ("dense_rank_limit", ctypes.c_int32), ("promote_on_compact", ctypes.c_int32),
+        ("max_frozen", ctypes.c_int32), ("force_dense", ctypes.c_int32),
+        ("n_groups", ctypes.c_int32),
+        ("group_of_state", _c_i32p), ("group_offset", _c_i32p),
+        ("rule", _c_u8p), ("eps", _c_f32p), ("eps_default", ctypes.c_float),
+        ("dense_capacity", ctypes.c_int64),
+    ]
+
+
+class Init(ctypes.Structure):
+    _fields_ = [("comp_off", _c_i64p), ("u", _c_f32p), ("v", _c_f32p), ("sigma", _c_f32p)]
+
+
+class Stats(ctypes.Structure):
+    _fields_ = [
+        ("n_states", ctypes.c_int64), ("n_dense", ctypes.c_int64), ("n_factored", ctypes.c_int64),
+        ("active_components", ctypes.c_int64), ("frozen_components", ctypes.c_int64),
+        ("pad_entries", ctypes.c_int64), ("live_bytes", ctypes.c_int64), ("reserved_bytes", ctypes.c_int64),
+        ("max_rank", ctypes.c_int64), ("rank_hist", ctypes.c_int64 * 65),
+        ("decode_calls", ctypes.c_int64), ("compact_calls", ctypes.c_int64), ("readout_calls", ctypes.c_int64),
+        ("decode_bytes", ctypes.c_uint64), ("decode_bytes_factored", ctypes.c_uint64),
+        ("decode_bytes_dense", ctypes.c_uint64), ("compact_states", ctypes.c_uint64),
+        ("compact_flops", ctypes.c_uint64), ("promotions", ctypes.c_int64), ("cap_truncations", ctypes.c_int64),
+        ("kernel_ms", ctypes.c_double * 8), ("kernel_launches", ctypes.c_int64 * 8),
+    ]
+
+
+KERNELS = ("decode_factored", "decode_dense", "readout_factored", "readout_dense", "compact", "materialize")
+
+
+_lib = None
+
+
+def load_library():
+    """Load libsinkstate.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with rank_recurrent_state_amd.build.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp = ctypes.c_void_p
+    lib.ss_state_pool_create.argtypes = [ctypes.POINTER(PoolDesc), ctypes.POINTER(Init), vp, ctypes.POINTER(vp)]
+    lib.ss_state_pool_destroy.argtypes = [vp]
+    lib.ss_decode_step.argtypes = [vp] + [vp] * 6 + [vp]
+    lib.ss_readout.argtypes = [vp, vp, vp, vp]
+    lib.ss_compact.argtypes = [vp, ctypes.c_int32, vp]
+    lib.ss_schedule_due.argtypes = [vp, ctypes.c_int64, _c_i32p, ctypes.c_int32, _c_i32p]
+    lib.ss_state_export.argtypes = [vp, _c_i64p, ctypes.c_int64, vp, ctypes.c_size_t,
+                                    ctypes.POINTER(ctypes.c_size_t), vp]
+    lib.ss_pool_stats.argtypes = [vp, ctypes.POINTER(Stats), vp]
+    lib.ss_pool_timing.argtypes = [vp, ctypes.c_int32]
+    lib.ss_dense_rank_limit.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    lib.ss_dense_rank_limit.restype = ctypes.c_int32
+    lib.ss_decode_bytes_per_state.argtypes = [ctypes.c_int32] * 6
+    lib.ss_decode_bytes_per_state.restype = ctypes.c_uint64
+    lib.ss_status_string.argtypes = [ctypes.c_int]
+    lib.ss_status_string.restype = ctypes.c_char_p
+    lib.ss_last_error.restype = ctypes.c_char_p
+    for name in ("ss_state_pool_create", "ss_state_pool_destroy", "ss_decode_step", "ss_readout", "ss_compact",
+                 "ss_schedule_due", "ss_state_export", "ss_pool_stats", "ss_pool_timing"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+class SinkStateError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+def _check(st):
+    if st != SS_OK:
+        lib = load_library()
+        raise SinkStateError(st, f"{lib.ss_status_string(st).decode()}: {lib.ss_last_error().decode()}")
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t, n_expected, name):
+    if t is None:
+        return None
+    if not (t.is_cuda and t.dtype == torch.float32 and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous float32 CUDA tensor")
+    if t.numel() != n_expected:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {n_expected}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _arr(a, dtype, ctype):
+    if a is None:
+        return None, None
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a, a.ctypes.data_as(ctype)
+
+
+def dense_rank_limit(d_k: int, d_v: int) -> int:
+    return int(load_library().ss_dense_rank_limit(d_k, d_v))
+
+
+def decode_bytes_per_state(d_k, d_v, n_comp, n_pad, rule, dense) -> int:
+    return int(load_library().ss_decode_bytes_per_state(d_k, d_v, n_comp, n_pad, rule, int(bool(dense))))
+
+
+class StatePool:
+    """Owner of one ss_pool handle."""
+
+    def __init__(self, handle, n_states, d_k, d_v, K, r, n_groups, any_delta):
+        self.handle = handle
+        self.N, self.d_k, self.d_v, self.K, self.r, self.n_groups = n_states, d_k, d_v, K, r, n_groups
+        self.any_delta = any_delta
+
+    def close(self):
+        if self.handle:
+            load_library().ss_state_pool_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def state_pool_create(n_states, d_k, d_v, pad_slots=8, r_active=8, dense_rank_limit=-1, promote_on_compact=True,
+                      max_frozen=0, force_dense=False, group_of_state=None, group_offset=None, rule=None, eps=None,
+                      eps_default=0.0, dense_capacity=0, comp_off=None, u=None, v=None, sigma=None,
+                      stream=None) -> StatePool:
+    lib = load_library()
+    n_groups = 1 if group_offset is None else len(group_offset)
+    keep = []
+    g_a, g_p = _arr(group_of_state, np.int32, _c_i32p)
+    o_a, o_p = _arr(group_offset, np.int32, _c_i32p)
+    r_a, r_p = _arr(rule, np.uint8, _c_u8p)
+    e_a, e_p = _arr(eps, np.float32, _c_f32p)
+    keep += [g_a, o_a, r_a, e_a]
+    desc = PoolDesc(int(n_states), int(d_k), int(d_v), int(pad_slots), int(r_active), int(dense_rank_limit),
+                    int(bool(promote_on_compact)), int(max_frozen), int(bool(force_dense)), int(n_groups),
+                    g_p, o_p, r_p, e_p, float(eps_default), int(dense_capacity))
+    init = None
+    if comp_off is not None:
+        c_a, c_p = _arr(comp_off, np.int64, _c_i64p)
+        u_a, u_p = _arr(u, np.float32, _c_f32p)
+        v_a, v_p = _arr(v, np.float32, _c_f32p)
+        s_a, s_p = _arr(sigma, np.float32, _c_f32p)
+        keep += [c_a, u_a, v_a, s_a]
+        init = Init(c_p, u_p, v_p, s_p)
+    handle = ctypes.c_void_p()
+    st = lib.ss_state_pool_create(ctypes.byref(desc), ctypes.byref(init) if init is not None else None,
+                                  _stream(stream) if torch.cuda.is_available() else None, ctypes.byref(handle))
+    _check(st)
+    any_delta = rule is not None and bool(np.any(np.asarray(rule) == 1))
+    return StatePool(handle, int(n_states), int(d_k), int(d_v), int(pad_slots), int(r_active), n_groups, any_delta)
+
+
+def decode_step(pool: StatePool, q, k, v, alpha, beta, o, stream=None):
+    N, dk, dv = pool.N, pool.d_k, pool.d_v
+    args = [_ptr(q, N * dk, "q"), _ptr(k, N * dk, "k"), _ptr(v, N * dv, "v"), _ptr(alpha, N, "alpha"),
+            _ptr(beta, N, "beta") if beta is not None else None, _ptr(o, N * dv, "o")]
+    _check(load_library().ss_decode_step(pool.handle, *args, _stream(stream)))
+
+
+def readout(pool: StatePool, q, o, stream=None):
+    N, dk, dv = pool.N, pool.d_k, pool.d_v
+    _check(load_library().ss_readout(pool.handle, _ptr(q, N * dk, "q"), _ptr(o, N * dv, "o"), _stream(stream)))
+
+
+def compact(pool: StatePool, group: int = -1, stream=None):
+    _check(load_library().ss_compact(pool.handle, int(group), _stream(stream)))
+
+
+def schedule_due(pool: StatePool, step: int) -> list:
+    out = (ctypes.c_int32 * max(1, pool.n_groups))()
+    n = ctypes.c_int32()
+    _check(load_library().ss_schedule_due(pool.handle, int(step), out, max(1, pool.n_groups), ctypes.byref(n)))
+    return [int(out[i]) for i in range(n.value)]
+
+
+def pool_stats(pool: StatePool, stream=None) -> dict:
+    s = Stats()
+    _check(load_library().ss_pool_stats(pool.handle, ctypes.byref(s), _stream(stream)))
+    d = {name: getattr(s, name) for name, _ in Stats._fields_ if name not in ("rank_hist", "kernel_ms",
+                                                                              "kernel_launches")}
+    d["rank_hist"] = list(s.rank_hist)
+    d["kernel_ms"] = {k: s.kernel_ms[i] for i, k in enumerate(KERNELS)}
+    d["kernel_launches"] = {k: s.kernel_launches[i] for i, k in enumerate(KERNELS)}
+    return d
+
+
+def pool_timing(pool: StatePool, enable: bool = True):
+    _check(load_library().ss_pool_timing(pool.handle, int(bool(enable))))
+
+
+def state_export(pool: StatePool, ids, stream=None) -> list:
+    """Canonical states (effective weights) as a list of dicts of float32 arrays."""
+    lib = load_library()
+    ids = np.ascontiguousarray(ids, dtype=np.int64)
+    need = ctypes.c_size_t()
+    st = lib.ss_state_export(pool.handle, ids.ctypes.data_as(_c_i64p), ids.shape[0], None, 0, ctypes.byref(need),
+                             _stream(stream))
+    if st not in (SS_OK, SS_ERR_CAPACITY):
+        _check(st)
+    buf = np.zeros(max(1, need.value), dtype=np.uint8)
+    _check(lib.ss_state_export(pool.handle, ids.ctypes.data_as(_c_i64p), ids.shape[0],
+                               buf.ctypes.data_as(ctypes.c_void_p), buf.nbytes, ctypes.byref(need), _stream(stream)))
+    dk, dv = pool.d_k, pool.d_v
+    out, pos = [], 0
+    for _ in range(ids.shape[0]):
+        hdr = buf[pos:pos + 32].view(np.int32)
+        pos += 32
+        sid, dense, R, ra, n, rule = (int(x) for x in hdr[:6])
+        if dense:
+            S = buf[pos:pos + 4 * dk * dv].view(np.float32).reshape(dk, dv).copy()
+            pos += 4 * dk * dv
+            out.append({"id": sid, "dense": True, "S": S, "rule": rule})
+            continue
+        f = buf[pos:pos + 4 * (R * (1 + dk + dv) + n * (1 + dk + dv))].view(np.float32)
+        pos += f.nbytes
+        o = 0
+        sig = f[o:o + R].copy(); o += R
+        U = f[o:o + R * dk].reshape(R, dk).copy(); o += R * dk
+        V = f[o:o + R * dv].reshape(R, dv).copy(); o += R * dv
+        c = f[o:o + n].copy(); o += n
+        Kp = f[o:o + n * dk].reshape(n, dk).copy(); o += n * dk
+        W = f[o:o + n * dv].reshape(n, dv).copy(); o += n * dv
+        out.append({"id": sid, "dense": False, "sigma": sig, "U": U, "V": V, "n_active": ra, "c": c, "K": Kp,
+                    "W": W, "rule": rule})
+    return out

@@ -1,0 +1,98 @@
+"""Helpers shared by the GPU parity tests: convert exported GPU states to oracle
+states and compare results with the tolerances of the parity protocol.
+
+Tolerances (fp32 GPU against the fp64 oracle):
+  outputs o         ||o_gpu - o_or|| <= 1e-4 * max(||o_or||, ||S||_F ||q||)
+  states            ||S_gpu - S_or||_F <= 1e-4 ||S_or||_F
+  singular values   |sigma_gpu - sigma_or| <= 1e-4 sigma_or for every kept component
+  subspaces         projectors of clusters split at relative gaps > 1e-2
+  ranks             equal, except keep/drop decisions within 1e-5 sigma_max of
+                    eps * sigma_max and active/frozen splits within 1e-5
+                    sigma_max ("guard band"), which are counted and accepted
+"""
+import numpy as np
+
+from oracle import OraclePool
+from oracle.oracle import OracleState
+
+TOL = 1e-4
+GUARD = 1e-5
+
+
+def to_oracle_state(st, eps):
+    if st["dense"]:
+        return OracleState(S=st["S"].astype(np.float64), rule=st["rule"], eps=float(eps))
+    return OracleState(st["U"].astype(np.float64), st["V"].astype(np.float64), st["sigma"].astype(np.float64),
+                       st["K"].astype(np.float64), st["W"].astype(np.float64), st["c"].astype(np.float64),
+                       rule=st["rule"], eps=float(eps))
+
+
+def reconstruct(st):
+    if st["dense"]:
+        return st["S"].astype(np.float64)
+    S = (st["U"].T.astype(np.float64) * st["sigma"].astype(np.float64)) @ st["V"].astype(np.float64)
+    if len(st["c"]):
+        S += (st["K"].T.astype(np.float64) * st["c"].astype(np.float64)) @ st["W"].astype(np.float64)
+    return S
+
+
+def oracle_from_export(states, eps, d_k, d_v, K, r, L=-1, promote=True):
+    P = OraclePool(len(states), d_k, d_v, K, r, L, promote)
+    for j, st in enumerate(states):
+        P.set_state(j, to_oracle_state(st, eps[j]), as_init=False)
+    return P
+
+
+def rel_out_err(o_gpu, o_or, S_norm, q_norm):
+    den = np.maximum(np.linalg.norm(o_or, axis=1), S_norm * q_norm)
+    den = np.maximum(den, 1e-30)
+    return np.linalg.norm(o_gpu - o_or, axis=1) / den
+
+
+def compare_compacted(gpu_states, P, eps, K=None):
+    """Compare GPU states after a compaction with the oracle's.  Returns
+    (max state rel err, max sigma rel err, guard-band count, rank mismatches outside the guard band)."""
+    worst_s, worst_sig, guard, bad = 0.0, 0.0, 0, []
+    for j, st in enumerate(gpu_states):
+        ost = P.get_state(j)
+        Sg = reconstruct(st)
+        So = P.reconstruct(j)
+        nrm = np.linalg.norm(So)
+        worst_s = max(worst_s, np.linalg.norm(Sg - So) / max(nrm, 1e-30))
+        if st["dense"] != ost.dense:
+            bad.append((j, "dense flag"))
+            continue
+        if st["dense"]:
+            continue
+        sg = np.sort(st["sigma"].astype(np.float64))[::-1]
+        so = ost.sigma
+        smax = max(sg[0] if len(sg) else 0.0, so[0] if len(so) else 0.0)
+        if len(sg) != len(so):
+            thr = eps[j] * smax
+            longer = sg if len(sg) > len(so) else so
+            extra = longer[min(len(sg), len(so)):]
+            if np.all(np.abs(extra - thr) <= GUARD * smax):
+                guard += 1
+            else:
+                bad.append((j, f"rank {len(sg)} vs {len(so)}"))
+            continue
+        if len(sg):
+            worst_sig = max(worst_sig, float(np.max(np.abs(sg - so) / so)))
+    return worst_s, worst_sig, guard, bad
+
+
+def active_projector_err(gpu_state, ost, r):
+    """Projector distance of the active block when it is separated from the rest by a gap > 1e-2 sigma_max."""
+    if gpu_state["dense"] or ost.dense:
+        return 0.0
+    sg = gpu_state["sigma"]
+    if len(sg) <= r:
+        return 0.0
+    smax = float(sg[0])
+    if (sg[r - 1] - sg[r]) / smax <= 1e-2:
+        return 0.0
+    Ug = gpu_state["U"][:r].T.astype(np.float64)
+    Uo = ost.U[:r].T
+    Vg = gpu_state["V"][:r].T.astype(np.float64)
+    Vo = ost.V[:r].T
+    return max(np.linalg.norm(Ug @ Ug.T - Uo @ Uo.T), np.linalg.norm(Vg @ Vg.T - Vo @ Vo.T))

@@ -1,0 +1,123 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, rejects bad arguments before any HIP call, and its host-side
+arithmetic matches what the pages print."""
+import ctypes
+import json
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sinkstate.h")
+GOLD = os.path.join(ROOT, "tests", "golden")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from rank_recurrent_state_amd import sinkstate
+    if not os.path.exists(sinkstate.LIB_PATH):
+        from rank_recurrent_state_amd.build import build
+        build()
+    return sinkstate.load_library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ss_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    from rank_recurrent_state_amd import sinkstate
+    names = _declared()
+    assert len(names) >= 10
+    out = subprocess.run(["nm", "-D", "--defined-only", sinkstate.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if " T " in line)
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        getattr(lib, n)
+
+
+def test_library_links_only_expected_runtimes():
+    from rank_recurrent_state_amd import sinkstate
+    out = subprocess.run(["readelf", "-d", sinkstate.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    needed = re.findall(r"NEEDED.*\[(.*)\]", out)
+    assert any("amdhip64" in n for n in needed)
+    assert not any("torch" in n or "python" in n or "oracle" in n for n in needed), needed
+
+
+def test_status_strings(lib):
+    for st in range(7):
+        assert lib.ss_status_string(st)
+    assert lib.ss_last_error() is not None
+
+
+def test_create_rejects_bad_arguments_without_touching_the_gpu(lib):
+    from rank_recurrent_state_amd import sinkstate as ss
+    out = ctypes.c_void_p()
+    assert lib.ss_state_pool_create(None, None, None, ctypes.byref(out)) == ss.SS_ERR_ARG
+    assert lib.ss_state_pool_create(None, None, None, None) == ss.SS_ERR_ARG
+    base = dict(n_states=4, d_k=16, d_v=32, pad_slots=8, r_active=8, dense_rank_limit=-1, promote_on_compact=1,
+                max_frozen=0, force_dense=0, n_groups=1, group_of_state=None, group_offset=None, rule=None,
+                eps=None, eps_default=1e-3, dense_capacity=0)
+    cases = [({"n_states": 0}, ss.SS_ERR_ARG), ({"d_k": 18}, ss.SS_ERR_SHAPE), ({"d_v": 260}, ss.SS_ERR_SHAPE),
+             ({"pad_slots": 9}, ss.SS_ERR_SHAPE), ({"r_active": 0}, ss.SS_ERR_SHAPE),
+             ({"n_groups": 0}, ss.SS_ERR_ARG), ({"max_frozen": 300}, ss.SS_ERR_ARG),
+             ({"eps_default": -1.0}, ss.SS_ERR_ARG), ({"dense_capacity": 5}, ss.SS_ERR_ARG),
+             ({"d_k": 256, "d_v": 256}, ss.SS_ERR_SHAPE)]
+    for over, expect in cases:
+        d = dict(base, **over)
+        desc = ss.PoolDesc(*[d[f] for f, _ in ss.PoolDesc._fields_])
+        st = lib.ss_state_pool_create(ctypes.byref(desc), None, None, ctypes.byref(out))
+        assert st == expect, (over, st, lib.ss_last_error())
+        assert not out.value
+    # unsorted sigma and a bad CSR are rejected on the host too
+    import numpy as np
+    d = dict(base)
+    desc = ss.PoolDesc(*[d[f] for f, _ in ss.PoolDesc._fields_])
+    off = np.array([0, 2, 2, 2, 2], np.int64)
+    u = np.zeros((2, 16), np.float32)
+    v = np.zeros((2, 32), np.float32)
+    for sig, expect in [(np.array([0.1, 0.5], np.float32), ss.SS_ERR_ARG), (np.array([1, np.nan], np.float32),
+                                                                             ss.SS_ERR_ARG)]:
+        init = ss.Init(off.ctypes.data_as(ss._c_i64p), u.ctypes.data_as(ss._c_f32p), v.ctypes.data_as(ss._c_f32p),
+                       sig.ctypes.data_as(ss._c_f32p))
+        assert lib.ss_state_pool_create(ctypes.byref(desc), ctypes.byref(init), None, ctypes.byref(out)) == expect
+
+
+def test_calls_on_null_pool_are_rejected(lib):
+    from rank_recurrent_state_amd import sinkstate as ss
+    assert lib.ss_decode_step(None, None, None, None, None, None, None, None) == ss.SS_ERR_ARG
+    assert lib.ss_readout(None, None, None, None) == ss.SS_ERR_ARG
+    assert lib.ss_compact(None, 0, None) == ss.SS_ERR_ARG
+    assert lib.ss_pool_stats(None, None, None) == ss.SS_ERR_ARG
+    n = ctypes.c_size_t()
+    assert lib.ss_state_export(None, None, 0, None, 0, ctypes.byref(n), None) == ss.SS_ERR_ARG
+    assert lib.ss_state_pool_destroy(None) == ss.SS_OK
+
+
+def test_dense_rank_limit_pins(lib):
+    g = json.load(open(os.path.join(GOLD, "memory_arithmetic.json")))
+    assert lib.ss_dense_rank_limit(128, 128) == g["threshold_128x128"]
+    assert lib.ss_dense_rank_limit(128, 80) == lib.ss_dense_rank_limit(80, 128) == 49
+    assert lib.ss_dense_rank_limit(16, 32) == 10
+
+
+def test_decode_byte_formula(lib):
+    """Algorithmic bytes: rank 8 with a half-full pad on 128x80 is the 12,126 B of the plan
+    (which counts Gamma as two 4-byte accesses) with the 16-byte record read and written instead."""
+    f = lib.ss_decode_bytes_per_state
+    avg = (f(128, 80, 8, 3, 0, 0) + f(128, 80, 8, 4, 0, 0)) / 2
+    assert avg == 12126 - 8 + 32
+    # a factored rank-r state with n slots reads (r + n) components of d_k + d_v + 1 floats
+    assert f(128, 80, 9, 0, 0, 0) - f(128, 80, 8, 0, 0, 0) == 4 * (128 + 80 + 1)
+    assert f(128, 80, 8, 0, 1, 0) - f(128, 80, 8, 0, 0, 0) == 4        # beta
+    # dense: the state read and written
+    assert f(128, 80, 0, 0, 0, 1) == 16 + 4 + 2 * 4 * 128 * 80 + 4 * (2 * 128 + 80 + 1) + 4 * 80
+    # page-printed footprint: rank-8 factors + a full pad of one 80x128 state = 13,376 B
+    g = json.load(open(os.path.join(GOLD, "memory_arithmetic.json")))
+    assert 2 * 8 * 4 * (128 + 80 + 1) == g["total_bytes"]

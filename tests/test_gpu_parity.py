@@ -1,0 +1,247 @@
+"""GPU parity: the HIP path (through the C-ABI) against the fp64 oracle.
+
+Lock-step protocol: before each call the sampled states are exported from the
+GPU (canonical form, fp32 upcast to fp64) and loaded into the oracle; both
+sides then run the same call on bit-identical inputs and the results are
+compared with the tolerances in parity_util.
+"""
+import numpy as np
+import pytest
+import torch
+
+from parity_util import (TOL, active_projector_err, compare_compacted, oracle_from_export, reconstruct,
+                         rel_out_err)
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from rank_recurrent_state_amd import sinkstate as ss
+    from rank_recurrent_state_amd import workloads as W
+
+
+def _pool_from_init(w, init, **kw):
+    return ss.state_pool_create(w.n_states, w.d_k, w.d_v, w.K, w.r, group_of_state=init["group_of_state"],
+                                group_offset=init["group_offset"], rule=init["rule"], eps=init["eps"],
+                                comp_off=init["comp_off"], u=init["u"], v=init["v"], sigma=init["sigma"], **kw)
+
+
+def _lockstep(w, init, pool, ids, steps, promote=True, check_readout=False):
+    """Run `steps` decode(+compaction) steps in lock-step on the states `ids`."""
+    gen = W.StepInputs(w, device="cuda")
+    eps = init["eps"][ids]
+    grp = init["group_of_state"][ids]
+    o = torch.empty(w.n_states, w.d_v, device="cuda")
+    worst = {"o": 0.0, "S": 0.0, "S_c": 0.0, "sigma": 0.0, "proj": 0.0, "ro": 0.0}
+    guard = 0
+    for t in range(1, steps + 1):
+        x = gen.generate(t)
+        before = ss.state_export(pool, ids)
+        P = oracle_from_export(before, eps, w.d_k, w.d_v, w.K, w.r, promote=promote)
+        sub = {k: v.cpu().numpy()[ids].astype(np.float64) for k, v in x.items()}
+        if check_readout:
+            ss.readout(pool, x["q"], o)
+            torch.cuda.synchronize()
+            oro = P.readout(sub["q"])
+            Sn = np.array([np.linalg.norm(reconstruct(s)) for s in before])
+            e = rel_out_err(o.cpu().numpy()[ids], oro, Sn, np.linalg.norm(sub["q"], axis=1))
+            worst["ro"] = max(worst["ro"], float(e.max()))
+        ss.decode_step(pool, x["q"], x["k"], x["v"], x["alpha"], x["beta"], o)
+        torch.cuda.synchronize()
+        oo = P.decode(sub["q"], sub["k"], sub["v"], sub["alpha"], sub["beta"])
+        after = ss.state_export(pool, ids)
+        Sn = np.array([np.linalg.norm(P.reconstruct(j)) for j in range(len(ids))])
+        e = rel_out_err(o.cpu().numpy()[ids], oo, Sn, np.linalg.norm(sub["q"], axis=1))
+        worst["o"] = max(worst["o"], float(e.max()))
+        for j, st in enumerate(after):
+            So = P.reconstruct(j)
+            worst["S"] = max(worst["S"], np.linalg.norm(reconstruct(st) - So) / max(np.linalg.norm(So), 1e-30))
+        due = ss.schedule_due(pool, t)
+        if due:
+            for g in due:
+                ss.compact(pool, g)
+            P2 = oracle_from_export(after, eps, w.d_k, w.d_v, w.K, w.r, promote=promote)
+            sel = np.nonzero(np.isin(grp, due))[0]
+            P2.compact(sel)
+            comp = ss.state_export(pool, ids)
+            ws, wsig, gd, bad = compare_compacted(comp, P2, eps)
+            assert not bad, f"step {t}: rank/dense mismatches outside the guard band: {bad[:5]}"
+            guard += gd
+            worst["S_c"] = max(worst["S_c"], ws)
+            worst["sigma"] = max(worst["sigma"], wsig)
+            for j in sel:
+                worst["proj"] = max(worst["proj"], active_projector_err(comp[j], P2.get_state(j), w.r))
+    return worst, guard
+
+
+def _assert_worst(worst):
+    for k, v in worst.items():
+        assert v <= TOL, f"{k}: {v:.3e} > {TOL}  (all: {worst})"
+
+
+@pytest.mark.parametrize("promote", [True, False])
+def test_tiny_lockstep(promote):
+    """64 states 16x32, empty start, compaction every 8 steps; with promotion the
+    states move to the dense region, without it the frozen part keeps growing."""
+    w = W.get("tiny")
+    init = W.initial_state(w)
+    pool = _pool_from_init(w, init, promote_on_compact=promote, max_frozen=200)
+    worst, guard = _lockstep(w, init, pool, np.arange(w.n_states), 40, promote=promote, check_readout=True)
+    st = ss.pool_stats(pool)
+    pool.close()
+    print("tiny", promote, worst, "guard", guard, "dense", st["n_dense"], "max_rank", st["max_rank"])
+    _assert_worst(worst)
+    if promote:
+        assert st["n_dense"] > 0
+    else:
+        assert st["n_dense"] == 0 and st["max_rank"] > 10
+
+
+def test_mamba2_lockstep_one_request():
+    """2,016 Mamba-2 states (one request of the 258k workload), 4 stagger groups, ragged sample."""
+    w = W.get("mamba2_258k", n_requests=1)
+    init = W.initial_state(w)
+    pool = _pool_from_init(w, init)
+    ids = np.unique(np.concatenate([np.arange(0, w.n_states, 17), [w.n_states - 1]]))
+    worst, guard = _lockstep(w, init, pool, ids, 24, check_readout=True)
+    pool.close()
+    print("mamba2", worst, "guard", guard)
+    _assert_worst(worst)
+
+
+def test_gdn_delta_lockstep_one_request():
+    """1,536 delta-rule states 128x128 (one request), random initial ranks 2..16."""
+    w = W.get("gdn_delta", n_requests=1)
+    init = W.initial_state(w)
+    pool = _pool_from_init(w, init)
+    ids = np.unique(np.concatenate([np.arange(0, w.n_states, 13), [w.n_states - 1]]))
+    worst, guard = _lockstep(w, init, pool, ids, 24)
+    pool.close()
+    print("gdn", worst, "guard", guard)
+    _assert_worst(worst)
+
+
+def test_mixed_dense_lockstep():
+    """Mixed scalar/delta states with ranks 2..64 + frozen extras; above 49 the state starts dense."""
+    w = W.get("mixed_dense", n_requests=1)
+    init = W.initial_state(w)
+    pool = _pool_from_init(w, init)
+    st0 = ss.pool_stats(pool)
+    ranks = np.diff(init["comp_off"])
+    assert st0["n_dense"] == int(np.sum(ranks > 49))
+    ids = np.arange(w.n_states)
+    worst, guard = _lockstep(w, init, pool, ids, 16, check_readout=True)
+    pool.close()
+    print("mixed", worst, "guard", guard)
+    _assert_worst(worst)
+
+
+def test_dense_baseline_matches_dense_recurrence():
+    """force_dense pool (the dense HIP baseline) against the oracle's dense recurrence."""
+    w = W.get("mamba2_258k", n_requests=1)
+    init = W.initial_state(w)
+    pool = _pool_from_init(w, init, force_dense=True)
+    ids = np.arange(0, w.n_states, 31)
+    worst, _ = _lockstep(w, init, pool, ids, 6)
+    st = ss.pool_stats(pool)
+    pool.close()
+    assert st["n_dense"] == w.n_states
+    _assert_worst(worst)
+
+
+def test_decode_bytes_accounting():
+    """In-kernel algorithmic byte counter equals the host formula over the live ranks."""
+    w = W.get("mixed_dense", n_requests=1)
+    init = W.initial_state(w)
+    pool = _pool_from_init(w, init)
+    gen = W.StepInputs(w, device="cuda")
+    o = torch.empty(w.n_states, w.d_v, device="cuda")
+    for t in range(1, 4):
+        states = ss.state_export(pool, np.arange(w.n_states))
+        expect = sum(ss.decode_bytes_per_state(w.d_k, w.d_v, 0 if s["dense"] else len(s["sigma"]),
+                                               0 if s["dense"] else len(s["c"]), s["rule"], s["dense"])
+                     for s in states)
+        b0 = ss.pool_stats(pool)["decode_bytes"]
+        x = gen.generate(t)
+        ss.decode_step(pool, x["q"], x["k"], x["v"], x["alpha"], x["beta"], o)
+        b1 = ss.pool_stats(pool)["decode_bytes"]
+        assert b1 - b0 == expect
+    pool.close()
+
+
+def test_edge_shapes_and_ragged():
+    """d = 4 (one lane per vector), 37 states (ragged workgroups), K = 1 (compaction every
+    step), r = 1, empty states, delta rule, against the oracle in lock-step."""
+    rng = np.random.default_rng(5)
+    for (dk, dv, K, r, N) in [(4, 8, 1, 1, 37), (12, 20, 3, 2, 37), (64, 44, 8, 8, 9)]:
+        R = rng.integers(0, 6, N)
+        R[0] = 0
+        off = np.concatenate([[0], np.cumsum(R)]).astype(np.int64)
+        T = int(off[-1])
+        u = rng.standard_normal((T, dk)).astype(np.float32)
+        v = rng.standard_normal((T, dv)).astype(np.float32)
+        sig = np.concatenate([np.sort(rng.uniform(0.1, 2, x))[::-1] for x in R]).astype(np.float32)
+        rule = (np.arange(N) % 2).astype(np.uint8)
+        eps = np.full(N, 1e-3, np.float32)
+        pool = ss.state_pool_create(N, dk, dv, K, r, rule=rule, eps=eps, comp_off=off, u=u, v=v, sigma=sig,
+                                    group_offset=[0], promote_on_compact=False, max_frozen=64)
+        o = torch.empty(N, dv, device="cuda")
+        ids = np.arange(N)
+        worst = 0.0
+        for t in range(1, 3 * K + 2):
+            q = torch.randn(N, dk, device="cuda")
+            k = torch.nn.functional.normalize(torch.randn(N, dk, device="cuda"), dim=1)
+            vv = torch.randn(N, dv, device="cuda")
+            a = 0.9 + 0.1 * torch.rand(N, device="cuda")
+            b = torch.rand(N, device="cuda")
+            before = ss.state_export(pool, ids)
+            P = oracle_from_export(before, eps, dk, dv, K, r, promote=False)
+            ss.decode_step(pool, q, k, vv, a, b, o)
+            if ss.schedule_due(pool, t):
+                ss.compact(pool, 0)
+            torch.cuda.synchronize()
+            oo = P.decode(q.cpu().numpy(), k.cpu().numpy(), vv.cpu().numpy(), a.cpu().numpy(), b.cpu().numpy())
+            Sn = np.array([np.linalg.norm(P.reconstruct(j)) for j in range(N)])
+            e = rel_out_err(o.cpu().numpy(), oo, Sn, np.linalg.norm(q.cpu().numpy(), axis=1))
+            worst = max(worst, float(e.max()))
+            if ss.schedule_due(pool, t):
+                P.compact()
+                ws, wsig, gd, bad = compare_compacted(ss.state_export(pool, ids), P, eps)
+                assert not bad and ws <= TOL and wsig <= TOL, (dk, dv, K, r, ws, wsig, bad)
+        pool.close()
+        assert worst <= TOL, (dk, dv, K, r, worst)
+
+
+def test_pad_overflow_poisons_pool():
+    """A skipped compaction is caught by the kernel's own check and reported on a later call."""
+    w = W.get("tiny")
+    init = W.initial_state(w)
+    pool = _pool_from_init(w, init)
+    gen = W.StepInputs(w, device="cuda")
+    o = torch.empty(w.n_states, w.d_v, device="cuda")
+    for t in range(1, w.K + 1):
+        x = gen.generate(t)
+        ss.decode_step(pool, x["q"], x["k"], x["v"], x["alpha"], x["beta"], o)
+    x = gen.generate(w.K + 1)
+    ss.decode_step(pool, x["q"], x["k"], x["v"], x["alpha"], x["beta"], o)  # pad full: flagged, state untouched
+    torch.cuda.synchronize()
+    with pytest.raises(ss.SinkStateError) as ei:
+        ss.decode_step(pool, x["q"], x["k"], x["v"], x["alpha"], x["beta"], o)
+    assert ei.value.status == ss.SS_ERR_STATE
+    pool.close()
+
+
+def test_dense_capacity_exhaustion_is_reported():
+    w = W.get("tiny")
+    init = W.initial_state(w)
+    pool = _pool_from_init(w, init, dense_capacity=2)
+    gen = W.StepInputs(w, device="cuda")
+    o = torch.empty(w.n_states, w.d_v, device="cuda")
+    with pytest.raises(ss.SinkStateError) as ei:
+        for t in range(1, 65):
+            x = gen.generate(t)
+            ss.decode_step(pool, x["q"], x["k"], x["v"], x["alpha"], x["beta"], o)
+            for g in ss.schedule_due(pool, t):
+                ss.compact(pool, g)
+            torch.cuda.synchronize()
+    assert ei.value.status == ss.SS_ERR_CAPACITY
+    pool.close()
