@@ -372,17 +372,20 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   }
 }
 
-// Materialize S = sum_c sigma_c u_c v_c^T into a new dense slot (256 threads
-// per state, components staged through LDS in chunks of CH).
+// Materialize a dense state into a new slot of the dense region, stored as
+// H = S^T row-major [d_v][d_k]: H[j][i] = sum_c sigma_c v_c[j] u_c[i]
+// (256 threads per state; thread t owns float4 column t % (d_k/4) of rows
+// t / (d_k/4) + RG * jj; components are staged through LDS in chunks of CH,
+// rows are covered in chunks of kMatRows per thread).
 constexpr int kMatCH = 16;
+constexpr int kMatRows = 8;
 
-template <int NR>
 __global__ __launch_bounds__(256) void k_materialize(MaterializeArgs a) {
   extern __shared__ float smem[];
   __shared__ int s_slot;
   const int t = threadIdx.x;
   const int dk = a.dk, dv = a.dv;
-  const int C4 = dv >> 2, RG = 256 / C4;
+  const int C4 = dk >> 2, RG = 256 / C4;
   const int c = t % C4, g = t / C4;
   const bool act = t < RG * C4;
   float *su = smem;                 // [CH][dk]
@@ -433,42 +436,45 @@ __global__ __launch_bounds__(256) void k_materialize(MaterializeArgs a) {
     const int slot = s_slot;
     if (slot < 0) continue;
     const int total = n1 + n2;
-    float4 acc[NR];
+    float *H = a.dense + (int64_t)slot * dk * dv;
+    for (int r0 = 0; r0 < dv; r0 += RG * kMatRows) {
+      float4 acc[kMatRows];
 #pragma unroll
-    for (int j = 0; j < NR; ++j) acc[j] = zero4();
-    for (int c0 = 0; c0 < total; c0 += kMatCH) {
-      __syncthreads();
-      for (int e = t; e < kMatCH * dk; e += 256) {
-        const int cc = e / dk, row = e - cc * dk, comp = c0 + cc;
-        su[e] = comp < total ? (comp < n1 ? u1[(int64_t)comp * dk + row] : u2[(int64_t)(comp - n1) * dk + row]) : 0.f;
-      }
-      for (int e = t; e < kMatCH * dv; e += 256) {
-        const int cc = e / dv, col = e - cc * dv, comp = c0 + cc;
-        sv[e] = comp < total ? (comp < n1 ? v1[(int64_t)comp * dv + col] : v2[(int64_t)(comp - n1) * dv + col]) : 0.f;
-      }
-      if (t < kMatCH) {
-        const int comp = c0 + t;
-        ss[t] = comp < total ? scale * (comp < n1 ? s1[comp] : s2[comp - n1]) : 0.f;
-      }
-      __syncthreads();
-      if (act) {
-        const int lim = (total - c0) < kMatCH ? (total - c0) : kMatCH;
-        for (int cc = 0; cc < lim; ++cc) {
-          const float4 v4 = scale4(ss[cc], *reinterpret_cast<const float4 *>(sv + cc * dv + 4 * c));
+      for (int jj = 0; jj < kMatRows; ++jj) acc[jj] = zero4();
+      for (int c0 = 0; c0 < total; c0 += kMatCH) {
+        __syncthreads();
+        for (int e = t; e < kMatCH * dk; e += 256) {
+          const int cc = e / dk, i = e - cc * dk, comp = c0 + cc;
+          su[e] = comp < total ? (comp < n1 ? u1[(int64_t)comp * dk + i] : u2[(int64_t)(comp - n1) * dk + i]) : 0.f;
+        }
+        for (int e = t; e < kMatCH * dv; e += 256) {
+          const int cc = e / dv, j = e - cc * dv, comp = c0 + cc;
+          sv[e] = comp < total ? (comp < n1 ? v1[(int64_t)comp * dv + j] : v2[(int64_t)(comp - n1) * dv + j]) : 0.f;
+        }
+        if (t < kMatCH) {
+          const int comp = c0 + t;
+          ss[t] = comp < total ? scale * (comp < n1 ? s1[comp] : s2[comp - n1]) : 0.f;
+        }
+        __syncthreads();
+        if (act) {
+          const int lim = (total - c0) < kMatCH ? (total - c0) : kMatCH;
+          for (int cc = 0; cc < lim; ++cc) {
+            const float4 u4 = *reinterpret_cast<const float4 *>(su + cc * dk + 4 * c);
+            const float sc = ss[cc];
 #pragma unroll
-          for (int j = 0; j < NR; ++j) {
-            const int row = g + j * RG;
-            if (row < dk) acc[j] = fma4(su[cc * dk + row], v4, acc[j]);
+            for (int jj = 0; jj < kMatRows; ++jj) {
+              const int j = r0 + g + RG * jj;
+              if (j < dv) acc[jj] = fma4(sc * sv[cc * dv + j], u4, acc[jj]);
+            }
           }
         }
       }
-    }
-    float *S = a.dense + (int64_t)slot * dk * dv;
-    if (act) {
+      if (act) {
 #pragma unroll
-      for (int j = 0; j < NR; ++j) {
-        const int row = g + j * RG;
-        if (row < dk) st4(S + (int64_t)row * dv + 4 * c, acc[j]);
+        for (int jj = 0; jj < kMatRows; ++jj) {
+          const int j = r0 + g + RG * jj;
+          if (j < dv) st4(H + (int64_t)j * dk + 4 * c, acc[jj]);
+        }
       }
     }
     if (t == 0) {
@@ -536,16 +542,7 @@ __global__ void k_zero_u32(uint32_t *p, int n) {
   if (i < n) p[i] = 0u;
 }
 
-template <int NR>
-hipError_t materialize_nr(const MaterializeArgs &a, unsigned grid, hipStream_t st) {
-  const size_t sh = sizeof(float) * (size_t)kMatCH * (a.dk + a.dv + 1);
-  hipLaunchKernelGGL((k_materialize<NR>), dim3(grid), dim3(256), sh, st, a);
-  return hipGetLastError();
-}
-
 }  // namespace
-
-int dense_rows_per_thread(int dk, int dv);
 
 hipError_t launch_compact(const CompactArgs &a, hipStream_t st) {
   if (a.n_members <= 0) return hipSuccess;
@@ -561,14 +558,9 @@ hipError_t launch_compact(const CompactArgs &a, hipStream_t st) {
 hipError_t launch_materialize(const MaterializeArgs &a, int64_t grid_upper, hipStream_t st) {
   if (grid_upper <= 0) return hipSuccess;
   const unsigned grid = (unsigned)(grid_upper < 2048 ? grid_upper : 2048);
-  const int nr = dense_rows_per_thread(a.dk, a.dv);
-  if (nr <= 1) return materialize_nr<1>(a, grid, st);
-  if (nr <= 2) return materialize_nr<2>(a, grid, st);
-  if (nr <= 4) return materialize_nr<4>(a, grid, st);
-  if (nr <= 8) return materialize_nr<8>(a, grid, st);
-  if (nr <= 12) return materialize_nr<12>(a, grid, st);
-  if (nr <= 16) return materialize_nr<16>(a, grid, st);
-  return hipErrorInvalidValue;
+  const size_t sh = sizeof(float) * (size_t)kMatCH * (a.dk + a.dv + 1);
+  hipLaunchKernelGGL(k_materialize, dim3(grid), dim3(256), sh, st, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_scatter(const ScatterArgs &a, hipStream_t st) {

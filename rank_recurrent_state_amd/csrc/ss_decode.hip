@@ -2,14 +2,15 @@
 //
 // Factored states (SinkState 4.2 "(i) Buffering", 4.4 "Kernel fusion"): one
 // 64-lane wavefront per state.  The factors are streamed once: every
-// component (active and frozen region) and every filled pad slot is a pair
-// (x in R^{d_k}, y in R^{d_v}) with a weight; the wave computes
-// coef = weight * <x, q> and accumulates coef * y.  Lanes are split into
-// 64/P groups of P lanes (P = next power of two >= max(d_k, d_v)/4); a group
-// reads one pair per step as float4 lanes, reduces <x, q> with DPP inside the
-// group and keeps a float4 slice of the d_v-vector accumulator.  The decay is
-// applied through Gamma (accumulated since the last compaction), so the
-// factors are never rewritten; only the new pad slot, o and the 16-byte
+// component of the active region, every component of the frozen region and
+// every filled pad slot is a pair (x in R^{d_k}, y in R^{d_v}) with a weight,
+// and the three lists are walked as one list, so a chunk of G * UN pairs is
+// in flight whatever region its pairs come from.  Lanes are split into 64/P
+// groups of P lanes (P = next power of two >= max(d_k, d_v) / 4); a group
+// reads one pair per step as float4 lanes, reduces <x, q> with DPP inside
+// the group and keeps a float4 slice of the d_v-vector accumulator.  The
+// decay is applied through Gamma (accumulated since the last compaction), so
+// the factors are never rewritten; only the new pad slot, o and the 16-byte
 // record are written.
 //
 //   p_q = S_{t-1}^T q,  p_k = S_{t-1}^T k  (delta rule only)
@@ -17,9 +18,15 @@
 //   o   = alpha p_q + <k, q> w            (= S_t^T q, read after the update)
 //   pad slot n <- (k, w, 1 / (alpha Gamma)),  Gamma <- alpha Gamma
 //
-// Dense states (SinkState 4.4 dense region; also the dense baseline): one
-// 256-thread workgroup per state holds S in registers, so S is read once and
-// written once: S <- alpha S + k w^T, o = alpha S_{t-1}^T q + <k, q> w.
+// Dense states (SinkState 4.4 dense region; also the dense baseline) are
+// stored transposed, H = S^T, row-major [d_v][d_k].  Row j of H is column j
+// of S, and everything the step does to it depends on that row alone:
+//   o_j = alpha <H_j, q> + <k, q> w_j,  w_j = v_j or beta (v_j - alpha <H_j, k>),
+//   H_j <- alpha H_j + w_j k.
+// So the dense kernel is a pure stream: one wavefront per state reads a
+// batch of rows (P lanes per row, float4 per lane), reduces each row inside
+// its lane group, and writes the rows back; nothing is held across rows and
+// no workgroup barrier is needed.
 #include "ss_internal.h"
 #include "ss_wave.h"
 
@@ -27,47 +34,24 @@ namespace ss {
 
 namespace {
 
-template <int P, bool DELTA>
-__device__ __forceinline__ void stream_pairs(const float *__restrict__ X, const float *__restrict__ Y,
-                                             const float *__restrict__ Wt, int cnt, int dk, int dv, int grp,
-                                             int col, bool kin, bool vin, float4 q4, float4 k4, float4 &acc,
-                                             float4 &acck) {
-  constexpr int G = 64 / P;
-  constexpr int UN = 2;
-  for (int i0 = 0; i0 < cnt; i0 += G * UN) {
-    float4 x[UN], y[UN];
-    float wt[UN];
-#pragma unroll
-    for (int j = 0; j < UN; ++j) {
-      const int i = i0 + j * G + grp;
-      const bool ok = i < cnt;
-      x[j] = (ok && kin) ? ld4(X + (int64_t)i * dk + 4 * col) : zero4();
-      y[j] = (ok && vin) ? ld4(Y + (int64_t)i * dv + 4 * col) : zero4();
-      wt[j] = ok ? Wt[i] : 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < UN; ++j) {
-      const float cq = group_sum<P>(dot4(x[j], q4)) * wt[j];
-      acc = fma4(cq, y[j], acc);
-      if constexpr (DELTA) {
-        const float ck = group_sum<P>(dot4(x[j], k4)) * wt[j];
-        acck = fma4(ck, y[j], acck);
-      }
-    }
-  }
-}
-
-template <int P, bool RO, bool ANYDELTA>
+// ---------------------------------------------------------------------------
+// factored states
+// ---------------------------------------------------------------------------
+template <int P, int UN, bool RO, bool ANYDELTA>
 __global__ __launch_bounds__(256) void k_decode_factored(DecodeArgs a) {
+  constexpr int G = 64 / P;
   const int lane = threadIdx.x & 63;
   const int64_t s = (int64_t)blockIdx.x * 4 + uniform(threadIdx.x >> 6);
   if (s >= a.N) return;
   const int grp = lane / P, col = lane % P;
   const int dk = a.dk, dv = a.dv, K = a.K;
+  const bool kin = col < (dk >> 2), vin = col < (dv >> 2);
   const Meta m = a.meta[s];
   const uint32_t packed = (uint32_t)uniform((int)m.packed);
   const uint32_t flags = meta_flags(packed);
-  if (flags & FLAG_DENSE) return;
+  if (flags & FLAG_DENSE) return;  // the dense-region kernel serves this state
+  const float4 q4 = kin ? ld4(a.q + s * dk + 4 * col) : zero4();
+  const float4 k4 = (!RO && kin) ? ld4(a.k + s * dk + 4 * col) : zero4();
   const bool delta = ANYDELTA && !RO && (flags & FLAG_DELTA);
   const int ra = meta_ra(packed), rf = meta_rf(packed), n = meta_n(packed);
   const int off_a = uniform(m.off_a), off_f = uniform(m.off_f);
@@ -79,25 +63,41 @@ __global__ __launch_bounds__(256) void k_decode_factored(DecodeArgs a) {
     }
     return;
   }
-  const bool kin = col < (dk >> 2), vin = col < (dv >> 2);
-  const float4 q4 = kin ? ld4(a.q + s * dk + 4 * col) : zero4();
-  const float4 k4 = (!RO && kin) ? ld4(a.k + s * dk + 4 * col) : zero4();
+  const int rr = ra + rf, T = rr + n;
+  const int64_t pad0 = s * (int64_t)K - rr;  // pad slot of list index i is pad0 + i
   float4 acc = zero4(), acck = zero4();
-  const float *pk = a.pk + s * (int64_t)K * dk;
-  const float *pw = a.pw + s * (int64_t)K * dv;
-  const float *pc = a.pc + s * (int64_t)K;
-  if (delta) {
-    stream_pairs<P, true>(a.act.u + (int64_t)off_a * dk, a.act.v + (int64_t)off_a * dv, a.act.s + off_a, ra, dk, dv,
-                          grp, col, kin, vin, q4, k4, acc, acck);
-    stream_pairs<P, true>(a.frz.u + (int64_t)off_f * dk, a.frz.v + (int64_t)off_f * dv, a.frz.s + off_f, rf, dk, dv,
-                          grp, col, kin, vin, q4, k4, acc, acck);
-    stream_pairs<P, true>(pk, pw, pc, n, dk, dv, grp, col, kin, vin, q4, k4, acc, acck);
-  } else {
-    stream_pairs<P, false>(a.act.u + (int64_t)off_a * dk, a.act.v + (int64_t)off_a * dv, a.act.s + off_a, ra, dk, dv,
-                           grp, col, kin, vin, q4, k4, acc, acck);
-    stream_pairs<P, false>(a.frz.u + (int64_t)off_f * dk, a.frz.v + (int64_t)off_f * dv, a.frz.s + off_f, rf, dk,
-                           dv, grp, col, kin, vin, q4, k4, acc, acck);
-    stream_pairs<P, false>(pk, pw, pc, n, dk, dv, grp, col, kin, vin, q4, k4, acc, acck);
+  for (int i0 = 0; i0 < T; i0 += G * UN) {
+    float4 x[UN], y[UN];
+    float wt[UN];
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const int i = i0 + u * G + grp;
+      const float *xp, *yp, *wp;
+      int64_t c;
+      if (i < ra) {
+        c = off_a + i;
+        xp = a.act.u; yp = a.act.v; wp = a.act.s;
+      } else if (i < rr) {
+        c = off_f + (i - ra);
+        xp = a.frz.u; yp = a.frz.v; wp = a.frz.s;
+      } else {
+        c = pad0 + i;
+        xp = a.pk; yp = a.pw; wp = a.pc;
+      }
+      const bool ok = i < T;
+      x[u] = (ok && kin) ? ld4(xp + c * dk + 4 * col) : zero4();
+      y[u] = (ok && vin) ? ld4(yp + c * dv + 4 * col) : zero4();
+      wt[u] = ok ? wp[c] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const float cq = group_sum<P>(dot4(x[u], q4)) * wt[u];
+      acc = fma4(cq, y[u], acc);
+      if (delta) {
+        const float ck = group_sum<P>(dot4(x[u], k4)) * wt[u];
+        acck = fma4(ck, y[u], acck);
+      }
+    }
   }
   acc = cross_group_sum4<P>(acc);
   const float4 pq = scale4(gamma, acc);
@@ -131,94 +131,80 @@ __global__ __launch_bounds__(256) void k_decode_factored(DecodeArgs a) {
       nm.gamma = gnew;
       nm.packed = meta_pack(ra, rf, n + 1, flags);
       a.meta[s] = nm;
-      const unsigned long long b = decode_bytes(dk, dv, ra + rf, n, delta, false);
+      const unsigned long long b = decode_bytes(dk, dv, rr, n, delta, false);
       __hip_atomic_fetch_add(&a.acct[s & (kAcctSlots - 1)], b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
 
-// Dense state: 256 threads; thread t owns column slice c = t % C4 (float4) of
-// rows g, g + RG, ... with g = t / C4, RG = 256 / C4.
-template <bool RO, int NR>
+// ---------------------------------------------------------------------------
+// dense states, H = S^T stored [d_v][d_k]
+// ---------------------------------------------------------------------------
+template <int P, int UN, bool RO, bool ANYDELTA>
 __global__ __launch_bounds__(256) void k_decode_dense(DenseArgs a) {
-  __shared__ float4 part_q[256];
-  __shared__ float4 part_k[256];
-  __shared__ float4 tot_q[64];
-  __shared__ float4 tot_k[64];
-  __shared__ float sq[256];
-  __shared__ float sk[256];
-  __shared__ float skq;
-  const int t = threadIdx.x;
-  const int dk = a.dk, dv = a.dv;
-  const int C4 = dv >> 2, RG = 256 / C4;
-  const int c = t % C4, g = t / C4;
-  const bool act = t < RG * C4;
+  constexpr int G = 64 / P;
+  const int lane = threadIdx.x & 63;
+  const uint32_t slot = blockIdx.x * 4u + (uint32_t)uniform(threadIdx.x >> 6);
   const uint32_t count = min(a.counters[C_DENSE_COUNT], a.cap_d);
-  for (uint32_t slot = blockIdx.x; slot < count; slot += gridDim.x) {
-    const int64_t s = a.dense_ids[slot];
-    const uint32_t flags = meta_flags(a.meta[s].packed);
-    const bool delta = flags & FLAG_DELTA;
-    float *S = a.dense + (int64_t)slot * dk * dv;
-    __syncthreads();  // LDS of the previous state is no longer read
-    if (t < dk) {
-      sq[t] = a.q[s * dk + t];
-      if (!RO) sk[t] = a.k[s * dk + t];
-    }
-    __syncthreads();
-    float4 reg[NR];
-    float4 pq = zero4(), pk = zero4();
+  if (slot >= count) return;
+  const int grp = lane / P, col = lane % P;
+  const int dk = a.dk, dv = a.dv;
+  const bool kin = col < (dk >> 2);
+  const float *H = a.dense + (int64_t)slot * dk * dv + 4 * col;
+  float *Hw = a.dense + (int64_t)slot * dk * dv + 4 * col;
+  // first batch of rows: depends on the slot only, so it is issued before the id lookup
+  float4 h[UN];
 #pragma unroll
-    for (int j = 0; j < NR; ++j) {
-      const int row = g + j * RG;
-      if (act && row < dk) {
-        reg[j] = ld4(S + (int64_t)row * dv + 4 * c);
-        pq = fma4(sq[row], reg[j], pq);
-        if (!RO && delta) pk = fma4(sk[row], reg[j], pk);
+  for (int u = 0; u < UN; ++u) {
+    const int j = u * G + grp;
+    h[u] = (j < dv && kin) ? ld4(H + (int64_t)j * dk) : zero4();
+  }
+  const int64_t s = uniform(a.dense_ids[slot]);
+  const uint32_t flags = meta_flags((uint32_t)uniform((int)a.meta[s].packed));
+  const bool delta = ANYDELTA && !RO && (flags & FLAG_DELTA);
+  const float4 q4 = kin ? ld4(a.q + s * dk + 4 * col) : zero4();
+  const float4 k4 = (!RO && kin) ? ld4(a.k + s * dk + 4 * col) : zero4();
+  const float al = RO ? 1.f : a.alpha[s];
+  const float be = delta ? a.beta[s] : 0.f;
+  const float kq = RO ? 0.f : group_sum<P>(dot4(k4, q4));
+  const float *vs = RO ? nullptr : a.v + s * dv;
+  float *os = a.o + s * dv;
+  for (int j0 = 0; j0 < dv; j0 += G * UN) {
+    if (j0 > 0) {
+#pragma unroll
+      for (int u = 0; u < UN; ++u) {
+        const int j = j0 + u * G + grp;
+        h[u] = (j < dv && kin) ? ld4(H + (int64_t)j * dk) : zero4();
+      }
+    }
+    float vj[UN];
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const int j = j0 + u * G + grp;
+      vj[u] = (!RO && j < dv) ? vs[j] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const int j = j0 + u * G + grp;
+      const float dq = group_sum<P>(dot4(h[u], q4));
+      float oj;
+      if constexpr (RO) {
+        oj = dq;
       } else {
-        reg[j] = zero4();
-      }
-    }
-    if (act) {
-      part_q[t] = pq;
-      part_k[t] = pk;
-    }
-    if (!RO && t < 64) {  // <k, q> on wave 0
-      float x = 0.f;
-      for (int i = t; i < dk; i += 64) x += sq[i] * sk[i];
-      x = wave_sum(x);
-      if (t == 0) skq = x;
-    }
-    __syncthreads();
-    if (t < C4) {
-      float4 aq = zero4(), ak = zero4();
-      for (int gg = 0; gg < RG; ++gg) {
-        aq = add4(aq, part_q[gg * C4 + t]);
-        if (delta) ak = add4(ak, part_k[gg * C4 + t]);
-      }
-      tot_q[t] = aq;
-      tot_k[t] = ak;
-    }
-    __syncthreads();
-    if constexpr (RO) {
-      if (act && g == 0) st4(a.o + s * dv + 4 * c, tot_q[c]);
-    } else {
-      if (act) {
-        const float al = a.alpha[s];
-        const float4 v4 = ld4(a.v + s * dv + 4 * c);
-        float4 w4 = v4;
-        if (delta) w4 = scale4(a.beta[s], sub4(v4, scale4(al, tot_k[c])));
-#pragma unroll
-        for (int j = 0; j < NR; ++j) {
-          const int row = g + j * RG;
-          if (row < dk) st4(S + (int64_t)row * dv + 4 * c, fma4(sk[row], w4, scale4(al, reg[j])));
+        float w = vj[u];
+        if (delta) {
+          const float dkk = group_sum<P>(dot4(h[u], k4));
+          w = be * (vj[u] - al * dkk);
         }
-        if (g == 0) st4(a.o + s * dv + 4 * c, add4(scale4(al, tot_q[c]), scale4(skq, w4)));
+        oj = fmaf(al, dq, kq * w);
+        if (j < dv && kin) st4(Hw + (int64_t)j * dk, fma4(w, k4, scale4(al, h[u])));
       }
-      if (t == 0) {
-        const unsigned long long b = decode_bytes(dk, dv, 0, 0, delta, true);
-        __hip_atomic_fetch_add(&a.acct[s & (kAcctSlots - 1)], b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      if (col == 0 && j < dv) os[j] = oj;
     }
+  }
+  if (!RO && lane == 0) {
+    const unsigned long long b = decode_bytes(dk, dv, 0, 0, delta, true);
+    __hip_atomic_fetch_add(&a.acct[s & (kAcctSlots - 1)], b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -226,58 +212,57 @@ template <bool RO, bool AD>
 hipError_t decode_factored_p(const DecodeArgs &a, int P, hipStream_t st) {
   const dim3 grid((unsigned)((a.N + 3) / 4)), block(256);
   switch (P) {
-    case 1: hipLaunchKernelGGL((k_decode_factored<1, RO, AD>), grid, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((k_decode_factored<2, RO, AD>), grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((k_decode_factored<4, RO, AD>), grid, block, 0, st, a); break;
-    case 8: hipLaunchKernelGGL((k_decode_factored<8, RO, AD>), grid, block, 0, st, a); break;
-    case 16: hipLaunchKernelGGL((k_decode_factored<16, RO, AD>), grid, block, 0, st, a); break;
-    case 32: hipLaunchKernelGGL((k_decode_factored<32, RO, AD>), grid, block, 0, st, a); break;
-    case 64: hipLaunchKernelGGL((k_decode_factored<64, RO, AD>), grid, block, 0, st, a); break;
+    case 1: hipLaunchKernelGGL((k_decode_factored<1, 1, RO, AD>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_decode_factored<2, 1, RO, AD>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((k_decode_factored<4, 1, RO, AD>), grid, block, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((k_decode_factored<8, 2, RO, AD>), grid, block, 0, st, a); break;
+    case 16: hipLaunchKernelGGL((k_decode_factored<16, 2, RO, AD>), grid, block, 0, st, a); break;
+    case 32: hipLaunchKernelGGL((k_decode_factored<32, 4, RO, AD>), grid, block, 0, st, a); break;
+    case 64: hipLaunchKernelGGL((k_decode_factored<64, 8, RO, AD>), grid, block, 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <bool RO>
-hipError_t decode_dense_nr(const DenseArgs &a, int nr, unsigned grid, hipStream_t st) {
+template <bool RO, bool AD>
+hipError_t decode_dense_p(const DenseArgs &a, int P, unsigned grid, hipStream_t st) {
   const dim3 g(grid), b(256);
-  if (nr <= 1) hipLaunchKernelGGL((k_decode_dense<RO, 1>), g, b, 0, st, a);
-  else if (nr <= 2) hipLaunchKernelGGL((k_decode_dense<RO, 2>), g, b, 0, st, a);
-  else if (nr <= 4) hipLaunchKernelGGL((k_decode_dense<RO, 4>), g, b, 0, st, a);
-  else if (nr <= 8) hipLaunchKernelGGL((k_decode_dense<RO, 8>), g, b, 0, st, a);
-  else if (nr <= 12) hipLaunchKernelGGL((k_decode_dense<RO, 12>), g, b, 0, st, a);
-  else if (nr <= 16) hipLaunchKernelGGL((k_decode_dense<RO, 16>), g, b, 0, st, a);
-  else return hipErrorInvalidValue;
+  switch (P) {
+    case 1: hipLaunchKernelGGL((k_decode_dense<1, 1, RO, AD>), g, b, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_decode_dense<2, 1, RO, AD>), g, b, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((k_decode_dense<4, 2, RO, AD>), g, b, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((k_decode_dense<8, 4, RO, AD>), g, b, 0, st, a); break;
+    case 16: hipLaunchKernelGGL((k_decode_dense<16, 8, RO, AD>), g, b, 0, st, a); break;
+    case 32: hipLaunchKernelGGL((k_decode_dense<32, 8, RO, AD>), g, b, 0, st, a); break;
+    case 64: hipLaunchKernelGGL((k_decode_dense<64, 8, RO, AD>), g, b, 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
-}  // namespace
-
-int lanes_per_pair(int dk, int dv) {
-  const int w = (dk > dv ? dk : dv) >> 2;
+int pow2_at_least(int w) {
   int P = 1;
   while (P < w) P <<= 1;
   return P;
 }
 
-int dense_rows_per_thread(int dk, int dv) {
-  const int C4 = dv >> 2;
-  const int RG = 256 / C4;
-  return (dk + RG - 1) / RG;
-}
+}  // namespace
+
+int lanes_per_pair(int dk, int dv) { return pow2_at_least((dk > dv ? dk : dv) >> 2); }
 
 hipError_t launch_decode_factored(const DecodeArgs &a, bool readonly, bool any_delta, hipStream_t st) {
   if (a.N <= 0) return hipSuccess;
   const int P = lanes_per_pair(a.dk, a.dv);
-  if (readonly) return any_delta ? decode_factored_p<true, true>(a, P, st) : decode_factored_p<true, false>(a, P, st);
+  if (readonly) return decode_factored_p<true, false>(a, P, st);
   return any_delta ? decode_factored_p<false, true>(a, P, st) : decode_factored_p<false, false>(a, P, st);
 }
 
-hipError_t launch_decode_dense(const DenseArgs &a, int64_t grid_upper, bool readonly, hipStream_t st) {
-  if (grid_upper <= 0) return hipSuccess;
-  const unsigned grid = (unsigned)(grid_upper < 4096 ? grid_upper : 4096);
-  const int nr = dense_rows_per_thread(a.dk, a.dv);
-  return readonly ? decode_dense_nr<true>(a, nr, grid, st) : decode_dense_nr<false>(a, nr, grid, st);
+hipError_t launch_decode_dense(const DenseArgs &a, int64_t n_upper, bool readonly, bool any_delta, hipStream_t st) {
+  if (n_upper <= 0) return hipSuccess;
+  const unsigned grid = (unsigned)((n_upper + 3) / 4);
+  const int P = pow2_at_least(a.dk >> 2);
+  if (readonly) return decode_dense_p<true, false>(a, P, grid, st);
+  return any_delta ? decode_dense_p<false, true>(a, P, grid, st) : decode_dense_p<false, false>(a, P, grid, st);
 }
 
 }  // namespace ss

@@ -8,7 +8,7 @@
 //   active arena              components: u [cap][d_k], v [cap][d_v], sigma [cap]
 //   frozen arena              same shape, separate allocation
 //   pad    [N][K]             k [N][K][d_k], w [N][K][d_v], c [N][K] (c = 1/Gamma at insertion)
-//   dense  [cap_d][d_k][d_v]  row-major states of the dense region, ids [cap_d]
+//   dense  [cap_d][d_v][d_k]  states of the dense region stored transposed (H = S^T), ids [cap_d]
 // Each compaction group owns two segments in each arena; a compaction reads
 // the group's current segment and writes the other one.  A state's slice of
 // a segment starts at (segment base + its index within the group * per-state
@@ -130,7 +130,7 @@ struct ScatterArgs {
 
 // launchers (return hipError_t of the launch)
 hipError_t launch_decode_factored(const DecodeArgs &a, bool readonly, bool any_delta, hipStream_t st);
-hipError_t launch_decode_dense(const DenseArgs &a, int64_t grid_upper, bool readonly, hipStream_t st);
+hipError_t launch_decode_dense(const DenseArgs &a, int64_t n_upper, bool readonly, bool any_delta, hipStream_t st);
 hipError_t launch_compact(const CompactArgs &a, hipStream_t st);
 hipError_t launch_materialize(const MaterializeArgs &a, int64_t grid_upper, hipStream_t st);
 hipError_t launch_scatter(const ScatterArgs &a, hipStream_t st);

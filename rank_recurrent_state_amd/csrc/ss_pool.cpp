@@ -21,10 +21,6 @@
 #include "../../include/sinkstate.h"
 #include "ss_internal.h"
 
-namespace ss {
-int dense_rows_per_thread(int dk, int dv);
-}
-
 namespace {
 
 thread_local std::string g_last_error;
@@ -195,8 +191,6 @@ ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipSt
   if (d->pad_slots < 1 || d->pad_slots > 8) return fail(SS_ERR_SHAPE, "pad_slots must be in [1, 8]");
   if (d->r_active < 1 || d->r_active > 8) return fail(SS_ERR_SHAPE, "r_active must be in [1, 8]");
   if (d->r_active + d->pad_slots > ss::kMaxM) return fail(SS_ERR_SHAPE, "r_active + pad_slots must be <= 16");
-  if (ss::dense_rows_per_thread(d->d_k, d->d_v) > 16)
-    return fail(SS_ERR_SHAPE, "dense region: d_k / floor(1024 / d_v) rows per thread must be <= 16");
   if (d->n_groups < 1) return fail(SS_ERR_ARG, "n_groups must be >= 1");
   if (d->max_frozen < 0 || d->max_frozen > 255) return fail(SS_ERR_ARG, "max_frozen must be in [0, 255]");
   if (d->dense_capacity < 0 || d->dense_capacity > N) return fail(SS_ERR_ARG, "dense_capacity must be in [0, N]");
@@ -430,7 +424,7 @@ static ss_status run_decode(ss_pool *p, const float *q, const float *k, const fl
     a.dense_ids = p->dense_ids; a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.o = o;
     a.counters = p->counters; a.acct = p->acct + ss::A_DECODE_DENSE * ss::kAcctSlots;
     e = timed(p, readonly ? SS_KERNEL_READOUT_DENSE : SS_KERNEL_DECODE_DENSE, stream,
-              [&] { return ss::launch_decode_dense(a, p->dense_upper, readonly, stream); });
+              [&] { return ss::launch_decode_dense(a, p->dense_upper, readonly, p->any_delta, stream); });
     if (e != hipSuccess) return hip_fail(e, "decode (dense) launch");
   }
   return SS_OK;
@@ -546,8 +540,12 @@ ss_status ss_state_export(ss_pool *p, const int64_t *ids, int64_t n, void *host_
     auto dl = [&](void *dst, const void *src, size_t bytes) {
       if (e == hipSuccess && bytes) e = hipMemcpy(dst, src, bytes, hipMemcpyDeviceToHost);
     };
-    if (dense) {
-      dl(w, p->dense + (size_t)m.off_a * dk * dv, sizeof(float) * (size_t)dk * dv);
+    if (dense) {  // the region holds H = S^T [d_v][d_k]; the export format is S [d_k][d_v]
+      std::vector<float> H((size_t)dk * dv);
+      dl(H.data(), p->dense + (size_t)m.off_a * dk * dv, sizeof(float) * H.size());
+      float *S = reinterpret_cast<float *>(w);
+      for (int j = 0; j < dv; ++j)
+        for (int i = 0; i < dk; ++i) S[(size_t)i * dv + j] = H[(size_t)j * dk + i];
       w += sizeof(float) * (size_t)dk * dv;
       continue;
     }

@@ -68,7 +68,7 @@ def test_create_rejects_bad_arguments_without_touching_the_gpu(lib):
              ({"pad_slots": 9}, ss.SS_ERR_SHAPE), ({"r_active": 0}, ss.SS_ERR_SHAPE),
              ({"n_groups": 0}, ss.SS_ERR_ARG), ({"max_frozen": 300}, ss.SS_ERR_ARG),
              ({"eps_default": -1.0}, ss.SS_ERR_ARG), ({"dense_capacity": 5}, ss.SS_ERR_ARG),
-             ({"d_k": 256, "d_v": 256}, ss.SS_ERR_SHAPE)]
+             ({"d_k": 260, "d_v": 128}, ss.SS_ERR_SHAPE)]
     for over, expect in cases:
         d = dict(base, **over)
         desc = ss.PoolDesc(*[d[f] for f, _ in ss.PoolDesc._fields_])

@@ -245,3 +245,48 @@ def test_dense_capacity_exhaustion_is_reported():
             torch.cuda.synchronize()
     assert ei.value.status == ss.SS_ERR_CAPACITY
     pool.close()
+
+
+@pytest.mark.parametrize("dk,dv", [(4, 8), (12, 20), (44, 64), (128, 80), (80, 128), (256, 256), (256, 4)])
+def test_dense_path_shapes(dk, dv):
+    """Dense region (stored transposed) on edge shapes: one lane per row (d_k = 4), lane groups with
+    idle lanes (12, 44), a full wavefront per row (256), both rules, ragged state count, readout and
+    decode against the oracle's dense recurrence."""
+    rng = np.random.default_rng(dk * 1000 + dv)
+    N = 37
+    R = np.full(N, 3)
+    off = np.concatenate([[0], np.cumsum(R)]).astype(np.int64)
+    u = rng.standard_normal((int(off[-1]), dk)).astype(np.float32)
+    v = rng.standard_normal((int(off[-1]), dv)).astype(np.float32)
+    sig = np.tile(np.array([2.0, 1.0, 0.5], np.float32), N)
+    rule = (np.arange(N) % 2).astype(np.uint8)
+    eps = np.full(N, 1e-3, np.float32)
+    pool = ss.state_pool_create(N, dk, dv, 8, 8, rule=rule, eps=eps, comp_off=off, u=u, v=v, sigma=sig,
+                                force_dense=True)
+    ids = np.arange(N)
+    o = torch.empty(N, dv, device="cuda")
+    worst = 0.0
+    for t in range(3):
+        q = torch.randn(N, dk, device="cuda")
+        k = torch.nn.functional.normalize(torch.randn(N, dk, device="cuda"), dim=1)
+        vv = torch.randn(N, dv, device="cuda")
+        a = 0.9 + 0.1 * torch.rand(N, device="cuda")
+        b = torch.rand(N, device="cuda")
+        before = ss.state_export(pool, ids)
+        assert all(s["dense"] for s in before)
+        P = oracle_from_export(before, eps, dk, dv, 8, 8)
+        Sn = np.array([np.linalg.norm(reconstruct(s)) for s in before])
+        qn = np.linalg.norm(q.cpu().numpy(), axis=1)
+        ss.readout(pool, q, o)
+        torch.cuda.synchronize()
+        worst = max(worst, float(rel_out_err(o.cpu().numpy(), P.readout(q.cpu().numpy()), Sn, qn).max()))
+        ss.decode_step(pool, q, k, vv, a, b, o)
+        torch.cuda.synchronize()
+        oo = P.decode(q.cpu().numpy(), k.cpu().numpy(), vv.cpu().numpy(), a.cpu().numpy(), b.cpu().numpy())
+        Sn = np.array([np.linalg.norm(P.reconstruct(j)) for j in range(N)])
+        worst = max(worst, float(rel_out_err(o.cpu().numpy(), oo, Sn, qn).max()))
+        for j, st in enumerate(ss.state_export(pool, ids)):
+            So = P.reconstruct(j)
+            worst = max(worst, float(np.linalg.norm(reconstruct(st) - So) / np.linalg.norm(So)))
+    pool.close()
+    assert worst <= TOL, (dk, dv, worst)
