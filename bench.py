@@ -46,8 +46,10 @@ def _run_steps(ss, torch, pool, xs, t0, o, ev=None):
         ev[len(xs)].record()
 
 
-def cpu_baseline(w, init, n_sample, n_steps):
-    """The fp64 oracle, as it stands, on a bounded sample of the same workload, all host cores."""
+def cpu_baseline(w, init, n_sample, n_steps, device="cpu"):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload, all host cores.
+    Inputs are drawn per step for the sampled states on `device` and copied to the host (not timed);
+    only the oracle calls are timed."""
     import numpy as np
     from oracle import OraclePool, schedule_due
     from oracle.oracle import OracleState, max_threads
@@ -62,15 +64,12 @@ def cpu_baseline(w, init, n_sample, n_steps):
         P.set_state(j, OracleState(init["u"][a:b].astype(np.float64), init["v"][a:b].astype(np.float64),
                                    init["sigma"][a:b].astype(np.float64), rule=int(init["rule"][s]),
                                    eps=float(init["eps"][s])))
-    gen = W.StepInputs(w, device="cpu")
-    xs = []
-    for t in range(1, n_steps + 1):
-        x = gen.generate(t, states=ids)
-        xs.append({k: v.numpy().astype(np.float64) for k, v in x.items()})
+    gen = W.StepInputs(w, device=device)
     grp = init["group_of_state"][ids]
     nthreads = max_threads()
     t_dec = t_cmp = 0.0
-    for t, x in enumerate(xs, start=1):
+    for t in range(1, n_steps + 1):
+        x = {k: v.cpu().numpy().astype(np.float64) for k, v in gen.generate(t, states=ids).items()}
         a = time.perf_counter()
         P.decode(x["q"], x["k"], x["v"], x["alpha"], x["beta"], nthreads=nthreads)
         b = time.perf_counter()
@@ -82,9 +81,38 @@ def cpu_baseline(w, init, n_sample, n_steps):
     tot = t_dec + t_cmp
     return {"value": len(ids) * n_steps / tot, "unit": "state-steps/s", "cores": nthreads, "kind": "oracle",
             "sample": f"{len(ids)} states drawn from the same {w.n_states}-state workload, steps 1-{n_steps} "
-                      f"(decode + staggered compaction), fp64, OpenMP over states",
+                      f"(decode + staggered compaction + promotion), fp64, OpenMP over states",
             "decode_state_steps_per_s": len(ids) * n_steps / t_dec, "seconds": tot,
             "cpu": _cpu_model()}
+
+
+def copy_calibration(gib=4, reps=5):
+    """A plain device-to-device copy of known size, for scaling HBM byte counters."""
+    import torch
+    n = int(gib * (1 << 30)) // 4
+    a = torch.ones(n, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": 4 * n, "copy_calibration_bytes_written": 4 * n,
+                      "reps": reps}), flush=True)
+
+
+def _traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None when the decode
+    kernel's source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in ("ss_decode.hip", "ss_internal.h", "ss_wave.h"):
+        h.update(open(os.path.join(ROOT, "rank_recurrent_state_amd", "csrc", f), "rb").read())
+    if rec.get("kernel") != kernel or rec.get("decode_source_sha256") != h.hexdigest():
+        return None
+    return rec["traffic_bytes_per_launch"]
 
 
 def _cpu_model():
@@ -106,14 +134,20 @@ def main():
     ap.add_argument("--requests", type=int, default=None, help="override the number of requests")
     ap.add_argument("--chunk", type=int, default=64, help="steps whose inputs are generated at once")
     ap.add_argument("--dense-steps", type=int, default=64, help="steps of the dense HIP baseline (0: skip)")
-    ap.add_argument("--cpu-sample", type=int, default=16384)
-    ap.add_argument("--cpu-steps", type=int, default=16)
+    ap.add_argument("--cpu-sample", type=int, default=65536)
+    ap.add_argument("--cpu-steps", type=int, default=64)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 4 GiB device copy (for scaling rocprof byte counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (the path shards by request "
                                    "with no exchange step, see DESIGN.md)"}))
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import numpy as np
     import torch
@@ -226,7 +260,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, init, args.cpu_sample, args.cpu_steps)
+        cpu = cpu_baseline(w, init, args.cpu_sample, args.cpu_steps, device="cuda")
         log(f"[bench] cpu baseline {cpu['value']:.3e} state-steps/s on {cpu['cores']} threads ({cpu['seconds']:.1f}s)")
 
     out = {
@@ -246,7 +280,8 @@ def main():
                                f"{w.n_heads} heads, K={w.K}, r={w.r}, stagger={w.stagger}, whole {K_steps}-step job",
                    "n_states": w.n_states, "d_k": w.d_k, "d_v": w.d_v},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": ach / HBM_PEAK_GBS, "traffic": None},
+                     "frac": ach / HBM_PEAK_GBS, "traffic": _traffic(dom, w.name),
+                     "algorithmic_bytes_per_launch": bytes_k[dom] / max(1, kn[dom])},
         "cpu_baseline": cpu,
         "decode_step": {"state_steps_per_s": w.n_states * K_steps / (decode_ms / 1e3) if decode_ms else None,
                         "achieved_GBs": decode_bytes / (decode_ms / 1e3) / 1e9 if decode_ms else None,

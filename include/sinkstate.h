@@ -102,6 +102,7 @@ enum {
   SS_KERNEL_READOUT_DENSE = 3,
   SS_KERNEL_COMPACT = 4,
   SS_KERNEL_MATERIALIZE = 5,
+  SS_KERNEL_DENSE_FOLD = 6,
   SS_KERNEL_COUNT = 8
 };
 
@@ -140,7 +141,10 @@ ss_status ss_state_pool_destroy(ss_pool *pool);
 /* One decode step of every state ([SS] 4.2 "(i) Buffering", 4.4 fused decode
  * kernel): Gamma <- alpha Gamma; w = v (scalar) or beta (v - alpha S_{t-1}^T k)
  * (delta); append (k, w, 1/Gamma) to the pad; o = S_t^T q, read after the
- * update.  Dense states run S <- alpha S + k w^T, o = S^T q.
+ * update.  States of the dense region are buffered the same way: the
+ * region holds H = S^T and a pad, a step appends to the pad, and the step
+ * that fills the pad folds it into H (exact algebra, no truncation).  In a
+ * force_dense pool (the dense baseline) every step runs S <- alpha S + k w^T.
  * q, k: [N][d_k]; v, o: [N][d_v]; alpha: [N] in (0, 1]; beta: [N], may be
  * NULL when no state uses the delta rule.  A factored state whose pad is
  * already full poisons the pool (SS_ERR_STATE on the next call): compact its
@@ -162,7 +166,8 @@ ss_status ss_readout(ss_pool *pool, const float *q, float *o, hipStream_t stream
  * the merged list become active, the rest frozen; the pad empties and Gamma
  * resets to 1.  The result is written to the group's other segment.  With
  * promote_on_compact, a state left with more than L components moves to the
- * dense region ([SS] 4.4). */
+ * dense region ([SS] 4.4).  Dense states of the group get a non-empty pad
+ * folded into H. */
 ss_status ss_compact(ss_pool *pool, int32_t group, hipStream_t stream);
 
 /* Staggered schedule ([SS] 4.2 "Staggered compaction across layers"): the
@@ -174,8 +179,8 @@ ss_status ss_schedule_due(const ss_pool *pool, int64_t step, int32_t *out, int32
 /* Test hook: copy states `ids` (host array) to host memory in the canonical
  * form, effective weights (Gamma folded in).  Waits on `stream`.  Layout per
  * state, packed in id order:
- *   int32 header[8] = {id_lo, dense, n_components, n_active, n_pad, rule, 0, 0}
- *   then, if dense: float S[d_k][d_v];
+ *   int32 header[8] = {id_lo, dense, n_components, n_active, n_pad, rule, dense_pad, 0}
+ *   then, if dense: float S[d_k][d_v] (dense_pad buffered slots folded in, on the host, in double);
  *   else: float sigma[n_components], u[n_components][d_k], v[n_components][d_v],
  *         c[n_pad], k[n_pad][d_k], w[n_pad][d_v]
  * Components are in stored order: the n_active active ones first, then the
@@ -198,13 +203,24 @@ ss_status ss_pool_timing(ss_pool *pool, int32_t enable);
  * form (d_k + d_v + 1 values each) is larger than the dense d_k d_v ([SS] 4.4). */
 int32_t ss_dense_rank_limit(int32_t d_k, int32_t d_v);
 
-/* Algorithmic bytes one decode_step moves for one state: a factored state
- * with n_comp components and n_pad filled slots reads its 16-byte record,
- * all components and slots (4 (d_k + d_v + 1) bytes each), q, k, v, alpha
- * (and beta for the delta rule), and writes the record, one slot and o.  A
- * dense state reads and writes d_k d_v floats instead of the factors. */
-uint64_t ss_decode_bytes_per_state(int32_t d_k, int32_t d_v, int32_t n_comp, int32_t n_pad, int32_t rule,
-                                   int32_t dense);
+/* How a state is decoded, for ss_decode_bytes_per_state. */
+enum {
+  SS_DECODE_FACTORED = 0,       /* factors + pad */
+  SS_DECODE_DENSE_BUFFERED = 1, /* dense region of a factored pool: H + pad */
+  SS_DECODE_DENSE_PLAIN = 2     /* force_dense pool (the dense baseline) */
+};
+
+/* Algorithmic bytes one decode_step moves for one state with n_comp
+ * components and n_pad filled slots before the step (K = pad_slots).
+ * FACTORED: reads the 16-byte record, all components and slots
+ * (4 (d_k + d_v + 1) bytes each), q, k, v, alpha (and beta for the delta
+ * rule); writes the record, one slot and o.  DENSE_BUFFERED: reads the
+ * record, the slot id, H (4 d_k d_v bytes), the slots and the inputs;
+ * writes the record, o, and one slot, or H when the step fills the pad
+ * (n_pad + 1 >= K).  DENSE_PLAIN: reads and writes H every step.  Returns 0
+ * for an unknown kind. */
+uint64_t ss_decode_bytes_per_state(int32_t d_k, int32_t d_v, int32_t pad_slots, int32_t n_comp, int32_t n_pad,
+                                   int32_t rule, int32_t kind);
 
 const char *ss_status_string(ss_status status);
 const char *ss_last_error(void);

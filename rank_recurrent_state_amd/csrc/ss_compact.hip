@@ -35,12 +35,6 @@ constexpr float kTolJ = 1e-6f;   // Jacobi: rotate while |a_i.a_j| > tol |a_i| |
 constexpr int kMaxSweeps = 16;
 constexpr int kLdsPerWave = 1152;
 
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // In-place CGS2 thin QR of the register-resident columns a[0..m).  R goes to
 // LDS, column-major 16 x 16: Rm[j * 16 + i] = R(i, j).
 template <int NS>
@@ -537,6 +531,30 @@ __global__ __launch_bounds__(256) void k_scatter(ScatterArgs a) {
   }
 }
 
+__global__ __launch_bounds__(256) void k_prune_factored(const int32_t *src, const uint32_t *src_count, int32_t *dst,
+                                                        uint32_t *dst_count, const Meta *meta) {
+  const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  int32_t s = -1;
+  bool keep = false;
+  if (i < *src_count) {
+    s = src[i];
+    keep = !(meta_flags(meta[s].packed) & FLAG_DENSE);
+  }
+  const unsigned long long mask = __builtin_amdgcn_ballot_w64(keep);
+  if (mask == 0ull) return;
+  uint32_t base = 0;
+  if (lane == 0)
+    base = __hip_atomic_fetch_add(dst_count, (uint32_t)__builtin_popcountll(mask), __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+  base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+  if (keep) dst[base + __builtin_popcountll(mask & ((1ull << lane) - 1ull))] = s;
+}
+
+__global__ void k_copy_count(const uint32_t *src, uint32_t *dst) {
+  if (threadIdx.x == 0) *dst = *src;
+}
+
 __global__ void k_zero_u32(uint32_t *p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0u;
@@ -566,6 +584,18 @@ hipError_t launch_materialize(const MaterializeArgs &a, int64_t grid_upper, hipS
 hipError_t launch_scatter(const ScatterArgs &a, hipStream_t st) {
   if (a.N <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_scatter, dim3((unsigned)((a.N + 3) / 4)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prune_factored(const int32_t *src, const uint32_t *src_count, int64_t n_upper, int32_t *dst,
+                                 uint32_t *dst_count, const Meta *meta, uint32_t *host_count, hipStream_t st) {
+  if (n_upper > 0) {
+    hipLaunchKernelGGL(k_prune_factored, dim3((unsigned)((n_upper + 255) / 256)), dim3(256), 0, st, src, src_count,
+                       dst, dst_count, meta);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_copy_count, dim3(1), dim3(64), 0, st, dst_count, host_count);
   return hipGetLastError();
 }
 

@@ -50,6 +50,8 @@ enum Counter : int {
   C_ERR_DENSE_CAP = 3, // promotion found the dense region full (also host-mapped)
   C_CAP_TRUNC = 4,     // frozen components dropped because max_frozen was reached
   C_PROMOTIONS = 5,    // total promotions
+  C_FACT0 = 6,         // length of factored-state list 0
+  C_FACT1 = 7,         // length of factored-state list 1
   C_N = 8
 };
 
@@ -60,6 +62,8 @@ struct Arena {
 struct DecodeArgs {
   int64_t N;
   int dk, dv, K;
+  const int32_t *fact_ids;     // ids of the factored states (dense ones are served by the dense kernel)
+  const uint32_t *fact_count;  // its length (device)
   Meta *meta;
   Arena act, frz;
   float *pk, *pw, *pc;
@@ -71,11 +75,14 @@ struct DecodeArgs {
 };
 
 struct DenseArgs {
-  int dk, dv;
+  int dk, dv, K;
   uint32_t cap_d;
   Meta *meta;
   float *dense;
   const int32_t *dense_ids;
+  float *pk, *pw, *pc;         // pads of the buffered dense region (nullptr for the plain baseline)
+  const int32_t *members;      // fold mode: state ids of a compaction group
+  int32_t n_members;
   const float *q, *k, *v, *alpha, *beta;
   float *o;
   uint32_t *counters;
@@ -130,22 +137,34 @@ struct ScatterArgs {
 
 // launchers (return hipError_t of the launch)
 hipError_t launch_decode_factored(const DecodeArgs &a, bool readonly, bool any_delta, hipStream_t st);
+// dense region: buffered (pads present) or plain (the dense baseline)
 hipError_t launch_decode_dense(const DenseArgs &a, int64_t n_upper, bool readonly, bool any_delta, hipStream_t st);
+// fold the pads of the dense states among a.members into their H (compaction of the dense region)
+hipError_t launch_dense_fold(const DenseArgs &a, hipStream_t st);
 hipError_t launch_compact(const CompactArgs &a, hipStream_t st);
 hipError_t launch_materialize(const MaterializeArgs &a, int64_t grid_upper, hipStream_t st);
 hipError_t launch_scatter(const ScatterArgs &a, hipStream_t st);
 hipError_t launch_zero_u32(uint32_t *p, int n, hipStream_t st);
+// drop the states that have become dense from a factored-state list (src -> dst, dst_count zeroed by
+// the caller), then copy the new length to a host-visible word
+hipError_t launch_prune_factored(const int32_t *src, const uint32_t *src_count, int64_t n_upper, int32_t *dst,
+                                 uint32_t *dst_count, const Meta *meta, uint32_t *host_count, hipStream_t st);
+
+// how a state is decoded
+enum DecodeKind : int { KIND_FACTORED = 0, KIND_DENSE_BUFFERED = 1, KIND_DENSE_PLAIN = 2 };
 
 // algorithmic bytes of one decode step of one state (kept identical to the
-// in-kernel accounting)
-__host__ __device__ inline unsigned long long decode_bytes(int dk, int dv, int ncomp, int npad, bool delta,
-                                                           bool dense) {
-  unsigned long long in = 4ull * (2ull * dk + dv + 1 + (delta ? 1 : 0));
-  if (dense) {
-    // record + slot id, state read and written, inputs, output
-    return 16ull + 4ull + 8ull * (unsigned long long)dk * dv + in + 4ull * dv;
-  }
-  unsigned long long comp = 4ull * (unsigned long long)(dk + dv + 1);
+// in-kernel accounting).  n_pad is the pad fill before the step; a buffered
+// dense state whose pad fills in this step rewrites H instead of a pad slot.
+__host__ __device__ inline unsigned long long decode_bytes(int dk, int dv, int K, int ncomp, int npad, bool delta,
+                                                           int kind) {
+  const unsigned long long in = 4ull * (2ull * dk + dv + 1 + (delta ? 1 : 0));
+  const unsigned long long comp = 4ull * (unsigned long long)(dk + dv + 1);
+  const unsigned long long st = 4ull * (unsigned long long)dk * dv;
+  if (kind == KIND_DENSE_PLAIN)  // record + slot id, state read and written, inputs, output
+    return 16ull + 4ull + 2ull * st + in + 4ull * dv;
+  if (kind == KIND_DENSE_BUFFERED)  // record read+write, slot id, H and the pad read, inputs, output, slot or H written
+    return 32ull + 4ull + st + comp * (unsigned long long)npad + in + 4ull * dv + (npad + 1 >= K ? st : comp);
   // record read+write, components and pad slots read, inputs, one slot written, output
   return 32ull + comp * (unsigned long long)(ncomp + npad) + in + comp + 4ull * dv;
 }

@@ -30,7 +30,8 @@ ss_status fail(ss_status st, const std::string &msg) {
   return st;
 }
 
-enum HostFlag { HF_PAD = 0, HF_DENSE_CAP = 1, HF_N = 4 };
+// host-mapped words: error flags raised by kernels, and the length of the factored-state list
+enum HostFlag { HF_PAD = 0, HF_DENSE_CAP = 1, HF_FACT = 2, HF_N = 4 };
 
 }  // namespace
 
@@ -52,9 +53,13 @@ struct ss_pool {
   float *dense = nullptr;
   int32_t *dense_ids = nullptr;
   int32_t *promote_list = nullptr;
+  int32_t *fact_ids[2] = {nullptr, nullptr};  // factored-state lists (ping-pong), lengths in counters
+  int fact_par = 0;
+  int64_t fact_upper = 0;                     // host upper bound of the current list's length
   uint32_t *counters = nullptr;
   unsigned long long *acct = nullptr;  // [A_N][kAcctSlots] accounting (see ss::Acct)
-  uint32_t *hflags = nullptr;          // host-mapped error flags
+  uint32_t *hflags = nullptr;          // host-mapped words (HostFlag)
+  uint32_t fact_count_host = 0;        // staging for the initial list length
   uint32_t *hflags_dev = nullptr;
   std::vector<void *> dev_allocs;
   int64_t reserved = 0;
@@ -160,9 +165,10 @@ int32_t ss_dense_rank_limit(int32_t d_k, int32_t d_v) {
   return (int32_t)(((int64_t)d_k * d_v) / ((int64_t)d_k + d_v));
 }
 
-uint64_t ss_decode_bytes_per_state(int32_t d_k, int32_t d_v, int32_t n_comp, int32_t n_pad, int32_t rule,
-                                   int32_t dense) {
-  return ss::decode_bytes(d_k, d_v, n_comp, n_pad, rule == SS_RULE_DELTA, dense != 0);
+uint64_t ss_decode_bytes_per_state(int32_t d_k, int32_t d_v, int32_t pad_slots, int32_t n_comp, int32_t n_pad,
+                                   int32_t rule, int32_t kind) {
+  if (kind < SS_DECODE_FACTORED || kind > SS_DECODE_DENSE_PLAIN) return 0;
+  return ss::decode_bytes(d_k, d_v, pad_slots, n_comp, n_pad, rule == SS_RULE_DELTA, kind);
 }
 
 const char *ss_status_string(ss_status st) {
@@ -297,6 +303,8 @@ ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipSt
     chk(dalloc(p, &p->pw, (size_t)N * K * dv));
     chk(dalloc(p, &p->pc, (size_t)N * K));
     chk(dalloc(p, &p->promote_list, N));
+    chk(dalloc(p, &p->fact_ids[0], N));
+    chk(dalloc(p, &p->fact_ids[1], N));
   }
   chk(dalloc(p, &p->dense, (size_t)cap_d * dk * dv));
   chk(dalloc(p, &p->dense_ids, cap_d));
@@ -362,6 +370,15 @@ ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipSt
   up(p->eps, epsv.data(), N * sizeof(float));
   if (e == hipSuccess) e = hipMemsetAsync(p->counters, 0, ss::C_N * sizeof(uint32_t), stream);
   if (e == hipSuccess) e = hipMemsetAsync(p->acct, 0, ss::A_N * ss::kAcctSlots * sizeof(unsigned long long), stream);
+  std::vector<int32_t> fact;
+  if (factored) {
+    fact.reserve(N);
+    for (int64_t s2 = 0; s2 < N; ++s2)
+      if (offp[s2 + 1] - offp[s2] <= L) fact.push_back((int32_t)s2);
+    p->fact_count_host = (uint32_t)fact.size();
+    up(p->fact_ids[0], fact.data(), fact.size() * sizeof(int32_t));
+    up(p->counters + ss::C_FACT0, &p->fact_count_host, sizeof(uint32_t));
+  }
   if (e == hipSuccess) {
     ss::ScatterArgs sa{};
     sa.N = N; sa.dk = dk; sa.dv = dv; sa.r = r; sa.L = L; sa.fcap = fcap; sa.force_dense = p->force_dense;
@@ -387,6 +404,8 @@ ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipSt
     return hip_fail(e, "pool upload");
   }
   p->dense_upper = n_dense0;
+  p->fact_upper = factored ? (int64_t)fact.size() : 0;
+  if (p->hflags) p->hflags[HF_FACT] = (uint32_t)p->fact_upper;
   *out = p;
   return SS_OK;
 }
@@ -408,9 +427,14 @@ static ss_status run_decode(ss_pool *p, const float *q, const float *k, const fl
   if (!readonly && (!k || !v || !alpha)) return fail(SS_ERR_ARG, "k, v and alpha are required");
   if (!readonly && p->any_delta && !beta) return fail(SS_ERR_ARG, "beta is required: the pool has delta-rule states");
   hipError_t e = hipSuccess;
-  if (!p->force_dense) {
+  if (p->hflags) {  // a stale value is still an upper bound: the list only shrinks
+    const uint32_t seen = ((const volatile uint32_t *)p->hflags)[HF_FACT];
+    p->fact_upper = std::min<int64_t>(p->fact_upper, seen);
+  }
+  if (!p->force_dense && p->fact_upper > 0) {
     ss::DecodeArgs a{};
-    a.N = p->N; a.dk = p->dk; a.dv = p->dv; a.K = p->K; a.meta = p->meta; a.act = p->act; a.frz = p->frz;
+    a.N = p->fact_upper; a.dk = p->dk; a.dv = p->dv; a.K = p->K; a.meta = p->meta; a.act = p->act; a.frz = p->frz;
+    a.fact_ids = p->fact_ids[p->fact_par]; a.fact_count = p->counters + ss::C_FACT0 + p->fact_par;
     a.pk = p->pk; a.pw = p->pw; a.pc = p->pc; a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.o = o;
     a.counters = p->counters; a.acct = p->acct + ss::A_DECODE_FACTORED * ss::kAcctSlots;
     a.hflag = p->hflags_dev + HF_PAD;
@@ -420,8 +444,9 @@ static ss_status run_decode(ss_pool *p, const float *q, const float *k, const fl
   }
   if (p->dense_upper > 0) {
     ss::DenseArgs a{};
-    a.dk = p->dk; a.dv = p->dv; a.cap_d = (uint32_t)p->cap_d; a.meta = p->meta; a.dense = p->dense;
-    a.dense_ids = p->dense_ids; a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.o = o;
+    a.dk = p->dk; a.dv = p->dv; a.K = p->K; a.cap_d = (uint32_t)p->cap_d; a.meta = p->meta; a.dense = p->dense;
+    a.dense_ids = p->dense_ids; a.pk = p->pk; a.pw = p->pw; a.pc = p->pc;
+    a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.o = o;
     a.counters = p->counters; a.acct = p->acct + ss::A_DECODE_DENSE * ss::kAcctSlots;
     e = timed(p, readonly ? SS_KERNEL_READOUT_DENSE : SS_KERNEL_DECODE_DENSE, stream,
               [&] { return ss::launch_decode_dense(a, p->dense_upper, readonly, p->any_delta, stream); });
@@ -454,6 +479,15 @@ ss_status ss_compact(ss_pool *p, int32_t group, hipStream_t stream) {
     if (p->group_size[g] == 0) continue;
     hipError_t e = ss::launch_zero_u32(p->counters + ss::C_PROMOTE_COUNT, 1, stream);
     if (e != hipSuccess) return hip_fail(e, "compact launch");
+    if (p->dense_upper > 0) {  // dense members: fold a non-empty pad into H
+      ss::DenseArgs da{};
+      da.dk = p->dk; da.dv = p->dv; da.K = p->K; da.cap_d = (uint32_t)p->cap_d; da.meta = p->meta;
+      da.dense = p->dense; da.dense_ids = p->dense_ids; da.pk = p->pk; da.pw = p->pw; da.pc = p->pc;
+      da.members = p->members + p->group_start[g]; da.n_members = (int32_t)p->group_size[g];
+      da.counters = p->counters; da.acct = p->acct;
+      e = timed(p, SS_KERNEL_DENSE_FOLD, stream, [&] { return ss::launch_dense_fold(da, stream); });
+      if (e != hipSuccess) return hip_fail(e, "dense fold launch");
+    }
     const int src = p->parity[g], dst = 1 - src;
     ss::CompactArgs a{};
     a.dk = p->dk; a.dv = p->dv; a.K = p->K; a.r = p->r; a.L = p->L; a.promote = p->promote; a.fcap = p->fcap;
@@ -479,6 +513,16 @@ ss_status ss_compact(ss_pool *p, int32_t group, hipStream_t stream) {
       p->dense_upper = std::min<int64_t>(p->cap_d, p->dense_upper + p->group_size[g]);
     }
     p->parity[g] = dst;
+  }
+  if (p->promote && p->fact_upper > 0) {  // promoted states leave the factored-state list
+    const int cur = p->fact_par, nxt = 1 - cur;
+    hipError_t e = ss::launch_zero_u32(p->counters + ss::C_FACT0 + nxt, 1, stream);
+    if (e == hipSuccess)
+      e = ss::launch_prune_factored(p->fact_ids[cur], p->counters + ss::C_FACT0 + cur, p->fact_upper,
+                                    p->fact_ids[nxt], p->counters + ss::C_FACT0 + nxt, p->meta,
+                                    p->hflags_dev + HF_FACT, stream);
+    if (e != hipSuccess) return hip_fail(e, "factored-list launch");
+    p->fact_par = nxt;
   }
   p->compact_calls++;
   return SS_OK;
@@ -533,19 +577,30 @@ ss_status ss_state_export(ss_pool *p, const int64_t *ids, int64_t n, void *host_
     const uint32_t pkd = m.packed;
     const bool dense = ss::meta_flags(pkd) & ss::FLAG_DENSE;
     const int ra = dense ? 0 : ss::meta_ra(pkd), rf = dense ? 0 : ss::meta_rf(pkd), nn = dense ? 0 : ss::meta_n(pkd);
+    const int dpad = (dense && !p->force_dense) ? (int)ss::meta_n(pkd) : 0;
     int32_t hdr[8] = {(int32_t)ids[i], dense ? 1 : 0, ra + rf, ra, nn,
-                      (ss::meta_flags(pkd) & ss::FLAG_DELTA) ? 1 : 0, 0, 0};
+                      (ss::meta_flags(pkd) & ss::FLAG_DELTA) ? 1 : 0, dpad, 0};
     std::memcpy(w, hdr, sizeof(hdr));
     w += sizeof(hdr);
     auto dl = [&](void *dst, const void *src, size_t bytes) {
       if (e == hipSuccess && bytes) e = hipMemcpy(dst, src, bytes, hipMemcpyDeviceToHost);
     };
-    if (dense) {  // the region holds H = S^T [d_v][d_k]; the export format is S [d_k][d_v]
-      std::vector<float> H((size_t)dk * dv);
+    if (dense) {  // the region holds H = S^T [d_v][d_k] and a pad; the export format is S [d_k][d_v]
+      const int np = p->force_dense ? 0 : ss::meta_n(pkd);
+      std::vector<float> H((size_t)dk * dv), PK((size_t)np * dk), PW((size_t)np * dv), PC(np);
       dl(H.data(), p->dense + (size_t)m.off_a * dk * dv, sizeof(float) * H.size());
+      dl(PK.data(), p->pk + (size_t)ids[i] * K * dk, sizeof(float) * PK.size());
+      dl(PW.data(), p->pw + (size_t)ids[i] * K * dv, sizeof(float) * PW.size());
+      dl(PC.data(), p->pc + (size_t)ids[i] * K, sizeof(float) * PC.size());
+      if (e != hipSuccess) return hip_fail(e, "export copy");
+      const double g = p->force_dense ? 1.0 : (double)m.gamma;
       float *S = reinterpret_cast<float *>(w);
-      for (int j = 0; j < dv; ++j)
-        for (int i = 0; i < dk; ++i) S[(size_t)i * dv + j] = H[(size_t)j * dk + i];
+      for (int i2 = 0; i2 < dk; ++i2)
+        for (int j = 0; j < dv; ++j) {
+          double x = H[(size_t)j * dk + i2];
+          for (int t = 0; t < np; ++t) x += (double)PC[t] * PK[(size_t)t * dk + i2] * PW[(size_t)t * dv + j];
+          S[(size_t)i2 * dv + j] = (float)(g * x);
+        }
       w += sizeof(float) * (size_t)dk * dv;
       continue;
     }
@@ -594,8 +649,10 @@ ss_status ss_pool_stats(ss_pool *p, ss_stats *out, hipStream_t stream) {
   for (int64_t s = 0; s < p->N; ++s) {
     const uint32_t pk = meta[s].packed;
     if (ss::meta_flags(pk) & ss::FLAG_DENSE) {
+      const int64_t nn = p->force_dense ? 0 : ss::meta_n(pk);
       out->n_dense++;
-      live += 4ll * p->dk * p->dv + 4;
+      out->pad_entries += nn;
+      live += 4ll * p->dk * p->dv + 4 + comp * nn;
       continue;
     }
     out->n_factored++;

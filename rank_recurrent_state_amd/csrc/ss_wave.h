@@ -76,7 +76,20 @@ __device__ __forceinline__ float4 cross_group_sum4(float4 a) {
 }
 
 __device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+// streaming (read-once) loads: the nontemporal hint keeps them from displacing reused lines
+__device__ __forceinline__ float4 ld4nt(const float *p) {
+  return make_float4(__builtin_nontemporal_load(p), __builtin_nontemporal_load(p + 1), __builtin_nontemporal_load(p + 2),
+                     __builtin_nontemporal_load(p + 3));
+}
+__device__ __forceinline__ float ldnt(const float *p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void st4(float *p, float4 v) { *reinterpret_cast<float4 *>(p) = v; }
+
+// make this lane's LDS writes visible to the other lanes of the wavefront
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 __device__ __forceinline__ float uniformf(float x) {

@@ -57,7 +57,8 @@ class Stats(ctypes.Structure):
     ]
 
 
-KERNELS = ("decode_factored", "decode_dense", "readout_factored", "readout_dense", "compact", "materialize")
+KERNELS = ("decode_factored", "decode_dense", "readout_factored", "readout_dense", "compact", "materialize",
+           "dense_fold")
 
 
 _lib = None
@@ -84,7 +85,7 @@ def load_library():
     lib.ss_pool_timing.argtypes = [vp, ctypes.c_int32]
     lib.ss_dense_rank_limit.argtypes = [ctypes.c_int32, ctypes.c_int32]
     lib.ss_dense_rank_limit.restype = ctypes.c_int32
-    lib.ss_decode_bytes_per_state.argtypes = [ctypes.c_int32] * 6
+    lib.ss_decode_bytes_per_state.argtypes = [ctypes.c_int32] * 7
     lib.ss_decode_bytes_per_state.restype = ctypes.c_uint64
     lib.ss_status_string.argtypes = [ctypes.c_int]
     lib.ss_status_string.restype = ctypes.c_char_p
@@ -135,8 +136,11 @@ def dense_rank_limit(d_k: int, d_v: int) -> int:
     return int(load_library().ss_dense_rank_limit(d_k, d_v))
 
 
-def decode_bytes_per_state(d_k, d_v, n_comp, n_pad, rule, dense) -> int:
-    return int(load_library().ss_decode_bytes_per_state(d_k, d_v, n_comp, n_pad, rule, int(bool(dense))))
+DECODE_FACTORED, DECODE_DENSE_BUFFERED, DECODE_DENSE_PLAIN = 0, 1, 2
+
+
+def decode_bytes_per_state(d_k, d_v, pad_slots, n_comp, n_pad, rule, kind) -> int:
+    return int(load_library().ss_decode_bytes_per_state(d_k, d_v, pad_slots, n_comp, n_pad, rule, int(kind)))
 
 
 class StatePool:
@@ -245,11 +249,11 @@ def state_export(pool: StatePool, ids, stream=None) -> list:
     for _ in range(ids.shape[0]):
         hdr = buf[pos:pos + 32].view(np.int32)
         pos += 32
-        sid, dense, R, ra, n, rule = (int(x) for x in hdr[:6])
+        sid, dense, R, ra, n, rule, dpad = (int(x) for x in hdr[:7])
         if dense:
             S = buf[pos:pos + 4 * dk * dv].view(np.float32).reshape(dk, dv).copy()
             pos += 4 * dk * dv
-            out.append({"id": sid, "dense": True, "S": S, "rule": rule})
+            out.append({"id": sid, "dense": True, "S": S, "rule": rule, "dense_pad": dpad})
             continue
         f = buf[pos:pos + 4 * (R * (1 + dk + dv) + n * (1 + dk + dv))].view(np.float32)
         pos += f.nbytes

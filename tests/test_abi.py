@@ -111,13 +111,20 @@ def test_decode_byte_formula(lib):
     """Algorithmic bytes: rank 8 with a half-full pad on 128x80 is the 12,126 B of the plan
     (which counts Gamma as two 4-byte accesses) with the 16-byte record read and written instead."""
     f = lib.ss_decode_bytes_per_state
-    avg = (f(128, 80, 8, 3, 0, 0) + f(128, 80, 8, 4, 0, 0)) / 2
+    FAC, BUF, PLAIN = 0, 1, 2
+    avg = (f(128, 80, 8, 8, 3, 0, FAC) + f(128, 80, 8, 8, 4, 0, FAC)) / 2
     assert avg == 12126 - 8 + 32
     # a factored rank-r state with n slots reads (r + n) components of d_k + d_v + 1 floats
-    assert f(128, 80, 9, 0, 0, 0) - f(128, 80, 8, 0, 0, 0) == 4 * (128 + 80 + 1)
-    assert f(128, 80, 8, 0, 1, 0) - f(128, 80, 8, 0, 0, 0) == 4        # beta
-    # dense: the state read and written
-    assert f(128, 80, 0, 0, 0, 1) == 16 + 4 + 2 * 4 * 128 * 80 + 4 * (2 * 128 + 80 + 1) + 4 * 80
+    assert f(128, 80, 8, 9, 0, 0, FAC) - f(128, 80, 8, 8, 0, 0, FAC) == 4 * (128 + 80 + 1)
+    assert f(128, 80, 8, 8, 0, 1, FAC) - f(128, 80, 8, 8, 0, 0, FAC) == 4        # beta
+    # plain dense (the baseline): the state read and written
+    inputs = 4 * (2 * 128 + 80 + 1)
+    assert f(128, 80, 8, 0, 0, 0, PLAIN) == 16 + 4 + 2 * 4 * 128 * 80 + inputs + 4 * 80
+    # buffered dense: H read, the pad read, one slot written; the step that fills the pad writes H
+    comp = 4 * (128 + 80 + 1)
+    assert f(128, 80, 8, 0, 3, 0, BUF) == 32 + 4 + 4 * 128 * 80 + 3 * comp + inputs + 4 * 80 + comp
+    assert f(128, 80, 8, 0, 7, 0, BUF) == 32 + 4 + 4 * 128 * 80 + 7 * comp + inputs + 4 * 80 + 4 * 128 * 80
+    assert f(128, 80, 8, 0, 0, 0, 3) == 0
     # page-printed footprint: rank-8 factors + a full pad of one 80x128 state = 13,376 B
     g = json.load(open(os.path.join(GOLD, "memory_arithmetic.json")))
     assert 2 * 8 * 4 * (128 + 80 + 1) == g["total_bytes"]

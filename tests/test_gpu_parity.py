@@ -149,23 +149,37 @@ def test_dense_baseline_matches_dense_recurrence():
 
 
 def test_decode_bytes_accounting():
-    """In-kernel algorithmic byte counter equals the host formula over the live ranks."""
+    """In-kernel algorithmic byte counter equals the host formula over the live ranks and pad fills,
+    across the steps where dense states fold their pad into H and the compactions between them."""
     w = W.get("mixed_dense", n_requests=1)
     init = W.initial_state(w)
-    pool = _pool_from_init(w, init)
-    gen = W.StepInputs(w, device="cuda")
-    o = torch.empty(w.n_states, w.d_v, device="cuda")
-    for t in range(1, 4):
-        states = ss.state_export(pool, np.arange(w.n_states))
-        expect = sum(ss.decode_bytes_per_state(w.d_k, w.d_v, 0 if s["dense"] else len(s["sigma"]),
-                                               0 if s["dense"] else len(s["c"]), s["rule"], s["dense"])
-                     for s in states)
-        b0 = ss.pool_stats(pool)["decode_bytes"]
-        x = gen.generate(t)
-        ss.decode_step(pool, x["q"], x["k"], x["v"], x["alpha"], x["beta"], o)
-        b1 = ss.pool_stats(pool)["decode_bytes"]
-        assert b1 - b0 == expect
-    pool.close()
+    for force_dense in (False, True):
+        pool = _pool_from_init(w, init, force_dense=force_dense)
+        gen = W.StepInputs(w, device="cuda")
+        o = torch.empty(w.n_states, w.d_v, device="cuda")
+        folds = 0
+        for t in range(1, 2 * w.K + 2):
+            states = ss.state_export(pool, np.arange(w.n_states))
+            expect = 0
+            for s in states:
+                if not s["dense"]:
+                    kind, nc, npad = ss.DECODE_FACTORED, len(s["sigma"]), len(s["c"])
+                elif force_dense:
+                    kind, nc, npad = ss.DECODE_DENSE_PLAIN, 0, 0
+                else:
+                    kind, nc, npad = ss.DECODE_DENSE_BUFFERED, 0, s["dense_pad"]
+                    folds += npad + 1 == w.K
+                expect += ss.decode_bytes_per_state(w.d_k, w.d_v, w.K, nc, npad, s["rule"], kind)
+            b0 = ss.pool_stats(pool)["decode_bytes"]
+            x = gen.generate(t)
+            ss.decode_step(pool, x["q"], x["k"], x["v"], x["alpha"], x["beta"], o)
+            b1 = ss.pool_stats(pool)["decode_bytes"]
+            assert b1 - b0 == expect, (force_dense, t)
+            for g in ss.schedule_due(pool, t):
+                ss.compact(pool, g)
+        pool.close()
+        if not force_dense:
+            assert folds > 0
 
 
 def test_edge_shapes_and_ragged():
@@ -247,35 +261,40 @@ def test_dense_capacity_exhaustion_is_reported():
     pool.close()
 
 
+@pytest.mark.parametrize("buffered", [False, True])
 @pytest.mark.parametrize("dk,dv", [(4, 8), (12, 20), (44, 64), (128, 80), (80, 128), (256, 256), (256, 4)])
-def test_dense_path_shapes(dk, dv):
+def test_dense_path_shapes(dk, dv, buffered):
     """Dense region (stored transposed) on edge shapes: one lane per row (d_k = 4), lane groups with
     idle lanes (12, 44), a full wavefront per row (256), both rules, ragged state count, readout and
-    decode against the oracle's dense recurrence."""
+    decode against the oracle's dense recurrence.  Plain: a force_dense pool (the dense baseline).
+    Buffered: states start dense (rank L + 1) in a factored pool with K = 3; the steps cross full
+    pads (folded inside decode) and an explicit compaction folds a partial pad."""
     rng = np.random.default_rng(dk * 1000 + dv)
-    N = 37
-    R = np.full(N, 3)
+    N, K = 37, 3
+    L = ss.dense_rank_limit(dk, dv)
+    R = np.full(N, L + 1 if buffered else 3)
     off = np.concatenate([[0], np.cumsum(R)]).astype(np.int64)
     u = rng.standard_normal((int(off[-1]), dk)).astype(np.float32)
     v = rng.standard_normal((int(off[-1]), dv)).astype(np.float32)
-    sig = np.tile(np.array([2.0, 1.0, 0.5], np.float32), N)
+    sig = np.concatenate([np.geomspace(2.0, 0.5, r) for r in R]).astype(np.float32)
     rule = (np.arange(N) % 2).astype(np.uint8)
     eps = np.full(N, 1e-3, np.float32)
-    pool = ss.state_pool_create(N, dk, dv, 8, 8, rule=rule, eps=eps, comp_off=off, u=u, v=v, sigma=sig,
-                                force_dense=True)
+    pool = ss.state_pool_create(N, dk, dv, K, 2, rule=rule, eps=eps, comp_off=off, u=u, v=v, sigma=sig,
+                                force_dense=not buffered)
     ids = np.arange(N)
     o = torch.empty(N, dv, device="cuda")
-    worst = 0.0
-    for t in range(3):
+    worst, folds = 0.0, 0
+    for t in range(1, 9):
         q = torch.randn(N, dk, device="cuda")
         k = torch.nn.functional.normalize(torch.randn(N, dk, device="cuda"), dim=1)
         vv = torch.randn(N, dv, device="cuda")
         a = 0.9 + 0.1 * torch.rand(N, device="cuda")
         b = torch.rand(N, device="cuda")
         before = ss.state_export(pool, ids)
-        assert all(s["dense"] for s in before)
-        P = oracle_from_export(before, eps, dk, dv, 8, 8)
-        Sn = np.array([np.linalg.norm(reconstruct(s)) for s in before])
+        assert all(st["dense"] for st in before)
+        folds += sum(st["dense_pad"] + 1 == K for st in before)
+        P = oracle_from_export(before, eps, dk, dv, K, 2)
+        Sn = np.array([np.linalg.norm(reconstruct(st)) for st in before])
         qn = np.linalg.norm(q.cpu().numpy(), axis=1)
         ss.readout(pool, q, o)
         torch.cuda.synchronize()
@@ -285,8 +304,14 @@ def test_dense_path_shapes(dk, dv):
         oo = P.decode(q.cpu().numpy(), k.cpu().numpy(), vv.cpu().numpy(), a.cpu().numpy(), b.cpu().numpy())
         Sn = np.array([np.linalg.norm(P.reconstruct(j)) for j in range(N)])
         worst = max(worst, float(rel_out_err(o.cpu().numpy(), oo, Sn, qn).max()))
+        if t == 4:
+            mid = ss.state_export(pool, ids)
+            assert buffered == any(st["dense_pad"] > 0 for st in mid)
+            ss.compact(pool, 0)  # folds the partial pads of the dense states
+            assert all(st["dense_pad"] == 0 for st in ss.state_export(pool, ids))
         for j, st in enumerate(ss.state_export(pool, ids)):
             So = P.reconstruct(j)
             worst = max(worst, float(np.linalg.norm(reconstruct(st) - So) / np.linalg.norm(So)))
     pool.close()
-    assert worst <= TOL, (dk, dv, worst)
+    assert worst <= TOL, (dk, dv, buffered, worst)
+    assert folds > 0 or not buffered
