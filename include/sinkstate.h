@@ -16,7 +16,7 @@
  * 3.2 Design 1: the first min(r, R) by sigma are "active", the rest
  * "frozen"), (k_j, w_j, c_j) are the pad slots ([SS] 4.2 "(i) Buffering"),
  * and Gamma is the decay accumulated since the last compaction ([SS] 4.4:
- * the decode kernel applies the accumulated decay on the fly).
+ * the decode kernel scales by the decay accumulated since the last compaction).
  *
  * Conventions for every entry point:
  *  - Every call returns ss_status.  Argument and shape checks run on the host
@@ -84,7 +84,7 @@ typedef struct {
 /* Initial states, host memory, copied during create.  Components of state s
  * are rows comp_off[s] .. comp_off[s+1]-1 of u / v / sigma and must be sorted
  * by sigma, descending.  A state with more than L components is stored dense
- * ([SS] 4.4: the fallback is decided after initialization).  The pad starts
+ * ([SS] 4.4: the dense test is made once the initial factors exist).  The pad starts
  * empty and Gamma = 1.  A NULL ss_init (or NULL comp_off) creates empty
  * states (S = 0). */
 typedef struct {
@@ -154,7 +154,7 @@ ss_status ss_decode_step(ss_pool *pool, const float *q, const float *k, const fl
 
 /* Read-only readout o = S^T q of every state from factors, pad and dense
  * region, without changing the pool ([SS] 4.2 "(i) Buffering": the output is
- * computed from the extended factors; 4.4: without materializing the state). */
+ * computed from the extended factors; 4.4: no dense state is formed). */
 ss_status ss_readout(ss_pool *pool, const float *q, float *o, hipStream_t stream);
 
 /* Compact every state of compaction group `group` (or of all groups when

@@ -313,8 +313,8 @@ static int make_dense(orc_pool *p, orc_state *x) {
 
 /* Set one state.  Components are given as rows and are sorted here by
  * sigma (descending, stable).  With as_init set, a factored state given with
- * R > L falls back to the dense form (SinkState 4.4: the fallback is decided
- * after initialization); without it the state is loaded as given, e.g. to
+ * R > L falls back to the dense form (SinkState 4.4: the dense test is made
+ * once the initial factors exist); without it the state is loaded as given, e.g. to
  * continue from a state taken in the middle of a run. */
 int orc_set_state(orc_pool *p, int64_t s, int rule, double eps, int R, const double *U, const double *V,
                   const double *sig, int n, const double *PK, const double *PW, const double *pc, int dense,
