@@ -33,59 +33,94 @@ namespace {
 constexpr float kTau2 = 1e-10f;  // (1e-5)^2: CGS2 dependent-column test on squared norms
 constexpr float kTolJ = 1e-6f;   // Jacobi: rotate while |a_i.a_j| > tol |a_i| |a_j|
 constexpr int kMaxSweeps = 16;
-constexpr int kLdsPerWave = 1152;
+constexpr int kMaxFrozen = 256;  // frozen components per state (max_frozen <= 255)
+// LDS per wavefront, in floats
+constexpr int kOffRl = 0, kOffRr = 256, kOffCm = 512, kOffVh = 768, kOffScw = 1024, kOffSgs = 1040, kOffSraw = 1056,
+              kOffPerm = 1072, kOffPosL = 1088, kOffFs = 1104, kOffPosF = kOffFs + kMaxFrozen,
+              kLdsPerWave = kOffPosF + kMaxFrozen;
 
-// In-place CGS2 thin QR of the register-resident columns a[0..m).  R goes to
-// LDS, column-major 16 x 16: Rm[j * 16 + i] = R(i, j).
+// In-place CGS2 thin QR of the register-resident columns u[0..m) and v[0..m),
+// both sides interleaved (they are independent, so their reductions overlap).
+// R goes to LDS column-major 16 x 16: R[j * 16 + i] = R(i, j).  A column whose
+// residual is at most 1e-5 of its input norm is dependent: it and its R row are zeroed.
 template <int NS>
-__device__ __forceinline__ void cgs2(float (&a)[kMaxM][NS], int m, int lane, float *Rm) {
+__device__ __forceinline__ void cgs2_pair(float (&u)[kMaxM][NS], float (&v)[kMaxM][NS], int m, int lane, float *Ru,
+                                          float *Rv) {
 #pragma unroll
   for (int j = 0; j < kMaxM; ++j) {
     if (j < m) {
-      float n0 = 0.f;
+      float n0u = 0.f, n0v = 0.f;
 #pragma unroll
-      for (int t = 0; t < NS; ++t) n0 = fmaf(a[j][t], a[j][t], n0);
-      n0 = wave_sum(n0);
-      float rc[kMaxM];
+      for (int t = 0; t < NS; ++t) {
+        n0u = fmaf(u[j][t], u[j][t], n0u);
+        n0v = fmaf(v[j][t], v[j][t], n0v);
+      }
+      n0u = wave_sum_u(n0u);
+      n0v = wave_sum_u(n0v);
+      float ru[kMaxM], rv[kMaxM];
 #pragma unroll
-      for (int i = 0; i < kMaxM; ++i) rc[i] = 0.f;
+      for (int i = 0; i < kMaxM; ++i) ru[i] = rv[i] = 0.f;
 #pragma unroll
       for (int pass = 0; pass < 2; ++pass) {
-        float d[kMaxM];
+        float du[kMaxM], dv[kMaxM];
 #pragma unroll
         for (int i = 0; i < j; ++i) {
-          float x = 0.f;
+          float x = 0.f, y = 0.f;
 #pragma unroll
-          for (int t = 0; t < NS; ++t) x = fmaf(a[i][t], a[j][t], x);
-          d[i] = wave_sum(x);
+          for (int t = 0; t < NS; ++t) {
+            x = fmaf(u[i][t], u[j][t], x);
+            y = fmaf(v[i][t], v[j][t], y);
+          }
+          du[i] = wave_sum_u(x);
+          dv[i] = wave_sum_u(y);
         }
 #pragma unroll
         for (int i = 0; i < j; ++i) {
-          rc[i] += d[i];
+          ru[i] += du[i];
+          rv[i] += dv[i];
 #pragma unroll
-          for (int t = 0; t < NS; ++t) a[j][t] = fmaf(-d[i], a[i][t], a[j][t]);
+          for (int t = 0; t < NS; ++t) {
+            u[j][t] = fmaf(-du[i], u[i][t], u[j][t]);
+            v[j][t] = fmaf(-dv[i], v[i][t], v[j][t]);
+          }
         }
       }
-      float nn = 0.f;
+      float nu = 0.f, nv = 0.f;
 #pragma unroll
-      for (int t = 0; t < NS; ++t) nn = fmaf(a[j][t], a[j][t], nn);
-      nn = wave_sum(nn);
-      const bool keep = nn > 0.f && nn > kTau2 * n0;
-      const float nrm = sqrtf(nn);
-      const float inv = keep ? 1.0f / nrm : 0.f;
+      for (int t = 0; t < NS; ++t) {
+        nu = fmaf(u[j][t], u[j][t], nu);
+        nv = fmaf(v[j][t], v[j][t], nv);
+      }
+      nu = wave_sum_u(nu);
+      nv = wave_sum_u(nv);
+      const bool ku = nu > 0.f && nu > kTau2 * n0u, kv = nv > 0.f && nv > kTau2 * n0v;
+      const float su = sqrtf(nu), sv = sqrtf(nv);
+      const float iu = ku ? 1.0f / su : 0.f, iv = kv ? 1.0f / sv : 0.f;
 #pragma unroll
-      for (int t = 0; t < NS; ++t) a[j][t] *= inv;
-      if (lane == 0) {
+      for (int t = 0; t < NS; ++t) {
+        u[j][t] *= iu;
+        v[j][t] *= iv;
+      }
+      if (lane < kMaxM) {  // R column j: lane i writes row i
+        float xu = 0.f, xv = 0.f;
 #pragma unroll
-        for (int i = 0; i < kMaxM; ++i) Rm[j * 16 + i] = (i < j) ? rc[i] : ((i == j && keep) ? nrm : 0.f);
+        for (int i = 0; i < kMaxM; ++i) {
+          if (i == lane && i < j) {
+            xu = ru[i];
+            xv = rv[i];
+          }
+        }
+        if (lane == j) {
+          xu = ku ? su : 0.f;
+          xv = kv ? sv : 0.f;
+        }
+        Ru[j * 16 + lane] = xu;
+        Rv[j * 16 + lane] = xv;
       }
     } else {
 #pragma unroll
-      for (int t = 0; t < NS; ++t) a[j][t] = 0.f;
-      if (lane == 0) {
-#pragma unroll
-        for (int i = 0; i < kMaxM; ++i) Rm[j * 16 + i] = 0.f;
-      }
+      for (int t = 0; t < NS; ++t) u[j][t] = v[j][t] = 0.f;
+      if (lane < kMaxM) Ru[j * 16 + lane] = Rv[j * 16 + lane] = 0.f;
     }
   }
 }
@@ -147,7 +182,7 @@ __device__ int jacobi16(float *Cm, float *Vh, int m, int lane) {
   return sweep;
 }
 
-// copy one component (u, v) between arenas with float4 lanes
+// copy one component (u, v) with float4 lanes
 __device__ __forceinline__ void copy_comp(const float *su, const float *sv, float *du, float *dv_, int dk, int dv,
                                           int lane) {
   const int dk4 = dk >> 2, tot = dk4 + (dv >> 2);
@@ -157,27 +192,39 @@ __device__ __forceinline__ void copy_comp(const float *su, const float *sv, floa
   }
 }
 
-// number of frozen sigma (descending, scaled by g) that are >= thr and > 0
-__device__ __forceinline__ int frozen_kept(const float *fs, int rf, float g, float thr) {
-  int lo = 0, hi = rf;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    const float x = fs[mid] * g;
-    if (x >= thr && x > 0.f) lo = mid + 1;
-    else hi = mid;
+// Copy `cnt` components (u, v) starting at source component c0 of arena `src`
+// to the positions dst_of(f) of the merged list (slots >= total are dropped).
+// All lanes take float4 pieces of consecutive components, UNC pieces in flight.
+template <typename DstOf>
+__device__ __forceinline__ void copy_comps(const Arena &src, int64_t c0, int cnt, int dk, int dv, int lane,
+                                           DstOf dst_of) {
+  constexpr int UNC = 4;
+  const int dk4 = dk >> 2, tot4 = dk4 + (dv >> 2);
+  const int n = cnt * tot4;
+  for (int e0 = 0; e0 < n; e0 += 64 * UNC) {
+    float4 x[UNC];
+#pragma unroll
+    for (int q = 0; q < UNC; ++q) {
+      const int e = e0 + q * 64 + lane;
+      x[q] = zero4();
+      if (e < n) {
+        const int f = e / tot4, c = e - f * tot4;
+        x[q] = c < dk4 ? ld4(src.u + (c0 + f) * dk + 4 * c) : ld4(src.v + (c0 + f) * dv + 4 * (c - dk4));
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < UNC; ++q) {
+      const int e = e0 + q * 64 + lane;
+      if (e < n) {
+        const int f = e / tot4, c = e - f * tot4;
+        float *du, *dvp;
+        if (dst_of(f, du, dvp)) {
+          if (c < dk4) st4(du + 4 * c, x[q]);
+          else st4(dvp + 4 * (c - dk4), x[q]);
+        }
+      }
+    }
   }
-  return lo;
-}
-
-// number of the first kf frozen sigma (descending, scaled by g) that are > x
-__device__ __forceinline__ int frozen_greater(const float *fs, int kf, float g, float x) {
-  int lo = 0, hi = kf;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (fs[mid] * g > x) lo = mid + 1;
-    else hi = mid;
-  }
-  return lo;
 }
 
 template <int NS>
@@ -186,14 +233,17 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   const int w = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int mi = blockIdx.x * 4 + w;
   if (mi >= a.n_members) return;
-  float *Rl = lds[w];
-  float *Rr = Rl + 256;
-  float *Cm = Rl + 512;
-  float *Vh = Rl + 768;
-  float *scw = Rl + 1024;
-  float *sgs = Rl + 1040;
-  float *sraw = Rl + 1056;
-  int *perm = reinterpret_cast<int *>(Rl + 1072);
+  float *Rl = lds[w] + kOffRl;
+  float *Rr = lds[w] + kOffRr;
+  float *Cm = lds[w] + kOffCm;
+  float *Vh = lds[w] + kOffVh;
+  float *scw = lds[w] + kOffScw;
+  float *sgs = lds[w] + kOffSgs;
+  float *sraw = lds[w] + kOffSraw;
+  int *perm = reinterpret_cast<int *>(lds[w] + kOffPerm);
+  int *posL = reinterpret_cast<int *>(lds[w] + kOffPosL);
+  float *fsl = lds[w] + kOffFs;
+  int *posF = reinterpret_cast<int *>(lds[w] + kOffPosF);
 
   const int s = uniform(a.members[mi]);
   const Meta m = a.meta[s];
@@ -208,16 +258,18 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   const int64_t dst_f = a.dst_base_f + (int64_t)mi * a.fcap;
 
   if (n == 0) {  // nothing buffered: move the components to the other segments unchanged
-    for (int j = 0; j < ra; ++j) {
-      copy_comp(a.act.u + (int64_t)(off_a + j) * dk, a.act.v + (int64_t)(off_a + j) * dv,
-                a.act.u + (dst_a + j) * dk, a.act.v + (dst_a + j) * dv, dk, dv, lane);
-      if (lane == 0) a.act.s[dst_a + j] = a.act.s[off_a + j] * gamma;
-    }
-    for (int j = 0; j < rf; ++j) {
-      copy_comp(a.frz.u + (int64_t)(off_f + j) * dk, a.frz.v + (int64_t)(off_f + j) * dv,
-                a.frz.u + (dst_f + j) * dk, a.frz.v + (dst_f + j) * dv, dk, dv, lane);
-      if (lane == 0) a.frz.s[dst_f + j] = a.frz.s[off_f + j] * gamma;
-    }
+    copy_comps(a.act, off_a, ra, dk, dv, lane, [&](int f, float *&du, float *&dvp) {
+      du = a.act.u + (dst_a + f) * dk;
+      dvp = a.act.v + (dst_a + f) * dv;
+      return true;
+    });
+    copy_comps(a.frz, off_f, rf, dk, dv, lane, [&](int f, float *&du, float *&dvp) {
+      du = a.frz.u + (dst_f + f) * dk;
+      dvp = a.frz.v + (dst_f + f) * dv;
+      return true;
+    });
+    for (int f = lane; f < ra; f += 64) a.act.s[dst_a + f] = a.act.s[off_a + f] * gamma;
+    for (int f = lane; f < rf; f += 64) a.frz.s[dst_f + f] = a.frz.s[off_f + f] * gamma;
     if (lane == 0) {
       Meta nm;
       nm.off_a = (int32_t)dst_a;
@@ -229,6 +281,8 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
     return;
   }
 
+  // frozen singular values (scaled by Gamma) to LDS: the merge searches them there
+  for (int f = lane; f < rf; f += 64) fsl[f] = a.frz.s[off_f + f] * gamma;
   const int mcol = ra + n;
   float uc[kMaxM][NS], vc[kMaxM][NS];
 #pragma unroll
@@ -250,8 +304,7 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
     else if (lane < mcol) wgt = a.pc[(int64_t)s * K + (lane - ra)] * gamma;
     scw[lane] = wgt;
   }
-  cgs2<NS>(uc, mcol, lane, Rl);
-  cgs2<NS>(vc, mcol, lane, Rr);
+  cgs2_pair<NS>(uc, vc, mcol, lane, Rl, Rr);
   wave_sync();
   for (int e = lane; e < 256; e += 64) {
     const int i = e & 15, j = e >> 4;
@@ -283,15 +336,16 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   }
   wave_sync();
 
-  // merge with the frozen part and truncate
-  const float *fs = a.frz.s + off_f;
-  const float eps = a.eps[s];
-  const float fs0 = rf > 0 ? fs[0] * gamma : 0.f;
-  const float smax = fmaxf(sgs[0], fs0);
-  const float thr = eps * smax;
-  int kl = 0;
-  for (int i = 0; i < mcol; ++i) kl += (sgs[i] >= thr && sgs[i] > 0.f) ? 1 : 0;
-  const int kf = frozen_kept(fs, rf, gamma, thr);
+  // merge with the frozen part and truncate: both lists are descending; on ties the local
+  // component comes first; drop sigma < eps * sigma_max and sigma = 0
+  const float smax = fmaxf(sgs[0], rf > 0 ? fsl[0] : 0.f);
+  const float thr = a.eps[s] * smax;
+  const int kl = __builtin_popcountll(__builtin_amdgcn_ballot_w64(lane < mcol && sgs[lane] >= thr && sgs[lane] > 0.f));
+  int kf = 0;
+  for (int f0 = 0; f0 < rf; f0 += 64) {
+    const int f = f0 + lane;
+    kf += __builtin_popcountll(__builtin_amdgcn_ballot_w64(f < rf && fsl[f] >= thr && fsl[f] > 0.f));
+  }
   int total = kl + kf;
   const int cap_total = r + a.fcap;
   if (total > cap_total) {
@@ -301,10 +355,27 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
     total = cap_total;
   }
   const int ra2 = total < r ? total : r, rf2 = total - ra2;
+  if (lane < kl) {  // local i goes after the frozen ones strictly greater than it
+    const float x = sgs[lane];
+    int lo = 0, hi = kf;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (fsl[mid] > x) lo = mid + 1;
+      else hi = mid;
+    }
+    posL[lane] = lane + lo;
+  }
+  for (int f = lane; f < kf; f += 64) {  // frozen f goes after the local ones >= it
+    const float x = fsl[f];
+    int c = 0;
+    for (int i = 0; i < kl; ++i) c += sgs[i] >= x ? 1 : 0;
+    posF[f] = f + c;
+  }
+  wave_sync();
 
   // kept local components: U' = Q_L U_hat, V' = Q_R V_hat
   for (int i = 0; i < kl; ++i) {
-    const int pos = i + frozen_greater(fs, kf, gamma, sgs[i]);
+    const int pos = posL[i];
     if (pos >= total) continue;
     const int j = perm[i];
     const float inv = 1.0f / sgs[i];
@@ -332,18 +403,22 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
       if (row < dk) du[row] = ou[t];
       if (row < dv) dvv[row] = ov[t];
     }
-    if (lane == 0) (pos < r ? a.act.s[dst_a + pos] : a.frz.s[dst_f + pos - r]) = sgs[i];
+  }
+  if (lane < kl && posL[lane] < total) {
+    const int pos = posL[lane];
+    (pos < r ? a.act.s[dst_a + pos] : a.frz.s[dst_f + pos - r]) = sgs[lane];
   }
   // kept frozen components: copied, sigma scaled by Gamma
-  for (int f = 0; f < kf; ++f) {
-    const float sf = fs[f] * gamma;
-    int pos = f;
-    for (int i = 0; i < kl; ++i) pos += (sgs[i] >= sf) ? 1 : 0;
-    if (pos >= total) continue;
-    float *du = pos < r ? a.act.u + (dst_a + pos) * dk : a.frz.u + (dst_f + pos - r) * dk;
-    float *dvv = pos < r ? a.act.v + (dst_a + pos) * dv : a.frz.v + (dst_f + pos - r) * dv;
-    copy_comp(a.frz.u + (int64_t)(off_f + f) * dk, a.frz.v + (int64_t)(off_f + f) * dv, du, dvv, dk, dv, lane);
-    if (lane == 0) (pos < r ? a.act.s[dst_a + pos] : a.frz.s[dst_f + pos - r]) = sf;
+  copy_comps(a.frz, off_f, kf, dk, dv, lane, [&](int f, float *&du, float *&dvp) {
+    const int pos = posF[f];
+    if (pos >= total) return false;
+    du = pos < r ? a.act.u + (dst_a + pos) * dk : a.frz.u + (dst_f + pos - r) * dk;
+    dvp = pos < r ? a.act.v + (dst_a + pos) * dv : a.frz.v + (dst_f + pos - r) * dv;
+    return true;
+  });
+  for (int f = lane; f < kf; f += 64) {
+    const int pos = posF[f];
+    if (pos < total) (pos < r ? a.act.s[dst_a + pos] : a.frz.s[dst_f + pos - r]) = fsl[f];
   }
   if (lane == 0) {
     Meta nm;

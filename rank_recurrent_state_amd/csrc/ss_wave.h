@@ -40,6 +40,25 @@ __device__ __forceinline__ float group_sum(float x) {
 
 __device__ __forceinline__ float wave_sum(float x) { return group_sum<64>(x); }
 
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float dpp_rows(float x) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWMASK, 0xF, false));
+}
+
+// sum over the 64 lanes as a wave-uniform value: row sums by DPP, then row 0 -> 1 and
+// row 2 -> 3 (row_bcast:15), rows 0-1 -> 2-3 (row_bcast:31); lane 63 holds the total and is
+// read into a scalar register, so no LDS permute is involved
+__device__ __forceinline__ float wave_sum_u(float x) {
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  x += dpp<0x141>(x);
+  x += dpp<0x140>(x);
+  x += dpp_rows<0x142, 0xA>(x);
+  x += dpp_rows<0x143, 0xC>(x);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
 // lane i reads lane i ^ S (S a power of two < 64)
 template <int S>
 __device__ __forceinline__ float lane_xor(float x) {
