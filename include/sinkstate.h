@@ -215,10 +215,10 @@ enum {
  * FACTORED: reads the 16-byte record, all components and slots
  * (4 (d_k + d_v + 1) bytes each), q, k, v, alpha (and beta for the delta
  * rule); writes the record, one slot and o.  DENSE_BUFFERED: reads the
- * record, the slot id, H (4 d_k d_v bytes), the slots and the inputs;
+ * 16-byte slot record, H (4 d_k d_v bytes), the slots and the inputs;
  * writes the record, o, and one slot, or H when the step fills the pad
- * (n_pad + 1 >= K).  DENSE_PLAIN: reads and writes H every step.  Returns 0
- * for an unknown kind. */
+ * (n_pad + 1 >= K).  DENSE_PLAIN: reads the slot record and reads and
+ * writes H every step.  Returns 0 for an unknown kind. */
 uint64_t ss_decode_bytes_per_state(int32_t d_k, int32_t d_v, int32_t pad_slots, int32_t n_comp, int32_t n_pad,
                                    int32_t rule, int32_t kind);
 

@@ -206,11 +206,10 @@ __device__ __forceinline__ void copy_comps(const Arena &src, int64_t c0, int cnt
 #pragma unroll
     for (int q = 0; q < UNC; ++q) {
       const int e = e0 + q * 64 + lane;
-      x[q] = zero4();
-      if (e < n) {
-        const int f = e / tot4, c = e - f * tot4;
-        x[q] = c < dk4 ? ld4(src.u + (c0 + f) * dk + 4 * c) : ld4(src.v + (c0 + f) * dv + 4 * (c - dk4));
-      }
+      const int ec = e < n ? e : n - 1;  // clamped (n >= 1 inside the loop)
+      const int f = ec / tot4, c = ec - f * tot4;
+      const float *p = c < dk4 ? src.u + (c0 + f) * dk + 4 * c : src.v + (c0 + f) * dv + 4 * (c - dk4);
+      x[q] = ld4(p);
     }
 #pragma unroll
     for (int q = 0; q < UNC; ++q) {
@@ -286,16 +285,17 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   const int mcol = ra + n;
   float uc[kMaxM][NS], vc[kMaxM][NS];
 #pragma unroll
-  for (int j = 0; j < kMaxM; ++j) {
-    const bool valid = j < mcol;
+  for (int jj = 0; jj < kMaxM; ++jj) {
+    const bool valid = jj < mcol;
+    const int j = valid ? jj : mcol - 1;  // clamped: the loads stay in bounds (mcol >= 1 here)
     const bool isact = j < ra;
     const float *su = isact ? a.act.u + (int64_t)(off_a + j) * dk : a.pk + ((int64_t)s * K + (j - ra)) * dk;
     const float *sv = isact ? a.act.v + (int64_t)(off_a + j) * dv : a.pw + ((int64_t)s * K + (j - ra)) * dv;
 #pragma unroll
     for (int t = 0; t < NS; ++t) {
       const int row = lane + 64 * t;
-      uc[j][t] = (valid && row < dk) ? su[row] : 0.f;
-      vc[j][t] = (valid && row < dv) ? sv[row] : 0.f;
+      uc[jj][t] = self(valid && row < dk, su[row < dk ? row : dk - 1]);
+      vc[jj][t] = self(valid && row < dv, sv[row < dv ? row : dv - 1]);
     }
   }
   if (lane < kMaxM) {
@@ -553,7 +553,12 @@ __global__ __launch_bounds__(256) void k_materialize(MaterializeArgs a) {
       nm.gamma = 1.0f;
       nm.packed = meta_pack(0, 0, 0, flags | FLAG_DENSE);
       a.meta[s] = nm;
-      a.dense_ids[slot] = s;
+      DenseSlot ds;
+      ds.s = s;
+      ds.packed = meta_pack(0, 0, 0, flags | FLAG_DENSE);  // empty pad
+      ds.gamma = 1.0f;
+      ds.spare = 0u;
+      a.dslot[slot] = ds;
       if (!a.csr_off)
         __hip_atomic_fetch_add(&a.counters[C_PROMOTIONS], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }

@@ -54,12 +54,13 @@ __global__ __launch_bounds__(256) void k_decode_factored(DecodeArgs a) {
   const int grp = lane / P, col = lane % P;
   const int dk = a.dk, dv = a.dv, K = a.K;
   const bool kin = col < (dk >> 2), vin = col < (dv >> 2);
+  const int colk = kin ? col : (dk >> 2) - 1, colv = vin ? col : (dv >> 2) - 1;  // clamped: loads stay in bounds
   const Meta m = a.meta[s];
   const uint32_t packed = (uint32_t)uniform((int)m.packed);
   const uint32_t flags = meta_flags(packed);
   if (flags & FLAG_DENSE) return;  // the dense-region kernel serves this state
-  const float4 q4 = kin ? ld4nt(a.q + s * dk + 4 * col) : zero4();
-  const float4 k4 = (!RO && kin) ? ld4nt(a.k + s * dk + 4 * col) : zero4();
+  const float4 q4 = sel4(kin, ld4nt(a.q + s * dk + 4 * colk));
+  const float4 k4 = RO ? zero4() : sel4(kin, ld4nt(a.k + s * dk + 4 * colk));
   const bool delta = ANYDELTA && !RO && (flags & FLAG_DELTA);
   const int ra = meta_ra(packed), rf = meta_rf(packed), n = meta_n(packed);
   const int off_a = uniform(m.off_a), off_f = uniform(m.off_f);
@@ -76,10 +77,12 @@ __global__ __launch_bounds__(256) void k_decode_factored(DecodeArgs a) {
   float4 acc = zero4(), acck = zero4();
   for (int i0 = 0; i0 < T; i0 += G * UN) {
     float4 x[UN], y[UN];
-    float wt[UN];
+    float wt[UN], okf[UN];
 #pragma unroll
     for (int u = 0; u < UN; ++u) {
-      const int i = i0 + u * G + grp;
+      const int iu = i0 + u * G + grp;
+      const bool ok = iu < T;
+      const int i = ok ? iu : T - 1;  // T >= 1 here
       const float *xp, *yp, *wp;
       int64_t c;
       if (i < ra) {
@@ -92,17 +95,20 @@ __global__ __launch_bounds__(256) void k_decode_factored(DecodeArgs a) {
         c = pad0 + i;
         xp = a.pk; yp = a.pw; wp = a.pc;
       }
-      const bool ok = i < T;
-      x[u] = (ok && kin) ? ld4nt(xp + c * dk + 4 * col) : zero4();
-      y[u] = (ok && vin) ? ld4nt(yp + c * dv + 4 * col) : zero4();
-      wt[u] = ok ? ldnt(wp + c) : 0.f;
+      // clamped pair and lanes: q4, k4 are 0 off the key lanes, lanes off the value range are
+      // never stored, and a pair past the list gets weight 0 (applied at use, not at load)
+      x[u] = ld4nt(xp + c * dk + 4 * colk);
+      y[u] = ld4nt(yp + c * dv + 4 * colv);
+      wt[u] = ldnt(wp + c);
+      okf[u] = ok ? 1.f : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < UN; ++u) {
-      const float cq = group_sum<P>(dot4(x[u], q4)) * wt[u];
+      const float wu = wt[u] * okf[u];
+      const float cq = group_sum<P>(dot4(x[u], q4)) * wu;
       acc = fma4(cq, y[u], acc);
       if (delta) {
-        const float ck = group_sum<P>(dot4(x[u], k4)) * wt[u];
+        const float ck = group_sum<P>(dot4(x[u], k4)) * wu;
         acck = fma4(ck, y[u], acck);
       }
     }
@@ -114,7 +120,7 @@ __global__ __launch_bounds__(256) void k_decode_factored(DecodeArgs a) {
     return;
   } else {
     const float al = a.alpha[s];
-    const float4 v4 = vin ? ld4nt(a.v + s * dv + 4 * col) : zero4();
+    const float4 v4 = sel4(vin, ld4nt(a.v + s * dv + 4 * colv));
     float4 w4 = v4;
     if (delta) {
       acck = cross_group_sum4<P>(acck);
@@ -154,12 +160,46 @@ constexpr int kMaxPad = 8;
 #endif
 enum DenseMode : int { DM_DECODE = 0, DM_READOUT = 1, DM_FOLD = 2 };
 
+// Stage segments of float4 data into LDS: the loads of a round (8 float4 per
+// lane, clamped so they stay in bounds) are all issued before any is written.
+struct Seg4 {
+  float *dst;
+  const float *src;
+  int cnt;  // float4 count
+};
+template <int NSEG>
+__device__ __forceinline__ void stage_lds(const Seg4 (&sg)[NSEG], int lane) {
+  int tot = 0;
+#pragma unroll
+  for (int i = 0; i < NSEG; ++i) tot += sg[i].cnt;
+  for (int e0 = 0; e0 < tot; e0 += 512) {
+    float4 x[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      int e = e0 + q * 64 + lane;
+      e = e < tot ? e : tot - 1;
+      const float *p = sg[0].src;
+#pragma unroll
+      for (int i = 0, b = 0; i < NSEG; b += sg[i].cnt, ++i)
+        if (e >= b && e < b + sg[i].cnt) p = sg[i].src + 4 * (e - b);
+      x[q] = ld4(p);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int e = e0 + q * 64 + lane;
+#pragma unroll
+      for (int i = 0, b = 0; i < NSEG; b += sg[i].cnt, ++i)
+        if (e >= b && e < b + sg[i].cnt) st4(sg[i].dst + 4 * (e - b), x[q]);
+    }
+  }
+}
+
 // buffered dense region.  DM_DECODE / DM_READOUT: one wavefront per dense
 // slot.  DM_FOLD: one wavefront per member of a compaction group; a dense
 // member with a non-empty pad gets its pad folded into H.  Rows stream in
 // batches of G * UN, double-buffered: the next batch is in flight while the
-// current one is reduced.  LDS per wave: the pad's w rows, the pad parts of
-// p_q and p_k, and v.
+// current one is reduced.  LDS per wave: the pad's keys and w rows, the pad
+// parts of p_q and p_k, and v.
 template <int P, int UN, int MODE, bool ANYDELTA>
 __global__ __launch_bounds__(256) void k_dense_buf(DenseArgs a) {
   constexpr int G = 64 / P, B = G * UN;
@@ -170,71 +210,78 @@ __global__ __launch_bounds__(256) void k_dense_buf(DenseArgs a) {
   const int grp = lane / P, col = lane % P;
   const int dk = a.dk, dv = a.dv, K = a.K;
   const bool kin = col < (dk >> 2);
-  float *W = smem + (size_t)wv * (K + 3) * dv;  // pad w rows [K][d_v]
-  float *PQ = W + (size_t)K * dv;               // pad part of p_q
-  float *PK = PQ + dv;                          // pad part of p_k
-  float *VS = PK + dv;                          // v
-  int64_t s;
+  const int colk = kin ? col : (dk >> 2) - 1;  // clamped: loads stay in bounds
+  float *W = smem + (size_t)wv * ((size_t)K * (dk + dv) + 3 * dv);  // pad w rows [K][d_v]
+  float *PQ = W + (size_t)K * dv;                                      // pad part of p_q
+  float *PK = PQ + dv;                                                 // pad part of p_k
+  float *VS = PK + dv;                                                 // v
+  float *KS = VS + dv;                                                 // pad keys [K][d_k]
+  float *OS = PK;  // o, collected here once PK has been read (the row loop reads PK[j] before writing OS[j])
+  float *WS = VS;  // the new pad w row, collected in place of v (v_j is read before w_j is written)
   uint32_t slot;
-  Meta m;
-  uint32_t packed;
   if constexpr (FO) {
     const int mi = blockIdx.x * 4 + wv;
     if (mi >= a.n_members) return;
-    s = uniform(a.members[mi]);
-    m = a.meta[s];
-    packed = (uint32_t)uniform((int)m.packed);
-    if (!(meta_flags(packed) & FLAG_DENSE) || meta_n(packed) == 0) return;
-    slot = (uint32_t)uniform(m.off_a);
+    const int sm = uniform(a.members[mi]);
+    const uint32_t mp = (uint32_t)uniform((int)a.meta[sm].packed);
+    if (!(meta_flags(mp) & FLAG_DENSE)) return;
+    slot = (uint32_t)uniform(a.meta[sm].off_a);
   } else {
     slot = blockIdx.x * 4u + (uint32_t)wv;
     if (slot >= min(a.counters[C_DENSE_COUNT], a.cap_d)) return;
   }
-  const float *H = a.dense + (int64_t)slot * dk * dv + 4 * col;
+  // everything but the inputs is addressed by the slot: the record and the first two row
+  // batches are issued together, then the pad (its fill comes from the record)
+  const DenseSlot rec = a.dslot[slot];
+  const float *H = a.dense + (int64_t)slot * dk * dv + 4 * colk;
   float *Hw = a.dense + (int64_t)slot * dk * dv + 4 * col;
   float4 hA[UN], hB[UN];
   auto load_rows = [&](float4 (&hb)[UN], int j0) {
 #pragma unroll
     for (int u = 0; u < UN; ++u) {
       const int j = j0 + u * G + grp;
-      hb[u] = (j < dv && kin) ? ld4nt(H + (int64_t)j * dk) : zero4();
+      hb[u] = ld4nt(H + (int64_t)(j < dv ? j : dv - 1) * dk);  // clamped row; q4, k4 are 0 off the key lanes
     }
   };
-  load_rows(hA, 0);  // depends on the slot only: issued before the id lookup
   if constexpr (!FO) {
-    s = uniform(a.dense_ids[slot]);
-    m = a.meta[s];
-    packed = (uint32_t)uniform((int)m.packed);
+    load_rows(hA, 0);
+    if (B < dv) load_rows(hB, B);
   }
-  if (B < dv) load_rows(hB, B);
-  const uint32_t flags = meta_flags(packed);
+  const uint32_t packed = (uint32_t)uniform((int)rec.packed);
   const int n = meta_n(packed);
-  const float gamma = uniformf(m.gamma);
+  if constexpr (FO) {
+    if (n == 0) return;
+    load_rows(hA, 0);
+    if (B < dv) load_rows(hB, B);
+  }
+  const int64_t s = uniform(rec.s);
+  const uint32_t flags = meta_flags(packed);
+  const float gamma = uniformf(rec.gamma);
   const bool delta = ANYDELTA && DEC && (flags & FLAG_DELTA);
   const bool fold = FO || (DEC && n + 1 >= K);
-  const float4 q4 = (!FO && kin) ? ld4nt(a.q + s * dk + 4 * col) : zero4();
-  const float4 k4 = (DEC && kin) ? ld4nt(a.k + s * dk + 4 * col) : zero4();
+  const float4 q4 = FO ? zero4() : sel4(kin, ld4nt(a.q + s * dk + 4 * colk));
+  const float4 k4 = DEC ? sel4(kin, ld4nt(a.k + s * dk + 4 * colk)) : zero4();
   const float al = DEC ? uniformf(a.alpha[s]) : 1.f;
   const float be = delta ? uniformf(a.beta[s]) : 0.f;
-  // the pad: w rows (and v) to LDS; each key is read once for its coefficients
-  // (wave-uniform, kept in scalar registers) and re-read from cache by a fold
-  const float *pks = a.pk + s * (int64_t)K * dk + 4 * col;
-  const float *pws = a.pw + s * (int64_t)K * dv;
+  // the pad (keys, w rows) and v to LDS in one batch of loads
+  const float *pks = a.pk + (int64_t)slot * K * dk;
+  const float *pws = a.pw + (int64_t)slot * K * dv;
   float cq[kMaxPad], ck[kMaxPad], cf[kMaxPad];
 #pragma unroll
   for (int i = 0; i < kMaxPad; ++i) {
-    cf[i] = i < n ? uniformf(a.pc[s * (int64_t)K + i]) : 0.f;
+    cf[i] = i < n ? uniformf(a.pc[(int64_t)slot * K + i]) : 0.f;
     cq[i] = ck[i] = 0.f;
   }
-  for (int e = lane; e < ((n * dv) >> 2); e += 64) st4(W + 4 * e, ld4(pws + 4 * e));
-  if constexpr (DEC) {
-    for (int e = lane; e < (dv >> 2); e += 64) st4(VS + 4 * e, ld4nt(a.v + s * dv + 4 * e));
+  {
+    const Seg4 sg[3] = {{KS, pks, (n * dk) >> 2}, {W, pws, (n * dv) >> 2}, {VS, a.v + s * dv, DEC ? (dv >> 2) : 0}};
+    stage_lds(sg, lane);
   }
+  wave_sync();
   if constexpr (!FO) {
 #pragma unroll
     for (int i = 0; i < kMaxPad; ++i) {
       if (i < n) {
-        const float4 ki = kin ? ld4(pks + (int64_t)i * dk) : zero4();
+        const float4 ki = *reinterpret_cast<const float4 *>(KS + i * dk + 4 * colk);
         cq[i] = uniformf(cf[i] * group_sum<P>(dot4(ki, q4)));
         if (delta) ck[i] = uniformf(cf[i] * group_sum<P>(dot4(ki, k4)));
       }
@@ -261,7 +308,7 @@ __global__ __launch_bounds__(256) void k_dense_buf(DenseArgs a) {
   const float ag = al * gamma;
   const float sc = FO ? gamma : ag;  // a fold scales H and the pad by this
   float *os = a.o + s * dv;
-  float *pwn = a.pw + (s * (int64_t)K + n) * dv;
+  float *pwn = a.pw + ((int64_t)slot * K + n) * dv;
   auto proc_rows = [&](float4 (&hb)[UN], int j0) {
 #pragma unroll
     for (int u = 0; u < UN; ++u) {
@@ -279,9 +326,9 @@ __global__ __launch_bounds__(256) void k_dense_buf(DenseArgs a) {
             w = be * (vj - al * pk);
           }
           oj = fmaf(al, pq, kq * w);
-          if (!fold && col == 0 && ok) pwn[j] = w;
+          if (!fold && col == 0 && ok) WS[j] = w;
         }
-        if (col == 0 && ok) os[j] = oj;
+        if (col == 0 && ok) OS[j] = oj;
       }
       // fold, first part: FO: H <- Gamma H;  DEC: H <- alpha Gamma H + w_j k
       if (fold) hb[u] = FO ? scale4(sc, hb[u]) : fma4(w, k4, scale4(sc, hb[u]));
@@ -289,7 +336,7 @@ __global__ __launch_bounds__(256) void k_dense_buf(DenseArgs a) {
     if (fold) {
       // second part: H_j += sc c_i w_i,j k_i for every pad slot i, one key at a time
       for (int i = 0; i < n; ++i) {
-        const float4 ki = kin ? ld4(pks + (int64_t)i * dk) : zero4();
+        const float4 ki = *reinterpret_cast<const float4 *>(KS + i * dk + 4 * colk);
         const float si = sc * cf[i];
 #pragma unroll
         for (int u = 0; u < UN; ++u) {
@@ -312,14 +359,22 @@ __global__ __launch_bounds__(256) void k_dense_buf(DenseArgs a) {
       if (j0 + 3 * B < dv) load_rows(hB, j0 + 3 * B);
     }
   }
+  // o and the new pad w row leave as whole float4 rows
+  wave_sync();
+  if constexpr (!FO) {
+    for (int e = lane; e < (dv >> 2); e += 64) {
+      st4(os + 4 * e, *reinterpret_cast<const float4 *>(OS + 4 * e));
+      if (DEC && !fold) st4(pwn + 4 * e, *reinterpret_cast<const float4 *>(WS + 4 * e));
+    }
+  }
   if constexpr (!RO) {
-    if (DEC && !fold && grp == 0 && kin) st4(a.pk + (s * (int64_t)K + n) * dk + 4 * col, k4);
+    if (DEC && !fold && grp == 0 && kin) st4(a.pk + ((int64_t)slot * K + n) * dk + 4 * col, k4);
     if (lane == 0) {
-      if (DEC && !fold) a.pc[s * (int64_t)K + n] = 1.0f / ag;
-      Meta nm = m;
-      nm.gamma = fold ? 1.0f : ag;
-      nm.packed = meta_pack(0, 0, fold ? 0 : n + 1, flags);
-      a.meta[s] = nm;
+      if (DEC && !fold) a.pc[(int64_t)slot * K + n] = 1.0f / ag;
+      DenseSlot nr = rec;
+      nr.gamma = fold ? 1.0f : ag;
+      nr.packed = meta_pack(0, 0, fold ? 0 : n + 1, flags);
+      a.dslot[slot] = nr;
       if (DEC) {
         const unsigned long long b = decode_bytes(dk, dv, K, 0, n, delta, KIND_DENSE_BUFFERED);
         __hip_atomic_fetch_add(&a.acct[s & (kAcctSlots - 1)], b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -328,67 +383,77 @@ __global__ __launch_bounds__(256) void k_dense_buf(DenseArgs a) {
   }
 }
 
-// plain dense recurrence (the dense baseline): every row read and written every step
+// plain dense recurrence (the dense baseline): every row read and written every
+// step.  Same row streaming as the buffered kernel (double-buffered batches, v in LDS).
 template <int P, int UN, bool RO, bool ANYDELTA>
 __global__ __launch_bounds__(256) void k_dense_plain(DenseArgs a) {
-  constexpr int G = 64 / P;
+  constexpr int G = 64 / P, B = G * UN;
+  extern __shared__ float smem[];
+  const int wv = uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const uint32_t slot = blockIdx.x * 4u + (uint32_t)uniform(threadIdx.x >> 6);
+  const uint32_t slot = blockIdx.x * 4u + (uint32_t)wv;
   const uint32_t count = min(a.counters[C_DENSE_COUNT], a.cap_d);
   if (slot >= count) return;
   const int grp = lane / P, col = lane % P;
   const int dk = a.dk, dv = a.dv;
   const bool kin = col < (dk >> 2);
-  const float *H = a.dense + (int64_t)slot * dk * dv + 4 * col;
+  const int colk = kin ? col : (dk >> 2) - 1;  // clamped: loads stay in bounds
+  float *VS = smem + (size_t)wv * dv;
+  const float *H = a.dense + (int64_t)slot * dk * dv + 4 * colk;
   float *Hw = a.dense + (int64_t)slot * dk * dv + 4 * col;
-  // first batch of rows: depends on the slot only, so it is issued before the id lookup
-  float4 h[UN];
+  float4 hA[UN], hB[UN];
+  auto load_rows = [&](float4 (&hb)[UN], int j0) {
 #pragma unroll
-  for (int u = 0; u < UN; ++u) {
-    const int j = u * G + grp;
-    h[u] = (j < dv && kin) ? ld4nt(H + (int64_t)j * dk) : zero4();
-  }
-  const int64_t s = uniform(a.dense_ids[slot]);
-  const uint32_t flags = meta_flags((uint32_t)uniform((int)a.meta[s].packed));
+    for (int u = 0; u < UN; ++u) {
+      const int j = j0 + u * G + grp;
+      hb[u] = ld4nt(H + (int64_t)(j < dv ? j : dv - 1) * dk);  // clamped row; q4, k4 are 0 off the key lanes
+    }
+  };
+  const DenseSlot rec = a.dslot[slot];
+  load_rows(hA, 0);  // depends on the slot only: issued before the record arrives
+  if (B < dv) load_rows(hB, B);
+  const int64_t s = uniform(rec.s);
+  const uint32_t flags = meta_flags((uint32_t)uniform((int)rec.packed));
   const bool delta = ANYDELTA && !RO && (flags & FLAG_DELTA);
-  const float4 q4 = kin ? ld4nt(a.q + s * dk + 4 * col) : zero4();
-  const float4 k4 = (!RO && kin) ? ld4nt(a.k + s * dk + 4 * col) : zero4();
-  const float al = RO ? 1.f : a.alpha[s];
-  const float be = delta ? a.beta[s] : 0.f;
-  const float kq = RO ? 0.f : group_sum<P>(dot4(k4, q4));
-  const float *vs = a.v + s * dv;
+  const float4 q4 = sel4(kin, ld4nt(a.q + s * dk + 4 * colk));
+  const float4 k4 = RO ? zero4() : sel4(kin, ld4nt(a.k + s * dk + 4 * colk));
+  const float al = RO ? 1.f : uniformf(a.alpha[s]);
+  const float be = delta ? uniformf(a.beta[s]) : 0.f;
+  if constexpr (!RO) {
+    const Seg4 sg[1] = {{VS, a.v + s * dv, dv >> 2}};
+    stage_lds(sg, lane);
+    wave_sync();
+  }
+  const float kq = RO ? 0.f : uniformf(group_sum<P>(dot4(k4, q4)));
   float *os = a.o + s * dv;
-  for (int j0 = 0; j0 < dv; j0 += G * UN) {
-    if (j0 > 0) {
-#pragma unroll
-      for (int u = 0; u < UN; ++u) {
-        const int j = j0 + u * G + grp;
-        h[u] = (j < dv && kin) ? ld4nt(H + (int64_t)j * dk) : zero4();
-      }
-    }
-    float vj[UN];
+  auto proc_rows = [&](float4 (&hb)[UN], int j0) {
 #pragma unroll
     for (int u = 0; u < UN; ++u) {
       const int j = j0 + u * G + grp;
-      vj[u] = (!RO && j < dv) ? ldnt(vs + j) : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < UN; ++u) {
-      const int j = j0 + u * G + grp;
-      const float dq = group_sum<P>(dot4(h[u], q4));
+      const bool ok = j < dv;
+      const float dq = group_sum<P>(dot4(hb[u], q4));
       float oj;
       if constexpr (RO) {
         oj = dq;
       } else {
-        float w = vj[u];
+        const float vj = ok ? VS[j] : 0.f;
+        float w = vj;
         if (delta) {
-          const float dkk = group_sum<P>(dot4(h[u], k4));
-          w = be * (vj[u] - al * dkk);
+          const float dkk = group_sum<P>(dot4(hb[u], k4));
+          w = be * (vj - al * dkk);
         }
         oj = fmaf(al, dq, kq * w);
-        if (j < dv && kin) st4(Hw + (int64_t)j * dk, fma4(w, k4, scale4(al, h[u])));
+        if (ok && kin) st4(Hw + (int64_t)j * dk, fma4(w, k4, scale4(al, hb[u])));
       }
-      if (col == 0 && j < dv) os[j] = oj;
+      if (col == 0 && ok) os[j] = oj;
+    }
+  };
+  for (int j0 = 0; j0 < dv; j0 += 2 * B) {
+    proc_rows(hA, j0);
+    if (j0 + 2 * B < dv) load_rows(hA, j0 + 2 * B);
+    if (j0 + B < dv) {
+      proc_rows(hB, j0 + B);
+      if (j0 + 3 * B < dv) load_rows(hB, j0 + 3 * B);
     }
   }
   if (!RO && lane == 0) {
@@ -415,7 +480,7 @@ hipError_t decode_factored_p(const DecodeArgs &a, int P, hipStream_t st) {
 
 template <int P, int UN, bool AD>
 hipError_t dense_buf_mode(const DenseArgs &a, int mode, unsigned grid, hipStream_t st) {
-  const size_t sh = sizeof(float) * 4 * (size_t)(a.K + 3) * a.dv;
+  const size_t sh = sizeof(float) * 4 * ((size_t)a.K * (a.dk + a.dv) + 3 * (size_t)a.dv);
   const dim3 g(grid), b(256);
   if (mode == DM_DECODE) hipLaunchKernelGGL((k_dense_buf<P, UN, DM_DECODE, AD>), g, b, sh, st, a);
   else if (mode == DM_READOUT) hipLaunchKernelGGL((k_dense_buf<P, UN, DM_READOUT, false>), g, b, sh, st, a);
@@ -440,14 +505,15 @@ hipError_t dense_buf_p(const DenseArgs &a, int mode, int P, unsigned grid, hipSt
 template <bool RO, bool AD>
 hipError_t dense_plain_p(const DenseArgs &a, int P, unsigned grid, hipStream_t st) {
   const dim3 g(grid), b(256);
+  const size_t sh = sizeof(float) * 4 * (size_t)a.dv;
   switch (P) {
-    case 1: hipLaunchKernelGGL((k_dense_plain<1, 1, RO, AD>), g, b, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((k_dense_plain<2, 1, RO, AD>), g, b, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((k_dense_plain<4, 2, RO, AD>), g, b, 0, st, a); break;
-    case 8: hipLaunchKernelGGL((k_dense_plain<8, 4, RO, AD>), g, b, 0, st, a); break;
-    case 16: hipLaunchKernelGGL((k_dense_plain<16, 8, RO, AD>), g, b, 0, st, a); break;
-    case 32: hipLaunchKernelGGL((k_dense_plain<32, 8, RO, AD>), g, b, 0, st, a); break;
-    case 64: hipLaunchKernelGGL((k_dense_plain<64, 8, RO, AD>), g, b, 0, st, a); break;
+    case 1: hipLaunchKernelGGL((k_dense_plain<1, 1, RO, AD>), g, b, sh, st, a); break;
+    case 2: hipLaunchKernelGGL((k_dense_plain<2, 1, RO, AD>), g, b, sh, st, a); break;
+    case 4: hipLaunchKernelGGL((k_dense_plain<4, 2, RO, AD>), g, b, sh, st, a); break;
+    case 8: hipLaunchKernelGGL((k_dense_plain<8, 4, RO, AD>), g, b, sh, st, a); break;
+    case 16: hipLaunchKernelGGL((k_dense_plain<16, 8, RO, AD>), g, b, sh, st, a); break;
+    case 32: hipLaunchKernelGGL((k_dense_plain<32, 8, RO, AD>), g, b, sh, st, a); break;
+    case 64: hipLaunchKernelGGL((k_dense_plain<64, 8, RO, AD>), g, b, sh, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

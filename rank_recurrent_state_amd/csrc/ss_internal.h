@@ -8,7 +8,10 @@
 //   active arena              components: u [cap][d_k], v [cap][d_v], sigma [cap]
 //   frozen arena              same shape, separate allocation
 //   pad    [N][K]             k [N][K][d_k], w [N][K][d_v], c [N][K] (c = 1/Gamma at insertion)
-//   dense  [cap_d][d_v][d_k]  states of the dense region stored transposed (H = S^T), ids [cap_d]
+//   dense  [cap_d][d_v][d_k]  states of the dense region stored transposed (H = S^T)
+//   dslot  [cap_d]            16-byte record per dense slot (state id, pad fill, flags, Gamma)
+//   dense pads [cap_d][K]     k [.][K][d_k], w [.][K][d_v], c [.][K], indexed by slot
+// Everything a dense-region step reads, except q, k, v, is addressed by the slot alone.
 // Each compaction group owns two segments in each arena; a compaction reads
 // the group's current segment and writes the other one.  A state's slice of
 // a segment starts at (segment base + its index within the group * per-state
@@ -55,6 +58,14 @@ enum Counter : int {
   C_N = 8
 };
 
+// 16-byte record of a dense slot.  packed: n << 16 | flags << 24, as Meta.
+struct __attribute__((aligned(16))) DenseSlot {
+  int32_t s;       // state id
+  uint32_t packed;
+  float gamma;     // decay accumulated since the pad was last folded
+  uint32_t spare;
+};
+
 struct Arena {
   float *u, *v, *s;
 };
@@ -79,8 +90,8 @@ struct DenseArgs {
   uint32_t cap_d;
   Meta *meta;
   float *dense;
-  const int32_t *dense_ids;
-  float *pk, *pw, *pc;         // pads of the buffered dense region (nullptr for the plain baseline)
+  DenseSlot *dslot;
+  float *pk, *pw, *pc;         // slot-indexed pads of the buffered dense region (nullptr: plain baseline)
   const int32_t *members;      // fold mode: state ids of a compaction group
   int32_t n_members;
   const float *q, *k, *v, *alpha, *beta;
@@ -115,7 +126,7 @@ struct MaterializeArgs {
   const float *csr_u, *csr_v, *csr_s;
   Arena act, frz;
   float *dense;
-  int32_t *dense_ids;
+  DenseSlot *dslot;
   uint32_t *counters;
   uint32_t *hflag;             // host-mapped flag raised when the dense region is full
 };
@@ -161,10 +172,10 @@ __host__ __device__ inline unsigned long long decode_bytes(int dk, int dv, int K
   const unsigned long long in = 4ull * (2ull * dk + dv + 1 + (delta ? 1 : 0));
   const unsigned long long comp = 4ull * (unsigned long long)(dk + dv + 1);
   const unsigned long long st = 4ull * (unsigned long long)dk * dv;
-  if (kind == KIND_DENSE_PLAIN)  // record + slot id, state read and written, inputs, output
-    return 16ull + 4ull + 2ull * st + in + 4ull * dv;
-  if (kind == KIND_DENSE_BUFFERED)  // record read+write, slot id, H and the pad read, inputs, output, slot or H written
-    return 32ull + 4ull + st + comp * (unsigned long long)npad + in + 4ull * dv + (npad + 1 >= K ? st : comp);
+  if (kind == KIND_DENSE_PLAIN)  // slot record read, state read and written, inputs, output
+    return 16ull + 2ull * st + in + 4ull * dv;
+  if (kind == KIND_DENSE_BUFFERED)  // slot record read+write, H and the pad read, inputs, output, slot or H written
+    return 32ull + st + comp * (unsigned long long)npad + in + 4ull * dv + (npad + 1 >= K ? st : comp);
   // record read+write, components and pad slots read, inputs, one slot written, output
   return 32ull + comp * (unsigned long long)(ncomp + npad) + in + comp + 4ull * dv;
 }

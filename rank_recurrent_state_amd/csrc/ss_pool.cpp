@@ -51,7 +51,8 @@ struct ss_pool {
   ss::Arena act{nullptr, nullptr, nullptr}, frz{nullptr, nullptr, nullptr};
   float *pk = nullptr, *pw = nullptr, *pc = nullptr;
   float *dense = nullptr;
-  int32_t *dense_ids = nullptr;
+  ss::DenseSlot *dslot = nullptr;
+  float *dpk = nullptr, *dpw = nullptr, *dpc = nullptr;  // slot-indexed pads of the dense region
   int32_t *promote_list = nullptr;
   int32_t *fact_ids[2] = {nullptr, nullptr};  // factored-state lists (ping-pong), lengths in counters
   int fact_par = 0;
@@ -307,7 +308,12 @@ ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipSt
     chk(dalloc(p, &p->fact_ids[1], N));
   }
   chk(dalloc(p, &p->dense, (size_t)cap_d * dk * dv));
-  chk(dalloc(p, &p->dense_ids, cap_d));
+  chk(dalloc(p, &p->dslot, cap_d));
+  if (factored) {
+    chk(dalloc(p, &p->dpk, (size_t)cap_d * K * dk));
+    chk(dalloc(p, &p->dpw, (size_t)cap_d * K * dv));
+    chk(dalloc(p, &p->dpc, (size_t)cap_d * K));
+  }
   chk(dalloc(p, &p->counters, ss::C_N));
   chk(dalloc(p, &p->acct, ss::A_N * ss::kAcctSlots));
   if (e == hipSuccess) {
@@ -391,7 +397,7 @@ ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipSt
     ss::MaterializeArgs ma{};
     ma.dk = dk; ma.dv = dv; ma.cap_d = (int)cap_d; ma.list = d_dlist; ma.count = p->counters + ss::C_PROMOTE_COUNT;
     ma.meta = p->meta; ma.csr_off = d_off; ma.csr_u = d_u; ma.csr_v = d_v; ma.csr_s = d_s;
-    ma.act = p->act; ma.frz = p->frz; ma.dense = p->dense; ma.dense_ids = p->dense_ids; ma.counters = p->counters;
+    ma.act = p->act; ma.frz = p->frz; ma.dense = p->dense; ma.dslot = p->dslot; ma.counters = p->counters;
     ma.hflag = p->hflags_dev + HF_DENSE_CAP;
     e = ss::launch_materialize(ma, n_dense0, stream);
   }
@@ -445,7 +451,7 @@ static ss_status run_decode(ss_pool *p, const float *q, const float *k, const fl
   if (p->dense_upper > 0) {
     ss::DenseArgs a{};
     a.dk = p->dk; a.dv = p->dv; a.K = p->K; a.cap_d = (uint32_t)p->cap_d; a.meta = p->meta; a.dense = p->dense;
-    a.dense_ids = p->dense_ids; a.pk = p->pk; a.pw = p->pw; a.pc = p->pc;
+    a.dslot = p->dslot; a.pk = p->dpk; a.pw = p->dpw; a.pc = p->dpc;
     a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.o = o;
     a.counters = p->counters; a.acct = p->acct + ss::A_DECODE_DENSE * ss::kAcctSlots;
     e = timed(p, readonly ? SS_KERNEL_READOUT_DENSE : SS_KERNEL_DECODE_DENSE, stream,
@@ -482,7 +488,7 @@ ss_status ss_compact(ss_pool *p, int32_t group, hipStream_t stream) {
     if (p->dense_upper > 0) {  // dense members: fold a non-empty pad into H
       ss::DenseArgs da{};
       da.dk = p->dk; da.dv = p->dv; da.K = p->K; da.cap_d = (uint32_t)p->cap_d; da.meta = p->meta;
-      da.dense = p->dense; da.dense_ids = p->dense_ids; da.pk = p->pk; da.pw = p->pw; da.pc = p->pc;
+      da.dense = p->dense; da.dslot = p->dslot; da.pk = p->dpk; da.pw = p->dpw; da.pc = p->dpc;
       da.members = p->members + p->group_start[g]; da.n_members = (int32_t)p->group_size[g];
       da.counters = p->counters; da.acct = p->acct;
       e = timed(p, SS_KERNEL_DENSE_FOLD, stream, [&] { return ss::launch_dense_fold(da, stream); });
@@ -505,7 +511,7 @@ ss_status ss_compact(ss_pool *p, int32_t group, hipStream_t stream) {
       ss::MaterializeArgs ma{};
       ma.dk = p->dk; ma.dv = p->dv; ma.cap_d = (int)p->cap_d; ma.list = p->promote_list;
       ma.count = p->counters + ss::C_PROMOTE_COUNT; ma.meta = p->meta; ma.act = p->act; ma.frz = p->frz;
-      ma.dense = p->dense; ma.dense_ids = p->dense_ids; ma.counters = p->counters;
+      ma.dense = p->dense; ma.dslot = p->dslot; ma.counters = p->counters;
       ma.hflag = p->hflags_dev + HF_DENSE_CAP;
       const int64_t gsz = p->group_size[g];
       e = timed(p, SS_KERNEL_MATERIALIZE, stream, [&] { return ss::launch_materialize(ma, gsz, stream); });
@@ -577,7 +583,12 @@ ss_status ss_state_export(ss_pool *p, const int64_t *ids, int64_t n, void *host_
     const uint32_t pkd = m.packed;
     const bool dense = ss::meta_flags(pkd) & ss::FLAG_DENSE;
     const int ra = dense ? 0 : ss::meta_ra(pkd), rf = dense ? 0 : ss::meta_rf(pkd), nn = dense ? 0 : ss::meta_n(pkd);
-    const int dpad = (dense && !p->force_dense) ? (int)ss::meta_n(pkd) : 0;
+    ss::DenseSlot rec{};
+    if (dense) {  // a dense state's pad fill and Gamma live in its slot record
+      e = hipMemcpy(&rec, p->dslot + m.off_a, sizeof(rec), hipMemcpyDeviceToHost);
+      if (e != hipSuccess) return hip_fail(e, "export slot");
+    }
+    const int dpad = (dense && !p->force_dense) ? (int)ss::meta_n(rec.packed) : 0;
     int32_t hdr[8] = {(int32_t)ids[i], dense ? 1 : 0, ra + rf, ra, nn,
                       (ss::meta_flags(pkd) & ss::FLAG_DELTA) ? 1 : 0, dpad, 0};
     std::memcpy(w, hdr, sizeof(hdr));
@@ -586,14 +597,14 @@ ss_status ss_state_export(ss_pool *p, const int64_t *ids, int64_t n, void *host_
       if (e == hipSuccess && bytes) e = hipMemcpy(dst, src, bytes, hipMemcpyDeviceToHost);
     };
     if (dense) {  // the region holds H = S^T [d_v][d_k] and a pad; the export format is S [d_k][d_v]
-      const int np = p->force_dense ? 0 : ss::meta_n(pkd);
+      const int np = dpad;
       std::vector<float> H((size_t)dk * dv), PK((size_t)np * dk), PW((size_t)np * dv), PC(np);
       dl(H.data(), p->dense + (size_t)m.off_a * dk * dv, sizeof(float) * H.size());
-      dl(PK.data(), p->pk + (size_t)ids[i] * K * dk, sizeof(float) * PK.size());
-      dl(PW.data(), p->pw + (size_t)ids[i] * K * dv, sizeof(float) * PW.size());
-      dl(PC.data(), p->pc + (size_t)ids[i] * K, sizeof(float) * PC.size());
+      dl(PK.data(), p->dpk + (size_t)m.off_a * K * dk, sizeof(float) * PK.size());
+      dl(PW.data(), p->dpw + (size_t)m.off_a * K * dv, sizeof(float) * PW.size());
+      dl(PC.data(), p->dpc + (size_t)m.off_a * K, sizeof(float) * PC.size());
       if (e != hipSuccess) return hip_fail(e, "export copy");
-      const double g = p->force_dense ? 1.0 : (double)m.gamma;
+      const double g = p->force_dense ? 1.0 : (double)rec.gamma;
       float *S = reinterpret_cast<float *>(w);
       for (int i2 = 0; i2 < dk; ++i2)
         for (int j = 0; j < dv; ++j) {
@@ -641,18 +652,22 @@ ss_status ss_pool_stats(ss_pool *p, ss_stats *out, hipStream_t stream) {
   if (e == hipSuccess) e = hipMemcpy(ctr, p->counters, sizeof(ctr), hipMemcpyDeviceToHost);
   std::vector<unsigned long long> acct(ss::A_N * ss::kAcctSlots);
   if (e == hipSuccess) e = hipMemcpy(acct.data(), p->acct, acct.size() * sizeof(unsigned long long), hipMemcpyDeviceToHost);
+  const int64_t nd = std::min<int64_t>(p->cap_d, ctr[ss::C_DENSE_COUNT]);
+  std::vector<ss::DenseSlot> dslot(nd);
+  if (e == hipSuccess && nd) e = hipMemcpy(dslot.data(), p->dslot, sizeof(ss::DenseSlot) * nd, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(e, "stats copy");
   std::memset(out, 0, sizeof(*out));
   out->n_states = p->N;
   const int64_t comp = 4ll * (p->dk + p->dv + 1);
-  int64_t live = 16ll * p->N;
+  int64_t live = 16ll * p->N + 16ll * nd;
   for (int64_t s = 0; s < p->N; ++s) {
     const uint32_t pk = meta[s].packed;
     if (ss::meta_flags(pk) & ss::FLAG_DENSE) {
-      const int64_t nn = p->force_dense ? 0 : ss::meta_n(pk);
+      const int64_t slot = meta[s].off_a;
+      const int64_t nn = (p->force_dense || slot < 0 || slot >= nd) ? 0 : ss::meta_n(dslot[slot].packed);
       out->n_dense++;
       out->pad_entries += nn;
-      live += 4ll * p->dk * p->dv + 4 + comp * nn;
+      live += 4ll * p->dk * p->dv + comp * nn;
       continue;
     }
     out->n_factored++;

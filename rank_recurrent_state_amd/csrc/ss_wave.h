@@ -101,6 +101,15 @@ __device__ __forceinline__ float4 ld4nt(const float *p) {
                      __builtin_nontemporal_load(p + 3));
 }
 __device__ __forceinline__ float ldnt(const float *p) { return __builtin_nontemporal_load(p); }
+
+// Guarded loads are written as an unconditional load from an address that is
+// always valid (the caller clamps it), followed by a select: a load placed
+// inside a branch is followed by a wait for its data, which would serialize
+// the loads of a batch.
+__device__ __forceinline__ float4 sel4(bool ok, float4 v) {
+  return make_float4(ok ? v.x : 0.f, ok ? v.y : 0.f, ok ? v.z : 0.f, ok ? v.w : 0.f);
+}
+__device__ __forceinline__ float self(bool ok, float v) { return ok ? v : 0.f; }
 __device__ __forceinline__ void st4(float *p, float4 v) { *reinterpret_cast<float4 *>(p) = v; }
 
 // make this lane's LDS writes visible to the other lanes of the wavefront

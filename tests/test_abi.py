@@ -119,11 +119,11 @@ def test_decode_byte_formula(lib):
     assert f(128, 80, 8, 8, 0, 1, FAC) - f(128, 80, 8, 8, 0, 0, FAC) == 4        # beta
     # plain dense (the baseline): the state read and written
     inputs = 4 * (2 * 128 + 80 + 1)
-    assert f(128, 80, 8, 0, 0, 0, PLAIN) == 16 + 4 + 2 * 4 * 128 * 80 + inputs + 4 * 80
+    assert f(128, 80, 8, 0, 0, 0, PLAIN) == 16 + 2 * 4 * 128 * 80 + inputs + 4 * 80
     # buffered dense: H read, the pad read, one slot written; the step that fills the pad writes H
     comp = 4 * (128 + 80 + 1)
-    assert f(128, 80, 8, 0, 3, 0, BUF) == 32 + 4 + 4 * 128 * 80 + 3 * comp + inputs + 4 * 80 + comp
-    assert f(128, 80, 8, 0, 7, 0, BUF) == 32 + 4 + 4 * 128 * 80 + 7 * comp + inputs + 4 * 80 + 4 * 128 * 80
+    assert f(128, 80, 8, 0, 3, 0, BUF) == 32 + 4 * 128 * 80 + 3 * comp + inputs + 4 * 80 + comp
+    assert f(128, 80, 8, 0, 7, 0, BUF) == 32 + 4 * 128 * 80 + 7 * comp + inputs + 4 * 80 + 4 * 128 * 80
     assert f(128, 80, 8, 0, 0, 0, 3) == 0
     # page-printed footprint: rank-8 factors + a full pad of one 80x128 state = 13,376 B
     g = json.load(open(os.path.join(GOLD, "memory_arithmetic.json")))
