@@ -134,7 +134,7 @@ def main():
     ap.add_argument("--requests", type=int, default=None, help="override the number of requests")
     ap.add_argument("--chunk", type=int, default=64, help="steps whose inputs are generated at once")
     ap.add_argument("--dense-steps", type=int, default=64, help="steps of the dense HIP baseline (0: skip)")
-    ap.add_argument("--cpu-sample", type=int, default=65536)
+    ap.add_argument("--cpu-sample", type=int, default=131072)
     ap.add_argument("--cpu-steps", type=int, default=64)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 4 GiB device copy (for scaling rocprof byte counters)")

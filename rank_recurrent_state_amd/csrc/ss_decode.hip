@@ -59,9 +59,6 @@ __global__ __launch_bounds__(256) void k_decode_factored(DecodeArgs a) {
   const uint32_t packed = (uint32_t)uniform((int)m.packed);
   const uint32_t flags = meta_flags(packed);
   if (flags & FLAG_DENSE) return;  // the dense-region kernel serves this state
-  const float4 q4 = sel4(kin, ld4nt(a.q + s * dk + 4 * colk));
-  const float4 k4 = RO ? zero4() : sel4(kin, ld4nt(a.k + s * dk + 4 * colk));
-  const bool delta = ANYDELTA && !RO && (flags & FLAG_DELTA);
   const int ra = meta_ra(packed), rf = meta_rf(packed), n = meta_n(packed);
   const int off_a = uniform(m.off_a), off_f = uniform(m.off_f);
   const float gamma = uniformf(m.gamma);
@@ -74,15 +71,21 @@ __global__ __launch_bounds__(256) void k_decode_factored(DecodeArgs a) {
   }
   const int rr = ra + rf, T = rr + n;
   const int64_t pad0 = s * (int64_t)K - rr;  // pad slot of list index i is pad0 + i
+  // the inputs are issued before the pair stream; pairs stream in chunks of G * UN
+  const float4 q4 = sel4(kin, ld4nt(a.q + s * dk + 4 * colk));
+  const float4 k4 = RO ? zero4() : sel4(kin, ld4nt(a.k + s * dk + 4 * colk));
+  const float4 v4 = RO ? zero4() : sel4(vin, ld4nt(a.v + s * dv + 4 * colv));
+  const bool delta = ANYDELTA && !RO && (flags & FLAG_DELTA);
+  const float al = RO ? 1.f : uniformf(a.alpha[s]);
+  const float be = delta ? uniformf(a.beta[s]) : 0.f;
   float4 acc = zero4(), acck = zero4();
   for (int i0 = 0; i0 < T; i0 += G * UN) {
     float4 x[UN], y[UN];
-    float wt[UN], okf[UN];
+    float wt[UN];
 #pragma unroll
     for (int u = 0; u < UN; ++u) {
       const int iu = i0 + u * G + grp;
-      const bool ok = iu < T;
-      const int i = ok ? iu : T - 1;  // T >= 1 here
+      const int i = iu < T ? iu : T - 1;  // clamped pair (T >= 1 here); its weight is masked at use
       const float *xp, *yp, *wp;
       int64_t c;
       if (i < ra) {
@@ -95,16 +98,14 @@ __global__ __launch_bounds__(256) void k_decode_factored(DecodeArgs a) {
         c = pad0 + i;
         xp = a.pk; yp = a.pw; wp = a.pc;
       }
-      // clamped pair and lanes: q4, k4 are 0 off the key lanes, lanes off the value range are
-      // never stored, and a pair past the list gets weight 0 (applied at use, not at load)
+      // clamped lanes: q4, k4 are 0 off the key lanes and lanes off the value range are never stored
       x[u] = ld4nt(xp + c * dk + 4 * colk);
       y[u] = ld4nt(yp + c * dv + 4 * colv);
       wt[u] = ldnt(wp + c);
-      okf[u] = ok ? 1.f : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < UN; ++u) {
-      const float wu = wt[u] * okf[u];
+      const float wu = (i0 + u * G + grp < T) ? wt[u] : 0.f;
       const float cq = group_sum<P>(dot4(x[u], q4)) * wu;
       acc = fma4(cq, y[u], acc);
       if (delta) {
@@ -119,21 +120,18 @@ __global__ __launch_bounds__(256) void k_decode_factored(DecodeArgs a) {
     if (grp == 0 && vin) st4(a.o + s * dv + 4 * col, pq);
     return;
   } else {
-    const float al = a.alpha[s];
-    const float4 v4 = sel4(vin, ld4nt(a.v + s * dv + 4 * colv));
     float4 w4 = v4;
     if (delta) {
       acck = cross_group_sum4<P>(acck);
-      const float be = a.beta[s];
       w4 = scale4(be, sub4(v4, scale4(al * gamma, acck)));
     }
     const float kq = group_sum<P>(dot4(k4, q4));
     const float4 o4 = add4(scale4(al, pq), scale4(kq, w4));
     const float gnew = al * gamma;
     if (grp == 0) {
-      if (kin) st4(a.pk + (s * (int64_t)K + n) * dk + 4 * col, k4);
+      if (kin) st4nt(a.pk + (s * (int64_t)K + n) * dk + 4 * col, k4);
       if (vin) {
-        st4(a.pw + (s * (int64_t)K + n) * dv + 4 * col, w4);
+        st4nt(a.pw + (s * (int64_t)K + n) * dv + 4 * col, w4);
         st4(a.o + s * dv + 4 * col, o4);
       }
     }
@@ -364,11 +362,11 @@ __global__ __launch_bounds__(256) void k_dense_buf(DenseArgs a) {
   if constexpr (!FO) {
     for (int e = lane; e < (dv >> 2); e += 64) {
       st4(os + 4 * e, *reinterpret_cast<const float4 *>(OS + 4 * e));
-      if (DEC && !fold) st4(pwn + 4 * e, *reinterpret_cast<const float4 *>(WS + 4 * e));
+      if (DEC && !fold) st4nt(pwn + 4 * e, *reinterpret_cast<const float4 *>(WS + 4 * e));
     }
   }
   if constexpr (!RO) {
-    if (DEC && !fold && grp == 0 && kin) st4(a.pk + ((int64_t)slot * K + n) * dk + 4 * col, k4);
+    if (DEC && !fold && grp == 0 && kin) st4nt(a.pk + ((int64_t)slot * K + n) * dk + 4 * col, k4);
     if (lane == 0) {
       if (DEC && !fold) a.pc[(int64_t)slot * K + n] = 1.0f / ag;
       DenseSlot nr = rec;

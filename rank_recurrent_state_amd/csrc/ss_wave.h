@@ -111,6 +111,13 @@ __device__ __forceinline__ float4 sel4(bool ok, float4 v) {
 }
 __device__ __forceinline__ float self(bool ok, float v) { return ok ? v : 0.f; }
 __device__ __forceinline__ void st4(float *p, float4 v) { *reinterpret_cast<float4 *>(p) = v; }
+// streaming (write-once, read much later) stores
+__device__ __forceinline__ void st4nt(float *p, float4 v) {
+  __builtin_nontemporal_store(v.x, p);
+  __builtin_nontemporal_store(v.y, p + 1);
+  __builtin_nontemporal_store(v.z, p + 2);
+  __builtin_nontemporal_store(v.w, p + 3);
+}
 
 // make this lane's LDS writes visible to the other lanes of the wavefront
 __device__ __forceinline__ void wave_sync() {
