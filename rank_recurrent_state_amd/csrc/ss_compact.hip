@@ -127,6 +127,13 @@ __device__ __forceinline__ void cgs2_pair(float (&u)[kMaxM][NS], float (&v)[kMax
 
 // One-sided Jacobi on the 16 x 16 column-major C (columns >= m are zero),
 // accumulating the rotations into Vh.  Returns the number of sweeps run.
+// Pairs follow the round-robin (circle) order on M = m rounded up to even:
+// in round k, pair 0 is (k, M-1) and pair p > 0 is ((k+p) mod (M-1),
+// (k-p) mod (M-1)); both indices advance by one (mod M-1) from a round to
+// the next, so they are carried in registers instead of recomputed.  The
+// rotation zeroes the pair's inner product: zeta = (|y|^2 - |x|^2) / (2 x.y),
+// t = sign(zeta) / (|zeta| + sqrt(1 + zeta^2)), c = 1 / sqrt(1 + t^2), s = c t,
+// with the hardware reciprocal and reciprocal square root (about 1 ulp).
 __device__ int jacobi16(float *Cm, float *Vh, int m, int lane) {
   const int M = (m + 1) & ~1;
   if (M < 2) return 0;
@@ -137,15 +144,9 @@ __device__ int jacobi16(float *Cm, float *Vh, int m, int lane) {
   while (sweep < kMaxSweeps) {
     ++sweep;
     bool any = false;
+    int ci = p == 0 ? 0 : p % (M - 1);
+    int cj = p == 0 ? M - 1 : (M - 1 - p) % (M - 1);
     for (int k = 0; k < rounds; ++k) {
-      int ci, cj;
-      if (p == 0) {
-        ci = k;
-        cj = M - 1;
-      } else {
-        ci = (k + p) % (M - 1);
-        cj = (k - p + (M - 1)) % (M - 1);
-      }
       float x0 = 0.f, x1 = 0.f, y0 = 0.f, y1 = 0.f;
       if (act) {
         x0 = Cm[ci * 16 + sub];
@@ -157,12 +158,13 @@ __device__ int jacobi16(float *Cm, float *Vh, int m, int lane) {
       aa = group_sum<8>(aa);
       bb = group_sum<8>(bb);
       gg = group_sum<8>(gg);
-      const bool rot = act && gg != 0.f && fabsf(gg) > kTolJ * sqrtf(aa * bb);
+      const bool rot = act && gg != 0.f && fabsf(gg) > kTolJ * __builtin_amdgcn_sqrtf(aa * bb);
       if (rot) {
-        const float zeta = (bb - aa) / (2.f * gg);
+        const float zeta = (bb - aa) * (0.5f * __builtin_amdgcn_rcpf(gg));
         const float az = fabsf(zeta);
-        const float t = az > 1e10f ? 0.5f / zeta : copysignf(1.f, zeta) / (az + sqrtf(fmaf(zeta, zeta, 1.f)));
-        const float c = 1.0f / sqrtf(fmaf(t, t, 1.f)), sn = c * t;
+        const float t = az > 1e10f ? 0.5f * __builtin_amdgcn_rcpf(zeta)
+                                   : copysignf(__builtin_amdgcn_rcpf(az + __builtin_amdgcn_sqrtf(fmaf(zeta, zeta, 1.f))), zeta);
+        const float c = __builtin_amdgcn_rsqf(fmaf(t, t, 1.f)), sn = c * t;
         Cm[ci * 16 + sub] = c * x0 - sn * y0;
         Cm[ci * 16 + sub + 8] = c * x1 - sn * y1;
         Cm[cj * 16 + sub] = sn * x0 + c * y0;
@@ -176,6 +178,8 @@ __device__ int jacobi16(float *Cm, float *Vh, int m, int lane) {
       }
       any = any || (__builtin_amdgcn_ballot_w64(rot) != 0ull);
       wave_sync();
+      ci = (ci + 1 == M - 1) ? 0 : ci + 1;
+      if (p != 0) cj = (cj + 1 == M - 1) ? 0 : cj + 1;
     }
     if (!any) break;
   }
@@ -198,7 +202,7 @@ __device__ __forceinline__ void copy_comp(const float *su, const float *sv, floa
 template <typename DstOf>
 __device__ __forceinline__ void copy_comps(const Arena &src, int64_t c0, int cnt, int dk, int dv, int lane,
                                            DstOf dst_of) {
-  constexpr int UNC = 4;
+  constexpr int UNC = 8;
   const int dk4 = dk >> 2, tot4 = dk4 + (dv >> 2);
   const int n = cnt * tot4;
   for (int e0 = 0; e0 < n; e0 += 64 * UNC) {
