@@ -79,6 +79,9 @@ typedef struct {
   const float *eps;           /* host [N] truncation threshold eps >= 0, or NULL: eps_default */
   float eps_default;
   int64_t dense_capacity;     /* dense slots; 0 = N */
+  int64_t arena_components;   /* initial capacity (components) of each component ring, at least
+                                 what the initial data needs; 0 = automatic.  The rings grow on
+                                 their own (see ss_compact). */
 } ss_pool_desc;
 
 /* Initial states, host memory, copied during create.  Components of state s
@@ -121,15 +124,20 @@ typedef struct {
   uint64_t compact_flops;   /* algorithmic flops of all compactions so far */
   int64_t promotions;       /* factored -> dense conversions after create */
   int64_t cap_truncations;  /* frozen components dropped because max_frozen was reached */
+  int64_t ring_capacity[2]; /* component capacity of the active [0] and frozen [1] rings */
+  int64_t ring_used[2];     /* ring span from the oldest live segment to the head */
+  int64_t ring_head[2];     /* components allocated since the last re-pack (> capacity: wrapped) */
+  int64_t ring_repacks;     /* re-packs (growth or defragmentation) so far */
+  int64_t ring_syncs;       /* compactions that had to wait for the device to check ring room */
   double kernel_ms[SS_KERNEL_COUNT];       /* summed HIP-event durations while timing is on */
   int64_t kernel_launches[SS_KERNEL_COUNT];
 } ss_stats;
 
 /* Create a pool ([SS] 4.4 "Memory layout"): per state a 16-byte metadata
  * record; an active region and a separate frozen region of components, each
- * split per compaction group into two segments that alternate at every
- * compaction of the group; a pad of K slots per state kept apart from the
- * factors; and a dense region.  Initial data is uploaded on `stream`, and
+ * a ring in which every compaction group holds one exactly packed segment
+ * (groups laid out in the order they fall due); a pad of K slots per state
+ * kept apart from the factors; and a dense region.  Initial data is uploaded on `stream`, and
  * the call waits for it.  Errors: SS_ERR_ARG, SS_ERR_SHAPE, SS_ERR_OOM,
  * SS_ERR_HIP.  On success *out owns the pool; release it with
  * ss_state_pool_destroy. */
@@ -164,10 +172,16 @@ ss_status ss_readout(ss_pool *pool, const float *q, float *o, hipStream_t stream
  * C = R_L Sigma_C R_R^T; rotate back; merge with the frozen components (whose
  * sigma are scaled by Gamma); drop sigma < eps * sigma_max; the first r of
  * the merged list become active, the rest frozen; the pad empties and Gamma
- * resets to 1.  The result is written to the group's other segment.  With
+ * resets to 1.  The group's new components are allocated as one segment at
+ * the head of each ring and its old segment is released.  Before that, the
+ * host checks that the segment fits: it bounds each ring's usage without
+ * waiting for the device and, only when the bound is too close to the
+ * capacity, synchronizes `stream`, and re-packs the rings (growing them, a
+ * device allocation, when the live components need it).  With
  * promote_on_compact, a state left with more than L components moves to the
  * dense region ([SS] 4.4).  Dense states of the group get a non-empty pad
- * folded into H. */
+ * folded into H.  A ring found full on the device (not expected: the host
+ * check is conservative) leaves the pool in error (SS_ERR_CAPACITY). */
 ss_status ss_compact(ss_pool *pool, int32_t group, hipStream_t stream);
 
 /* Staggered schedule ([SS] 4.2 "Staggered compaction across layers"): the

@@ -196,8 +196,8 @@ __device__ __forceinline__ void copy_comp(const float *su, const float *sv, floa
   }
 }
 
-// Copy `cnt` components (u, v) starting at source component c0 of arena `src`
-// to the positions dst_of(f) of the merged list (slots >= total are dropped).
+// Copy `cnt` components (u, v) starting at ring position c0 of arena `src`
+// to the positions dst_of(f) (a component for which it returns false is dropped).
 // All lanes take float4 pieces of consecutive components, UNC pieces in flight.
 template <typename DstOf>
 __device__ __forceinline__ void copy_comps(const Arena &src, int64_t c0, int cnt, int dk, int dv, int lane,
@@ -212,7 +212,8 @@ __device__ __forceinline__ void copy_comps(const Arena &src, int64_t c0, int cnt
       const int e = e0 + q * 64 + lane;
       const int ec = e < n ? e : n - 1;  // clamped (n >= 1 inside the loop)
       const int f = ec / tot4, c = ec - f * tot4;
-      const float *p = c < dk4 ? src.u + (c0 + f) * dk + 4 * c : src.v + (c0 + f) * dv + 4 * (c - dk4);
+      const int64_t cs = wrap(c0 + f, src.cap);
+      const float *p = c < dk4 ? src.u + cs * dk + 4 * c : src.v + cs * dv + 4 * (c - dk4);
       x[q] = ld4(p);
     }
 #pragma unroll
@@ -233,9 +234,11 @@ __device__ __forceinline__ void copy_comps(const Arena &src, int64_t c0, int cnt
 template <int NS>
 __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   __shared__ float lds[4][kLdsPerWave];
+  __shared__ int wg_cnt[4][2];
+  __shared__ unsigned long long wg_base[2];
+  __shared__ int wg_ok;
   const int w = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int mi = blockIdx.x * 4 + w;
-  if (mi >= a.n_members) return;
   float *Rl = lds[w] + kOffRl;
   float *Rr = lds[w] + kOffRr;
   float *Cm = lds[w] + kOffCm;
@@ -247,32 +250,183 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   int *posL = reinterpret_cast<int *>(lds[w] + kOffPosL);
   float *fsl = lds[w] + kOffFs;
   int *posF = reinterpret_cast<int *>(lds[w] + kOffPosF);
-
-  const int s = uniform(a.members[mi]);
-  const Meta m = a.meta[s];
-  const uint32_t packed = (uint32_t)uniform((int)m.packed);
-  const uint32_t flags = meta_flags(packed);
-  if (flags & FLAG_DENSE) return;
-  const int ra = meta_ra(packed), rf = meta_rf(packed), n = meta_n(packed);
-  const int off_a = uniform(m.off_a), off_f = uniform(m.off_f);
-  const float gamma = uniformf(m.gamma);
   const int dk = a.dk, dv = a.dv, K = a.K, r = a.r;
-  const int64_t dst_a = a.dst_base_a + (int64_t)mi * r;
-  const int64_t dst_f = a.dst_base_f + (int64_t)mi * a.fcap;
+  const int64_t capA = a.act.cap, capF = a.frz.cap;
 
-  if (n == 0) {  // nothing buffered: move the components to the other segments unchanged
+  // ---- phase A: what this wave's state becomes -------------------------------------------
+  bool live = mi < a.n_members;  // a member of the group held in factored form
+  int s = 0, ra = 0, rf = 0, n = 0, off_a = 0, off_f = 0;
+  uint32_t flags = 0;
+  float gamma = 1.0f;
+  if (live) {
+    s = uniform(a.members[mi]);
+    const Meta m = a.meta[s];
+    const uint32_t packed = (uint32_t)uniform((int)m.packed);
+    flags = meta_flags(packed);
+    if (flags & FLAG_DENSE) {
+      live = false;
+    } else {
+      ra = meta_ra(packed);
+      rf = meta_rf(packed);
+      n = meta_n(packed);
+      off_a = uniform(m.off_a);
+      off_f = uniform(m.off_f);
+      gamma = uniformf(m.gamma);
+    }
+  }
+  const bool work = live && n > 0;  // a Brand update; without a pad the components move unchanged
+  const int mcol = ra + n;
+  int kl = 0, kf = 0, total = 0, ra2 = ra, rf2 = rf, sweeps = 0;
+  float uc[kMaxM][NS], vc[kMaxM][NS];
+  if (work) {
+    // frozen singular values (scaled by Gamma) to LDS: the merge searches them there
+    for (int f = lane; f < rf; f += 64) fsl[f] = a.frz.s[wrap(off_f + f, capF)] * gamma;
+#pragma unroll
+    for (int jj = 0; jj < kMaxM; ++jj) {
+      const bool valid = jj < mcol;
+      const int j = valid ? jj : mcol - 1;  // clamped: the loads stay in bounds (mcol >= 1 here)
+      const bool isact = j < ra;
+      const int64_t ca = wrap(off_a + j, capA);
+      const float *su = isact ? a.act.u + ca * dk : a.pk + ((int64_t)s * K + (j - ra)) * dk;
+      const float *sv = isact ? a.act.v + ca * dv : a.pw + ((int64_t)s * K + (j - ra)) * dv;
+#pragma unroll
+      for (int t = 0; t < NS; ++t) {
+        const int row = lane + 64 * t;
+        uc[jj][t] = self(valid && row < dk, su[row < dk ? row : dk - 1]);
+        vc[jj][t] = self(valid && row < dv, sv[row < dv ? row : dv - 1]);
+      }
+    }
+    if (lane < kMaxM) {
+      float wgt = 0.f;
+      if (lane < ra) wgt = a.act.s[wrap(off_a + lane, capA)] * gamma;
+      else if (lane < mcol) wgt = a.pc[(int64_t)s * K + (lane - ra)] * gamma;
+      scw[lane] = wgt;
+    }
+    cgs2_pair<NS>(uc, vc, mcol, lane, Rl, Rr);
+    wave_sync();
+    for (int e = lane; e < 256; e += 64) {
+      const int i = e & 15, j = e >> 4;
+      float acc = 0.f;
+      if (i < mcol && j < mcol) {
+        for (int t = (i > j ? i : j); t < mcol; ++t) acc = fmaf(Rl[t * 16 + i] * scw[t], Rr[t * 16 + j], acc);
+      }
+      Cm[j * 16 + i] = acc;
+      Vh[j * 16 + i] = (i == j) ? 1.f : 0.f;
+    }
+    wave_sync();
+    sweeps = jacobi16(Cm, Vh, mcol, lane);
+    if (lane < 16) {
+      float x = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x = fmaf(Cm[lane * 16 + i], Cm[lane * 16 + i], x);
+      sraw[lane] = lane < mcol ? sqrtf(x) : -1.f;
+    }
+    wave_sync();
+    if (lane < mcol) {
+      const float my = sraw[lane];
+      int rank = 0;
+      for (int i = 0; i < mcol; ++i) {
+        const float o = sraw[i];
+        rank += (o > my) || (o == my && i < lane);
+      }
+      perm[rank] = lane;
+      sgs[rank] = my;
+    }
+    wave_sync();
+
+    // merge with the frozen part and truncate: both lists are descending; on ties the local
+    // component comes first; drop sigma < eps * sigma_max and sigma = 0
+    const float smax = fmaxf(sgs[0], rf > 0 ? fsl[0] : 0.f);
+    const float thr = a.eps[s] * smax;
+    kl = __builtin_popcountll(__builtin_amdgcn_ballot_w64(lane < mcol && sgs[lane] >= thr && sgs[lane] > 0.f));
+    for (int f0 = 0; f0 < rf; f0 += 64) {
+      const int f = f0 + lane;
+      kf += __builtin_popcountll(__builtin_amdgcn_ballot_w64(f < rf && fsl[f] >= thr && fsl[f] > 0.f));
+    }
+    total = kl + kf;
+    const int cap_total = r + a.fcap;
+    if (total > cap_total) {
+      if (lane == 0)
+        __hip_atomic_fetch_add(&a.counters[C_CAP_TRUNC], (uint32_t)(total - cap_total), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+      total = cap_total;
+    }
+    ra2 = total < r ? total : r;
+    rf2 = total - ra2;
+    if (lane < kl) {  // local i goes after the frozen ones strictly greater than it
+      const float x = sgs[lane];
+      int lo = 0, hi = kf;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (fsl[mid] > x) lo = mid + 1;
+        else hi = mid;
+      }
+      posL[lane] = lane + lo;
+    }
+    for (int f = lane; f < kf; f += 64) {  // frozen f goes after the local ones >= it
+      const float x = fsl[f];
+      int c = 0;
+      for (int i = 0; i < kl; ++i) c += sgs[i] >= x ? 1 : 0;
+      posF[f] = f + c;
+    }
+    wave_sync();
+  }
+
+  // ---- allocation: the workgroup's new components, one atomic add per ring ----------------
+  if (lane == 0) {
+    wg_cnt[w][0] = live ? ra2 : 0;
+    wg_cnt[w][1] = live ? rf2 : 0;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int sa = 0, sf = 0;
+    for (int i = 0; i < 4; ++i) {
+      sa += wg_cnt[i][0];
+      sf += wg_cnt[i][1];
+    }
+    unsigned long long ba = 0, bf = 0;
+    bool ok = true;
+    if (sa) {
+      ba = __hip_atomic_fetch_add(&a.ring_a->head, (unsigned long long)sa, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ok = ok && ba + sa <= a.ring_a->limit;
+    }
+    if (sf) {
+      bf = __hip_atomic_fetch_add(&a.ring_f->head, (unsigned long long)sf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ok = ok && bf + sf <= a.ring_f->limit;
+    }
+    if (!ok) {  // the ring is full: the group's states keep their old form and the pool reports it
+      __hip_atomic_fetch_add(&a.ring_a->overflow, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *a.hflag = 1u;
+    }
+    wg_base[0] = ba;
+    wg_base[1] = bf;
+    wg_ok = ok ? 1 : 0;
+  }
+  __syncthreads();
+  if (!live || !wg_ok) return;
+  unsigned long long va = wg_base[0], vf = wg_base[1];
+  for (int i = 0; i < w; ++i) {
+    va += (unsigned long long)wg_cnt[i][0];
+    vf += (unsigned long long)wg_cnt[i][1];
+  }
+  const int64_t dst_a = (int64_t)(va % (unsigned long long)capA), dst_f = (int64_t)(vf % (unsigned long long)capF);
+
+  // ---- phase B: write the new components and the record ------------------------------------
+  if (!work) {  // nothing buffered: the components move unchanged, sigma takes Gamma in
     copy_comps(a.act, off_a, ra, dk, dv, lane, [&](int f, float *&du, float *&dvp) {
-      du = a.act.u + (dst_a + f) * dk;
-      dvp = a.act.v + (dst_a + f) * dv;
+      const int64_t c = wrap(dst_a + f, capA);
+      du = a.act.u + c * dk;
+      dvp = a.act.v + c * dv;
       return true;
     });
     copy_comps(a.frz, off_f, rf, dk, dv, lane, [&](int f, float *&du, float *&dvp) {
-      du = a.frz.u + (dst_f + f) * dk;
-      dvp = a.frz.v + (dst_f + f) * dv;
+      const int64_t c = wrap(dst_f + f, capF);
+      du = a.frz.u + c * dk;
+      dvp = a.frz.v + c * dv;
       return true;
     });
-    for (int f = lane; f < ra; f += 64) a.act.s[dst_a + f] = a.act.s[off_a + f] * gamma;
-    for (int f = lane; f < rf; f += 64) a.frz.s[dst_f + f] = a.frz.s[off_f + f] * gamma;
+    for (int f = lane; f < ra; f += 64) a.act.s[wrap(dst_a + f, capA)] = a.act.s[wrap(off_a + f, capA)] * gamma;
+    for (int f = lane; f < rf; f += 64) a.frz.s[wrap(dst_f + f, capF)] = a.frz.s[wrap(off_f + f, capF)] * gamma;
     if (lane == 0) {
       Meta nm;
       nm.off_a = (int32_t)dst_a;
@@ -283,100 +437,16 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
     }
     return;
   }
-
-  // frozen singular values (scaled by Gamma) to LDS: the merge searches them there
-  for (int f = lane; f < rf; f += 64) fsl[f] = a.frz.s[off_f + f] * gamma;
-  const int mcol = ra + n;
-  float uc[kMaxM][NS], vc[kMaxM][NS];
-#pragma unroll
-  for (int jj = 0; jj < kMaxM; ++jj) {
-    const bool valid = jj < mcol;
-    const int j = valid ? jj : mcol - 1;  // clamped: the loads stay in bounds (mcol >= 1 here)
-    const bool isact = j < ra;
-    const float *su = isact ? a.act.u + (int64_t)(off_a + j) * dk : a.pk + ((int64_t)s * K + (j - ra)) * dk;
-    const float *sv = isact ? a.act.v + (int64_t)(off_a + j) * dv : a.pw + ((int64_t)s * K + (j - ra)) * dv;
-#pragma unroll
-    for (int t = 0; t < NS; ++t) {
-      const int row = lane + 64 * t;
-      uc[jj][t] = self(valid && row < dk, su[row < dk ? row : dk - 1]);
-      vc[jj][t] = self(valid && row < dv, sv[row < dv ? row : dv - 1]);
-    }
-  }
-  if (lane < kMaxM) {
-    float wgt = 0.f;
-    if (lane < ra) wgt = a.act.s[off_a + lane] * gamma;
-    else if (lane < mcol) wgt = a.pc[(int64_t)s * K + (lane - ra)] * gamma;
-    scw[lane] = wgt;
-  }
-  cgs2_pair<NS>(uc, vc, mcol, lane, Rl, Rr);
-  wave_sync();
-  for (int e = lane; e < 256; e += 64) {
-    const int i = e & 15, j = e >> 4;
-    float acc = 0.f;
-    if (i < mcol && j < mcol) {
-      for (int t = (i > j ? i : j); t < mcol; ++t) acc = fmaf(Rl[t * 16 + i] * scw[t], Rr[t * 16 + j], acc);
-    }
-    Cm[j * 16 + i] = acc;
-    Vh[j * 16 + i] = (i == j) ? 1.f : 0.f;
-  }
-  wave_sync();
-  const int sweeps = jacobi16(Cm, Vh, mcol, lane);
-  if (lane < 16) {
-    float x = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) x = fmaf(Cm[lane * 16 + i], Cm[lane * 16 + i], x);
-    sraw[lane] = lane < mcol ? sqrtf(x) : -1.f;
-  }
-  wave_sync();
-  if (lane < mcol) {
-    const float my = sraw[lane];
-    int rank = 0;
-    for (int i = 0; i < mcol; ++i) {
-      const float o = sraw[i];
-      rank += (o > my) || (o == my && i < lane);
-    }
-    perm[rank] = lane;
-    sgs[rank] = my;
-  }
-  wave_sync();
-
-  // merge with the frozen part and truncate: both lists are descending; on ties the local
-  // component comes first; drop sigma < eps * sigma_max and sigma = 0
-  const float smax = fmaxf(sgs[0], rf > 0 ? fsl[0] : 0.f);
-  const float thr = a.eps[s] * smax;
-  const int kl = __builtin_popcountll(__builtin_amdgcn_ballot_w64(lane < mcol && sgs[lane] >= thr && sgs[lane] > 0.f));
-  int kf = 0;
-  for (int f0 = 0; f0 < rf; f0 += 64) {
-    const int f = f0 + lane;
-    kf += __builtin_popcountll(__builtin_amdgcn_ballot_w64(f < rf && fsl[f] >= thr && fsl[f] > 0.f));
-  }
-  int total = kl + kf;
-  const int cap_total = r + a.fcap;
-  if (total > cap_total) {
-    if (lane == 0)
-      __hip_atomic_fetch_add(&a.counters[C_CAP_TRUNC], (uint32_t)(total - cap_total), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-    total = cap_total;
-  }
-  const int ra2 = total < r ? total : r, rf2 = total - ra2;
-  if (lane < kl) {  // local i goes after the frozen ones strictly greater than it
-    const float x = sgs[lane];
-    int lo = 0, hi = kf;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (fsl[mid] > x) lo = mid + 1;
-      else hi = mid;
-    }
-    posL[lane] = lane + lo;
-  }
-  for (int f = lane; f < kf; f += 64) {  // frozen f goes after the local ones >= it
-    const float x = fsl[f];
-    int c = 0;
-    for (int i = 0; i < kl; ++i) c += sgs[i] >= x ? 1 : 0;
-    posF[f] = f + c;
-  }
-  wave_sync();
-
+  // merged position pos -> slot of the new active (pos < r) or frozen component
+  auto slot_u = [&](int pos) -> float * {
+    return pos < r ? a.act.u + wrap(dst_a + pos, capA) * dk : a.frz.u + wrap(dst_f + pos - r, capF) * dk;
+  };
+  auto slot_v = [&](int pos) -> float * {
+    return pos < r ? a.act.v + wrap(dst_a + pos, capA) * dv : a.frz.v + wrap(dst_f + pos - r, capF) * dv;
+  };
+  auto slot_s = [&](int pos) -> float * {
+    return pos < r ? a.act.s + wrap(dst_a + pos, capA) : a.frz.s + wrap(dst_f + pos - r, capF);
+  };
   // kept local components: U' = Q_L U_hat, V' = Q_R V_hat
   for (int i = 0; i < kl; ++i) {
     const int pos = posL[i];
@@ -399,8 +469,8 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
         ov[t] = fmaf(vc[tt][t], cv, ov[t]);
       }
     }
-    float *du = pos < r ? a.act.u + (dst_a + pos) * dk : a.frz.u + (dst_f + pos - r) * dk;
-    float *dvv = pos < r ? a.act.v + (dst_a + pos) * dv : a.frz.v + (dst_f + pos - r) * dv;
+    float *du = slot_u(pos);
+    float *dvv = slot_v(pos);
 #pragma unroll
     for (int t = 0; t < NS; ++t) {
       const int row = lane + 64 * t;
@@ -408,21 +478,18 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
       if (row < dv) dvv[row] = ov[t];
     }
   }
-  if (lane < kl && posL[lane] < total) {
-    const int pos = posL[lane];
-    (pos < r ? a.act.s[dst_a + pos] : a.frz.s[dst_f + pos - r]) = sgs[lane];
-  }
+  if (lane < kl && posL[lane] < total) *slot_s(posL[lane]) = sgs[lane];
   // kept frozen components: copied, sigma scaled by Gamma
   copy_comps(a.frz, off_f, kf, dk, dv, lane, [&](int f, float *&du, float *&dvp) {
     const int pos = posF[f];
     if (pos >= total) return false;
-    du = pos < r ? a.act.u + (dst_a + pos) * dk : a.frz.u + (dst_f + pos - r) * dk;
-    dvp = pos < r ? a.act.v + (dst_a + pos) * dv : a.frz.v + (dst_f + pos - r) * dv;
+    du = slot_u(pos);
+    dvp = slot_v(pos);
     return true;
   });
   for (int f = lane; f < kf; f += 64) {
     const int pos = posF[f];
-    if (pos < total) (pos < r ? a.act.s[dst_a + pos] : a.frz.s[dst_f + pos - r]) = fsl[f];
+    if (pos < total) *slot_s(pos) = fsl[f];
   }
   if (lane == 0) {
     Meta nm;
@@ -469,30 +536,33 @@ __global__ __launch_bounds__(256) void k_materialize(MaterializeArgs a) {
     const int s = a.list[li];
     const Meta m = a.meta[s];
     const uint32_t flags = meta_flags(m.packed) & FLAG_DELTA;
+    // component comp: the CSR row (initial states) or the ring slot of the active / frozen part
     int n1, n2;
-    const float *u1, *v1, *s1, *u2, *v2, *s2;
+    int64_t o0 = 0;
     float scale = 1.0f;
     if (a.csr_off) {
-      const int64_t o0 = a.csr_off[s], o1 = a.csr_off[s + 1];
-      n1 = (int)(o1 - o0);
-      u1 = a.csr_u + o0 * dk;
-      v1 = a.csr_v + o0 * dv;
-      s1 = a.csr_s + o0;
+      o0 = a.csr_off[s];
+      n1 = (int)(a.csr_off[s + 1] - o0);
       n2 = 0;
-      u2 = u1;
-      v2 = v1;
-      s2 = s1;
     } else {
       n1 = (int)meta_ra(m.packed);
       n2 = (int)meta_rf(m.packed);
-      u1 = a.act.u + (int64_t)m.off_a * dk;
-      v1 = a.act.v + (int64_t)m.off_a * dv;
-      s1 = a.act.s + m.off_a;
-      u2 = a.frz.u + (int64_t)m.off_f * dk;
-      v2 = a.frz.v + (int64_t)m.off_f * dv;
-      s2 = a.frz.s + m.off_f;
       scale = m.gamma;
     }
+    auto comp_u = [&](int comp) -> const float * {
+      if (a.csr_off) return a.csr_u + (o0 + comp) * dk;
+      return comp < n1 ? a.act.u + wrap(m.off_a + comp, a.act.cap) * dk
+                       : a.frz.u + wrap(m.off_f + comp - n1, a.frz.cap) * dk;
+    };
+    auto comp_v = [&](int comp) -> const float * {
+      if (a.csr_off) return a.csr_v + (o0 + comp) * dv;
+      return comp < n1 ? a.act.v + wrap(m.off_a + comp, a.act.cap) * dv
+                       : a.frz.v + wrap(m.off_f + comp - n1, a.frz.cap) * dv;
+    };
+    auto comp_s = [&](int comp) -> float {
+      if (a.csr_off) return a.csr_s[o0 + comp];
+      return comp < n1 ? a.act.s[wrap(m.off_a + comp, a.act.cap)] : a.frz.s[wrap(m.off_f + comp - n1, a.frz.cap)];
+    };
     __syncthreads();
     if (t == 0) {
       const uint32_t slot =
@@ -518,15 +588,15 @@ __global__ __launch_bounds__(256) void k_materialize(MaterializeArgs a) {
         __syncthreads();
         for (int e = t; e < kMatCH * dk; e += 256) {
           const int cc = e / dk, i = e - cc * dk, comp = c0 + cc;
-          su[e] = comp < total ? (comp < n1 ? u1[(int64_t)comp * dk + i] : u2[(int64_t)(comp - n1) * dk + i]) : 0.f;
+          su[e] = comp < total ? comp_u(comp)[i] : 0.f;
         }
         for (int e = t; e < kMatCH * dv; e += 256) {
           const int cc = e / dv, j = e - cc * dv, comp = c0 + cc;
-          sv[e] = comp < total ? (comp < n1 ? v1[(int64_t)comp * dv + j] : v2[(int64_t)(comp - n1) * dv + j]) : 0.f;
+          sv[e] = comp < total ? comp_v(comp)[j] : 0.f;
         }
         if (t < kMatCH) {
           const int comp = c0 + t;
-          ss[t] = comp < total ? scale * (comp < n1 ? s1[comp] : s2[comp - n1]) : 0.f;
+          ss[t] = comp < total ? scale * comp_s(comp) : 0.f;
         }
         __syncthreads();
         if (act) {
@@ -592,9 +662,7 @@ __global__ __launch_bounds__(256) void k_scatter(ScatterArgs a) {
     }
     return;
   }
-  const int g = a.group_of_state[s];
-  const int64_t mi = a.member_index[s];
-  const int64_t dst_a = a.base_a[g] + mi * a.r, dst_f = a.base_f[g] + mi * a.fcap;
+  const int64_t dst_a = a.dst_a[s], dst_f = a.dst_f[s];
   const int ra = R < a.r ? R : a.r, rf = R - ra;
   const int dk = a.dk, dv = a.dv;
   for (int c = 0; c < R; ++c) {
@@ -633,6 +701,61 @@ __global__ __launch_bounds__(256) void k_prune_factored(const int32_t *src, cons
                                   __HIP_MEMORY_SCOPE_AGENT);
   base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
   if (keep) dst[base + __builtin_popcountll(mask & ((1ull << lane) - 1ull))] = s;
+}
+
+// ring bookkeeping around a compaction: seg_x[2 g] / seg_x[2 g + 1] are the virtual start / end of
+// group g's segment (start == end: no live segment)
+__global__ void k_ring_begin(Ring *ra, Ring *rf, const unsigned long long *seg_a, const unsigned long long *seg_f,
+                             int n_groups, int64_t cap_a, int64_t cap_f) {
+  if (threadIdx.x != 0) return;
+  unsigned long long ta = ra->head, tf = rf->head;
+  for (int g = 0; g < n_groups; ++g) {
+    if (seg_a[2 * g + 1] > seg_a[2 * g] && seg_a[2 * g] < ta) ta = seg_a[2 * g];
+    if (seg_f[2 * g + 1] > seg_f[2 * g] && seg_f[2 * g] < tf) tf = seg_f[2 * g];
+  }
+  ra->limit = ta + (unsigned long long)cap_a;
+  rf->limit = tf + (unsigned long long)cap_f;
+  ra->begin = ra->head;
+  rf->begin = rf->head;
+}
+
+__global__ void k_ring_end(Ring *ra, Ring *rf, unsigned long long *seg_a, unsigned long long *seg_f, int g) {
+  if (threadIdx.x != 0) return;
+  seg_a[2 * g] = ra->begin;
+  seg_a[2 * g + 1] = ra->head;
+  seg_f[2 * g] = rf->begin;
+  seg_f[2 * g + 1] = rf->head;
+}
+
+// one wavefront per state: copy its live components to the new rings
+__global__ __launch_bounds__(256) void k_repack(RepackArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t s = (int64_t)blockIdx.x * 4 + uniform(threadIdx.x >> 6);
+  if (s >= a.N) return;
+  const int64_t na = a.new_a[s], nf = a.new_f[s];
+  if (na < 0) return;
+  const Meta m = a.meta[s];
+  const uint32_t packed = (uint32_t)uniform((int)m.packed);
+  const int ra = meta_ra(packed), rf = meta_rf(packed);
+  const int dk = a.dk, dv = a.dv;
+  copy_comps(a.src_a, m.off_a, ra, dk, dv, lane, [&](int f, float *&du, float *&dvp) {
+    du = a.dst_a.u + wrap(na + f, a.dst_a.cap) * dk;
+    dvp = a.dst_a.v + wrap(na + f, a.dst_a.cap) * dv;
+    return true;
+  });
+  copy_comps(a.src_f, m.off_f, rf, dk, dv, lane, [&](int f, float *&du, float *&dvp) {
+    du = a.dst_f.u + wrap(nf + f, a.dst_f.cap) * dk;
+    dvp = a.dst_f.v + wrap(nf + f, a.dst_f.cap) * dv;
+    return true;
+  });
+  for (int f = lane; f < ra; f += 64) a.dst_a.s[wrap(na + f, a.dst_a.cap)] = a.src_a.s[wrap(m.off_a + f, a.src_a.cap)];
+  for (int f = lane; f < rf; f += 64) a.dst_f.s[wrap(nf + f, a.dst_f.cap)] = a.src_f.s[wrap(m.off_f + f, a.src_f.cap)];
+  if (lane == 0) {
+    Meta nm = m;
+    nm.off_a = (int32_t)na;
+    nm.off_f = (int32_t)nf;
+    a.meta[s] = nm;
+  }
 }
 
 __global__ void k_copy_count(const uint32_t *src, uint32_t *dst) {
@@ -680,6 +803,24 @@ hipError_t launch_prune_factored(const int32_t *src, const uint32_t *src_count, 
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(k_copy_count, dim3(1), dim3(64), 0, st, dst_count, host_count);
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_begin(Ring *ra, Ring *rf, const unsigned long long *seg_a, const unsigned long long *seg_f,
+                             int n_groups, int64_t cap_a, int64_t cap_f, hipStream_t st) {
+  hipLaunchKernelGGL(k_ring_begin, dim3(1), dim3(64), 0, st, ra, rf, seg_a, seg_f, n_groups, cap_a, cap_f);
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_end(Ring *ra, Ring *rf, unsigned long long *seg_a, unsigned long long *seg_f, int g,
+                           hipStream_t st) {
+  hipLaunchKernelGGL(k_ring_end, dim3(1), dim3(64), 0, st, ra, rf, seg_a, seg_f, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_repack(const RepackArgs &a, hipStream_t st) {
+  if (a.N <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_repack, dim3((unsigned)((a.N + 3) / 4)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

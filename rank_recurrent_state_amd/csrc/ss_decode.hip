@@ -89,10 +89,10 @@ __global__ __launch_bounds__(256) void k_decode_factored(DecodeArgs a) {
       const float *xp, *yp, *wp;
       int64_t c;
       if (i < ra) {
-        c = off_a + i;
+        c = wrap(off_a + i, a.act.cap);
         xp = a.act.u; yp = a.act.v; wp = a.act.s;
       } else if (i < rr) {
-        c = off_f + (i - ra);
+        c = wrap(off_f + (i - ra), a.frz.cap);
         xp = a.frz.u; yp = a.frz.v; wp = a.frz.s;
       } else {
         c = pad0 + i;

@@ -12,10 +12,15 @@
 //   dslot  [cap_d]            16-byte record per dense slot (state id, pad fill, flags, Gamma)
 //   dense pads [cap_d][K]     k [.][K][d_k], w [.][K][d_v], c [.][K], indexed by slot
 // Everything a dense-region step reads, except q, k, v, is addressed by the slot alone.
-// Each compaction group owns two segments in each arena; a compaction reads
-// the group's current segment and writes the other one.  A state's slice of
-// a segment starts at (segment base + its index within the group * per-state
-// capacity); the record holds the start of the live components.
+//
+// The active and frozen arenas are rings of `cap` components.  Positions are
+// virtual (64-bit, only growing); component c lives at c mod cap, and a
+// state's components are consecutive in that sense, so the record holds the
+// physical start and a reader wraps once (wrap()).  A compaction allocates
+// the new components of its group from the ring head, one atomic add per
+// workgroup, so a group's components form one exactly packed segment; the
+// group's previous segment is released when the compaction completes, and
+// the ring tail is the oldest segment still live.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -68,6 +73,18 @@ struct __attribute__((aligned(16))) DenseSlot {
 
 struct Arena {
   float *u, *v, *s;
+  int64_t cap;  // components (a ring)
+};
+
+// physical slot of ring position (start + i), start < cap, i < cap
+__host__ __device__ inline int64_t wrap(int64_t c, int64_t cap) { return c >= cap ? c - cap : c; }
+
+// allocation state of one ring (device memory)
+struct Ring {
+  unsigned long long head;   // next free virtual position
+  unsigned long long limit;  // allocations must end at or before this (tail + cap), set per compaction
+  unsigned long long begin;  // head when the running compaction started
+  unsigned long long overflow;  // allocations refused (the ring was full)
 };
 
 struct DecodeArgs {
@@ -106,8 +123,9 @@ struct CompactArgs {
   const int32_t *members;      // state ids of the group, in member order
   const float *eps;
   Meta *meta;
-  Arena act, frz;              // arenas (segments addressed through bases)
-  int64_t src_base_a, dst_base_a, src_base_f, dst_base_f;   // segment bases (components); src only informative
+  Arena act, frz;
+  Ring *ring_a, *ring_f;       // the new components are allocated from these
+  uint32_t *hflag;             // host-mapped flag raised when a ring is full
   float *pk, *pw, *pc;
   int32_t *promote_list;
   uint32_t *counters;
@@ -136,9 +154,7 @@ struct ScatterArgs {
   int dk, dv, r, L, fcap, force_dense;
   const int64_t *csr_off;
   const float *csr_u, *csr_v, *csr_s;
-  const int32_t *member_index;   // index of each state within its group
-  const int32_t *group_of_state;
-  const int64_t *base_a, *base_f;  // per group: segment base (components) for parity 0
+  const int64_t *dst_a, *dst_f;   // per state: first ring position of its active / frozen components
   const uint8_t *rule;
   Meta *meta;
   Arena act, frz;
@@ -156,6 +172,21 @@ hipError_t launch_compact(const CompactArgs &a, hipStream_t st);
 hipError_t launch_materialize(const MaterializeArgs &a, int64_t grid_upper, hipStream_t st);
 hipError_t launch_scatter(const ScatterArgs &a, hipStream_t st);
 hipError_t launch_zero_u32(uint32_t *p, int n, hipStream_t st);
+// before a compaction of group g: limit = (oldest live segment start) + cap, begin = head, per ring;
+// after it: the group's segment becomes [begin, head)
+hipError_t launch_ring_begin(Ring *ra, Ring *rf, const unsigned long long *seg_a, const unsigned long long *seg_f,
+                             int n_groups, int64_t cap_a, int64_t cap_f, hipStream_t st);
+hipError_t launch_ring_end(Ring *ra, Ring *rf, unsigned long long *seg_a, unsigned long long *seg_f, int g,
+                           hipStream_t st);
+// copy every factored state's components into new rings at the given positions (arena growth)
+struct RepackArgs {
+  int64_t N;
+  int dk, dv;
+  Meta *meta;
+  Arena src_a, src_f, dst_a, dst_f;
+  const int64_t *new_a, *new_f;  // per state: new first position (physical) or -1 for dense states
+};
+hipError_t launch_repack(const RepackArgs &a, hipStream_t st);
 // drop the states that have become dense from a factored-state list (src -> dst, dst_count zeroed by
 // the caller), then copy the new length to a host-visible word
 hipError_t launch_prune_factored(const int32_t *src, const uint32_t *src_count, int64_t n_upper, int32_t *dst,

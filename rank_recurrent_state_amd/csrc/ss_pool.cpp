@@ -1,18 +1,21 @@
 // ss_pool.cpp -- host side of libsinkstate.so: argument checks, pool layout
 // and device allocation, launch orchestration, export and statistics.
 //
-// Pool layout (SinkState 4.4 "Memory layout"): the states are listed by
-// compaction group; group g with n_g states owns, in each of the active and
-// frozen arenas, two segments of n_g * cap components (cap = r for the
-// active arena; L + K - r, or max_frozen when promotion is off, for the
-// frozen arena).  A compaction of g reads its current segment and writes the
-// other one, so the group's storage is rewritten to fit the new ranks and the
-// per-state offsets in the 16-byte records are updated; nothing is ever
-// written in place while it may still be read.
+// Pool layout (SinkState 4.4 "Memory layout": active and frozen factors in
+// their own contiguous regions, offsets per state).  Each region is a ring of
+// components; the states are listed by compaction group, and each group's
+// components form one exactly packed segment of the ring.  A compaction of
+// group g allocates the group's new segment at the ring head (never writing
+// what may still be read) and releases the old one, so with the groups laid
+// out in the order in which they fall due the ring holds the live components
+// plus one group's growth.  The host bounds the ring usage without waiting
+// for the device (see ensure_ring_space) and re-packs, growing the ring,
+// only when the bound says the next compaction might not fit.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cmath>
+#include <deque>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -31,7 +34,7 @@ ss_status fail(ss_status st, const std::string &msg) {
 }
 
 // host-mapped words: error flags raised by kernels, and the length of the factored-state list
-enum HostFlag { HF_PAD = 0, HF_DENSE_CAP = 1, HF_FACT = 2, HF_N = 4 };
+enum HostFlag { HF_PAD = 0, HF_DENSE_CAP = 1, HF_FACT = 2, HF_RING = 3, HF_N = 4 };
 
 }  // namespace
 
@@ -41,14 +44,28 @@ struct ss_pool {
   bool any_delta = false;
   std::vector<int32_t> group_offset;
   std::vector<int64_t> group_start, group_size;
-  std::vector<int> parity;
+  std::vector<int32_t> members_host;  // state ids grouped by compaction group
   int64_t cap_d = 0;
   int64_t dense_upper = 0;
   // device memory
   ss::Meta *meta = nullptr;
   int32_t *members = nullptr;
   float *eps = nullptr;
-  ss::Arena act{nullptr, nullptr, nullptr}, frz{nullptr, nullptr, nullptr};
+  ss::Arena act{nullptr, nullptr, nullptr, 0}, frz{nullptr, nullptr, nullptr, 0};
+  // rings of components (0: active, 1: frozen): device allocation state and per-group segments,
+  // and the host's bounds on them (see ensure_ring_space)
+  void *ring_blk[2] = {nullptr, nullptr};
+  size_t ring_bytes[2] = {0, 0};
+  ss::Ring *ring = nullptr;            // [2]
+  unsigned long long *seg = nullptr;   // [2][2 G]: virtual start, end of each group's segment
+  // Segments of each ring in allocation order (group -1: a released gap), each with an upper
+  // bound of its size; the latest record of a group is its live segment.
+  struct RingRec { int64_t seq; int g; int64_t n; };
+  std::deque<RingRec> recs[2];
+  std::vector<int64_t> last_seq[2];    // per group: seq of its live segment, -1 if none
+  std::vector<int64_t> seg_bound[2];   // per group: upper bound of its live segment size
+  int64_t seq = 0;
+  int64_t repacks = 0, ring_syncs = 0;
   float *pk = nullptr, *pw = nullptr, *pc = nullptr;
   float *dense = nullptr;
   ss::DenseSlot *dslot = nullptr;
@@ -78,8 +95,8 @@ struct ss_pool {
   double kernel_ms[SS_KERNEL_COUNT] = {0};
   int64_t kernel_launches[SS_KERNEL_COUNT] = {0};
 
-  int64_t base_a(int g, int p) const { return 2 * r * group_start[g] + (int64_t)p * r * group_size[g]; }
-  int64_t base_f(int g, int p) const { return 2 * (int64_t)fcap * group_start[g] + (int64_t)p * fcap * group_size[g]; }
+  ss::Arena &arena(int R) { return R == 0 ? act : frz; }
+  int64_t per_state_cap(int R) const { return R == 0 ? r : fcap; }
 };
 
 namespace {
@@ -107,6 +124,10 @@ void free_all(ss_pool *p) {
   p->spare.clear();
   for (void *q : p->dev_allocs) (void)hipFree(q);
   p->dev_allocs.clear();
+  for (int R = 0; R < 2; ++R) {
+    if (p->ring_blk[R]) (void)hipFree(p->ring_blk[R]);
+    p->ring_blk[R] = nullptr;
+  }
   if (p->hflags) (void)hipHostFree(p->hflags);
   p->hflags = nullptr;
 }
@@ -140,6 +161,196 @@ ss_status hip_fail(hipError_t e, const char *what) {
   return fail(SS_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
+// one ring: u [cap][d_k], v [cap][d_v], sigma [cap] in a single allocation
+hipError_t ring_alloc(ss_pool *p, int64_t cap, void **blk, size_t *bytes, ss::Arena *out) {
+  *bytes = sizeof(float) * (size_t)cap * (p->dk + p->dv + 1);
+  hipError_t e = hipMalloc(blk, *bytes);
+  if (e != hipSuccess) return e;
+  float *f = static_cast<float *>(*blk);
+  out->u = f;
+  out->v = f + (size_t)cap * p->dk;
+  out->s = out->v + (size_t)cap * p->dv;
+  out->cap = cap;
+  return hipSuccess;
+}
+
+// Group order in which the rings are laid out: by the next step at which each group is
+// due, counted from a step at which group `first` is due (first < 0: from step 0, before
+// any compaction), so that the group compacted next holds the oldest segment.
+std::vector<int> ring_order(const ss_pool *p, int first) {
+  std::vector<int> ord(p->G);
+  std::vector<int64_t> key(p->G);
+  for (int g = 0; g < p->G; ++g) {
+    ord[g] = g;
+    if (first >= 0) {
+      key[g] = (((int64_t)p->group_offset[first] - p->group_offset[g]) % p->K + p->K) % p->K;
+    } else {
+      const int64_t k = ((-(int64_t)p->group_offset[g]) % p->K + p->K) % p->K;
+      key[g] = k == 0 ? p->K : k;
+    }
+  }
+  std::stable_sort(ord.begin(), ord.end(), [&](int x, int y) { return key[x] < key[y]; });
+  return ord;
+}
+
+// Lay the factored states' components out group by group in `ord`, from ring position 0.
+// cnt[R][s]: active (R = 0) / frozen (R = 1) components of state s, -1 for dense states.
+void ring_layout(const ss_pool *p, const std::vector<int> &ord, const std::vector<int32_t> (&cnt)[2],
+                 std::vector<int64_t> (&pos)[2], std::vector<unsigned long long> &seg, int64_t (&tot)[2]) {
+  for (int R = 0; R < 2; ++R) {
+    pos[R].assign(p->N, -1);
+    tot[R] = 0;
+  }
+  seg.assign(4 * (size_t)p->G, 0ull);
+  for (int g : ord) {
+    for (int R = 0; R < 2; ++R) seg[(size_t)R * 2 * p->G + 2 * g] = (unsigned long long)tot[R];
+    for (int64_t i = p->group_start[g]; i < p->group_start[g] + p->group_size[g]; ++i) {
+      const int32_t s = p->members_host[i];
+      if (cnt[0][s] < 0) continue;
+      for (int R = 0; R < 2; ++R) {
+        pos[R][s] = tot[R];
+        tot[R] += cnt[R][s];
+      }
+    }
+    for (int R = 0; R < 2; ++R) seg[(size_t)R * 2 * p->G + 2 * g + 1] = (unsigned long long)tot[R];
+  }
+}
+
+ss_status hip_fail(hipError_t e, const char *what);
+
+// Reset a ring's records from exact segments ([2 G] virtual start, end) and head.
+void ring_records(ss_pool *p, int R, const unsigned long long *seg, unsigned long long head) {
+  std::vector<int> live;
+  for (int g = 0; g < p->G; ++g) {
+    p->last_seq[R][g] = -1;
+    p->seg_bound[R][g] = (int64_t)(seg[2 * g + 1] - seg[2 * g]);
+    if (seg[2 * g + 1] > seg[2 * g]) live.push_back(g);
+  }
+  std::sort(live.begin(), live.end(), [&](int x, int y) { return seg[2 * x] < seg[2 * y]; });
+  p->recs[R].clear();
+  unsigned long long at = live.empty() ? head : seg[2 * live[0]];
+  for (int g : live) {
+    if (seg[2 * g] > at) p->recs[R].push_back({p->seq++, -1, (int64_t)(seg[2 * g] - at)});
+    p->last_seq[R][g] = p->seq;
+    p->recs[R].push_back({p->seq++, g, (int64_t)(seg[2 * g + 1] - seg[2 * g])});
+    at = seg[2 * g + 1];
+  }
+  if (head > at) p->recs[R].push_back({p->seq++, -1, (int64_t)(head - at)});
+}
+
+// Upper bound of head - tail of ring R: the records from the oldest live segment on.
+int64_t ring_usage_bound(ss_pool *p, int R) {
+  int64_t oldest = INT64_MAX;
+  for (int g = 0; g < p->G; ++g)
+    if (p->last_seq[R][g] >= 0 && p->seg_bound[R][g] > 0) oldest = std::min(oldest, p->last_seq[R][g]);
+  while (!p->recs[R].empty() && p->recs[R].front().seq < oldest) p->recs[R].pop_front();
+  int64_t u = 0;
+  for (const auto &x : p->recs[R]) u += x.n;
+  return u;
+}
+
+// Re-pack every factored state's components, exactly, into rings of capacity newcap (after a
+// synchronization), with group `first` at the tail.
+ss_status ring_repack(ss_pool *p, int first, const int64_t (&newcap)[2], hipStream_t stream) {
+  std::vector<ss::Meta> meta(p->N);
+  hipError_t e = hipMemcpy(meta.data(), p->meta, sizeof(ss::Meta) * p->N, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "repack meta");
+  std::vector<int32_t> cnt[2] = {std::vector<int32_t>(p->N, -1), std::vector<int32_t>(p->N, -1)};
+  for (int64_t s = 0; s < p->N; ++s) {
+    const uint32_t pk = meta[s].packed;
+    if (ss::meta_flags(pk) & ss::FLAG_DENSE) continue;
+    cnt[0][s] = (int32_t)ss::meta_ra(pk);
+    cnt[1][s] = (int32_t)ss::meta_rf(pk);
+  }
+  std::vector<int64_t> pos[2];
+  std::vector<unsigned long long> seg;
+  int64_t tot[2];
+  ring_layout(p, ring_order(p, first), cnt, pos, seg, tot);
+  void *blk[2] = {nullptr, nullptr};
+  size_t bytes[2] = {0, 0};
+  ss::Arena na[2];
+  int64_t *d_pos[2] = {nullptr, nullptr};
+  for (int R = 0; R < 2 && e == hipSuccess; ++R) e = ring_alloc(p, newcap[R], &blk[R], &bytes[R], &na[R]);
+  for (int R = 0; R < 2 && e == hipSuccess; ++R) e = hipMalloc(&d_pos[R], sizeof(int64_t) * p->N);
+  for (int R = 0; R < 2 && e == hipSuccess; ++R)
+    e = hipMemcpy(d_pos[R], pos[R].data(), sizeof(int64_t) * p->N, hipMemcpyHostToDevice);
+  if (e == hipSuccess) {
+    ss::RepackArgs ra{};
+    ra.N = p->N; ra.dk = p->dk; ra.dv = p->dv; ra.meta = p->meta;
+    ra.src_a = p->act; ra.src_f = p->frz; ra.dst_a = na[0]; ra.dst_f = na[1]; ra.new_a = d_pos[0]; ra.new_f = d_pos[1];
+    e = ss::launch_repack(ra, stream);
+  }
+  ss::Ring ring[2] = {};
+  for (int R = 0; R < 2; ++R) ring[R].head = ring[R].begin = (unsigned long long)tot[R];
+  if (e == hipSuccess) e = hipMemcpyAsync(p->ring, ring, sizeof(ring), hipMemcpyHostToDevice, stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(p->seg, seg.data(), sizeof(unsigned long long) * seg.size(),
+                                          hipMemcpyHostToDevice, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  for (int R = 0; R < 2; ++R)
+    if (d_pos[R]) (void)hipFree(d_pos[R]);
+  if (e != hipSuccess) {
+    for (int R = 0; R < 2; ++R)
+      if (blk[R]) (void)hipFree(blk[R]);
+    return e == hipErrorOutOfMemory ? fail(SS_ERR_OOM, "ring growth: device allocation failed")
+                                    : hip_fail(e, "ring repack");
+  }
+  for (int R = 0; R < 2; ++R) {
+    (void)hipFree(p->ring_blk[R]);
+    p->ring_blk[R] = blk[R];
+    p->ring_bytes[R] = bytes[R];
+    p->arena(R) = na[R];
+    ring_records(p, R, seg.data() + (size_t)R * 2 * p->G, (unsigned long long)tot[R]);
+  }
+  p->repacks++;
+  return SS_OK;
+}
+
+// Before a compaction of group g: make sure each ring can take the group's new segment.  A
+// state's new active (frozen) count exceeds its old one by at most its pad fill <= K, and is
+// at most r (the frozen capacity), so the segment bound ab[R] is the old bound plus K per
+// member, capped.  The host bounds head - tail by the records from the oldest live segment on
+// and synchronizes only when that bound plus ab could exceed the capacity; it then takes the
+// exact figures from the device, and re-packs (growing the ring if the live components need
+// it) only if those leave too little room.
+ss_status ensure_ring_space(ss_pool *p, int g, hipStream_t stream, int64_t (&ab)[2]) {
+  const int64_t ng = p->group_size[g];
+  auto bound = [&](int R) {
+    return std::min<int64_t>(ng * p->per_state_cap(R), p->seg_bound[R][g] + (int64_t)p->K * ng);
+  };
+  bool need = false;
+  for (int R = 0; R < 2; ++R) {
+    ab[R] = bound(R);
+    need = need || ring_usage_bound(p, R) + ab[R] > p->arena(R).cap;
+  }
+  if (!need) return SS_OK;
+  hipError_t e = hipStreamSynchronize(stream);
+  ss::Ring ring[2];
+  std::vector<unsigned long long> seg(4 * (size_t)p->G);
+  if (e == hipSuccess) e = hipMemcpy(ring, p->ring, sizeof(ring), hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemcpy(seg.data(), p->seg, sizeof(unsigned long long) * seg.size(), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "ring sync");
+  p->ring_syncs++;
+  bool repack = false;
+  int64_t live[2] = {0, 0};
+  for (int R = 0; R < 2; ++R) {
+    ring_records(p, R, seg.data() + (size_t)R * 2 * p->G, ring[R].head);
+    for (int gg = 0; gg < p->G; ++gg) live[R] += p->seg_bound[R][gg];
+    ab[R] = bound(R);
+    repack = repack || ring_usage_bound(p, R) + ab[R] > p->arena(R).cap;
+  }
+  if (!repack) return SS_OK;
+  int64_t newcap[2];
+  for (int R = 0; R < 2; ++R) {
+    const int64_t need_R = live[R] + ab[R], cap = p->arena(R).cap;
+    newcap[R] = 2 * need_R > cap ? std::max<int64_t>(cap, 2 * need_R) : cap;
+    if (newcap[R] >= (int64_t)INT32_MAX) return fail(SS_ERR_CAPACITY, "a component ring would exceed 2^31 slots");
+  }
+  const ss_status st = ring_repack(p, g, newcap, stream);
+  if (st != SS_OK) return st;
+  for (int R = 0; R < 2; ++R) ab[R] = bound(R);
+  return SS_OK;
+}
+
 // check the host-visible error flags that kernels raise
 ss_status poll(ss_pool *p) {
   if (p->sticky != SS_OK) return fail(p->sticky, p->sticky_msg);
@@ -151,6 +362,9 @@ ss_status poll(ss_pool *p) {
     } else if (f[HF_DENSE_CAP]) {
       p->sticky = SS_ERR_CAPACITY;
       p->sticky_msg = "the dense region is full; raise dense_capacity";
+    } else if (f[HF_RING]) {
+      p->sticky = SS_ERR_CAPACITY;
+      p->sticky_msg = "a component ring was full during a compaction";
     }
   }
   if (p->sticky != SS_OK) return fail(p->sticky, p->sticky_msg);
@@ -253,8 +467,8 @@ ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipSt
   const int64_t cap_d = d->force_dense ? N : (d->dense_capacity ? d->dense_capacity : N);
   if (n_dense0 > cap_d) return fail(SS_ERR_CAPACITY, "more initial dense states than dense_capacity");
   const bool factored = !d->force_dense;
-  if (factored && (2 * (int64_t)fcap * N >= (int64_t)INT32_MAX || 2 * (int64_t)r * N >= (int64_t)INT32_MAX))
-    return fail(SS_ERR_CAPACITY, "too many states for 32-bit component offsets");
+  if (d->arena_components < 0 || d->arena_components >= (int64_t)INT32_MAX)
+    return fail(SS_ERR_ARG, "arena_components must be in [0, 2^31)");
 
   ss_pool *p = new (std::nothrow) ss_pool();
   if (!p) return fail(SS_ERR_OOM, "host allocation failed");
@@ -264,22 +478,40 @@ ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipSt
   if (d->group_offset) for (int g = 0; g < G; ++g) p->group_offset[g] = d->group_offset[g];
   p->group_size.assign(G, 0);
   p->group_start.assign(G, 0);
-  p->parity.assign(G, 0);
   for (int64_t s = 0; s < N; ++s) p->group_size[grp[s]]++;
   for (int g = 1; g < G; ++g) p->group_start[g] = p->group_start[g - 1] + p->group_size[g - 1];
-  std::vector<int32_t> members(N), member_index(N);
+  std::vector<int32_t> &members = p->members_host;
+  members.assign(N, 0);
   {
     std::vector<int64_t> fill(p->group_start);
-    for (int64_t s = 0; s < N; ++s) {
-      const int64_t i = fill[grp[s]]++;
-      members[i] = (int32_t)s;
-      member_index[s] = (int32_t)(i - p->group_start[grp[s]]);
-    }
+    for (int64_t s = 0; s < N; ++s) members[fill[grp[s]]++] = (int32_t)s;
   }
-  std::vector<int64_t> base_a(G), base_f(G);
-  for (int g = 0; g < G; ++g) {
-    base_a[g] = p->base_a(g, 0);
-    base_f[g] = p->base_f(g, 0);
+  std::vector<int64_t> zero_off;
+  if (!off) zero_off.assign(N + 1, 0);
+  const int64_t *offp = off ? off : zero_off.data();
+  // ring layout: the factored states' components, group by group in the order the groups fall due
+  std::vector<int64_t> pos[2];
+  std::vector<unsigned long long> seg;
+  int64_t tot[2] = {0, 0}, cap_ring[2] = {0, 0};
+  if (factored) {
+    std::vector<int32_t> cnt[2] = {std::vector<int32_t>(N, -1), std::vector<int32_t>(N, -1)};
+    for (int64_t s = 0; s < N; ++s) {
+      const int64_t R = offp[s + 1] - offp[s];
+      if (R > L) continue;
+      cnt[0][s] = (int32_t)std::min<int64_t>(R, r);
+      cnt[1][s] = (int32_t)(R - cnt[0][s]);
+    }
+    ring_layout(p, ring_order(p, -1), cnt, pos, seg, tot);
+    // automatic capacity: the active ring never needs more than r per factored state plus one
+    // group's worth; the frozen ring starts at twice its contents plus one group's growth
+    int64_t nf = 0, ngmax = 0;
+    for (int g = 0; g < G; ++g) ngmax = std::max(ngmax, p->group_size[g]);
+    for (int64_t s = 0; s < N; ++s) nf += cnt[0][s] >= 0 ? 1 : 0;
+    for (int R = 0; R < 2; ++R) {
+      const int64_t autocap = R == 0 ? (int64_t)r * (nf + ngmax) : 2 * (tot[1] + (int64_t)K * ngmax);
+      cap_ring[R] = std::max<int64_t>({1, tot[R], d->arena_components ? d->arena_components : autocap});
+      if (cap_ring[R] >= (int64_t)INT32_MAX) return fail(SS_ERR_CAPACITY, "too many components for 32-bit offsets");
+    }
   }
   std::vector<float> epsv(N);
   for (int64_t s = 0; s < N; ++s) epsv[s] = d->eps ? d->eps[s] : d->eps_default;
@@ -287,19 +519,15 @@ ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipSt
   if (d->rule) std::memcpy(rulev.data(), d->rule, N);
 
   // device allocations
-  const int64_t cap_a = factored ? 2 * r * N : 0, cap_f = factored ? 2 * (int64_t)fcap * N : 0;
   hipError_t e = hipSuccess;
   auto chk = [&](hipError_t x) { if (e == hipSuccess) e = x; };
   chk(dalloc(p, &p->meta, N));
   chk(dalloc(p, &p->members, N));
   chk(dalloc(p, &p->eps, N));
-  chk(dalloc(p, &p->act.u, cap_a * dk));
-  chk(dalloc(p, &p->act.v, cap_a * dv));
-  chk(dalloc(p, &p->act.s, cap_a));
-  chk(dalloc(p, &p->frz.u, cap_f * dk));
-  chk(dalloc(p, &p->frz.v, cap_f * dv));
-  chk(dalloc(p, &p->frz.s, cap_f));
   if (factored) {
+    for (int R = 0; R < 2; ++R) chk(ring_alloc(p, cap_ring[R], &p->ring_blk[R], &p->ring_bytes[R], &p->arena(R)));
+    chk(dalloc(p, &p->ring, 2));
+    chk(dalloc(p, &p->seg, 4 * (size_t)G));
     chk(dalloc(p, &p->pk, (size_t)N * K * dk));
     chk(dalloc(p, &p->pw, (size_t)N * K * dv));
     chk(dalloc(p, &p->pc, (size_t)N * K));
@@ -336,8 +564,8 @@ ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipSt
   // temporaries for the initial upload
   int64_t *d_off = nullptr;
   float *d_u = nullptr, *d_v = nullptr, *d_s = nullptr;
-  int32_t *d_midx = nullptr, *d_grp = nullptr, *d_dlist = nullptr;
-  int64_t *d_ba = nullptr, *d_bf = nullptr;
+  int32_t *d_dlist = nullptr;
+  int64_t *d_pos[2] = {nullptr, nullptr};
   uint8_t *d_rule = nullptr;
   std::vector<void *> tmp;
   auto talloc = [&](void **q, size_t bytes) {
@@ -345,18 +573,13 @@ ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipSt
     e = hipMalloc(q, bytes);
     if (e == hipSuccess) tmp.push_back(*q);
   };
-  std::vector<int64_t> zero_off;
-  if (!off) zero_off.assign(N + 1, 0);
-  const int64_t *offp = off ? off : zero_off.data();
   talloc((void **)&d_off, (N + 1) * sizeof(int64_t));
   talloc((void **)&d_u, total * dk * sizeof(float));
   talloc((void **)&d_v, total * dv * sizeof(float));
   talloc((void **)&d_s, total * sizeof(float));
-  talloc((void **)&d_midx, N * sizeof(int32_t));
-  talloc((void **)&d_grp, N * sizeof(int32_t));
   talloc((void **)&d_dlist, N * sizeof(int32_t));
-  talloc((void **)&d_ba, G * sizeof(int64_t));
-  talloc((void **)&d_bf, G * sizeof(int64_t));
+  if (factored)
+    for (int R = 0; R < 2; ++R) talloc((void **)&d_pos[R], N * sizeof(int64_t));
   talloc((void **)&d_rule, N);
   auto up = [&](void *dst, const void *src, size_t bytes) {
     if (e == hipSuccess && bytes) e = hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, stream);
@@ -367,10 +590,15 @@ ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipSt
     up(d_v, init->v, total * dv * sizeof(float));
     up(d_s, init->sigma, total * sizeof(float));
   }
-  up(d_midx, member_index.data(), N * sizeof(int32_t));
-  up(d_grp, grp.data(), N * sizeof(int32_t));
-  up(d_ba, base_a.data(), G * sizeof(int64_t));
-  up(d_bf, base_f.data(), G * sizeof(int64_t));
+  ss::Ring ring0[2] = {};
+  if (factored) {
+    for (int R = 0; R < 2; ++R) {
+      up(d_pos[R], pos[R].data(), N * sizeof(int64_t));
+      ring0[R].head = ring0[R].begin = (unsigned long long)tot[R];
+    }
+    up(p->ring, ring0, sizeof(ring0));
+    up(p->seg, seg.data(), seg.size() * sizeof(unsigned long long));
+  }
   up(d_rule, rulev.data(), N);
   up(p->members, members.data(), N * sizeof(int32_t));
   up(p->eps, epsv.data(), N * sizeof(float));
@@ -389,7 +617,7 @@ ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipSt
     ss::ScatterArgs sa{};
     sa.N = N; sa.dk = dk; sa.dv = dv; sa.r = r; sa.L = L; sa.fcap = fcap; sa.force_dense = p->force_dense;
     sa.csr_off = d_off; sa.csr_u = d_u; sa.csr_v = d_v; sa.csr_s = d_s;
-    sa.member_index = d_midx; sa.group_of_state = d_grp; sa.base_a = d_ba; sa.base_f = d_bf; sa.rule = d_rule;
+    sa.dst_a = d_pos[0]; sa.dst_f = d_pos[1]; sa.rule = d_rule;
     sa.meta = p->meta; sa.act = p->act; sa.frz = p->frz; sa.dense_list = d_dlist; sa.counters = p->counters;
     e = ss::launch_scatter(sa, stream);
   }
@@ -411,6 +639,11 @@ ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipSt
   }
   p->dense_upper = n_dense0;
   p->fact_upper = factored ? (int64_t)fact.size() : 0;
+  for (int R = 0; R < 2; ++R) {
+    p->last_seq[R].assign(G, -1);
+    p->seg_bound[R].assign(G, 0);
+    if (factored) ring_records(p, R, seg.data() + (size_t)R * 2 * G, (unsigned long long)tot[R]);
+  }
   if (p->hflags) p->hflags[HF_FACT] = (uint32_t)p->fact_upper;
   *out = p;
   return SS_OK;
@@ -494,19 +727,28 @@ ss_status ss_compact(ss_pool *p, int32_t group, hipStream_t stream) {
       e = timed(p, SS_KERNEL_DENSE_FOLD, stream, [&] { return ss::launch_dense_fold(da, stream); });
       if (e != hipSuccess) return hip_fail(e, "dense fold launch");
     }
-    const int src = p->parity[g], dst = 1 - src;
+    int64_t ab[2];
+    st = ensure_ring_space(p, g, stream, ab);
+    if (st != SS_OK) return st;
+    e = ss::launch_ring_begin(p->ring, p->ring + 1, p->seg, p->seg + 2 * p->G, p->G, p->act.cap, p->frz.cap, stream);
+    if (e != hipSuccess) return hip_fail(e, "ring launch");
     ss::CompactArgs a{};
     a.dk = p->dk; a.dv = p->dv; a.K = p->K; a.r = p->r; a.L = p->L; a.promote = p->promote; a.fcap = p->fcap;
     a.n_members = (int32_t)p->group_size[g];
     a.members = p->members + p->group_start[g];
     a.eps = p->eps; a.meta = p->meta; a.act = p->act; a.frz = p->frz;
-    a.src_base_a = p->base_a(g, src); a.dst_base_a = p->base_a(g, dst);
-    a.src_base_f = p->base_f(g, src); a.dst_base_f = p->base_f(g, dst);
+    a.ring_a = p->ring; a.ring_f = p->ring + 1; a.hflag = p->hflags_dev + HF_RING;
     a.pk = p->pk; a.pw = p->pw; a.pc = p->pc; a.promote_list = p->promote_list; a.counters = p->counters;
     a.acct_flops = p->acct + ss::A_COMPACT_FLOPS * ss::kAcctSlots;
     a.acct_states = p->acct + ss::A_COMPACT_STATES * ss::kAcctSlots;
     e = timed(p, SS_KERNEL_COMPACT, stream, [&] { return ss::launch_compact(a, stream); });
+    if (e == hipSuccess) e = ss::launch_ring_end(p->ring, p->ring + 1, p->seg, p->seg + 2 * p->G, g, stream);
     if (e != hipSuccess) return hip_fail(e, "compact launch");
+    for (int R = 0; R < 2; ++R) {  // the group's new segment, by its bound
+      p->last_seq[R][g] = p->seq;
+      p->seg_bound[R][g] = ab[R];
+      p->recs[R].push_back({p->seq++, g, ab[R]});
+    }
     if (p->promote) {
       ss::MaterializeArgs ma{};
       ma.dk = p->dk; ma.dv = p->dv; ma.cap_d = (int)p->cap_d; ma.list = p->promote_list;
@@ -518,7 +760,6 @@ ss_status ss_compact(ss_pool *p, int32_t group, hipStream_t stream) {
       if (e != hipSuccess) return hip_fail(e, "promote launch");
       p->dense_upper = std::min<int64_t>(p->cap_d, p->dense_upper + p->group_size[g]);
     }
-    p->parity[g] = dst;
   }
   if (p->promote && p->fact_upper > 0) {  // promoted states leave the factored-state list
     const int cur = p->fact_par, nxt = 1 - cur;
@@ -622,12 +863,18 @@ ss_status ss_state_export(ss_pool *p, const int64_t *ids, int64_t n, void *host_
     float *c = v + (size_t)R * dv;
     float *kk = c + nn;
     float *ww = kk + (size_t)nn * dk;
-    dl(sig, p->act.s + m.off_a, sizeof(float) * ra);
-    dl(sig + ra, p->frz.s + m.off_f, sizeof(float) * rf);
-    dl(u, p->act.u + (size_t)m.off_a * dk, sizeof(float) * (size_t)ra * dk);
-    dl(u + (size_t)ra * dk, p->frz.u + (size_t)m.off_f * dk, sizeof(float) * (size_t)rf * dk);
-    dl(v, p->act.v + (size_t)m.off_a * dv, sizeof(float) * (size_t)ra * dv);
-    dl(v + (size_t)ra * dv, p->frz.v + (size_t)m.off_f * dv, sizeof(float) * (size_t)rf * dv);
+    // `cnt` components of a ring from physical slot c0, wrapping once at the ring's end
+    auto dl_ring = [&](float *dst, const float *base, int64_t cap, int64_t c0, int64_t cnt, int row) {
+      const int64_t first = std::min(cnt, cap - c0);
+      dl(dst, base + c0 * row, sizeof(float) * first * row);
+      dl(dst + first * row, base, sizeof(float) * (cnt - first) * row);
+    };
+    dl_ring(sig, p->act.s, p->act.cap, m.off_a, ra, 1);
+    dl_ring(sig + ra, p->frz.s, p->frz.cap, m.off_f, rf, 1);
+    dl_ring(u, p->act.u, p->act.cap, m.off_a, ra, dk);
+    dl_ring(u + (size_t)ra * dk, p->frz.u, p->frz.cap, m.off_f, rf, dk);
+    dl_ring(v, p->act.v, p->act.cap, m.off_a, ra, dv);
+    dl_ring(v + (size_t)ra * dv, p->frz.v, p->frz.cap, m.off_f, rf, dv);
     dl(c, p->pc + (size_t)ids[i] * K, sizeof(float) * nn);
     dl(kk, p->pk + (size_t)ids[i] * K * dk, sizeof(float) * (size_t)nn * dk);
     dl(ww, p->pw + (size_t)ids[i] * K * dv, sizeof(float) * (size_t)nn * dv);
@@ -680,7 +927,7 @@ ss_status ss_pool_stats(ss_pool *p, ss_stats *out, hipStream_t stream) {
     out->rank_hist[std::min<int64_t>(64, ra + rf)]++;
   }
   out->live_bytes = live;
-  out->reserved_bytes = p->reserved;
+  out->reserved_bytes = p->reserved + (int64_t)(p->ring_bytes[0] + p->ring_bytes[1]);
   out->decode_calls = p->decode_calls;
   out->compact_calls = p->compact_calls;
   out->readout_calls = p->readout_calls;
@@ -693,6 +940,25 @@ ss_status ss_pool_stats(ss_pool *p, ss_stats *out, hipStream_t stream) {
   out->decode_bytes = out->decode_bytes_factored + out->decode_bytes_dense;
   out->promotions = ctr[ss::C_PROMOTIONS];
   out->cap_truncations = ctr[ss::C_CAP_TRUNC];
+  if (!p->force_dense) {  // exact ring figures (the stream is idle here)
+    ss::Ring ring[2];
+    std::vector<unsigned long long> seg(4 * (size_t)p->G);
+    e = hipMemcpy(ring, p->ring, sizeof(ring), hipMemcpyDeviceToHost);
+    if (e == hipSuccess) e = hipMemcpy(seg.data(), p->seg, sizeof(unsigned long long) * seg.size(), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "stats copy");
+    for (int R = 0; R < 2; ++R) {
+      unsigned long long tail = ring[R].head;
+      for (int g = 0; g < p->G; ++g) {
+        const unsigned long long *sg = seg.data() + (size_t)R * 2 * p->G + 2 * g;
+        if (sg[1] > sg[0]) tail = std::min(tail, sg[0]);
+      }
+      out->ring_capacity[R] = p->arena(R).cap;
+      out->ring_used[R] = (int64_t)(ring[R].head - tail);
+      out->ring_head[R] = (int64_t)ring[R].head;
+    }
+  }
+  out->ring_repacks = p->repacks;
+  out->ring_syncs = p->ring_syncs;
   for (auto &ev : p->pending) {
     float ms = 0.f;
     if (hipEventElapsedTime(&ms, ev.a, ev.b) == hipSuccess) {

@@ -35,7 +35,7 @@ class PoolDesc(ctypes.Structure):
         ("n_groups", ctypes.c_int32),
         ("group_of_state", _c_i32p), ("group_offset", _c_i32p),
         ("rule", _c_u8p), ("eps", _c_f32p), ("eps_default", ctypes.c_float),
-        ("dense_capacity", ctypes.c_int64),
+        ("dense_capacity", ctypes.c_int64), ("arena_components", ctypes.c_int64),
     ]
 
 
@@ -53,6 +53,9 @@ class Stats(ctypes.Structure):
         ("decode_bytes", ctypes.c_uint64), ("decode_bytes_factored", ctypes.c_uint64),
         ("decode_bytes_dense", ctypes.c_uint64), ("compact_states", ctypes.c_uint64),
         ("compact_flops", ctypes.c_uint64), ("promotions", ctypes.c_int64), ("cap_truncations", ctypes.c_int64),
+        ("ring_capacity", ctypes.c_int64 * 2), ("ring_used", ctypes.c_int64 * 2),
+        ("ring_head", ctypes.c_int64 * 2),
+        ("ring_repacks", ctypes.c_int64), ("ring_syncs", ctypes.c_int64),
         ("kernel_ms", ctypes.c_double * 8), ("kernel_launches", ctypes.c_int64 * 8),
     ]
 
@@ -166,7 +169,7 @@ class StatePool:
 def state_pool_create(n_states, d_k, d_v, pad_slots=8, r_active=8, dense_rank_limit=-1, promote_on_compact=True,
                       max_frozen=0, force_dense=False, group_of_state=None, group_offset=None, rule=None, eps=None,
                       eps_default=0.0, dense_capacity=0, comp_off=None, u=None, v=None, sigma=None,
-                      stream=None) -> StatePool:
+                      arena_components=0, stream=None) -> StatePool:
     lib = load_library()
     n_groups = 1 if group_offset is None else len(group_offset)
     keep = []
@@ -177,7 +180,8 @@ def state_pool_create(n_states, d_k, d_v, pad_slots=8, r_active=8, dense_rank_li
     keep += [g_a, o_a, r_a, e_a]
     desc = PoolDesc(int(n_states), int(d_k), int(d_v), int(pad_slots), int(r_active), int(dense_rank_limit),
                     int(bool(promote_on_compact)), int(max_frozen), int(bool(force_dense)), int(n_groups),
-                    g_p, o_p, r_p, e_p, float(eps_default), int(dense_capacity))
+                    g_p, o_p, r_p, e_p, float(eps_default), int(dense_capacity),
+                    int(arena_components))
     init = None
     if comp_off is not None:
         c_a, c_p = _arr(comp_off, np.int64, _c_i64p)
@@ -221,7 +225,10 @@ def pool_stats(pool: StatePool, stream=None) -> dict:
     s = Stats()
     _check(load_library().ss_pool_stats(pool.handle, ctypes.byref(s), _stream(stream)))
     d = {name: getattr(s, name) for name, _ in Stats._fields_ if name not in ("rank_hist", "kernel_ms",
-                                                                              "kernel_launches")}
+                                                                              "kernel_launches", "ring_capacity",
+                                                                              "ring_used", "ring_head")}
+    for name in ("ring_capacity", "ring_used", "ring_head"):
+        d[name] = list(getattr(s, name))
     d["rank_hist"] = list(s.rank_hist)
     d["kernel_ms"] = {k: s.kernel_ms[i] for i, k in enumerate(KERNELS)}
     d["kernel_launches"] = {k: s.kernel_launches[i] for i, k in enumerate(KERNELS)}

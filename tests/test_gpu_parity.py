@@ -315,3 +315,63 @@ def test_dense_path_shapes(dk, dv, buffered):
     pool.close()
     assert worst <= TOL, (dk, dv, buffered, worst)
     assert folds > 0 or not buffered
+
+
+@pytest.mark.parametrize("name,promote,order", [("tiny", False, "schedule"), ("mamba2_258k", True, "schedule"),
+                                                ("gdn_delta", True, "random")])
+def test_ring_growth_wrap_and_repack(name, promote, order):
+    """Component rings created at exactly the initial size (arena_components=1): the first
+    compaction must grow them, later ones wrap around the ring end (once the ranks settle), and
+    with groups compacted in random order (out of their schedule) the segments leave gaps that
+    force defragmenting re-packs.  Sampled states are checked in lock-step against the oracle."""
+    w = W.get(name, n_requests=1 if name != "tiny" else None)
+    init = W.initial_state(w)
+    pool = _pool_from_init(w, init, promote_on_compact=promote, max_frozen=0 if promote else 200, arena_components=1)
+    st0 = ss.pool_stats(pool)
+    ranks = np.diff(init["comp_off"])
+    fact = ranks <= ss.dense_rank_limit(w.d_k, w.d_v)
+    assert st0["ring_capacity"][0] == max(1, int(np.minimum(ranks[fact], w.r).sum()))
+    ids = np.unique(np.concatenate([np.arange(0, w.n_states, max(1, w.n_states // 96)), [w.n_states - 1]]))
+    if order == "schedule":
+        worst, guard = _lockstep(w, init, pool, ids, 40 if name == "tiny" else 24, promote=promote)
+    else:
+        rng = np.random.default_rng(5)
+        gen = W.StepInputs(w, device="cuda")
+        eps = init["eps"][ids]
+        o = torch.empty(w.n_states, w.d_v, device="cuda")
+        worst = {"o": 0.0, "S_c": 0.0, "sigma": 0.0}
+        grp = init["group_of_state"][ids]
+        for t in range(1, 25):
+            x = gen.generate(t)
+            before = ss.state_export(pool, ids)
+            P = oracle_from_export(before, eps, w.d_k, w.d_v, w.K, w.r)
+            sub = {k: v.cpu().numpy()[ids].astype(np.float64) for k, v in x.items()}
+            ss.decode_step(pool, x["q"], x["k"], x["v"], x["alpha"], x["beta"], o)
+            torch.cuda.synchronize()
+            oo = P.decode(sub["q"], sub["k"], sub["v"], sub["alpha"], sub["beta"])
+            Sn = np.array([np.linalg.norm(P.reconstruct(j)) for j in range(len(ids))])
+            e = rel_out_err(o.cpu().numpy()[ids], oo, Sn, np.linalg.norm(sub["q"], axis=1))
+            worst["o"] = max(worst["o"], float(e.max()))
+            # a random group each step (pads never overflow: every group is compacted at least
+            # once in K steps below), plus the scheduled ones
+            due = sorted(set(ss.schedule_due(pool, t)) | {int(rng.integers(len(init["group_offset"])))})
+            after = ss.state_export(pool, ids)
+            for g in due:
+                ss.compact(pool, g)
+            P2 = oracle_from_export(after, eps, w.d_k, w.d_v, w.K, w.r)
+            sel = np.nonzero(np.isin(grp, due))[0]
+            P2.compact(sel)
+            ws, wsig, gd, bad = compare_compacted(ss.state_export(pool, ids), P2, eps)
+            assert not bad, f"step {t}: rank/dense mismatches outside the guard band: {bad[:5]}"
+            worst["S_c"] = max(worst["S_c"], ws)
+            worst["sigma"] = max(worst["sigma"], wsig)
+    st = ss.pool_stats(pool)
+    pool.close()
+    print(name, order, worst, {k: st[k] for k in ("ring_capacity", "ring_used", "ring_head", "ring_repacks",
+                                                  "ring_syncs", "n_dense")})
+    _assert_worst(worst)
+    assert st["ring_repacks"] >= 1
+    if name == "tiny":  # ranks settle here, so the rings stop growing and the heads pass the ring end
+        assert max(h - c for h, c in zip(st["ring_head"], st["ring_capacity"])) > 0, "no ring wrapped"
+    for R in range(2):
+        assert st["ring_used"][R] <= st["ring_capacity"][R]
