@@ -141,8 +141,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (the path shards by request "
-                                   "with no exchange step, see DESIGN.md)"}))
+        print(json.dumps({"error": "single-GPU implementation: --gpus must be 1 (the path shards by request "
+                                   "with no exchange step between GPUs)"}))
         sys.exit(2)
 
     if args.copy_calibration:

@@ -197,7 +197,10 @@ __device__ __forceinline__ void stage_lds(const Seg4 (&sg)[NSEG], int lane) {
 // member with a non-empty pad gets its pad folded into H.  Rows stream in
 // batches of G * UN, double-buffered: the next batch is in flight while the
 // current one is reduced.  LDS per wave: the pad's keys and w rows, the pad
-// parts of p_q and p_k, and v.
+// parts of p_q and p_k, and v.  The decode writes o, the slot record, c and a
+// delta-rule w row; the new key and a scalar-rule w = v are copied into the
+// pad by k_dense_append after it (a few small writes inside the row stream
+// cost more than a pass of their own).
 template <int P, int UN, int MODE, bool ANYDELTA>
 __global__ __launch_bounds__(256) void k_dense_buf(DenseArgs a) {
   constexpr int G = 64 / P, B = G * UN;
@@ -324,7 +327,7 @@ __global__ __launch_bounds__(256) void k_dense_buf(DenseArgs a) {
             w = be * (vj - al * pk);
           }
           oj = fmaf(al, pq, kq * w);
-          if (!fold && col == 0 && ok) WS[j] = w;
+          if (delta && !fold && col == 0 && ok) WS[j] = w;
         }
         if (col == 0 && ok) OS[j] = oj;
       }
@@ -361,12 +364,11 @@ __global__ __launch_bounds__(256) void k_dense_buf(DenseArgs a) {
   wave_sync();
   if constexpr (!FO) {
     for (int e = lane; e < (dv >> 2); e += 64) {
-      st4(os + 4 * e, *reinterpret_cast<const float4 *>(OS + 4 * e));
-      if (DEC && !fold) st4nt(pwn + 4 * e, *reinterpret_cast<const float4 *>(WS + 4 * e));
+      st4nt(os + 4 * e, *reinterpret_cast<const float4 *>(OS + 4 * e));
+      if (DEC && !fold && delta) st4nt(pwn + 4 * e, *reinterpret_cast<const float4 *>(WS + 4 * e));
     }
   }
   if constexpr (!RO) {
-    if (DEC && !fold && grp == 0 && kin) st4nt(a.pk + ((int64_t)slot * K + n) * dk + 4 * col, k4);
     if (lane == 0) {
       if (DEC && !fold) a.pc[(int64_t)slot * K + n] = 1.0f / ag;
       DenseSlot nr = rec;
@@ -378,6 +380,28 @@ __global__ __launch_bounds__(256) void k_dense_buf(DenseArgs a) {
         __hip_atomic_fetch_add(&a.acct[s & (kAcctSlots - 1)], b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
+  }
+}
+
+// The new pad entry of each dense slot that did not fold in the step just decoded: its key, and
+// for the scalar rule its w = v, copied from the inputs in a pass of its own (delta-rule w rows
+// depend on the state and are written by the decode).  The decode has already advanced the
+// slot record, so the entry goes to pad slot n - 1; n = 0 means the step folded.
+__global__ __launch_bounds__(256) void k_dense_append(DenseArgs a) {
+  const int wv = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const uint32_t slot = blockIdx.x * 4u + (uint32_t)wv;
+  if (slot >= min(a.counters[C_DENSE_COUNT], a.cap_d)) return;
+  const DenseSlot rec = a.dslot[slot];
+  const uint32_t packed = (uint32_t)uniform((int)rec.packed);
+  const int n = meta_n(packed);
+  if (n == 0) return;
+  const int64_t s = uniform(rec.s);
+  const int dk4 = a.dk >> 2, dv4 = (meta_flags(packed) & FLAG_DELTA) ? 0 : (a.dv >> 2);
+  float *pkn = a.pk + ((int64_t)slot * a.K + n - 1) * a.dk;
+  float *pwn = a.pw + ((int64_t)slot * a.K + n - 1) * a.dv;
+  for (int e = lane; e < dk4 + dv4; e += 64) {
+    if (e < dk4) st4nt(pkn + 4 * e, ld4nt(a.k + s * a.dk + 4 * e));
+    else st4nt(pwn + 4 * (e - dk4), ld4nt(a.v + s * a.dv + 4 * (e - dk4)));
   }
 }
 
@@ -541,7 +565,12 @@ hipError_t launch_decode_dense(const DenseArgs &a, int64_t n_upper, bool readonl
   if (a.pk) {
     if (a.K > kMaxPad) return hipErrorInvalidValue;
     const int mode = readonly ? DM_READOUT : DM_DECODE;
-    return any_delta ? dense_buf_p<true>(a, mode, P, grid, st) : dense_buf_p<false>(a, mode, P, grid, st);
+    hipError_t e = any_delta ? dense_buf_p<true>(a, mode, P, grid, st) : dense_buf_p<false>(a, mode, P, grid, st);
+    if (e == hipSuccess && !readonly) {  // the pad entries of the step, in a pass of their own
+      hipLaunchKernelGGL(k_dense_append, dim3(grid), dim3(256), 0, st, a);
+      e = hipGetLastError();
+    }
+    return e;
   }
   if (readonly) return dense_plain_p<true, false>(a, P, grid, st);
   return any_delta ? dense_plain_p<false, true>(a, P, grid, st) : dense_plain_p<false, false>(a, P, grid, st);
