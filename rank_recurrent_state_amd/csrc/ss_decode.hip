@@ -348,7 +348,7 @@ __global__ __launch_bounds__(256) void k_dense_buf(DenseArgs a) {
 #pragma unroll
       for (int u = 0; u < UN; ++u) {
         const int j = j0 + u * G + grp;
-        if (j < dv && kin) st4(Hw + (int64_t)j * dk, hb[u]);
+        if (j < dv && kin) st4nt(Hw + (int64_t)j * dk, hb[u]);  // streamed out: nothing reads it again this step
       }
     }
   };
@@ -406,7 +406,7 @@ __global__ __launch_bounds__(256) void k_dense_append(DenseArgs a) {
 }
 
 // plain dense recurrence (the dense baseline): every row read and written every
-// step.  Same row streaming as the buffered kernel (double-buffered batches, v in LDS).
+// step.  Same row streaming as the buffered kernel (double-buffered batches, v and o in LDS).
 template <int P, int UN, bool RO, bool ANYDELTA>
 __global__ __launch_bounds__(256) void k_dense_plain(DenseArgs a) {
   constexpr int G = 64 / P, B = G * UN;
@@ -420,7 +420,8 @@ __global__ __launch_bounds__(256) void k_dense_plain(DenseArgs a) {
   const int dk = a.dk, dv = a.dv;
   const bool kin = col < (dk >> 2);
   const int colk = kin ? col : (dk >> 2) - 1;  // clamped: loads stay in bounds
-  float *VS = smem + (size_t)wv * dv;
+  float *VS = smem + (size_t)wv * 2 * dv;  // v
+  float *OS = VS + dv;                      // o, collected row by row
   const float *H = a.dense + (int64_t)slot * dk * dv + 4 * colk;
   float *Hw = a.dense + (int64_t)slot * dk * dv + 4 * col;
   float4 hA[UN], hB[UN];
@@ -447,7 +448,6 @@ __global__ __launch_bounds__(256) void k_dense_plain(DenseArgs a) {
     wave_sync();
   }
   const float kq = RO ? 0.f : uniformf(group_sum<P>(dot4(k4, q4)));
-  float *os = a.o + s * dv;
   auto proc_rows = [&](float4 (&hb)[UN], int j0) {
 #pragma unroll
     for (int u = 0; u < UN; ++u) {
@@ -465,9 +465,9 @@ __global__ __launch_bounds__(256) void k_dense_plain(DenseArgs a) {
           w = be * (vj - al * dkk);
         }
         oj = fmaf(al, dq, kq * w);
-        if (ok && kin) st4(Hw + (int64_t)j * dk, fma4(w, k4, scale4(al, hb[u])));
+        if (ok && kin) st4nt(Hw + (int64_t)j * dk, fma4(w, k4, scale4(al, hb[u])));
       }
-      if (col == 0 && ok) os[j] = oj;
+      if (col == 0 && ok) OS[j] = oj;
     }
   };
   for (int j0 = 0; j0 < dv; j0 += 2 * B) {
@@ -478,6 +478,8 @@ __global__ __launch_bounds__(256) void k_dense_plain(DenseArgs a) {
       if (j0 + 3 * B < dv) load_rows(hB, j0 + 3 * B);
     }
   }
+  wave_sync();
+  for (int e = lane; e < (dv >> 2); e += 64) st4nt(a.o + s * dv + 4 * e, *reinterpret_cast<const float4 *>(OS + 4 * e));
   if (!RO && lane == 0) {
     const unsigned long long b = decode_bytes(dk, dv, 0, 0, 0, delta, KIND_DENSE_PLAIN);
     __hip_atomic_fetch_add(&a.acct[s & (kAcctSlots - 1)], b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -527,7 +529,7 @@ hipError_t dense_buf_p(const DenseArgs &a, int mode, int P, unsigned grid, hipSt
 template <bool RO, bool AD>
 hipError_t dense_plain_p(const DenseArgs &a, int P, unsigned grid, hipStream_t st) {
   const dim3 g(grid), b(256);
-  const size_t sh = sizeof(float) * 4 * (size_t)a.dv;
+  const size_t sh = sizeof(float) * 4 * 2 * (size_t)a.dv;
   switch (P) {
     case 1: hipLaunchKernelGGL((k_dense_plain<1, 1, RO, AD>), g, b, sh, st, a); break;
     case 2: hipLaunchKernelGGL((k_dense_plain<2, 1, RO, AD>), g, b, sh, st, a); break;
