@@ -46,6 +46,48 @@ def _run_steps(ss, torch, pool, xs, t0, o, ev=None):
         ev[len(xs)].record()
 
 
+def graph_replay(ss, torch, W, steps=256, warm=16):
+    """Per-step wall time of whole steps (decode + due compactions) launched eagerly versus replayed
+    as step graphs, at batch sizes where launch overhead matters.  Inputs sit in fixed buffers and
+    are refreshed every step on the device (same work on both paths)."""
+    import time as _t
+    out = {}
+    for name, req in (("tiny", None), ("mamba2_258k", 1)):
+        w = W.get(name, n_requests=req)
+        init = W.initial_state(w)
+        gen = W.StepInputs(w, device="cuda")
+        xs = [gen.generate(t) for t in range(1, 9)]
+        buf = {k: v.clone() for k, v in xs[0].items()}
+        o = torch.empty(w.n_states, w.d_v, device="cuda")
+        res = {}
+        for mode in ("eager", "graph"):
+            pool = _pool(ss, w, init)
+            g = ss.StepGraph(pool, buf["q"], buf["k"], buf["v"], buf["alpha"], buf["beta"], o) if mode == "graph" \
+                else None
+            t0 = None
+            for t in range(1, warm + steps + 1):
+                if t == warm + 1:
+                    torch.cuda.synchronize()
+                    t0 = _t.perf_counter()
+                x = xs[t % len(xs)]
+                for k in buf:
+                    buf[k].copy_(x[k])
+                if g is not None:
+                    g.launch(t)
+                else:
+                    ss.decode_step(pool, buf["q"], buf["k"], buf["v"], buf["alpha"], buf["beta"], o)
+                    for gg in ss.schedule_due(pool, t):
+                        ss.compact(pool, gg)
+            torch.cuda.synchronize()
+            res[mode] = 1e6 * (_t.perf_counter() - t0) / steps
+            if g is not None:
+                g.close()
+            pool.close()
+        out[name] = {"n_states": w.n_states, "eager_us_per_step": res["eager"], "graph_us_per_step": res["graph"],
+                     "speedup": res["eager"] / res["graph"]}
+    return out
+
+
 def cpu_baseline(w, init, n_sample, n_steps, device="cpu"):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload, all host cores.
     Inputs are drawn per step for the sampled states on `device` and copied to the host (not timed);
@@ -139,6 +181,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 4 GiB device copy (for scaling rocprof byte counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the eager-versus-graph step timing")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "single-GPU implementation: --gpus must be 1 (the path shards by request "
@@ -258,6 +301,11 @@ def main():
                  "kernel_avg_us": 1e3 * kd / args.dense_steps, "bytes_per_step": bd / args.dense_steps}
         log(f"[bench] dense baseline {dense['ms_per_step']:.3f} ms/step, {dense['achieved_GBs']:.0f} GB/s")
 
+    graphs = graph_replay(ss, torch, W) if not args.no_graph else None
+    if graphs:
+        log("[bench] graph replay " + ", ".join(f"{k}: {v['eager_us_per_step']:.0f} -> {v['graph_us_per_step']:.0f} us/step"
+                                                for k, v in graphs.items()))
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, init, args.cpu_sample, args.cpu_steps, device="cuda")
@@ -289,6 +337,7 @@ def main():
         "compaction": compaction,
         "phases": phases,
         "dense_baseline": dense,
+        "graph_replay": graphs,
     }
     print(json.dumps(out), flush=True)
 

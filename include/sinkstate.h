@@ -190,6 +190,32 @@ ss_status ss_compact(ss_pool *pool, int32_t group, hipStream_t stream);
  * and returns their count in *n_due.  Host only. */
 ss_status ss_schedule_due(const ss_pool *pool, int64_t step, int32_t *out, int32_t cap, int32_t *n_due);
 
+/* Whole decode steps as HIP graphs ([SS] 4.4 "Kernel fusion, load balancing,
+ * and support for CUDA graphs": the pages replay steps as graphs; here one
+ * graph is captured per phase of the schedule, step mod K).  Replaying
+ * phase p runs ss_decode_step on the fixed buffers given at creation,
+ * followed by ss_compact of every group due at a step in that phase and the
+ * pruning of the factored-state list, with no launch from the host but the
+ * graph's.  The caller writes each step's inputs into q, k, v, alpha, beta
+ * (device, [N][d_k], [N][d_k], [N][d_v], [N], [N]; beta may be NULL when the
+ * pool has no delta-rule state) before launching, in stream order; o [N][d_v]
+ * receives the output.  The buffers stay owned by the caller and must
+ * outlive the graph object, which must be destroyed before its pool.
+ *
+ * ss_step_graph_launch(g, step, stream) is equivalent, result for result,
+ * to ss_decode_step followed by ss_compact for each group returned by
+ * ss_schedule_due(step), and may be mixed freely with those calls.  Before
+ * the launch it runs the host-side ring check of ss_compact (which may
+ * synchronize `stream` and re-pack); a re-pack moves the rings, and the
+ * graphs are then captured again before the launch.  Kernel timing
+ * (ss_pool_timing) does not cover graph launches.  Errors: SS_ERR_ARG,
+ * SS_ERR_OOM, SS_ERR_HIP, and the pool's sticky errors. */
+typedef struct ss_step_graph ss_step_graph;
+ss_status ss_step_graph_create(ss_pool *pool, const float *q, const float *k, const float *v, const float *alpha,
+                               const float *beta, float *o, ss_step_graph **out);
+ss_status ss_step_graph_launch(ss_step_graph *graph, int64_t step, hipStream_t stream);
+ss_status ss_step_graph_destroy(ss_step_graph *graph);
+
 /* Test hook: copy states `ids` (host array) to host memory in the canonical
  * form, effective weights (Gamma folded in).  Waits on `stream`.  Layout per
  * state, packed in id order:

@@ -706,8 +706,10 @@ __global__ __launch_bounds__(256) void k_prune_factored(const int32_t *src, cons
 // ring bookkeeping around a compaction: seg_x[2 g] / seg_x[2 g + 1] are the virtual start / end of
 // group g's segment (start == end: no live segment)
 __global__ void k_ring_begin(Ring *ra, Ring *rf, const unsigned long long *seg_a, const unsigned long long *seg_f,
-                             int n_groups, int64_t cap_a, int64_t cap_f) {
+                             int n_groups, int64_t cap_a, int64_t cap_f, uint32_t *counters) {
   if (threadIdx.x != 0) return;
+  counters[C_PROMOTE_COUNT] = 0u;  // the compaction's promotion list starts empty
+  counters[C_FACT1] = 0u;          // scratch length for a pruning of the factored-state list
   unsigned long long ta = ra->head, tf = rf->head;
   for (int g = 0; g < n_groups; ++g) {
     if (seg_a[2 * g + 1] > seg_a[2 * g] && seg_a[2 * g] < ta) ta = seg_a[2 * g];
@@ -758,8 +760,16 @@ __global__ __launch_bounds__(256) void k_repack(RepackArgs a) {
   }
 }
 
-__global__ void k_copy_count(const uint32_t *src, uint32_t *dst) {
-  if (threadIdx.x == 0) *dst = *src;
+// list[i] = tmp[i] for i < *tmp_count; the length goes to *count and to a host-visible word
+__global__ __launch_bounds__(256) void k_copy_list(const int32_t *tmp, const uint32_t *tmp_count, int32_t *list,
+                                                   uint32_t *count, uint32_t *host) {
+  const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+  const uint32_t c = *tmp_count;
+  if (i < c) list[i] = tmp[i];
+  if (i == 0) {
+    *count = c;
+    *host = c;
+  }
 }
 
 __global__ void k_zero_u32(uint32_t *p, int n) {
@@ -794,21 +804,18 @@ hipError_t launch_scatter(const ScatterArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_prune_factored(const int32_t *src, const uint32_t *src_count, int64_t n_upper, int32_t *dst,
-                                 uint32_t *dst_count, const Meta *meta, uint32_t *host_count, hipStream_t st) {
-  if (n_upper > 0) {
-    hipLaunchKernelGGL(k_prune_factored, dim3((unsigned)((n_upper + 255) / 256)), dim3(256), 0, st, src, src_count,
-                       dst, dst_count, meta);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(k_copy_count, dim3(1), dim3(64), 0, st, dst_count, host_count);
+hipError_t launch_prune_factored(int32_t *list, uint32_t *count, int32_t *tmp, uint32_t *tmp_count, int64_t n_upper,
+                                 const Meta *meta, uint32_t *host_count, hipStream_t st) {
+  if (n_upper <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((n_upper + 255) / 256)), block(256);
+  hipLaunchKernelGGL(k_prune_factored, grid, block, 0, st, list, count, tmp, tmp_count, meta);
+  hipLaunchKernelGGL(k_copy_list, grid, block, 0, st, tmp, tmp_count, list, count, host_count);
   return hipGetLastError();
 }
 
 hipError_t launch_ring_begin(Ring *ra, Ring *rf, const unsigned long long *seg_a, const unsigned long long *seg_f,
-                             int n_groups, int64_t cap_a, int64_t cap_f, hipStream_t st) {
-  hipLaunchKernelGGL(k_ring_begin, dim3(1), dim3(64), 0, st, ra, rf, seg_a, seg_f, n_groups, cap_a, cap_f);
+                             int n_groups, int64_t cap_a, int64_t cap_f, uint32_t *counters, hipStream_t st) {
+  hipLaunchKernelGGL(k_ring_begin, dim3(1), dim3(64), 0, st, ra, rf, seg_a, seg_f, n_groups, cap_a, cap_f, counters);
   return hipGetLastError();
 }
 

@@ -58,8 +58,8 @@ enum Counter : int {
   C_ERR_DENSE_CAP = 3, // promotion found the dense region full (also host-mapped)
   C_CAP_TRUNC = 4,     // frozen components dropped because max_frozen was reached
   C_PROMOTIONS = 5,    // total promotions
-  C_FACT0 = 6,         // length of factored-state list 0
-  C_FACT1 = 7,         // length of factored-state list 1
+  C_FACT0 = 6,         // length of the factored-state list
+  C_FACT1 = 7,         // length of its scratch copy while it is pruned
   C_N = 8
 };
 
@@ -172,10 +172,10 @@ hipError_t launch_compact(const CompactArgs &a, hipStream_t st);
 hipError_t launch_materialize(const MaterializeArgs &a, int64_t grid_upper, hipStream_t st);
 hipError_t launch_scatter(const ScatterArgs &a, hipStream_t st);
 hipError_t launch_zero_u32(uint32_t *p, int n, hipStream_t st);
-// before a compaction of group g: limit = (oldest live segment start) + cap, begin = head, per ring;
-// after it: the group's segment becomes [begin, head)
+// before a compaction of group g: limit = (oldest live segment start) + cap, begin = head, per ring,
+// and the promotion list and the pruning scratch emptied; after it: the group's segment becomes [begin, head)
 hipError_t launch_ring_begin(Ring *ra, Ring *rf, const unsigned long long *seg_a, const unsigned long long *seg_f,
-                             int n_groups, int64_t cap_a, int64_t cap_f, hipStream_t st);
+                             int n_groups, int64_t cap_a, int64_t cap_f, uint32_t *counters, hipStream_t st);
 hipError_t launch_ring_end(Ring *ra, Ring *rf, unsigned long long *seg_a, unsigned long long *seg_f, int g,
                            hipStream_t st);
 // copy every factored state's components into new rings at the given positions (arena growth)
@@ -187,10 +187,11 @@ struct RepackArgs {
   const int64_t *new_a, *new_f;  // per state: new first position (physical) or -1 for dense states
 };
 hipError_t launch_repack(const RepackArgs &a, hipStream_t st);
-// drop the states that have become dense from a factored-state list (src -> dst, dst_count zeroed by
-// the caller), then copy the new length to a host-visible word
-hipError_t launch_prune_factored(const int32_t *src, const uint32_t *src_count, int64_t n_upper, int32_t *dst,
-                                 uint32_t *dst_count, const Meta *meta, uint32_t *host_count, hipStream_t st);
+// drop the states that have become dense from the factored-state list: list -> tmp, then back into
+// list, so the decode always reads the same list; the new length goes to *count and a host-visible word.
+// *tmp_count must be 0 (a compaction's launch_ring_begin clears it).
+hipError_t launch_prune_factored(int32_t *list, uint32_t *count, int32_t *tmp, uint32_t *tmp_count, int64_t n_upper,
+                                 const Meta *meta, uint32_t *host_count, hipStream_t st);
 
 // how a state is decoded
 enum DecodeKind : int { KIND_FACTORED = 0, KIND_DENSE_BUFFERED = 1, KIND_DENSE_PLAIN = 2 };

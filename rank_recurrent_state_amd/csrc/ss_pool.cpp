@@ -66,13 +66,13 @@ struct ss_pool {
   std::vector<int64_t> seg_bound[2];   // per group: upper bound of its live segment size
   int64_t seq = 0;
   int64_t repacks = 0, ring_syncs = 0;
+  int64_t layout_version = 0;          // bumped whenever device addresses captured in graphs change
   float *pk = nullptr, *pw = nullptr, *pc = nullptr;
   float *dense = nullptr;
   ss::DenseSlot *dslot = nullptr;
   float *dpk = nullptr, *dpw = nullptr, *dpc = nullptr;  // slot-indexed pads of the dense region
   int32_t *promote_list = nullptr;
-  int32_t *fact_ids[2] = {nullptr, nullptr};  // factored-state lists (ping-pong), lengths in counters
-  int fact_par = 0;
+  int32_t *fact_ids[2] = {nullptr, nullptr};  // factored-state list and its scratch copy, lengths in counters
   int64_t fact_upper = 0;                     // host upper bound of the current list's length
   uint32_t *counters = nullptr;
   unsigned long long *acct = nullptr;  // [A_N][kAcctSlots] accounting (see ss::Acct)
@@ -302,27 +302,34 @@ ss_status ring_repack(ss_pool *p, int first, const int64_t (&newcap)[2], hipStre
     ring_records(p, R, seg.data() + (size_t)R * 2 * p->G, (unsigned long long)tot[R]);
   }
   p->repacks++;
+  p->layout_version++;
   return SS_OK;
 }
 
-// Before a compaction of group g: make sure each ring can take the group's new segment.  A
-// state's new active (frozen) count exceeds its old one by at most its pad fill <= K, and is
-// at most r (the frozen capacity), so the segment bound ab[R] is the old bound plus K per
-// member, capped.  The host bounds head - tail by the records from the oldest live segment on
-// and synchronizes only when that bound plus ab could exceed the capacity; it then takes the
-// exact figures from the device, and re-packs (growing the ring if the live components need
-// it) only if those leave too little room.
-ss_status ensure_ring_space(ss_pool *p, int g, hipStream_t stream, int64_t (&ab)[2]) {
-  const int64_t ng = p->group_size[g];
-  auto bound = [&](int R) {
-    return std::min<int64_t>(ng * p->per_state_cap(R), p->seg_bound[R][g] + (int64_t)p->K * ng);
+// Before the compactions of groups gs[0..ng) (in that order, with nothing else allocating in
+// between): make sure each ring can take their new segments.  A state's new active (frozen) count
+// exceeds its old one by at most its pad fill, and is at most r (the frozen capacity), so a
+// group's segment bound ab[i][R] is its old bound plus K per member, capped.  The host bounds
+// head - tail by the records from the oldest live segment on and synchronizes only when that
+// bound plus the new segments could exceed the capacity; it then takes the exact figures from the
+// device, and re-packs (growing the ring if the live components need it) only if those leave
+// too little room.
+ss_status ensure_ring_space(ss_pool *p, const int *gs, int ng, hipStream_t stream, int64_t (*ab)[2]) {
+  auto bounds = [&](int64_t (&need)[2]) {
+    need[0] = need[1] = 0;
+    for (int i = 0; i < ng; ++i) {
+      const int64_t n = p->group_size[gs[i]];
+      for (int R = 0; R < 2; ++R) {
+        ab[i][R] = std::min<int64_t>(n * p->per_state_cap(R), p->seg_bound[R][gs[i]] + (int64_t)p->K * n);
+        need[R] += ab[i][R];
+      }
+    }
   };
-  bool need = false;
-  for (int R = 0; R < 2; ++R) {
-    ab[R] = bound(R);
-    need = need || ring_usage_bound(p, R) + ab[R] > p->arena(R).cap;
-  }
-  if (!need) return SS_OK;
+  int64_t need[2];
+  bounds(need);
+  bool sync = false;
+  for (int R = 0; R < 2; ++R) sync = sync || ring_usage_bound(p, R) + need[R] > p->arena(R).cap;
+  if (!sync) return SS_OK;
   hipError_t e = hipStreamSynchronize(stream);
   ss::Ring ring[2];
   std::vector<unsigned long long> seg(4 * (size_t)p->G);
@@ -330,24 +337,24 @@ ss_status ensure_ring_space(ss_pool *p, int g, hipStream_t stream, int64_t (&ab)
   if (e == hipSuccess) e = hipMemcpy(seg.data(), p->seg, sizeof(unsigned long long) * seg.size(), hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(e, "ring sync");
   p->ring_syncs++;
-  bool repack = false;
   int64_t live[2] = {0, 0};
   for (int R = 0; R < 2; ++R) {
     ring_records(p, R, seg.data() + (size_t)R * 2 * p->G, ring[R].head);
-    for (int gg = 0; gg < p->G; ++gg) live[R] += p->seg_bound[R][gg];
-    ab[R] = bound(R);
-    repack = repack || ring_usage_bound(p, R) + ab[R] > p->arena(R).cap;
+    for (int g = 0; g < p->G; ++g) live[R] += p->seg_bound[R][g];
   }
+  bounds(need);
+  bool repack = false;
+  for (int R = 0; R < 2; ++R) repack = repack || ring_usage_bound(p, R) + need[R] > p->arena(R).cap;
   if (!repack) return SS_OK;
   int64_t newcap[2];
   for (int R = 0; R < 2; ++R) {
-    const int64_t need_R = live[R] + ab[R], cap = p->arena(R).cap;
-    newcap[R] = 2 * need_R > cap ? std::max<int64_t>(cap, 2 * need_R) : cap;
+    const int64_t want = live[R] + need[R], cap = p->arena(R).cap;
+    newcap[R] = 2 * want > cap ? std::max<int64_t>(cap, 2 * want) : cap;
     if (newcap[R] >= (int64_t)INT32_MAX) return fail(SS_ERR_CAPACITY, "a component ring would exceed 2^31 slots");
   }
-  const ss_status st = ring_repack(p, g, newcap, stream);
+  const ss_status st = ring_repack(p, gs[0], newcap, stream);
   if (st != SS_OK) return st;
-  for (int R = 0; R < 2; ++R) ab[R] = bound(R);
+  bounds(need);
   return SS_OK;
 }
 
@@ -657,6 +664,98 @@ ss_status ss_state_pool_destroy(ss_pool *p) {
   return SS_OK;
 }
 
+// Enqueue the decode (or read-only readout) of every state.  fact_grid / dense_grid bound the
+// factored-state list and the dense slots in use (the kernels read the exact counts on the device).
+static hipError_t enqueue_decode(ss_pool *p, const float *q, const float *k, const float *v, const float *alpha,
+                                 const float *beta, float *o, bool readonly, int64_t fact_grid, int64_t dense_grid,
+                                 bool timing, hipStream_t stream) {
+  hipError_t e = hipSuccess;
+  if (!p->force_dense && fact_grid > 0) {
+    ss::DecodeArgs a{};
+    a.N = fact_grid; a.dk = p->dk; a.dv = p->dv; a.K = p->K; a.meta = p->meta; a.act = p->act; a.frz = p->frz;
+    a.fact_ids = p->fact_ids[0]; a.fact_count = p->counters + ss::C_FACT0;
+    a.pk = p->pk; a.pw = p->pw; a.pc = p->pc; a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.o = o;
+    a.counters = p->counters; a.acct = p->acct + ss::A_DECODE_FACTORED * ss::kAcctSlots;
+    a.hflag = p->hflags_dev + HF_PAD;
+    auto fn = [&] { return ss::launch_decode_factored(a, readonly, p->any_delta, stream); };
+    e = timing ? timed(p, readonly ? SS_KERNEL_READOUT_FACTORED : SS_KERNEL_DECODE_FACTORED, stream, fn) : fn();
+    if (e != hipSuccess) return e;
+  }
+  if (dense_grid > 0) {
+    ss::DenseArgs a{};
+    a.dk = p->dk; a.dv = p->dv; a.K = p->K; a.cap_d = (uint32_t)p->cap_d; a.meta = p->meta; a.dense = p->dense;
+    a.dslot = p->dslot; a.pk = p->dpk; a.pw = p->dpw; a.pc = p->dpc;
+    a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.o = o;
+    a.counters = p->counters; a.acct = p->acct + ss::A_DECODE_DENSE * ss::kAcctSlots;
+    auto fn = [&] { return ss::launch_decode_dense(a, dense_grid, readonly, p->any_delta, stream); };
+    e = timing ? timed(p, readonly ? SS_KERNEL_READOUT_DENSE : SS_KERNEL_DECODE_DENSE, stream, fn) : fn();
+  }
+  return e;
+}
+
+// Enqueue the compaction of group g (the ring space must have been checked): fold the pads of its
+// dense members, compact its factored members into a new ring segment, promote.  with_dense:
+// whether dense members may exist.
+static hipError_t enqueue_compact_group(ss_pool *p, int g, bool with_dense, bool timing, hipStream_t stream) {
+  hipError_t e = ss::launch_ring_begin(p->ring, p->ring + 1, p->seg, p->seg + 2 * p->G, p->G, p->act.cap, p->frz.cap,
+                                       p->counters, stream);
+  if (e != hipSuccess) return e;
+  if (with_dense) {
+    ss::DenseArgs da{};
+    da.dk = p->dk; da.dv = p->dv; da.K = p->K; da.cap_d = (uint32_t)p->cap_d; da.meta = p->meta;
+    da.dense = p->dense; da.dslot = p->dslot; da.pk = p->dpk; da.pw = p->dpw; da.pc = p->dpc;
+    da.members = p->members + p->group_start[g]; da.n_members = (int32_t)p->group_size[g];
+    da.counters = p->counters; da.acct = p->acct;
+    auto fn = [&] { return ss::launch_dense_fold(da, stream); };
+    e = timing ? timed(p, SS_KERNEL_DENSE_FOLD, stream, fn) : fn();
+    if (e != hipSuccess) return e;
+  }
+  ss::CompactArgs a{};
+  a.dk = p->dk; a.dv = p->dv; a.K = p->K; a.r = p->r; a.L = p->L; a.promote = p->promote; a.fcap = p->fcap;
+  a.n_members = (int32_t)p->group_size[g];
+  a.members = p->members + p->group_start[g];
+  a.eps = p->eps; a.meta = p->meta; a.act = p->act; a.frz = p->frz;
+  a.ring_a = p->ring; a.ring_f = p->ring + 1; a.hflag = p->hflags_dev + HF_RING;
+  a.pk = p->pk; a.pw = p->pw; a.pc = p->pc; a.promote_list = p->promote_list; a.counters = p->counters;
+  a.acct_flops = p->acct + ss::A_COMPACT_FLOPS * ss::kAcctSlots;
+  a.acct_states = p->acct + ss::A_COMPACT_STATES * ss::kAcctSlots;
+  auto fc = [&] { return ss::launch_compact(a, stream); };
+  e = timing ? timed(p, SS_KERNEL_COMPACT, stream, fc) : fc();
+  if (e == hipSuccess) e = ss::launch_ring_end(p->ring, p->ring + 1, p->seg, p->seg + 2 * p->G, g, stream);
+  if (e != hipSuccess || !p->promote) return e;
+  ss::MaterializeArgs ma{};
+  ma.dk = p->dk; ma.dv = p->dv; ma.cap_d = (int)p->cap_d; ma.list = p->promote_list;
+  ma.count = p->counters + ss::C_PROMOTE_COUNT; ma.meta = p->meta; ma.act = p->act; ma.frz = p->frz;
+  ma.dense = p->dense; ma.dslot = p->dslot; ma.counters = p->counters;
+  ma.hflag = p->hflags_dev + HF_DENSE_CAP;
+  const int64_t gsz = p->group_size[g];
+  auto fm = [&] { return ss::launch_materialize(ma, gsz, stream); };
+  return timing ? timed(p, SS_KERNEL_MATERIALIZE, stream, fm) : fm();
+}
+
+// promoted states leave the factored-state list
+static hipError_t enqueue_prune(ss_pool *p, int64_t fact_grid, hipStream_t stream) {
+  return ss::launch_prune_factored(p->fact_ids[0], p->counters + ss::C_FACT0, p->fact_ids[1],
+                                   p->counters + ss::C_FACT1, fact_grid, p->meta, p->hflags_dev + HF_FACT, stream);
+}
+
+// host bookkeeping after the compaction of group g was enqueued with segment bounds ab
+static void after_compact_group(ss_pool *p, int g, const int64_t (&ab)[2]) {
+  for (int R = 0; R < 2; ++R) {  // the group's new segment, by its bound
+    p->last_seq[R][g] = p->seq;
+    p->seg_bound[R][g] = ab[R];
+    p->recs[R].push_back({p->seq++, g, ab[R]});
+  }
+  if (p->promote) p->dense_upper = std::min<int64_t>(p->cap_d, p->dense_upper + p->group_size[g]);
+}
+
+static void refresh_fact_upper(ss_pool *p) {
+  if (p->hflags) {  // a stale value is still an upper bound: the list only shrinks
+    const uint32_t seen = ((const volatile uint32_t *)p->hflags)[HF_FACT];
+    p->fact_upper = std::min<int64_t>(p->fact_upper, seen);
+  }
+}
+
 static ss_status run_decode(ss_pool *p, const float *q, const float *k, const float *v, const float *alpha,
                             const float *beta, float *o, bool readonly, hipStream_t stream) {
   if (!p) return fail(SS_ERR_ARG, "pool is NULL");
@@ -665,33 +764,9 @@ static ss_status run_decode(ss_pool *p, const float *q, const float *k, const fl
   if (!q || !o) return fail(SS_ERR_ARG, "q and o are required");
   if (!readonly && (!k || !v || !alpha)) return fail(SS_ERR_ARG, "k, v and alpha are required");
   if (!readonly && p->any_delta && !beta) return fail(SS_ERR_ARG, "beta is required: the pool has delta-rule states");
-  hipError_t e = hipSuccess;
-  if (p->hflags) {  // a stale value is still an upper bound: the list only shrinks
-    const uint32_t seen = ((const volatile uint32_t *)p->hflags)[HF_FACT];
-    p->fact_upper = std::min<int64_t>(p->fact_upper, seen);
-  }
-  if (!p->force_dense && p->fact_upper > 0) {
-    ss::DecodeArgs a{};
-    a.N = p->fact_upper; a.dk = p->dk; a.dv = p->dv; a.K = p->K; a.meta = p->meta; a.act = p->act; a.frz = p->frz;
-    a.fact_ids = p->fact_ids[p->fact_par]; a.fact_count = p->counters + ss::C_FACT0 + p->fact_par;
-    a.pk = p->pk; a.pw = p->pw; a.pc = p->pc; a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.o = o;
-    a.counters = p->counters; a.acct = p->acct + ss::A_DECODE_FACTORED * ss::kAcctSlots;
-    a.hflag = p->hflags_dev + HF_PAD;
-    e = timed(p, readonly ? SS_KERNEL_READOUT_FACTORED : SS_KERNEL_DECODE_FACTORED, stream,
-              [&] { return ss::launch_decode_factored(a, readonly, p->any_delta, stream); });
-    if (e != hipSuccess) return hip_fail(e, "decode (factored) launch");
-  }
-  if (p->dense_upper > 0) {
-    ss::DenseArgs a{};
-    a.dk = p->dk; a.dv = p->dv; a.K = p->K; a.cap_d = (uint32_t)p->cap_d; a.meta = p->meta; a.dense = p->dense;
-    a.dslot = p->dslot; a.pk = p->dpk; a.pw = p->dpw; a.pc = p->dpc;
-    a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.o = o;
-    a.counters = p->counters; a.acct = p->acct + ss::A_DECODE_DENSE * ss::kAcctSlots;
-    e = timed(p, readonly ? SS_KERNEL_READOUT_DENSE : SS_KERNEL_DECODE_DENSE, stream,
-              [&] { return ss::launch_decode_dense(a, p->dense_upper, readonly, p->any_delta, stream); });
-    if (e != hipSuccess) return hip_fail(e, "decode (dense) launch");
-  }
-  return SS_OK;
+  refresh_fact_upper(p);
+  const hipError_t e = enqueue_decode(p, q, k, v, alpha, beta, o, readonly, p->fact_upper, p->dense_upper, true, stream);
+  return e == hipSuccess ? SS_OK : hip_fail(e, "decode launch");
 }
 
 ss_status ss_decode_step(ss_pool *p, const float *q, const float *k, const float *v, const float *alpha,
@@ -714,62 +789,21 @@ ss_status ss_compact(ss_pool *p, int32_t group, hipStream_t stream) {
   if (group >= p->G) return fail(SS_ERR_ARG, "group out of range");
   if (p->force_dense) return SS_OK;  // dense states have no pad to compact
   const int g0 = group < 0 ? 0 : group, g1 = group < 0 ? p->G : group + 1;
+  bool any = false;
   for (int g = g0; g < g1; ++g) {
     if (p->group_size[g] == 0) continue;
-    hipError_t e = ss::launch_zero_u32(p->counters + ss::C_PROMOTE_COUNT, 1, stream);
-    if (e != hipSuccess) return hip_fail(e, "compact launch");
-    if (p->dense_upper > 0) {  // dense members: fold a non-empty pad into H
-      ss::DenseArgs da{};
-      da.dk = p->dk; da.dv = p->dv; da.K = p->K; da.cap_d = (uint32_t)p->cap_d; da.meta = p->meta;
-      da.dense = p->dense; da.dslot = p->dslot; da.pk = p->dpk; da.pw = p->dpw; da.pc = p->dpc;
-      da.members = p->members + p->group_start[g]; da.n_members = (int32_t)p->group_size[g];
-      da.counters = p->counters; da.acct = p->acct;
-      e = timed(p, SS_KERNEL_DENSE_FOLD, stream, [&] { return ss::launch_dense_fold(da, stream); });
-      if (e != hipSuccess) return hip_fail(e, "dense fold launch");
-    }
-    int64_t ab[2];
-    st = ensure_ring_space(p, g, stream, ab);
+    any = true;
+    int64_t ab[1][2];
+    st = ensure_ring_space(p, &g, 1, stream, ab);
     if (st != SS_OK) return st;
-    e = ss::launch_ring_begin(p->ring, p->ring + 1, p->seg, p->seg + 2 * p->G, p->G, p->act.cap, p->frz.cap, stream);
-    if (e != hipSuccess) return hip_fail(e, "ring launch");
-    ss::CompactArgs a{};
-    a.dk = p->dk; a.dv = p->dv; a.K = p->K; a.r = p->r; a.L = p->L; a.promote = p->promote; a.fcap = p->fcap;
-    a.n_members = (int32_t)p->group_size[g];
-    a.members = p->members + p->group_start[g];
-    a.eps = p->eps; a.meta = p->meta; a.act = p->act; a.frz = p->frz;
-    a.ring_a = p->ring; a.ring_f = p->ring + 1; a.hflag = p->hflags_dev + HF_RING;
-    a.pk = p->pk; a.pw = p->pw; a.pc = p->pc; a.promote_list = p->promote_list; a.counters = p->counters;
-    a.acct_flops = p->acct + ss::A_COMPACT_FLOPS * ss::kAcctSlots;
-    a.acct_states = p->acct + ss::A_COMPACT_STATES * ss::kAcctSlots;
-    e = timed(p, SS_KERNEL_COMPACT, stream, [&] { return ss::launch_compact(a, stream); });
-    if (e == hipSuccess) e = ss::launch_ring_end(p->ring, p->ring + 1, p->seg, p->seg + 2 * p->G, g, stream);
+    const hipError_t e = enqueue_compact_group(p, g, p->dense_upper > 0, true, stream);
     if (e != hipSuccess) return hip_fail(e, "compact launch");
-    for (int R = 0; R < 2; ++R) {  // the group's new segment, by its bound
-      p->last_seq[R][g] = p->seq;
-      p->seg_bound[R][g] = ab[R];
-      p->recs[R].push_back({p->seq++, g, ab[R]});
-    }
-    if (p->promote) {
-      ss::MaterializeArgs ma{};
-      ma.dk = p->dk; ma.dv = p->dv; ma.cap_d = (int)p->cap_d; ma.list = p->promote_list;
-      ma.count = p->counters + ss::C_PROMOTE_COUNT; ma.meta = p->meta; ma.act = p->act; ma.frz = p->frz;
-      ma.dense = p->dense; ma.dslot = p->dslot; ma.counters = p->counters;
-      ma.hflag = p->hflags_dev + HF_DENSE_CAP;
-      const int64_t gsz = p->group_size[g];
-      e = timed(p, SS_KERNEL_MATERIALIZE, stream, [&] { return ss::launch_materialize(ma, gsz, stream); });
-      if (e != hipSuccess) return hip_fail(e, "promote launch");
-      p->dense_upper = std::min<int64_t>(p->cap_d, p->dense_upper + p->group_size[g]);
-    }
+    after_compact_group(p, g, ab[0]);
   }
-  if (p->promote && p->fact_upper > 0) {  // promoted states leave the factored-state list
-    const int cur = p->fact_par, nxt = 1 - cur;
-    hipError_t e = ss::launch_zero_u32(p->counters + ss::C_FACT0 + nxt, 1, stream);
-    if (e == hipSuccess)
-      e = ss::launch_prune_factored(p->fact_ids[cur], p->counters + ss::C_FACT0 + cur, p->fact_upper,
-                                    p->fact_ids[nxt], p->counters + ss::C_FACT0 + nxt, p->meta,
-                                    p->hflags_dev + HF_FACT, stream);
+  refresh_fact_upper(p);
+  if (any && p->promote && p->fact_upper > 0) {
+    const hipError_t e = enqueue_prune(p, p->fact_upper, stream);
     if (e != hipSuccess) return hip_fail(e, "factored-list launch");
-    p->fact_par = nxt;
   }
   p->compact_calls++;
   return SS_OK;
@@ -980,6 +1014,134 @@ ss_status ss_pool_stats(ss_pool *p, ss_stats *out, hipStream_t stream) {
 ss_status ss_pool_timing(ss_pool *p, int32_t enable) {
   if (!p) return fail(SS_ERR_ARG, "pool is NULL");
   p->timing = enable != 0;
+  return SS_OK;
+}
+
+// ---- graph replay of whole steps ---------------------------------------------------------------
+}  // extern "C"
+
+struct ss_step_graph {
+  ss_pool *pool = nullptr;
+  const float *q = nullptr, *k = nullptr, *v = nullptr, *alpha = nullptr, *beta = nullptr;
+  float *o = nullptr;
+  hipStream_t cs = nullptr;                // capture stream (graphs are launched on the caller's stream)
+  std::vector<hipGraphExec_t> exec;        // one per phase of the schedule (step mod K)
+  std::vector<std::vector<int>> due;       // groups compacted in each phase
+  int64_t version = -1;                    // pool layout the graphs were captured against
+  int64_t fact_grid = 0, dense_grid = 0;   // grid bounds captured
+};
+
+namespace {
+
+void drop_execs(ss_step_graph *sg) {
+  for (auto &x : sg->exec)
+    if (x) (void)hipGraphExecDestroy(x);
+  for (auto &x : sg->exec) x = nullptr;
+}
+
+// Capture one graph per phase: the decode of every state, then the compactions due in that
+// phase, then the pruning of the factored-state list.  Grid sizes are bounds that stay valid for
+// the pool's life: the factored list only shrinks, and the dense slots in use never exceed the
+// dense states at capture plus every factored one.
+ss_status capture_all(ss_step_graph *sg) {
+  ss_pool *p = sg->pool;
+  drop_execs(sg);
+  refresh_fact_upper(p);
+  sg->fact_grid = p->force_dense ? 0 : p->fact_upper;
+  sg->dense_grid = std::min<int64_t>(p->cap_d, p->dense_upper + (p->promote ? sg->fact_grid : 0));
+  for (int ph = 0; ph < p->K; ++ph) {
+    hipError_t e = hipStreamBeginCapture(sg->cs, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) return hip_fail(e, "graph capture");
+    e = enqueue_decode(p, sg->q, sg->k, sg->v, sg->alpha, sg->beta, sg->o, false, sg->fact_grid, sg->dense_grid,
+                       false, sg->cs);
+    for (size_t i = 0; e == hipSuccess && i < sg->due[ph].size(); ++i)
+      e = enqueue_compact_group(p, sg->due[ph][i], sg->dense_grid > 0, false, sg->cs);
+    if (e == hipSuccess && !sg->due[ph].empty() && p->promote && sg->fact_grid > 0)
+      e = enqueue_prune(p, sg->fact_grid, sg->cs);
+    hipGraph_t graph = nullptr;
+    const hipError_t e2 = hipStreamEndCapture(sg->cs, &graph);
+    if (e == hipSuccess) e = e2;
+    if (e == hipSuccess) e = hipGraphInstantiate(&sg->exec[ph], graph, nullptr, nullptr, 0);
+    if (graph) (void)hipGraphDestroy(graph);
+    if (e != hipSuccess) {
+      drop_execs(sg);
+      return hip_fail(e, "graph capture");
+    }
+  }
+  sg->version = p->layout_version;
+  return SS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ss_status ss_step_graph_create(ss_pool *p, const float *q, const float *k, const float *v, const float *alpha,
+                               const float *beta, float *o, ss_step_graph **out) {
+  if (!out) return fail(SS_ERR_ARG, "out is NULL");
+  *out = nullptr;
+  if (!p) return fail(SS_ERR_ARG, "pool is NULL");
+  if (!q || !k || !v || !alpha || !o) return fail(SS_ERR_ARG, "q, k, v, alpha and o are required");
+  if (p->any_delta && !beta) return fail(SS_ERR_ARG, "beta is required: the pool has delta-rule states");
+  ss_status st = poll(p);
+  if (st != SS_OK) return st;
+  ss_step_graph *sg = new (std::nothrow) ss_step_graph();
+  if (!sg) return fail(SS_ERR_OOM, "host allocation failed");
+  sg->pool = p; sg->q = q; sg->k = k; sg->v = v; sg->alpha = alpha; sg->beta = beta; sg->o = o;
+  sg->exec.assign(p->K, nullptr);
+  sg->due.assign(p->K, {});
+  for (int ph = 0; ph < p->K; ++ph)
+    for (int g = 0; g < p->G; ++g)
+      if (!p->force_dense && p->group_size[g] > 0 && (ph + p->group_offset[g]) % p->K == 0) sg->due[ph].push_back(g);
+  hipError_t e = hipStreamCreateWithFlags(&sg->cs, hipStreamNonBlocking);
+  if (e != hipSuccess) {
+    delete sg;
+    return hip_fail(e, "capture stream");
+  }
+  st = capture_all(sg);
+  if (st != SS_OK) {
+    (void)hipStreamDestroy(sg->cs);
+    delete sg;
+    return st;
+  }
+  *out = sg;
+  return SS_OK;
+}
+
+ss_status ss_step_graph_launch(ss_step_graph *sg, int64_t step, hipStream_t stream) {
+  if (!sg) return fail(SS_ERR_ARG, "graph is NULL");
+  ss_pool *p = sg->pool;
+  ss_status st = poll(p);
+  if (st != SS_OK) return st;
+  const int ph = (int)(((step % p->K) + p->K) % p->K);
+  const std::vector<int> &due = sg->due[ph];
+  std::vector<int64_t> ab(2 * due.size() + 2, 0);
+  auto abp = reinterpret_cast<int64_t(*)[2]>(ab.data());
+  if (!due.empty()) {
+    st = ensure_ring_space(p, due.data(), (int)due.size(), stream, abp);
+    if (st != SS_OK) return st;
+  }
+  refresh_fact_upper(p);
+  // capture again when a re-pack moved the rings, or when the factored list has shrunk to half the
+  // captured grid (the graphs then stop launching work for states that have gone dense)
+  if (sg->version != p->layout_version || 2 * p->fact_upper < sg->fact_grid) {
+    st = capture_all(sg);
+    if (st != SS_OK) return st;
+  }
+  const hipError_t e = hipGraphLaunch(sg->exec[ph], stream);
+  if (e != hipSuccess) return hip_fail(e, "graph launch");
+  for (size_t i = 0; i < due.size(); ++i) after_compact_group(p, due[i], abp[i]);
+  p->decode_calls++;
+  if (!due.empty()) p->compact_calls++;
+  return SS_OK;
+}
+
+ss_status ss_step_graph_destroy(ss_step_graph *sg) {
+  if (!sg) return SS_OK;
+  (void)hipStreamSynchronize(sg->cs);
+  drop_execs(sg);
+  (void)hipStreamDestroy(sg->cs);
+  delete sg;
   return SS_OK;
 }
 

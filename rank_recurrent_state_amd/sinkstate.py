@@ -90,11 +90,15 @@ def load_library():
     lib.ss_dense_rank_limit.restype = ctypes.c_int32
     lib.ss_decode_bytes_per_state.argtypes = [ctypes.c_int32] * 7
     lib.ss_decode_bytes_per_state.restype = ctypes.c_uint64
+    lib.ss_step_graph_create.argtypes = [vp] + [vp] * 6 + [ctypes.POINTER(vp)]
+    lib.ss_step_graph_launch.argtypes = [vp, ctypes.c_int64, vp]
+    lib.ss_step_graph_destroy.argtypes = [vp]
     lib.ss_status_string.argtypes = [ctypes.c_int]
     lib.ss_status_string.restype = ctypes.c_char_p
     lib.ss_last_error.restype = ctypes.c_char_p
     for name in ("ss_state_pool_create", "ss_state_pool_destroy", "ss_decode_step", "ss_readout", "ss_compact",
-                 "ss_schedule_due", "ss_state_export", "ss_pool_stats", "ss_pool_timing"):
+                 "ss_schedule_due", "ss_state_export", "ss_pool_stats", "ss_pool_timing", "ss_step_graph_create",
+                 "ss_step_graph_launch", "ss_step_graph_destroy"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -203,6 +207,35 @@ def decode_step(pool: StatePool, q, k, v, alpha, beta, o, stream=None):
     args = [_ptr(q, N * dk, "q"), _ptr(k, N * dk, "k"), _ptr(v, N * dv, "v"), _ptr(alpha, N, "alpha"),
             _ptr(beta, N, "beta") if beta is not None else None, _ptr(o, N * dv, "o")]
     _check(load_library().ss_decode_step(pool.handle, *args, _stream(stream)))
+
+
+class StepGraph:
+    """Owner of one ss_step_graph: whole steps (decode + due compactions) replayed as HIP graphs
+    on fixed input/output tensors."""
+
+    def __init__(self, pool: StatePool, q, k, v, alpha, beta, o):
+        N, dk, dv = pool.N, pool.d_k, pool.d_v
+        self.pool = pool
+        self.buffers = (q, k, v, alpha, beta, o)  # kept alive while the graphs may read them
+        args = [_ptr(q, N * dk, "q"), _ptr(k, N * dk, "k"), _ptr(v, N * dv, "v"), _ptr(alpha, N, "alpha"),
+                _ptr(beta, N, "beta") if beta is not None else None, _ptr(o, N * dv, "o")]
+        h = ctypes.c_void_p()
+        _check(load_library().ss_step_graph_create(pool.handle, *args, ctypes.byref(h)))
+        self.handle = h
+
+    def launch(self, step: int, stream=None):
+        _check(load_library().ss_step_graph_launch(self.handle, int(step), _stream(stream)))
+
+    def close(self):
+        if self.handle:
+            load_library().ss_step_graph_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def readout(pool: StatePool, q, o, stream=None):

@@ -99,6 +99,11 @@ def test_calls_on_null_pool_are_rejected(lib):
     n = ctypes.c_size_t()
     assert lib.ss_state_export(None, None, 0, None, 0, ctypes.byref(n), None) == ss.SS_ERR_ARG
     assert lib.ss_state_pool_destroy(None) == ss.SS_OK
+    out = ctypes.c_void_p()
+    assert lib.ss_step_graph_create(None, None, None, None, None, None, None, ctypes.byref(out)) == ss.SS_ERR_ARG
+    assert lib.ss_step_graph_create(None, None, None, None, None, None, None, None) == ss.SS_ERR_ARG
+    assert lib.ss_step_graph_launch(None, 0, None) == ss.SS_ERR_ARG
+    assert lib.ss_step_graph_destroy(None) == ss.SS_OK
 
 
 def test_dense_rank_limit_pins(lib):
