@@ -68,6 +68,9 @@ def _load():
     lib.orc_brand.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _dp, _dp, _dp, _dp, _dp, _dp]
     lib.orc_schedule_due.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                      ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+    lib.orc_rsvd_init.argtypes = [ctypes.c_int, ctypes.c_int, _dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _dp,
+                                  ctypes.c_double, ctypes.c_int, _dp, _dp, _dp]
+    lib.orc_rsvd_init.restype = ctypes.c_int
     lib.orc_max_threads.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -129,6 +132,26 @@ def brand_update(UC, VC, sc):
     if rc < 0:
         raise MemoryError("oracle brand update failed")
     return Uo.T.copy(), so, Vo.T.copy()
+
+
+def rsvd_init(S, omega, eps, iters=2, max_rank=None):
+    """Randomized block SVD of a dense state S (d_k x d_v): omega is (nb, d_k, b), one Gaussian
+    block per entry.  Returns U (R x d_k), V (R x d_v), sigma (R) with S ~ U^T diag(sigma) V."""
+    S = np.asarray(S, dtype=np.float64)
+    d_k, d_v = S.shape
+    omega = np.asarray(omega, dtype=np.float64)
+    nb, dk2, b = omega.shape
+    assert dk2 == d_k
+    max_rank = min(d_k, d_v) if max_rank is None else int(max_rank)
+    om = _f64(np.transpose(omega, (0, 2, 1)))  # per block column-major (d_k x b)
+    U = np.zeros((max(1, max_rank), d_k))
+    V = np.zeros((max(1, max_rank), d_v))
+    sig = np.zeros(max(1, max_rank))
+    R = _load().orc_rsvd_init(d_k, d_v, _ptr(_f64(S)), b, nb, int(iters), _ptr(om), float(eps), max_rank, _ptr(U),
+                              _ptr(V), _ptr(sig))
+    if R < 0:
+        raise MemoryError("oracle randomized SVD failed")
+    return U[:R].copy(), V[:R].copy(), sig[:R].copy()
 
 
 def schedule_due(step: int, K: int, offsets) -> list:

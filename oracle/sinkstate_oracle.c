@@ -26,6 +26,8 @@
  *             (SinkState, 4.2 "(ii) Top-subspace SVD", Figure 6(b) step 3).
  *   dense     states whose rank exceeds floor(d_k d_v / (d_k + d_v)) are held
  *             as a dense matrix (SinkState, 4.4 "Memory layout").
+ *   init      randomized block SVD of a dense state after prefill
+ *             (SinkState, 4.2 "Randomized SVD initialization after prefill").
  *
  * Decay is applied literally, every step, to every sigma and pad weight.  QR
  * is Householder, the small SVD is cyclic one-sided (Hestenes) Jacobi, both
@@ -622,6 +624,90 @@ int orc_schedule_due(int64_t step, int K, int n_groups, const int32_t *offsets, 
     if (x == 0) out[c++] = g;
   }
   return c;
+}
+
+/* ------------------------------------------------------------------ */
+/* Randomized SVD initialization of a dense state, block by block       */
+/* (SinkState 4.1; 4.2 "Randomized SVD initialization after prefill",   */
+/* Figure 6(a); Halko et al. 2011).  The pages write the state as        */
+/* H = S^T (d_v x d_k, y = H q); here S is d_k x d_v row-major.           */
+/* For each block k, with the caller's Gaussian Omega_k (d_k x b):       */
+/*   repeat `iters` times:  Y = H Omega (= S^T Omega),  Q = orth(Y),      */
+/*                          Omega = H^T Q (= S Q);                        */
+/*   block SVD of Omega = X diag(sig) W^T gives the block's components    */
+/*   u = X (d_k side), v = Q W (d_v side), sig;                           */
+/*   the first block's largest sig is sigma_0; components with            */
+/*   sig >= eps sigma_0 and sig > 0 are kept; if any is below, no further */
+/*   block is taken.  Otherwise the block is removed from the residual,   */
+/*   S <- S - X diag(sig) (Q W)^T, and the next block starts from it.     */
+/* Also stops after nb blocks or once `max_rank` components are kept.    */
+/* orth is the Q of the Householder thin QR; the block SVD is the        */
+/* one-sided Jacobi SVD above.  omega: block k at omega + k d_k b,        */
+/* column-major (column c at + c d_k).  Outputs are rows: U[i] at         */
+/* U + i d_k, V[i] at V + i d_v, sig[i], descending within each block.   */
+/* Returns the number of components kept, or -1 on allocation failure.  */
+/* ------------------------------------------------------------------ */
+int orc_rsvd_init(int d_k, int d_v, const double *S, int b, int nb, int iters, const double *omega, double eps,
+                  int max_rank, double *U, double *V, double *sig) {
+  int R = 0, rc = -1;
+  double sigma0 = 0.0;
+  if (iters < 1) iters = 1;
+  double *Sr = (double *)malloc((size_t)d_k * d_v * sizeof(double));
+  double *Om = (double *)malloc((size_t)d_k * b * sizeof(double));  /* d_k x b, column-major */
+  double *Y = (double *)malloc((size_t)d_v * b * sizeof(double));   /* d_v x b */
+  double *Q = (double *)malloc((size_t)d_v * b * sizeof(double));
+  double *Rq = (double *)malloc((size_t)b * b * sizeof(double));
+  double *X = (double *)malloc((size_t)d_k * b * sizeof(double));
+  double *W = (double *)malloc((size_t)b * b * sizeof(double));
+  double *sb = (double *)malloc((size_t)b * sizeof(double));
+  double *QW = (double *)malloc((size_t)d_v * b * sizeof(double));
+  if (!Sr || !Om || !Y || !Q || !Rq || !X || !W || !sb || !QW || b < 1 || b > d_v || b > d_k) goto done;
+  memcpy(Sr, S, (size_t)d_k * d_v * sizeof(double));
+  for (int blk = 0; blk < nb && R < max_rank; ++blk) {
+    memcpy(Om, omega + (size_t)blk * d_k * b, (size_t)d_k * b * sizeof(double));
+    for (int it = 0; it < iters; ++it) {
+      for (int c = 0; c < b; ++c) /* Y = S^T Omega */
+        for (int j = 0; j < d_v; ++j) {
+          double acc = 0.0;
+          for (int i = 0; i < d_k; ++i) acc += Sr[(size_t)i * d_v + j] * Om[(size_t)c * d_k + i];
+          Y[(size_t)c * d_v + j] = acc;
+        }
+      if (orc_householder_qr(d_v, b, Y, Q, Rq) < 0) goto done;
+      for (int c = 0; c < b; ++c) /* Omega = S Q */
+        for (int i = 0; i < d_k; ++i) {
+          double acc = 0.0;
+          for (int j = 0; j < d_v; ++j) acc += Sr[(size_t)i * d_v + j] * Q[(size_t)c * d_v + j];
+          Om[(size_t)c * d_k + i] = acc;
+        }
+    }
+    if (orc_jacobi_svd(d_k, b, Om, X, sb, W) < 0) goto done;
+    for (int c = 0; c < b; ++c) /* v = Q W */
+      for (int j = 0; j < d_v; ++j) {
+        double acc = 0.0;
+        for (int t = 0; t < b; ++t) acc += Q[(size_t)t * d_v + j] * W[(size_t)c * b + t];
+        QW[(size_t)c * d_v + j] = acc;
+      }
+    if (blk == 0) sigma0 = sb[0];
+    int kept = 0;
+    for (int c = 0; c < b && R < max_rank; ++c) {
+      if (!(sb[c] >= eps * sigma0 && sb[c] > 0.0)) break;  /* descending: the rest are below too */
+      for (int i = 0; i < d_k; ++i) U[(size_t)R * d_k + i] = X[(size_t)c * d_k + i];
+      for (int j = 0; j < d_v; ++j) V[(size_t)R * d_v + j] = QW[(size_t)c * d_v + j];
+      sig[R] = sb[c];
+      ++R;
+      ++kept;
+    }
+    if (kept < b) break;
+    for (int c = 0; c < b; ++c) /* remove the block from the residual */
+      for (int i = 0; i < d_k; ++i) {
+        const double f = sb[c] * X[(size_t)c * d_k + i];
+        for (int j = 0; j < d_v; ++j) Sr[(size_t)i * d_v + j] -= f * QW[(size_t)c * d_v + j];
+      }
+  }
+  rc = R;
+done:
+  free(Sr); free(Om); free(Y); free(Q); free(Rq); free(X); free(W); free(sb); free(QW);
+  return rc;
 }
 
 int orc_max_threads(void) {

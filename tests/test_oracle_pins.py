@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 
 from oracle import OraclePool, brand_update, householder_qr, jacobi_svd, schedule_due
+from oracle.oracle import rsvd_init
 from oracle.oracle import OracleState
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
@@ -452,3 +453,76 @@ def test_pad_overflow_is_reported():
     P.decode(x, x, x, np.array([0.9]))
     with pytest.raises(RuntimeError):
         P.decode(x, x, x, np.array([0.9]))
+
+
+# --------------------------------------------------------------------------
+# randomized block SVD initialization after prefill
+# --------------------------------------------------------------------------
+def test_rsvd_fig6a_blocks_and_stop():
+    """Figure 6(a): blocks of 2 on a 4x4 state with singular values [8.0, 1.95, 1.10, 0.06] and
+    eps = 0.1: the first block finds [8.0, 1.95], the second [1.10, 0.06]; 0.06 < 0.8 is dropped
+    and no third block is taken."""
+    g = json.load(open(os.path.join(GOLD, "sinkstate_fig6a_rsvd_init.json")))
+    rng = np.random.default_rng(61)
+    U, V = _orth(rng, 4, 4), _orth(rng, 4, 4)
+    S = (U * np.array(g["state_sigma"])) @ V.T
+    om = rng.standard_normal((3, 4, g["block"]))
+    Uo, Vo, so = rsvd_init(S, om, g["eps"], iters=40)
+    assert np.allclose(so, g["kept_printed"], atol=1e-9)
+    assert abs(g["threshold_printed"] - g["eps"] * g["block1_printed"][0]) < 1e-12
+    # what is left out is the 0.06 component: the reconstruction error is exactly it
+    err = np.linalg.norm(S - Uo.T @ np.diag(so) @ Vo, 2)
+    assert abs(err - g["block2_printed"][1]) < 1e-9
+    # the threshold is eps times the first block's sigma_0, not the current block's largest:
+    # a second-block 0.5 is below 0.8 although it is above 0.1 * 1.10
+    S2 = (U * np.array([8.0, 1.95, 1.10, 0.5])) @ V.T
+    _, _, so2 = rsvd_init(S2, om, g["eps"], iters=40)
+    assert np.allclose(so2, [8.0, 1.95, 1.10], atol=1e-9)
+
+
+@pytest.mark.parametrize("shape,rank,b", [((16, 12), 5, 8), ((32, 20), 8, 8), ((24, 24), 3, 4)])
+def test_rsvd_exact_when_rank_fits_one_block(shape, rank, b):
+    """A state whose rank fits in one block: the range finder spans it exactly, so the first
+    block is the exact SVD (numpy's, to 1e-10) and the second finds nothing (stop)."""
+    rng = np.random.default_rng(7 + rank)
+    d_k, d_v = shape
+    U, V = _orth(rng, d_k, rank), _orth(rng, d_v, rank)
+    sig = np.sort(rng.uniform(0.1, 3.0, rank))[::-1]
+    S = (U * sig) @ V.T
+    om = rng.standard_normal((3, d_k, b))
+    Uo, Vo, so = rsvd_init(S, om, 1e-8, iters=1)
+    assert len(so) == rank
+    assert np.allclose(so, np.linalg.svd(S, compute_uv=False)[:rank], rtol=1e-10, atol=0)
+    assert np.linalg.norm(S - Uo.T @ np.diag(so) @ Vo) <= 1e-12 * np.linalg.norm(S)
+    assert np.allclose(Uo @ Uo.T, np.eye(rank), atol=1e-10)
+    assert np.allclose(Vo @ Vo.T, np.eye(rank), atol=1e-10)
+
+
+def test_rsvd_full_block_is_exact_svd():
+    """With one block as wide as the state, orth(S^T Omega) spans everything and the block SVD is
+    the SVD of the state (numpy's singular values to 1e-10); eps drops the tail exactly as the
+    threshold says."""
+    rng = np.random.default_rng(5)
+    d_k, d_v = 12, 8
+    S = rng.standard_normal((d_k, d_v)) * np.logspace(0, -3, d_v)
+    ref = np.linalg.svd(S, compute_uv=False)
+    om = rng.standard_normal((1, d_k, d_v))
+    eps = 0.02
+    Uo, Vo, so = rsvd_init(S, om, eps, iters=1)
+    keep = ref[ref >= eps * ref[0]]
+    assert np.allclose(so, keep, rtol=1e-10, atol=0)
+    assert np.allclose(np.linalg.norm(S - Uo.T @ np.diag(so) @ Vo, 2), ref[len(keep)], rtol=1e-8)
+
+
+def test_rsvd_blocks_cover_the_state_and_zero_state_is_empty():
+    """Blocks after the first are taken from the residual: on a full-rank state with eps = 0
+    they keep going until max_rank, and the factors then reconstruct the state exactly.
+    A zero state has no component."""
+    rng = np.random.default_rng(9)
+    S = rng.standard_normal((10, 6))
+    om = rng.standard_normal((3, 10, 2))
+    Uo, Vo, so = rsvd_init(S, om, 0.0, iters=2)
+    assert len(so) == 6
+    assert np.linalg.norm(S - Uo.T @ np.diag(so) @ Vo) <= 1e-12 * np.linalg.norm(S)
+    Uz, Vz, sz = rsvd_init(np.zeros((10, 6)), om, 0.1, iters=2)
+    assert len(sz) == 0
