@@ -88,6 +88,35 @@ def graph_replay(ss, torch, W, steps=256, warm=16):
     return out
 
 
+def rsvd_init_rate(ss, torch, n=32768, d_k=128, d_v=80, b=8, nb=7, iters=2, eps=3e-3, seed=20261202):
+    """Randomized block SVD initialization of prefill-like dense states (a spectrum decaying as
+    0.6^i over 24 random directions plus 1e-4 noise) on the GPU.  Algorithmic flops per block:
+    (4 iters + 2) d_k d_v b for the products with the state and the subtraction, plus the QRs."""
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    r = 24
+    A = torch.randn(n, d_k, r, device="cuda", generator=g) * (0.6 ** torch.arange(r, device="cuda"))
+    B = torch.randn(n, d_v, r, device="cuda", generator=g)
+    S = torch.bmm(A, B.transpose(1, 2).contiguous()) / r ** 0.5
+    S += 1e-4 * torch.randn(n, d_k, d_v, device="cuda", generator=g)
+    om = torch.randn(n, nb, d_k, b, device="cuda", generator=g)
+    del A, B
+    ss.rsvd_init(S[:64].contiguous(), om[:64].contiguous(), eps, iters=iters)  # warm-up
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    u, v, sg, rk = ss.rsvd_init(S, om, eps, iters=iters)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    rk = rk.double()
+    blocks = torch.clamp(torch.floor(rk / b) + 1, max=nb)
+    per_block = (4 * iters + 2) * d_k * d_v * b + iters * 4 * d_v * b * b + 4 * d_k * b * b + 2 * (d_k + d_v) * b * b
+    flops = float(blocks.sum().item()) * per_block
+    return {"n_states": n, "shape": [d_k, d_v], "block": b, "iters": iters, "ms": ms,
+            "states_per_s": n / (ms / 1e3), "mean_rank": float(rk.mean().item()),
+            "algorithmic_TFLOPs": flops / (ms / 1e3) / 1e12, "fp32_peak_TFLOPs": 157.3}
+
+
 def cpu_baseline(w, init, n_sample, n_steps, device="cpu"):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload, all host cores.
     Inputs are drawn per step for the sampled states on `device` and copied to the host (not timed);
@@ -181,7 +210,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 4 GiB device copy (for scaling rocprof byte counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-graph", action="store_true", help="skip the eager-versus-graph step timing")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the eager-versus-graph step timing and the initialization timing")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "single-GPU implementation: --gpus must be 1 (the path shards by request "
@@ -302,6 +332,10 @@ def main():
         log(f"[bench] dense baseline {dense['ms_per_step']:.3f} ms/step, {dense['achieved_GBs']:.0f} GB/s")
 
     graphs = graph_replay(ss, torch, W) if not args.no_graph else None
+    init_rate = rsvd_init_rate(ss, torch) if not args.no_graph else None
+    if init_rate:
+        log(f"[bench] randomized SVD init: {init_rate['states_per_s']:.3e} states/s, "
+            f"{init_rate['algorithmic_TFLOPs']:.1f} TFLOP/s, mean rank {init_rate['mean_rank']:.1f}")
     if graphs:
         log("[bench] graph replay " + ", ".join(f"{k}: {v['eager_us_per_step']:.0f} -> {v['graph_us_per_step']:.0f} us/step"
                                                 for k, v in graphs.items()))
@@ -338,6 +372,7 @@ def main():
         "phases": phases,
         "dense_baseline": dense,
         "graph_replay": graphs,
+        "rsvd_init": init_rate,
     }
     print(json.dumps(out), flush=True)
 

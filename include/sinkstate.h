@@ -95,6 +95,9 @@ typedef struct {
   const float *u;          /* [comp_off[N]][d_k] */
   const float *v;          /* [comp_off[N]][d_v] */
   const float *sigma;      /* [comp_off[N]] */
+  const uint8_t *dense_mask; /* [N] or NULL: 1 = the state is given dense, in `dense`
+                                (it must have no components in the CSR) */
+  const float *dense;      /* [N][d_k][d_v] row-major S, read for the masked states only */
 } ss_init;
 
 /* kernels timed by ss_pool_timing */
@@ -189,6 +192,31 @@ ss_status ss_compact(ss_pool *pool, int32_t group, hipStream_t stream);
  * (step + group_offset[g]) mod K == 0.  Writes up to `cap` group ids to out
  * and returns their count in *n_due.  Host only. */
 ss_status ss_schedule_due(const ss_pool *pool, int64_t step, int32_t *out, int32_t cap, int32_t *n_due);
+
+/* Randomized block SVD initialization of dense states after prefill
+ * ([SS] 4.1; 4.2 "Randomized SVD initialization after prefill", Figure
+ * 6(a)).  For each of the n states S [d_k][d_v] (the pages' H = S^T), block
+ * by block, from the caller's Gaussian Omega_k [d_k][block]:
+ *   `iters` times:  Y = S^T Omega,  Q = orth(Y),  Omega = S Q;
+ *   block SVD Omega = X diag(sigma) W^T;  components u = X, v = Q W, sigma;
+ * sigma_0 is the first block's largest sigma; components with
+ * sigma >= eps sigma_0 and sigma > 0 are kept, in descending order within a
+ * block; if one is below, no further block is taken; otherwise the block is
+ * subtracted from the residual and the next block starts.  At most n_blocks
+ * blocks and max_rank components.  (The dense-fallback decision, rank > L,
+ * is the caller's: see ss_init.dense_mask.)
+ * All pointers are device memory, row-major, caller-owned:
+ *   S [n][d_k][d_v] (read), omega [n][n_blocks][d_k][block] (read),
+ *   eps [n] (read), work [n][d_k][d_v] (scratch, overwritten),
+ *   u [n][max_rank][d_k], v [n][max_rank][d_v], sigma [n][max_rank] (written
+ *   up to rank[s] per state), rank [n] (written).
+ * Enqueued on `stream`, no synchronization.  Shapes: d_k, d_v multiples of 4
+ * in [4, 256]; 1 <= block <= min(16, d_k, d_v); 1 <= iters <= 64;
+ * 1 <= max_rank <= min(d_k, d_v, n_blocks block).  Errors: SS_ERR_ARG,
+ * SS_ERR_SHAPE (checked on the host), SS_ERR_HIP. */
+ss_status ss_rsvd_init(const float *S, int64_t n, int32_t d_k, int32_t d_v, int32_t block, int32_t n_blocks,
+                       int32_t iters, const float *omega, const float *eps, int32_t max_rank, float *work, float *u,
+                       float *v, float *sigma, int32_t *rank, hipStream_t stream);
 
 /* Whole decode steps as HIP graphs ([SS] 4.4 "Kernel fusion, load balancing,
  * and support for CUDA graphs": the pages replay steps as graphs; here one

@@ -24,167 +24,18 @@
 // No global-memory intermediates: QR factors live in registers, the small
 // matrices in LDS (SinkState 4.4: fused chains of factor algebra).
 #include "ss_internal.h"
+#include "ss_linalg.h"
 #include "ss_wave.h"
 
 namespace ss {
 
 namespace {
 
-constexpr float kTau2 = 1e-10f;  // (1e-5)^2: CGS2 dependent-column test on squared norms
-constexpr float kTolJ = 1e-6f;   // Jacobi: rotate while |a_i.a_j| > tol |a_i| |a_j|
-constexpr int kMaxSweeps = 16;
 constexpr int kMaxFrozen = 256;  // frozen components per state (max_frozen <= 255)
 // LDS per wavefront, in floats
 constexpr int kOffRl = 0, kOffRr = 256, kOffCm = 512, kOffVh = 768, kOffScw = 1024, kOffSgs = 1040, kOffSraw = 1056,
               kOffPerm = 1072, kOffPosL = 1088, kOffFs = 1104, kOffPosF = kOffFs + kMaxFrozen,
               kLdsPerWave = kOffPosF + kMaxFrozen;
-
-// In-place CGS2 thin QR of the register-resident columns u[0..m) and v[0..m),
-// both sides interleaved (they are independent, so their reductions overlap).
-// R goes to LDS column-major 16 x 16: R[j * 16 + i] = R(i, j).  A column whose
-// residual is at most 1e-5 of its input norm is dependent: it and its R row are zeroed.
-template <int NS>
-__device__ __forceinline__ void cgs2_pair(float (&u)[kMaxM][NS], float (&v)[kMaxM][NS], int m, int lane, float *Ru,
-                                          float *Rv) {
-#pragma unroll
-  for (int j = 0; j < kMaxM; ++j) {
-    if (j < m) {
-      float n0u = 0.f, n0v = 0.f;
-#pragma unroll
-      for (int t = 0; t < NS; ++t) {
-        n0u = fmaf(u[j][t], u[j][t], n0u);
-        n0v = fmaf(v[j][t], v[j][t], n0v);
-      }
-      n0u = wave_sum_u(n0u);
-      n0v = wave_sum_u(n0v);
-      float ru[kMaxM], rv[kMaxM];
-#pragma unroll
-      for (int i = 0; i < kMaxM; ++i) ru[i] = rv[i] = 0.f;
-#pragma unroll
-      for (int pass = 0; pass < 2; ++pass) {
-        float du[kMaxM], dv[kMaxM];
-#pragma unroll
-        for (int i = 0; i < j; ++i) {
-          float x = 0.f, y = 0.f;
-#pragma unroll
-          for (int t = 0; t < NS; ++t) {
-            x = fmaf(u[i][t], u[j][t], x);
-            y = fmaf(v[i][t], v[j][t], y);
-          }
-          du[i] = wave_sum_u(x);
-          dv[i] = wave_sum_u(y);
-        }
-#pragma unroll
-        for (int i = 0; i < j; ++i) {
-          ru[i] += du[i];
-          rv[i] += dv[i];
-#pragma unroll
-          for (int t = 0; t < NS; ++t) {
-            u[j][t] = fmaf(-du[i], u[i][t], u[j][t]);
-            v[j][t] = fmaf(-dv[i], v[i][t], v[j][t]);
-          }
-        }
-      }
-      float nu = 0.f, nv = 0.f;
-#pragma unroll
-      for (int t = 0; t < NS; ++t) {
-        nu = fmaf(u[j][t], u[j][t], nu);
-        nv = fmaf(v[j][t], v[j][t], nv);
-      }
-      nu = wave_sum_u(nu);
-      nv = wave_sum_u(nv);
-      const bool ku = nu > 0.f && nu > kTau2 * n0u, kv = nv > 0.f && nv > kTau2 * n0v;
-      const float su = sqrtf(nu), sv = sqrtf(nv);
-      const float iu = ku ? 1.0f / su : 0.f, iv = kv ? 1.0f / sv : 0.f;
-#pragma unroll
-      for (int t = 0; t < NS; ++t) {
-        u[j][t] *= iu;
-        v[j][t] *= iv;
-      }
-      if (lane < kMaxM) {  // R column j: lane i writes row i
-        float xu = 0.f, xv = 0.f;
-#pragma unroll
-        for (int i = 0; i < kMaxM; ++i) {
-          if (i == lane && i < j) {
-            xu = ru[i];
-            xv = rv[i];
-          }
-        }
-        if (lane == j) {
-          xu = ku ? su : 0.f;
-          xv = kv ? sv : 0.f;
-        }
-        Ru[j * 16 + lane] = xu;
-        Rv[j * 16 + lane] = xv;
-      }
-    } else {
-#pragma unroll
-      for (int t = 0; t < NS; ++t) u[j][t] = v[j][t] = 0.f;
-      if (lane < kMaxM) Ru[j * 16 + lane] = Rv[j * 16 + lane] = 0.f;
-    }
-  }
-}
-
-// One-sided Jacobi on the 16 x 16 column-major C (columns >= m are zero),
-// accumulating the rotations into Vh.  Returns the number of sweeps run.
-// Pairs follow the round-robin (circle) order on M = m rounded up to even:
-// in round k, pair 0 is (k, M-1) and pair p > 0 is ((k+p) mod (M-1),
-// (k-p) mod (M-1)); both indices advance by one (mod M-1) from a round to
-// the next, so they are carried in registers instead of recomputed.  The
-// rotation zeroes the pair's inner product: zeta = (|y|^2 - |x|^2) / (2 x.y),
-// t = sign(zeta) / (|zeta| + sqrt(1 + zeta^2)), c = 1 / sqrt(1 + t^2), s = c t,
-// with the hardware reciprocal and reciprocal square root (about 1 ulp).
-__device__ int jacobi16(float *Cm, float *Vh, int m, int lane) {
-  const int M = (m + 1) & ~1;
-  if (M < 2) return 0;
-  const int np = M >> 1, rounds = M - 1;
-  const int p = lane >> 3, sub = lane & 7;
-  const bool act = p < np;
-  int sweep = 0;
-  while (sweep < kMaxSweeps) {
-    ++sweep;
-    bool any = false;
-    int ci = p == 0 ? 0 : p % (M - 1);
-    int cj = p == 0 ? M - 1 : (M - 1 - p) % (M - 1);
-    for (int k = 0; k < rounds; ++k) {
-      float x0 = 0.f, x1 = 0.f, y0 = 0.f, y1 = 0.f;
-      if (act) {
-        x0 = Cm[ci * 16 + sub];
-        x1 = Cm[ci * 16 + sub + 8];
-        y0 = Cm[cj * 16 + sub];
-        y1 = Cm[cj * 16 + sub + 8];
-      }
-      float aa = fmaf(x0, x0, x1 * x1), bb = fmaf(y0, y0, y1 * y1), gg = fmaf(x0, y0, x1 * y1);
-      aa = group_sum<8>(aa);
-      bb = group_sum<8>(bb);
-      gg = group_sum<8>(gg);
-      const bool rot = act && gg != 0.f && fabsf(gg) > kTolJ * __builtin_amdgcn_sqrtf(aa * bb);
-      if (rot) {
-        const float zeta = (bb - aa) * (0.5f * __builtin_amdgcn_rcpf(gg));
-        const float az = fabsf(zeta);
-        const float t = az > 1e10f ? 0.5f * __builtin_amdgcn_rcpf(zeta)
-                                   : copysignf(__builtin_amdgcn_rcpf(az + __builtin_amdgcn_sqrtf(fmaf(zeta, zeta, 1.f))), zeta);
-        const float c = __builtin_amdgcn_rsqf(fmaf(t, t, 1.f)), sn = c * t;
-        Cm[ci * 16 + sub] = c * x0 - sn * y0;
-        Cm[ci * 16 + sub + 8] = c * x1 - sn * y1;
-        Cm[cj * 16 + sub] = sn * x0 + c * y0;
-        Cm[cj * 16 + sub + 8] = sn * x1 + c * y1;
-        const float vx0 = Vh[ci * 16 + sub], vx1 = Vh[ci * 16 + sub + 8];
-        const float vy0 = Vh[cj * 16 + sub], vy1 = Vh[cj * 16 + sub + 8];
-        Vh[ci * 16 + sub] = c * vx0 - sn * vy0;
-        Vh[ci * 16 + sub + 8] = c * vx1 - sn * vy1;
-        Vh[cj * 16 + sub] = sn * vx0 + c * vy0;
-        Vh[cj * 16 + sub + 8] = sn * vx1 + c * vy1;
-      }
-      any = any || (__builtin_amdgcn_ballot_w64(rot) != 0ull);
-      wave_sync();
-      ci = (ci + 1 == M - 1) ? 0 : ci + 1;
-      if (p != 0) cj = (cj + 1 == M - 1) ? 0 : cj + 1;
-    }
-    if (!any) break;
-  }
-  return sweep;
-}
 
 // copy one component (u, v) with float4 lanes
 __device__ __forceinline__ void copy_comp(const float *su, const float *sv, float *du, float *dv_, int dk, int dv,
@@ -580,7 +431,16 @@ __global__ __launch_bounds__(256) void k_materialize(MaterializeArgs a) {
     if (slot < 0) continue;
     const int total = n1 + n2;
     float *H = a.dense + (int64_t)slot * dk * dv;
-    for (int r0 = 0; r0 < dv; r0 += RG * kMatRows) {
+    const int64_t di = a.dsrc_idx ? a.dsrc_idx[s] : -1;
+    if (di >= 0) {  // given dense: H = S^T
+      const float *S = a.dsrc + di * dk * dv;
+      if (act)
+        for (int j = g; j < dv; j += RG) {
+          const float *col = S + (int64_t)(4 * c) * dv + j;
+          st4(H + (int64_t)j * dk + 4 * c, make_float4(col[0], col[dv], col[2 * dv], col[3 * dv]));
+        }
+    }
+    for (int r0 = 0; r0 < (di >= 0 ? 0 : dv); r0 += RG * kMatRows) {
       float4 acc[kMatRows];
 #pragma unroll
       for (int jj = 0; jj < kMatRows; ++jj) acc[jj] = zero4();
@@ -648,7 +508,7 @@ __global__ __launch_bounds__(256) void k_scatter(ScatterArgs a) {
   const int64_t o0 = a.csr_off[s], o1 = a.csr_off[s + 1];
   const int R = (int)(o1 - o0);
   const uint32_t flags = a.rule[s] ? FLAG_DELTA : 0u;
-  if (a.force_dense || R > a.L) {
+  if (a.force_dense || R > a.L || (a.dense_mask && a.dense_mask[s])) {
     if (lane == 0) {
       const uint32_t idx =
           __hip_atomic_fetch_add(&a.counters[C_PROMOTE_COUNT], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

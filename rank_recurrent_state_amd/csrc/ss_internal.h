@@ -142,6 +142,8 @@ struct MaterializeArgs {
   const Meta *src_meta;        // where the components are (meta after compaction), or nullptr
   const int64_t *csr_off;      // alternative source: CSR offsets per state (init)
   const float *csr_u, *csr_v, *csr_s;
+  const int64_t *dsrc_idx;     // init: per state, index of its given dense S in dsrc, or -1
+  const float *dsrc;           // [.][d_k][d_v] row-major
   Arena act, frz;
   float *dense;
   DenseSlot *dslot;
@@ -156,6 +158,7 @@ struct ScatterArgs {
   const float *csr_u, *csr_v, *csr_s;
   const int64_t *dst_a, *dst_f;   // per state: first ring position of its active / frozen components
   const uint8_t *rule;
+  const uint8_t *dense_mask;     // states given dense (or nullptr)
   Meta *meta;
   Arena act, frz;
   int32_t *dense_list;           // states to materialize
@@ -192,6 +195,19 @@ hipError_t launch_repack(const RepackArgs &a, hipStream_t st);
 // *tmp_count must be 0 (a compaction's launch_ring_begin clears it).
 hipError_t launch_prune_factored(int32_t *list, uint32_t *count, int32_t *tmp, uint32_t *tmp_count, int64_t n_upper,
                                  const Meta *meta, uint32_t *host_count, hipStream_t st);
+
+// randomized block SVD initialization of n dense states (one workgroup each)
+struct RsvdArgs {
+  int64_t n;
+  int dk, dv, b, nb, iters, max_rank;
+  const float *S;      // [n][d_k][d_v]
+  const float *omega;  // [n][nb][d_k][b]
+  const float *eps;    // [n]
+  float *work;         // [n][d_k][d_v] residual
+  float *u, *v, *sigma;  // [n][max_rank][d_k], [n][max_rank][d_v], [n][max_rank]
+  int32_t *rank;       // [n]
+};
+hipError_t launch_rsvd_init(const RsvdArgs &a, hipStream_t st);
 
 // how a state is decoded
 enum DecodeKind : int { KIND_FACTORED = 0, KIND_DENSE_BUFFERED = 1, KIND_DENSE_PLAIN = 2 };

@@ -471,6 +471,20 @@ ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipSt
   } else if (d->force_dense) {
     n_dense0 = N;
   }
+  // states given dense
+  const uint8_t *dmask = (init && init->dense_mask) ? init->dense_mask : nullptr;
+  int64_t n_given = 0;
+  if (dmask) {
+    for (int64_t s = 0; s < N; ++s) {
+      if (!dmask[s]) continue;
+      if (off && off[s + 1] != off[s]) return fail(SS_ERR_ARG, "a state given dense must have no components");
+      ++n_given;
+      if (!d->force_dense) ++n_dense0;  // (force_dense already counts every state)
+    }
+    if (n_given > 0 && !init->dense) return fail(SS_ERR_ARG, "dense is required when dense_mask marks states");
+    if (!off && !d->force_dense) n_dense0 = n_given;
+  }
+  auto given = [&](int64_t s) { return dmask && dmask[s]; };
   const int64_t cap_d = d->force_dense ? N : (d->dense_capacity ? d->dense_capacity : N);
   if (n_dense0 > cap_d) return fail(SS_ERR_CAPACITY, "more initial dense states than dense_capacity");
   const bool factored = !d->force_dense;
@@ -504,7 +518,7 @@ ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipSt
     std::vector<int32_t> cnt[2] = {std::vector<int32_t>(N, -1), std::vector<int32_t>(N, -1)};
     for (int64_t s = 0; s < N; ++s) {
       const int64_t R = offp[s + 1] - offp[s];
-      if (R > L) continue;
+      if (R > L || given(s)) continue;
       cnt[0][s] = (int32_t)std::min<int64_t>(R, r);
       cnt[1][s] = (int32_t)(R - cnt[0][s]);
     }
@@ -585,6 +599,20 @@ ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipSt
   talloc((void **)&d_v, total * dv * sizeof(float));
   talloc((void **)&d_s, total * sizeof(float));
   talloc((void **)&d_dlist, N * sizeof(int32_t));
+  uint8_t *d_mask = nullptr;
+  int64_t *d_didx = nullptr;
+  float *d_dsrc = nullptr;
+  std::vector<int64_t> didx;
+  std::vector<float> dense_pack;
+  if (n_given > 0) {
+    talloc((void **)&d_mask, N);
+    talloc((void **)&d_didx, N * sizeof(int64_t));
+    talloc((void **)&d_dsrc, (size_t)n_given * dk * dv * sizeof(float));
+    didx.assign(N, -1);
+    int64_t k = 0;
+    for (int64_t s = 0; s < N; ++s)
+      if (dmask[s]) didx[s] = k++;
+  }
   if (factored)
     for (int R = 0; R < 2; ++R) talloc((void **)&d_pos[R], N * sizeof(int64_t));
   talloc((void **)&d_rule, N);
@@ -607,6 +635,19 @@ ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipSt
     up(p->seg, seg.data(), seg.size() * sizeof(unsigned long long));
   }
   up(d_rule, rulev.data(), N);
+  if (n_given > 0) {
+    up(d_mask, dmask, N);
+    up(d_didx, didx.data(), N * sizeof(int64_t));
+    const size_t per = (size_t)dk * dv;
+    if (n_given == N) {
+      up(d_dsrc, init->dense, sizeof(float) * per * N);
+    } else {  // the given states' S, packed in state order (the upload is synchronized below)
+      dense_pack.resize(per * n_given);
+      for (int64_t s = 0; s < N; ++s)
+        if (dmask[s]) std::memcpy(dense_pack.data() + (size_t)didx[s] * per, init->dense + (size_t)s * per, sizeof(float) * per);
+      up(d_dsrc, dense_pack.data(), sizeof(float) * dense_pack.size());
+    }
+  }
   up(p->members, members.data(), N * sizeof(int32_t));
   up(p->eps, epsv.data(), N * sizeof(float));
   if (e == hipSuccess) e = hipMemsetAsync(p->counters, 0, ss::C_N * sizeof(uint32_t), stream);
@@ -615,7 +656,7 @@ ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipSt
   if (factored) {
     fact.reserve(N);
     for (int64_t s2 = 0; s2 < N; ++s2)
-      if (offp[s2 + 1] - offp[s2] <= L) fact.push_back((int32_t)s2);
+      if (offp[s2 + 1] - offp[s2] <= L && !given(s2)) fact.push_back((int32_t)s2);
     p->fact_count_host = (uint32_t)fact.size();
     up(p->fact_ids[0], fact.data(), fact.size() * sizeof(int32_t));
     up(p->counters + ss::C_FACT0, &p->fact_count_host, sizeof(uint32_t));
@@ -624,7 +665,7 @@ ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipSt
     ss::ScatterArgs sa{};
     sa.N = N; sa.dk = dk; sa.dv = dv; sa.r = r; sa.L = L; sa.fcap = fcap; sa.force_dense = p->force_dense;
     sa.csr_off = d_off; sa.csr_u = d_u; sa.csr_v = d_v; sa.csr_s = d_s;
-    sa.dst_a = d_pos[0]; sa.dst_f = d_pos[1]; sa.rule = d_rule;
+    sa.dst_a = d_pos[0]; sa.dst_f = d_pos[1]; sa.rule = d_rule; sa.dense_mask = d_mask;
     sa.meta = p->meta; sa.act = p->act; sa.frz = p->frz; sa.dense_list = d_dlist; sa.counters = p->counters;
     e = ss::launch_scatter(sa, stream);
   }
@@ -632,6 +673,7 @@ ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipSt
     ss::MaterializeArgs ma{};
     ma.dk = dk; ma.dv = dv; ma.cap_d = (int)cap_d; ma.list = d_dlist; ma.count = p->counters + ss::C_PROMOTE_COUNT;
     ma.meta = p->meta; ma.csr_off = d_off; ma.csr_u = d_u; ma.csr_v = d_v; ma.csr_s = d_s;
+    ma.dsrc_idx = d_didx; ma.dsrc = d_dsrc;
     ma.act = p->act; ma.frz = p->frz; ma.dense = p->dense; ma.dslot = p->dslot; ma.counters = p->counters;
     ma.hflag = p->hflags_dev + HF_DENSE_CAP;
     e = ss::launch_materialize(ma, n_dense0, stream);
@@ -807,6 +849,27 @@ ss_status ss_compact(ss_pool *p, int32_t group, hipStream_t stream) {
   }
   p->compact_calls++;
   return SS_OK;
+}
+
+ss_status ss_rsvd_init(const float *S, int64_t n, int32_t d_k, int32_t d_v, int32_t block, int32_t n_blocks,
+                       int32_t iters, const float *omega, const float *eps, int32_t max_rank, float *work, float *u,
+                       float *v, float *sigma, int32_t *rank, hipStream_t stream) {
+  if (n < 0) return fail(SS_ERR_ARG, "n must be >= 0");
+  if (d_k < 4 || d_v < 4 || d_k > 256 || d_v > 256 || (d_k & 3) || (d_v & 3))
+    return fail(SS_ERR_SHAPE, "d_k and d_v must be multiples of 4 in [4, 256]");
+  if (block < 1 || block > ss::kMaxM || block > d_k || block > d_v)
+    return fail(SS_ERR_SHAPE, "block must be in [1, min(16, d_k, d_v)]");
+  if (n_blocks < 1 || iters < 1 || iters > 64) return fail(SS_ERR_ARG, "n_blocks >= 1 and iters in [1, 64] required");
+  if (max_rank < 1 || max_rank > std::min(d_k, d_v) || (int64_t)max_rank > (int64_t)n_blocks * block)
+    return fail(SS_ERR_ARG, "max_rank must be in [1, min(d_k, d_v, n_blocks * block)]");
+  if (n == 0) return SS_OK;
+  if (!S || !omega || !eps || !work || !u || !v || !sigma || !rank) return fail(SS_ERR_ARG, "null pointer");
+  if (n > (int64_t)INT32_MAX) return fail(SS_ERR_ARG, "too many states for one launch");
+  ss::RsvdArgs a{};
+  a.n = n; a.dk = d_k; a.dv = d_v; a.b = block; a.nb = n_blocks; a.iters = iters; a.max_rank = max_rank;
+  a.S = S; a.omega = omega; a.eps = eps; a.work = work; a.u = u; a.v = v; a.sigma = sigma; a.rank = rank;
+  const hipError_t e = ss::launch_rsvd_init(a, stream);
+  return e == hipSuccess ? SS_OK : hip_fail(e, "randomized SVD launch");
 }
 
 ss_status ss_schedule_due(const ss_pool *p, int64_t step, int32_t *out, int32_t cap, int32_t *n_due) {

@@ -40,7 +40,8 @@ class PoolDesc(ctypes.Structure):
 
 
 class Init(ctypes.Structure):
-    _fields_ = [("comp_off", _c_i64p), ("u", _c_f32p), ("v", _c_f32p), ("sigma", _c_f32p)]
+    _fields_ = [("comp_off", _c_i64p), ("u", _c_f32p), ("v", _c_f32p), ("sigma", _c_f32p),
+                ("dense_mask", _c_u8p), ("dense", _c_f32p)]
 
 
 class Stats(ctypes.Structure):
@@ -93,6 +94,9 @@ def load_library():
     lib.ss_step_graph_create.argtypes = [vp] + [vp] * 6 + [ctypes.POINTER(vp)]
     lib.ss_step_graph_launch.argtypes = [vp, ctypes.c_int64, vp]
     lib.ss_step_graph_destroy.argtypes = [vp]
+    lib.ss_rsvd_init.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                 ctypes.c_int32, vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp]
+    lib.ss_rsvd_init.restype = ctypes.c_int
     lib.ss_status_string.argtypes = [ctypes.c_int]
     lib.ss_status_string.restype = ctypes.c_char_p
     lib.ss_last_error.restype = ctypes.c_char_p
@@ -173,7 +177,7 @@ class StatePool:
 def state_pool_create(n_states, d_k, d_v, pad_slots=8, r_active=8, dense_rank_limit=-1, promote_on_compact=True,
                       max_frozen=0, force_dense=False, group_of_state=None, group_offset=None, rule=None, eps=None,
                       eps_default=0.0, dense_capacity=0, comp_off=None, u=None, v=None, sigma=None,
-                      arena_components=0, stream=None) -> StatePool:
+                      arena_components=0, dense_mask=None, dense=None, stream=None) -> StatePool:
     lib = load_library()
     n_groups = 1 if group_offset is None else len(group_offset)
     keep = []
@@ -187,13 +191,15 @@ def state_pool_create(n_states, d_k, d_v, pad_slots=8, r_active=8, dense_rank_li
                     g_p, o_p, r_p, e_p, float(eps_default), int(dense_capacity),
                     int(arena_components))
     init = None
-    if comp_off is not None:
+    if comp_off is not None or dense_mask is not None:
         c_a, c_p = _arr(comp_off, np.int64, _c_i64p)
         u_a, u_p = _arr(u, np.float32, _c_f32p)
         v_a, v_p = _arr(v, np.float32, _c_f32p)
         s_a, s_p = _arr(sigma, np.float32, _c_f32p)
-        keep += [c_a, u_a, v_a, s_a]
-        init = Init(c_p, u_p, v_p, s_p)
+        m_a, m_p = _arr(dense_mask, np.uint8, _c_u8p)
+        d_a, d_p = _arr(dense, np.float32, _c_f32p)
+        keep += [c_a, u_a, v_a, s_a, m_a, d_a]
+        init = Init(c_p, u_p, v_p, s_p, m_p, d_p)
     handle = ctypes.c_void_p()
     st = lib.ss_state_pool_create(ctypes.byref(desc), ctypes.byref(init) if init is not None else None,
                                   _stream(stream) if torch.cuda.is_available() else None, ctypes.byref(handle))
@@ -236,6 +242,65 @@ class StepGraph:
             self.close()
         except Exception:
             pass
+
+
+def rsvd_init(S, omega, eps, iters=2, max_rank=None, stream=None):
+    """Randomized block SVD of dense states on the GPU.  S: (n, d_k, d_v) float32 CUDA tensor;
+    omega: (n, n_blocks, d_k, block) Gaussian; eps: (n,).  Returns u (n, max_rank, d_k),
+    v (n, max_rank, d_v), sigma (n, max_rank) and rank (n,) as CUDA tensors (entries beyond a
+    state's rank are unspecified)."""
+    n, dk, dv = S.shape
+    n2, nb, dk2, b = omega.shape
+    if n2 != n or dk2 != dk:
+        raise ValueError("omega must be (n, n_blocks, d_k, block)")
+    max_rank = min(dk, dv, nb * b) if max_rank is None else int(max_rank)
+    dev = S.device
+    work = torch.empty_like(S)
+    u = torch.empty(n, max_rank, dk, device=dev)
+    v = torch.empty(n, max_rank, dv, device=dev)
+    sigma = torch.empty(n, max_rank, device=dev)
+    rank = torch.empty(n, dtype=torch.int32, device=dev)
+    eps_t = torch.as_tensor(eps, dtype=torch.float32, device=dev).expand(n).contiguous()
+    p = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    for t, name in ((S, "S"), (omega, "omega")):
+        if not (t.is_cuda and t.dtype == torch.float32 and t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous float32 CUDA tensor")
+    _check(load_library().ss_rsvd_init(p(S), n, dk, dv, b, nb, int(iters), p(omega), p(eps_t), max_rank, p(work),
+                                       p(u), p(v), p(sigma), p(rank), _stream(stream)))
+    return u, v, sigma, rank
+
+
+def state_pool_from_dense(S, omega, eps, d_k=None, d_v=None, pad_slots=8, r_active=8, iters=2, rule=None,
+                          **create_kw) -> StatePool:
+    """A pool initialized from dense states after prefill: randomized block SVD of each state on
+    the GPU (rsvd_init), then the dense fallback for states whose rank exceeds L, which are kept
+    as their exact S.  S: (N, d_k, d_v) float32 (host array or CUDA tensor); omega: (N, n_blocks,
+    d_k, block) Gaussian; eps: scalar or (N,).  create_kw go to state_pool_create."""
+    St = torch.as_tensor(S, dtype=torch.float32).cuda().contiguous()
+    Om = torch.as_tensor(omega, dtype=torch.float32).cuda().contiguous()
+    N, dk, dv = St.shape
+    L = create_kw.get("dense_rank_limit", -1)
+    L = dense_rank_limit(dk, dv) if L is None or L < 0 else L
+    nb, b = Om.shape[1], Om.shape[3]
+    max_rank = min(dk, dv, nb * b)
+    eps_a = np.broadcast_to(np.asarray(eps, dtype=np.float32), (N,)).copy()
+    u, v, sg, rk = rsvd_init(St, Om, torch.from_numpy(eps_a).cuda(), iters=iters, max_rank=max_rank)
+    rk = rk.cpu().numpy().astype(np.int64)
+    dense_mask = (rk > L).astype(np.uint8)
+    R = np.where(dense_mask == 1, 0, rk)
+    comp_off = np.concatenate([[0], np.cumsum(R)]).astype(np.int64)
+    # components in descending sigma per state (blocks are each descending, not across blocks)
+    sgh = sg.cpu().numpy()
+    sel = np.concatenate([i * max_rank + np.argsort(-sgh[i, :r], kind="stable") for i, r in enumerate(R)]) \
+        .astype(np.int64) if R.sum() else np.zeros(0, dtype=np.int64)
+    idx = torch.from_numpy(sel).cuda()
+    uu = u.reshape(N * max_rank, dk).index_select(0, idx).cpu().numpy()
+    vv = v.reshape(N * max_rank, dv).index_select(0, idx).cpu().numpy()
+    ss_ = sg.reshape(N * max_rank).index_select(0, idx).cpu().numpy()
+    dense_host = St.cpu().numpy() if dense_mask.any() else None
+    return state_pool_create(N, dk, dv, pad_slots, r_active, rule=rule, eps=eps_a, comp_off=comp_off, u=uu, v=vv,
+                             sigma=ss_, dense_mask=dense_mask if dense_mask.any() else None, dense=dense_host,
+                             **create_kw)
 
 
 def readout(pool: StatePool, q, o, stream=None):
