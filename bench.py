@@ -241,8 +241,9 @@ def main():
     # warmup on a scratch pool of the same workload
     if args.warmup > 0:
         pool = _pool(ss, w, init)
-        for c0 in range(0, args.warmup, args.chunk):
-            xs = [gen.generate(t) for t in range(c0 + 1, min(args.warmup, c0 + args.chunk) + 1)]
+        wchunk = max(1, min(args.chunk, int(16e9 // (w.n_states * (2 * w.d_k + w.d_v + 2) * 4))))
+        for c0 in range(0, args.warmup, wchunk):
+            xs = [gen.generate(t) for t in range(c0 + 1, min(args.warmup, c0 + wchunk) + 1)]
             _run_steps(ss, torch, pool, xs, c0, o)
         torch.cuda.synchronize()
         pool.close()
@@ -256,8 +257,10 @@ def main():
     step_ms = []
     hist_marks = {}
     t = 0
+    # inputs of a chunk are generated at once: keep them within about 16 GB
+    chunk = max(1, min(args.chunk, int(16e9 // (w.n_states * (2 * w.d_k + w.d_v + 2) * 4))))
     while t < K_steps:
-        n = min(args.chunk, K_steps - t)
+        n = min(chunk, K_steps - t)
         xs = [gen.generate(s) for s in range(t + 1, t + n + 1)]
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
         torch.cuda.synchronize()
@@ -308,6 +311,7 @@ def main():
     # dense HIP baseline on the same inputs
     dense = None
     if args.dense_steps > 0:
+        args.dense_steps = min(args.dense_steps, chunk)  # its inputs are generated at once too
         dp = _pool(ss, w, init, force_dense=True)
         xs = [gen.generate(s) for s in range(1, args.dense_steps + 1)]
         ss.pool_timing(dp, True)

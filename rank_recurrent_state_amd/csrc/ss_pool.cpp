@@ -348,8 +348,9 @@ ss_status ensure_ring_space(ss_pool *p, const int *gs, int ng, hipStream_t strea
   if (!repack) return SS_OK;
   int64_t newcap[2];
   for (int R = 0; R < 2; ++R) {
+    // grow to 1.5x what the live components and this step need, when they pass 2/3 of the ring
     const int64_t want = live[R] + need[R], cap = p->arena(R).cap;
-    newcap[R] = 2 * want > cap ? std::max<int64_t>(cap, 2 * want) : cap;
+    newcap[R] = 3 * want > 2 * cap ? std::max<int64_t>(cap, want + want / 2) : cap;
     if (newcap[R] >= (int64_t)INT32_MAX) return fail(SS_ERR_CAPACITY, "a component ring would exceed 2^31 slots");
   }
   const ss_status st = ring_repack(p, gs[0], newcap, stream);
