@@ -80,8 +80,10 @@ typedef struct {
   float eps_default;
   int64_t dense_capacity;     /* dense slots; 0 = N */
   int64_t arena_components;   /* initial capacity (components) of each component ring, at least
-                                 what the initial data needs; 0 = automatic.  The rings grow on
-                                 their own (see ss_compact). */
+                                 what the initial data needs; 0 = automatic: the most the pool
+                                 can ever need when that fits in a quarter of the free device
+                                 memory, else a smaller start.  The rings grow on their own (see
+                                 ss_compact); a growth is a device allocation. */
 } ss_pool_desc;
 
 /* Initial states, host memory, copied during create.  Components of state s

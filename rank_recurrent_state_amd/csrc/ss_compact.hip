@@ -23,6 +23,8 @@
 //      for the dense region (SinkState 4.4).
 // No global-memory intermediates: QR factors live in registers, the small
 // matrices in LDS (SinkState 4.4: fused chains of factor algebra).
+#include <hipcub/hipcub.hpp>
+
 #include "ss_internal.h"
 #include "ss_linalg.h"
 #include "ss_wave.h"
@@ -620,6 +622,65 @@ __global__ __launch_bounds__(256) void k_repack(RepackArgs a) {
   }
 }
 
+// layout index li -> (ord slot, member) -> state; its component counts (0 for dense states)
+__global__ __launch_bounds__(256) void k_layout_counts(LayoutArgs a) {
+  const int64_t li = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (li >= a.N) return;
+  int lo = 0, hi = a.G - 1;  // the ord slot k with lstart[k] <= li < lstart[k + 1]
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.lstart[mid] <= li) lo = mid;
+    else hi = mid - 1;
+  }
+  const int g = a.ord[lo];
+  const int32_t s = a.members[a.gstart[g] + (li - a.lstart[lo])];
+  const uint32_t pk = a.meta[s].packed;
+  const bool dense = meta_flags(pk) & FLAG_DENSE;
+  a.cnt_a[li] = dense ? 0 : (int64_t)meta_ra(pk);
+  a.cnt_f[li] = dense ? 0 : (int64_t)meta_rf(pk);
+}
+
+__global__ __launch_bounds__(256) void k_layout_scatter(LayoutArgs a) {
+  const int64_t li = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (li >= a.N) return;
+  int lo = 0, hi = a.G - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.lstart[mid] <= li) lo = mid;
+    else hi = mid - 1;
+  }
+  const int g = a.ord[lo];
+  const int32_t s = a.members[a.gstart[g] + (li - a.lstart[lo])];
+  const bool dense = meta_flags(a.meta[s].packed) & FLAG_DENSE;
+  a.new_a[s] = dense ? -1 : a.off_a[li];
+  a.new_f[s] = dense ? -1 : a.off_f[li];
+}
+
+// group segments and ring heads from the scans (one thread per ord slot)
+__global__ void k_layout_segs(LayoutArgs a) {
+  const int k = blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n = a.N;
+  const unsigned long long tot_a = n ? (unsigned long long)(a.off_a[n - 1] + a.cnt_a[n - 1]) : 0ull;
+  const unsigned long long tot_f = n ? (unsigned long long)(a.off_f[n - 1] + a.cnt_f[n - 1]) : 0ull;
+  if (k < a.G) {
+    const int g = a.ord[k];
+    const int64_t b0 = a.lstart[k], b1 = a.lstart[k + 1];
+    const unsigned long long sa = b0 < n ? (unsigned long long)a.off_a[b0] : tot_a;
+    const unsigned long long sf = b0 < n ? (unsigned long long)a.off_f[b0] : tot_f;
+    const unsigned long long ea = b1 > b0 ? (unsigned long long)(a.off_a[b1 - 1] + a.cnt_a[b1 - 1]) : sa;
+    const unsigned long long ef = b1 > b0 ? (unsigned long long)(a.off_f[b1 - 1] + a.cnt_f[b1 - 1]) : sf;
+    a.seg[2 * g] = sa;
+    a.seg[2 * g + 1] = ea;
+    a.seg[2 * a.G + 2 * g] = sf;
+    a.seg[2 * a.G + 2 * g + 1] = ef;
+  }
+  if (k == 0) {
+    a.ring[0].head = a.ring[0].begin = tot_a;
+    a.ring[1].head = a.ring[1].begin = tot_f;
+    a.ring[0].overflow = a.ring[1].overflow = 0ull;
+  }
+}
+
 // list[i] = tmp[i] for i < *tmp_count; the length goes to *count and to a host-visible word
 __global__ __launch_bounds__(256) void k_copy_list(const int32_t *tmp, const uint32_t *tmp_count, int32_t *list,
                                                    uint32_t *count, uint32_t *host) {
@@ -682,6 +743,29 @@ hipError_t launch_ring_begin(Ring *ra, Ring *rf, const unsigned long long *seg_a
 hipError_t launch_ring_end(Ring *ra, Ring *rf, unsigned long long *seg_a, unsigned long long *seg_f, int g,
                            hipStream_t st) {
   hipLaunchKernelGGL(k_ring_end, dim3(1), dim3(64), 0, st, ra, rf, seg_a, seg_f, g);
+  return hipGetLastError();
+}
+
+size_t layout_scan_bytes(int64_t N) {
+  size_t bytes = 0;
+  if (hipcub::DeviceScan::ExclusiveSum(nullptr, bytes, (const int64_t *)nullptr, (int64_t *)nullptr, (int)N) !=
+      hipSuccess)
+    return 0;
+  return bytes;
+}
+
+hipError_t launch_ring_layout(const LayoutArgs &a, hipStream_t st) {
+  if (a.N <= 0 || a.G <= 0) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((a.N + 255) / 256)), block(256);
+  hipLaunchKernelGGL(k_layout_counts, grid, block, 0, st, a);
+  hipError_t e = hipGetLastError();
+  size_t bytes = a.scan_bytes;
+  if (e == hipSuccess) e = hipcub::DeviceScan::ExclusiveSum(a.scan_tmp, bytes, a.cnt_a, a.off_a, (int)a.N, st);
+  bytes = a.scan_bytes;
+  if (e == hipSuccess) e = hipcub::DeviceScan::ExclusiveSum(a.scan_tmp, bytes, a.cnt_f, a.off_f, (int)a.N, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_layout_scatter, grid, block, 0, st, a);
+  hipLaunchKernelGGL(k_layout_segs, dim3((unsigned)((a.G + 63) / 64)), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 

@@ -190,6 +190,25 @@ struct RepackArgs {
   const int64_t *new_a, *new_f;  // per state: new first position (physical) or -1 for dense states
 };
 hipError_t launch_repack(const RepackArgs &a, hipStream_t st);
+// Exact ring layout of every factored state on the device: groups in the order `ord` (device
+// [G]: group id; gstart/gsize: device [G] of the groups' member ranges in `members`), each
+// group's members in member order, counts from the records; writes new_a/new_f per state (-1 for
+// dense states), seg [2][2G] and the rings' head = begin = total.  scratch: see layout_scratch_bytes.
+struct LayoutArgs {
+  int64_t N;
+  int G;
+  const int32_t *members, *ord;
+  const int64_t *gstart, *gsize, *lstart;  // lstart [G + 1]: layout index where ord slot k starts
+  const Meta *meta;
+  int64_t *cnt_a, *cnt_f, *off_a, *off_f;  // [N] each
+  int64_t *new_a, *new_f;                  // [N]
+  unsigned long long *seg;
+  Ring *ring;
+  void *scan_tmp;
+  size_t scan_bytes;
+};
+size_t layout_scan_bytes(int64_t N);
+hipError_t launch_ring_layout(const LayoutArgs &a, hipStream_t st);
 // drop the states that have become dense from the factored-state list: list -> tmp, then back into
 // list, so the decode always reads the same list; the new length goes to *count and a host-visible word.
 // *tmp_count must be 0 (a compaction's launch_ring_begin clears it).

@@ -67,6 +67,12 @@ struct ss_pool {
   int64_t seq = 0;
   int64_t repacks = 0, ring_syncs = 0;
   int64_t layout_version = 0;          // bumped whenever device addresses captured in graphs change
+  // device scratch of a re-pack's layout (allocated at the first re-pack)
+  int64_t *lay_cnt = nullptr;          // [6][N]: counts, offsets, new positions (active, frozen)
+  int64_t *lay_g = nullptr;            // [3G + 1]: group starts, sizes, layout starts
+  int32_t *lay_ord = nullptr;          // [G]
+  unsigned char *lay_scan = nullptr;
+  size_t lay_scan_bytes = 0;
   float *pk = nullptr, *pw = nullptr, *pc = nullptr;
   float *dense = nullptr;
   ss::DenseSlot *dslot = nullptr;
@@ -252,42 +258,52 @@ int64_t ring_usage_bound(ss_pool *p, int R) {
 // Re-pack every factored state's components, exactly, into rings of capacity newcap (after a
 // synchronization), with group `first` at the tail.
 ss_status ring_repack(ss_pool *p, int first, const int64_t (&newcap)[2], hipStream_t stream) {
-  std::vector<ss::Meta> meta(p->N);
-  hipError_t e = hipMemcpy(meta.data(), p->meta, sizeof(ss::Meta) * p->N, hipMemcpyDeviceToHost);
-  if (e != hipSuccess) return hip_fail(e, "repack meta");
-  std::vector<int32_t> cnt[2] = {std::vector<int32_t>(p->N, -1), std::vector<int32_t>(p->N, -1)};
-  for (int64_t s = 0; s < p->N; ++s) {
-    const uint32_t pk = meta[s].packed;
-    if (ss::meta_flags(pk) & ss::FLAG_DENSE) continue;
-    cnt[0][s] = (int32_t)ss::meta_ra(pk);
-    cnt[1][s] = (int32_t)ss::meta_rf(pk);
+  hipError_t e = hipSuccess;
+  const int64_t N = p->N;
+  const int G = p->G;
+  if (!p->lay_cnt) {  // device scratch of the layout, kept for later re-packs
+    auto chk = [&](hipError_t x) { if (e == hipSuccess) e = x; };
+    chk(dalloc(p, &p->lay_cnt, 6 * (size_t)N));
+    chk(dalloc(p, &p->lay_g, 3 * (size_t)G + 1));
+    chk(dalloc(p, &p->lay_ord, (size_t)G));
+    p->lay_scan_bytes = ss::layout_scan_bytes(N);
+    chk(dalloc(p, &p->lay_scan, p->lay_scan_bytes + 1));
+    std::vector<int64_t> gs(2 * (size_t)G);
+    for (int g = 0; g < G; ++g) {
+      gs[g] = p->group_start[g];
+      gs[G + g] = p->group_size[g];
+    }
+    if (e == hipSuccess) e = hipMemcpy(p->lay_g, gs.data(), sizeof(int64_t) * gs.size(), hipMemcpyHostToDevice);
+    if (e != hipSuccess) return e == hipErrorOutOfMemory ? fail(SS_ERR_OOM, "ring re-pack scratch") : hip_fail(e, "ring re-pack");
   }
-  std::vector<int64_t> pos[2];
-  std::vector<unsigned long long> seg;
-  int64_t tot[2];
-  ring_layout(p, ring_order(p, first), cnt, pos, seg, tot);
+  const std::vector<int> ord = ring_order(p, first);
+  std::vector<int64_t> lstart(G + 1, 0);
+  for (int k = 0; k < G; ++k) lstart[k + 1] = lstart[k] + p->group_size[ord[k]];
+  e = hipMemcpyAsync(p->lay_ord, ord.data(), sizeof(int32_t) * G, hipMemcpyHostToDevice, stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(p->lay_g + 2 * G, lstart.data(), sizeof(int64_t) * (G + 1), hipMemcpyHostToDevice, stream);
   void *blk[2] = {nullptr, nullptr};
   size_t bytes[2] = {0, 0};
   ss::Arena na[2];
-  int64_t *d_pos[2] = {nullptr, nullptr};
   for (int R = 0; R < 2 && e == hipSuccess; ++R) e = ring_alloc(p, newcap[R], &blk[R], &bytes[R], &na[R]);
-  for (int R = 0; R < 2 && e == hipSuccess; ++R) e = hipMalloc(&d_pos[R], sizeof(int64_t) * p->N);
-  for (int R = 0; R < 2 && e == hipSuccess; ++R)
-    e = hipMemcpy(d_pos[R], pos[R].data(), sizeof(int64_t) * p->N, hipMemcpyHostToDevice);
+  ss::LayoutArgs la{};
+  la.N = N; la.G = G; la.members = p->members; la.ord = p->lay_ord;
+  la.gstart = p->lay_g; la.gsize = p->lay_g + G; la.lstart = p->lay_g + 2 * G; la.meta = p->meta;
+  la.cnt_a = p->lay_cnt; la.cnt_f = p->lay_cnt + N; la.off_a = p->lay_cnt + 2 * N; la.off_f = p->lay_cnt + 3 * N;
+  la.new_a = p->lay_cnt + 4 * N; la.new_f = p->lay_cnt + 5 * N;
+  la.seg = p->seg; la.ring = p->ring; la.scan_tmp = p->lay_scan; la.scan_bytes = p->lay_scan_bytes;
+  if (e == hipSuccess) e = ss::launch_ring_layout(la, stream);
   if (e == hipSuccess) {
     ss::RepackArgs ra{};
-    ra.N = p->N; ra.dk = p->dk; ra.dv = p->dv; ra.meta = p->meta;
-    ra.src_a = p->act; ra.src_f = p->frz; ra.dst_a = na[0]; ra.dst_f = na[1]; ra.new_a = d_pos[0]; ra.new_f = d_pos[1];
+    ra.N = N; ra.dk = p->dk; ra.dv = p->dv; ra.meta = p->meta;
+    ra.src_a = p->act; ra.src_f = p->frz; ra.dst_a = na[0]; ra.dst_f = na[1]; ra.new_a = la.new_a; ra.new_f = la.new_f;
     e = ss::launch_repack(ra, stream);
   }
-  ss::Ring ring[2] = {};
-  for (int R = 0; R < 2; ++R) ring[R].head = ring[R].begin = (unsigned long long)tot[R];
-  if (e == hipSuccess) e = hipMemcpyAsync(p->ring, ring, sizeof(ring), hipMemcpyHostToDevice, stream);
-  if (e == hipSuccess) e = hipMemcpyAsync(p->seg, seg.data(), sizeof(unsigned long long) * seg.size(),
-                                          hipMemcpyHostToDevice, stream);
+  std::vector<unsigned long long> seg(4 * (size_t)G);
+  ss::Ring ring[2];
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
-  for (int R = 0; R < 2; ++R)
-    if (d_pos[R]) (void)hipFree(d_pos[R]);
+  if (e == hipSuccess) e = hipMemcpy(seg.data(), p->seg, sizeof(unsigned long long) * seg.size(), hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemcpy(ring, p->ring, sizeof(ring), hipMemcpyDeviceToHost);
   if (e != hipSuccess) {
     for (int R = 0; R < 2; ++R)
       if (blk[R]) (void)hipFree(blk[R]);
@@ -299,7 +315,7 @@ ss_status ring_repack(ss_pool *p, int first, const int64_t (&newcap)[2], hipStre
     p->ring_blk[R] = blk[R];
     p->ring_bytes[R] = bytes[R];
     p->arena(R) = na[R];
-    ring_records(p, R, seg.data() + (size_t)R * 2 * p->G, (unsigned long long)tot[R]);
+    ring_records(p, R, seg.data() + (size_t)R * 2 * G, ring[R].head);
   }
   p->repacks++;
   p->layout_version++;
@@ -348,9 +364,9 @@ ss_status ensure_ring_space(ss_pool *p, const int *gs, int ng, hipStream_t strea
   if (!repack) return SS_OK;
   int64_t newcap[2];
   for (int R = 0; R < 2; ++R) {
-    // grow to 1.5x what the live components and this step need, when they pass 2/3 of the ring
+    // grow to twice what the live components and this step need, when they pass half the ring
     const int64_t want = live[R] + need[R], cap = p->arena(R).cap;
-    newcap[R] = 3 * want > 2 * cap ? std::max<int64_t>(cap, want + want / 2) : cap;
+    newcap[R] = 2 * want > cap ? std::max<int64_t>(cap, 2 * want) : cap;
     if (newcap[R] >= (int64_t)INT32_MAX) return fail(SS_ERR_CAPACITY, "a component ring would exceed 2^31 slots");
   }
   const ss_status st = ring_repack(p, gs[0], newcap, stream);
@@ -524,13 +540,24 @@ ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipSt
       cnt[1][s] = (int32_t)(R - cnt[0][s]);
     }
     ring_layout(p, ring_order(p, -1), cnt, pos, seg, tot);
-    // automatic capacity: the active ring never needs more than r per factored state plus one
-    // group's worth; the frozen ring starts at twice its contents plus one group's growth
+    // Automatic capacity.  No ring ever needs more than (factored states + one group) times the
+    // per-state cap (r active; L + K - r, or max_frozen, frozen).  Growing a ring later costs a
+    // device allocation, and large ones are slow (tens of ms per GB here), so when that maximum
+    // fits in a quarter of the free device memory it is reserved at once; otherwise the active
+    // ring starts at its maximum and the frozen ring at twice its contents plus one group's
+    // growth, and they grow when needed.  Segments stay exactly packed either way.
     int64_t nf = 0, ngmax = 0;
     for (int g = 0; g < G; ++g) ngmax = std::max(ngmax, p->group_size[g]);
     for (int64_t s = 0; s < N; ++s) nf += cnt[0][s] >= 0 ? 1 : 0;
+    const int64_t comp_bytes = 4ll * (dk + dv + 1);
+    int64_t maxcap[2];
+    for (int R = 0; R < 2; ++R) maxcap[R] = (nf + ngmax) * (R == 0 ? (int64_t)r : (int64_t)fcap);
+    size_t free_b = 0, total_b = 0;
+    const bool roomy = hipMemGetInfo(&free_b, &total_b) == hipSuccess &&
+                       (maxcap[0] + maxcap[1]) * comp_bytes <= (int64_t)(free_b / 4) &&
+                       maxcap[1] < (int64_t)INT32_MAX;
     for (int R = 0; R < 2; ++R) {
-      const int64_t autocap = R == 0 ? (int64_t)r * (nf + ngmax) : 2 * (tot[1] + (int64_t)K * ngmax);
+      const int64_t autocap = R == 0 || roomy ? maxcap[R] : 2 * (tot[1] + (int64_t)K * ngmax);
       cap_ring[R] = std::max<int64_t>({1, tot[R], d->arena_components ? d->arena_components : autocap});
       if (cap_ring[R] >= (int64_t)INT32_MAX) return fail(SS_ERR_CAPACITY, "too many components for 32-bit offsets");
     }
