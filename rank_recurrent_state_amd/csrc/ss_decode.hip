@@ -31,7 +31,7 @@
 //   fold:  H_j <- alpha Gamma (H_j + sum_i c_i w_i,j k_i) + w_j k.
 // One wavefront per state streams batches of rows (P lanes per row, float4
 // per lane) and reduces each row inside its lane group; the pad's w rows and
-// its contribution vectors sit in LDS, the pad keys in registers.  The plain
+// its contribution vectors sit in LDS, and so do the pad keys.  The plain
 // kernel (the dense baseline: the recurrence the dense Mamba-2 / GDN kernels
 // run) reads and writes every row every step: H_j <- alpha H_j + w_j k.
 #include "ss_internal.h"
@@ -495,7 +495,10 @@ hipError_t decode_factored_p(const DecodeArgs &a, int P, hipStream_t st) {
     case 4: hipLaunchKernelGGL((k_decode_factored<4, 1, RO, AD>), grid, block, 0, st, a); break;
     case 8: hipLaunchKernelGGL((k_decode_factored<8, 2, RO, AD>), grid, block, 0, st, a); break;
     case 16: hipLaunchKernelGGL((k_decode_factored<16, 2, RO, AD>), grid, block, 0, st, a); break;
-    case 32: hipLaunchKernelGGL((k_decode_factored<32, 4, RO, AD>), grid, block, 0, st, a); break;
+#ifndef SS_FACT_UN32
+#define SS_FACT_UN32 4
+#endif
+    case 32: hipLaunchKernelGGL((k_decode_factored<32, SS_FACT_UN32, RO, AD>), grid, block, 0, st, a); break;
     case 64: hipLaunchKernelGGL((k_decode_factored<64, 8, RO, AD>), grid, block, 0, st, a); break;
     default: return hipErrorInvalidValue;
   }

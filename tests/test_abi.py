@@ -134,3 +134,41 @@ def test_decode_byte_formula(lib):
     # page-printed footprint: rank-8 factors + a full pad of one 80x128 state = 13,376 B
     g = json.load(open(os.path.join(GOLD, "memory_arithmetic.json")))
     assert 2 * 8 * 4 * (128 + 80 + 1) == g["total_bytes"]
+
+
+def test_rsvd_init_rejects_bad_arguments_without_touching_the_gpu(lib):
+    from rank_recurrent_state_amd import sinkstate as ss
+    vp = ctypes.c_void_p(1)  # never dereferenced: every case fails the host-side checks first
+    base = dict(n=4, d_k=16, d_v=16, block=4, n_blocks=2, iters=2, max_rank=8)
+    cases = [({"n": -1}, ss.SS_ERR_ARG), ({"d_k": 18}, ss.SS_ERR_SHAPE), ({"d_v": 260}, ss.SS_ERR_SHAPE),
+             ({"block": 0}, ss.SS_ERR_SHAPE), ({"block": 17}, ss.SS_ERR_SHAPE),
+             ({"block": 8, "d_k": 4}, ss.SS_ERR_SHAPE), ({"n_blocks": 0}, ss.SS_ERR_ARG),
+             ({"iters": 0}, ss.SS_ERR_ARG), ({"iters": 65}, ss.SS_ERR_ARG), ({"max_rank": 0}, ss.SS_ERR_ARG),
+             ({"max_rank": 9}, ss.SS_ERR_ARG), ({"max_rank": 17, "n_blocks": 8}, ss.SS_ERR_ARG)]
+    for over, expect in cases:
+        d = dict(base, **over)
+        st = lib.ss_rsvd_init(vp, d["n"], d["d_k"], d["d_v"], d["block"], d["n_blocks"], d["iters"], vp, vp,
+                              d["max_rank"], vp, vp, vp, vp, vp, None)
+        assert st == expect, (over, st, lib.ss_last_error())
+    d = base
+    assert lib.ss_rsvd_init(None, 4, 16, 16, 4, 2, 2, None, None, 8, None, None, None, None, None, None) == ss.SS_ERR_ARG
+    assert lib.ss_rsvd_init(None, 0, 16, 16, 4, 2, 2, None, None, 8, None, None, None, None, None, None) == ss.SS_OK
+
+
+def test_create_rejects_bad_dense_given_states(lib):
+    import numpy as np
+    from rank_recurrent_state_amd import sinkstate as ss
+    out = ctypes.c_void_p()
+    desc = ss.PoolDesc(4, 16, 16, 8, 8, -1, 1, 0, 0, 1, None, None, None, None, 1e-3, 0, 0)
+    off = np.array([0, 2, 2, 2, 2], np.int64)
+    u = np.zeros((2, 16), np.float32)
+    sig = np.array([1.0, 0.5], np.float32)
+    mask = np.array([1, 0, 0, 0], np.uint8)  # state 0 has components: rejected
+    S = np.zeros((4, 16, 16), np.float32)
+    init = ss.Init(off.ctypes.data_as(ss._c_i64p), u.ctypes.data_as(ss._c_f32p), u.ctypes.data_as(ss._c_f32p),
+                   sig.ctypes.data_as(ss._c_f32p), mask.ctypes.data_as(ss._c_u8p), S.ctypes.data_as(ss._c_f32p))
+    assert lib.ss_state_pool_create(ctypes.byref(desc), ctypes.byref(init), None, ctypes.byref(out)) == ss.SS_ERR_ARG
+    mask2 = np.array([0, 1, 0, 0], np.uint8)  # a masked state without `dense`: rejected
+    init2 = ss.Init(off.ctypes.data_as(ss._c_i64p), u.ctypes.data_as(ss._c_f32p), u.ctypes.data_as(ss._c_f32p),
+                    sig.ctypes.data_as(ss._c_f32p), mask2.ctypes.data_as(ss._c_u8p), None)
+    assert lib.ss_state_pool_create(ctypes.byref(desc), ctypes.byref(init2), None, ctypes.byref(out)) == ss.SS_ERR_ARG
