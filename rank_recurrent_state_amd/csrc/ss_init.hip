@@ -13,11 +13,13 @@
 // block is taken; otherwise the block is subtracted from the residual
 // (S <- S - X diag(sigma) (Q W)^T) and the next block starts from it.
 //
-// One 256-thread workgroup per state.  The residual lives in a caller-given
-// workspace; the products S^T Omega and S Q and the subtraction use all
-// threads, with Omega and Q in LDS; orth is the CGS2 thin QR and the block
-// SVD is the thin QR of Omega followed by one-sided Jacobi on its R, both on
-// wavefront 0.
+// One 256-thread workgroup per state.  The residual lives in LDS when it fits
+// (rows padded by one float, so that both row and column walks are free of
+// bank conflicts), else in a caller-given workspace.  The products S^T Omega
+// and S Q and the subtraction use all threads (a thread owns one row of the
+// product and four of its block columns), with Omega and
+// Q in LDS; orth is the CGS2 thin QR and the block SVD is the thin QR of
+// Omega followed by one-sided Jacobi on its R, both on wavefront 0.
 #include "ss_internal.h"
 #include "ss_linalg.h"
 #include "ss_wave.h"
@@ -28,8 +30,9 @@ namespace {
 
 constexpr int kDMax = 256;
 
-template <int NSK, int NSV>
+template <int NSK, int NSV, bool LDSS>
 __global__ __launch_bounds__(256) void k_rsvd(RsvdArgs a) {
+  extern __shared__ float smem[];  // the residual, [d_k][d_v + 1], when LDSS
   __shared__ float Om[kMaxM][kDMax];  // Omega, then X diag(sigma) for the subtraction (column c at Om[c])
   __shared__ float Qv[kMaxM][kDMax];  // Y, then Q, then Q W
   __shared__ float Rq[256], Cm[256], Vh[256];
@@ -40,8 +43,12 @@ __global__ __launch_bounds__(256) void k_rsvd(RsvdArgs a) {
   const int64_t s = blockIdx.x;
   const int dk = a.dk, dv = a.dv, b = a.b;
   const float *S = a.S + s * dk * dv;
-  float *Wr = a.work + s * dk * dv;  // the residual
-  for (int e = tid; e < dk * dv; e += 256) Wr[e] = S[e];
+  const int ld = LDSS ? dv + 1 : dv;                // row stride of the residual
+  float *Wr = LDSS ? smem : a.work + s * dk * dv;   // the residual
+  for (int e = tid; e < dk * dv; e += 256) {
+    const int i = e / dv, j = e - i * dv;
+    Wr[i * ld + j] = S[e];
+  }
   if (tid == 0) {
     ctl[0] = 0;
     ctl[1] = 0;
@@ -58,20 +65,19 @@ __global__ __launch_bounds__(256) void k_rsvd(RsvdArgs a) {
     }
     __syncthreads();
     for (int it = 0; it < a.iters; ++it) {
-      // Y = S^T Omega: thread j, all b columns
-      for (int j = tid; j < dv; j += 256) {
-        float acc[kMaxM];
-#pragma unroll
-        for (int c = 0; c < kMaxM; ++c) acc[c] = 0.f;
+      // Y = S^T Omega: a thread owns row j of Y and a group of 4 of its columns
+      for (int o = tid; o < dv * ((b + 3) >> 2); o += 256) {
+        const int j = o % dv, c0 = 4 * (o / dv);
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
         for (int i = 0; i < dk; ++i) {
-          const float w = Wr[(int64_t)i * dv + j];
+          const float w = Wr[i * ld + j];
 #pragma unroll
-          for (int c = 0; c < kMaxM; ++c)
-            if (c < b) acc[c] = fmaf(w, Om[c][i], acc[c]);
+          for (int u = 0; u < 4; ++u)
+            if (c0 + u < b) acc[u] = fmaf(w, Om[c0 + u][i], acc[u]);
         }
 #pragma unroll
-        for (int c = 0; c < kMaxM; ++c)
-          if (c < b) Qv[c][j] = acc[c];
+        for (int u = 0; u < 4; ++u)
+          if (c0 + u < b) Qv[c0 + u][j] = acc[u];
       }
       __syncthreads();
       if (wv == 0) {  // Q = orth(Y)
@@ -93,21 +99,20 @@ __global__ __launch_bounds__(256) void k_rsvd(RsvdArgs a) {
           }
       }
       __syncthreads();
-      // Omega = S Q: thread i, all b columns
-      for (int i = tid; i < dk; i += 256) {
-        float acc[kMaxM];
-#pragma unroll
-        for (int c = 0; c < kMaxM; ++c) acc[c] = 0.f;
-        const float *row = Wr + (int64_t)i * dv;
+      // Omega = S Q: a thread owns row i of Omega and a group of 4 of its columns
+      for (int o = tid; o < dk * ((b + 3) >> 2); o += 256) {
+        const int i = o % dk, c0 = 4 * (o / dk);
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        const float *row = Wr + i * ld;
         for (int j = 0; j < dv; ++j) {
           const float w = row[j];
 #pragma unroll
-          for (int c = 0; c < kMaxM; ++c)
-            if (c < b) acc[c] = fmaf(w, Qv[c][j], acc[c]);
+          for (int u = 0; u < 4; ++u)
+            if (c0 + u < b) acc[u] = fmaf(w, Qv[c0 + u][j], acc[u]);
         }
 #pragma unroll
-        for (int c = 0; c < kMaxM; ++c)
-          if (c < b) Om[c][i] = acc[c];
+        for (int u = 0; u < 4; ++u)
+          if (c0 + u < b) Om[c0 + u][i] = acc[u];
       }
       __syncthreads();
     }
@@ -228,11 +233,11 @@ __global__ __launch_bounds__(256) void k_rsvd(RsvdArgs a) {
     // the block leaves the residual: S <- S - X diag(sigma) (Q W)^T
     for (int e = tid; e < dk * dv; e += 256) {
       const int i = e / dv, j = e - i * dv;
-      float w = Wr[e];
+      float w = Wr[i * ld + j];
 #pragma unroll
       for (int c = 0; c < kMaxM; ++c)
         if (c < b) w = fmaf(-Om[c][i], Qv[c][j], w);
-      Wr[e] = w;
+      Wr[i * ld + j] = w;
     }
     __syncthreads();
   }
@@ -245,8 +250,15 @@ hipError_t launch_rsvd_init(const RsvdArgs &a, hipStream_t st) {
   if (a.n <= 0) return hipSuccess;
   const int nk = a.dk <= 64 ? 1 : a.dk <= 128 ? 2 : 4, nv = a.dv <= 64 ? 1 : a.dv <= 128 ? 2 : 4;
   const dim3 g((unsigned)a.n), b(256);
-#define SS_RSVD(K, V) \
-  if (nk == K && nv == V) { hipLaunchKernelGGL((k_rsvd<K, V>), g, b, 0, st, a); return hipGetLastError(); }
+  // the residual in LDS when it fits beside the kernel's 33 KB of static LDS
+  const size_t sh = sizeof(float) * (size_t)a.dk * (a.dv + 1);
+  const bool lds = sh <= 120 * 1024;
+#define SS_RSVD(K, V)                                                                        \
+  if (nk == K && nv == V) {                                                                  \
+    if (lds) hipLaunchKernelGGL((k_rsvd<K, V, true>), g, b, sh, st, a);                      \
+    else hipLaunchKernelGGL((k_rsvd<K, V, false>), g, b, 0, st, a);                          \
+    return hipGetLastError();                                                                \
+  }
   SS_RSVD(1, 1) SS_RSVD(1, 2) SS_RSVD(1, 4) SS_RSVD(2, 1) SS_RSVD(2, 2) SS_RSVD(2, 4) SS_RSVD(4, 1) SS_RSVD(4, 2)
   SS_RSVD(4, 4)
 #undef SS_RSVD
