@@ -122,3 +122,31 @@ def test_graph_gdn_delta_with_eager_work_between_replays():
     """1,536 delta-rule states 128x128, with eager readouts and out-of-schedule compactions
     between the replays."""
     _twin_run("gdn_delta", 20, eager_extra=True, oracle_steps={3, 8})
+
+
+def test_graph_on_dense_baseline_pool():
+    """A force_dense pool has no compaction: its graphs hold the plain dense decode only and must
+    match eager decode steps bit for bit."""
+    w = W.get("tiny")
+    init = W.initial_state(w)
+    A = _pool(w, init, force_dense=True)
+    B = _pool(w, init, force_dense=True)
+    N, dk, dv = w.n_states, w.d_k, w.d_v
+    buf = {"q": torch.zeros(N, dk, device="cuda"), "k": torch.zeros(N, dk, device="cuda"),
+           "v": torch.zeros(N, dv, device="cuda"), "alpha": torch.zeros(N, device="cuda")}
+    oA = torch.empty(N, dv, device="cuda")
+    oB = torch.empty(N, dv, device="cuda")
+    graph = ss.StepGraph(B, buf["q"], buf["k"], buf["v"], buf["alpha"], None, oB)
+    gen = W.StepInputs(w, device="cuda")
+    for t in range(1, 13):
+        x = gen.generate(t)
+        for key, b in buf.items():
+            b.copy_(x[key])
+        graph.launch(t)
+        ss.decode_step(A, x["q"], x["k"], x["v"], x["alpha"], None, oA)
+        torch.cuda.synchronize()
+        assert torch.equal(oA, oB), t
+    _same_states(ss.state_export(A, np.arange(N)), ss.state_export(B, np.arange(N)), 12)
+    graph.close()
+    A.close()
+    B.close()

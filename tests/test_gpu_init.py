@@ -143,3 +143,29 @@ def test_pool_from_dense_states():
         e = rel_out_err(o.cpu().numpy(), oo, Sn, np.linalg.norm(f64(q), axis=1))
         assert e.max() <= TOL, (t, e.max())
     pool.close()
+
+
+@pytest.mark.parametrize("d_k,d_v,b", [(4, 8, 1), (8, 4, 4), (20, 12, 2)])
+def test_rsvd_small_edge_shapes(d_k, d_v, b):
+    nb = -(-min(d_k, d_v) // b)
+    _check(d_k, d_v, b, nb, 3, 1e-3, "lowrank", n=16, seed=d_k * 7 + d_v)
+
+
+def test_pool_from_dense_all_dense_and_none_dense():
+    """Every state given dense (full rank) or none (low rank): both create paths."""
+    rng = np.random.default_rng(21)
+    n, d_k, d_v, b = 16, 16, 32, 4
+    S = _states(rng, n, d_k, d_v, "flat")
+    om = rng.standard_normal((n, 4, d_k, b)).astype(np.float32)
+    pool = ss.state_pool_from_dense(S, om, 1e-3)
+    ex = ss.state_export(pool, np.arange(n))
+    assert all(x["dense"] and np.array_equal(x["S"], S[i]) for i, x in enumerate(ex))
+    pool.close()
+    S2 = _states(rng, n, d_k, d_v, "exact")
+    pool = ss.state_pool_from_dense(S2, om, 1e-3)
+    ex = ss.state_export(pool, np.arange(n))
+    from parity_util import reconstruct
+    for i, x in enumerate(ex):
+        assert not x["dense"]
+        assert np.linalg.norm(reconstruct(x) - S2[i]) <= 1e-4 * np.linalg.norm(S2[i])
+    pool.close()
