@@ -63,6 +63,8 @@ def _load():
     lib.orc_readout.argtypes = [ctypes.c_void_p, _dp, _dp, ctypes.c_int]
     lib.orc_compact.restype = ctypes.c_int64
     lib.orc_compact.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64), ctypes.c_int64, ctypes.c_int]
+    lib.orc_consolidate.restype = ctypes.c_int64
+    lib.orc_consolidate.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64), ctypes.c_int64, ctypes.c_int]
     lib.orc_householder_qr.argtypes = [ctypes.c_int, ctypes.c_int, _dp, _dp, _dp]
     lib.orc_jacobi_svd.argtypes = [ctypes.c_int, ctypes.c_int, _dp, _dp, _dp, _dp]
     lib.orc_brand.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _dp, _dp, _dp, _dp, _dp, _dp]
@@ -286,3 +288,15 @@ class OraclePool:
                                         int(nthreads))
         if bad:
             raise RuntimeError(f"oracle compact failed for {bad} states")
+
+    def consolidate(self, ids=None, nthreads=0):
+        """Exact SVD of each listed state's frozen part, dropping singular values below
+        eps * sigma_0 (SinkState 4.3, Figure 7(a)); the active part and the pad stay."""
+        if ids is None:
+            bad = self._lib.orc_consolidate(self._p, None, 0, int(nthreads))
+        else:
+            ids = np.ascontiguousarray(ids, dtype=np.int64)
+            bad = self._lib.orc_consolidate(self._p, ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                            ids.shape[0], int(nthreads))
+        if bad:
+            raise RuntimeError(f"oracle consolidate failed for {bad} states")

@@ -28,6 +28,8 @@
  *             as a dense matrix (SinkState, 4.4 "Memory layout").
  *   init      randomized block SVD of a dense state after prefill
  *             (SinkState, 4.2 "Randomized SVD initialization after prefill").
+ *   consolidate  exact SVD of the frozen part, drop sigma < eps * sigma_0
+ *             (SinkState, 4.3 "Asynchronous CPU Consolidation", Figure 7(a)).
  *
  * Decay is applied literally, every step, to every sigma and pad weight.  QR
  * is Householder, the small SVD is cyclic one-sided (Hestenes) Jacobi, both
@@ -608,6 +610,82 @@ int64_t orc_compact(orc_pool *p, const int64_t *ids, int64_t n_ids, int nthreads
   for (int64_t i = 0; i < cnt; ++i) {
     int64_t s = ids ? ids[i] : i;
     if (s < 0 || s >= p->N || compact_one(p, &p->st[s])) bad += 1;
+  }
+  (void)nthreads;
+  return bad;
+}
+
+/* Consolidation of the frozen part of one state (SinkState 4.3 "Asynchronous
+ * CPU Consolidation", Figure 7(a)):
+ *  1. frozen = components ra..R-1 (ra = min(r, R)); the active part and the
+ *     pad are not touched;
+ *  2. sigma_0 is the state's largest stored singular value before the
+ *     consolidation (active and frozen lists are each descending, so it is
+ *     the larger of their first entries);
+ *  3. exact SVD of the frozen part U_F diag(sigma_F) V_F^T (the Brand routine
+ *     above applied to the frozen components alone is that SVD);
+ *  4. keep the singular values >= eps * sigma_0 (and > 0), in descending
+ *     order; they replace the frozen part.  The dropped part goes into the
+ *     open-loop bound as its Frobenius norm.
+ * A dense state, or one with no frozen component, is left unchanged.  The
+ * result's frozen list is sorted on its own; its first entry may exceed the
+ * last active one, as the active part is left as it was. */
+static int consolidate_one(orc_pool *p, orc_state *x) {
+  int dk = p->d_k, dv = p->d_v;
+  if (x->dense) return 0;
+  int ra = x->R < p->r ? x->R : p->r;
+  int nf = x->R - ra;
+  if (nf <= 0) return 0;
+  int pr = dv < nf ? dv : nf;
+  double *UF = (double *)malloc((size_t)dk * nf * sizeof(double));
+  double *VF = (double *)malloc((size_t)dv * nf * sizeof(double));
+  double *sf = (double *)malloc((size_t)nf * sizeof(double));
+  double *Uo = (double *)malloc((size_t)dk * pr * sizeof(double));
+  double *Vo = (double *)malloc((size_t)dv * pr * sizeof(double));
+  double *so = (double *)malloc((size_t)pr * sizeof(double));
+  int rc = -1;
+  if (!UF || !VF || !sf || !Uo || !Vo || !so) goto done;
+  memcpy(UF, x->U + (size_t)ra * dk, (size_t)nf * dk * sizeof(double));
+  memcpy(VF, x->V + (size_t)ra * dv, (size_t)nf * dv * sizeof(double));
+  memcpy(sf, x->sig + ra, (size_t)nf * sizeof(double));
+  {
+    double s0 = x->sig[ra];
+    if (ra > 0 && x->sig[0] > s0) s0 = x->sig[0];
+    double thr = x->eps * s0;
+    if (orc_brand(dk, dv, nf, UF, VF, sf, Uo, Vo, so) != pr) goto done;
+    int out = 0;
+    double dropped2 = 0.0;
+    for (int c = 0; c < pr; ++c) {
+      if (so[c] > 0.0 && so[c] >= thr) {
+        memcpy(x->U + (size_t)(ra + out) * dk, Uo + (size_t)c * dk, dk * sizeof(double));
+        memcpy(x->V + (size_t)(ra + out) * dv, Vo + (size_t)c * dv, dv * sizeof(double));
+        x->sig[ra + out] = so[c];
+        ++out;
+      } else {
+        dropped2 += so[c] * so[c];
+      }
+    }
+    x->R = ra + out;
+    x->bound += sqrt(dropped2);
+    rc = 0;
+  }
+done:
+  free(UF); free(VF); free(sf); free(Uo); free(Vo); free(so);
+  return rc;
+}
+
+/* Consolidates the listed states (all states when ids == NULL).  Returns the
+ * number of failures (allocation only). */
+int64_t orc_consolidate(orc_pool *p, const int64_t *ids, int64_t n_ids, int nthreads) {
+  int64_t bad = 0;
+  int64_t cnt = ids ? n_ids : p->N;
+#ifdef _OPENMP
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 4) num_threads(nthreads) reduction(+ : bad)
+#endif
+  for (int64_t i = 0; i < cnt; ++i) {
+    int64_t s = ids ? ids[i] : i;
+    if (s < 0 || s >= p->N || consolidate_one(p, &p->st[s])) bad += 1;
   }
   (void)nthreads;
   return bad;
