@@ -209,7 +209,8 @@ class OraclePool:
     # -- state access ------------------------------------------------------
     def set_state(self, s, st: OracleState, as_init: bool = True):
         """Load a state.  as_init=True applies the create-time dense fallback (R > L);
-        as_init=False loads a mid-run state exactly as given."""
+        as_init=False loads a mid-run state as given: its first min(r, R) components are the
+        active part and the rest the frozen part, each sorted on its own."""
         dk, dv = self.d_k, self.d_v
         if st.S is not None:
             S = _f64(st.S).reshape(dk, dv)

@@ -315,11 +315,14 @@ static int make_dense(orc_pool *p, orc_state *x) {
   return 0;
 }
 
-/* Set one state.  Components are given as rows and are sorted here by
- * sigma (descending, stable).  With as_init set, a factored state given with
+/* Set one state.  Components are given as rows.  With as_init set they are
+ * sorted by sigma (descending, stable), and a factored state given with
  * R > L falls back to the dense form (SinkState 4.4: the dense test is made
- * once the initial factors exist); without it the state is loaded as given, e.g. to
- * continue from a state taken in the middle of a run. */
+ * once the initial factors exist).  Without it the state is loaded as given,
+ * e.g. to continue from a state taken in the middle of a run: the first
+ * min(r, R) components stay the active part and the rest the frozen part,
+ * each sorted on its own (after a consolidation, SinkState 4.3, the frozen
+ * list can start above the last active value). */
 int orc_set_state(orc_pool *p, int64_t s, int rule, double eps, int R, const double *U, const double *V,
                   const double *sig, int n, const double *PK, const double *PW, const double *pc, int dense,
                   const double *S, int as_init) {
@@ -346,10 +349,14 @@ int orc_set_state(orc_pool *p, int64_t s, int rule, double eps, int R, const dou
   int *ord = (int *)malloc((size_t)(R > 0 ? R : 1) * sizeof(int));
   if (!ord) return -1;
   for (int i = 0; i < R; ++i) ord[i] = i;
-  for (int a = 1; a < R; ++a) {
-    int t = ord[a], b = a - 1;
-    while (b >= 0 && sig[ord[b]] < sig[t]) { ord[b + 1] = ord[b]; --b; }
-    ord[b + 1] = t;
+  int split = as_init ? R : (R < p->r ? R : p->r);
+  for (int part = 0; part < 2; ++part) {
+    int lo = part == 0 ? 0 : split, hi = part == 0 ? split : R;
+    for (int a = lo + 1; a < hi; ++a) {
+      int t = ord[a], b = a - 1;
+      while (b >= lo && sig[ord[b]] < sig[t]) { ord[b + 1] = ord[b]; --b; }
+      ord[b + 1] = t;
+    }
   }
   for (int i = 0; i < R; ++i) {
     memcpy(x->U + (size_t)i * dk, U + (size_t)ord[i] * dk, dk * sizeof(double));

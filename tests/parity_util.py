@@ -65,7 +65,7 @@ def compare_compacted(gpu_states, P, eps, K=None):
         if st["dense"]:
             continue
         sg = np.sort(st["sigma"].astype(np.float64))[::-1]
-        so = ost.sigma
+        so = np.sort(ost.sigma)[::-1]
         smax = max(sg[0] if len(sg) else 0.0, so[0] if len(so) else 0.0)
         if len(sg) != len(so):
             thr = eps[j] * smax

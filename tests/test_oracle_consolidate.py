@@ -247,3 +247,33 @@ def test_eps0_run_with_consolidation_equals_dense(rule):
     assert max(len(Pf.get_state(s).sigma) for s in range(N)) > r  # frozen parts existed
     Pf.close()
     Pd.close()
+
+
+def test_mid_run_reload_keeps_the_active_frozen_split():
+    """After a consolidation the frozen list may start above the last active value; a state
+    reloaded as a mid-run state keeps its split, so both copies compact identically."""
+    rng = np.random.default_rng(8)
+    d, eps = 8, 0.01
+    Q, W = _orth(rng, d, 4), _orth(rng, d, 4)
+    U = np.vstack([Q[:, 0], Q[:, 1], Q[:, 2], Q[:, 2]])
+    V = np.vstack([W[:, 0], W[:, 1], W[:, 2], W[:, 2]])
+    P = _pool(OracleState(U, V, np.array([6.0, 5.0, 4.0, 3.5]), rule=0, eps=eps), d, d, 2)
+    P.consolidate()
+    a = P.get_state(0)
+    assert len(a.sigma) == 3 and abs(a.sigma[2] - 7.5) < 1e-12 and a.sigma[2] > a.sigma[1]
+    a.PK = rng.standard_normal((2, d))
+    a.PW = rng.standard_normal((2, d))
+    a.pc = np.array([1.0, 0.5])
+    P2 = _pool(a, d, d, 2)
+    b = P2.get_state(0)
+    assert np.array_equal(b.sigma, a.sigma) and np.array_equal(b.U, a.U)
+    P3 = _pool(OracleState(a.U, a.V, a.sigma, a.PK, a.PW, a.pc, rule=0, eps=eps), d, d, 2)
+    P2.compact()
+    P3.compact()
+    assert np.array_equal(P2.reconstruct(0), P3.reconstruct(0))
+    # the compaction merges the frozen 7.5 into the active part: the first two values are the top two
+    c = P2.get_state(0)
+    assert c.sigma[0] >= c.sigma[1] >= c.sigma[2]
+    P.close()
+    P2.close()
+    P3.close()
