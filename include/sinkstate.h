@@ -111,6 +111,7 @@ enum {
   SS_KERNEL_COMPACT = 4,
   SS_KERNEL_MATERIALIZE = 5,
   SS_KERNEL_DENSE_FOLD = 6,
+  SS_KERNEL_CONSOLIDATE = 7,
   SS_KERNEL_COUNT = 8
 };
 
@@ -136,6 +137,10 @@ typedef struct {
   int64_t ring_syncs;       /* compactions that had to wait for the device to check ring room */
   double kernel_ms[SS_KERNEL_COUNT];       /* summed HIP-event durations while timing is on */
   int64_t kernel_launches[SS_KERNEL_COUNT];
+  int64_t consolidate_calls;     /* group consolidations launched so far */
+  uint64_t consolidate_states;   /* states whose frozen part was consolidated */
+  uint64_t consolidate_flops;    /* algorithmic flops of those consolidations */
+  uint64_t consolidate_removed;  /* frozen components they removed */
 } ss_stats;
 
 /* Create a pool ([SS] 4.4 "Memory layout"): per state a 16-byte metadata
@@ -188,6 +193,34 @@ ss_status ss_readout(ss_pool *pool, const float *q, float *o, hipStream_t stream
  * folded into H.  A ring found full on the device (not expected: the host
  * check is conservative) leaves the pool in error (SS_ERR_CAPACITY). */
 ss_status ss_compact(ss_pool *pool, int32_t group, hipStream_t stream);
+
+/* Consolidation of the frozen part ([SS] 4.3 "Asynchronous CPU
+ * Consolidation", Figure 7(a)), run on the device: for every factored state
+ * of group `group` (of all groups when group < 0), the frozen components are
+ * replaced by the exact SVD of their sum, keeping the singular values
+ * >= eps * sigma_0, where sigma_0 is the state's largest stored singular
+ * value before the call (the larger of the first active and the first frozen
+ * one).  The active part, the pad and Gamma are left as they are; the new
+ * frozen list is sorted descending on its own.  The components are rewritten
+ * in place (there are never more of them), so the group's ring segment keeps
+ * its size until its next compaction.  The work is ordered on `stream` with
+ * decode steps and compactions: it sees the frozen part the last compaction
+ * left and is done before the next one reads it, so a result is never stale.
+ * Errors: SS_ERR_ARG (bad group), SS_ERR_SHAPE (the pool's largest frozen part,
+ * f = min(max_frozen, L - r_active) with promotion and max_frozen without,
+ * needs more than 160 KB of LDS: 4 (f' d_k + f d_v + f'^2 + 3 f' + 4) bytes,
+ * f' = f rounded up to even), SS_ERR_HIP.  A force_dense pool is a no-op. */
+ss_status ss_consolidate(ss_pool *pool, int32_t group, hipStream_t stream);
+
+/* Consolidation scheduling ([SS] 4.3, Figure 7(b)) on one stream: each
+ * compaction puts its group in a wait queue; this call consolidates up to
+ * max_groups waiting groups, the least recently consolidated first (groups
+ * never consolidated before all others, then by id), removes them from the
+ * queue, writes their ids to out (NULL: not reported; otherwise room for
+ * max_groups) and their count to *n_done.  The pages' drop of stale results
+ * and retry-first rule have nothing to act on here: stream order makes every
+ * result current.  Errors as ss_consolidate. */
+ss_status ss_consolidate_next(ss_pool *pool, int32_t max_groups, int32_t *out, int32_t *n_done, hipStream_t stream);
 
 /* Staggered schedule ([SS] 4.2 "Staggered compaction across layers"): the
  * groups due after decode step `step` (counted from 1) are those with

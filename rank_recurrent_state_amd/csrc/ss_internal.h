@@ -32,7 +32,10 @@ constexpr uint32_t FLAG_DENSE = 2u;
 constexpr int kMaxM = 16;      // r + K
 constexpr int kAcctSlots = 256;
 // accounting arrays, kAcctSlots entries each
-enum Acct : int { A_DECODE_FACTORED = 0, A_DECODE_DENSE = 1, A_COMPACT_FLOPS = 2, A_COMPACT_STATES = 3, A_N = 4 };
+enum Acct : int {
+  A_DECODE_FACTORED = 0, A_DECODE_DENSE = 1, A_COMPACT_FLOPS = 2, A_COMPACT_STATES = 3,
+  A_CONS_FLOPS = 4, A_CONS_STATES = 5, A_CONS_REMOVED = 6, A_N = 7
+};
 
 // 16-byte per-state record.  packed: ra | rf << 8 | n << 16 | flags << 24.
 struct __attribute__((aligned(16))) Meta {
@@ -227,6 +230,20 @@ struct RsvdArgs {
   int32_t *rank;       // [n]
 };
 hipError_t launch_rsvd_init(const RsvdArgs &a, hipStream_t st);
+
+// consolidation of the frozen parts of a group's factored states (one workgroup each, in place)
+struct ConsolidateArgs {
+  int dk, dv, fmax;            // fmax: largest frozen count a state can hold (sizes the LDS)
+  int32_t n_members;
+  const int32_t *members;
+  const float *eps;
+  Meta *meta;
+  Arena act, frz;
+  unsigned long long *acct_flops, *acct_states, *acct_removed;
+};
+constexpr size_t kConsolidateLdsMax = 160 * 1024;  // LDS per workgroup on gfx950
+size_t consolidate_lds_bytes(int dk, int dv, int fmax);
+hipError_t launch_consolidate(const ConsolidateArgs &a, hipStream_t st);
 
 // how a state is decoded
 enum DecodeKind : int { KIND_FACTORED = 0, KIND_DENSE_BUFFERED = 1, KIND_DENSE_PLAIN = 2 };

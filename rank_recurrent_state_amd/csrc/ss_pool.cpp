@@ -88,6 +88,11 @@ struct ss_pool {
   std::vector<void *> dev_allocs;
   int64_t reserved = 0;
   int64_t decode_calls = 0, compact_calls = 0, readout_calls = 0;
+  // consolidation queue: groups compacted since their last consolidation, and when each group
+  // was last consolidated (-1: never)
+  std::vector<char> cons_wait;
+  std::vector<int64_t> cons_last;
+  int64_t cons_seq = 0, consolidate_calls = 0;
   ss_status sticky = SS_OK;
   std::string sticky_msg;
   // measurement hook: event pairs around kernel launches
@@ -721,6 +726,8 @@ ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipSt
     p->seg_bound[R].assign(G, 0);
     if (factored) ring_records(p, R, seg.data() + (size_t)R * 2 * G, (unsigned long long)tot[R]);
   }
+  p->cons_wait.assign(G, 0);
+  p->cons_last.assign(G, -1);
   if (p->hflags) p->hflags[HF_FACT] = (uint32_t)p->fact_upper;
   *out = p;
   return SS_OK;
@@ -811,6 +818,7 @@ static hipError_t enqueue_prune(ss_pool *p, int64_t fact_grid, hipStream_t strea
 
 // host bookkeeping after the compaction of group g was enqueued with segment bounds ab
 static void after_compact_group(ss_pool *p, int g, const int64_t (&ab)[2]) {
+  p->cons_wait[g] = 1;
   for (int R = 0; R < 2; ++R) {  // the group's new segment, by its bound
     p->last_seq[R][g] = p->seq;
     p->seg_bound[R][g] = ab[R];
@@ -898,6 +906,78 @@ ss_status ss_rsvd_init(const float *S, int64_t n, int32_t d_k, int32_t d_v, int3
   a.S = S; a.omega = omega; a.eps = eps; a.work = work; a.u = u; a.v = v; a.sigma = sigma; a.rank = rank;
   const hipError_t e = ss::launch_rsvd_init(a, stream);
   return e == hipSuccess ? SS_OK : hip_fail(e, "randomized SVD launch");
+}
+
+// Largest frozen count a factored state of the pool can hold: with promotion a state keeps at
+// most L components, r of them active; without, the per-state frozen capacity.
+static int frozen_max(const ss_pool *p) {
+  return p->promote ? std::max(0, std::min(p->fcap, p->L - p->r)) : p->fcap;
+}
+
+static hipError_t enqueue_consolidate_group(ss_pool *p, int g, hipStream_t stream) {
+  ss::ConsolidateArgs a{};
+  a.dk = p->dk; a.dv = p->dv; a.fmax = frozen_max(p);
+  a.n_members = (int32_t)p->group_size[g];
+  a.members = p->members + p->group_start[g];
+  a.eps = p->eps; a.meta = p->meta; a.act = p->act; a.frz = p->frz;
+  a.acct_flops = p->acct + ss::A_CONS_FLOPS * ss::kAcctSlots;
+  a.acct_states = p->acct + ss::A_CONS_STATES * ss::kAcctSlots;
+  a.acct_removed = p->acct + ss::A_CONS_REMOVED * ss::kAcctSlots;
+  auto fn = [&] { return ss::launch_consolidate(a, stream); };
+  return timed(p, SS_KERNEL_CONSOLIDATE, stream, fn);
+}
+
+static ss_status consolidate_checked(ss_pool *p, int g, hipStream_t stream) {
+  p->cons_wait[g] = 0;
+  p->cons_last[g] = p->cons_seq++;
+  if (p->group_size[g] == 0 || frozen_max(p) == 0) return SS_OK;
+  const hipError_t e = enqueue_consolidate_group(p, g, stream);
+  if (e != hipSuccess) return hip_fail(e, "consolidate launch");
+  p->consolidate_calls++;
+  return SS_OK;
+}
+
+static ss_status consolidate_precheck(ss_pool *p) {
+  if (!p) return fail(SS_ERR_ARG, "pool is NULL");
+  ss_status st = poll(p);
+  if (st != SS_OK) return st;
+  if (ss::consolidate_lds_bytes(p->dk, p->dv, frozen_max(p)) > ss::kConsolidateLdsMax)
+    return fail(SS_ERR_SHAPE, "the pool's largest frozen part does not fit the consolidation kernel's LDS");
+  return SS_OK;
+}
+
+ss_status ss_consolidate(ss_pool *p, int32_t group, hipStream_t stream) {
+  ss_status st = consolidate_precheck(p);
+  if (st != SS_OK) return st;
+  if (group >= p->G) return fail(SS_ERR_ARG, "group out of range");
+  if (p->force_dense) return SS_OK;
+  const int g0 = group < 0 ? 0 : group, g1 = group < 0 ? p->G : group + 1;
+  for (int g = g0; g < g1; ++g) {
+    st = consolidate_checked(p, g, stream);
+    if (st != SS_OK) return st;
+  }
+  return SS_OK;
+}
+
+ss_status ss_consolidate_next(ss_pool *p, int32_t max_groups, int32_t *out, int32_t *n_done, hipStream_t stream) {
+  if (!p || !n_done || max_groups < 0) return fail(SS_ERR_ARG, "bad arguments");
+  *n_done = 0;
+  ss_status st = consolidate_precheck(p);
+  if (st != SS_OK) return st;
+  if (p->force_dense) return SS_OK;
+  std::vector<int> wait;
+  for (int g = 0; g < p->G; ++g)
+    if (p->cons_wait[g]) wait.push_back(g);
+  // least recently consolidated first (never consolidated: -1), then by group id
+  std::stable_sort(wait.begin(), wait.end(), [&](int x, int y) { return p->cons_last[x] < p->cons_last[y]; });
+  const int take = std::min<int>(max_groups, (int)wait.size());
+  for (int i = 0; i < take; ++i) {
+    st = consolidate_checked(p, wait[i], stream);
+    if (st != SS_OK) return st;
+    if (out) out[i] = wait[i];
+    *n_done = i + 1;
+  }
+  return SS_OK;
 }
 
 ss_status ss_schedule_due(const ss_pool *p, int64_t step, int32_t *out, int32_t cap, int32_t *n_due) {
@@ -1061,7 +1141,11 @@ ss_status ss_pool_stats(ss_pool *p, ss_stats *out, hipStream_t stream) {
     out->decode_bytes_dense += acct[ss::A_DECODE_DENSE * ss::kAcctSlots + i];
     out->compact_flops += acct[ss::A_COMPACT_FLOPS * ss::kAcctSlots + i];
     out->compact_states += acct[ss::A_COMPACT_STATES * ss::kAcctSlots + i];
+    out->consolidate_flops += acct[ss::A_CONS_FLOPS * ss::kAcctSlots + i];
+    out->consolidate_states += acct[ss::A_CONS_STATES * ss::kAcctSlots + i];
+    out->consolidate_removed += acct[ss::A_CONS_REMOVED * ss::kAcctSlots + i];
   }
+  out->consolidate_calls = p->consolidate_calls;
   out->decode_bytes = out->decode_bytes_factored + out->decode_bytes_dense;
   out->promotions = ctr[ss::C_PROMOTIONS];
   out->cap_truncations = ctr[ss::C_CAP_TRUNC];

@@ -58,11 +58,13 @@ class Stats(ctypes.Structure):
         ("ring_head", ctypes.c_int64 * 2),
         ("ring_repacks", ctypes.c_int64), ("ring_syncs", ctypes.c_int64),
         ("kernel_ms", ctypes.c_double * 8), ("kernel_launches", ctypes.c_int64 * 8),
+        ("consolidate_calls", ctypes.c_int64), ("consolidate_states", ctypes.c_uint64),
+        ("consolidate_flops", ctypes.c_uint64), ("consolidate_removed", ctypes.c_uint64),
     ]
 
 
 KERNELS = ("decode_factored", "decode_dense", "readout_factored", "readout_dense", "compact", "materialize",
-           "dense_fold")
+           "dense_fold", "consolidate")
 
 
 _lib = None
@@ -82,6 +84,8 @@ def load_library():
     lib.ss_decode_step.argtypes = [vp] + [vp] * 6 + [vp]
     lib.ss_readout.argtypes = [vp, vp, vp, vp]
     lib.ss_compact.argtypes = [vp, ctypes.c_int32, vp]
+    lib.ss_consolidate.argtypes = [vp, ctypes.c_int32, vp]
+    lib.ss_consolidate_next.argtypes = [vp, ctypes.c_int32, _c_i32p, _c_i32p, vp]
     lib.ss_schedule_due.argtypes = [vp, ctypes.c_int64, _c_i32p, ctypes.c_int32, _c_i32p]
     lib.ss_state_export.argtypes = [vp, _c_i64p, ctypes.c_int64, vp, ctypes.c_size_t,
                                     ctypes.POINTER(ctypes.c_size_t), vp]
@@ -310,6 +314,19 @@ def readout(pool: StatePool, q, o, stream=None):
 
 def compact(pool: StatePool, group: int = -1, stream=None):
     _check(load_library().ss_compact(pool.handle, int(group), _stream(stream)))
+
+
+def consolidate(pool: StatePool, group: int = -1, stream=None):
+    """Consolidate the frozen parts of group `group` (all groups when < 0) on the device."""
+    _check(load_library().ss_consolidate(pool.handle, int(group), _stream(stream)))
+
+
+def consolidate_next(pool: StatePool, max_groups: int, stream=None) -> list:
+    """Consolidate up to max_groups groups from the wait queue; returns their ids."""
+    out = (ctypes.c_int32 * max(1, int(max_groups)))()
+    n = ctypes.c_int32()
+    _check(load_library().ss_consolidate_next(pool.handle, int(max_groups), out, ctypes.byref(n), _stream(stream)))
+    return [int(out[i]) for i in range(n.value)]
 
 
 def schedule_due(pool: StatePool, step: int) -> list:

@@ -104,6 +104,11 @@ def test_calls_on_null_pool_are_rejected(lib):
     assert lib.ss_step_graph_create(None, None, None, None, None, None, None, None) == ss.SS_ERR_ARG
     assert lib.ss_step_graph_launch(None, 0, None) == ss.SS_ERR_ARG
     assert lib.ss_step_graph_destroy(None) == ss.SS_OK
+    assert lib.ss_consolidate(None, 0, None) == ss.SS_ERR_ARG
+    n32 = ctypes.c_int32(7)
+    assert lib.ss_consolidate_next(None, 1, None, ctypes.byref(n32), None) == ss.SS_ERR_ARG
+    assert n32.value == 7
+    assert lib.ss_consolidate_next(None, 1, None, None, None) == ss.SS_ERR_ARG
 
 
 def test_dense_rank_limit_pins(lib):

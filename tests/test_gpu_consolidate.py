@@ -1,0 +1,192 @@
+"""GPU parity of the frozen-part consolidation (SinkState 4.3, Figure 7(a)) against the oracle.
+
+Each test runs decode steps and compactions on the GPU until frozen parts have
+built up, exports the states, loads them into the oracle, consolidates on both
+sides and compares: active parts and pads unchanged bit for bit, states and
+singular values within the parity tolerance, ranks equal outside the guard
+band, and the new frozen factors orthonormal.
+"""
+import numpy as np
+import pytest
+import torch
+
+from parity_util import TOL, compare_compacted, oracle_from_export, reconstruct
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from rank_recurrent_state_amd import sinkstate as ss
+    from rank_recurrent_state_amd import workloads as W
+
+
+def _pool(w, init, **kw):
+    return ss.state_pool_create(w.n_states, w.d_k, w.d_v, w.K, w.r, group_of_state=init["group_of_state"],
+                                group_offset=init["group_offset"], rule=init["rule"], eps=init["eps"],
+                                comp_off=init["comp_off"], u=init["u"], v=init["v"], sigma=init["sigma"], **kw)
+
+
+def _run(w, pool, t0, t1):
+    gen = W.StepInputs(w, device="cuda")
+    o = torch.empty(w.n_states, w.d_v, device="cuda")
+    for t in range(t0, t1 + 1):
+        x = gen.generate(t)
+        ss.decode_step(pool, x["q"], x["k"], x["v"], x["alpha"], x["beta"], o)
+        for g in ss.schedule_due(pool, t):
+            ss.compact(pool, g)
+    torch.cuda.synchronize()
+
+
+def _consolidate_and_compare(w, init, pool, ids, group=-1):
+    eps = init["eps"][ids]
+    before = ss.state_export(pool, ids)
+    P = oracle_from_export(before, eps, w.d_k, w.d_v, w.K, w.r)
+    st0 = ss.pool_stats(pool)
+    ss.consolidate(pool, group)
+    torch.cuda.synchronize()
+    after = ss.state_export(pool, ids)
+    sel = np.arange(len(ids)) if group < 0 else np.nonzero(init["group_of_state"][ids] == group)[0]
+    P.consolidate(sel)
+    in_sel = np.zeros(len(ids), bool)
+    in_sel[sel] = True
+    for b, a, mine in zip(before, after, in_sel):
+        assert a["dense"] == b["dense"]
+        if b["dense"]:
+            assert np.array_equal(a["S"], b["S"])
+            continue
+        ra = b["n_active"]
+        assert a["n_active"] == ra
+        for key in ("U", "V", "sigma"):
+            assert np.array_equal(a[key][:ra], b[key][:ra]), key
+        for key in ("c", "K", "W"):
+            assert np.array_equal(a[key], b[key]), key
+        rf = len(a["sigma"]) - ra
+        assert rf <= len(b["sigma"]) - ra
+        if rf and mine:  # states of other groups keep their frozen parts as they were
+            Uf = a["U"][ra:].astype(np.float64)
+            Vf = a["V"][ra:].astype(np.float64)
+            assert np.abs(Uf @ Uf.T - np.eye(rf)).max() <= 1e-4
+            assert np.abs(Vf @ Vf.T - np.eye(rf)).max() <= 1e-4
+            assert np.all(np.diff(a["sigma"][ra:]) <= 0)
+    ws, wsig, guard, bad = compare_compacted(after, P, eps)
+    assert not bad, bad[:5]
+    assert ws <= TOL and wsig <= TOL, (ws, wsig)
+    st1 = ss.pool_stats(pool)
+    removed = st1["consolidate_removed"] - st0["consolidate_removed"]
+    assert st0["frozen_components"] - st1["frozen_components"] == removed
+    return removed, guard
+
+
+def test_consolidate_tiny():
+    w = W.get("tiny")
+    init = W.initial_state(w)
+    pool = _pool(w, init)
+    _run(w, pool, 1, 64)
+    removed, _ = _consolidate_and_compare(w, init, pool, np.arange(w.n_states))
+    print("tiny removed", removed)
+    pool.close()
+
+
+@pytest.mark.parametrize("name,steps", [("gdn_delta", 48), ("mamba2_258k", 48)])
+def test_consolidate_one_request(name, steps):
+    w = W.get(name, n_requests=1)
+    init = W.initial_state(w)
+    pool = _pool(w, init)
+    _run(w, pool, 1, steps)
+    ids = np.unique(np.concatenate([np.arange(0, w.n_states, 7), [w.n_states - 1]]))
+    removed, guard = _consolidate_and_compare(w, init, pool, ids)
+    st = ss.pool_stats(pool)
+    print(name, "removed", st["consolidate_removed"], "states", st["consolidate_states"], "guard", guard)
+    if name == "gdn_delta":
+        assert st["consolidate_removed"] > 0
+    pool.close()
+
+
+def test_consolidate_mixed_initial_tails_and_dense_states():
+    """Initial frozen tails and dense states (mixed workload), one group at a time."""
+    w = W.get("mixed_dense", n_requests=1)
+    init = W.initial_state(w)
+    pool = _pool(w, init)
+    ids = np.arange(w.n_states)
+    for g in range(len(init["group_offset"])):
+        _consolidate_and_compare(w, init, pool, ids, group=g)
+    _run(w, pool, 1, 16)
+    _consolidate_and_compare(w, init, pool, ids)
+    pool.close()
+
+
+def test_decode_and_compaction_continue_after_consolidation():
+    """Lock-step decode and compaction after a consolidation (frozen lists may now start above
+    the last active value)."""
+    from test_gpu_parity import _assert_worst, _lockstep
+    w = W.get("gdn_delta", n_requests=1)
+    init = W.initial_state(w)
+    pool = _pool(w, init)
+    _run(w, pool, 1, 40)
+    ss.consolidate(pool)
+    ids = np.unique(np.concatenate([np.arange(0, w.n_states, 11), [w.n_states - 1]]))
+    worst, guard = _lockstep(w, init, pool, ids, 16)
+    print("after consolidation", worst, "guard", guard)
+    _assert_worst(worst)
+    pool.close()
+
+
+def test_consolidate_twice_changes_nothing():
+    w = W.get("gdn_delta", n_requests=1)
+    init = W.initial_state(w)
+    pool = _pool(w, init)
+    _run(w, pool, 1, 32)
+    ss.consolidate(pool)
+    ids = np.arange(0, w.n_states, 5)
+    a = ss.state_export(pool, ids)
+    st0 = ss.pool_stats(pool)
+    ss.consolidate(pool)
+    b = ss.state_export(pool, ids)
+    st1 = ss.pool_stats(pool)
+    assert st1["consolidate_removed"] == st0["consolidate_removed"]
+    for x, y in zip(a, b):
+        if x["dense"]:
+            continue
+        assert len(x["sigma"]) == len(y["sigma"])
+        Sx, Sy = reconstruct(x), reconstruct(y)
+        assert np.linalg.norm(Sx - Sy) <= 1e-5 * np.linalg.norm(Sx)
+    pool.close()
+
+
+def test_consolidate_next_queue_order():
+    w = W.get("gdn_delta", n_requests=1)
+    init = W.initial_state(w)
+    pool = _pool(w, init)
+    G = len(init["group_offset"])
+    assert G >= 3
+    assert ss.consolidate_next(pool, 4) == []
+    gen = W.StepInputs(w, device="cuda")
+    o = torch.empty(w.n_states, w.d_v, device="cuda")
+    x = gen.generate(1)
+    ss.decode_step(pool, x["q"], x["k"], x["v"], x["alpha"], x["beta"], o)
+    ss.compact(pool, 2)
+    ss.compact(pool, 0)
+    assert ss.consolidate_next(pool, 1) == [0]       # never consolidated: lowest id first
+    assert ss.consolidate_next(pool, 5) == [2]
+    assert ss.consolidate_next(pool, 5) == []
+    x = gen.generate(2)
+    ss.decode_step(pool, x["q"], x["k"], x["v"], x["alpha"], x["beta"], o)
+    ss.compact(pool, 2)
+    ss.compact(pool, 0)
+    ss.compact(pool, 1)
+    assert ss.consolidate_next(pool, 2) == [1, 0]    # 1 never; then 0 (consolidated before 2)
+    assert ss.consolidate_next(pool, 2) == [2]
+    torch.cuda.synchronize()
+    st = ss.pool_stats(pool)
+    assert st["consolidate_calls"] == 5
+    pool.close()
+
+
+def test_consolidate_rejects_frozen_parts_beyond_lds():
+    """Without promotion a 256x256 pool allows 255 frozen components: more than the kernel's LDS."""
+    pool = ss.state_pool_create(4, 256, 256, 8, 8, promote_on_compact=False, max_frozen=255)
+    with pytest.raises(RuntimeError):
+        ss.consolidate(pool)
+    pool.close()
+    pool = ss.state_pool_create(4, 256, 256, 8, 8, promote_on_compact=False, max_frozen=64)
+    ss.consolidate(pool)
+    pool.close()
