@@ -33,8 +33,9 @@ def _pool(ss, w, init, **kw):
                                 comp_off=init["comp_off"], u=init["u"], v=init["v"], sigma=init["sigma"], **kw)
 
 
-def _run_steps(ss, torch, pool, xs, t0, o, ev=None):
-    """Run len(xs) steps starting after step t0; optional per-step events."""
+def _run_steps(ss, torch, pool, xs, t0, o, ev=None, cons=(0, 1)):
+    """Run len(xs) steps starting after step t0; optional per-step events.  cons = (groups, period):
+    every `period` steps, consolidate up to `groups` groups from the wait queue after the compactions."""
     for i, x in enumerate(xs):
         t = t0 + i + 1
         if ev is not None:
@@ -42,6 +43,8 @@ def _run_steps(ss, torch, pool, xs, t0, o, ev=None):
         ss.decode_step(pool, x["q"], x["k"], x["v"], x["alpha"], x["beta"], o)
         for g in ss.schedule_due(pool, t):
             ss.compact(pool, g)
+        if cons[0] > 0 and t % cons[1] == 0:
+            ss.consolidate_next(pool, cons[0])
     if ev is not None:
         ev[len(xs)].record()
 
@@ -210,6 +213,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 4 GiB device copy (for scaling rocprof byte counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--consolidate", type=int, default=0,
+                    help="groups consolidated from the wait queue after a step's compactions (0: off)")
+    ap.add_argument("--consolidate-period", type=int, default=1, help="steps between consolidation calls")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the eager-versus-graph step timing and the initialization timing")
     args = ap.parse_args()
@@ -238,13 +244,14 @@ def main():
     gen = W.StepInputs(w, device="cuda")
     o = torch.empty(w.n_states, w.d_v, device="cuda")
 
+    cons = (max(0, args.consolidate), max(1, args.consolidate_period))
     # warmup on a scratch pool of the same workload
     if args.warmup > 0:
         pool = _pool(ss, w, init)
         wchunk = max(1, min(args.chunk, int(16e9 // (w.n_states * (2 * w.d_k + w.d_v + 2) * 4))))
         for c0 in range(0, args.warmup, wchunk):
             xs = [gen.generate(t) for t in range(c0 + 1, min(args.warmup, c0 + wchunk) + 1)]
-            _run_steps(ss, torch, pool, xs, c0, o)
+            _run_steps(ss, torch, pool, xs, c0, o, cons=cons)
         torch.cuda.synchronize()
         pool.close()
         del xs
@@ -264,7 +271,7 @@ def main():
         xs = [gen.generate(s) for s in range(t + 1, t + n + 1)]
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
         torch.cuda.synchronize()
-        _run_steps(ss, torch, pool, xs, t, o, ev)
+        _run_steps(ss, torch, pool, xs, t, o, ev, cons=cons)
         torch.cuda.synchronize()
         step_ms += [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
         t += n
@@ -301,6 +308,15 @@ def main():
                   "states_per_s": cstates / (kms["compact"] / 1e3) if kms["compact"] else None,
                   "algorithmic_TFLOPs": cflops / (kms["compact"] / 1e3) / 1e12 if kms["compact"] else None,
                   "materialize_ms_total": kms["materialize"], "promotions": st1["promotions"] - st0["promotions"]}
+    consolidation = None
+    if cons[0] > 0:
+        xf = st1["consolidate_flops"] - st0["consolidate_flops"]
+        consolidation = {"groups_per_call": cons[0], "period": cons[1], "launches": kn["consolidate"],
+                         "ms_total": kms["consolidate"], "states": st1["consolidate_states"] - st0["consolidate_states"],
+                         "removed_components": st1["consolidate_removed"] - st0["consolidate_removed"],
+                         "algorithmic_TFLOPs": xf / (kms["consolidate"] / 1e3) / 1e12 if kms["consolidate"] else None,
+                         "frozen_components_end": st1["frozen_components"],
+                         "active_components_end": st1["active_components"]}
     sm = np.array(step_ms)
     first = min(64, K_steps)
     phases = {"steps_1_%d_ms_per_step" % first: float(sm[:first].mean()),
@@ -373,6 +389,8 @@ def main():
                         "achieved_GBs": decode_bytes / (decode_ms / 1e3) / 1e9 if decode_ms else None,
                         "kernels": per_kernel},
         "compaction": compaction,
+        "consolidation": consolidation,
+        "frozen_components_end": st1["frozen_components"],
         "phases": phases,
         "dense_baseline": dense,
         "graph_replay": graphs,

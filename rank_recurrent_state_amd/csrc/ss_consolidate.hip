@@ -8,23 +8,29 @@
 // stay as they are; Gamma scales every component alike, so the work is done
 // on the stored values.
 //
-// One 256-thread workgroup per state; the frozen part is staged in LDS:
-//   1. B = U_F diag(sigma_F) (d_k x f) and V_F (d_v x f) from the frozen ring.
+// One 256-thread workgroup per state; the frozen part goes through one LDS
+// panel A (f columns) and the small matrix Y (f x f):
+//   1. V_F (d_v x f) from the frozen ring into A.
 //   2. Thin QR V_F = Q R by CGS2 over the workgroup: one wavefront per dot
-//      product, one thread per row for the updates.  A column whose residual
-//      is at most 1e-5 of its own norm is dependent: it is zeroed, and so is
-//      its row of R, so it cannot create a component.
-//   3. B <- B R^T (one thread per row, in place): the frozen part is B Q^T
-//      with Q orthonormal.
+//      product, one thread per row for the updates; R goes to Y.  A column
+//      whose residual is at most 1e-5 of its own norm is dependent: it is
+//      zeroed, and so is its row of R, so it cannot create a component.
+//      Q is parked in the state's own frozen v slots (their old contents are
+//      consumed), which frees A.
+//   3. B = U_F diag(sigma_F) R^T into A (one thread per row): the frozen
+//      part is B Q^T with Q orthonormal.
 //   4. One-sided (Hestenes) Jacobi on the columns of B: 8 lanes per column
 //      pair, up to 32 pairs per round in round-robin (circle) order, one
 //      barrier per round; the rotations are accumulated in Y (f x f).  At
 //      convergence B = X diag(s), and the frozen part is X diag(s) (Q Y)^T.
-//   5. Sort s; keep s >= eps sigma_0 (and s > 0); write u = B_j / s_j,
-//      v = Q Y_j and s_j over the state's frozen slots.  The result never has
-//      more components than the old frozen part, and every global read is done
-//      in step 1, so the write is in place: the group's ring segment keeps its
-//      size until the group's next compaction re-packs it.
+//   5. Sort s; keep s >= eps sigma_0 (and s > 0); write u = B_j / s_j and
+//      s_j over the state's frozen slots, bring Q back into A, and write
+//      v = Q Y_j.  The result never has more components than the old frozen
+//      part, so the write is in place: the group's ring segment keeps its size
+//      until the group's next compaction re-packs it.
+// Column strides in LDS are odd multiples of 8 floats, so the 8 lanes of a
+// Jacobi pair and the 8 pairs of a wavefront (consecutive columns) fall in
+// distinct banks.
 #include "ss_internal.h"
 #include "ss_linalg.h"
 #include "ss_wave.h"
@@ -36,6 +42,11 @@ namespace {
 constexpr int kCT = 256;         // threads per workgroup
 constexpr int kConsSweeps = 32;  // Jacobi sweep limit
 
+// smallest stride >= d that is an odd multiple of 8 floats
+__host__ __device__ inline int bank_stride(int d) { return ((d + 7) / 8 | 1) * 8; }
+
+// KE: elements per lane of a Jacobi column pair (8 lanes per pair), KE * 8 >= max(d_k, f)
+template <int KE>
 __global__ __launch_bounds__(256) void k_consolidate(ConsolidateArgs a) {
   extern __shared__ float sm[];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -46,45 +57,38 @@ __global__ __launch_bounds__(256) void k_consolidate(ConsolidateArgs a) {
   const int ra = meta_ra(packed), rf = meta_rf(packed), n = meta_n(packed);
   if (rf == 0 || rf > a.fmax) return;  // the host sizes fmax to the pool's largest frozen part
   const int dk = a.dk, dv = a.dv, F2 = (a.fmax + 1) & ~1;
-  float *B = sm;                                // [F2][dk]: column j at B + j dk
-  float *Q = B + (size_t)F2 * dk;               // [fmax][dv]
-  float *Y = Q + (size_t)a.fmax * dv;           // [F2][F2]: R(i, j) at Y[j F2 + i], then the rotations
-  float *sg = Y + (size_t)F2 * F2;              // [F2]: frozen sigma, later the column norms
-  float *dt = sg + F2;                          // [F2]: dot products
-  int *perm = reinterpret_cast<int *>(dt + F2);  // [F2]
+  const int bs = bank_stride(dk), ys = bank_stride(F2);
+  float *A = sm;                                      // [F2][max(bs, dv)]: Q (stride dv), then B (stride bs)
+  float *Y = A + (size_t)F2 * (bs > dv ? bs : dv);    // [F2][ys]: R(i, j) at Y[j ys + i], then the rotations
+  float *sg = Y + (size_t)F2 * ys;                    // [F2]: frozen sigma, later the column norms
+  float *dt = sg + F2;                                // [F2]: dot products
+  int *perm = reinterpret_cast<int *>(dt + F2);       // [F2]
   float *ctl = reinterpret_cast<float *>(perm + F2);  // [2]
   int *flag = reinterpret_cast<int *>(ctl + 2);       // [2]: rotation seen, per sweep parity
   const int64_t capF = a.frz.cap;
   const int off_f = uniform(m.off_f);
+  const int dk4 = dk >> 2, dv4 = dv >> 2;
 
-  // ---- 1. stage the frozen part --------------------------------------------------------------
+  // ---- 1. stage V_F --------------------------------------------------------------------------
   for (int j = tid; j < rf; j += kCT) sg[j] = a.frz.s[wrap(off_f + j, capF)];
-  for (int e = tid; e < F2 * F2; e += kCT) Y[e] = 0.f;
-  if (rf & 1)
-    for (int e = tid; e < dk; e += kCT) B[(size_t)rf * dk + e] = 0.f;
+  for (int e = tid; e < F2 * ys; e += kCT) Y[e] = 0.f;
   if (tid < 2) flag[tid] = 0;
+  for (int e = tid; e < rf * dv4; e += kCT) {
+    const int j = e / dv4, c = e - j * dv4;
+    st4(A + (size_t)j * dv + 4 * c, ld4(a.frz.v + wrap(off_f + j, capF) * dv + 4 * c));
+  }
   __syncthreads();
   float s0 = sg[0];
   if (ra > 0) s0 = fmaxf(s0, a.act.s[m.off_a]);
   const float thr = a.eps[s] * s0;
-  {
-    const int dk4 = dk >> 2, tot4 = dk4 + (dv >> 2);
-    for (int e = tid; e < rf * tot4; e += kCT) {
-      const int j = e / tot4, c = e - j * tot4;
-      const int64_t pos = wrap(off_f + j, capF);
-      if (c < dk4) st4(B + (size_t)j * dk + 4 * c, scale4(sg[j], ld4(a.frz.u + pos * dk + 4 * c)));
-      else st4(Q + (size_t)j * dv + 4 * (c - dk4), ld4(a.frz.v + pos * dv + 4 * (c - dk4)));
-    }
-  }
-  __syncthreads();
 
   // ---- 2. CGS2 thin QR of V_F ----------------------------------------------------------------
   for (int j = 0; j < rf; ++j) {
-    float *qj = Q + (size_t)j * dv;
+    float *qj = A + (size_t)j * dv;
     for (int pass = 0; pass < 2; ++pass) {
       const int hi = pass == 0 ? j + 1 : j;  // the first pass also takes |q_j|^2 (i = j)
       for (int i = w; i < hi; i += 4) {
-        const float *qi = Q + (size_t)i * dv;
+        const float *qi = A + (size_t)i * dv;
         float x = 0.f;
         for (int e = lane; e < dv; e += 64) x = fmaf(qi[e], qj[e], x);
         x = wave_sum_u(x);
@@ -93,10 +97,11 @@ __global__ __launch_bounds__(256) void k_consolidate(ConsolidateArgs a) {
       __syncthreads();
       if (tid < dv) {
         float x = qj[tid];
-        for (int i = 0; i < j; ++i) x = fmaf(-dt[i], Q[(size_t)i * dv + tid], x);
+#pragma unroll 8
+        for (int i = 0; i < j; ++i) x = fmaf(-dt[i], A[(size_t)i * dv + tid], x);
         qj[tid] = x;
       }
-      if (tid < j) Y[(size_t)j * F2 + tid] += dt[tid];
+      if (tid < j) Y[(size_t)j * ys + tid] += dt[tid];
       __syncthreads();
     }
     if (w == 0) {
@@ -110,27 +115,41 @@ __global__ __launch_bounds__(256) void k_consolidate(ConsolidateArgs a) {
     const bool keep = nu > 0.f && nu > kTau2 * n0;
     const float su = sqrtf(nu), iu = keep ? 1.0f / su : 0.f;
     if (tid < dv) qj[tid] *= iu;
-    if (tid == 0) Y[(size_t)j * F2 + j] = keep ? su : 0.f;
+    if (tid == 0) Y[(size_t)j * ys + j] = keep ? su : 0.f;
     __syncthreads();
   }
+  // park Q in the frozen v slots (V_F has been consumed)
+  for (int e = tid; e < rf * dv4; e += kCT) {
+    const int j = e / dv4, c = e - j * dv4;
+    st4(a.frz.v + wrap(off_f + j, capF) * dv + 4 * c, ld4(A + (size_t)j * dv + 4 * c));
+  }
+  __syncthreads();
 
-  // ---- 3. B <- B R^T, then Y <- I ------------------------------------------------------------
+  // ---- 3. B = U_F diag(sigma_F) R^T into A, then Y <- I --------------------------------------
+  for (int e = tid; e < rf * dk4; e += kCT) {
+    const int j = e / dk4, c = e - j * dk4;
+    st4(A + (size_t)j * bs + 4 * c, scale4(sg[j], ld4(a.frz.u + wrap(off_f + j, capF) * dk + 4 * c)));
+  }
+  if (rf & 1)  // an odd count is paired with a zero column in the Jacobi
+    for (int e = tid; e < dk; e += kCT) A[(size_t)rf * bs + e] = 0.f;
+  __syncthreads();
   if (tid < dk) {
-    for (int jp = 0; jp < rf; ++jp) {
+    for (int jp = 0; jp < rf; ++jp) {  // column jp reads columns >= jp only: in place, row-private
       float acc = 0.f;
-      for (int i = jp; i < rf; ++i) acc = fmaf(B[(size_t)i * dk + tid], Y[(size_t)i * F2 + jp], acc);
-      B[(size_t)jp * dk + tid] = acc;
+#pragma unroll 8
+      for (int i = jp; i < rf; ++i) acc = fmaf(A[(size_t)i * bs + tid], Y[(size_t)i * ys + jp], acc);
+      A[(size_t)jp * bs + tid] = acc;
     }
   }
   __syncthreads();
-  for (int e = tid; e < F2 * F2; e += kCT) {
-    const int c = e / F2;
-    Y[e] = (e - c * F2) == c ? 1.f : 0.f;
+  for (int e = tid; e < F2 * ys; e += kCT) {
+    const int c = e / ys;
+    Y[e] = (e - c * ys) == c ? 1.f : 0.f;
   }
   __syncthreads();
 
   // ---- 4. one-sided Jacobi on B's columns ----------------------------------------------------
-  const int M = (rf + 1) & ~1;  // an odd count is paired with B's zero column rf
+  const int M = (rf + 1) & ~1;
   int sweeps = 0;
   if (M >= 2) {
     const int np = M >> 1, rounds = M - 1, grp = tid >> 3, sub = tid & 7;
@@ -141,13 +160,20 @@ __global__ __launch_bounds__(256) void k_consolidate(ConsolidateArgs a) {
         for (int p = grp; p < np; p += kCT / 8) {
           const int ci = p == 0 ? k : (k + p) % (M - 1);
           const int cj = p == 0 ? M - 1 : (k - p + (M - 1)) % (M - 1);
-          float *x = B + (size_t)ci * dk, *y = B + (size_t)cj * dk;
+          float *x = A + (size_t)ci * bs, *y = A + (size_t)cj * bs;
+          float xr[KE], yr[KE];
+#pragma unroll
+          for (int t = 0; t < KE; ++t) {  // all loads in flight at once (clamped index, then select)
+            const int e = sub + 8 * t, ec = e < dk ? e : 0;
+            xr[t] = self(e < dk, x[ec]);
+            yr[t] = self(e < dk, y[ec]);
+          }
           float aa = 0.f, bb = 0.f, gg = 0.f;
-          for (int e = sub; e < dk; e += 8) {
-            const float xe = x[e], ye = y[e];
-            aa = fmaf(xe, xe, aa);
-            bb = fmaf(ye, ye, bb);
-            gg = fmaf(xe, ye, gg);
+#pragma unroll
+          for (int t = 0; t < KE; ++t) {
+            aa = fmaf(xr[t], xr[t], aa);
+            bb = fmaf(yr[t], yr[t], bb);
+            gg = fmaf(xr[t], yr[t], gg);
           }
           aa = group_sum<8>(aa);
           bb = group_sum<8>(bb);
@@ -160,16 +186,25 @@ __global__ __launch_bounds__(256) void k_consolidate(ConsolidateArgs a) {
             const float t = az > 1e10f ? 0.5f * __builtin_amdgcn_rcpf(zeta)
                                        : copysignf(__builtin_amdgcn_rcpf(az + __builtin_amdgcn_sqrtf(fmaf(zeta, zeta, 1.f))), zeta);
             const float c = __builtin_amdgcn_rsqf(fmaf(t, t, 1.f)), sn = c * t;
-            for (int e = sub; e < dk; e += 8) {
-              const float xe = x[e], ye = y[e];
-              x[e] = c * xe - sn * ye;
-              y[e] = sn * xe + c * ye;
+            float *yx = Y + (size_t)ci * ys, *yy = Y + (size_t)cj * ys;
+            float ux[KE], uy[KE];
+#pragma unroll
+            for (int q = 0; q < KE; ++q) {
+              const int e = sub + 8 * q, ec = e < rf ? e : 0;
+              ux[q] = yx[ec];
+              uy[q] = yy[ec];
             }
-            float *yx = Y + (size_t)ci * F2, *yy = Y + (size_t)cj * F2;
-            for (int e = sub; e < rf; e += 8) {
-              const float xe = yx[e], ye = yy[e];
-              yx[e] = c * xe - sn * ye;
-              yy[e] = sn * xe + c * ye;
+#pragma unroll
+            for (int q = 0; q < KE; ++q) {
+              const int e = sub + 8 * q;
+              if (e < dk) {
+                x[e] = c * xr[q] - sn * yr[q];
+                y[e] = sn * xr[q] + c * yr[q];
+              }
+              if (e < rf) {
+                yx[e] = c * ux[q] - sn * uy[q];
+                yy[e] = sn * ux[q] + c * uy[q];
+              }
             }
             if (sub == 0) *fl = 1;
           }
@@ -185,7 +220,7 @@ __global__ __launch_bounds__(256) void k_consolidate(ConsolidateArgs a) {
 
   // ---- 5. norms, order, truncation, in-place write -------------------------------------------
   for (int j = w; j < rf; j += 4) {
-    const float *bj = B + (size_t)j * dk;
+    const float *bj = A + (size_t)j * bs;
     float x = 0.f;
     for (int e = lane; e < dk; e += 64) x = fmaf(bj[e], bj[e], x);
     x = wave_sum_u(x);
@@ -206,16 +241,23 @@ __global__ __launch_bounds__(256) void k_consolidate(ConsolidateArgs a) {
   __syncthreads();
   for (int e = tid; e < kept * dk; e += kCT) {
     const int k = e / dk, i = e - k * dk, j = perm[k];
-    a.frz.u[wrap(off_f + k, capF) * dk + i] = B[(size_t)j * dk + i] * (1.0f / sg[j]);
-  }
-  for (int e = tid; e < kept * dv; e += kCT) {
-    const int k = e / dv, i = e - k * dv, j = perm[k];
-    const float *yj = Y + (size_t)j * F2;
-    float acc = 0.f;
-    for (int c = 0; c < rf; ++c) acc = fmaf(Q[(size_t)c * dv + i], yj[c], acc);
-    a.frz.v[wrap(off_f + k, capF) * dv + i] = acc;
+    a.frz.u[wrap(off_f + k, capF) * dk + i] = A[(size_t)j * bs + i] * (1.0f / sg[j]);
   }
   if (tid < kept) a.frz.s[wrap(off_f + tid, capF)] = sg[perm[tid]];
+  __syncthreads();  // B is consumed: bring Q back into A
+  for (int e = tid; e < rf * dv4; e += kCT) {
+    const int j = e / dv4, c = e - j * dv4;
+    st4(A + (size_t)j * dv + 4 * c, ld4(a.frz.v + wrap(off_f + j, capF) * dv + 4 * c));
+  }
+  __syncthreads();
+  for (int e = tid; e < kept * dv; e += kCT) {
+    const int k = e / dv, i = e - k * dv, j = perm[k];
+    const float *yj = Y + (size_t)j * ys;
+    float acc = 0.f;
+#pragma unroll 8
+    for (int c = 0; c < rf; ++c) acc = fmaf(A[(size_t)c * dv + i], yj[c], acc);
+    a.frz.v[wrap(off_f + k, capF) * dv + i] = acc;
+  }
   if (tid == 0) {
     a.meta[s].packed = meta_pack(ra, kept, n, meta_flags(packed));
     const unsigned long long f = (unsigned long long)rf * rf;
@@ -232,15 +274,22 @@ __global__ __launch_bounds__(256) void k_consolidate(ConsolidateArgs a) {
 }  // namespace
 
 size_t consolidate_lds_bytes(int dk, int dv, int fmax) {
-  const size_t F2 = (size_t)((fmax + 1) & ~1);
-  return sizeof(float) * (F2 * dk + (size_t)fmax * dv + F2 * F2 + 3 * F2 + 4);
+  const int F2 = (fmax + 1) & ~1, bs = bank_stride(dk);
+  return sizeof(float) * ((size_t)F2 * (bs > dv ? bs : dv) + (size_t)F2 * bank_stride(F2) + 3 * (size_t)F2 + 4);
 }
 
 hipError_t launch_consolidate(const ConsolidateArgs &a, hipStream_t st) {
   if (a.n_members <= 0 || a.fmax <= 0) return hipSuccess;
   const size_t sh = consolidate_lds_bytes(a.dk, a.dv, a.fmax);
   if (sh > kConsolidateLdsMax) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_consolidate, dim3((unsigned)a.n_members), dim3(kCT), sh, st, a);
+  const int need = a.dk > a.fmax ? a.dk : a.fmax;  // elements of a column pair: 8 lanes x KE
+  const dim3 g((unsigned)a.n_members), b(kCT);
+  if (need <= 16) hipLaunchKernelGGL(k_consolidate<2>, g, b, sh, st, a);
+  else if (need <= 32) hipLaunchKernelGGL(k_consolidate<4>, g, b, sh, st, a);
+  else if (need <= 64) hipLaunchKernelGGL(k_consolidate<8>, g, b, sh, st, a);
+  else if (need <= 128) hipLaunchKernelGGL(k_consolidate<16>, g, b, sh, st, a);
+  else if (need <= 256) hipLaunchKernelGGL(k_consolidate<32>, g, b, sh, st, a);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
