@@ -63,6 +63,9 @@ def _load():
     lib.orc_readout.argtypes = [ctypes.c_void_p, _dp, _dp, ctypes.c_int]
     lib.orc_compact.restype = ctypes.c_int64
     lib.orc_compact.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64), ctypes.c_int64, ctypes.c_int]
+    lib.orc_round_fp16.restype = ctypes.c_double
+    lib.orc_round_fp16.argtypes = [ctypes.c_double]
+    lib.orc_set_factor_fp16.argtypes = [ctypes.c_void_p, ctypes.c_int]
     lib.orc_consolidate.restype = ctypes.c_int64
     lib.orc_consolidate.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64), ctypes.c_int64, ctypes.c_int]
     lib.orc_householder_qr.argtypes = [ctypes.c_int, ctypes.c_int, _dp, _dp, _dp]
@@ -156,6 +159,11 @@ def rsvd_init(S, omega, eps, iters=2, max_rank=None):
     return U[:R].copy(), V[:R].copy(), sig[:R].copy()
 
 
+def round_fp16(x: float) -> float:
+    """binary16 rounding (nearest, ties to even) of one value, as the oracle stores fp16 factors."""
+    return float(_load().orc_round_fp16(float(x)))
+
+
 def schedule_due(step: int, K: int, offsets) -> list:
     offs = np.ascontiguousarray(offsets, dtype=np.int32)
     out = np.zeros(max(1, len(offs)), dtype=np.int32)
@@ -186,13 +194,14 @@ class OracleState:
 class OraclePool:
     """A pool of N states held by the C oracle."""
 
-    def __init__(self, n_states, d_k, d_v, K=8, r=8, L=-1, promote=True):
+    def __init__(self, n_states, d_k, d_v, K=8, r=8, L=-1, promote=True, factor_fp16=False):
         lib = _load()
         self._lib = lib
         self.N, self.d_k, self.d_v, self.K, self.r = int(n_states), int(d_k), int(d_v), int(K), int(r)
         self._p = lib.orc_create(self.N, self.d_k, self.d_v, self.K, self.r, int(L), int(bool(promote)))
         if not self._p:
             raise MemoryError("orc_create failed")
+        lib.orc_set_factor_fp16(self._p, int(bool(factor_fp16)))
         self.L = int(lib.orc_dense_limit(self._p))
 
     def close(self):

@@ -30,6 +30,10 @@
  *             (SinkState, 4.2 "Randomized SVD initialization after prefill").
  *   consolidate  exact SVD of the frozen part, drop sigma < eps * sigma_0
  *             (SinkState, 4.3 "Asynchronous CPU Consolidation", Figure 7(a)).
+ *   fp16      optional fp16 factor storage (SEED, section 6 "Lower precision
+ *             composes"): every factor vector written (initial factors,
+ *             compaction and consolidation results) is rounded to binary16;
+ *             sigma and the pad keep full precision.
  *
  * Decay is applied literally, every step, to every sigma and pad weight.  QR
  * is Householder, the small SVD is cyclic one-sided (Hestenes) Jacobi, both
@@ -67,6 +71,7 @@ typedef struct {
 typedef struct {
   int64_t N;
   int d_k, d_v, K, r, L, promote;
+  int fp16;     /* factor vectors stored in fp16: rounded whenever they are written */
   orc_state *st;
 } orc_pool;
 
@@ -78,6 +83,31 @@ static double dot(const double *a, const double *b, int n) {
   for (int i = 0; i < n; ++i) s += a[i] * b[i];
   return s;
 }
+
+/* IEEE 754 binary16 rounding of x, round to nearest with ties to even
+ * (11-bit significand; normal exponents -14..15, subnormal step 2^-24;
+ * magnitudes that round to 2^16 or above become infinite).  Used for fp16
+ * factor storage (SEED section 6: fp16 factors with an fp32 pad). */
+double orc_round_fp16(double x) {
+  if (x == 0.0 || x != x) return x;
+  double a = fabs(x);
+  if (a >= 65520.0) return x > 0 ? INFINITY : -INFINITY;
+  int e;
+  frexp(a, &e);               /* a = m 2^e, m in [0.5, 1): the leading bit is 2^(e-1) */
+  int q = e - 11;             /* quantum 2^(e-1-10) */
+  if (q < -24) q = -24;       /* subnormal range */
+  double y = ldexp(a, -q);    /* exact: a power-of-two scaling */
+  double f = floor(y), r = y - f;
+  if (r > 0.5 || (r == 0.5 && fmod(f, 2.0) != 0.0)) f += 1.0;
+  double out = ldexp(f, q);
+  return x < 0 ? -out : out;
+}
+
+static void round_rows(double *A, size_t n) {
+  for (size_t i = 0; i < n; ++i) A[i] = orc_round_fp16(A[i]);
+}
+
+void orc_set_factor_fp16(orc_pool *p, int on) { p->fp16 = on ? 1 : 0; }
 
 static int ensure_cap(orc_state *s, int need, int d_k, int d_v) {
   if (need <= s->cap) return 0;
@@ -365,6 +395,10 @@ int orc_set_state(orc_pool *p, int64_t s, int rule, double eps, int R, const dou
   }
   free(ord);
   x->R = R;
+  if (p->fp16) {
+    round_rows(x->U, (size_t)R * dk);
+    round_rows(x->V, (size_t)R * dv);
+  }
   for (int j = 0; j < n; ++j) {
     memcpy(x->PK + (size_t)j * dk, PK + (size_t)j * dk, dk * sizeof(double));
     memcpy(x->PW + (size_t)j * dv, PW + (size_t)j * dv, dv * sizeof(double));
@@ -588,6 +622,10 @@ static int compact_one(orc_pool *p, orc_state *x) {
       }
     }
     if (ensure_cap(x, out, dk, dv)) goto done;
+    if (p->fp16) {  /* factors are stored in fp16 when a compaction writes them */
+      round_rows(nU, (size_t)out * dk);
+      round_rows(nV, (size_t)out * dv);
+    }
     memcpy(x->U, nU, (size_t)out * dk * sizeof(double));
     memcpy(x->V, nV, (size_t)out * dv * sizeof(double));
     memcpy(x->sig, ns, (size_t)out * sizeof(double));
@@ -673,6 +711,10 @@ static int consolidate_one(orc_pool *p, orc_state *x) {
       }
     }
     x->R = ra + out;
+    if (p->fp16) {
+      round_rows(x->U + (size_t)ra * dk, (size_t)out * dk);
+      round_rows(x->V + (size_t)ra * dv, (size_t)out * dv);
+    }
     x->bound += sqrt(dropped2);
     rc = 0;
   }
