@@ -216,6 +216,8 @@ def main():
     ap.add_argument("--consolidate", type=int, default=0,
                     help="groups consolidated from the wait queue after a step's compactions (0: off)")
     ap.add_argument("--consolidate-period", type=int, default=1, help="steps between consolidation calls")
+    ap.add_argument("--factor-fp16", action="store_true",
+                    help="store the factor vectors in fp16 (pad, sigma, dense region and arithmetic stay fp32)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the eager-versus-graph step timing and the initialization timing")
     args = ap.parse_args()
@@ -246,8 +248,9 @@ def main():
 
     cons = (max(0, args.consolidate), max(1, args.consolidate_period))
     # warmup on a scratch pool of the same workload
+    fkw = {"factor_fp16": True} if args.factor_fp16 else {}
     if args.warmup > 0:
-        pool = _pool(ss, w, init)
+        pool = _pool(ss, w, init, **fkw)
         wchunk = max(1, min(args.chunk, int(16e9 // (w.n_states * (2 * w.d_k + w.d_v + 2) * 4))))
         for c0 in range(0, args.warmup, wchunk):
             xs = [gen.generate(t) for t in range(c0 + 1, min(args.warmup, c0 + wchunk) + 1)]
@@ -258,7 +261,7 @@ def main():
         log(f"[bench] warmup {args.warmup} steps done")
 
     # the timed job
-    pool = _pool(ss, w, init)
+    pool = _pool(ss, w, init, **fkw)
     st0 = ss.pool_stats(pool)
     ss.pool_timing(pool, True)
     step_ms = []
@@ -380,7 +383,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.description}; {w.n_requests} requests x {w.n_layers} layers x "
                                f"{w.n_heads} heads, K={w.K}, r={w.r}, stagger={w.stagger}, whole {K_steps}-step job",
-                   "n_states": w.n_states, "d_k": w.d_k, "d_v": w.d_v},
+                   "n_states": w.n_states, "d_k": w.d_k, "d_v": w.d_v,
+                   "factor_storage": "fp16" if args.factor_fp16 else "fp32"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBS, "traffic": _traffic(dom, w.name),
                      "algorithmic_bytes_per_launch": bytes_k[dom] / max(1, kn[dom])},

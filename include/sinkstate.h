@@ -84,6 +84,16 @@ typedef struct {
                                  can ever need when that fits in a quarter of the free device
                                  memory, else a smaller start.  The rings grow on their own (see
                                  ss_compact); a growth is a device allocation. */
+  int32_t factor_fp16;        /* 1: the component vectors u, v are stored in IEEE binary16
+                                 ([SEED] 6 "Lower precision composes": fp16 factors, rounded
+                                 when a compression writes them, while the newest columns, the
+                                 pad, stay in fp32).  Rounding (to nearest, ties to even) happens
+                                 when create stores the initial factors and whenever a
+                                 compaction or a consolidation writes factors; sigma, the pad,
+                                 the dense region and all arithmetic stay fp32, and the dense
+                                 test keeps the same L.  A stored component then takes
+                                 2 (d_k + d_v) + 4 bytes instead of 4 (d_k + d_v + 1).
+                                 0: fp32 factors.  Other values: SS_ERR_ARG. */
 } ss_pool_desc;
 
 /* Initial states, host memory, copied during create.  Components of state s
@@ -310,7 +320,8 @@ int32_t ss_dense_rank_limit(int32_t d_k, int32_t d_v);
 enum {
   SS_DECODE_FACTORED = 0,       /* factors + pad */
   SS_DECODE_DENSE_BUFFERED = 1, /* dense region of a factored pool: H + pad */
-  SS_DECODE_DENSE_PLAIN = 2     /* force_dense pool (the dense baseline) */
+  SS_DECODE_DENSE_PLAIN = 2,    /* force_dense pool (the dense baseline) */
+  SS_DECODE_FACTORED_FP16 = 3   /* factors + pad in a pool with factor_fp16 = 1 */
 };
 
 /* Algorithmic bytes one decode_step moves for one state with n_comp
@@ -321,7 +332,9 @@ enum {
  * 16-byte slot record, H (4 d_k d_v bytes), the slots and the inputs;
  * writes the record, o, and one slot, or H when the step fills the pad
  * (n_pad + 1 >= K).  DENSE_PLAIN: reads the slot record and reads and
- * writes H every step.  Returns 0 for an unknown kind. */
+ * writes H every step.  FACTORED_FP16: as FACTORED with 2 (d_k + d_v) + 4
+ * bytes per stored component (pad slots stay 4 (d_k + d_v + 1)).  Returns 0
+ * for an unknown kind. */
 uint64_t ss_decode_bytes_per_state(int32_t d_k, int32_t d_v, int32_t pad_slots, int32_t n_comp, int32_t n_pad,
                                    int32_t rule, int32_t kind);
 

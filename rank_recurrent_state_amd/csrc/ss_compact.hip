@@ -25,6 +25,8 @@
 // matrices in LDS (SinkState 4.4: fused chains of factor algebra).
 #include <hipcub/hipcub.hpp>
 
+#include <type_traits>
+
 #include "ss_internal.h"
 #include "ss_linalg.h"
 #include "ss_wave.h"
@@ -39,20 +41,20 @@ constexpr int kOffRl = 0, kOffRr = 256, kOffCm = 512, kOffVh = 768, kOffScw = 10
               kOffPerm = 1072, kOffPosL = 1088, kOffFs = 1104, kOffPosF = kOffFs + kMaxFrozen,
               kLdsPerWave = kOffPosF + kMaxFrozen;
 
-// copy one component (u, v) with float4 lanes
-__device__ __forceinline__ void copy_comp(const float *su, const float *sv, float *du, float *dv_, int dk, int dv,
-                                          int lane) {
+// copy one fp32 component (u, v) into factor storage of type F, with float4 lanes
+template <typename F>
+__device__ __forceinline__ void copy_comp(const float *su, const float *sv, F *du, F *dv_, int dk, int dv, int lane) {
   const int dk4 = dk >> 2, tot = dk4 + (dv >> 2);
   for (int e = lane; e < tot; e += 64) {
-    if (e < dk4) st4(du + 4 * e, ld4(su + 4 * e));
-    else st4(dv_ + 4 * (e - dk4), ld4(sv + 4 * (e - dk4)));
+    if (e < dk4) stf4(du + 4 * e, ld4(su + 4 * e));
+    else stf4(dv_ + 4 * (e - dk4), ld4(sv + 4 * (e - dk4)));
   }
 }
 
 // Copy `cnt` components (u, v) starting at ring position c0 of arena `src`
 // to the positions dst_of(f) (a component for which it returns false is dropped).
 // All lanes take float4 pieces of consecutive components, UNC pieces in flight.
-template <typename DstOf>
+template <typename F, typename DstOf>
 __device__ __forceinline__ void copy_comps(const Arena &src, int64_t c0, int cnt, int dk, int dv, int lane,
                                            DstOf dst_of) {
   constexpr int UNC = 8;
@@ -66,25 +68,25 @@ __device__ __forceinline__ void copy_comps(const Arena &src, int64_t c0, int cnt
       const int ec = e < n ? e : n - 1;  // clamped (n >= 1 inside the loop)
       const int f = ec / tot4, c = ec - f * tot4;
       const int64_t cs = wrap(c0 + f, src.cap);
-      const float *p = c < dk4 ? src.u + cs * dk + 4 * c : src.v + cs * dv + 4 * (c - dk4);
-      x[q] = ld4(p);
+      const F *p = c < dk4 ? src.U<F>() + cs * dk + 4 * c : src.V<F>() + cs * dv + 4 * (c - dk4);
+      x[q] = ldf4(p);
     }
 #pragma unroll
     for (int q = 0; q < UNC; ++q) {
       const int e = e0 + q * 64 + lane;
       if (e < n) {
         const int f = e / tot4, c = e - f * tot4;
-        float *du, *dvp;
+        F *du, *dvp;
         if (dst_of(f, du, dvp)) {
-          if (c < dk4) st4(du + 4 * c, x[q]);
-          else st4(dvp + 4 * (c - dk4), x[q]);
+          if (c < dk4) stf4(du + 4 * c, x[q]);
+          else stf4(dvp + 4 * (c - dk4), x[q]);
         }
       }
     }
   }
 }
 
-template <int NS>
+template <int NS, typename F>
 __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   __shared__ float lds[4][kLdsPerWave];
   __shared__ int wg_cnt[4][2];
@@ -140,13 +142,24 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
       const int j = valid ? jj : mcol - 1;  // clamped: the loads stay in bounds (mcol >= 1 here)
       const bool isact = j < ra;
       const int64_t ca = wrap(off_a + j, capA);
-      const float *su = isact ? a.act.u + ca * dk : a.pk + ((int64_t)s * K + (j - ra)) * dk;
-      const float *sv = isact ? a.act.v + ca * dv : a.pw + ((int64_t)s * K + (j - ra)) * dv;
+      if (std::is_same<F, float>::value || !isact) {
+        const float *su = isact ? a.act.U<float>() + ca * dk : a.pk + ((int64_t)s * K + (j - ra)) * dk;
+        const float *sv = isact ? a.act.V<float>() + ca * dv : a.pw + ((int64_t)s * K + (j - ra)) * dv;
 #pragma unroll
-      for (int t = 0; t < NS; ++t) {
-        const int row = lane + 64 * t;
-        uc[jj][t] = self(valid && row < dk, su[row < dk ? row : dk - 1]);
-        vc[jj][t] = self(valid && row < dv, sv[row < dv ? row : dv - 1]);
+        for (int t = 0; t < NS; ++t) {
+          const int row = lane + 64 * t;
+          uc[jj][t] = self(valid && row < dk, su[row < dk ? row : dk - 1]);
+          vc[jj][t] = self(valid && row < dv, sv[row < dv ? row : dv - 1]);
+        }
+      } else {  // fp16 factors (wave-uniform branch)
+        const F *su = a.act.U<F>() + ca * dk;
+        const F *sv = a.act.V<F>() + ca * dv;
+#pragma unroll
+        for (int t = 0; t < NS; ++t) {
+          const int row = lane + 64 * t;
+          uc[jj][t] = self(valid && row < dk, ldf(su + (row < dk ? row : dk - 1)));
+          vc[jj][t] = self(valid && row < dv, ldf(sv + (row < dv ? row : dv - 1)));
+        }
       }
     }
     if (lane < kMaxM) {
@@ -266,16 +279,16 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
 
   // ---- phase B: write the new components and the record ------------------------------------
   if (!work) {  // nothing buffered: the components move unchanged, sigma takes Gamma in
-    copy_comps(a.act, off_a, ra, dk, dv, lane, [&](int f, float *&du, float *&dvp) {
+    copy_comps<F>(a.act, off_a, ra, dk, dv, lane, [&](int f, F *&du, F *&dvp) {
       const int64_t c = wrap(dst_a + f, capA);
-      du = a.act.u + c * dk;
-      dvp = a.act.v + c * dv;
+      du = a.act.U<F>() + c * dk;
+      dvp = a.act.V<F>() + c * dv;
       return true;
     });
-    copy_comps(a.frz, off_f, rf, dk, dv, lane, [&](int f, float *&du, float *&dvp) {
+    copy_comps<F>(a.frz, off_f, rf, dk, dv, lane, [&](int f, F *&du, F *&dvp) {
       const int64_t c = wrap(dst_f + f, capF);
-      du = a.frz.u + c * dk;
-      dvp = a.frz.v + c * dv;
+      du = a.frz.U<F>() + c * dk;
+      dvp = a.frz.V<F>() + c * dv;
       return true;
     });
     for (int f = lane; f < ra; f += 64) a.act.s[wrap(dst_a + f, capA)] = a.act.s[wrap(off_a + f, capA)] * gamma;
@@ -291,11 +304,11 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
     return;
   }
   // merged position pos -> slot of the new active (pos < r) or frozen component
-  auto slot_u = [&](int pos) -> float * {
-    return pos < r ? a.act.u + wrap(dst_a + pos, capA) * dk : a.frz.u + wrap(dst_f + pos - r, capF) * dk;
+  auto slot_u = [&](int pos) -> F * {
+    return pos < r ? a.act.U<F>() + wrap(dst_a + pos, capA) * dk : a.frz.U<F>() + wrap(dst_f + pos - r, capF) * dk;
   };
-  auto slot_v = [&](int pos) -> float * {
-    return pos < r ? a.act.v + wrap(dst_a + pos, capA) * dv : a.frz.v + wrap(dst_f + pos - r, capF) * dv;
+  auto slot_v = [&](int pos) -> F * {
+    return pos < r ? a.act.V<F>() + wrap(dst_a + pos, capA) * dv : a.frz.V<F>() + wrap(dst_f + pos - r, capF) * dv;
   };
   auto slot_s = [&](int pos) -> float * {
     return pos < r ? a.act.s + wrap(dst_a + pos, capA) : a.frz.s + wrap(dst_f + pos - r, capF);
@@ -322,18 +335,18 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
         ov[t] = fmaf(vc[tt][t], cv, ov[t]);
       }
     }
-    float *du = slot_u(pos);
-    float *dvv = slot_v(pos);
+    F *du = slot_u(pos);
+    F *dvv = slot_v(pos);
 #pragma unroll
-    for (int t = 0; t < NS; ++t) {
+    for (int t = 0; t < NS; ++t) {  // rounded to the storage type here (fp16 factors: at every compaction)
       const int row = lane + 64 * t;
-      if (row < dk) du[row] = ou[t];
-      if (row < dv) dvv[row] = ov[t];
+      if (row < dk) stf(du + row, ou[t]);
+      if (row < dv) stf(dvv + row, ov[t]);
     }
   }
   if (lane < kl && posL[lane] < total) *slot_s(posL[lane]) = sgs[lane];
   // kept frozen components: copied, sigma scaled by Gamma
-  copy_comps(a.frz, off_f, kf, dk, dv, lane, [&](int f, float *&du, float *&dvp) {
+  copy_comps<F>(a.frz, off_f, kf, dk, dv, lane, [&](int f, F *&du, F *&dvp) {
     const int pos = posF[f];
     if (pos >= total) return false;
     du = slot_u(pos);
@@ -373,6 +386,7 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
 constexpr int kMatCH = 16;
 constexpr int kMatRows = 8;
 
+template <typename F>
 __global__ __launch_bounds__(256) void k_materialize(MaterializeArgs a) {
   extern __shared__ float smem[];
   __shared__ int s_slot;
@@ -402,15 +416,16 @@ __global__ __launch_bounds__(256) void k_materialize(MaterializeArgs a) {
       n2 = (int)meta_rf(m.packed);
       scale = m.gamma;
     }
-    auto comp_u = [&](int comp) -> const float * {
-      if (a.csr_off) return a.csr_u + (o0 + comp) * dk;
-      return comp < n1 ? a.act.u + wrap(m.off_a + comp, a.act.cap) * dk
-                       : a.frz.u + wrap(m.off_f + comp - n1, a.frz.cap) * dk;
+    // element i of u (or v) of component comp
+    auto comp_u = [&](int comp, int i) -> float {
+      if (a.csr_off) return a.csr_u[(o0 + comp) * dk + i];
+      return ldf(comp < n1 ? a.act.U<F>() + wrap(m.off_a + comp, a.act.cap) * dk + i
+                           : a.frz.U<F>() + wrap(m.off_f + comp - n1, a.frz.cap) * dk + i);
     };
-    auto comp_v = [&](int comp) -> const float * {
-      if (a.csr_off) return a.csr_v + (o0 + comp) * dv;
-      return comp < n1 ? a.act.v + wrap(m.off_a + comp, a.act.cap) * dv
-                       : a.frz.v + wrap(m.off_f + comp - n1, a.frz.cap) * dv;
+    auto comp_v = [&](int comp, int j) -> float {
+      if (a.csr_off) return a.csr_v[(o0 + comp) * dv + j];
+      return ldf(comp < n1 ? a.act.V<F>() + wrap(m.off_a + comp, a.act.cap) * dv + j
+                           : a.frz.V<F>() + wrap(m.off_f + comp - n1, a.frz.cap) * dv + j);
     };
     auto comp_s = [&](int comp) -> float {
       if (a.csr_off) return a.csr_s[o0 + comp];
@@ -450,11 +465,11 @@ __global__ __launch_bounds__(256) void k_materialize(MaterializeArgs a) {
         __syncthreads();
         for (int e = t; e < kMatCH * dk; e += 256) {
           const int cc = e / dk, i = e - cc * dk, comp = c0 + cc;
-          su[e] = comp < total ? comp_u(comp)[i] : 0.f;
+          su[e] = comp < total ? comp_u(comp, i) : 0.f;
         }
         for (int e = t; e < kMatCH * dv; e += 256) {
           const int cc = e / dv, j = e - cc * dv, comp = c0 + cc;
-          sv[e] = comp < total ? comp_v(comp)[j] : 0.f;
+          sv[e] = comp < total ? comp_v(comp, j) : 0.f;
         }
         if (t < kMatCH) {
           const int comp = c0 + t;
@@ -503,6 +518,7 @@ __global__ __launch_bounds__(256) void k_materialize(MaterializeArgs a) {
 
 // Pool creation: place the CSR components of every state into its slice of
 // the group's first segments, or queue it for the dense region.
+template <typename F>
 __global__ __launch_bounds__(256) void k_scatter(ScatterArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t s = (int64_t)blockIdx.x * 4 + uniform(threadIdx.x >> 6);
@@ -530,9 +546,9 @@ __global__ __launch_bounds__(256) void k_scatter(ScatterArgs a) {
   for (int c = 0; c < R; ++c) {
     const float *su = a.csr_u + (o0 + c) * dk, *sv = a.csr_v + (o0 + c) * dv;
     const bool isa = c < ra;
-    float *du = isa ? a.act.u + (dst_a + c) * dk : a.frz.u + (dst_f + c - ra) * dk;
-    float *dvv = isa ? a.act.v + (dst_a + c) * dv : a.frz.v + (dst_f + c - ra) * dv;
-    copy_comp(su, sv, du, dvv, dk, dv, lane);
+    F *du = isa ? a.act.U<F>() + (dst_a + c) * dk : a.frz.U<F>() + (dst_f + c - ra) * dk;
+    F *dvv = isa ? a.act.V<F>() + (dst_a + c) * dv : a.frz.V<F>() + (dst_f + c - ra) * dv;
+    copy_comp<F>(su, sv, du, dvv, dk, dv, lane);
     if (lane == 0) (isa ? a.act.s[dst_a + c] : a.frz.s[dst_f + c - ra]) = a.csr_s[o0 + c];
   }
   if (lane == 0) {
@@ -592,6 +608,7 @@ __global__ void k_ring_end(Ring *ra, Ring *rf, unsigned long long *seg_a, unsign
 }
 
 // one wavefront per state: copy its live components to the new rings
+template <typename F>
 __global__ __launch_bounds__(256) void k_repack(RepackArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t s = (int64_t)blockIdx.x * 4 + uniform(threadIdx.x >> 6);
@@ -602,14 +619,14 @@ __global__ __launch_bounds__(256) void k_repack(RepackArgs a) {
   const uint32_t packed = (uint32_t)uniform((int)m.packed);
   const int ra = meta_ra(packed), rf = meta_rf(packed);
   const int dk = a.dk, dv = a.dv;
-  copy_comps(a.src_a, m.off_a, ra, dk, dv, lane, [&](int f, float *&du, float *&dvp) {
-    du = a.dst_a.u + wrap(na + f, a.dst_a.cap) * dk;
-    dvp = a.dst_a.v + wrap(na + f, a.dst_a.cap) * dv;
+  copy_comps<F>(a.src_a, m.off_a, ra, dk, dv, lane, [&](int f, F *&du, F *&dvp) {
+    du = a.dst_a.U<F>() + wrap(na + f, a.dst_a.cap) * dk;
+    dvp = a.dst_a.V<F>() + wrap(na + f, a.dst_a.cap) * dv;
     return true;
   });
-  copy_comps(a.src_f, m.off_f, rf, dk, dv, lane, [&](int f, float *&du, float *&dvp) {
-    du = a.dst_f.u + wrap(nf + f, a.dst_f.cap) * dk;
-    dvp = a.dst_f.v + wrap(nf + f, a.dst_f.cap) * dv;
+  copy_comps<F>(a.src_f, m.off_f, rf, dk, dv, lane, [&](int f, F *&du, F *&dvp) {
+    du = a.dst_f.U<F>() + wrap(nf + f, a.dst_f.cap) * dk;
+    dvp = a.dst_f.V<F>() + wrap(nf + f, a.dst_f.cap) * dv;
     return true;
   });
   for (int f = lane; f < ra; f += 64) a.dst_a.s[wrap(na + f, a.dst_a.cap)] = a.src_a.s[wrap(m.off_a + f, a.src_a.cap)];
@@ -704,10 +721,17 @@ hipError_t launch_compact(const CompactArgs &a, hipStream_t st) {
   if (a.n_members <= 0) return hipSuccess;
   const dim3 grid((unsigned)((a.n_members + 3) / 4)), block(256);
   const int d = a.dk > a.dv ? a.dk : a.dv;
-  if (d <= 64) hipLaunchKernelGGL((k_compact<1>), grid, block, 0, st, a);
-  else if (d <= 128) hipLaunchKernelGGL((k_compact<2>), grid, block, 0, st, a);
-  else if (d <= 256) hipLaunchKernelGGL((k_compact<4>), grid, block, 0, st, a);
-  else return hipErrorInvalidValue;
+  const int ns = d <= 64 ? 1 : d <= 128 ? 2 : d <= 256 ? 4 : 0;
+  if (ns == 0) return hipErrorInvalidValue;
+  if (a.act.half) {
+    if (ns == 1) hipLaunchKernelGGL((k_compact<1, _Float16>), grid, block, 0, st, a);
+    else if (ns == 2) hipLaunchKernelGGL((k_compact<2, _Float16>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_compact<4, _Float16>), grid, block, 0, st, a);
+  } else {
+    if (ns == 1) hipLaunchKernelGGL((k_compact<1, float>), grid, block, 0, st, a);
+    else if (ns == 2) hipLaunchKernelGGL((k_compact<2, float>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_compact<4, float>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 
@@ -715,13 +739,16 @@ hipError_t launch_materialize(const MaterializeArgs &a, int64_t grid_upper, hipS
   if (grid_upper <= 0) return hipSuccess;
   const unsigned grid = (unsigned)(grid_upper < 2048 ? grid_upper : 2048);
   const size_t sh = sizeof(float) * (size_t)kMatCH * (a.dk + a.dv + 1);
-  hipLaunchKernelGGL(k_materialize, dim3(grid), dim3(256), sh, st, a);
+  if (a.act.half) hipLaunchKernelGGL(k_materialize<_Float16>, dim3(grid), dim3(256), sh, st, a);
+  else hipLaunchKernelGGL(k_materialize<float>, dim3(grid), dim3(256), sh, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_scatter(const ScatterArgs &a, hipStream_t st) {
   if (a.N <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_scatter, dim3((unsigned)((a.N + 3) / 4)), dim3(256), 0, st, a);
+  const dim3 grid((unsigned)((a.N + 3) / 4)), block(256);
+  if (a.act.half) hipLaunchKernelGGL(k_scatter<_Float16>, grid, block, 0, st, a);
+  else hipLaunchKernelGGL(k_scatter<float>, grid, block, 0, st, a);
   return hipGetLastError();
 }
 
@@ -771,7 +798,9 @@ hipError_t launch_ring_layout(const LayoutArgs &a, hipStream_t st) {
 
 hipError_t launch_repack(const RepackArgs &a, hipStream_t st) {
   if (a.N <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_repack, dim3((unsigned)((a.N + 3) / 4)), dim3(256), 0, st, a);
+  const dim3 grid((unsigned)((a.N + 3) / 4)), block(256);
+  if (a.src_a.half) hipLaunchKernelGGL(k_repack<_Float16>, grid, block, 0, st, a);
+  else hipLaunchKernelGGL(k_repack<float>, grid, block, 0, st, a);
   return hipGetLastError();
 }
 

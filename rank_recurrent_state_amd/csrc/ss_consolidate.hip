@@ -31,6 +31,8 @@
 // Column strides in LDS are odd multiples of 8 floats, so the 8 lanes of a
 // Jacobi pair and the 8 pairs of a wavefront (consecutive columns) fall in
 // distinct banks.
+#include <type_traits>
+
 #include "ss_internal.h"
 #include "ss_linalg.h"
 #include "ss_wave.h"
@@ -46,7 +48,7 @@ constexpr int kConsSweeps = 32;  // Jacobi sweep limit
 __host__ __device__ inline int bank_stride(int d) { return ((d + 7) / 8 | 1) * 8; }
 
 // KE: elements per lane of a Jacobi column pair (8 lanes per pair), KE * 8 >= max(d_k, f)
-template <int KE>
+template <int KE, typename F>
 __global__ __launch_bounds__(256) void k_consolidate(ConsolidateArgs a) {
   extern __shared__ float sm[];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -65,9 +67,16 @@ __global__ __launch_bounds__(256) void k_consolidate(ConsolidateArgs a) {
   int *perm = reinterpret_cast<int *>(dt + F2);       // [F2]
   float *ctl = reinterpret_cast<float *>(perm + F2);  // [2]
   int *flag = reinterpret_cast<int *>(ctl + 2);       // [2]: rotation seen, per sweep parity
+  // where Q is parked: fp32 factors park it in the frozen v slots; fp16 factors would round it,
+  // so they park it in LDS after the other arrays ([F2][d_v])
+  constexpr bool kHalf = !std::is_same<F, float>::value;
+  float *QL = sm + ((reinterpret_cast<float *>(flag + 2) - sm + 3) & ~(ptrdiff_t)3);  // float4-aligned
   const int64_t capF = a.frz.cap;
   const int off_f = uniform(m.off_f);
   const int dk4 = dk >> 2, dv4 = dv >> 2;
+  auto qpark = [&](int j) -> float * {
+    return kHalf ? QL + (size_t)j * dv : reinterpret_cast<float *>(a.frz.V<F>()) + wrap(off_f + j, capF) * dv;
+  };
 
   // ---- 1. stage V_F --------------------------------------------------------------------------
   for (int j = tid; j < rf; j += kCT) sg[j] = a.frz.s[wrap(off_f + j, capF)];
@@ -75,7 +84,7 @@ __global__ __launch_bounds__(256) void k_consolidate(ConsolidateArgs a) {
   if (tid < 2) flag[tid] = 0;
   for (int e = tid; e < rf * dv4; e += kCT) {
     const int j = e / dv4, c = e - j * dv4;
-    st4(A + (size_t)j * dv + 4 * c, ld4(a.frz.v + wrap(off_f + j, capF) * dv + 4 * c));
+    st4(A + (size_t)j * dv + 4 * c, ldf4(a.frz.V<F>() + wrap(off_f + j, capF) * dv + 4 * c));
   }
   __syncthreads();
   float s0 = sg[0];
@@ -118,17 +127,17 @@ __global__ __launch_bounds__(256) void k_consolidate(ConsolidateArgs a) {
     if (tid == 0) Y[(size_t)j * ys + j] = keep ? su : 0.f;
     __syncthreads();
   }
-  // park Q in the frozen v slots (V_F has been consumed)
+  // park Q (V_F has been consumed)
   for (int e = tid; e < rf * dv4; e += kCT) {
     const int j = e / dv4, c = e - j * dv4;
-    st4(a.frz.v + wrap(off_f + j, capF) * dv + 4 * c, ld4(A + (size_t)j * dv + 4 * c));
+    st4(qpark(j) + 4 * c, ld4(A + (size_t)j * dv + 4 * c));
   }
   __syncthreads();
 
   // ---- 3. B = U_F diag(sigma_F) R^T into A, then Y <- I --------------------------------------
   for (int e = tid; e < rf * dk4; e += kCT) {
     const int j = e / dk4, c = e - j * dk4;
-    st4(A + (size_t)j * bs + 4 * c, scale4(sg[j], ld4(a.frz.u + wrap(off_f + j, capF) * dk + 4 * c)));
+    st4(A + (size_t)j * bs + 4 * c, scale4(sg[j], ldf4(a.frz.U<F>() + wrap(off_f + j, capF) * dk + 4 * c)));
   }
   if (rf & 1)  // an odd count is paired with a zero column in the Jacobi
     for (int e = tid; e < dk; e += kCT) A[(size_t)rf * bs + e] = 0.f;
@@ -241,13 +250,13 @@ __global__ __launch_bounds__(256) void k_consolidate(ConsolidateArgs a) {
   __syncthreads();
   for (int e = tid; e < kept * dk; e += kCT) {
     const int k = e / dk, i = e - k * dk, j = perm[k];
-    a.frz.u[wrap(off_f + k, capF) * dk + i] = A[(size_t)j * bs + i] * (1.0f / sg[j]);
+    stf(a.frz.U<F>() + wrap(off_f + k, capF) * dk + i, A[(size_t)j * bs + i] * (1.0f / sg[j]));
   }
   if (tid < kept) a.frz.s[wrap(off_f + tid, capF)] = sg[perm[tid]];
   __syncthreads();  // B is consumed: bring Q back into A
   for (int e = tid; e < rf * dv4; e += kCT) {
     const int j = e / dv4, c = e - j * dv4;
-    st4(A + (size_t)j * dv + 4 * c, ld4(a.frz.v + wrap(off_f + j, capF) * dv + 4 * c));
+    st4(A + (size_t)j * dv + 4 * c, ld4(qpark(j) + 4 * c));
   }
   __syncthreads();
   for (int e = tid; e < kept * dv; e += kCT) {
@@ -256,7 +265,7 @@ __global__ __launch_bounds__(256) void k_consolidate(ConsolidateArgs a) {
     float acc = 0.f;
 #pragma unroll 8
     for (int c = 0; c < rf; ++c) acc = fmaf(A[(size_t)c * dv + i], yj[c], acc);
-    a.frz.v[wrap(off_f + k, capF) * dv + i] = acc;
+    stf(a.frz.V<F>() + wrap(off_f + k, capF) * dv + i, acc);
   }
   if (tid == 0) {
     a.meta[s].packed = meta_pack(ra, kept, n, meta_flags(packed));
@@ -271,26 +280,32 @@ __global__ __launch_bounds__(256) void k_consolidate(ConsolidateArgs a) {
   }
 }
 
+template <typename F>
+hipError_t consolidate_f(const ConsolidateArgs &a, int need, size_t sh, hipStream_t st) {
+  const dim3 g((unsigned)a.n_members), b(kCT);
+  if (need <= 16) hipLaunchKernelGGL((k_consolidate<2, F>), g, b, sh, st, a);
+  else if (need <= 32) hipLaunchKernelGGL((k_consolidate<4, F>), g, b, sh, st, a);
+  else if (need <= 64) hipLaunchKernelGGL((k_consolidate<8, F>), g, b, sh, st, a);
+  else if (need <= 128) hipLaunchKernelGGL((k_consolidate<16, F>), g, b, sh, st, a);
+  else hipLaunchKernelGGL((k_consolidate<32, F>), g, b, sh, st, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
-size_t consolidate_lds_bytes(int dk, int dv, int fmax) {
+size_t consolidate_lds_bytes(int dk, int dv, int fmax, bool half) {
   const int F2 = (fmax + 1) & ~1, bs = bank_stride(dk);
-  return sizeof(float) * ((size_t)F2 * (bs > dv ? bs : dv) + (size_t)F2 * bank_stride(F2) + 3 * (size_t)F2 + 4);
+  return sizeof(float) * ((size_t)F2 * (bs > dv ? bs : dv) + (size_t)F2 * bank_stride(F2) + 3 * (size_t)F2 + 4 +
+                          (half ? (size_t)F2 * dv + 4 : 0));
 }
 
 hipError_t launch_consolidate(const ConsolidateArgs &a, hipStream_t st) {
   if (a.n_members <= 0 || a.fmax <= 0) return hipSuccess;
-  const size_t sh = consolidate_lds_bytes(a.dk, a.dv, a.fmax);
+  const size_t sh = consolidate_lds_bytes(a.dk, a.dv, a.fmax, a.frz.half != 0);
   if (sh > kConsolidateLdsMax) return hipErrorInvalidValue;
   const int need = a.dk > a.fmax ? a.dk : a.fmax;  // elements of a column pair: 8 lanes x KE
-  const dim3 g((unsigned)a.n_members), b(kCT);
-  if (need <= 16) hipLaunchKernelGGL(k_consolidate<2>, g, b, sh, st, a);
-  else if (need <= 32) hipLaunchKernelGGL(k_consolidate<4>, g, b, sh, st, a);
-  else if (need <= 64) hipLaunchKernelGGL(k_consolidate<8>, g, b, sh, st, a);
-  else if (need <= 128) hipLaunchKernelGGL(k_consolidate<16>, g, b, sh, st, a);
-  else if (need <= 256) hipLaunchKernelGGL(k_consolidate<32>, g, b, sh, st, a);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (need > 256) return hipErrorInvalidValue;
+  return a.frz.half ? consolidate_f<_Float16>(a, need, sh, st) : consolidate_f<float>(a, need, sh, st);
 }
 
 }  // namespace ss

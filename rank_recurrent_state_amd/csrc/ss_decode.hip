@@ -11,7 +11,9 @@
 // the group and keeps a float4 slice of the d_v-vector accumulator.  The
 // decay is applied through Gamma (accumulated since the last compaction), so
 // the factors are never rewritten; only the new pad slot, o and the 16-byte
-// record are written.
+// record are written.  With fp16 factors (SEED 6 "Lower precision composes")
+// a lane reads four fp16 elements (8 bytes) per vector; the components then
+// stream as one list and the fp32 pad as a second one.
 //
 //   p_q = S_{t-1}^T q,  p_k = S_{t-1}^T k  (delta rule only)
 //   w   = v (scalar rule)  or  beta (v - alpha p_k)  (Gated DeltaNet, SEED eq. (2))
@@ -34,6 +36,8 @@
 // its contribution vectors sit in LDS, and so do the pad keys.  The plain
 // kernel (the dense baseline: the recurrence the dense Mamba-2 / GDN kernels
 // run) reads and writes every row every step: H_j <- alpha H_j + w_j k.
+#include <type_traits>
+
 #include "ss_internal.h"
 #include "ss_wave.h"
 
@@ -44,7 +48,7 @@ namespace {
 // ---------------------------------------------------------------------------
 // factored states
 // ---------------------------------------------------------------------------
-template <int P, int UN, bool RO, bool ANYDELTA>
+template <int P, int UN, bool RO, bool ANYDELTA, typename F>
 __global__ __launch_bounds__(256) void k_decode_factored(DecodeArgs a) {
   constexpr int G = 64 / P;
   const int lane = threadIdx.x & 63;
@@ -79,40 +83,65 @@ __global__ __launch_bounds__(256) void k_decode_factored(DecodeArgs a) {
   const float al = RO ? 1.f : uniformf(a.alpha[s]);
   const float be = delta ? uniformf(a.beta[s]) : 0.f;
   float4 acc = zero4(), acck = zero4();
-  for (int i0 = 0; i0 < T; i0 += G * UN) {
-    float4 x[UN], y[UN];
-    float wt[UN];
+  // pairs [ib, ie) of the list in chunks of G * UN; ld(i, x, y, w) issues the loads of pair i
+  auto stream = [&](int ib, int ie, auto ld) {
+    for (int i0 = ib; i0 < ie; i0 += G * UN) {
+      float4 x[UN], y[UN];
+      float wt[UN];
 #pragma unroll
-    for (int u = 0; u < UN; ++u) {
-      const int iu = i0 + u * G + grp;
-      const int i = iu < T ? iu : T - 1;  // clamped pair (T >= 1 here); its weight is masked at use
+      for (int u = 0; u < UN; ++u) {
+        const int iu = i0 + u * G + grp;
+        ld(iu < ie ? iu : ie - 1, x[u], y[u], wt[u]);  // clamped pair (ie > ib here); its weight is masked at use
+      }
+#pragma unroll
+      for (int u = 0; u < UN; ++u) {
+        const float wu = (i0 + u * G + grp < ie) ? wt[u] : 0.f;
+        const float cq = group_sum<P>(dot4(x[u], q4)) * wu;
+        acc = fma4(cq, y[u], acc);
+        if (delta) {
+          const float ck = group_sum<P>(dot4(x[u], k4)) * wu;
+          acck = fma4(ck, y[u], acck);
+        }
+      }
+    }
+  };
+  // clamped lanes: q4, k4 are 0 off the key lanes and lanes off the value range are never stored
+  auto ld_pad = [&](int i, float4 &x, float4 &y, float &w) {
+    const int64_t c = pad0 + i;
+    x = ld4nt(a.pk + c * dk + 4 * colk);
+    y = ld4nt(a.pw + c * dv + 4 * colv);
+    w = ldnt(a.pc + c);
+  };
+  if constexpr (std::is_same<F, float>::value) {
+    // one list: active, frozen and pad pairs share the chunks
+    stream(0, T, [&](int i, float4 &x, float4 &y, float &w) {
       const float *xp, *yp, *wp;
       int64_t c;
       if (i < ra) {
         c = wrap(off_a + i, a.act.cap);
-        xp = a.act.u; yp = a.act.v; wp = a.act.s;
+        xp = a.act.U<float>(); yp = a.act.V<float>(); wp = a.act.s;
       } else if (i < rr) {
         c = wrap(off_f + (i - ra), a.frz.cap);
-        xp = a.frz.u; yp = a.frz.v; wp = a.frz.s;
+        xp = a.frz.U<float>(); yp = a.frz.V<float>(); wp = a.frz.s;
       } else {
         c = pad0 + i;
         xp = a.pk; yp = a.pw; wp = a.pc;
       }
-      // clamped lanes: q4, k4 are 0 off the key lanes and lanes off the value range are never stored
-      x[u] = ld4nt(xp + c * dk + 4 * colk);
-      y[u] = ld4nt(yp + c * dv + 4 * colv);
-      wt[u] = ldnt(wp + c);
-    }
-#pragma unroll
-    for (int u = 0; u < UN; ++u) {
-      const float wu = (i0 + u * G + grp < T) ? wt[u] : 0.f;
-      const float cq = group_sum<P>(dot4(x[u], q4)) * wu;
-      acc = fma4(cq, y[u], acc);
-      if (delta) {
-        const float ck = group_sum<P>(dot4(x[u], k4)) * wu;
-        acck = fma4(ck, y[u], acck);
-      }
-    }
+      x = ld4nt(xp + c * dk + 4 * colk);
+      y = ld4nt(yp + c * dv + 4 * colv);
+      w = ldnt(wp + c);
+    });
+  } else {
+    // fp16 components, then the fp32 pad
+    stream(0, rr, [&](int i, float4 &x, float4 &y, float &w) {
+      const bool act = i < ra;
+      const int64_t c = act ? wrap(off_a + i, a.act.cap) : wrap(off_f + (i - ra), a.frz.cap);
+      const Arena &ar = act ? a.act : a.frz;
+      x = ldf4nt(ar.U<F>() + c * dk + 4 * colk);
+      y = ldf4nt(ar.V<F>() + c * dv + 4 * colv);
+      w = ldnt(ar.s + c);
+    });
+    stream(rr, T, ld_pad);
   }
   acc = cross_group_sum4<P>(acc);
   const float4 pq = scale4(gamma, acc);
@@ -143,7 +172,7 @@ __global__ __launch_bounds__(256) void k_decode_factored(DecodeArgs a) {
       nm.gamma = gnew;
       nm.packed = meta_pack(ra, rf, n + 1, flags);
       a.meta[s] = nm;
-      const unsigned long long b = decode_bytes(dk, dv, K, rr, n, delta, KIND_FACTORED);
+      const unsigned long long b = decode_bytes(dk, dv, K, rr, n, delta, KIND_FACTORED, (int)sizeof(F));
       __hip_atomic_fetch_add(&a.acct[s & (kAcctSlots - 1)], b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -486,23 +515,29 @@ __global__ __launch_bounds__(256) void k_dense_plain(DenseArgs a) {
   }
 }
 
-template <bool RO, bool AD>
+template <bool RO, bool AD, typename F>
 hipError_t decode_factored_p(const DecodeArgs &a, int P, hipStream_t st) {
   const dim3 grid((unsigned)((a.N + 3) / 4)), block(256);  // a.N: upper bound of the list length
   switch (P) {
-    case 1: hipLaunchKernelGGL((k_decode_factored<1, 1, RO, AD>), grid, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((k_decode_factored<2, 1, RO, AD>), grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((k_decode_factored<4, 1, RO, AD>), grid, block, 0, st, a); break;
-    case 8: hipLaunchKernelGGL((k_decode_factored<8, 2, RO, AD>), grid, block, 0, st, a); break;
-    case 16: hipLaunchKernelGGL((k_decode_factored<16, 2, RO, AD>), grid, block, 0, st, a); break;
+    case 1: hipLaunchKernelGGL((k_decode_factored<1, 1, RO, AD, F>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_decode_factored<2, 1, RO, AD, F>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((k_decode_factored<4, 1, RO, AD, F>), grid, block, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((k_decode_factored<8, 2, RO, AD, F>), grid, block, 0, st, a); break;
+    case 16: hipLaunchKernelGGL((k_decode_factored<16, 2, RO, AD, F>), grid, block, 0, st, a); break;
 #ifndef SS_FACT_UN32
 #define SS_FACT_UN32 4
 #endif
-    case 32: hipLaunchKernelGGL((k_decode_factored<32, SS_FACT_UN32, RO, AD>), grid, block, 0, st, a); break;
-    case 64: hipLaunchKernelGGL((k_decode_factored<64, 8, RO, AD>), grid, block, 0, st, a); break;
+    case 32: hipLaunchKernelGGL((k_decode_factored<32, SS_FACT_UN32, RO, AD, F>), grid, block, 0, st, a); break;
+    case 64: hipLaunchKernelGGL((k_decode_factored<64, 8, RO, AD, F>), grid, block, 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <typename F>
+hipError_t decode_factored_f(const DecodeArgs &a, bool readonly, bool any_delta, int P, hipStream_t st) {
+  if (readonly) return decode_factored_p<true, false, F>(a, P, st);
+  return any_delta ? decode_factored_p<false, true, F>(a, P, st) : decode_factored_p<false, false, F>(a, P, st);
 }
 
 template <int P, int UN, bool AD>
@@ -559,8 +594,8 @@ int lanes_per_pair(int dk, int dv) { return pow2_at_least((dk > dv ? dk : dv) >>
 hipError_t launch_decode_factored(const DecodeArgs &a, bool readonly, bool any_delta, hipStream_t st) {
   if (a.N <= 0) return hipSuccess;
   const int P = lanes_per_pair(a.dk, a.dv);
-  if (readonly) return decode_factored_p<true, false>(a, P, st);
-  return any_delta ? decode_factored_p<false, true>(a, P, st) : decode_factored_p<false, false>(a, P, st);
+  if (a.act.half) return decode_factored_f<_Float16>(a, readonly, any_delta, P, st);
+  return decode_factored_f<float>(a, readonly, any_delta, P, st);
 }
 
 hipError_t launch_decode_dense(const DenseArgs &a, int64_t n_upper, bool readonly, bool any_delta, hipStream_t st) {

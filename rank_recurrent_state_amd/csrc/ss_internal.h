@@ -74,10 +74,21 @@ struct __attribute__((aligned(16))) DenseSlot {
   uint32_t spare;
 };
 
+// A ring of components.  The factor vectors u, v are stored in fp32 or, in a
+// pool created with fp16 factors (SEED 6 "Lower precision composes": factors
+// rounded to fp16 when a compaction writes them, the pad kept in fp32), in
+// fp16; sigma is always fp32.  Kernels take the element type F as a template
+// parameter and reach the vectors through U<F>() / V<F>().
 struct Arena {
-  float *u, *v, *s;
+  void *u, *v;
+  float *s;
   int64_t cap;  // components (a ring)
+  int half;     // 1: u, v hold _Float16
+  template <typename F> __host__ __device__ F *U() const { return static_cast<F *>(u); }
+  template <typename F> __host__ __device__ F *V() const { return static_cast<F *>(v); }
 };
+// bytes of one factor element
+__host__ __device__ inline int fac_bytes(const Arena &a) { return a.half ? 2 : 4; }
 
 // physical slot of ring position (start + i), start < cap, i < cap
 __host__ __device__ inline int64_t wrap(int64_t c, int64_t cap) { return c >= cap ? c - cap : c; }
@@ -242,7 +253,7 @@ struct ConsolidateArgs {
   unsigned long long *acct_flops, *acct_states, *acct_removed;
 };
 constexpr size_t kConsolidateLdsMax = 160 * 1024;  // LDS per workgroup on gfx950
-size_t consolidate_lds_bytes(int dk, int dv, int fmax);
+size_t consolidate_lds_bytes(int dk, int dv, int fmax, bool half);
 hipError_t launch_consolidate(const ConsolidateArgs &a, hipStream_t st);
 
 // how a state is decoded
@@ -251,17 +262,19 @@ enum DecodeKind : int { KIND_FACTORED = 0, KIND_DENSE_BUFFERED = 1, KIND_DENSE_P
 // algorithmic bytes of one decode step of one state (kept identical to the
 // in-kernel accounting).  n_pad is the pad fill before the step; a buffered
 // dense state whose pad fills in this step rewrites H instead of a pad slot.
+// fsz: bytes of a stored factor element (4, or 2 with fp16 factors); pad slots are fp32.
 __host__ __device__ inline unsigned long long decode_bytes(int dk, int dv, int K, int ncomp, int npad, bool delta,
-                                                           int kind) {
+                                                           int kind, int fsz = 4) {
   const unsigned long long in = 4ull * (2ull * dk + dv + 1 + (delta ? 1 : 0));
   const unsigned long long comp = 4ull * (unsigned long long)(dk + dv + 1);
+  const unsigned long long fcomp = (unsigned long long)fsz * (unsigned long long)(dk + dv) + 4ull;
   const unsigned long long st = 4ull * (unsigned long long)dk * dv;
   if (kind == KIND_DENSE_PLAIN)  // slot record read, state read and written, inputs, output
     return 16ull + 2ull * st + in + 4ull * dv;
   if (kind == KIND_DENSE_BUFFERED)  // slot record read+write, H and the pad read, inputs, output, slot or H written
     return 32ull + st + comp * (unsigned long long)npad + in + 4ull * dv + (npad + 1 >= K ? st : comp);
   // record read+write, components and pad slots read, inputs, one slot written, output
-  return 32ull + comp * (unsigned long long)(ncomp + npad) + in + comp + 4ull * dv;
+  return 32ull + fcomp * (unsigned long long)ncomp + comp * (unsigned long long)npad + in + comp + 4ull * dv;
 }
 
 }  // namespace ss

@@ -18,6 +18,7 @@
 #include <deque>
 #include <cstdio>
 #include <cstring>
+#include <limits>
 #include <string>
 #include <vector>
 
@@ -41,6 +42,7 @@ enum HostFlag { HF_PAD = 0, HF_DENSE_CAP = 1, HF_FACT = 2, HF_RING = 3, HF_N = 4
 struct ss_pool {
   int64_t N = 0;
   int dk = 0, dv = 0, K = 0, r = 0, L = 0, promote = 0, force_dense = 0, fcap = 0, G = 0;
+  int half = 0;  // factor vectors stored in fp16
   bool any_delta = false;
   std::vector<int32_t> group_offset;
   std::vector<int64_t> group_start, group_size;
@@ -51,7 +53,7 @@ struct ss_pool {
   ss::Meta *meta = nullptr;
   int32_t *members = nullptr;
   float *eps = nullptr;
-  ss::Arena act{nullptr, nullptr, nullptr, 0}, frz{nullptr, nullptr, nullptr, 0};
+  ss::Arena act{nullptr, nullptr, nullptr, 0, 0}, frz{nullptr, nullptr, nullptr, 0, 0};
   // rings of components (0: active, 1: frozen): device allocation state and per-group segments,
   // and the host's bounds on them (see ensure_ring_space)
   void *ring_blk[2] = {nullptr, nullptr};
@@ -168,20 +170,40 @@ hipError_t timed(ss_pool *p, int kernel, hipStream_t st, F fn) {
   return e;
 }
 
+// IEEE 754 binary16 -> binary32 (exact): sign, 5-bit exponent (bias 15), 10-bit fraction;
+// exponent 0 holds zero and the subnormals (fraction * 2^-24), exponent 31 infinities and NaNs
+float half_to_float(uint16_t h) {
+  const uint32_t sign = (uint32_t)(h >> 15) << 31, ex = (h >> 10) & 0x1fu, fr = h & 0x3ffu;
+  float mag;
+  if (ex == 0) mag = std::ldexp((float)fr, -24);
+  else if (ex == 31) mag = fr ? std::numeric_limits<float>::quiet_NaN() : std::numeric_limits<float>::infinity();
+  else mag = std::ldexp((float)(fr | 0x400u), (int)ex - 25);
+  uint32_t bits;
+  std::memcpy(&bits, &mag, 4);
+  bits |= sign;
+  std::memcpy(&mag, &bits, 4);
+  return mag;
+}
+
 ss_status hip_fail(hipError_t e, const char *what) {
   return fail(SS_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-// one ring: u [cap][d_k], v [cap][d_v], sigma [cap] in a single allocation
+// bytes of one stored component: u and v (fp32 or fp16) and sigma (fp32)
+int64_t comp_bytes(const ss_pool *p) { return (int64_t)(p->half ? 2 : 4) * (p->dk + p->dv) + 4; }
+
+// one ring: u [cap][d_k], v [cap][d_v] (fp32 or fp16), sigma [cap] in a single allocation
 hipError_t ring_alloc(ss_pool *p, int64_t cap, void **blk, size_t *bytes, ss::Arena *out) {
-  *bytes = sizeof(float) * (size_t)cap * (p->dk + p->dv + 1);
+  const size_t fsz = p->half ? 2 : 4;
+  *bytes = (size_t)cap * (size_t)comp_bytes(p);
   hipError_t e = hipMalloc(blk, *bytes);
   if (e != hipSuccess) return e;
-  float *f = static_cast<float *>(*blk);
-  out->u = f;
-  out->v = f + (size_t)cap * p->dk;
-  out->s = out->v + (size_t)cap * p->dv;
+  char *b = static_cast<char *>(*blk);  // d_k, d_v are multiples of 4: every part stays 8-byte aligned
+  out->u = b;
+  out->v = b + (size_t)cap * p->dk * fsz;
+  out->s = reinterpret_cast<float *>(b + (size_t)cap * (p->dk + p->dv) * fsz);
   out->cap = cap;
+  out->half = p->half;
   return hipSuccess;
 }
 
@@ -411,7 +433,9 @@ int32_t ss_dense_rank_limit(int32_t d_k, int32_t d_v) {
 
 uint64_t ss_decode_bytes_per_state(int32_t d_k, int32_t d_v, int32_t pad_slots, int32_t n_comp, int32_t n_pad,
                                    int32_t rule, int32_t kind) {
-  if (kind < SS_DECODE_FACTORED || kind > SS_DECODE_DENSE_PLAIN) return 0;
+  if (kind < SS_DECODE_FACTORED || kind > SS_DECODE_FACTORED_FP16) return 0;
+  if (kind == SS_DECODE_FACTORED_FP16)
+    return ss::decode_bytes(d_k, d_v, pad_slots, n_comp, n_pad, rule == SS_RULE_DELTA, ss::KIND_FACTORED, 2);
   return ss::decode_bytes(d_k, d_v, pad_slots, n_comp, n_pad, rule == SS_RULE_DELTA, kind);
 }
 
@@ -512,11 +536,12 @@ ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipSt
   const bool factored = !d->force_dense;
   if (d->arena_components < 0 || d->arena_components >= (int64_t)INT32_MAX)
     return fail(SS_ERR_ARG, "arena_components must be in [0, 2^31)");
+  if (d->factor_fp16 != 0 && d->factor_fp16 != 1) return fail(SS_ERR_ARG, "factor_fp16 must be 0 or 1");
 
   ss_pool *p = new (std::nothrow) ss_pool();
   if (!p) return fail(SS_ERR_OOM, "host allocation failed");
   p->N = N; p->dk = dk; p->dv = dv; p->K = K; p->r = r; p->L = L; p->promote = promote;
-  p->force_dense = d->force_dense ? 1 : 0; p->fcap = fcap; p->G = G; p->any_delta = any_delta; p->cap_d = cap_d;
+  p->force_dense = d->force_dense ? 1 : 0; p->half = d->factor_fp16; p->fcap = fcap; p->G = G; p->any_delta = any_delta; p->cap_d = cap_d;
   p->group_offset.assign(G, 0);
   if (d->group_offset) for (int g = 0; g < G; ++g) p->group_offset[g] = d->group_offset[g];
   p->group_size.assign(G, 0);
@@ -554,12 +579,12 @@ ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipSt
     int64_t nf = 0, ngmax = 0;
     for (int g = 0; g < G; ++g) ngmax = std::max(ngmax, p->group_size[g]);
     for (int64_t s = 0; s < N; ++s) nf += cnt[0][s] >= 0 ? 1 : 0;
-    const int64_t comp_bytes = 4ll * (dk + dv + 1);
+    const int64_t cbytes = (int64_t)(d->factor_fp16 ? 2 : 4) * (dk + dv) + 4;
     int64_t maxcap[2];
     for (int R = 0; R < 2; ++R) maxcap[R] = (nf + ngmax) * (R == 0 ? (int64_t)r : (int64_t)fcap);
     size_t free_b = 0, total_b = 0;
     const bool roomy = hipMemGetInfo(&free_b, &total_b) == hipSuccess &&
-                       (maxcap[0] + maxcap[1]) * comp_bytes <= (int64_t)(free_b / 4) &&
+                       (maxcap[0] + maxcap[1]) * cbytes <= (int64_t)(free_b / 4) &&
                        maxcap[1] < (int64_t)INT32_MAX;
     for (int R = 0; R < 2; ++R) {
       const int64_t autocap = R == 0 || roomy ? maxcap[R] : 2 * (tot[1] + (int64_t)K * ngmax);
@@ -941,7 +966,7 @@ static ss_status consolidate_precheck(ss_pool *p) {
   if (!p) return fail(SS_ERR_ARG, "pool is NULL");
   ss_status st = poll(p);
   if (st != SS_OK) return st;
-  if (ss::consolidate_lds_bytes(p->dk, p->dv, frozen_max(p)) > ss::kConsolidateLdsMax)
+  if (ss::consolidate_lds_bytes(p->dk, p->dv, frozen_max(p), p->half != 0) > ss::kConsolidateLdsMax)
     return fail(SS_ERR_SHAPE, "the pool's largest frozen part does not fit the consolidation kernel's LDS");
   return SS_OK;
 }
@@ -1069,17 +1094,28 @@ ss_status ss_state_export(ss_pool *p, const int64_t *ids, int64_t n, void *host_
     float *kk = c + nn;
     float *ww = kk + (size_t)nn * dk;
     // `cnt` components of a ring from physical slot c0, wrapping once at the ring's end
-    auto dl_ring = [&](float *dst, const float *base, int64_t cap, int64_t c0, int64_t cnt, int row) {
+    // (elements of `esz` bytes; fp16 elements are staged and widened to fp32)
+    std::vector<uint16_t> hbuf;
+    auto dl_ring = [&](float *dst, const void *base, int64_t cap, int64_t c0, int64_t cnt, int row, int esz) {
       const int64_t first = std::min(cnt, cap - c0);
-      dl(dst, base + c0 * row, sizeof(float) * first * row);
-      dl(dst + first * row, base, sizeof(float) * (cnt - first) * row);
+      char *d8 = reinterpret_cast<char *>(dst);
+      if (esz == 2) {
+        hbuf.resize((size_t)cnt * row);
+        d8 = reinterpret_cast<char *>(hbuf.data());
+      }
+      const char *b8 = static_cast<const char *>(base);
+      dl(d8, b8 + (size_t)c0 * row * esz, (size_t)esz * first * row);
+      dl(d8 + (size_t)first * row * esz, b8, (size_t)esz * (cnt - first) * row);
+      if (esz == 2 && e == hipSuccess)
+        for (size_t x = 0; x < hbuf.size(); ++x) dst[x] = half_to_float(hbuf[x]);
     };
-    dl_ring(sig, p->act.s, p->act.cap, m.off_a, ra, 1);
-    dl_ring(sig + ra, p->frz.s, p->frz.cap, m.off_f, rf, 1);
-    dl_ring(u, p->act.u, p->act.cap, m.off_a, ra, dk);
-    dl_ring(u + (size_t)ra * dk, p->frz.u, p->frz.cap, m.off_f, rf, dk);
-    dl_ring(v, p->act.v, p->act.cap, m.off_a, ra, dv);
-    dl_ring(v + (size_t)ra * dv, p->frz.v, p->frz.cap, m.off_f, rf, dv);
+    const int fz = p->half ? 2 : 4;
+    dl_ring(sig, p->act.s, p->act.cap, m.off_a, ra, 1, 4);
+    dl_ring(sig + ra, p->frz.s, p->frz.cap, m.off_f, rf, 1, 4);
+    dl_ring(u, p->act.u, p->act.cap, m.off_a, ra, dk, fz);
+    dl_ring(u + (size_t)ra * dk, p->frz.u, p->frz.cap, m.off_f, rf, dk, fz);
+    dl_ring(v, p->act.v, p->act.cap, m.off_a, ra, dv, fz);
+    dl_ring(v + (size_t)ra * dv, p->frz.v, p->frz.cap, m.off_f, rf, dv, fz);
     dl(c, p->pc + (size_t)ids[i] * K, sizeof(float) * nn);
     dl(kk, p->pk + (size_t)ids[i] * K * dk, sizeof(float) * (size_t)nn * dk);
     dl(ww, p->pw + (size_t)ids[i] * K * dv, sizeof(float) * (size_t)nn * dv);
@@ -1110,7 +1146,7 @@ ss_status ss_pool_stats(ss_pool *p, ss_stats *out, hipStream_t stream) {
   if (e != hipSuccess) return hip_fail(e, "stats copy");
   std::memset(out, 0, sizeof(*out));
   out->n_states = p->N;
-  const int64_t comp = 4ll * (p->dk + p->dv + 1);
+  const int64_t comp = 4ll * (p->dk + p->dv + 1), fcomp = comp_bytes(p);  // a pad slot, a stored component
   int64_t live = 16ll * p->N + 16ll * nd;
   for (int64_t s = 0; s < p->N; ++s) {
     const uint32_t pk = meta[s].packed;
@@ -1127,7 +1163,7 @@ ss_status ss_pool_stats(ss_pool *p, ss_stats *out, hipStream_t stream) {
     out->active_components += ra;
     out->frozen_components += rf;
     out->pad_entries += nn;
-    live += comp * (ra + rf + nn);
+    live += fcomp * (ra + rf) + comp * nn;
     out->max_rank = std::max<int64_t>(out->max_rank, ra + rf);
     out->rank_hist[std::min<int64_t>(64, ra + rf)]++;
   }

@@ -119,6 +119,33 @@ __device__ __forceinline__ void st4nt(float *p, float4 v) {
   __builtin_nontemporal_store(v.w, p + 3);
 }
 
+// Factor storage element types: float, or _Float16 (four elements = 8 bytes per lane).
+// Conversions to fp16 round to nearest, ties to even (the hardware's default mode).
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 ldf4(const float *p) { return ld4(p); }
+__device__ __forceinline__ float4 ldf4(const _Float16 *p) {
+  const half4_t h = *reinterpret_cast<const half4_t *>(p);
+  return make_float4((float)h.x, (float)h.y, (float)h.z, (float)h.w);
+}
+__device__ __forceinline__ float4 ldf4nt(const float *p) { return ld4nt(p); }
+__device__ __forceinline__ float4 ldf4nt(const _Float16 *p) {
+  const half4_t h = __builtin_nontemporal_load(reinterpret_cast<const half4_t *>(p));
+  return make_float4((float)h.x, (float)h.y, (float)h.z, (float)h.w);
+}
+__device__ __forceinline__ void stf4(float *p, float4 v) { st4(p, v); }
+__device__ __forceinline__ void stf4(_Float16 *p, float4 v) {
+  half4_t h;
+  h.x = (_Float16)v.x;
+  h.y = (_Float16)v.y;
+  h.z = (_Float16)v.z;
+  h.w = (_Float16)v.w;
+  *reinterpret_cast<half4_t *>(p) = h;
+}
+__device__ __forceinline__ float ldf(const float *p) { return *p; }
+__device__ __forceinline__ float ldf(const _Float16 *p) { return (float)*p; }
+__device__ __forceinline__ void stf(float *p, float v) { *p = v; }
+__device__ __forceinline__ void stf(_Float16 *p, float v) { *p = (_Float16)v; }
+
 // make this lane's LDS writes visible to the other lanes of the wavefront
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

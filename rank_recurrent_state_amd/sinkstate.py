@@ -36,6 +36,7 @@ class PoolDesc(ctypes.Structure):
         ("group_of_state", _c_i32p), ("group_offset", _c_i32p),
         ("rule", _c_u8p), ("eps", _c_f32p), ("eps_default", ctypes.c_float),
         ("dense_capacity", ctypes.c_int64), ("arena_components", ctypes.c_int64),
+        ("factor_fp16", ctypes.c_int32),
     ]
 
 
@@ -151,7 +152,7 @@ def dense_rank_limit(d_k: int, d_v: int) -> int:
     return int(load_library().ss_dense_rank_limit(d_k, d_v))
 
 
-DECODE_FACTORED, DECODE_DENSE_BUFFERED, DECODE_DENSE_PLAIN = 0, 1, 2
+DECODE_FACTORED, DECODE_DENSE_BUFFERED, DECODE_DENSE_PLAIN, DECODE_FACTORED_FP16 = 0, 1, 2, 3
 
 
 def decode_bytes_per_state(d_k, d_v, pad_slots, n_comp, n_pad, rule, kind) -> int:
@@ -181,7 +182,7 @@ class StatePool:
 def state_pool_create(n_states, d_k, d_v, pad_slots=8, r_active=8, dense_rank_limit=-1, promote_on_compact=True,
                       max_frozen=0, force_dense=False, group_of_state=None, group_offset=None, rule=None, eps=None,
                       eps_default=0.0, dense_capacity=0, comp_off=None, u=None, v=None, sigma=None,
-                      arena_components=0, dense_mask=None, dense=None, stream=None) -> StatePool:
+                      arena_components=0, dense_mask=None, dense=None, factor_fp16=False, stream=None) -> StatePool:
     lib = load_library()
     n_groups = 1 if group_offset is None else len(group_offset)
     keep = []
@@ -193,7 +194,7 @@ def state_pool_create(n_states, d_k, d_v, pad_slots=8, r_active=8, dense_rank_li
     desc = PoolDesc(int(n_states), int(d_k), int(d_v), int(pad_slots), int(r_active), int(dense_rank_limit),
                     int(bool(promote_on_compact)), int(max_frozen), int(bool(force_dense)), int(n_groups),
                     g_p, o_p, r_p, e_p, float(eps_default), int(dense_capacity),
-                    int(arena_components))
+                    int(arena_components), int(factor_fp16))
     init = None
     if comp_off is not None or dense_mask is not None:
         c_a, c_p = _arr(comp_off, np.int64, _c_i64p)

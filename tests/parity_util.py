@@ -9,6 +9,18 @@ Tolerances (fp32 GPU against the fp64 oracle):
   ranks             equal, except keep/drop decisions within 1e-5 sigma_max of
                     eps * sigma_max and active/frozen splits within 1e-5
                     sigma_max ("guard band"), which are counted and accepted
+
+fp16 factor storage: each side rounds the factors it writes to binary16.  Where
+singular values cluster, the two sides' exact results are different bases of
+the same subspace, and their roundings differ.  Rounding moves an element by at
+most 2^-11 of itself (normal range) or 2^-25 (subnormal range), so a stored unit
+vector moves by at most delta = 2^-11 + sqrt(d) 2^-25 and a component
+sigma u v^T by at most sigma (delta_u + delta_v + delta_u delta_v).  A compacted
+state is therefore compared as ||S_gpu - S_or||_F <= 1e-4 ||S_or||_F + 2 rho,
+rho = sum_i sigma_i (delta_u + delta_v + delta_u delta_v) over the oracle's
+components (both sides round).  The projector of an active block of r rounded
+unit vectors moves by at most 2 sqrt(r) delta + r delta^2 (Frobenius), so the
+active projectors are compared within 1e-4 plus twice that.
 """
 import numpy as np
 
@@ -17,6 +29,15 @@ from oracle.oracle import OracleState
 
 TOL = 1e-4
 GUARD = 1e-5
+U16 = 2.0 ** -11   # binary16 unit roundoff (round to nearest)
+SUB16 = 2.0 ** -25  # binary16 half spacing of the subnormals
+
+
+def fp16_rounding_bound(sigma, d_k, d_v):
+    """rho: the Frobenius-norm bound on how far rounding unit factors to binary16 moves sum sigma_i u_i v_i^T."""
+    du = U16 + np.sqrt(d_k) * SUB16
+    dv = U16 + np.sqrt(d_v) * SUB16
+    return float(np.sum(np.abs(sigma)) * (du + dv + du * dv))
 
 
 def to_oracle_state(st, eps):
@@ -36,8 +57,8 @@ def reconstruct(st):
     return S
 
 
-def oracle_from_export(states, eps, d_k, d_v, K, r, L=-1, promote=True):
-    P = OraclePool(len(states), d_k, d_v, K, r, L, promote)
+def oracle_from_export(states, eps, d_k, d_v, K, r, L=-1, promote=True, factor_fp16=False):
+    P = OraclePool(len(states), d_k, d_v, K, r, L, promote, factor_fp16=factor_fp16)
     for j, st in enumerate(states):
         P.set_state(j, to_oracle_state(st, eps[j]), as_init=False)
     return P
@@ -49,16 +70,23 @@ def rel_out_err(o_gpu, o_or, S_norm, q_norm):
     return np.linalg.norm(o_gpu - o_or, axis=1) / den
 
 
-def compare_compacted(gpu_states, P, eps, K=None):
+def compare_compacted(gpu_states, P, eps, K=None, fp16=False):
     """Compare GPU states after a compaction with the oracle's.  Returns
-    (max state rel err, max sigma rel err, guard-band count, rank mismatches outside the guard band)."""
+    (max state rel err, max sigma rel err, guard-band count, rank mismatches outside the guard band).
+    fp16: the state error is reported as TOL * err / (TOL ||S|| + 2 rho), so that TOL stays the bar."""
     worst_s, worst_sig, guard, bad = 0.0, 0.0, 0, []
     for j, st in enumerate(gpu_states):
         ost = P.get_state(j)
         Sg = reconstruct(st)
         So = P.reconstruct(j)
         nrm = np.linalg.norm(So)
-        worst_s = max(worst_s, np.linalg.norm(Sg - So) / max(nrm, 1e-30))
+        err = np.linalg.norm(Sg - So)
+        if fp16 and not ost.dense:
+            d_k, d_v = So.shape
+            allowed = TOL * nrm + 2.0 * fp16_rounding_bound(ost.sigma, d_k, d_v)
+            worst_s = max(worst_s, TOL * err / max(allowed, 1e-30))
+        else:
+            worst_s = max(worst_s, err / max(nrm, 1e-30))
         if st["dense"] != ost.dense:
             bad.append((j, "dense flag"))
             continue
@@ -81,8 +109,9 @@ def compare_compacted(gpu_states, P, eps, K=None):
     return worst_s, worst_sig, guard, bad
 
 
-def active_projector_err(gpu_state, ost, r):
-    """Projector distance of the active block when it is separated from the rest by a gap > 1e-2 sigma_max."""
+def active_projector_err(gpu_state, ost, r, fp16=False):
+    """Projector distance of the active block when it is separated from the rest by a gap > 1e-2 sigma_max.
+    fp16: reported as TOL * err / (TOL + 2 (2 sqrt(r) delta + r delta^2)), so that TOL stays the bar."""
     if gpu_state["dense"] or ost.dense:
         return 0.0
     sg = gpu_state["sigma"]
@@ -95,4 +124,11 @@ def active_projector_err(gpu_state, ost, r):
     Uo = ost.U[:r].T
     Vg = gpu_state["V"][:r].T.astype(np.float64)
     Vo = ost.V[:r].T
-    return max(np.linalg.norm(Ug @ Ug.T - Uo @ Uo.T), np.linalg.norm(Vg @ Vg.T - Vo @ Vo.T))
+    eu, ev = np.linalg.norm(Ug @ Ug.T - Uo @ Uo.T), np.linalg.norm(Vg @ Vg.T - Vo @ Vo.T)
+    if not fp16:
+        return max(eu, ev)
+    out = 0.0
+    for e, d in ((eu, Ug.shape[0]), (ev, Vg.shape[0])):
+        delta = U16 + np.sqrt(d) * SUB16
+        out = max(out, TOL * e / (TOL + 2.0 * (2.0 * np.sqrt(r) * delta + r * delta * delta)))
+    return out

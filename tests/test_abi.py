@@ -63,13 +63,14 @@ def test_create_rejects_bad_arguments_without_touching_the_gpu(lib):
     assert lib.ss_state_pool_create(None, None, None, None) == ss.SS_ERR_ARG
     base = dict(n_states=4, d_k=16, d_v=32, pad_slots=8, r_active=8, dense_rank_limit=-1, promote_on_compact=1,
                 max_frozen=0, force_dense=0, n_groups=1, group_of_state=None, group_offset=None, rule=None,
-                eps=None, eps_default=1e-3, dense_capacity=0, arena_components=0)
+                eps=None, eps_default=1e-3, dense_capacity=0, arena_components=0, factor_fp16=0)
     cases = [({"n_states": 0}, ss.SS_ERR_ARG), ({"d_k": 18}, ss.SS_ERR_SHAPE), ({"d_v": 260}, ss.SS_ERR_SHAPE),
              ({"pad_slots": 9}, ss.SS_ERR_SHAPE), ({"r_active": 0}, ss.SS_ERR_SHAPE),
              ({"n_groups": 0}, ss.SS_ERR_ARG), ({"max_frozen": 300}, ss.SS_ERR_ARG),
              ({"eps_default": -1.0}, ss.SS_ERR_ARG), ({"dense_capacity": 5}, ss.SS_ERR_ARG),
              ({"d_k": 260, "d_v": 128}, ss.SS_ERR_SHAPE), ({"arena_components": -1}, ss.SS_ERR_ARG),
-             ({"arena_components": 1 << 31}, ss.SS_ERR_ARG)]
+             ({"arena_components": 1 << 31}, ss.SS_ERR_ARG), ({"factor_fp16": 2}, ss.SS_ERR_ARG),
+             ({"factor_fp16": -1}, ss.SS_ERR_ARG)]
     for over, expect in cases:
         d = dict(base, **over)
         desc = ss.PoolDesc(*[d[f] for f, _ in ss.PoolDesc._fields_])
@@ -135,7 +136,12 @@ def test_decode_byte_formula(lib):
     comp = 4 * (128 + 80 + 1)
     assert f(128, 80, 8, 0, 3, 0, BUF) == 32 + 4 * 128 * 80 + 3 * comp + inputs + 4 * 80 + comp
     assert f(128, 80, 8, 0, 7, 0, BUF) == 32 + 4 * 128 * 80 + 7 * comp + inputs + 4 * 80 + 4 * 128 * 80
-    assert f(128, 80, 8, 0, 0, 0, 3) == 0
+    # fp16 factors: a stored component is 2 (d_k + d_v) + 4 bytes, a pad slot stays 4 (d_k + d_v + 1)
+    H16 = 3
+    assert f(128, 80, 8, 9, 0, 0, H16) - f(128, 80, 8, 8, 0, 0, H16) == 2 * (128 + 80) + 4
+    assert f(128, 80, 8, 8, 4, 0, H16) - f(128, 80, 8, 8, 3, 0, H16) == comp
+    assert f(128, 80, 8, 8, 3, 0, FAC) - f(128, 80, 8, 8, 3, 0, H16) == 8 * 2 * (128 + 80)
+    assert f(128, 80, 8, 0, 0, 0, 4) == 0 and f(128, 80, 8, 0, 0, 0, -1) == 0
     # page-printed footprint: rank-8 factors + a full pad of one 80x128 state = 13,376 B
     g = json.load(open(os.path.join(GOLD, "memory_arithmetic.json")))
     assert 2 * 8 * 4 * (128 + 80 + 1) == g["total_bytes"]

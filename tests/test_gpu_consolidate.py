@@ -36,10 +36,13 @@ def _run(w, pool, t0, t1):
     torch.cuda.synchronize()
 
 
-def _consolidate_and_compare(w, init, pool, ids, group=-1):
+def _consolidate_and_compare(w, init, pool, ids, group=-1, fp16=False):
     eps = init["eps"][ids]
     before = ss.state_export(pool, ids)
-    P = oracle_from_export(before, eps, w.d_k, w.d_v, w.K, w.r)
+    P = oracle_from_export(before, eps, w.d_k, w.d_v, w.K, w.r, factor_fp16=fp16)
+    # fp16 factors: each stored element is within 2^-11 (relative) of its exact value, so the
+    # Gram matrix of unit vectors deviates from I by at most about 2 * 2^-11
+    otol = 1.0e-3 + 1e-5 if fp16 else 1e-4
     st0 = ss.pool_stats(pool)
     ss.consolidate(pool, group)
     torch.cuda.synchronize()
@@ -64,10 +67,13 @@ def _consolidate_and_compare(w, init, pool, ids, group=-1):
         if rf and mine:  # states of other groups keep their frozen parts as they were
             Uf = a["U"][ra:].astype(np.float64)
             Vf = a["V"][ra:].astype(np.float64)
-            assert np.abs(Uf @ Uf.T - np.eye(rf)).max() <= 1e-4
-            assert np.abs(Vf @ Vf.T - np.eye(rf)).max() <= 1e-4
+            assert np.abs(Uf @ Uf.T - np.eye(rf)).max() <= otol
+            assert np.abs(Vf @ Vf.T - np.eye(rf)).max() <= otol
+            if fp16:
+                for x in (a["U"], a["V"]):
+                    assert np.array_equal(x.astype(np.float16).astype(np.float32), x)
             assert np.all(np.diff(a["sigma"][ra:]) <= 0)
-    ws, wsig, guard, bad = compare_compacted(after, P, eps)
+    ws, wsig, guard, bad = compare_compacted(after, P, eps, fp16=fp16)
     assert not bad, bad[:5]
     assert ws <= TOL and wsig <= TOL, (ws, wsig)
     st1 = ss.pool_stats(pool)
@@ -189,4 +195,19 @@ def test_consolidate_rejects_frozen_parts_beyond_lds():
     pool.close()
     pool = ss.state_pool_create(4, 256, 256, 8, 8, promote_on_compact=False, max_frozen=64)
     ss.consolidate(pool)
+    pool.close()
+
+
+@pytest.mark.parametrize("name", ["tiny", "gdn_delta"])
+def test_consolidate_fp16_factors(name):
+    """fp16 factor storage: the consolidated frozen factors are rounded to fp16 on both sides; Q is
+    kept in fp32 while the kernel runs, so only the final factors carry the rounding."""
+    w = W.get(name, n_requests=1 if name != "tiny" else None)
+    init = W.initial_state(w)
+    pool = _pool(w, init, factor_fp16=True)
+    _run(w, pool, 1, 48 if name != "tiny" else 64)
+    ids = np.arange(w.n_states) if name == "tiny" else \
+        np.unique(np.concatenate([np.arange(0, w.n_states, 7), [w.n_states - 1]]))
+    removed, guard = _consolidate_and_compare(w, init, pool, ids, fp16=True)
+    print("fp16", name, "removed", removed, "guard", guard)
     pool.close()

@@ -25,8 +25,10 @@ def _pool_from_init(w, init, **kw):
                                 comp_off=init["comp_off"], u=init["u"], v=init["v"], sigma=init["sigma"], **kw)
 
 
-def _lockstep(w, init, pool, ids, steps, promote=True, check_readout=False):
-    """Run `steps` decode(+compaction) steps in lock-step on the states `ids`."""
+def _lockstep(w, init, pool, ids, steps, promote=True, check_readout=False, fp16=False):
+    """Run `steps` decode(+compaction) steps in lock-step on the states `ids`.  fp16: the pool
+    stores fp16 factors; the oracle rounds the factors it writes the same way, and every exported
+    factor must be exactly representable in fp16."""
     gen = W.StepInputs(w, device="cuda")
     eps = init["eps"][ids]
     grp = init["group_of_state"][ids]
@@ -36,7 +38,9 @@ def _lockstep(w, init, pool, ids, steps, promote=True, check_readout=False):
     for t in range(1, steps + 1):
         x = gen.generate(t)
         before = ss.state_export(pool, ids)
-        P = oracle_from_export(before, eps, w.d_k, w.d_v, w.K, w.r, promote=promote)
+        if fp16:
+            _assert_fp16_factors(before)
+        P = oracle_from_export(before, eps, w.d_k, w.d_v, w.K, w.r, promote=promote, factor_fp16=fp16)
         sub = {k: v.cpu().numpy()[ids].astype(np.float64) for k, v in x.items()}
         if check_readout:
             ss.readout(pool, x["q"], o)
@@ -59,18 +63,26 @@ def _lockstep(w, init, pool, ids, steps, promote=True, check_readout=False):
         if due:
             for g in due:
                 ss.compact(pool, g)
-            P2 = oracle_from_export(after, eps, w.d_k, w.d_v, w.K, w.r, promote=promote)
+            P2 = oracle_from_export(after, eps, w.d_k, w.d_v, w.K, w.r, promote=promote, factor_fp16=fp16)
             sel = np.nonzero(np.isin(grp, due))[0]
             P2.compact(sel)
             comp = ss.state_export(pool, ids)
-            ws, wsig, gd, bad = compare_compacted(comp, P2, eps)
+            ws, wsig, gd, bad = compare_compacted(comp, P2, eps, fp16=fp16)
             assert not bad, f"step {t}: rank/dense mismatches outside the guard band: {bad[:5]}"
             guard += gd
             worst["S_c"] = max(worst["S_c"], ws)
             worst["sigma"] = max(worst["sigma"], wsig)
             for j in sel:
-                worst["proj"] = max(worst["proj"], active_projector_err(comp[j], P2.get_state(j), w.r))
+                worst["proj"] = max(worst["proj"], active_projector_err(comp[j], P2.get_state(j), w.r, fp16=fp16))
     return worst, guard
+
+
+def _assert_fp16_factors(states):
+    for st in states:
+        if not st["dense"]:
+            for key in ("U", "V"):
+                x = st[key]
+                assert np.array_equal(x.astype(np.float16).astype(np.float32), x), key
 
 
 def _assert_worst(worst):
@@ -375,3 +387,117 @@ def test_ring_growth_wrap_and_repack(name, promote, order):
         assert max(h - c for h, c in zip(st["ring_head"], st["ring_capacity"])) > 0, "no ring wrapped"
     for R in range(2):
         assert st["ring_used"][R] <= st["ring_capacity"][R]
+
+
+# ---------------------------------------------------------------------------------------------
+# fp16 factor storage (SEED 6 "Lower precision composes"): factors rounded when written, pad fp32
+# ---------------------------------------------------------------------------------------------
+
+def test_fp16_create_rounds_initial_factors_exactly():
+    """The stored initial factors are the round-to-nearest-even fp16 values of the given ones
+    (bit-exact against numpy's float16 conversion); sigma and the layout are unchanged, and the
+    factor part of the live bytes halves."""
+    w = W.get("gdn_delta", n_requests=1)
+    init = W.initial_state(w)
+    p16 = _pool_from_init(w, init, factor_fp16=True)
+    p32 = _pool_from_init(w, init)
+    ids = np.unique(np.concatenate([np.arange(0, w.n_states, 37), [w.n_states - 1]]))
+    off = init["comp_off"]
+    for s, a, b in zip(ids, ss.state_export(p16, ids), ss.state_export(p32, ids)):
+        U0 = init["u"][off[s]:off[s + 1]]
+        V0 = init["v"][off[s]:off[s + 1]]
+        assert np.array_equal(a["U"], U0.astype(np.float16).astype(np.float32))
+        assert np.array_equal(a["V"], V0.astype(np.float16).astype(np.float32))
+        assert np.array_equal(a["sigma"], b["sigma"]) and a["n_active"] == b["n_active"]
+    s16, s32 = ss.pool_stats(p16), ss.pool_stats(p32)
+    ncomp = s32["active_components"] + s32["frozen_components"]
+    assert s32["live_bytes"] - s16["live_bytes"] == ncomp * 2 * (w.d_k + w.d_v)
+    p16.close()
+    p32.close()
+
+
+@pytest.mark.parametrize("promote", [True, False])
+def test_fp16_tiny_lockstep(promote):
+    w = W.get("tiny")
+    init = W.initial_state(w)
+    pool = _pool_from_init(w, init, promote_on_compact=promote, max_frozen=200, factor_fp16=True)
+    worst, guard = _lockstep(w, init, pool, np.arange(w.n_states), 40, promote=promote, check_readout=True,
+                             fp16=True)
+    pool.close()
+    print("fp16 tiny", promote, worst, "guard", guard)
+    _assert_worst(worst)
+
+
+def test_fp16_mamba2_lockstep_one_request():
+    w = W.get("mamba2_258k", n_requests=1)
+    init = W.initial_state(w)
+    pool = _pool_from_init(w, init, factor_fp16=True)
+    ids = np.unique(np.concatenate([np.arange(0, w.n_states, 17), [w.n_states - 1]]))
+    worst, guard = _lockstep(w, init, pool, ids, 24, check_readout=True, fp16=True)
+    pool.close()
+    print("fp16 mamba2", worst, "guard", guard)
+    _assert_worst(worst)
+
+
+def test_fp16_gdn_delta_lockstep_one_request():
+    w = W.get("gdn_delta", n_requests=1)
+    init = W.initial_state(w)
+    pool = _pool_from_init(w, init, factor_fp16=True)
+    ids = np.unique(np.concatenate([np.arange(0, w.n_states, 13), [w.n_states - 1]]))
+    worst, guard = _lockstep(w, init, pool, ids, 24, fp16=True)
+    pool.close()
+    print("fp16 gdn", worst, "guard", guard)
+    _assert_worst(worst)
+
+
+def test_fp16_mixed_dense_lockstep():
+    """Mixed rules, ranks 2..64 (dense above 49), promotion of fp16-stored factors into the dense region."""
+    w = W.get("mixed_dense", n_requests=1)
+    init = W.initial_state(w)
+    pool = _pool_from_init(w, init, factor_fp16=True)
+    ids = np.unique(np.concatenate([np.arange(0, w.n_states, 11), [w.n_states - 1]]))
+    worst, guard = _lockstep(w, init, pool, ids, 16, fp16=True)
+    pool.close()
+    print("fp16 mixed", worst, "guard", guard)
+    _assert_worst(worst)
+
+
+@pytest.mark.parametrize("name", ["tiny", "gdn_delta"])
+def test_fp16_ring_growth_and_repack(name):
+    """fp16 rings created at the initial size: growth re-packs copy fp16 components unchanged."""
+    w = W.get(name, n_requests=1 if name != "tiny" else None)
+    init = W.initial_state(w)
+    promote = name != "tiny"
+    pool = _pool_from_init(w, init, promote_on_compact=promote, max_frozen=0 if promote else 200,
+                           arena_components=1, factor_fp16=True)
+    ids = np.unique(np.concatenate([np.arange(0, w.n_states, max(1, w.n_states // 96)), [w.n_states - 1]]))
+    worst, guard = _lockstep(w, init, pool, ids, 40 if name == "tiny" else 24, promote=promote, fp16=True)
+    st = ss.pool_stats(pool)
+    pool.close()
+    print("fp16 ring", name, worst, "guard", guard, st["ring_repacks"])
+    _assert_worst(worst)
+    assert st["ring_repacks"] >= 1
+
+
+def test_fp16_decode_bytes_accounting():
+    """The in-kernel byte counter of an fp16 pool follows the FACTORED_FP16 formula."""
+    w = W.get("gdn_delta", n_requests=1)
+    init = W.initial_state(w)
+    pool = _pool_from_init(w, init, factor_fp16=True)
+    gen = W.StepInputs(w, device="cuda")
+    o = torch.empty(w.n_states, w.d_v, device="cuda")
+    for t in range(1, w.K + 3):
+        expect = 0
+        for s in ss.state_export(pool, np.arange(w.n_states)):
+            if s["dense"]:
+                kind, nc, npad = ss.DECODE_DENSE_BUFFERED, 0, s["dense_pad"]
+            else:
+                kind, nc, npad = ss.DECODE_FACTORED_FP16, len(s["sigma"]), len(s["c"])
+            expect += ss.decode_bytes_per_state(w.d_k, w.d_v, w.K, nc, npad, s["rule"], kind)
+        b0 = ss.pool_stats(pool)["decode_bytes"]
+        x = gen.generate(t)
+        ss.decode_step(pool, x["q"], x["k"], x["v"], x["alpha"], x["beta"], o)
+        assert ss.pool_stats(pool)["decode_bytes"] - b0 == expect, t
+        for g in ss.schedule_due(pool, t):
+            ss.compact(pool, g)
+    pool.close()
