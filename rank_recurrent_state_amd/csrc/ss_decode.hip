@@ -179,6 +179,146 @@ __global__ __launch_bounds__(256) void k_decode_factored(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// factored states with fp16 factors, d_k and d_v multiples of 8: eight elements per lane, so a
+// component vector is one 16-byte load per lane (an fp32 pad vector two float4 loads), and
+// P = next power of two >= max(d_k, d_v) / 8 lanes serve a pair: twice the pairs of the fp32
+// kernel per wavefront instruction.  Same arithmetic and writes as k_decode_factored.
+// ---------------------------------------------------------------------------
+struct f8 {
+  float4 a, b;
+};
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f8 zero8() { return {zero4(), zero4()}; }
+__device__ __forceinline__ f8 ld8nt(const float *p) { return {ld4nt(p), ld4nt(p + 4)}; }
+__device__ __forceinline__ f8 ldh8nt(const _Float16 *p) {
+  const half8_t h = __builtin_nontemporal_load(reinterpret_cast<const half8_t *>(p));
+  return {make_float4((float)h[0], (float)h[1], (float)h[2], (float)h[3]),
+          make_float4((float)h[4], (float)h[5], (float)h[6], (float)h[7])};
+}
+__device__ __forceinline__ f8 sel8(bool ok, f8 x) { return {sel4(ok, x.a), sel4(ok, x.b)}; }
+__device__ __forceinline__ float dot8(f8 x, f8 y) { return dot4(x.a, y.a) + dot4(x.b, y.b); }
+__device__ __forceinline__ f8 fma8(float s, f8 x, f8 c) { return {fma4(s, x.a, c.a), fma4(s, x.b, c.b)}; }
+__device__ __forceinline__ f8 scale8(float s, f8 x) { return {scale4(s, x.a), scale4(s, x.b)}; }
+__device__ __forceinline__ f8 add8(f8 x, f8 y) { return {add4(x.a, y.a), add4(x.b, y.b)}; }
+__device__ __forceinline__ f8 sub8(f8 x, f8 y) { return {sub4(x.a, y.a), sub4(x.b, y.b)}; }
+__device__ __forceinline__ void st8(float *p, f8 x) {
+  st4(p, x.a);
+  st4(p + 4, x.b);
+}
+__device__ __forceinline__ void st8nt(float *p, f8 x) {
+  st4nt(p, x.a);
+  st4nt(p + 4, x.b);
+}
+template <int P>
+__device__ __forceinline__ f8 cross_group_sum8(f8 x) {
+  return {cross_group_sum4<P>(x.a), cross_group_sum4<P>(x.b)};
+}
+
+template <int P, int UN, bool RO, bool ANYDELTA>
+__global__ __launch_bounds__(256) void k_decode_factored_h8(DecodeArgs a) {
+  constexpr int G = 64 / P;
+  const int lane = threadIdx.x & 63;
+  const uint32_t li = blockIdx.x * 4u + (uint32_t)uniform(threadIdx.x >> 6);
+  if (li >= *a.fact_count) return;
+  const int64_t s = uniform(a.fact_ids[li]);
+  const int grp = lane / P, col = lane % P;
+  const int dk = a.dk, dv = a.dv, K = a.K;
+  const bool kin = col < (dk >> 3), vin = col < (dv >> 3);
+  const int colk = kin ? col : (dk >> 3) - 1, colv = vin ? col : (dv >> 3) - 1;  // clamped: loads stay in bounds
+  const Meta m = a.meta[s];
+  const uint32_t packed = (uint32_t)uniform((int)m.packed);
+  const uint32_t flags = meta_flags(packed);
+  if (flags & FLAG_DENSE) return;
+  const int ra = meta_ra(packed), rf = meta_rf(packed), n = meta_n(packed);
+  const int off_a = uniform(m.off_a), off_f = uniform(m.off_f);
+  const float gamma = uniformf(m.gamma);
+  if (!RO && n >= K) {
+    if (lane == 0) {
+      __hip_atomic_fetch_add(&a.counters[C_ERR_PAD], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *a.hflag = 1u;
+    }
+    return;
+  }
+  const int rr = ra + rf, T = rr + n;
+  const int64_t pad0 = s * (int64_t)K - rr;
+  const f8 q8 = sel8(kin, ld8nt(a.q + s * dk + 8 * colk));
+  const f8 k8 = RO ? zero8() : sel8(kin, ld8nt(a.k + s * dk + 8 * colk));
+  const f8 v8 = RO ? zero8() : sel8(vin, ld8nt(a.v + s * dv + 8 * colv));
+  const bool delta = ANYDELTA && !RO && (flags & FLAG_DELTA);
+  const float al = RO ? 1.f : uniformf(a.alpha[s]);
+  const float be = delta ? uniformf(a.beta[s]) : 0.f;
+  f8 acc = zero8(), acck = zero8();
+  auto stream = [&](int ib, int ie, auto ld) {
+    for (int i0 = ib; i0 < ie; i0 += G * UN) {
+      f8 x[UN], y[UN];
+      float wt[UN];
+#pragma unroll
+      for (int u = 0; u < UN; ++u) {
+        const int iu = i0 + u * G + grp;
+        ld(iu < ie ? iu : ie - 1, x[u], y[u], wt[u]);  // clamped pair; its weight is masked at use
+      }
+#pragma unroll
+      for (int u = 0; u < UN; ++u) {
+        const float wu = (i0 + u * G + grp < ie) ? wt[u] : 0.f;
+        const float cq = group_sum<P>(dot8(x[u], q8)) * wu;
+        acc = fma8(cq, y[u], acc);
+        if (delta) {
+          const float ck = group_sum<P>(dot8(x[u], k8)) * wu;
+          acck = fma8(ck, y[u], acck);
+        }
+      }
+    }
+  };
+  stream(0, rr, [&](int i, f8 &x, f8 &y, float &w) {
+    const bool act = i < ra;
+    const int64_t c = act ? wrap(off_a + i, a.act.cap) : wrap(off_f + (i - ra), a.frz.cap);
+    const Arena &ar = act ? a.act : a.frz;
+    x = ldh8nt(ar.U<_Float16>() + c * dk + 8 * colk);
+    y = ldh8nt(ar.V<_Float16>() + c * dv + 8 * colv);
+    w = ldnt(ar.s + c);
+  });
+  stream(rr, T, [&](int i, f8 &x, f8 &y, float &w) {
+    const int64_t c = pad0 + i;
+    x = ld8nt(a.pk + c * dk + 8 * colk);
+    y = ld8nt(a.pw + c * dv + 8 * colv);
+    w = ldnt(a.pc + c);
+  });
+  acc = cross_group_sum8<P>(acc);
+  const f8 pq = scale8(gamma, acc);
+  if constexpr (RO) {
+    if (grp == 0 && vin) st8(a.o + s * dv + 8 * col, pq);
+    return;
+  } else {
+    f8 w8 = v8;
+    if (delta) {
+      acck = cross_group_sum8<P>(acck);
+      w8 = scale8(be, sub8(v8, scale8(al * gamma, acck)));
+    }
+    const float kq = group_sum<P>(dot8(k8, q8));
+    const f8 o8 = add8(scale8(al, pq), scale8(kq, w8));
+    const float gnew = al * gamma;
+    if (grp == 0) {
+      if (kin) st8nt(a.pk + (s * (int64_t)K + n) * dk + 8 * col, k8);
+      if (vin) {
+        st8nt(a.pw + (s * (int64_t)K + n) * dv + 8 * col, w8);
+        st8(a.o + s * dv + 8 * col, o8);
+      }
+    }
+    if (lane == 0) {
+      a.pc[s * (int64_t)K + n] = 1.0f / gnew;
+      Meta nm;
+      nm.off_a = off_a;
+      nm.off_f = off_f;
+      nm.gamma = gnew;
+      nm.packed = meta_pack(ra, rf, n + 1, flags);
+      a.meta[s] = nm;
+      const unsigned long long b = decode_bytes(dk, dv, K, rr, n, delta, KIND_FACTORED, 2);
+      __hip_atomic_fetch_add(&a.acct[s & (kAcctSlots - 1)], b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dense states, H = S^T stored [d_v][d_k]
 // ---------------------------------------------------------------------------
 constexpr int kMaxPad = 8;
@@ -534,6 +674,24 @@ hipError_t decode_factored_p(const DecodeArgs &a, int P, hipStream_t st) {
   return hipGetLastError();
 }
 
+#ifndef SS_FACT_H8_UN
+#define SS_FACT_H8_UN 4
+#endif
+template <bool RO, bool AD>
+hipError_t decode_factored_h8_p(const DecodeArgs &a, int P, hipStream_t st) {
+  const dim3 grid((unsigned)((a.N + 3) / 4)), block(256);
+  switch (P) {
+    case 1: hipLaunchKernelGGL((k_decode_factored_h8<1, 1, RO, AD>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_decode_factored_h8<2, 1, RO, AD>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((k_decode_factored_h8<4, 2, RO, AD>), grid, block, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((k_decode_factored_h8<8, 2, RO, AD>), grid, block, 0, st, a); break;
+    case 16: hipLaunchKernelGGL((k_decode_factored_h8<16, SS_FACT_H8_UN, RO, AD>), grid, block, 0, st, a); break;
+    case 32: hipLaunchKernelGGL((k_decode_factored_h8<32, 4, RO, AD>), grid, block, 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <typename F>
 hipError_t decode_factored_f(const DecodeArgs &a, bool readonly, bool any_delta, int P, hipStream_t st) {
   if (readonly) return decode_factored_p<true, false, F>(a, P, st);
@@ -594,6 +752,11 @@ int lanes_per_pair(int dk, int dv) { return pow2_at_least((dk > dv ? dk : dv) >>
 hipError_t launch_decode_factored(const DecodeArgs &a, bool readonly, bool any_delta, hipStream_t st) {
   if (a.N <= 0) return hipSuccess;
   const int P = lanes_per_pair(a.dk, a.dv);
+  if (a.act.half && a.dk % 8 == 0 && a.dv % 8 == 0) {  // fp16 factors, eight elements per lane
+    const int P8 = pow2_at_least((a.dk > a.dv ? a.dk : a.dv) >> 3);
+    if (readonly) return decode_factored_h8_p<true, false>(a, P8, st);
+    return any_delta ? decode_factored_h8_p<false, true>(a, P8, st) : decode_factored_h8_p<false, false>(a, P8, st);
+  }
   if (a.act.half) return decode_factored_f<_Float16>(a, readonly, any_delta, P, st);
   return decode_factored_f<float>(a, readonly, any_delta, P, st);
 }

@@ -194,11 +194,15 @@ def test_decode_bytes_accounting():
             assert folds > 0
 
 
-def test_edge_shapes_and_ragged():
+@pytest.mark.parametrize("fp16", [False, True])
+def test_edge_shapes_and_ragged(fp16):
     """d = 4 (one lane per vector), 37 states (ragged workgroups), K = 1 (compaction every
-    step), r = 1, empty states, delta rule, against the oracle in lock-step."""
+    step), r = 1, empty states, delta rule, against the oracle in lock-step.  With fp16 factors
+    the shapes cover both decode kernels: eight elements per lane (d_k, d_v multiples of 8) and
+    four (the rest)."""
     rng = np.random.default_rng(5)
-    for (dk, dv, K, r, N) in [(4, 8, 1, 1, 37), (12, 20, 3, 2, 37), (64, 44, 8, 8, 9)]:
+    for (dk, dv, K, r, N) in [(4, 8, 1, 1, 37), (12, 20, 3, 2, 37), (64, 44, 8, 8, 9), (8, 256, 2, 3, 37),
+                              (256, 16, 8, 8, 13)]:
         R = rng.integers(0, 6, N)
         R[0] = 0
         off = np.concatenate([[0], np.cumsum(R)]).astype(np.int64)
@@ -209,7 +213,7 @@ def test_edge_shapes_and_ragged():
         rule = (np.arange(N) % 2).astype(np.uint8)
         eps = np.full(N, 1e-3, np.float32)
         pool = ss.state_pool_create(N, dk, dv, K, r, rule=rule, eps=eps, comp_off=off, u=u, v=v, sigma=sig,
-                                    group_offset=[0], promote_on_compact=False, max_frozen=64)
+                                    group_offset=[0], promote_on_compact=False, max_frozen=64, factor_fp16=fp16)
         o = torch.empty(N, dv, device="cuda")
         ids = np.arange(N)
         worst = 0.0
@@ -220,7 +224,9 @@ def test_edge_shapes_and_ragged():
             a = 0.9 + 0.1 * torch.rand(N, device="cuda")
             b = torch.rand(N, device="cuda")
             before = ss.state_export(pool, ids)
-            P = oracle_from_export(before, eps, dk, dv, K, r, promote=False)
+            if fp16:
+                _assert_fp16_factors(before)
+            P = oracle_from_export(before, eps, dk, dv, K, r, promote=False, factor_fp16=fp16)
             ss.decode_step(pool, q, k, vv, a, b, o)
             if ss.schedule_due(pool, t):
                 ss.compact(pool, 0)
@@ -231,7 +237,7 @@ def test_edge_shapes_and_ragged():
             worst = max(worst, float(e.max()))
             if ss.schedule_due(pool, t):
                 P.compact()
-                ws, wsig, gd, bad = compare_compacted(ss.state_export(pool, ids), P, eps)
+                ws, wsig, gd, bad = compare_compacted(ss.state_export(pool, ids), P, eps, fp16=fp16)
                 assert not bad and ws <= TOL and wsig <= TOL, (dk, dv, K, r, ws, wsig, bad)
         pool.close()
         assert worst <= TOL, (dk, dv, K, r, worst)
