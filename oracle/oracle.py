@@ -66,6 +66,7 @@ def _load():
     lib.orc_round_fp16.restype = ctypes.c_double
     lib.orc_round_fp16.argtypes = [ctypes.c_double]
     lib.orc_set_factor_fp16.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    lib.orc_set_diag_decay.argtypes = [ctypes.c_void_p, ctypes.c_int]
     lib.orc_consolidate.restype = ctypes.c_int64
     lib.orc_consolidate.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64), ctypes.c_int64, ctypes.c_int]
     lib.orc_householder_qr.argtypes = [ctypes.c_int, ctypes.c_int, _dp, _dp, _dp]
@@ -194,7 +195,7 @@ class OracleState:
 class OraclePool:
     """A pool of N states held by the C oracle."""
 
-    def __init__(self, n_states, d_k, d_v, K=8, r=8, L=-1, promote=True, factor_fp16=False):
+    def __init__(self, n_states, d_k, d_v, K=8, r=8, L=-1, promote=True, factor_fp16=False, diag_decay=False):
         lib = _load()
         self._lib = lib
         self.N, self.d_k, self.d_v, self.K, self.r = int(n_states), int(d_k), int(d_v), int(K), int(r)
@@ -202,6 +203,8 @@ class OraclePool:
         if not self._p:
             raise MemoryError("orc_create failed")
         lib.orc_set_factor_fp16(self._p, int(bool(factor_fp16)))
+        lib.orc_set_diag_decay(self._p, int(bool(diag_decay)))
+        self.diag_decay = bool(diag_decay)
         self.L = int(lib.orc_dense_limit(self._p))
 
     def close(self):
@@ -275,7 +278,7 @@ class OraclePool:
         q = _f64(q).reshape(N, dk)
         k = _f64(k).reshape(N, dk)
         v = _f64(v).reshape(N, dv)
-        alpha = _f64(alpha).reshape(N)
+        alpha = _f64(alpha).reshape((N, dk) if self.diag_decay else N)  # per-channel decay: [N][d_k]
         b = None if beta is None else _f64(beta).reshape(N)
         o = np.zeros((N, dv))
         bad = self._lib.orc_decode(self._p, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(o), int(nthreads))

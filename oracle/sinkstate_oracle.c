@@ -34,6 +34,15 @@
  *             composes"): every factor vector written (initial factors,
  *             compaction and consolidation results) is rounded to binary16;
  *             sigma and the pad keep full precision.
+ *   diag      optional per-channel decay (Kimi Delta Attention; SEED
+ *             appendix B.1 eq. (6): S_t = (I - theta b k k^T) Lambda S_{t-1}
+ *             + b k v^T with Lambda = diag(lambda_1..lambda_dk)).  Written as
+ *             S_t = Lambda S_{t-1} + k w^T with w = b (v - S_{t-1}^T Lambda k)
+ *             (delta rule) or w = v (scalar rule).  Applied literally: every
+ *             factor u_i and every pad key is multiplied by Lambda each step
+ *             (SEED Lemma 2: U+ = [Lambda U, k]); at a compaction the frozen
+ *             components are renormalized (sigma_f <- sigma_f |u_f|,
+ *             u_f <- u_f / |u_f|) and re-sorted before the merge.
  *
  * Decay is applied literally, every step, to every sigma and pad weight.  QR
  * is Householder, the small SVD is cyclic one-sided (Hestenes) Jacobi, both
@@ -72,6 +81,7 @@ typedef struct {
   int64_t N;
   int d_k, d_v, K, r, L, promote;
   int fp16;     /* factor vectors stored in fp16: rounded whenever they are written */
+  int diag;     /* per-channel decay: alpha is [N][d_k] */
   orc_state *st;
 } orc_pool;
 
@@ -108,6 +118,7 @@ static void round_rows(double *A, size_t n) {
 }
 
 void orc_set_factor_fp16(orc_pool *p, int on) { p->fp16 = on ? 1 : 0; }
+void orc_set_diag_decay(orc_pool *p, int on) { p->diag = on ? 1 : 0; }
 
 static int ensure_cap(orc_state *s, int need, int d_k, int d_v) {
   if (need <= s->cap) return 0;
@@ -480,6 +491,48 @@ static void dense_apply_t(const orc_pool *p, const double *S, const double *vec,
 
 /* One decode step of one state: returns 0, or -2 if the pad is full (the
  * caller's compaction schedule missed this state). */
+/* One decode step with per-channel decay lam[0..d_k-1] (Kimi Delta Attention,
+ * SEED appendix B.1 eq. (6)), applied literally; tmp holds d_k doubles. */
+static int decode_one_diag(orc_pool *p, orc_state *x, const double *q, const double *k, const double *v,
+                           const double *lam, double beta, double *o, double *w, double *tmp) {
+  int dk = p->d_k, dv = p->d_v;
+  double lmax = 0.0;
+  for (int a = 0; a < dk; ++a) lmax = lam[a] > lmax ? lam[a] : lmax;
+  if (x->dense) {
+    if (x->rule == ORC_DELTA) {
+      for (int a = 0; a < dk; ++a) tmp[a] = lam[a] * k[a];
+      dense_apply_t(p, x->S, tmp, w); /* S_{t-1}^T Lambda k */
+      for (int b = 0; b < dv; ++b) w[b] = beta * (v[b] - w[b]);
+    } else {
+      for (int b = 0; b < dv; ++b) w[b] = v[b];
+    }
+    for (int a = 0; a < dk; ++a)
+      for (int b = 0; b < dv; ++b) x->S[(size_t)a * dv + b] = lam[a] * x->S[(size_t)a * dv + b] + k[a] * w[b];
+    dense_apply_t(p, x->S, q, o);
+    x->bound *= lmax;
+    return 0;
+  }
+  if (x->n >= p->K) return -2;
+  /* Lambda S~: every u_i and every pad key, channel by channel */
+  for (int i = 0; i < x->R; ++i)
+    for (int a = 0; a < dk; ++a) x->U[(size_t)i * dk + a] *= lam[a];
+  for (int j = 0; j < x->n; ++j)
+    for (int a = 0; a < dk; ++a) x->PK[(size_t)j * dk + a] *= lam[a];
+  if (x->rule == ORC_DELTA) {
+    factored_apply_t(p, x, k, w); /* (Lambda S~_{t-1})^T k = S~_{t-1}^T Lambda k */
+    for (int b = 0; b < dv; ++b) w[b] = beta * (v[b] - w[b]);
+  } else {
+    for (int b = 0; b < dv; ++b) w[b] = v[b];
+  }
+  memcpy(x->PK + (size_t)x->n * dk, k, dk * sizeof(double));
+  memcpy(x->PW + (size_t)x->n * dv, w, dv * sizeof(double));
+  x->pc[x->n] = 1.0;
+  x->n += 1;
+  factored_apply_t(p, x, q, o);
+  x->bound *= lmax;
+  return 0;
+}
+
 static int decode_one(orc_pool *p, orc_state *x, const double *q, const double *k, const double *v, double alpha,
                       double beta, double *o, double *w) {
   int dk = p->d_k, dv = p->d_v;
@@ -515,8 +568,9 @@ static int decode_one(orc_pool *p, orc_state *x, const double *q, const double *
 }
 
 /* All states, one step.  Inputs are [N][d] row-major; beta may be NULL when
- * no state uses the delta rule.  Returns 0 or the number of states whose pad
- * was already full (their step is skipped). */
+ * no state uses the delta rule; alpha is [N], or [N][d_k] in a pool with
+ * per-channel decay.  Returns 0 or the number of states whose pad was already
+ * full (their step is skipped). */
 int64_t orc_decode(orc_pool *p, const double *q, const double *k, const double *v, const double *alpha,
                    const double *beta, double *o, int nthreads) {
   int64_t bad = 0;
@@ -526,9 +580,12 @@ int64_t orc_decode(orc_pool *p, const double *q, const double *k, const double *
 #pragma omp parallel for schedule(dynamic, 16) num_threads(nthreads) reduction(+ : bad)
 #endif
   for (int64_t s = 0; s < p->N; ++s) {
-    double w[1024];
+    double w[1024], tmp[1024];
     double b = beta ? beta[s] : 0.0;
-    if (decode_one(p, &p->st[s], q + s * dk, k + s * dk, v + s * dv, alpha[s], b, o + s * dv, w)) bad += 1;
+    int rc = p->diag ? decode_one_diag(p, &p->st[s], q + s * dk, k + s * dk, v + s * dv, alpha + s * dk, b,
+                                       o + s * dv, w, tmp)
+                     : decode_one(p, &p->st[s], q + s * dk, k + s * dk, v + s * dv, alpha[s], b, o + s * dv, w);
+    if (rc) bad += 1;
   }
   (void)nthreads;
   return bad;
@@ -563,10 +620,49 @@ int orc_readout(const orc_pool *p, const double *q, double *o, int nthreads) {
  *  6. with promotion on, a state left with more than L components is
  *     re-stored dense (the memory test of SinkState 4.4, applied again).
  * An empty pad leaves the state unchanged. */
+/* Per-channel decay leaves the frozen u_f scaled by Lambda: give them unit
+ * norm again (sigma takes the norm; a zero vector gets sigma 0 and is
+ * dropped by the merge) and sort the frozen part by the new sigma,
+ * descending, equal values in their stored order (insertion sort). */
+static void renormalize_frozen(orc_pool *p, orc_state *x, int ra) {
+  int dk = p->d_k, dv = p->d_v;
+  for (int f = ra; f < x->R; ++f) {
+    double *u = x->U + (size_t)f * dk;
+    double nrm = sqrt(dot(u, u, dk));
+    if (nrm > 0.0) {
+      for (int a = 0; a < dk; ++a) u[a] /= nrm;
+      x->sig[f] *= nrm;
+    } else {
+      x->sig[f] = 0.0;
+    }
+  }
+  double *tu = (double *)malloc((size_t)dk * sizeof(double));
+  double *tv = (double *)malloc((size_t)dv * sizeof(double));
+  if (!tu || !tv) { free(tu); free(tv); return; }
+  for (int f = ra + 1; f < x->R; ++f) {
+    double sg = x->sig[f];
+    memcpy(tu, x->U + (size_t)f * dk, dk * sizeof(double));
+    memcpy(tv, x->V + (size_t)f * dv, dv * sizeof(double));
+    int g = f;
+    while (g > ra && x->sig[g - 1] < sg) {
+      x->sig[g] = x->sig[g - 1];
+      memcpy(x->U + (size_t)g * dk, x->U + (size_t)(g - 1) * dk, dk * sizeof(double));
+      memcpy(x->V + (size_t)g * dv, x->V + (size_t)(g - 1) * dv, dv * sizeof(double));
+      --g;
+    }
+    x->sig[g] = sg;
+    memcpy(x->U + (size_t)g * dk, tu, dk * sizeof(double));
+    memcpy(x->V + (size_t)g * dv, tv, dv * sizeof(double));
+  }
+  free(tu);
+  free(tv);
+}
+
 static int compact_one(orc_pool *p, orc_state *x) {
   int dk = p->d_k, dv = p->d_v;
   if (x->dense || x->n == 0) return 0;
   int ra = x->R < p->r ? x->R : p->r;
+  if (p->diag) renormalize_frozen(p, x, ra);
   int m = ra + x->n;
   int pr = dv < m ? dv : m;
   int nf = x->R - ra;
