@@ -30,7 +30,8 @@ METRIC = "state-steps/sec and achieved HBM GB/s (% peak) for decode_step, 258k s
 def _pool(ss, w, init, **kw):
     return ss.state_pool_create(w.n_states, w.d_k, w.d_v, w.K, w.r, group_of_state=init["group_of_state"],
                                 group_offset=init["group_offset"], rule=init["rule"], eps=init["eps"],
-                                comp_off=init["comp_off"], u=init["u"], v=init["v"], sigma=init["sigma"], **kw)
+                                comp_off=init["comp_off"], u=init["u"], v=init["v"], sigma=init["sigma"],
+                                diag_decay=w.diag_decay, **kw)
 
 
 def _run_steps(ss, torch, pool, xs, t0, o, ev=None, cons=(0, 1)):
@@ -131,7 +132,7 @@ def cpu_baseline(w, init, n_sample, n_steps, device="cpu"):
 
     rng = np.random.default_rng(7)
     ids = np.sort(rng.choice(w.n_states, size=min(n_sample, w.n_states), replace=False))
-    P = OraclePool(len(ids), w.d_k, w.d_v, w.K, w.r, -1, True)
+    P = OraclePool(len(ids), w.d_k, w.d_v, w.K, w.r, -1, True, diag_decay=w.diag_decay)
     off = init["comp_off"]
     for j, s in enumerate(ids):
         a, b = off[s], off[s + 1]
@@ -251,7 +252,7 @@ def main():
     fkw = {"factor_fp16": True} if args.factor_fp16 else {}
     if args.warmup > 0:
         pool = _pool(ss, w, init, **fkw)
-        wchunk = max(1, min(args.chunk, int(16e9 // (w.n_states * (2 * w.d_k + w.d_v + 2) * 4))))
+        wchunk = max(1, min(args.chunk, int(16e9 // (w.n_states * (2 * w.d_k + w.d_v + 2 + (w.d_k if w.diag_decay else 0)) * 4))))
         for c0 in range(0, args.warmup, wchunk):
             xs = [gen.generate(t) for t in range(c0 + 1, min(args.warmup, c0 + wchunk) + 1)]
             _run_steps(ss, torch, pool, xs, c0, o, cons=cons)
@@ -268,7 +269,7 @@ def main():
     hist_marks = {}
     t = 0
     # inputs of a chunk are generated at once: keep them within about 16 GB
-    chunk = max(1, min(args.chunk, int(16e9 // (w.n_states * (2 * w.d_k + w.d_v + 2) * 4))))
+    chunk = max(1, min(args.chunk, int(16e9 // (w.n_states * (2 * w.d_k + w.d_v + 2 + (w.d_k if w.diag_decay else 0)) * 4))))
     while t < K_steps:
         n = min(chunk, K_steps - t)
         xs = [gen.generate(s) for s in range(t + 1, t + n + 1)]

@@ -94,6 +94,16 @@ typedef struct {
                                  test keeps the same L.  A stored component then takes
                                  2 (d_k + d_v) + 4 bytes instead of 4 (d_k + d_v + 1).
                                  0: fp32 factors.  Other values: SS_ERR_ARG. */
+  int32_t diag_decay;         /* 1: per-channel decay (Kimi Delta Attention; [SEED] appendix B.1
+                                 eq. (6): Lambda_t = diag(lambda_1 .. lambda_{d_k}), one decay
+                                 per key channel): ss_decode_step's alpha is [n_states][d_k]
+                                 and a step is S_t = Lambda_t S_{t-1} + k w^T with
+                                 w = beta (v - S_{t-1}^T Lambda_t k) (delta rule) or w = v.
+                                 The pool keeps the decays accumulated since the last
+                                 compaction per state and key channel (d_k floats per state,
+                                 and per dense slot); a compaction folds them into the
+                                 factors.  Consolidation is not available on such a pool
+                                 (SS_ERR_ARG).  0: scalar decay, alpha is [n_states]. */
 } ss_pool_desc;
 
 /* Initial states, host memory, copied during create.  Components of state s
@@ -173,7 +183,7 @@ ss_status ss_state_pool_destroy(ss_pool *pool);
  * region holds H = S^T and a pad, a step appends to the pad, and the step
  * that fills the pad folds it into H (exact algebra, no truncation).  In a
  * force_dense pool (the dense baseline) every step runs S <- alpha S + k w^T.
- * q, k: [N][d_k]; v, o: [N][d_v]; alpha: [N] in (0, 1]; beta: [N], may be
+ * q, k: [N][d_k]; v, o: [N][d_v]; alpha: [N] in (0, 1] ([N][d_k] in a diag_decay pool); beta: [N], may be
  * NULL when no state uses the delta rule.  A factored state whose pad is
  * already full poisons the pool (SS_ERR_STATE on the next call): compact its
  * group first. */

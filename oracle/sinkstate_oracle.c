@@ -406,7 +406,8 @@ int orc_set_state(orc_pool *p, int64_t s, int rule, double eps, int R, const dou
   }
   free(ord);
   x->R = R;
-  if (p->fp16) {
+  if (p->fp16 && as_init) {  /* initial factors are written in fp16; a mid-run state is taken as given
+                                (with per-channel decay its u carry the decays since the last compaction) */
     round_rows(x->U, (size_t)R * dk);
     round_rows(x->V, (size_t)R * dv);
   }

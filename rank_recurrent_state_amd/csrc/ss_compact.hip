@@ -40,6 +40,9 @@ constexpr int kMaxFrozen = 256;  // frozen components per state (max_frozen <= 2
 constexpr int kOffRl = 0, kOffRr = 256, kOffCm = 512, kOffVh = 768, kOffScw = 1024, kOffSgs = 1040, kOffSraw = 1056,
               kOffPerm = 1072, kOffPosL = 1088, kOffFs = 1104, kOffPosF = kOffFs + kMaxFrozen,
               kLdsPerWave = kOffPosF + kMaxFrozen;
+// per-channel decay adds, per wavefront: the frozen sigma before sorting, the sorted order, the norms
+constexpr int kOffFraw = kLdsPerWave, kOffForig = kOffFraw + kMaxFrozen, kOffFnorm = kOffForig + kMaxFrozen,
+              kLdsPerWaveDiag = kOffFnorm + kMaxFrozen;
 
 // copy one fp32 component (u, v) into factor storage of type F, with float4 lanes
 template <typename F>
@@ -86,9 +89,14 @@ __device__ __forceinline__ void copy_comps(const Arena &src, int64_t c0, int cnt
   }
 }
 
-template <int NS, typename F>
+// DIAG (per-channel decay): the state is diag(gamma) times its stored parts, gamma holding the
+// decays accumulated per key channel since the last compaction.  The active columns and the pad
+// keys enter the QR scaled by gamma; each frozen u_f is scaled by gamma and given unit norm again
+// (sigma_f takes the norm), and the frozen list is re-sorted by the new sigma (stored order on
+// ties) before the merge; gamma is reset to 1.
+template <int NS, typename F, bool DIAG>
 __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
-  __shared__ float lds[4][kLdsPerWave];
+  __shared__ float lds[4][DIAG ? kLdsPerWaveDiag : kLdsPerWave];
   __shared__ int wg_cnt[4][2];
   __shared__ unsigned long long wg_base[2];
   __shared__ int wg_ok;
@@ -133,9 +141,63 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   const int mcol = ra + n;
   int kl = 0, kf = 0, total = 0, ra2 = ra, rf2 = rf, sweeps = 0;
   float uc[kMaxM][NS], vc[kMaxM][NS];
+  float gr[NS];  // DIAG: the state's decays, row lane + 64 t (0 past d_k)
+#pragma unroll
+  for (int t = 0; t < NS; ++t) gr[t] = 1.f;
+  if (DIAG && work) {
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+      const int row = lane + 64 * t;
+      gr[t] = self(row < dk, a.gam[(int64_t)s * dk + (row < dk ? row : dk - 1)]);
+    }
+  }
   if (work) {
-    // frozen singular values (scaled by Gamma) to LDS: the merge searches them there
-    for (int f = lane; f < rf; f += 64) fsl[f] = a.frz.s[wrap(off_f + f, capF)] * gamma;
+    if constexpr (DIAG) {
+      float *fraw = lds[w] + kOffFraw, *fnrm = lds[w] + kOffFnorm;
+      int *forig = reinterpret_cast<int *>(lds[w] + kOffForig);
+      // norms |gamma u_f|, four components in flight
+      for (int f0 = 0; f0 < rf; f0 += 4) {
+        float x[4][NS];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int f = f0 + c < rf ? f0 + c : rf - 1;  // clamped (rf >= 1 inside the loop)
+          const F *fu = a.frz.U<F>() + wrap(off_f + f, capF) * dk;
+#pragma unroll
+          for (int t = 0; t < NS; ++t) {
+            const int row = lane + 64 * t;
+            x[c][t] = ldf(fu + (row < dk ? row : dk - 1));
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          float acc = 0.f;
+#pragma unroll
+          for (int t = 0; t < NS; ++t) {
+            const float y = x[c][t] * gr[t];
+            acc = fmaf(y, y, acc);
+          }
+          acc = wave_sum(acc);
+          if (lane == 0 && f0 + c < rf) fnrm[f0 + c] = sqrtf(acc);
+        }
+      }
+      wave_sync();
+      for (int f = lane; f < rf; f += 64) fraw[f] = a.frz.s[wrap(off_f + f, capF)] * fnrm[f];
+      wave_sync();
+      for (int f = lane; f < rf; f += 64) {  // descending, stored order on ties
+        const float x = fraw[f];
+        int rk = 0;
+        for (int g = 0; g < rf; ++g) {
+          const float y = fraw[g];
+          rk += (y > x) || (y == x && g < f);
+        }
+        fsl[rk] = x;
+        forig[rk] = f;
+      }
+      wave_sync();
+    } else {
+      // frozen singular values (scaled by Gamma) to LDS: the merge searches them there
+      for (int f = lane; f < rf; f += 64) fsl[f] = a.frz.s[wrap(off_f + f, capF)] * gamma;
+    }
 #pragma unroll
     for (int jj = 0; jj < kMaxM; ++jj) {
       const bool valid = jj < mcol;
@@ -160,6 +222,10 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
           uc[jj][t] = self(valid && row < dk, ldf(su + (row < dk ? row : dk - 1)));
           vc[jj][t] = self(valid && row < dv, ldf(sv + (row < dv ? row : dv - 1)));
         }
+      }
+      if constexpr (DIAG) {  // active columns and pad keys carry the decays
+#pragma unroll
+        for (int t = 0; t < NS; ++t) uc[jj][t] *= gr[t];
       }
     }
     if (lane < kMaxM) {
@@ -345,14 +411,42 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
     }
   }
   if (lane < kl && posL[lane] < total) *slot_s(posL[lane]) = sgs[lane];
-  // kept frozen components: copied, sigma scaled by Gamma
-  copy_comps<F>(a.frz, off_f, kf, dk, dv, lane, [&](int f, F *&du, F *&dvp) {
-    const int pos = posF[f];
-    if (pos >= total) return false;
-    du = slot_u(pos);
-    dvp = slot_v(pos);
-    return true;
-  });
+  if constexpr (DIAG) {
+    // kept frozen components in sorted order: u <- gamma u / |gamma u|, v copied; gamma <- 1
+    const float *fnrm = lds[w] + kOffFnorm;
+    const int *forig = reinterpret_cast<const int *>(lds[w] + kOffForig);
+    for (int f = 0; f < kf; ++f) {
+      const int pos = posF[f];
+      if (pos >= total) continue;
+      const int src = forig[f];
+      const int64_t cs = wrap(off_f + src, capF);
+      const float inv = 1.0f / fnrm[src];
+      const F *su = a.frz.U<F>() + cs * dk;
+      const F *sv = a.frz.V<F>() + cs * dv;
+      F *du = slot_u(pos);
+      F *dvv = slot_v(pos);
+#pragma unroll
+      for (int t = 0; t < NS; ++t) {
+        const int row = lane + 64 * t;
+        if (row < dk) stf(du + row, ldf(su + row) * gr[t] * inv);
+        if (row < dv) stf(dvv + row, ldf(sv + row));
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+      const int row = lane + 64 * t;
+      if (row < dk) a.gam[(int64_t)s * dk + row] = 1.f;
+    }
+  } else {
+    // kept frozen components: copied, sigma scaled by Gamma
+    copy_comps<F>(a.frz, off_f, kf, dk, dv, lane, [&](int f, F *&du, F *&dvp) {
+      const int pos = posF[f];
+      if (pos >= total) return false;
+      du = slot_u(pos);
+      dvp = slot_v(pos);
+      return true;
+    });
+  }
   for (int f = lane; f < kf; f += 64) {
     const int pos = posF[f];
     if (pos < total) *slot_s(pos) = fsl[f];
@@ -446,6 +540,8 @@ __global__ __launch_bounds__(256) void k_materialize(MaterializeArgs a) {
     __syncthreads();
     const int slot = s_slot;
     if (slot < 0) continue;
+    if (a.dgam)  // per-channel decay: the new slot starts with no decay accumulated
+      for (int e = t; e < dk; e += 256) a.dgam[(int64_t)slot * dk + e] = 1.f;
     const int total = n1 + n2;
     float *H = a.dense + (int64_t)slot * dk * dv;
     const int64_t di = a.dsrc_idx ? a.dsrc_idx[s] : -1;
@@ -715,24 +811,29 @@ __global__ void k_zero_u32(uint32_t *p, int n) {
   if (i < n) p[i] = 0u;
 }
 
+__global__ void k_fill_f32(float *p, int64_t n, float x) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = x;
+}
+
+template <typename F, bool DG>
+hipError_t compact_ns(const CompactArgs &a, int ns, hipStream_t st) {
+  const dim3 grid((unsigned)((a.n_members + 3) / 4)), block(256);
+  if (ns == 1) hipLaunchKernelGGL((k_compact<1, F, DG>), grid, block, 0, st, a);
+  else if (ns == 2) hipLaunchKernelGGL((k_compact<2, F, DG>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((k_compact<4, F, DG>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_compact(const CompactArgs &a, hipStream_t st) {
   if (a.n_members <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((a.n_members + 3) / 4)), block(256);
   const int d = a.dk > a.dv ? a.dk : a.dv;
   const int ns = d <= 64 ? 1 : d <= 128 ? 2 : d <= 256 ? 4 : 0;
   if (ns == 0) return hipErrorInvalidValue;
-  if (a.act.half) {
-    if (ns == 1) hipLaunchKernelGGL((k_compact<1, _Float16>), grid, block, 0, st, a);
-    else if (ns == 2) hipLaunchKernelGGL((k_compact<2, _Float16>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k_compact<4, _Float16>), grid, block, 0, st, a);
-  } else {
-    if (ns == 1) hipLaunchKernelGGL((k_compact<1, float>), grid, block, 0, st, a);
-    else if (ns == 2) hipLaunchKernelGGL((k_compact<2, float>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k_compact<4, float>), grid, block, 0, st, a);
-  }
-  return hipGetLastError();
+  if (a.gam) return a.act.half ? compact_ns<_Float16, true>(a, ns, st) : compact_ns<float, true>(a, ns, st);
+  return a.act.half ? compact_ns<_Float16, false>(a, ns, st) : compact_ns<float, false>(a, ns, st);
 }
 
 hipError_t launch_materialize(const MaterializeArgs &a, int64_t grid_upper, hipStream_t st) {
@@ -801,6 +902,12 @@ hipError_t launch_repack(const RepackArgs &a, hipStream_t st) {
   const dim3 grid((unsigned)((a.N + 3) / 4)), block(256);
   if (a.src_a.half) hipLaunchKernelGGL(k_repack<_Float16>, grid, block, 0, st, a);
   else hipLaunchKernelGGL(k_repack<float>, grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_f32(float *p, int64_t n, float x, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n, x);
   return hipGetLastError();
 }
 

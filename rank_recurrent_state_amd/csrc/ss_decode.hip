@@ -48,7 +48,17 @@ namespace {
 // ---------------------------------------------------------------------------
 // factored states
 // ---------------------------------------------------------------------------
-template <int P, int UN, bool RO, bool ANYDELTA, typename F>
+__device__ __forceinline__ float4 mul4(float4 a, float4 b) { return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w); }
+__device__ __forceinline__ float4 div4(float4 a, float4 b) { return make_float4(a.x / b.x, a.y / b.y, a.z / b.z, a.w / b.w); }
+__device__ __forceinline__ float4 one4() { return make_float4(1.f, 1.f, 1.f, 1.f); }
+
+// DIAG: per-channel decay (Kimi Delta Attention, SEED appendix B.1 eq. (6)).  The decay is
+// accumulated per key channel in gamma (d_k values per state, reset by a compaction), so
+//   S = diag(gamma) (sum sigma_i u_i v_i^T + sum_j k~_j w_j^T),  k~_j = k_j / gamma_j (at insertion),
+// and a step with decays lambda reads the stored parts with q~ = gamma' q and k~ = gamma' k,
+// gamma' = gamma lambda:  p_q = stored^T q~,  w = beta (v - stored^T k~) (delta) or v,
+// o = p_q + <k, q> w;  the new slot is (k / gamma', w, 1).
+template <int P, int UN, bool RO, bool ANYDELTA, typename F, bool DIAG>
 __global__ __launch_bounds__(256) void k_decode_factored(DecodeArgs a) {
   constexpr int G = 64 / P;
   const int lane = threadIdx.x & 63;
@@ -80,8 +90,15 @@ __global__ __launch_bounds__(256) void k_decode_factored(DecodeArgs a) {
   const float4 k4 = RO ? zero4() : sel4(kin, ld4nt(a.k + s * dk + 4 * colk));
   const float4 v4 = RO ? zero4() : sel4(vin, ld4nt(a.v + s * dv + 4 * colv));
   const bool delta = ANYDELTA && !RO && (flags & FLAG_DELTA);
-  const float al = RO ? 1.f : uniformf(a.alpha[s]);
+  const float al = (RO || DIAG) ? 1.f : uniformf(a.alpha[s]);
   const float be = delta ? uniformf(a.beta[s]) : 0.f;
+  float4 gn4 = one4();  // DIAG: the accumulated decays after this step (readout: as they are)
+  if constexpr (DIAG) {
+    const float4 g4 = ld4(a.gam + s * dk + 4 * colk);  // clamped lanes: q4 = k4 = 0 and nothing is stored
+    gn4 = RO ? g4 : mul4(g4, ld4nt(a.alpha + s * dk + 4 * colk));
+  }
+  const float4 qs = DIAG ? mul4(gn4, q4) : q4;  // what the stored parts are read with
+  const float4 ks = DIAG ? mul4(gn4, k4) : k4;
   float4 acc = zero4(), acck = zero4();
   // pairs [ib, ie) of the list in chunks of G * UN; ld(i, x, y, w) issues the loads of pair i
   auto stream = [&](int ib, int ie, auto ld) {
@@ -96,10 +113,10 @@ __global__ __launch_bounds__(256) void k_decode_factored(DecodeArgs a) {
 #pragma unroll
       for (int u = 0; u < UN; ++u) {
         const float wu = (i0 + u * G + grp < ie) ? wt[u] : 0.f;
-        const float cq = group_sum<P>(dot4(x[u], q4)) * wu;
+        const float cq = group_sum<P>(dot4(x[u], qs)) * wu;
         acc = fma4(cq, y[u], acc);
         if (delta) {
-          const float ck = group_sum<P>(dot4(x[u], k4)) * wu;
+          const float ck = group_sum<P>(dot4(x[u], ks)) * wu;
           acck = fma4(ck, y[u], acck);
         }
       }
@@ -144,7 +161,7 @@ __global__ __launch_bounds__(256) void k_decode_factored(DecodeArgs a) {
     stream(rr, T, ld_pad);
   }
   acc = cross_group_sum4<P>(acc);
-  const float4 pq = scale4(gamma, acc);
+  const float4 pq = DIAG ? acc : scale4(gamma, acc);
   if constexpr (RO) {
     if (grp == 0 && vin) st4(a.o + s * dv + 4 * col, pq);
     return;
@@ -152,13 +169,16 @@ __global__ __launch_bounds__(256) void k_decode_factored(DecodeArgs a) {
     float4 w4 = v4;
     if (delta) {
       acck = cross_group_sum4<P>(acck);
-      w4 = scale4(be, sub4(v4, scale4(al * gamma, acck)));
+      w4 = scale4(be, sub4(v4, DIAG ? acck : scale4(al * gamma, acck)));
     }
     const float kq = group_sum<P>(dot4(k4, q4));
     const float4 o4 = add4(scale4(al, pq), scale4(kq, w4));
-    const float gnew = al * gamma;
+    const float gnew = al * gamma;  // DIAG: stays 1 (the decays live in gam)
     if (grp == 0) {
-      if (kin) st4nt(a.pk + (s * (int64_t)K + n) * dk + 4 * col, k4);
+      if (kin) {
+        st4nt(a.pk + (s * (int64_t)K + n) * dk + 4 * col, DIAG ? div4(k4, gn4) : k4);
+        if constexpr (DIAG) st4(a.gam + s * dk + 4 * col, gn4);
+      }
       if (vin) {
         st4nt(a.pw + (s * (int64_t)K + n) * dv + 4 * col, w4);
         st4(a.o + s * dv + 4 * col, o4);
@@ -172,7 +192,7 @@ __global__ __launch_bounds__(256) void k_decode_factored(DecodeArgs a) {
       nm.gamma = gnew;
       nm.packed = meta_pack(ra, rf, n + 1, flags);
       a.meta[s] = nm;
-      const unsigned long long b = decode_bytes(dk, dv, K, rr, n, delta, KIND_FACTORED, (int)sizeof(F));
+      const unsigned long long b = decode_bytes(dk, dv, K, rr, n, delta, KIND_FACTORED, (int)sizeof(F), DIAG);
       __hip_atomic_fetch_add(&a.acct[s & (kAcctSlots - 1)], b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -370,7 +390,11 @@ __device__ __forceinline__ void stage_lds(const Seg4 (&sg)[NSEG], int lane) {
 // delta-rule w row; the new key and a scalar-rule w = v are copied into the
 // pad by k_dense_append after it (a few small writes inside the row stream
 // cost more than a pass of their own).
-template <int P, int UN, int MODE, bool ANYDELTA>
+// DIAG (per-channel decay): the slot's decays gamma (d_k values) replace the scalar Gamma, so a
+// dense state is S = diag(gamma) (H^T + sum_i k~_i w_i^T) with c_i = 1, rows are read with
+// q~ = gamma' q and k~ = gamma' k (gamma' = gamma lambda), and a fold is
+//   H_j <- gamma' (H_j + sum_i w_i,j k~_i) + w_j k  (element by element), gamma <- 1.
+template <int P, int UN, int MODE, bool ANYDELTA, bool DIAG>
 __global__ __launch_bounds__(256) void k_dense_buf(DenseArgs a) {
   constexpr int G = 64 / P, B = G * UN;
   constexpr bool DEC = MODE == DM_DECODE, RO = MODE == DM_READOUT, FO = MODE == DM_FOLD;
@@ -431,7 +455,14 @@ __global__ __launch_bounds__(256) void k_dense_buf(DenseArgs a) {
   const bool fold = FO || (DEC && n + 1 >= K);
   const float4 q4 = FO ? zero4() : sel4(kin, ld4nt(a.q + s * dk + 4 * colk));
   const float4 k4 = DEC ? sel4(kin, ld4nt(a.k + s * dk + 4 * colk)) : zero4();
-  const float al = DEC ? uniformf(a.alpha[s]) : 1.f;
+  const float al = (DEC && !DIAG) ? uniformf(a.alpha[s]) : 1.f;
+  float4 gn4 = one4();  // DIAG: the slot's decays after this step (readout and fold: as they are)
+  if constexpr (DIAG) {
+    const float4 g4 = ld4(a.dgam + (int64_t)slot * dk + 4 * colk);  // clamped lanes store nothing
+    gn4 = DEC ? mul4(g4, ld4nt(a.alpha + s * dk + 4 * colk)) : g4;
+  }
+  const float4 qs = DIAG ? mul4(gn4, q4) : q4;
+  const float4 ks = DIAG ? mul4(gn4, k4) : k4;
   const float be = delta ? uniformf(a.beta[s]) : 0.f;
   // the pad (keys, w rows) and v to LDS in one batch of loads
   const float *pks = a.pk + (int64_t)slot * K * dk;
@@ -452,8 +483,8 @@ __global__ __launch_bounds__(256) void k_dense_buf(DenseArgs a) {
     for (int i = 0; i < kMaxPad; ++i) {
       if (i < n) {
         const float4 ki = *reinterpret_cast<const float4 *>(KS + i * dk + 4 * colk);
-        cq[i] = uniformf(cf[i] * group_sum<P>(dot4(ki, q4)));
-        if (delta) ck[i] = uniformf(cf[i] * group_sum<P>(dot4(ki, k4)));
+        cq[i] = uniformf(cf[i] * group_sum<P>(dot4(ki, qs)));
+        if (delta) ck[i] = uniformf(cf[i] * group_sum<P>(dot4(ki, ks)));
       }
     }
   }
@@ -475,8 +506,8 @@ __global__ __launch_bounds__(256) void k_dense_buf(DenseArgs a) {
     wave_sync();
   }
   const float kq = DEC ? uniformf(group_sum<P>(dot4(k4, q4))) : 0.f;
-  const float ag = al * gamma;
-  const float sc = FO ? gamma : ag;  // a fold scales H and the pad by this
+  const float ag = al * gamma;       // DIAG: 1 (the decays are in gn4)
+  const float sc = FO ? gamma : ag;  // a fold scales H and the pad by this (DIAG: by gn4)
   float *os = a.o + s * dv;
   float *pwn = a.pw + ((int64_t)slot * K + n) * dv;
   auto proc_rows = [&](float4 (&hb)[UN], int j0) {
@@ -486,13 +517,13 @@ __global__ __launch_bounds__(256) void k_dense_buf(DenseArgs a) {
       const bool ok = j < dv;
       float w = 0.f;
       if constexpr (!FO) {
-        const float pq = gamma * (group_sum<P>(dot4(hb[u], q4)) + (ok ? PQ[j] : 0.f));
+        const float pq = gamma * (group_sum<P>(dot4(hb[u], qs)) + (ok ? PQ[j] : 0.f));
         float oj = pq;
         if constexpr (DEC) {
           const float vj = ok ? VS[j] : 0.f;
           w = vj;
           if (delta) {
-            const float pk = gamma * (group_sum<P>(dot4(hb[u], k4)) + (ok ? PK[j] : 0.f));
+            const float pk = gamma * (group_sum<P>(dot4(hb[u], ks)) + (ok ? PK[j] : 0.f));
             w = be * (vj - al * pk);
           }
           oj = fmaf(al, pq, kq * w);
@@ -500,14 +531,18 @@ __global__ __launch_bounds__(256) void k_dense_buf(DenseArgs a) {
         }
         if (col == 0 && ok) OS[j] = oj;
       }
-      // fold, first part: FO: H <- Gamma H;  DEC: H <- alpha Gamma H + w_j k
-      if (fold) hb[u] = FO ? scale4(sc, hb[u]) : fma4(w, k4, scale4(sc, hb[u]));
+      // fold, first part: FO: H <- Gamma H;  DEC: H <- alpha Gamma H + w_j k  (DIAG: gn4 for the scalar)
+      if (fold) {
+        const float4 h = DIAG ? mul4(gn4, hb[u]) : scale4(sc, hb[u]);
+        hb[u] = FO ? h : fma4(w, k4, h);
+      }
     }
     if (fold) {
       // second part: H_j += sc c_i w_i,j k_i for every pad slot i, one key at a time
       for (int i = 0; i < n; ++i) {
-        const float4 ki = *reinterpret_cast<const float4 *>(KS + i * dk + 4 * colk);
-        const float si = sc * cf[i];
+        const float4 kr = *reinterpret_cast<const float4 *>(KS + i * dk + 4 * colk);
+        const float4 ki = DIAG ? mul4(gn4, kr) : kr;
+        const float si = DIAG ? cf[i] : sc * cf[i];
 #pragma unroll
         for (int u = 0; u < UN; ++u) {
           const int j = j0 + u * G + grp;
@@ -538,6 +573,9 @@ __global__ __launch_bounds__(256) void k_dense_buf(DenseArgs a) {
     }
   }
   if constexpr (!RO) {
+    if constexpr (DIAG) {  // the decays after the step, or 1 after a fold
+      if (grp == 0 && kin) st4(a.dgam + (int64_t)slot * dk + 4 * col, fold ? one4() : gn4);
+    }
     if (lane == 0) {
       if (DEC && !fold) a.pc[(int64_t)slot * K + n] = 1.0f / ag;
       DenseSlot nr = rec;
@@ -545,7 +583,7 @@ __global__ __launch_bounds__(256) void k_dense_buf(DenseArgs a) {
       nr.packed = meta_pack(0, 0, fold ? 0 : n + 1, flags);
       a.dslot[slot] = nr;
       if (DEC) {
-        const unsigned long long b = decode_bytes(dk, dv, K, 0, n, delta, KIND_DENSE_BUFFERED);
+        const unsigned long long b = decode_bytes(dk, dv, K, 0, n, delta, KIND_DENSE_BUFFERED, 4, DIAG);
         __hip_atomic_fetch_add(&a.acct[s & (kAcctSlots - 1)], b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
@@ -569,14 +607,20 @@ __global__ __launch_bounds__(256) void k_dense_append(DenseArgs a) {
   float *pkn = a.pk + ((int64_t)slot * a.K + n - 1) * a.dk;
   float *pwn = a.pw + ((int64_t)slot * a.K + n - 1) * a.dv;
   for (int e = lane; e < dk4 + dv4; e += 64) {
-    if (e < dk4) st4nt(pkn + 4 * e, ld4nt(a.k + s * a.dk + 4 * e));
-    else st4nt(pwn + 4 * (e - dk4), ld4nt(a.v + s * a.dv + 4 * (e - dk4)));
+    if (e < dk4) {
+      const float4 kk = ld4nt(a.k + s * a.dk + 4 * e);  // per-channel decay: stored as k / gamma
+      st4nt(pkn + 4 * e, a.dgam ? div4(kk, ld4(a.dgam + (int64_t)slot * a.dk + 4 * e)) : kk);
+    } else {
+      st4nt(pwn + 4 * (e - dk4), ld4nt(a.v + s * a.dv + 4 * (e - dk4)));
+    }
   }
 }
 
 // plain dense recurrence (the dense baseline): every row read and written every
 // step.  Same row streaming as the buffered kernel (double-buffered batches, v and o in LDS).
-template <int P, int UN, bool RO, bool ANYDELTA>
+// DIAG: per-channel decay lambda (d_k values per state): H_j <- lambda H_j + w_j k, with
+// w_j = beta (v_j - <H_j, lambda k>) for the delta rule, and o_j = <H_j, lambda q> + <k, q> w_j.
+template <int P, int UN, bool RO, bool ANYDELTA, bool DIAG>
 __global__ __launch_bounds__(256) void k_dense_plain(DenseArgs a) {
   constexpr int G = 64 / P, B = G * UN;
   extern __shared__ float smem[];
@@ -609,8 +653,11 @@ __global__ __launch_bounds__(256) void k_dense_plain(DenseArgs a) {
   const bool delta = ANYDELTA && !RO && (flags & FLAG_DELTA);
   const float4 q4 = sel4(kin, ld4nt(a.q + s * dk + 4 * colk));
   const float4 k4 = RO ? zero4() : sel4(kin, ld4nt(a.k + s * dk + 4 * colk));
-  const float al = RO ? 1.f : uniformf(a.alpha[s]);
+  const float al = (RO || DIAG) ? 1.f : uniformf(a.alpha[s]);
   const float be = delta ? uniformf(a.beta[s]) : 0.f;
+  const float4 l4 = (DIAG && !RO) ? ld4nt(a.alpha + s * dk + 4 * colk) : one4();  // clamped lanes store nothing
+  const float4 qs = (DIAG && !RO) ? mul4(l4, q4) : q4;
+  const float4 ks = (DIAG && !RO) ? mul4(l4, k4) : k4;
   if constexpr (!RO) {
     const Seg4 sg[1] = {{VS, a.v + s * dv, dv >> 2}};
     stage_lds(sg, lane);
@@ -622,7 +669,7 @@ __global__ __launch_bounds__(256) void k_dense_plain(DenseArgs a) {
     for (int u = 0; u < UN; ++u) {
       const int j = j0 + u * G + grp;
       const bool ok = j < dv;
-      const float dq = group_sum<P>(dot4(hb[u], q4));
+      const float dq = group_sum<P>(dot4(hb[u], qs));
       float oj;
       if constexpr (RO) {
         oj = dq;
@@ -630,11 +677,11 @@ __global__ __launch_bounds__(256) void k_dense_plain(DenseArgs a) {
         const float vj = ok ? VS[j] : 0.f;
         float w = vj;
         if (delta) {
-          const float dkk = group_sum<P>(dot4(hb[u], k4));
+          const float dkk = group_sum<P>(dot4(hb[u], ks));
           w = be * (vj - al * dkk);
         }
         oj = fmaf(al, dq, kq * w);
-        if (ok && kin) st4nt(Hw + (int64_t)j * dk, fma4(w, k4, scale4(al, hb[u])));
+        if (ok && kin) st4nt(Hw + (int64_t)j * dk, fma4(w, k4, DIAG ? mul4(l4, hb[u]) : scale4(al, hb[u])));
       }
       if (col == 0 && ok) OS[j] = oj;
     }
@@ -650,25 +697,25 @@ __global__ __launch_bounds__(256) void k_dense_plain(DenseArgs a) {
   wave_sync();
   for (int e = lane; e < (dv >> 2); e += 64) st4nt(a.o + s * dv + 4 * e, *reinterpret_cast<const float4 *>(OS + 4 * e));
   if (!RO && lane == 0) {
-    const unsigned long long b = decode_bytes(dk, dv, 0, 0, 0, delta, KIND_DENSE_PLAIN);
+    const unsigned long long b = decode_bytes(dk, dv, 0, 0, 0, delta, KIND_DENSE_PLAIN, 4, DIAG);
     __hip_atomic_fetch_add(&a.acct[s & (kAcctSlots - 1)], b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-template <bool RO, bool AD, typename F>
+template <bool RO, bool AD, typename F, bool DG>
 hipError_t decode_factored_p(const DecodeArgs &a, int P, hipStream_t st) {
   const dim3 grid((unsigned)((a.N + 3) / 4)), block(256);  // a.N: upper bound of the list length
   switch (P) {
-    case 1: hipLaunchKernelGGL((k_decode_factored<1, 1, RO, AD, F>), grid, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((k_decode_factored<2, 1, RO, AD, F>), grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((k_decode_factored<4, 1, RO, AD, F>), grid, block, 0, st, a); break;
-    case 8: hipLaunchKernelGGL((k_decode_factored<8, 2, RO, AD, F>), grid, block, 0, st, a); break;
-    case 16: hipLaunchKernelGGL((k_decode_factored<16, 2, RO, AD, F>), grid, block, 0, st, a); break;
+    case 1: hipLaunchKernelGGL((k_decode_factored<1, 1, RO, AD, F, DG>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_decode_factored<2, 1, RO, AD, F, DG>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((k_decode_factored<4, 1, RO, AD, F, DG>), grid, block, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((k_decode_factored<8, 2, RO, AD, F, DG>), grid, block, 0, st, a); break;
+    case 16: hipLaunchKernelGGL((k_decode_factored<16, 2, RO, AD, F, DG>), grid, block, 0, st, a); break;
 #ifndef SS_FACT_UN32
 #define SS_FACT_UN32 4
 #endif
-    case 32: hipLaunchKernelGGL((k_decode_factored<32, SS_FACT_UN32, RO, AD, F>), grid, block, 0, st, a); break;
-    case 64: hipLaunchKernelGGL((k_decode_factored<64, 8, RO, AD, F>), grid, block, 0, st, a); break;
+    case 32: hipLaunchKernelGGL((k_decode_factored<32, SS_FACT_UN32, RO, AD, F, DG>), grid, block, 0, st, a); break;
+    case 64: hipLaunchKernelGGL((k_decode_factored<64, 8, RO, AD, F, DG>), grid, block, 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -692,51 +739,64 @@ hipError_t decode_factored_h8_p(const DecodeArgs &a, int P, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <typename F>
+template <typename F, bool DG>
 hipError_t decode_factored_f(const DecodeArgs &a, bool readonly, bool any_delta, int P, hipStream_t st) {
-  if (readonly) return decode_factored_p<true, false, F>(a, P, st);
-  return any_delta ? decode_factored_p<false, true, F>(a, P, st) : decode_factored_p<false, false, F>(a, P, st);
+  if (readonly) return decode_factored_p<true, false, F, DG>(a, P, st);
+  return any_delta ? decode_factored_p<false, true, F, DG>(a, P, st) : decode_factored_p<false, false, F, DG>(a, P, st);
 }
 
-template <int P, int UN, bool AD>
+template <int P, int UN, bool AD, bool DG>
 hipError_t dense_buf_mode(const DenseArgs &a, int mode, unsigned grid, hipStream_t st) {
   const size_t sh = sizeof(float) * 4 * ((size_t)a.K * (a.dk + a.dv) + 3 * (size_t)a.dv);
   const dim3 g(grid), b(256);
-  if (mode == DM_DECODE) hipLaunchKernelGGL((k_dense_buf<P, UN, DM_DECODE, AD>), g, b, sh, st, a);
-  else if (mode == DM_READOUT) hipLaunchKernelGGL((k_dense_buf<P, UN, DM_READOUT, false>), g, b, sh, st, a);
-  else hipLaunchKernelGGL((k_dense_buf<P, UN, DM_FOLD, false>), g, b, sh, st, a);
+  if (mode == DM_DECODE) hipLaunchKernelGGL((k_dense_buf<P, UN, DM_DECODE, AD, DG>), g, b, sh, st, a);
+  else if (mode == DM_READOUT) hipLaunchKernelGGL((k_dense_buf<P, UN, DM_READOUT, false, DG>), g, b, sh, st, a);
+  else hipLaunchKernelGGL((k_dense_buf<P, UN, DM_FOLD, false, DG>), g, b, sh, st, a);
   return hipGetLastError();
+}
+
+template <bool AD, bool DG>
+hipError_t dense_buf_pd(const DenseArgs &a, int mode, int P, unsigned grid, hipStream_t st) {
+  switch (P) {
+    case 1: return dense_buf_mode<1, 1, AD, DG>(a, mode, grid, st);
+    case 2: return dense_buf_mode<2, 1, AD, DG>(a, mode, grid, st);
+    case 4: return dense_buf_mode<4, 2, AD, DG>(a, mode, grid, st);
+    case 8: return dense_buf_mode<8, 4, AD, DG>(a, mode, grid, st);
+    case 16: return dense_buf_mode<16, 8, AD, DG>(a, mode, grid, st);
+    case 32: return dense_buf_mode<32, SS_DENSE_UN, AD, DG>(a, mode, grid, st);
+    case 64: return dense_buf_mode<64, 8, AD, DG>(a, mode, grid, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <bool AD>
 hipError_t dense_buf_p(const DenseArgs &a, int mode, int P, unsigned grid, hipStream_t st) {
+  if (a.diag) return a.dgam ? dense_buf_pd<AD, true>(a, mode, P, grid, st) : hipErrorInvalidValue;
+  return dense_buf_pd<AD, false>(a, mode, P, grid, st);
+}
+
+template <bool RO, bool AD, bool DG>
+hipError_t dense_plain_pd(const DenseArgs &a, int P, unsigned grid, hipStream_t st) {
+  const dim3 g(grid), b(256);
+  const size_t sh = sizeof(float) * 4 * 2 * (size_t)a.dv;
   switch (P) {
-    case 1: return dense_buf_mode<1, 1, AD>(a, mode, grid, st);
-    case 2: return dense_buf_mode<2, 1, AD>(a, mode, grid, st);
-    case 4: return dense_buf_mode<4, 2, AD>(a, mode, grid, st);
-    case 8: return dense_buf_mode<8, 4, AD>(a, mode, grid, st);
-    case 16: return dense_buf_mode<16, 8, AD>(a, mode, grid, st);
-    case 32: return dense_buf_mode<32, SS_DENSE_UN, AD>(a, mode, grid, st);
-    case 64: return dense_buf_mode<64, 8, AD>(a, mode, grid, st);
+    case 1: hipLaunchKernelGGL((k_dense_plain<1, 1, RO, AD, DG>), g, b, sh, st, a); break;
+    case 2: hipLaunchKernelGGL((k_dense_plain<2, 1, RO, AD, DG>), g, b, sh, st, a); break;
+    case 4: hipLaunchKernelGGL((k_dense_plain<4, 2, RO, AD, DG>), g, b, sh, st, a); break;
+    case 8: hipLaunchKernelGGL((k_dense_plain<8, 4, RO, AD, DG>), g, b, sh, st, a); break;
+    case 16: hipLaunchKernelGGL((k_dense_plain<16, 8, RO, AD, DG>), g, b, sh, st, a); break;
+    case 32: hipLaunchKernelGGL((k_dense_plain<32, 8, RO, AD, DG>), g, b, sh, st, a); break;
+    case 64: hipLaunchKernelGGL((k_dense_plain<64, 8, RO, AD, DG>), g, b, sh, st, a); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
 }
 
 template <bool RO, bool AD>
 hipError_t dense_plain_p(const DenseArgs &a, int P, unsigned grid, hipStream_t st) {
-  const dim3 g(grid), b(256);
-  const size_t sh = sizeof(float) * 4 * 2 * (size_t)a.dv;
-  switch (P) {
-    case 1: hipLaunchKernelGGL((k_dense_plain<1, 1, RO, AD>), g, b, sh, st, a); break;
-    case 2: hipLaunchKernelGGL((k_dense_plain<2, 1, RO, AD>), g, b, sh, st, a); break;
-    case 4: hipLaunchKernelGGL((k_dense_plain<4, 2, RO, AD>), g, b, sh, st, a); break;
-    case 8: hipLaunchKernelGGL((k_dense_plain<8, 4, RO, AD>), g, b, sh, st, a); break;
-    case 16: hipLaunchKernelGGL((k_dense_plain<16, 8, RO, AD>), g, b, sh, st, a); break;
-    case 32: hipLaunchKernelGGL((k_dense_plain<32, 8, RO, AD>), g, b, sh, st, a); break;
-    case 64: hipLaunchKernelGGL((k_dense_plain<64, 8, RO, AD>), g, b, sh, st, a); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  // a readout applies no decay: the per-channel variant is only needed for the step
+  if (a.diag && !RO) return dense_plain_pd<RO, AD, true>(a, P, grid, st);
+  return dense_plain_pd<RO, AD, false>(a, P, grid, st);
 }
 
 int pow2_at_least(int w) {
@@ -752,13 +812,17 @@ int lanes_per_pair(int dk, int dv) { return pow2_at_least((dk > dv ? dk : dv) >>
 hipError_t launch_decode_factored(const DecodeArgs &a, bool readonly, bool any_delta, hipStream_t st) {
   if (a.N <= 0) return hipSuccess;
   const int P = lanes_per_pair(a.dk, a.dv);
+  if (a.gam) {  // per-channel decay
+    return a.act.half ? decode_factored_f<_Float16, true>(a, readonly, any_delta, P, st)
+                      : decode_factored_f<float, true>(a, readonly, any_delta, P, st);
+  }
   if (a.act.half && a.dk % 8 == 0 && a.dv % 8 == 0) {  // fp16 factors, eight elements per lane
     const int P8 = pow2_at_least((a.dk > a.dv ? a.dk : a.dv) >> 3);
     if (readonly) return decode_factored_h8_p<true, false>(a, P8, st);
     return any_delta ? decode_factored_h8_p<false, true>(a, P8, st) : decode_factored_h8_p<false, false>(a, P8, st);
   }
-  if (a.act.half) return decode_factored_f<_Float16>(a, readonly, any_delta, P, st);
-  return decode_factored_f<float>(a, readonly, any_delta, P, st);
+  if (a.act.half) return decode_factored_f<_Float16, false>(a, readonly, any_delta, P, st);
+  return decode_factored_f<float, false>(a, readonly, any_delta, P, st);
 }
 
 hipError_t launch_decode_dense(const DenseArgs &a, int64_t n_upper, bool readonly, bool any_delta, hipStream_t st) {

@@ -114,6 +114,8 @@ struct DecodeArgs {
   uint32_t *counters;
   unsigned long long *acct;   // [kAcctSlots] algorithmic bytes
   uint32_t *hflag;            // host-mapped flag raised when a pad is found full
+  float *gam;                 // per-channel decay pools: [N][d_k] decay accumulated since the last
+                              // compaction (alpha is then [N][d_k]); nullptr: scalar decay
 };
 
 struct DenseArgs {
@@ -129,6 +131,8 @@ struct DenseArgs {
   float *o;
   uint32_t *counters;
   unsigned long long *acct;
+  int diag;                    // per-channel decay: alpha is [N][d_k]
+  float *dgam;                 // buffered region with per-channel decay: [cap_d][d_k] per slot
 };
 
 struct CompactArgs {
@@ -145,6 +149,7 @@ struct CompactArgs {
   uint32_t *counters;
   unsigned long long *acct_flops;
   unsigned long long *acct_states;
+  float *gam;                  // per-channel decay pools: [N][d_k] (reset to 1 by a compaction); nullptr otherwise
 };
 
 struct MaterializeArgs {
@@ -163,6 +168,7 @@ struct MaterializeArgs {
   DenseSlot *dslot;
   uint32_t *counters;
   uint32_t *hflag;             // host-mapped flag raised when the dense region is full
+  float *dgam;                 // per-channel decay pools: the new slot's [d_k] decay, set to 1; or nullptr
 };
 
 struct ScatterArgs {
@@ -189,6 +195,7 @@ hipError_t launch_compact(const CompactArgs &a, hipStream_t st);
 hipError_t launch_materialize(const MaterializeArgs &a, int64_t grid_upper, hipStream_t st);
 hipError_t launch_scatter(const ScatterArgs &a, hipStream_t st);
 hipError_t launch_zero_u32(uint32_t *p, int n, hipStream_t st);
+hipError_t launch_fill_f32(float *p, int64_t n, float x, hipStream_t st);
 // before a compaction of group g: limit = (oldest live segment start) + cap, begin = head, per ring,
 // and the promotion list and the pruning scratch emptied; after it: the group's segment becomes [begin, head)
 hipError_t launch_ring_begin(Ring *ra, Ring *rf, const unsigned long long *seg_a, const unsigned long long *seg_f,
@@ -263,9 +270,12 @@ enum DecodeKind : int { KIND_FACTORED = 0, KIND_DENSE_BUFFERED = 1, KIND_DENSE_P
 // in-kernel accounting).  n_pad is the pad fill before the step; a buffered
 // dense state whose pad fills in this step rewrites H instead of a pad slot.
 // fsz: bytes of a stored factor element (4, or 2 with fp16 factors); pad slots are fp32.
+// diag: per-channel decay (alpha has d_k entries; the buffered forms also read and write the
+// d_k accumulated decays).
 __host__ __device__ inline unsigned long long decode_bytes(int dk, int dv, int K, int ncomp, int npad, bool delta,
-                                                           int kind, int fsz = 4) {
-  const unsigned long long in = 4ull * (2ull * dk + dv + 1 + (delta ? 1 : 0));
+                                                           int kind, int fsz = 4, bool diag = false) {
+  const unsigned long long in = 4ull * (2ull * dk + dv + (diag ? dk : 1) + (delta ? 1 : 0)) +
+                                (diag && kind != KIND_DENSE_PLAIN ? 8ull * dk : 0ull);
   const unsigned long long comp = 4ull * (unsigned long long)(dk + dv + 1);
   const unsigned long long fcomp = (unsigned long long)fsz * (unsigned long long)(dk + dv) + 4ull;
   const unsigned long long st = 4ull * (unsigned long long)dk * dv;

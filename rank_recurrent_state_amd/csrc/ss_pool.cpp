@@ -43,6 +43,7 @@ struct ss_pool {
   int64_t N = 0;
   int dk = 0, dv = 0, K = 0, r = 0, L = 0, promote = 0, force_dense = 0, fcap = 0, G = 0;
   int half = 0;  // factor vectors stored in fp16
+  int diag = 0;  // per-channel decay (alpha is [N][d_k])
   bool any_delta = false;
   std::vector<int32_t> group_offset;
   std::vector<int64_t> group_start, group_size;
@@ -76,6 +77,7 @@ struct ss_pool {
   unsigned char *lay_scan = nullptr;
   size_t lay_scan_bytes = 0;
   float *pk = nullptr, *pw = nullptr, *pc = nullptr;
+  float *gam = nullptr, *dgam = nullptr;  // per-channel decay: accumulated decays per state [N][d_k], per dense slot
   float *dense = nullptr;
   ss::DenseSlot *dslot = nullptr;
   float *dpk = nullptr, *dpw = nullptr, *dpc = nullptr;  // slot-indexed pads of the dense region
@@ -537,11 +539,12 @@ ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipSt
   if (d->arena_components < 0 || d->arena_components >= (int64_t)INT32_MAX)
     return fail(SS_ERR_ARG, "arena_components must be in [0, 2^31)");
   if (d->factor_fp16 != 0 && d->factor_fp16 != 1) return fail(SS_ERR_ARG, "factor_fp16 must be 0 or 1");
+  if (d->diag_decay != 0 && d->diag_decay != 1) return fail(SS_ERR_ARG, "diag_decay must be 0 or 1");
 
   ss_pool *p = new (std::nothrow) ss_pool();
   if (!p) return fail(SS_ERR_OOM, "host allocation failed");
   p->N = N; p->dk = dk; p->dv = dv; p->K = K; p->r = r; p->L = L; p->promote = promote;
-  p->force_dense = d->force_dense ? 1 : 0; p->half = d->factor_fp16; p->fcap = fcap; p->G = G; p->any_delta = any_delta; p->cap_d = cap_d;
+  p->force_dense = d->force_dense ? 1 : 0; p->half = d->factor_fp16; p->diag = d->diag_decay; p->fcap = fcap; p->G = G; p->any_delta = any_delta; p->cap_d = cap_d;
   p->group_offset.assign(G, 0);
   if (d->group_offset) for (int g = 0; g < G; ++g) p->group_offset[g] = d->group_offset[g];
   p->group_size.assign(G, 0);
@@ -620,6 +623,10 @@ ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipSt
     chk(dalloc(p, &p->dpk, (size_t)cap_d * K * dk));
     chk(dalloc(p, &p->dpw, (size_t)cap_d * K * dv));
     chk(dalloc(p, &p->dpc, (size_t)cap_d * K));
+    if (p->diag) {
+      chk(dalloc(p, &p->gam, (size_t)N * dk));
+      chk(dalloc(p, &p->dgam, (size_t)cap_d * dk));
+    }
   }
   chk(dalloc(p, &p->counters, ss::C_N));
   chk(dalloc(p, &p->acct, ss::A_N * ss::kAcctSlots));
@@ -733,9 +740,10 @@ ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipSt
     ma.meta = p->meta; ma.csr_off = d_off; ma.csr_u = d_u; ma.csr_v = d_v; ma.csr_s = d_s;
     ma.dsrc_idx = d_didx; ma.dsrc = d_dsrc;
     ma.act = p->act; ma.frz = p->frz; ma.dense = p->dense; ma.dslot = p->dslot; ma.counters = p->counters;
-    ma.hflag = p->hflags_dev + HF_DENSE_CAP;
+    ma.hflag = p->hflags_dev + HF_DENSE_CAP; ma.dgam = p->dgam;
     e = ss::launch_materialize(ma, n_dense0, stream);
   }
+  if (e == hipSuccess && p->gam) e = ss::launch_fill_f32(p->gam, N * (int64_t)dk, 1.0f, stream);
   if (e == hipSuccess) e = ss::launch_zero_u32(p->counters + ss::C_PROMOTE_COUNT, 1, stream);
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
   for (void *q : tmp) (void)hipFree(q);
@@ -778,7 +786,7 @@ static hipError_t enqueue_decode(ss_pool *p, const float *q, const float *k, con
     a.fact_ids = p->fact_ids[0]; a.fact_count = p->counters + ss::C_FACT0;
     a.pk = p->pk; a.pw = p->pw; a.pc = p->pc; a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.o = o;
     a.counters = p->counters; a.acct = p->acct + ss::A_DECODE_FACTORED * ss::kAcctSlots;
-    a.hflag = p->hflags_dev + HF_PAD;
+    a.hflag = p->hflags_dev + HF_PAD; a.gam = p->gam;
     auto fn = [&] { return ss::launch_decode_factored(a, readonly, p->any_delta, stream); };
     e = timing ? timed(p, readonly ? SS_KERNEL_READOUT_FACTORED : SS_KERNEL_DECODE_FACTORED, stream, fn) : fn();
     if (e != hipSuccess) return e;
@@ -789,6 +797,7 @@ static hipError_t enqueue_decode(ss_pool *p, const float *q, const float *k, con
     a.dslot = p->dslot; a.pk = p->dpk; a.pw = p->dpw; a.pc = p->dpc;
     a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.o = o;
     a.counters = p->counters; a.acct = p->acct + ss::A_DECODE_DENSE * ss::kAcctSlots;
+    a.diag = p->diag; a.dgam = p->dgam;
     auto fn = [&] { return ss::launch_decode_dense(a, dense_grid, readonly, p->any_delta, stream); };
     e = timing ? timed(p, readonly ? SS_KERNEL_READOUT_DENSE : SS_KERNEL_DECODE_DENSE, stream, fn) : fn();
   }
@@ -807,7 +816,7 @@ static hipError_t enqueue_compact_group(ss_pool *p, int g, bool with_dense, bool
     da.dk = p->dk; da.dv = p->dv; da.K = p->K; da.cap_d = (uint32_t)p->cap_d; da.meta = p->meta;
     da.dense = p->dense; da.dslot = p->dslot; da.pk = p->dpk; da.pw = p->dpw; da.pc = p->dpc;
     da.members = p->members + p->group_start[g]; da.n_members = (int32_t)p->group_size[g];
-    da.counters = p->counters; da.acct = p->acct;
+    da.counters = p->counters; da.acct = p->acct; da.diag = p->diag; da.dgam = p->dgam;
     auto fn = [&] { return ss::launch_dense_fold(da, stream); };
     e = timing ? timed(p, SS_KERNEL_DENSE_FOLD, stream, fn) : fn();
     if (e != hipSuccess) return e;
@@ -821,6 +830,7 @@ static hipError_t enqueue_compact_group(ss_pool *p, int g, bool with_dense, bool
   a.pk = p->pk; a.pw = p->pw; a.pc = p->pc; a.promote_list = p->promote_list; a.counters = p->counters;
   a.acct_flops = p->acct + ss::A_COMPACT_FLOPS * ss::kAcctSlots;
   a.acct_states = p->acct + ss::A_COMPACT_STATES * ss::kAcctSlots;
+  a.gam = p->gam;
   auto fc = [&] { return ss::launch_compact(a, stream); };
   e = timing ? timed(p, SS_KERNEL_COMPACT, stream, fc) : fc();
   if (e == hipSuccess) e = ss::launch_ring_end(p->ring, p->ring + 1, p->seg, p->seg + 2 * p->G, g, stream);
@@ -829,7 +839,7 @@ static hipError_t enqueue_compact_group(ss_pool *p, int g, bool with_dense, bool
   ma.dk = p->dk; ma.dv = p->dv; ma.cap_d = (int)p->cap_d; ma.list = p->promote_list;
   ma.count = p->counters + ss::C_PROMOTE_COUNT; ma.meta = p->meta; ma.act = p->act; ma.frz = p->frz;
   ma.dense = p->dense; ma.dslot = p->dslot; ma.counters = p->counters;
-  ma.hflag = p->hflags_dev + HF_DENSE_CAP;
+  ma.hflag = p->hflags_dev + HF_DENSE_CAP; ma.dgam = p->dgam;
   const int64_t gsz = p->group_size[g];
   auto fm = [&] { return ss::launch_materialize(ma, gsz, stream); };
   return timing ? timed(p, SS_KERNEL_MATERIALIZE, stream, fm) : fm();
@@ -968,6 +978,7 @@ static ss_status consolidate_precheck(ss_pool *p) {
   if (st != SS_OK) return st;
   if (ss::consolidate_lds_bytes(p->dk, p->dv, frozen_max(p), p->half != 0) > ss::kConsolidateLdsMax)
     return fail(SS_ERR_SHAPE, "the pool's largest frozen part does not fit the consolidation kernel's LDS");
+  if (p->diag) return fail(SS_ERR_ARG, "consolidation is not available with per-channel decay");
   return SS_OK;
 }
 
@@ -1074,6 +1085,8 @@ ss_status ss_state_export(ss_pool *p, const int64_t *ids, int64_t n, void *host_
       dl(PK.data(), p->dpk + (size_t)m.off_a * K * dk, sizeof(float) * PK.size());
       dl(PW.data(), p->dpw + (size_t)m.off_a * K * dv, sizeof(float) * PW.size());
       dl(PC.data(), p->dpc + (size_t)m.off_a * K, sizeof(float) * PC.size());
+      std::vector<float> G(dk, 1.0f);  // per-channel decay: the slot's accumulated decays scale row i2 of S
+      if (p->dgam) dl(G.data(), p->dgam + (size_t)m.off_a * dk, sizeof(float) * dk);
       if (e != hipSuccess) return hip_fail(e, "export copy");
       const double g = p->force_dense ? 1.0 : (double)rec.gamma;
       float *S = reinterpret_cast<float *>(w);
@@ -1081,7 +1094,7 @@ ss_status ss_state_export(ss_pool *p, const int64_t *ids, int64_t n, void *host_
         for (int j = 0; j < dv; ++j) {
           double x = H[(size_t)j * dk + i2];
           for (int t = 0; t < np; ++t) x += (double)PC[t] * PK[(size_t)t * dk + i2] * PW[(size_t)t * dv + j];
-          S[(size_t)i2 * dv + j] = (float)(g * x);
+          S[(size_t)i2 * dv + j] = (float)(g * (double)G[i2] * x);
         }
       w += sizeof(float) * (size_t)dk * dv;
       continue;
@@ -1119,9 +1132,20 @@ ss_status ss_state_export(ss_pool *p, const int64_t *ids, int64_t n, void *host_
     dl(c, p->pc + (size_t)ids[i] * K, sizeof(float) * nn);
     dl(kk, p->pk + (size_t)ids[i] * K * dk, sizeof(float) * (size_t)nn * dk);
     dl(ww, p->pw + (size_t)ids[i] * K * dv, sizeof(float) * (size_t)nn * dv);
+    std::vector<float> G;
+    if (p->gam) {  // per-channel decay: the effective u and pad keys carry the accumulated decays
+      G.resize(dk);
+      dl(G.data(), p->gam + (size_t)ids[i] * dk, sizeof(float) * dk);
+    }
     if (e != hipSuccess) return hip_fail(e, "export copy");
     for (int j = 0; j < R; ++j) sig[j] *= m.gamma;
     for (int j = 0; j < nn; ++j) c[j] *= m.gamma;
+    if (p->gam) {
+      for (int j = 0; j < R; ++j)
+        for (int x = 0; x < dk; ++x) u[(size_t)j * dk + x] *= G[x];
+      for (int j = 0; j < nn; ++j)
+        for (int x = 0; x < dk; ++x) kk[(size_t)j * dk + x] *= G[x];
+    }
     w = reinterpret_cast<char *>(ww + (size_t)nn * dv);
   }
   if (e != hipSuccess) return hip_fail(e, "export copy");

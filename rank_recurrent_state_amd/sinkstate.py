@@ -36,7 +36,7 @@ class PoolDesc(ctypes.Structure):
         ("group_of_state", _c_i32p), ("group_offset", _c_i32p),
         ("rule", _c_u8p), ("eps", _c_f32p), ("eps_default", ctypes.c_float),
         ("dense_capacity", ctypes.c_int64), ("arena_components", ctypes.c_int64),
-        ("factor_fp16", ctypes.c_int32),
+        ("factor_fp16", ctypes.c_int32), ("diag_decay", ctypes.c_int32),
     ]
 
 
@@ -162,10 +162,12 @@ def decode_bytes_per_state(d_k, d_v, pad_slots, n_comp, n_pad, rule, kind) -> in
 class StatePool:
     """Owner of one ss_pool handle."""
 
-    def __init__(self, handle, n_states, d_k, d_v, K, r, n_groups, any_delta):
+    def __init__(self, handle, n_states, d_k, d_v, K, r, n_groups, any_delta, diag_decay=False):
         self.handle = handle
         self.N, self.d_k, self.d_v, self.K, self.r, self.n_groups = n_states, d_k, d_v, K, r, n_groups
         self.any_delta = any_delta
+        self.diag_decay = diag_decay
+        self.n_alpha = n_states * d_k if diag_decay else n_states  # per-channel decay: alpha is [N][d_k]
 
     def close(self):
         if self.handle:
@@ -182,7 +184,8 @@ class StatePool:
 def state_pool_create(n_states, d_k, d_v, pad_slots=8, r_active=8, dense_rank_limit=-1, promote_on_compact=True,
                       max_frozen=0, force_dense=False, group_of_state=None, group_offset=None, rule=None, eps=None,
                       eps_default=0.0, dense_capacity=0, comp_off=None, u=None, v=None, sigma=None,
-                      arena_components=0, dense_mask=None, dense=None, factor_fp16=False, stream=None) -> StatePool:
+                      arena_components=0, dense_mask=None, dense=None, factor_fp16=False, diag_decay=False,
+                      stream=None) -> StatePool:
     lib = load_library()
     n_groups = 1 if group_offset is None else len(group_offset)
     keep = []
@@ -194,7 +197,7 @@ def state_pool_create(n_states, d_k, d_v, pad_slots=8, r_active=8, dense_rank_li
     desc = PoolDesc(int(n_states), int(d_k), int(d_v), int(pad_slots), int(r_active), int(dense_rank_limit),
                     int(bool(promote_on_compact)), int(max_frozen), int(bool(force_dense)), int(n_groups),
                     g_p, o_p, r_p, e_p, float(eps_default), int(dense_capacity),
-                    int(arena_components), int(factor_fp16))
+                    int(arena_components), int(factor_fp16), int(bool(diag_decay)))
     init = None
     if comp_off is not None or dense_mask is not None:
         c_a, c_p = _arr(comp_off, np.int64, _c_i64p)
@@ -210,12 +213,13 @@ def state_pool_create(n_states, d_k, d_v, pad_slots=8, r_active=8, dense_rank_li
                                   _stream(stream) if torch.cuda.is_available() else None, ctypes.byref(handle))
     _check(st)
     any_delta = rule is not None and bool(np.any(np.asarray(rule) == 1))
-    return StatePool(handle, int(n_states), int(d_k), int(d_v), int(pad_slots), int(r_active), n_groups, any_delta)
+    return StatePool(handle, int(n_states), int(d_k), int(d_v), int(pad_slots), int(r_active), n_groups, any_delta,
+                     bool(diag_decay))
 
 
 def decode_step(pool: StatePool, q, k, v, alpha, beta, o, stream=None):
     N, dk, dv = pool.N, pool.d_k, pool.d_v
-    args = [_ptr(q, N * dk, "q"), _ptr(k, N * dk, "k"), _ptr(v, N * dv, "v"), _ptr(alpha, N, "alpha"),
+    args = [_ptr(q, N * dk, "q"), _ptr(k, N * dk, "k"), _ptr(v, N * dv, "v"), _ptr(alpha, pool.n_alpha, "alpha"),
             _ptr(beta, N, "beta") if beta is not None else None, _ptr(o, N * dv, "o")]
     _check(load_library().ss_decode_step(pool.handle, *args, _stream(stream)))
 
@@ -228,7 +232,7 @@ class StepGraph:
         N, dk, dv = pool.N, pool.d_k, pool.d_v
         self.pool = pool
         self.buffers = (q, k, v, alpha, beta, o)  # kept alive while the graphs may read them
-        args = [_ptr(q, N * dk, "q"), _ptr(k, N * dk, "k"), _ptr(v, N * dv, "v"), _ptr(alpha, N, "alpha"),
+        args = [_ptr(q, N * dk, "q"), _ptr(k, N * dk, "k"), _ptr(v, N * dv, "v"), _ptr(alpha, pool.n_alpha, "alpha"),
                 _ptr(beta, N, "beta") if beta is not None else None, _ptr(o, N * dv, "o")]
         h = ctypes.c_void_p()
         _check(load_library().ss_step_graph_create(pool.handle, *args, ctypes.byref(h)))

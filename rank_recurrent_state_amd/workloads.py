@@ -45,6 +45,7 @@ class Workload:
     inputs: str = "split70"       # shared4 | split70 | sub6
     alpha_lo: float = 0.95
     stagger: str = "even4"        # none | even4 | paper8 | state8
+    decay: str = "scalar"         # scalar: one alpha per state | channel: one per key channel ([N][d_k])
     description: str = ""
     extra: dict = field(default_factory=dict)
 
@@ -55,6 +56,10 @@ class Workload:
     @property
     def heads_per_request(self) -> int:
         return self.n_layers * self.n_heads
+
+    @property
+    def diag_decay(self) -> bool:
+        return self.decay == "channel"
 
     def scaled(self, n_requests: int) -> "Workload":
         return replace(self, n_requests=int(n_requests))
@@ -86,6 +91,13 @@ WORKLOADS = {
     "mamba2_1m": Workload("mamba2_1m", 5, n_requests=512, n_layers=21, n_heads=96, d_k=128, d_v=80, steps=128,
                           kind="scalar", eps_scalar=3e-3, init="aligned8", inputs="split70", alpha_lo=0.95,
                           stagger="even4", description="1,032,192 Mamba-2 states 128x80"),
+    # Kimi Delta Attention (per-channel decay): 64 requests x 20 layers x 32 heads = 40,960 states
+    # 128x128 (Kimi-Linear's KDA layers, SEED section 5), delta rule, inputs and initial ranks as
+    # gdn_delta, each key channel's decay drawn from U(0.9, 1.0) every step.
+    "kda_delta": Workload("kda_delta", 6, n_requests=64, n_layers=20, n_heads=32, d_k=128, d_v=128, steps=512,
+                          kind="delta", eps_delta=1e-2, init="random_rank", inputs="sub6", alpha_lo=0.90,
+                          stagger="paper8", decay="channel",
+                          description="40,960 Kimi Delta Attention states 128x128, per-channel decay"),
 }
 
 
@@ -305,7 +317,8 @@ class StepInputs:
         gen = _gen(self.seed * 1_000_003 + w.config_id * 65_537 + int(step), self.device)
         dev, f32 = self.device, torch.float32
         dk, dv = w.d_k, w.d_v
-        alpha = w.alpha_lo + (1.0 - w.alpha_lo) * torch.rand(n, generator=gen, device=dev, dtype=f32)
+        ashape = (n, dk) if w.diag_decay else (n,)  # per-channel decay: one alpha per key channel
+        alpha = w.alpha_lo + (1.0 - w.alpha_lo) * torch.rand(ashape, generator=gen, device=dev, dtype=f32)
         beta = torch.sigmoid(torch.randn(n, generator=gen, device=dev, dtype=f32))
 
         def draw(m, d):

@@ -57,8 +57,8 @@ def reconstruct(st):
     return S
 
 
-def oracle_from_export(states, eps, d_k, d_v, K, r, L=-1, promote=True, factor_fp16=False):
-    P = OraclePool(len(states), d_k, d_v, K, r, L, promote, factor_fp16=factor_fp16)
+def oracle_from_export(states, eps, d_k, d_v, K, r, L=-1, promote=True, factor_fp16=False, diag_decay=False):
+    P = OraclePool(len(states), d_k, d_v, K, r, L, promote, factor_fp16=factor_fp16, diag_decay=diag_decay)
     for j, st in enumerate(states):
         P.set_state(j, to_oracle_state(st, eps[j]), as_init=False)
     return P

@@ -63,14 +63,14 @@ def test_create_rejects_bad_arguments_without_touching_the_gpu(lib):
     assert lib.ss_state_pool_create(None, None, None, None) == ss.SS_ERR_ARG
     base = dict(n_states=4, d_k=16, d_v=32, pad_slots=8, r_active=8, dense_rank_limit=-1, promote_on_compact=1,
                 max_frozen=0, force_dense=0, n_groups=1, group_of_state=None, group_offset=None, rule=None,
-                eps=None, eps_default=1e-3, dense_capacity=0, arena_components=0, factor_fp16=0)
+                eps=None, eps_default=1e-3, dense_capacity=0, arena_components=0, factor_fp16=0, diag_decay=0)
     cases = [({"n_states": 0}, ss.SS_ERR_ARG), ({"d_k": 18}, ss.SS_ERR_SHAPE), ({"d_v": 260}, ss.SS_ERR_SHAPE),
              ({"pad_slots": 9}, ss.SS_ERR_SHAPE), ({"r_active": 0}, ss.SS_ERR_SHAPE),
              ({"n_groups": 0}, ss.SS_ERR_ARG), ({"max_frozen": 300}, ss.SS_ERR_ARG),
              ({"eps_default": -1.0}, ss.SS_ERR_ARG), ({"dense_capacity": 5}, ss.SS_ERR_ARG),
              ({"d_k": 260, "d_v": 128}, ss.SS_ERR_SHAPE), ({"arena_components": -1}, ss.SS_ERR_ARG),
              ({"arena_components": 1 << 31}, ss.SS_ERR_ARG), ({"factor_fp16": 2}, ss.SS_ERR_ARG),
-             ({"factor_fp16": -1}, ss.SS_ERR_ARG)]
+             ({"factor_fp16": -1}, ss.SS_ERR_ARG), ({"diag_decay": 2}, ss.SS_ERR_ARG)]
     for over, expect in cases:
         d = dict(base, **over)
         desc = ss.PoolDesc(*[d[f] for f, _ in ss.PoolDesc._fields_])
