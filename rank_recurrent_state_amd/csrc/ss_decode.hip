@@ -594,6 +594,7 @@ __global__ __launch_bounds__(256) void k_dense_buf(DenseArgs a) {
 // for the scalar rule its w = v, copied from the inputs in a pass of its own (delta-rule w rows
 // depend on the state and are written by the decode).  The decode has already advanced the
 // slot record, so the entry goes to pad slot n - 1; n = 0 means the step folded.
+template <bool DIAG>
 __global__ __launch_bounds__(256) void k_dense_append(DenseArgs a) {
   const int wv = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const uint32_t slot = blockIdx.x * 4u + (uint32_t)wv;
@@ -607,12 +608,16 @@ __global__ __launch_bounds__(256) void k_dense_append(DenseArgs a) {
   float *pkn = a.pk + ((int64_t)slot * a.K + n - 1) * a.dk;
   float *pwn = a.pw + ((int64_t)slot * a.K + n - 1) * a.dv;
   for (int e = lane; e < dk4 + dv4; e += 64) {
-    if (e < dk4) {
-      const float4 kk = ld4nt(a.k + s * a.dk + 4 * e);  // per-channel decay: stored as k / gamma
-      st4nt(pkn + 4 * e, a.dgam ? div4(kk, ld4(a.dgam + (int64_t)slot * a.dk + 4 * e)) : kk);
-    } else {
-      st4nt(pwn + 4 * (e - dk4), ld4nt(a.v + s * a.dv + 4 * (e - dk4)));
+    // one 16-byte load and one 16-byte store per lane: source and destination are selected first
+    const bool isk = e < dk4;
+    const float *src = isk ? a.k + s * a.dk + 4 * e : a.v + s * a.dv + 4 * (e - dk4);
+    float *dst = isk ? pkn + 4 * e : pwn + 4 * (e - dk4);
+    float4 x = ld4nt(src);
+    if constexpr (DIAG) {  // per-channel decay: the key is stored as k / gamma
+      const float4 g = ld4(a.dgam + (int64_t)slot * a.dk + 4 * (isk ? e : dk4 - 1));
+      x = isk ? div4(x, g) : x;
     }
+    st4nt(dst, x);
   }
 }
 
@@ -834,7 +839,8 @@ hipError_t launch_decode_dense(const DenseArgs &a, int64_t n_upper, bool readonl
     const int mode = readonly ? DM_READOUT : DM_DECODE;
     hipError_t e = any_delta ? dense_buf_p<true>(a, mode, P, grid, st) : dense_buf_p<false>(a, mode, P, grid, st);
     if (e == hipSuccess && !readonly) {  // the pad entries of the step, in a pass of their own
-      hipLaunchKernelGGL(k_dense_append, dim3(grid), dim3(256), 0, st, a);
+      if (a.diag) hipLaunchKernelGGL(k_dense_append<true>, dim3(grid), dim3(256), 0, st, a);
+      else hipLaunchKernelGGL(k_dense_append<false>, dim3(grid), dim3(256), 0, st, a);
       e = hipGetLastError();
     }
     return e;
