@@ -415,21 +415,37 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
     // kept frozen components in sorted order: u <- gamma u / |gamma u|, v copied; gamma <- 1
     const float *fnrm = lds[w] + kOffFnorm;
     const int *forig = reinterpret_cast<const int *>(lds[w] + kOffForig);
-    for (int f = 0; f < kf; ++f) {
-      const int pos = posF[f];
-      if (pos >= total) continue;
-      const int src = forig[f];
-      const int64_t cs = wrap(off_f + src, capF);
-      const float inv = 1.0f / fnrm[src];
-      const F *su = a.frz.U<F>() + cs * dk;
-      const F *sv = a.frz.V<F>() + cs * dv;
-      F *du = slot_u(pos);
-      F *dvv = slot_v(pos);
+    constexpr int FC = 4;  // components in flight: all loads of a batch are issued before its stores
+    for (int f0 = 0; f0 < kf; f0 += FC) {
+      float xu[FC][NS], xv[FC][NS];
 #pragma unroll
-      for (int t = 0; t < NS; ++t) {
-        const int row = lane + 64 * t;
-        if (row < dk) stf(du + row, ldf(su + row) * gr[t] * inv);
-        if (row < dv) stf(dvv + row, ldf(sv + row));
+      for (int c = 0; c < FC; ++c) {
+        const int f = f0 + c < kf ? f0 + c : kf - 1;  // clamped (kf >= 1 inside the loop)
+        const int64_t cs = wrap(off_f + forig[f], capF);
+        const F *su = a.frz.U<F>() + cs * dk;
+        const F *sv = a.frz.V<F>() + cs * dv;
+#pragma unroll
+        for (int t = 0; t < NS; ++t) {
+          const int row = lane + 64 * t;
+          xu[c][t] = ldf(su + (row < dk ? row : dk - 1));
+          xv[c][t] = ldf(sv + (row < dv ? row : dv - 1));
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < FC; ++c) {
+        const int f = f0 + c;
+        if (f >= kf) break;
+        const int pos = posF[f];
+        if (pos >= total) continue;
+        const float inv = 1.0f / fnrm[forig[f]];
+        F *du = slot_u(pos);
+        F *dvv = slot_v(pos);
+#pragma unroll
+        for (int t = 0; t < NS; ++t) {
+          const int row = lane + 64 * t;
+          if (row < dk) stf(du + row, xu[c][t] * gr[t] * inv);
+          if (row < dv) stf(dvv + row, xv[c][t]);
+        }
       }
     }
 #pragma unroll

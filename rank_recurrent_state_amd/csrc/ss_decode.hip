@@ -100,16 +100,19 @@ __global__ __launch_bounds__(256) void k_decode_factored(DecodeArgs a) {
   const float4 qs = DIAG ? mul4(gn4, q4) : q4;  // what the stored parts are read with
   const float4 ks = DIAG ? mul4(gn4, k4) : k4;
   float4 acc = zero4(), acck = zero4();
-  // pairs [ib, ie) of the list in chunks of G * UN; ld(i, x, y, w) issues the loads of pair i
+  // pairs [ib, ie) of the list in chunks of G * UN, double-buffered: the next chunk's loads are in
+  // flight while the current one is reduced; ld(i, x, y, w) issues the loads of pair i
   auto stream = [&](int ib, int ie, auto ld) {
-    for (int i0 = ib; i0 < ie; i0 += G * UN) {
-      float4 x[UN], y[UN];
-      float wt[UN];
+    float4 xA[UN], yA[UN], xB[UN], yB[UN];
+    float wA[UN], wB[UN];
+    auto load = [&](float4 (&x)[UN], float4 (&y)[UN], float (&wt)[UN], int i0) {
 #pragma unroll
       for (int u = 0; u < UN; ++u) {
         const int iu = i0 + u * G + grp;
         ld(iu < ie ? iu : ie - 1, x[u], y[u], wt[u]);  // clamped pair (ie > ib here); its weight is masked at use
       }
+    };
+    auto reduce = [&](const float4 (&x)[UN], const float4 (&y)[UN], const float (&wt)[UN], int i0) {
 #pragma unroll
       for (int u = 0; u < UN; ++u) {
         const float wu = (i0 + u * G + grp < ie) ? wt[u] : 0.f;
@@ -120,6 +123,14 @@ __global__ __launch_bounds__(256) void k_decode_factored(DecodeArgs a) {
           acck = fma4(ck, y[u], acck);
         }
       }
+    };
+    constexpr int C = G * UN;
+    if (ib < ie) load(xA, yA, wA, ib);
+    for (int i0 = ib; i0 < ie; i0 += 2 * C) {
+      if (i0 + C < ie) load(xB, yB, wB, i0 + C);
+      reduce(xA, yA, wA, i0);
+      if (i0 + 2 * C < ie) load(xA, yA, wA, i0 + 2 * C);
+      if (i0 + C < ie) reduce(xB, yB, wB, i0 + C);
     }
   };
   // clamped lanes: q4, k4 are 0 off the key lanes and lanes off the value range are never stored
@@ -233,8 +244,12 @@ template <int P>
 __device__ __forceinline__ f8 cross_group_sum8(f8 x) {
   return {cross_group_sum4<P>(x.a), cross_group_sum4<P>(x.b)};
 }
+__device__ __forceinline__ f8 mul8(f8 x, f8 y) { return {mul4(x.a, y.a), mul4(x.b, y.b)}; }
+__device__ __forceinline__ f8 div8(f8 x, f8 y) { return {div4(x.a, y.a), div4(x.b, y.b)}; }
+__device__ __forceinline__ f8 ld8(const float *p) { return {ld4(p), ld4(p + 4)}; }
 
-template <int P, int UN, bool RO, bool ANYDELTA>
+// DIAG: per-channel decay, as in k_decode_factored.
+template <int P, int UN, bool RO, bool ANYDELTA, bool DIAG>
 __global__ __launch_bounds__(256) void k_decode_factored_h8(DecodeArgs a) {
   constexpr int G = 64 / P;
   const int lane = threadIdx.x & 63;
@@ -265,9 +280,18 @@ __global__ __launch_bounds__(256) void k_decode_factored_h8(DecodeArgs a) {
   const f8 k8 = RO ? zero8() : sel8(kin, ld8nt(a.k + s * dk + 8 * colk));
   const f8 v8 = RO ? zero8() : sel8(vin, ld8nt(a.v + s * dv + 8 * colv));
   const bool delta = ANYDELTA && !RO && (flags & FLAG_DELTA);
-  const float al = RO ? 1.f : uniformf(a.alpha[s]);
+  const float al = (RO || DIAG) ? 1.f : uniformf(a.alpha[s]);
   const float be = delta ? uniformf(a.beta[s]) : 0.f;
+  f8 gn8 = {one4(), one4()};  // DIAG: the accumulated decays after this step (readout: as they are)
+  if constexpr (DIAG) {
+    const f8 g8 = ld8(a.gam + s * dk + 8 * colk);  // clamped lanes: q8 = k8 = 0 and nothing is stored
+    gn8 = RO ? g8 : mul8(g8, ld8nt(a.alpha + s * dk + 8 * colk));
+  }
+  const f8 qs = DIAG ? mul8(gn8, q8) : q8;
+  const f8 ks = DIAG ? mul8(gn8, k8) : k8;
   f8 acc = zero8(), acck = zero8();
+  // pairs in chunks of G * UN (single-buffered: with eight elements per lane a second buffer
+  // costs more occupancy than it hides latency)
   auto stream = [&](int ib, int ie, auto ld) {
     for (int i0 = ib; i0 < ie; i0 += G * UN) {
       f8 x[UN], y[UN];
@@ -280,10 +304,10 @@ __global__ __launch_bounds__(256) void k_decode_factored_h8(DecodeArgs a) {
 #pragma unroll
       for (int u = 0; u < UN; ++u) {
         const float wu = (i0 + u * G + grp < ie) ? wt[u] : 0.f;
-        const float cq = group_sum<P>(dot8(x[u], q8)) * wu;
+        const float cq = group_sum<P>(dot8(x[u], qs)) * wu;
         acc = fma8(cq, y[u], acc);
         if (delta) {
-          const float ck = group_sum<P>(dot8(x[u], k8)) * wu;
+          const float ck = group_sum<P>(dot8(x[u], ks)) * wu;
           acck = fma8(ck, y[u], acck);
         }
       }
@@ -304,7 +328,7 @@ __global__ __launch_bounds__(256) void k_decode_factored_h8(DecodeArgs a) {
     w = ldnt(a.pc + c);
   });
   acc = cross_group_sum8<P>(acc);
-  const f8 pq = scale8(gamma, acc);
+  const f8 pq = DIAG ? acc : scale8(gamma, acc);
   if constexpr (RO) {
     if (grp == 0 && vin) st8(a.o + s * dv + 8 * col, pq);
     return;
@@ -312,13 +336,16 @@ __global__ __launch_bounds__(256) void k_decode_factored_h8(DecodeArgs a) {
     f8 w8 = v8;
     if (delta) {
       acck = cross_group_sum8<P>(acck);
-      w8 = scale8(be, sub8(v8, scale8(al * gamma, acck)));
+      w8 = scale8(be, sub8(v8, DIAG ? acck : scale8(al * gamma, acck)));
     }
     const float kq = group_sum<P>(dot8(k8, q8));
     const f8 o8 = add8(scale8(al, pq), scale8(kq, w8));
     const float gnew = al * gamma;
     if (grp == 0) {
-      if (kin) st8nt(a.pk + (s * (int64_t)K + n) * dk + 8 * col, k8);
+      if (kin) {
+        st8nt(a.pk + (s * (int64_t)K + n) * dk + 8 * col, DIAG ? div8(k8, gn8) : k8);
+        if constexpr (DIAG) st8(a.gam + s * dk + 8 * col, gn8);
+      }
       if (vin) {
         st8nt(a.pw + (s * (int64_t)K + n) * dv + 8 * col, w8);
         st8(a.o + s * dv + 8 * col, o8);
@@ -332,7 +359,7 @@ __global__ __launch_bounds__(256) void k_decode_factored_h8(DecodeArgs a) {
       nm.gamma = gnew;
       nm.packed = meta_pack(ra, rf, n + 1, flags);
       a.meta[s] = nm;
-      const unsigned long long b = decode_bytes(dk, dv, K, rr, n, delta, KIND_FACTORED, 2);
+      const unsigned long long b = decode_bytes(dk, dv, K, rr, n, delta, KIND_FACTORED, 2, DIAG);
       __hip_atomic_fetch_add(&a.acct[s & (kAcctSlots - 1)], b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -729,19 +756,25 @@ hipError_t decode_factored_p(const DecodeArgs &a, int P, hipStream_t st) {
 #ifndef SS_FACT_H8_UN
 #define SS_FACT_H8_UN 4
 #endif
-template <bool RO, bool AD>
+template <bool RO, bool AD, bool DG>
 hipError_t decode_factored_h8_p(const DecodeArgs &a, int P, hipStream_t st) {
   const dim3 grid((unsigned)((a.N + 3) / 4)), block(256);
   switch (P) {
-    case 1: hipLaunchKernelGGL((k_decode_factored_h8<1, 1, RO, AD>), grid, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((k_decode_factored_h8<2, 1, RO, AD>), grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((k_decode_factored_h8<4, 2, RO, AD>), grid, block, 0, st, a); break;
-    case 8: hipLaunchKernelGGL((k_decode_factored_h8<8, 2, RO, AD>), grid, block, 0, st, a); break;
-    case 16: hipLaunchKernelGGL((k_decode_factored_h8<16, SS_FACT_H8_UN, RO, AD>), grid, block, 0, st, a); break;
-    case 32: hipLaunchKernelGGL((k_decode_factored_h8<32, 4, RO, AD>), grid, block, 0, st, a); break;
+    case 1: hipLaunchKernelGGL((k_decode_factored_h8<1, 1, RO, AD, DG>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_decode_factored_h8<2, 1, RO, AD, DG>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((k_decode_factored_h8<4, 2, RO, AD, DG>), grid, block, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((k_decode_factored_h8<8, 2, RO, AD, DG>), grid, block, 0, st, a); break;
+    case 16: hipLaunchKernelGGL((k_decode_factored_h8<16, SS_FACT_H8_UN, RO, AD, DG>), grid, block, 0, st, a); break;
+    case 32: hipLaunchKernelGGL((k_decode_factored_h8<32, 4, RO, AD, DG>), grid, block, 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <bool DG>
+hipError_t decode_factored_h8_f(const DecodeArgs &a, bool readonly, bool any_delta, int P, hipStream_t st) {
+  if (readonly) return decode_factored_h8_p<true, false, DG>(a, P, st);
+  return any_delta ? decode_factored_h8_p<false, true, DG>(a, P, st) : decode_factored_h8_p<false, false, DG>(a, P, st);
 }
 
 template <typename F, bool DG>
@@ -817,14 +850,14 @@ int lanes_per_pair(int dk, int dv) { return pow2_at_least((dk > dv ? dk : dv) >>
 hipError_t launch_decode_factored(const DecodeArgs &a, bool readonly, bool any_delta, hipStream_t st) {
   if (a.N <= 0) return hipSuccess;
   const int P = lanes_per_pair(a.dk, a.dv);
+  if (a.act.half && a.dk % 8 == 0 && a.dv % 8 == 0) {  // fp16 factors, eight elements per lane
+    const int P8 = pow2_at_least((a.dk > a.dv ? a.dk : a.dv) >> 3);
+    return a.gam ? decode_factored_h8_f<true>(a, readonly, any_delta, P8, st)
+                 : decode_factored_h8_f<false>(a, readonly, any_delta, P8, st);
+  }
   if (a.gam) {  // per-channel decay
     return a.act.half ? decode_factored_f<_Float16, true>(a, readonly, any_delta, P, st)
                       : decode_factored_f<float, true>(a, readonly, any_delta, P, st);
-  }
-  if (a.act.half && a.dk % 8 == 0 && a.dv % 8 == 0) {  // fp16 factors, eight elements per lane
-    const int P8 = pow2_at_least((a.dk > a.dv ? a.dk : a.dv) >> 3);
-    if (readonly) return decode_factored_h8_p<true, false>(a, P8, st);
-    return any_delta ? decode_factored_h8_p<false, true>(a, P8, st) : decode_factored_h8_p<false, false>(a, P8, st);
   }
   if (a.act.half) return decode_factored_f<_Float16, false>(a, readonly, any_delta, P, st);
   return decode_factored_f<float, false>(a, readonly, any_delta, P, st);
