@@ -34,9 +34,14 @@ def _pool(ss, w, init, **kw):
                                 diag_decay=w.diag_decay, **kw)
 
 
-def _run_steps(ss, torch, pool, xs, t0, o, ev=None, cons=(0, 1)):
+ASYNC_LOG = {}  # poll results (and launches) of the asynchronous consolidation, per step
+
+
+def _run_steps(ss, torch, pool, xs, t0, o, ev=None, cons=(0, 1), side=None):
     """Run len(xs) steps starting after step t0; optional per-step events.  cons = (groups, period):
-    every `period` steps, consolidate up to `groups` groups from the wait queue after the compactions."""
+    every `period` steps, consolidate up to `groups` groups from the wait queue after the compactions.
+    side: a second stream for the asynchronous consolidation: after each step's compactions the
+    finished result is installed (or dropped when stale) and the next group from the queue starts."""
     for i, x in enumerate(xs):
         t = t0 + i + 1
         if ev is not None:
@@ -44,7 +49,12 @@ def _run_steps(ss, torch, pool, xs, t0, o, ev=None, cons=(0, 1)):
         ss.decode_step(pool, x["q"], x["k"], x["v"], x["alpha"], x["beta"], o)
         for g in ss.schedule_due(pool, t):
             ss.compact(pool, g)
-        if cons[0] > 0 and t % cons[1] == 0:
+        if side is not None:
+            st = ss.consolidate_poll(pool)
+            ASYNC_LOG[st] = ASYNC_LOG.get(st, 0) + 1
+            if st != ss.CONS_RUNNING and ss.consolidate_async(pool, side) >= 0:
+                ASYNC_LOG["launched"] = ASYNC_LOG.get("launched", 0) + 1
+        elif cons[0] > 0 and t % cons[1] == 0:
             ss.consolidate_next(pool, cons[0])
     if ev is not None:
         ev[len(xs)].record()
@@ -217,6 +227,8 @@ def main():
     ap.add_argument("--consolidate", type=int, default=0,
                     help="groups consolidated from the wait queue after a step's compactions (0: off)")
     ap.add_argument("--consolidate-period", type=int, default=1, help="steps between consolidation calls")
+    ap.add_argument("--consolidate-async", action="store_true",
+                    help="consolidate on a second stream, one group at a time from the wait queue, beside the decode")
     ap.add_argument("--factor-fp16", action="store_true",
                     help="store the factor vectors in fp16 (pad, sigma, dense region and arithmetic stay fp32)")
     ap.add_argument("--no-graph", action="store_true",
@@ -248,6 +260,7 @@ def main():
     o = torch.empty(w.n_states, w.d_v, device="cuda")
 
     cons = (max(0, args.consolidate), max(1, args.consolidate_period))
+    side = torch.cuda.Stream() if args.consolidate_async else None  # default priority
     # warmup on a scratch pool of the same workload
     fkw = {"factor_fp16": True} if args.factor_fp16 else {}
     if args.warmup > 0:
@@ -255,13 +268,16 @@ def main():
         wchunk = max(1, min(args.chunk, int(16e9 // (w.n_states * (2 * w.d_k + w.d_v + 2 + (w.d_k if w.diag_decay else 0)) * 4))))
         for c0 in range(0, args.warmup, wchunk):
             xs = [gen.generate(t) for t in range(c0 + 1, min(args.warmup, c0 + wchunk) + 1)]
-            _run_steps(ss, torch, pool, xs, c0, o, cons=cons)
+            _run_steps(ss, torch, pool, xs, c0, o, cons=cons, side=side)
+        if side is not None:
+            ss.consolidate_poll(pool, wait=True)
         torch.cuda.synchronize()
         pool.close()
         del xs
         log(f"[bench] warmup {args.warmup} steps done")
 
     # the timed job
+    ASYNC_LOG.clear()
     pool = _pool(ss, w, init, **fkw)
     st0 = ss.pool_stats(pool)
     ss.pool_timing(pool, True)
@@ -275,7 +291,7 @@ def main():
         xs = [gen.generate(s) for s in range(t + 1, t + n + 1)]
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
         torch.cuda.synchronize()
-        _run_steps(ss, torch, pool, xs, t, o, ev, cons=cons)
+        _run_steps(ss, torch, pool, xs, t, o, ev, cons=cons, side=side)
         torch.cuda.synchronize()
         step_ms += [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
         t += n
@@ -313,9 +329,14 @@ def main():
                   "algorithmic_TFLOPs": cflops / (kms["compact"] / 1e3) / 1e12 if kms["compact"] else None,
                   "materialize_ms_total": kms["materialize"], "promotions": st1["promotions"] - st0["promotions"]}
     consolidation = None
-    if cons[0] > 0:
+    if cons[0] > 0 or side is not None:
         xf = st1["consolidate_flops"] - st0["consolidate_flops"]
-        consolidation = {"groups_per_call": cons[0], "period": cons[1], "launches": kn["consolidate"],
+        alog = {"launched": ASYNC_LOG.get("launched", 0), "steps_running": ASYNC_LOG.get(ss.CONS_RUNNING, 0),
+                "installed": ASYNC_LOG.get(ss.CONS_INSTALLED, 0), "discarded": ASYNC_LOG.get(ss.CONS_DISCARDED, 0)}
+        consolidation = {"mode": "async (second stream)" if side is not None else "in the step",
+                         "async_polls": alog if side is not None else None,
+                         "groups_per_call": cons[0], "period": cons[1], "launches": kn["consolidate"],
+                         "live_bytes_end": st1["live_bytes"], "n_dense_end": st1["n_dense"],
                          "ms_total": kms["consolidate"], "states": st1["consolidate_states"] - st0["consolidate_states"],
                          "removed_components": st1["consolidate_removed"] - st0["consolidate_removed"],
                          "algorithmic_TFLOPs": xf / (kms["consolidate"] / 1e3) / 1e12 if kms["consolidate"] else None,

@@ -242,6 +242,31 @@ ss_status ss_consolidate(ss_pool *pool, int32_t group, hipStream_t stream);
  * result current.  Errors as ss_consolidate. */
 ss_status ss_consolidate_next(ss_pool *pool, int32_t max_groups, int32_t *out, int32_t *n_done, hipStream_t stream);
 
+/* Asynchronous consolidation ([SS] 4.3 "Asynchronous CPU Consolidation": the consolidation runs
+ * beside the decode, a result that has gone stale is dropped, and a fresh one replaces the frozen
+ * part).  Here the exact SVD runs on the GPU, on a second stream `side` given by the caller, while
+ * the pool's stream goes on decoding.
+ *  ss_consolidate_async: group >= 0 selects that group; group < 0 takes, among the groups waiting
+ *    (compacted since their last consolidation), the one compacted most recently, whose result has
+ *    the longest time to land before the group compacts again; then the least recently
+ *    consolidated, then the lowest id (*launched = -1 when no group waits).  On
+ *    `stream` it copies the group's 16-byte records aside; `side` waits for that copy and runs the
+ *    kernel, which reads the frozen parts and writes its results to staging only (the rings and
+ *    records are not touched).  One consolidation may be in flight per pool (SS_ERR_STATE for a
+ *    second); the staging (largest group x frozen cap x (d_k + d_v + 1) floats) is allocated at the
+ *    first call.  Not available with diag_decay (SS_ERR_ARG); a frozen part too large for the
+ *    kernel's LDS gives SS_ERR_SHAPE.
+ *  ss_consolidate_poll: *state = SS_CONS_IDLE (nothing in flight), SS_CONS_RUNNING (the kernel has
+ *    not finished; wait = 0 returns at once, wait != 0 blocks until it has), SS_CONS_INSTALLED (an
+ *    install is enqueued on `stream`: each state whose record still shows the active and frozen
+ *    counts of the copy gets the result in place of its frozen part), or SS_CONS_DISCARDED (the
+ *    group was compacted, or consolidated synchronously, after the launch: the result is dropped).
+ * The caller keeps `side` alive until the poll has returned INSTALLED or DISCARDED; a ring re-pack
+ * waits for the kernel before it frees the rings the kernel reads.  Streams of default priority. */
+enum { SS_CONS_IDLE = 0, SS_CONS_RUNNING = 1, SS_CONS_INSTALLED = 2, SS_CONS_DISCARDED = 3 };
+ss_status ss_consolidate_async(ss_pool *pool, int32_t group, hipStream_t stream, hipStream_t side, int32_t *launched);
+ss_status ss_consolidate_poll(ss_pool *pool, int32_t wait, hipStream_t stream, int32_t *state);
+
 /* Staggered schedule ([SS] 4.2 "Staggered compaction across layers"): the
  * groups due after decode step `step` (counted from 1) are those with
  * (step + group_offset[g]) mod K == 0.  Writes up to `cap` group ids to out

@@ -53,7 +53,8 @@ __global__ __launch_bounds__(256) void k_consolidate(ConsolidateArgs a) {
   extern __shared__ float sm[];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int s = uniform(a.members[blockIdx.x]);
-  const Meta m = a.meta[s];
+  const Meta m = a.snap ? a.snap[blockIdx.x] : a.meta[s];
+  const bool staged = a.st_u != nullptr;  // asynchronous form: results to staging, rings and records untouched
   const uint32_t packed = (uint32_t)uniform((int)m.packed);
   if (meta_flags(packed) & FLAG_DENSE) return;
   const int ra = meta_ra(packed), rf = meta_rf(packed), n = meta_n(packed);
@@ -67,14 +68,17 @@ __global__ __launch_bounds__(256) void k_consolidate(ConsolidateArgs a) {
   int *perm = reinterpret_cast<int *>(dt + F2);       // [F2]
   float *ctl = reinterpret_cast<float *>(perm + F2);  // [2]
   int *flag = reinterpret_cast<int *>(ctl + 2);       // [2]: rotation seen, per sweep parity
-  // where Q is parked: fp32 factors park it in the frozen v slots; fp16 factors would round it,
-  // so they park it in LDS after the other arrays ([F2][d_v])
+  // where Q is parked: fp32 factors park it in the frozen v slots; fp16 factors would round it, so
+  // they park it in LDS after the other arrays ([F2][d_v]); the asynchronous form must not write
+  // the rings and parks it in its own staging rows (fp32), keeping the LDS of the in-place form
   constexpr bool kHalf = !std::is_same<F, float>::value;
+  const size_t sbase = (size_t)blockIdx.x * a.fmax;  // staging rows of this member
   float *QL = sm + ((reinterpret_cast<float *>(flag + 2) - sm + 3) & ~(ptrdiff_t)3);  // float4-aligned
   const int64_t capF = a.frz.cap;
   const int off_f = uniform(m.off_f);
   const int dk4 = dk >> 2, dv4 = dv >> 2;
   auto qpark = [&](int j) -> float * {
+    if (staged) return a.st_v + (sbase + j) * dv;
     return kHalf ? QL + (size_t)j * dv : reinterpret_cast<float *>(a.frz.V<F>()) + wrap(off_f + j, capF) * dv;
   };
 
@@ -250,9 +254,14 @@ __global__ __launch_bounds__(256) void k_consolidate(ConsolidateArgs a) {
   __syncthreads();
   for (int e = tid; e < kept * dk; e += kCT) {
     const int k = e / dk, i = e - k * dk, j = perm[k];
-    stf(a.frz.U<F>() + wrap(off_f + k, capF) * dk + i, A[(size_t)j * bs + i] * (1.0f / sg[j]));
+    const float x = A[(size_t)j * bs + i] * (1.0f / sg[j]);
+    if (staged) a.st_u[(sbase + k) * dk + i] = x;
+    else stf(a.frz.U<F>() + wrap(off_f + k, capF) * dk + i, x);
   }
-  if (tid < kept) a.frz.s[wrap(off_f + tid, capF)] = sg[perm[tid]];
+  if (tid < kept) {
+    if (staged) a.st_s[sbase + tid] = sg[perm[tid]];
+    else a.frz.s[wrap(off_f + tid, capF)] = sg[perm[tid]];
+  }
   __syncthreads();  // B is consumed: bring Q back into A
   for (int e = tid; e < rf * dv4; e += kCT) {
     const int j = e / dv4, c = e - j * dv4;
@@ -265,10 +274,12 @@ __global__ __launch_bounds__(256) void k_consolidate(ConsolidateArgs a) {
     float acc = 0.f;
 #pragma unroll 8
     for (int c = 0; c < rf; ++c) acc = fmaf(A[(size_t)c * dv + i], yj[c], acc);
-    stf(a.frz.V<F>() + wrap(off_f + k, capF) * dv + i, acc);
+    if (staged) a.st_v[(sbase + k) * dv + i] = acc;
+    else stf(a.frz.V<F>() + wrap(off_f + k, capF) * dv + i, acc);
   }
   if (tid == 0) {
-    a.meta[s].packed = meta_pack(ra, kept, n, meta_flags(packed));
+    if (staged) a.st_cnt[blockIdx.x] = kept;
+    else a.meta[s].packed = meta_pack(ra, kept, n, meta_flags(packed));
     const unsigned long long f = (unsigned long long)rf * rf;
     const unsigned long long flops = 4ull * dv * f + (unsigned long long)dk * f +
                                      (unsigned long long)sweeps * (rf * (rf - 1) / 2) * (12ull * dk + 6ull * rf) +
@@ -276,7 +287,7 @@ __global__ __launch_bounds__(256) void k_consolidate(ConsolidateArgs a) {
     const int slot = blockIdx.x % kAcctSlots;
     atomicAdd(a.acct_flops + slot, flops);
     atomicAdd(a.acct_states + slot, 1ull);
-    atomicAdd(a.acct_removed + slot, (unsigned long long)(rf - kept));
+    if (!staged) atomicAdd(a.acct_removed + slot, (unsigned long long)(rf - kept));
   }
 }
 
@@ -291,17 +302,67 @@ hipError_t consolidate_f(const ConsolidateArgs &a, int need, size_t sh, hipStrea
   return hipGetLastError();
 }
 
+__global__ __launch_bounds__(256) void k_cons_snapshot(const Meta *meta, const int32_t *members, int32_t n,
+                                                       Meta *snap) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) snap[i] = meta[members[i]];
+}
+
+// one wavefront per member: the staged frozen part replaces the stored one in place (it never has
+// more components), where the record still matches the snapshot the result was computed from
+template <typename F>
+__global__ __launch_bounds__(256) void k_cons_install(InstallArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 4 + uniform(threadIdx.x >> 6);
+  if (i >= a.n_members) return;
+  const int s = uniform(a.members[i]);
+  const Meta m = a.meta[s], sm = a.snap[i];
+  const uint32_t pk = (uint32_t)uniform((int)m.packed), spk = (uint32_t)uniform((int)sm.packed);
+  const int rf0 = meta_rf(spk);
+  if (rf0 == 0 || rf0 > a.fmax) return;  // the kernel skipped this state
+  if ((meta_flags(pk) & FLAG_DENSE) || meta_ra(pk) != meta_ra(spk) || meta_rf(pk) != meta_rf(spk)) return;
+  const int kept = uniform(a.st_cnt[i]);
+  const int64_t capF = a.frz.cap, off_f = uniform(m.off_f);
+  const size_t sbase = (size_t)i * a.fmax;
+  const int dk = a.dk, dv = a.dv;
+  for (int k = 0; k < kept; ++k) {
+    const int64_t c = wrap(off_f + k, capF);
+    for (int e = lane; e < dk; e += 64) stf(a.frz.U<F>() + c * dk + e, a.st_u[(sbase + k) * dk + e]);
+    for (int e = lane; e < dv; e += 64) stf(a.frz.V<F>() + c * dv + e, a.st_v[(sbase + k) * dv + e]);
+    if (lane == 0) a.frz.s[c] = a.st_s[sbase + k];
+  }
+  if (lane == 0) {
+    a.meta[s].packed = meta_pack(meta_ra(pk), kept, meta_n(pk), meta_flags(pk));
+    atomicAdd(a.acct_removed + (s & (kAcctSlots - 1)), (unsigned long long)(rf0 - kept));
+    atomicAdd(a.installed, 1u);
+  }
+}
+
 }  // namespace
 
-size_t consolidate_lds_bytes(int dk, int dv, int fmax, bool half) {
+hipError_t launch_cons_snapshot(const Meta *meta, const int32_t *members, int32_t n, Meta *snap, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_cons_snapshot, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, meta, members, n, snap);
+  return hipGetLastError();
+}
+
+hipError_t launch_cons_install(const InstallArgs &a, hipStream_t st) {
+  if (a.n_members <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((a.n_members + 3) / 4)), block(256);
+  if (a.frz.half) hipLaunchKernelGGL(k_cons_install<_Float16>, grid, block, 0, st, a);
+  else hipLaunchKernelGGL(k_cons_install<float>, grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+size_t consolidate_lds_bytes(int dk, int dv, int fmax, bool q_in_lds) {
   const int F2 = (fmax + 1) & ~1, bs = bank_stride(dk);
   return sizeof(float) * ((size_t)F2 * (bs > dv ? bs : dv) + (size_t)F2 * bank_stride(F2) + 3 * (size_t)F2 + 4 +
-                          (half ? (size_t)F2 * dv + 4 : 0));
+                          (q_in_lds ? (size_t)F2 * dv + 4 : 0));
 }
 
 hipError_t launch_consolidate(const ConsolidateArgs &a, hipStream_t st) {
   if (a.n_members <= 0 || a.fmax <= 0) return hipSuccess;
-  const size_t sh = consolidate_lds_bytes(a.dk, a.dv, a.fmax, a.frz.half != 0);
+  const size_t sh = consolidate_lds_bytes(a.dk, a.dv, a.fmax, a.frz.half != 0 && a.st_u == nullptr);
   if (sh > kConsolidateLdsMax) return hipErrorInvalidValue;
   const int need = a.dk > a.fmax ? a.dk : a.fmax;  // elements of a column pair: 8 lanes x KE
   if (need > 256) return hipErrorInvalidValue;

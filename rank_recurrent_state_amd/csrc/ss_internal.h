@@ -258,10 +258,32 @@ struct ConsolidateArgs {
   Meta *meta;
   Arena act, frz;
   unsigned long long *acct_flops, *acct_states, *acct_removed;
+  // asynchronous form (all nullptr: in place).  The kernel reads the group's records from `snap`
+  // (taken at launch) and writes its results to staging instead of the rings:
+  const Meta *snap;            // [n_members]
+  float *st_u, *st_v, *st_s;   // [n_members][fmax][d_k], [n_members][fmax][d_v], [n_members][fmax]
+  int32_t *st_cnt;             // [n_members] kept frozen components
 };
 constexpr size_t kConsolidateLdsMax = 160 * 1024;  // LDS per workgroup on gfx950
-size_t consolidate_lds_bytes(int dk, int dv, int fmax, bool half);
+size_t consolidate_lds_bytes(int dk, int dv, int fmax, bool q_in_lds);
 hipError_t launch_consolidate(const ConsolidateArgs &a, hipStream_t st);
+// asynchronous consolidation: the group's records copied aside at launch (on the pool's stream),
+// and the install of the staged results, state by state, where a state's record still shows the
+// frozen part the result was computed from (same active and frozen counts, not dense)
+hipError_t launch_cons_snapshot(const Meta *meta, const int32_t *members, int32_t n, Meta *snap, hipStream_t st);
+struct InstallArgs {
+  int dk, dv, fmax;
+  int32_t n_members;
+  const int32_t *members;
+  const Meta *snap;
+  Meta *meta;
+  Arena frz;
+  const float *st_u, *st_v, *st_s;
+  const int32_t *st_cnt;
+  unsigned long long *acct_removed;
+  uint32_t *installed;         // states installed (device counter)
+};
+hipError_t launch_cons_install(const InstallArgs &a, hipStream_t st);
 
 // how a state is decoded
 enum DecodeKind : int { KIND_FACTORED = 0, KIND_DENSE_BUFFERED = 1, KIND_DENSE_PLAIN = 2 };

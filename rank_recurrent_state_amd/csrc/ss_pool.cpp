@@ -97,6 +97,22 @@ struct ss_pool {
   std::vector<char> cons_wait;
   std::vector<int64_t> cons_last;
   int64_t cons_seq = 0, consolidate_calls = 0;
+  // asynchronous consolidation: one group at a time on a caller's second stream, results staged and
+  // installed by ss_consolidate_poll on the pool's stream; stale once the group compacts meanwhile
+  struct ConsAsync {
+    bool inflight = false, stale = false;
+    int group = -1;
+    hipEvent_t snap_ev = nullptr, done_ev = nullptr;
+    ss::Meta *snap = nullptr;
+    float *st_u = nullptr, *st_v = nullptr, *st_s = nullptr;
+    int32_t *st_cnt = nullptr;
+    uint32_t *installed = nullptr;
+    int64_t cap_members = 0;
+    int fmax = 0;
+    int64_t launched = 0, installs = 0, discarded = 0;
+    std::vector<int64_t> last_compact;  // per group: sequence number of its latest compaction (-1: none)
+    int64_t compact_seq = 0;
+  } ca;
   ss_status sticky = SS_OK;
   std::string sticky_msg;
   // measurement hook: event pairs around kernel launches
@@ -338,6 +354,13 @@ ss_status ring_repack(ss_pool *p, int first, const int64_t (&newcap)[2], hipStre
       if (blk[R]) (void)hipFree(blk[R]);
     return e == hipErrorOutOfMemory ? fail(SS_ERR_OOM, "ring growth: device allocation failed")
                                     : hip_fail(e, "ring repack");
+  }
+  if (p->ca.inflight) {  // an asynchronous consolidation may still read the old rings
+    e = hipEventSynchronize(p->ca.done_ev);
+    if (e != hipSuccess) {
+      for (int R = 0; R < 2; ++R) (void)hipFree(blk[R]);
+      return hip_fail(e, "ring repack: waiting for the consolidation");
+    }
   }
   for (int R = 0; R < 2; ++R) {
     (void)hipFree(p->ring_blk[R]);
@@ -769,6 +792,8 @@ ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipSt
 ss_status ss_state_pool_destroy(ss_pool *p) {
   if (!p) return SS_OK;
   (void)hipDeviceSynchronize();
+  if (p->ca.snap_ev) (void)hipEventDestroy(p->ca.snap_ev);
+  if (p->ca.done_ev) (void)hipEventDestroy(p->ca.done_ev);
   free_all(p);
   delete p;
   return SS_OK;
@@ -854,6 +879,9 @@ static hipError_t enqueue_prune(ss_pool *p, int64_t fact_grid, hipStream_t strea
 // host bookkeeping after the compaction of group g was enqueued with segment bounds ab
 static void after_compact_group(ss_pool *p, int g, const int64_t (&ab)[2]) {
   p->cons_wait[g] = 1;
+  if (p->ca.inflight && p->ca.group == g) p->ca.stale = true;  // its snapshot no longer describes the group
+  if ((int)p->ca.last_compact.size() < p->G) p->ca.last_compact.assign(p->G, -1);
+  p->ca.last_compact[g] = p->ca.compact_seq++;
   for (int R = 0; R < 2; ++R) {  // the group's new segment, by its bound
     p->last_seq[R][g] = p->seq;
     p->seg_bound[R][g] = ab[R];
@@ -963,6 +991,7 @@ static hipError_t enqueue_consolidate_group(ss_pool *p, int g, hipStream_t strea
 }
 
 static ss_status consolidate_checked(ss_pool *p, int g, hipStream_t stream) {
+  if (p->ca.inflight && p->ca.group == g) p->ca.stale = true;
   p->cons_wait[g] = 0;
   p->cons_last[g] = p->cons_seq++;
   if (p->group_size[g] == 0 || frozen_max(p) == 0) return SS_OK;
@@ -1013,6 +1042,108 @@ ss_status ss_consolidate_next(ss_pool *p, int32_t max_groups, int32_t *out, int3
     if (out) out[i] = wait[i];
     *n_done = i + 1;
   }
+  return SS_OK;
+}
+
+ss_status ss_consolidate_async(ss_pool *p, int32_t group, hipStream_t stream, hipStream_t side, int32_t *launched) {
+  if (!p || !launched) return fail(SS_ERR_ARG, "bad arguments");
+  *launched = -1;
+  ss_status st = consolidate_precheck(p);
+  if (st != SS_OK) return st;
+  if (group >= p->G) return fail(SS_ERR_ARG, "group out of range");
+  if (p->ca.inflight) return fail(SS_ERR_STATE, "an asynchronous consolidation is already in flight");
+  if (p->force_dense) return SS_OK;
+  const int fmax = frozen_max(p);
+  if (ss::consolidate_lds_bytes(p->dk, p->dv, fmax, false) > ss::kConsolidateLdsMax)
+    return fail(SS_ERR_SHAPE, "the pool's largest frozen part does not fit the consolidation kernel's LDS");
+  int g = group;
+  if (g < 0) {
+    // among the waiting groups, the one compacted most recently: its result has the longest time
+    // to land before the group's next compaction makes it stale; then least recently
+    // consolidated, then lowest id
+    if ((int)p->ca.last_compact.size() < p->G) p->ca.last_compact.assign(p->G, -1);
+    const std::vector<int64_t> &lc = p->ca.last_compact;
+    for (int h = 0; h < p->G; ++h) {
+      if (!p->cons_wait[h]) continue;
+      if (g < 0 || lc[h] > lc[g] || (lc[h] == lc[g] && p->cons_last[h] < p->cons_last[g])) g = h;
+    }
+    if (g < 0) return SS_OK;
+  }
+  p->cons_wait[g] = 0;
+  p->cons_last[g] = p->cons_seq++;
+  if (p->group_size[g] == 0 || fmax == 0) return SS_OK;
+  hipError_t e = hipSuccess;
+  int64_t gmax = 0;
+  for (int h = 0; h < p->G; ++h) gmax = std::max<int64_t>(gmax, p->group_size[h]);
+  if (p->ca.cap_members < gmax || p->ca.fmax < fmax) {  // staging for the largest group (first call)
+    if (p->ca.cap_members) return fail(SS_ERR_STATE, "staging shape changed");
+    e = dalloc(p, &p->ca.snap, (size_t)gmax);
+    if (e == hipSuccess) e = dalloc(p, &p->ca.st_u, (size_t)gmax * fmax * p->dk);
+    if (e == hipSuccess) e = dalloc(p, &p->ca.st_v, (size_t)gmax * fmax * p->dv);
+    if (e == hipSuccess) e = dalloc(p, &p->ca.st_s, (size_t)gmax * fmax);
+    if (e == hipSuccess) e = dalloc(p, &p->ca.st_cnt, (size_t)gmax);
+    if (e == hipSuccess) e = dalloc(p, &p->ca.installed, 1);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ca.snap_ev, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ca.done_ev, hipEventDisableTiming);
+    if (e != hipSuccess) return e == hipErrorOutOfMemory ? fail(SS_ERR_OOM, "consolidation staging") : hip_fail(e, "consolidation staging");
+    p->ca.cap_members = gmax;
+    p->ca.fmax = fmax;
+  }
+  const int32_t n = (int32_t)p->group_size[g];
+  const int32_t *members = p->members + p->group_start[g];
+  e = ss::launch_cons_snapshot(p->meta, members, n, p->ca.snap, stream);
+  if (e == hipSuccess) e = hipEventRecord(p->ca.snap_ev, stream);
+  if (e == hipSuccess) e = hipStreamWaitEvent(side, p->ca.snap_ev, 0);
+  if (e == hipSuccess) {
+    ss::ConsolidateArgs a{};
+    a.dk = p->dk; a.dv = p->dv; a.fmax = fmax; a.n_members = n; a.members = members;
+    a.eps = p->eps; a.meta = p->meta; a.act = p->act; a.frz = p->frz;
+    a.acct_flops = p->acct + ss::A_CONS_FLOPS * ss::kAcctSlots;
+    a.acct_states = p->acct + ss::A_CONS_STATES * ss::kAcctSlots;
+    a.acct_removed = p->acct + ss::A_CONS_REMOVED * ss::kAcctSlots;
+    a.snap = p->ca.snap; a.st_u = p->ca.st_u; a.st_v = p->ca.st_v; a.st_s = p->ca.st_s; a.st_cnt = p->ca.st_cnt;
+    e = ss::launch_consolidate(a, side);
+  }
+  if (e == hipSuccess) e = hipEventRecord(p->ca.done_ev, side);
+  if (e != hipSuccess) return hip_fail(e, "asynchronous consolidation launch");
+  p->ca.inflight = true;
+  p->ca.stale = false;
+  p->ca.group = g;
+  p->ca.launched++;
+  *launched = g;
+  return SS_OK;
+}
+
+ss_status ss_consolidate_poll(ss_pool *p, int32_t wait, hipStream_t stream, int32_t *state) {
+  if (!p || !state) return fail(SS_ERR_ARG, "bad arguments");
+  *state = SS_CONS_IDLE;
+  ss_status st = poll(p);
+  if (st != SS_OK) return st;
+  if (!p->ca.inflight) return SS_OK;
+  hipError_t e = wait ? hipEventSynchronize(p->ca.done_ev) : hipEventQuery(p->ca.done_ev);
+  if (e == hipErrorNotReady) {
+    *state = SS_CONS_RUNNING;
+    return SS_OK;
+  }
+  if (e != hipSuccess) return hip_fail(e, "asynchronous consolidation");
+  p->ca.inflight = false;
+  if (p->ca.stale) {
+    p->ca.discarded++;
+    *state = SS_CONS_DISCARDED;
+    return SS_OK;
+  }
+  ss::InstallArgs ia{};
+  const int g = p->ca.group;
+  ia.dk = p->dk; ia.dv = p->dv; ia.fmax = p->ca.fmax; ia.n_members = (int32_t)p->group_size[g];
+  ia.members = p->members + p->group_start[g]; ia.snap = p->ca.snap; ia.meta = p->meta; ia.frz = p->frz;
+  ia.st_u = p->ca.st_u; ia.st_v = p->ca.st_v; ia.st_s = p->ca.st_s; ia.st_cnt = p->ca.st_cnt;
+  ia.acct_removed = p->acct + ss::A_CONS_REMOVED * ss::kAcctSlots; ia.installed = p->ca.installed;
+  e = hipStreamWaitEvent(stream, p->ca.done_ev, 0);
+  if (e == hipSuccess) e = ss::launch_cons_install(ia, stream);
+  if (e != hipSuccess) return hip_fail(e, "consolidation install");
+  p->ca.installs++;
+  p->consolidate_calls++;
+  *state = SS_CONS_INSTALLED;
   return SS_OK;
 }
 

@@ -87,6 +87,8 @@ def load_library():
     lib.ss_compact.argtypes = [vp, ctypes.c_int32, vp]
     lib.ss_consolidate.argtypes = [vp, ctypes.c_int32, vp]
     lib.ss_consolidate_next.argtypes = [vp, ctypes.c_int32, _c_i32p, _c_i32p, vp]
+    lib.ss_consolidate_async.argtypes = [vp, ctypes.c_int32, vp, vp, _c_i32p]
+    lib.ss_consolidate_poll.argtypes = [vp, ctypes.c_int32, vp, _c_i32p]
     lib.ss_schedule_due.argtypes = [vp, ctypes.c_int64, _c_i32p, ctypes.c_int32, _c_i32p]
     lib.ss_state_export.argtypes = [vp, _c_i64p, ctypes.c_int64, vp, ctypes.c_size_t,
                                     ctypes.POINTER(ctypes.c_size_t), vp]
@@ -332,6 +334,24 @@ def consolidate_next(pool: StatePool, max_groups: int, stream=None) -> list:
     n = ctypes.c_int32()
     _check(load_library().ss_consolidate_next(pool.handle, int(max_groups), out, ctypes.byref(n), _stream(stream)))
     return [int(out[i]) for i in range(n.value)]
+
+
+CONS_IDLE, CONS_RUNNING, CONS_INSTALLED, CONS_DISCARDED = 0, 1, 2, 3
+
+
+def consolidate_async(pool: StatePool, side, group: int = -1, stream=None) -> int:
+    """Start the consolidation of one group on the stream `side` (group < 0: the head of the wait
+    queue); returns the group launched, or -1 when none waits."""
+    g = ctypes.c_int32()
+    _check(load_library().ss_consolidate_async(pool.handle, int(group), _stream(stream), _stream(side), ctypes.byref(g)))
+    return int(g.value)
+
+
+def consolidate_poll(pool: StatePool, wait: bool = False, stream=None) -> int:
+    """CONS_IDLE, CONS_RUNNING, CONS_INSTALLED (install enqueued on `stream`) or CONS_DISCARDED."""
+    st = ctypes.c_int32()
+    _check(load_library().ss_consolidate_poll(pool.handle, int(bool(wait)), _stream(stream), ctypes.byref(st)))
+    return int(st.value)
 
 
 def schedule_due(pool: StatePool, step: int) -> list:

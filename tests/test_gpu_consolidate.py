@@ -211,3 +211,155 @@ def test_consolidate_fp16_factors(name):
     removed, guard = _consolidate_and_compare(w, init, pool, ids, fp16=True)
     print("fp16", name, "removed", removed, "guard", guard)
     pool.close()
+
+
+# ---------------------------------------------------------------------------------------------
+# asynchronous consolidation on a second stream (SinkState 4.3): staged, installed, or dropped
+# ---------------------------------------------------------------------------------------------
+def _run_steps(w, pool, t0, t1, o, gen):
+    for t in range(t0, t1 + 1):
+        x = gen.generate(t)
+        ss.decode_step(pool, x["q"], x["k"], x["v"], x["alpha"], x["beta"], o)
+        for g in ss.schedule_due(pool, t):
+            ss.compact(pool, g)
+
+
+def _not_due(pool, t0, t1, G):
+    due = set()
+    for t in range(t0, t1 + 1):
+        due |= set(ss.schedule_due(pool, t))
+    return [g for g in range(G) if g not in due]
+
+
+@pytest.mark.parametrize("name,fp16", [("gdn_delta", False), ("gdn_delta", True), ("mamba2_258k", False)])
+def test_consolidate_async_equals_sync(name, fp16):
+    """Launch on a side stream, keep decoding on the pool's stream (the group is not compacted
+    meanwhile), install: the group's frozen parts equal those of a twin pool consolidated
+    synchronously at the launch point; every other part of the state stays the pool's own."""
+    w = W.get(name, n_requests=1)
+    init = W.initial_state(w)
+    kw = {"factor_fp16": True} if fp16 else {}
+    pa, pb = _pool(w, init, **kw), _pool(w, init, **kw)
+    gen = W.StepInputs(w, device="cuda")
+    o = torch.empty(w.n_states, w.d_v, device="cuda")
+    for p in (pa, pb):
+        _run_steps(w, p, 1, 40, o, gen)
+    G = len(init["group_offset"])
+    g = _not_due(pa, 41, 43, G)[0]
+    side = torch.cuda.Stream()
+    assert ss.consolidate_async(pa, side, group=g) == g
+    with pytest.raises(RuntimeError):  # one in flight per pool
+        ss.consolidate_async(pa, side, group=g)
+    ss.consolidate(pb, g)
+    for p in (pa, pb):
+        _run_steps(w, p, 41, 43, o, gen)
+    assert ss.consolidate_poll(pa, wait=True) == ss.CONS_INSTALLED
+    assert ss.consolidate_poll(pa) == ss.CONS_IDLE
+    torch.cuda.synchronize()
+    ids = np.nonzero(init["group_of_state"] == g)[0]
+    a, b = ss.state_export(pa, ids), ss.state_export(pb, ids)
+    removed = 0
+    for x, y in zip(a, b):
+        assert x["dense"] == y["dense"]
+        if x["dense"]:
+            continue
+        ra = x["n_active"]
+        assert ra == y["n_active"] and len(x["sigma"]) == len(y["sigma"])
+        for key in ("U", "V", "sigma"):
+            assert np.array_equal(x[key][ra:], y[key][ra:]), key  # the same kernel arithmetic
+            assert np.array_equal(x[key][:ra], y[key][:ra]), key
+    sa, sb = ss.pool_stats(pa), ss.pool_stats(pb)
+    assert sa["consolidate_removed"] == sb["consolidate_removed"]
+    print(name, fp16, "group", g, "removed", sa["consolidate_removed"])
+    pa.close()
+    pb.close()
+
+
+def test_consolidate_async_stale_is_dropped():
+    """The group compacts before the poll: the result is dropped and the pool equals a twin that
+    never consolidated."""
+    w = W.get("gdn_delta", n_requests=1)
+    init = W.initial_state(w)
+    pa, pb = _pool(w, init), _pool(w, init)
+    gen = W.StepInputs(w, device="cuda")
+    o = torch.empty(w.n_states, w.d_v, device="cuda")
+    for p in (pa, pb):
+        _run_steps(w, p, 1, 40, o, gen)
+    due = ss.schedule_due(pa, 41)
+    g = due[0]
+    side = torch.cuda.Stream()
+    assert ss.consolidate_async(pa, side, group=g) == g
+    for p in (pa, pb):
+        _run_steps(w, p, 41, 41, o, gen)  # compacts g
+    assert ss.consolidate_poll(pa, wait=True) == ss.CONS_DISCARDED
+    torch.cuda.synchronize()
+    ids = np.arange(w.n_states)
+    for x, y in zip(ss.state_export(pa, ids), ss.state_export(pb, ids)):
+        assert x["dense"] == y["dense"]
+        key = "S" if x["dense"] else "sigma"
+        assert np.array_equal(x[key], y[key])
+    pa.close()
+    pb.close()
+
+
+def test_consolidate_async_across_ring_repacks():
+    """Rings created at the initial size: compactions of other groups re-pack them while the
+    consolidation reads them (the re-pack waits for it); the install then lands at the moved
+    positions, equal to a synchronous twin."""
+    w = W.get("gdn_delta", n_requests=1)
+    init = W.initial_state(w)
+    pa = _pool(w, init, arena_components=1)
+    pb = _pool(w, init, arena_components=1)
+    gen = W.StepInputs(w, device="cuda")
+    o = torch.empty(w.n_states, w.d_v, device="cuda")
+    for p in (pa, pb):
+        _run_steps(w, p, 1, 12, o, gen)
+    G = len(init["group_offset"])
+    g = _not_due(pa, 13, 16, G)[0]
+    side = torch.cuda.Stream()
+    r0 = ss.pool_stats(pa)["ring_repacks"]
+    assert ss.consolidate_async(pa, side, group=g) == g
+    ss.consolidate(pb, g)
+    for p in (pa, pb):
+        _run_steps(w, p, 13, 16, o, gen)
+    st = ss.consolidate_poll(pa, wait=True)
+    r1 = ss.pool_stats(pa)["ring_repacks"]
+    print("repacks during the consolidation", r1 - r0)
+    assert st == ss.CONS_INSTALLED
+    torch.cuda.synchronize()
+    ids = np.nonzero(init["group_of_state"] == g)[0]
+    for x, y in zip(ss.state_export(pa, ids), ss.state_export(pb, ids)):
+        if not x["dense"]:
+            for key in ("U", "V", "sigma"):
+                assert np.array_equal(x[key], y[key]), key
+    pa.close()
+    pb.close()
+
+
+def test_consolidate_async_queue_head_and_rejections():
+    w = W.get("gdn_delta", n_requests=1)
+    init = W.initial_state(w)
+    pool = _pool(w, init)
+    side = torch.cuda.Stream()
+    assert ss.consolidate_async(pool, side) == -1  # nothing compacted yet: no group waits
+    assert ss.consolidate_poll(pool) == ss.CONS_IDLE
+    gen = W.StepInputs(w, device="cuda")
+    o = torch.empty(w.n_states, w.d_v, device="cuda")
+    x = gen.generate(1)
+    ss.decode_step(pool, x["q"], x["k"], x["v"], x["alpha"], x["beta"], o)
+    ss.compact(pool, 3)
+    ss.compact(pool, 1)
+    assert ss.consolidate_async(pool, side) == 1   # compacted most recently first
+    assert ss.consolidate_poll(pool, wait=True) == ss.CONS_INSTALLED
+    assert ss.consolidate_async(pool, side) == 3
+    assert ss.consolidate_poll(pool, wait=True) == ss.CONS_INSTALLED
+    assert ss.consolidate_async(pool, side) == -1
+    pool.close()
+    kda = W.get("kda_delta", n_requests=1)
+    ki = W.initial_state(kda)
+    kp = ss.state_pool_create(kda.n_states, kda.d_k, kda.d_v, kda.K, kda.r, group_of_state=ki["group_of_state"],
+                              group_offset=ki["group_offset"], rule=ki["rule"], eps=ki["eps"], comp_off=ki["comp_off"],
+                              u=ki["u"], v=ki["v"], sigma=ki["sigma"], diag_decay=True)
+    with pytest.raises(RuntimeError):
+        ss.consolidate_async(kp, side, group=0)
+    kp.close()
