@@ -214,6 +214,15 @@ ss_status ss_readout(ss_pool *pool, const float *q, float *o, hipStream_t stream
  * check is conservative) leaves the pool in error (SS_ERR_CAPACITY). */
 ss_status ss_compact(ss_pool *pool, int32_t group, hipStream_t stream);
 
+/* Compaction of the listed states only (ids: host [n], each in [0, n_states), repeats allowed):
+ * the same Brand update, merge, truncation, re-split and promotion as ss_compact for each listed
+ * state, legal with any pad fill.  The other members of the groups the ids belong to are moved
+ * unchanged (components, pad and Gamma kept), because a compaction writes each touched group as
+ * one new ring segment.  It therefore costs a copy of the touched groups; the schedule of
+ * ss_compact is not affected.  Bad ids: SS_ERR_ARG before any device work.  It waits for
+ * `stream` before uploading the selection (not for use inside a captured graph). */
+ss_status ss_compact_ids(ss_pool *pool, const int32_t *ids, int64_t n, hipStream_t stream);
+
 /* Consolidation of the frozen part ([SS] 4.3 "Asynchronous CPU
  * Consolidation", Figure 7(a)), run on the device: for every factored state
  * of group `group` (of all groups when group < 0), the frozen components are

@@ -137,7 +137,9 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
       gamma = uniformf(m.gamma);
     }
   }
-  const bool work = live && n > 0;  // a Brand update; without a pad the components move unchanged
+  // an unselected member (compaction of listed states) keeps its pad and Gamma and only moves
+  const bool keep = live && a.sel != nullptr && a.sel[s] == 0;
+  const bool work = live && n > 0 && !keep;  // a Brand update; otherwise the components move unchanged
   const int mcol = ra + n;
   int kl = 0, kf = 0, total = 0, ra2 = ra, rf2 = rf, sweeps = 0;
   float uc[kMaxM][NS], vc[kMaxM][NS];
@@ -344,7 +346,7 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   const int64_t dst_a = (int64_t)(va % (unsigned long long)capA), dst_f = (int64_t)(vf % (unsigned long long)capF);
 
   // ---- phase B: write the new components and the record ------------------------------------
-  if (!work) {  // nothing buffered: the components move unchanged, sigma takes Gamma in
+  if (!work) {  // nothing buffered (or not selected): the components move unchanged
     copy_comps<F>(a.act, off_a, ra, dk, dv, lane, [&](int f, F *&du, F *&dvp) {
       const int64_t c = wrap(dst_a + f, capA);
       du = a.act.U<F>() + c * dk;
@@ -357,14 +359,17 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
       dvp = a.frz.V<F>() + c * dv;
       return true;
     });
-    for (int f = lane; f < ra; f += 64) a.act.s[wrap(dst_a + f, capA)] = a.act.s[wrap(off_a + f, capA)] * gamma;
-    for (int f = lane; f < rf; f += 64) a.frz.s[wrap(dst_f + f, capF)] = a.frz.s[wrap(off_f + f, capF)] * gamma;
+    // an empty pad means Gamma = 1 (no step since the last compaction) and sigma takes it in;
+    // an unselected member keeps Gamma with its pad
+    const float gs = keep ? 1.0f : gamma;
+    for (int f = lane; f < ra; f += 64) a.act.s[wrap(dst_a + f, capA)] = a.act.s[wrap(off_a + f, capA)] * gs;
+    for (int f = lane; f < rf; f += 64) a.frz.s[wrap(dst_f + f, capF)] = a.frz.s[wrap(off_f + f, capF)] * gs;
     if (lane == 0) {
       Meta nm;
       nm.off_a = (int32_t)dst_a;
       nm.off_f = (int32_t)dst_f;
-      nm.gamma = 1.0f;
-      nm.packed = meta_pack(ra, rf, 0, flags);
+      nm.gamma = keep ? gamma : 1.0f;
+      nm.packed = meta_pack(ra, rf, keep ? n : 0, flags);
       a.meta[s] = nm;
     }
     return;

@@ -444,6 +444,7 @@ __global__ __launch_bounds__(256) void k_dense_buf(DenseArgs a) {
     const int mi = blockIdx.x * 4 + wv;
     if (mi >= a.n_members) return;
     const int sm = uniform(a.members[mi]);
+    if (a.sel && a.sel[sm] == 0) return;  // compaction of listed states: this one is not listed
     const uint32_t mp = (uint32_t)uniform((int)a.meta[sm].packed);
     if (!(meta_flags(mp) & FLAG_DENSE)) return;
     slot = (uint32_t)uniform(a.meta[sm].off_a);

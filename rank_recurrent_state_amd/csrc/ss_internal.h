@@ -133,6 +133,7 @@ struct DenseArgs {
   unsigned long long *acct;
   int diag;                    // per-channel decay: alpha is [N][d_k]
   float *dgam;                 // buffered region with per-channel decay: [cap_d][d_k] per slot
+  const uint8_t *sel;          // fold mode: [N] states to fold, or nullptr: all members
 };
 
 struct CompactArgs {
@@ -150,6 +151,8 @@ struct CompactArgs {
   unsigned long long *acct_flops;
   unsigned long long *acct_states;
   float *gam;                  // per-channel decay pools: [N][d_k] (reset to 1 by a compaction); nullptr otherwise
+  const uint8_t *sel;          // [N] states to compact, or nullptr: all members.  An unselected member
+                               // of the group is moved to the new segment unchanged (pad, Gamma kept).
 };
 
 struct MaterializeArgs {

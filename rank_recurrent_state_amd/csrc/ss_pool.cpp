@@ -78,6 +78,7 @@ struct ss_pool {
   size_t lay_scan_bytes = 0;
   float *pk = nullptr, *pw = nullptr, *pc = nullptr;
   float *gam = nullptr, *dgam = nullptr;  // per-channel decay: accumulated decays per state [N][d_k], per dense slot
+  uint8_t *sel = nullptr;                 // [N] selection mask of ss_compact_ids (allocated at its first call)
   float *dense = nullptr;
   ss::DenseSlot *dslot = nullptr;
   float *dpk = nullptr, *dpw = nullptr, *dpc = nullptr;  // slot-indexed pads of the dense region
@@ -832,7 +833,8 @@ static hipError_t enqueue_decode(ss_pool *p, const float *q, const float *k, con
 // Enqueue the compaction of group g (the ring space must have been checked): fold the pads of its
 // dense members, compact its factored members into a new ring segment, promote.  with_dense:
 // whether dense members may exist.
-static hipError_t enqueue_compact_group(ss_pool *p, int g, bool with_dense, bool timing, hipStream_t stream) {
+static hipError_t enqueue_compact_group(ss_pool *p, int g, bool with_dense, bool timing, hipStream_t stream,
+                                        const uint8_t *sel = nullptr) {
   hipError_t e = ss::launch_ring_begin(p->ring, p->ring + 1, p->seg, p->seg + 2 * p->G, p->G, p->act.cap, p->frz.cap,
                                        p->counters, stream);
   if (e != hipSuccess) return e;
@@ -841,7 +843,7 @@ static hipError_t enqueue_compact_group(ss_pool *p, int g, bool with_dense, bool
     da.dk = p->dk; da.dv = p->dv; da.K = p->K; da.cap_d = (uint32_t)p->cap_d; da.meta = p->meta;
     da.dense = p->dense; da.dslot = p->dslot; da.pk = p->dpk; da.pw = p->dpw; da.pc = p->dpc;
     da.members = p->members + p->group_start[g]; da.n_members = (int32_t)p->group_size[g];
-    da.counters = p->counters; da.acct = p->acct; da.diag = p->diag; da.dgam = p->dgam;
+    da.counters = p->counters; da.acct = p->acct; da.diag = p->diag; da.dgam = p->dgam; da.sel = sel;
     auto fn = [&] { return ss::launch_dense_fold(da, stream); };
     e = timing ? timed(p, SS_KERNEL_DENSE_FOLD, stream, fn) : fn();
     if (e != hipSuccess) return e;
@@ -855,7 +857,7 @@ static hipError_t enqueue_compact_group(ss_pool *p, int g, bool with_dense, bool
   a.pk = p->pk; a.pw = p->pw; a.pc = p->pc; a.promote_list = p->promote_list; a.counters = p->counters;
   a.acct_flops = p->acct + ss::A_COMPACT_FLOPS * ss::kAcctSlots;
   a.acct_states = p->acct + ss::A_COMPACT_STATES * ss::kAcctSlots;
-  a.gam = p->gam;
+  a.gam = p->gam; a.sel = sel;
   auto fc = [&] { return ss::launch_compact(a, stream); };
   e = timing ? timed(p, SS_KERNEL_COMPACT, stream, fc) : fc();
   if (e == hipSuccess) e = ss::launch_ring_end(p->ring, p->ring + 1, p->seg, p->seg + 2 * p->G, g, stream);
@@ -944,6 +946,50 @@ ss_status ss_compact(ss_pool *p, int32_t group, hipStream_t stream) {
   refresh_fact_upper(p);
   if (any && p->promote && p->fact_upper > 0) {
     const hipError_t e = enqueue_prune(p, p->fact_upper, stream);
+    if (e != hipSuccess) return hip_fail(e, "factored-list launch");
+  }
+  p->compact_calls++;
+  return SS_OK;
+}
+
+ss_status ss_compact_ids(ss_pool *p, const int32_t *ids, int64_t n, hipStream_t stream) {
+  if (!p || n < 0 || (n > 0 && !ids)) return fail(SS_ERR_ARG, "bad arguments");
+  for (int64_t i = 0; i < n; ++i)
+    if (ids[i] < 0 || ids[i] >= p->N) return fail(SS_ERR_ARG, "state id out of range");
+  ss_status st = poll(p);
+  if (st != SS_OK) return st;
+  if (p->force_dense || n == 0) return SS_OK;
+  std::vector<uint8_t> mask(p->N, 0);
+  std::vector<char> touched(p->G, 0);
+  std::vector<int32_t> grp(p->N);
+  for (int g = 0; g < p->G; ++g)
+    for (int64_t i = 0; i < p->group_size[g]; ++i) grp[p->members_host[p->group_start[g] + i]] = g;
+  for (int64_t i = 0; i < n; ++i) {
+    mask[ids[i]] = 1;
+    touched[grp[ids[i]]] = 1;
+  }
+  hipError_t e = hipSuccess;
+  if (!p->sel) {
+    e = dalloc(p, &p->sel, (size_t)p->N);
+    if (e != hipSuccess) return e == hipErrorOutOfMemory ? fail(SS_ERR_OOM, "selection mask") : hip_fail(e, "selection mask");
+  }
+  e = hipStreamSynchronize(stream);  // the previous mask may still be read by enqueued work
+  if (e == hipSuccess) e = hipMemcpy(p->sel, mask.data(), (size_t)p->N, hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(e, "selection mask upload");
+  bool any = false;
+  for (int g = 0; g < p->G; ++g) {
+    if (!touched[g] || p->group_size[g] == 0) continue;
+    any = true;
+    int64_t ab[1][2];
+    st = ensure_ring_space(p, &g, 1, stream, ab);
+    if (st != SS_OK) return st;
+    e = enqueue_compact_group(p, g, p->dense_upper > 0, true, stream, p->sel);
+    if (e != hipSuccess) return hip_fail(e, "compact launch");
+    after_compact_group(p, g, ab[0]);
+  }
+  refresh_fact_upper(p);
+  if (any && p->promote && p->fact_upper > 0) {
+    e = enqueue_prune(p, p->fact_upper, stream);
     if (e != hipSuccess) return hip_fail(e, "factored-list launch");
   }
   p->compact_calls++;

@@ -85,6 +85,7 @@ def load_library():
     lib.ss_decode_step.argtypes = [vp] + [vp] * 6 + [vp]
     lib.ss_readout.argtypes = [vp, vp, vp, vp]
     lib.ss_compact.argtypes = [vp, ctypes.c_int32, vp]
+    lib.ss_compact_ids.argtypes = [vp, _c_i32p, ctypes.c_int64, vp]
     lib.ss_consolidate.argtypes = [vp, ctypes.c_int32, vp]
     lib.ss_consolidate_next.argtypes = [vp, ctypes.c_int32, _c_i32p, _c_i32p, vp]
     lib.ss_consolidate_async.argtypes = [vp, ctypes.c_int32, vp, vp, _c_i32p]
@@ -352,6 +353,12 @@ def consolidate_poll(pool: StatePool, wait: bool = False, stream=None) -> int:
     st = ctypes.c_int32()
     _check(load_library().ss_consolidate_poll(pool.handle, int(bool(wait)), _stream(stream), ctypes.byref(st)))
     return int(st.value)
+
+
+def compact_ids(pool: StatePool, ids, stream=None):
+    """Compact the listed states only (the rest of their groups moves unchanged)."""
+    a = np.ascontiguousarray(ids, dtype=np.int32)
+    _check(load_library().ss_compact_ids(pool.handle, a.ctypes.data_as(_c_i32p), int(a.shape[0]), _stream(stream)))
 
 
 def schedule_due(pool: StatePool, step: int) -> list:

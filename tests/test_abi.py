@@ -106,6 +106,7 @@ def test_calls_on_null_pool_are_rejected(lib):
     assert lib.ss_step_graph_launch(None, 0, None) == ss.SS_ERR_ARG
     assert lib.ss_step_graph_destroy(None) == ss.SS_OK
     assert lib.ss_consolidate(None, 0, None) == ss.SS_ERR_ARG
+    assert lib.ss_compact_ids(None, None, 0, None) == ss.SS_ERR_ARG
     g = ctypes.c_int32()
     assert lib.ss_consolidate_async(None, 0, None, None, ctypes.byref(g)) == ss.SS_ERR_ARG
     assert lib.ss_consolidate_poll(None, 0, None, ctypes.byref(g)) == ss.SS_ERR_ARG

@@ -25,7 +25,7 @@ def _pool_from_init(w, init, **kw):
                                 comp_off=init["comp_off"], u=init["u"], v=init["v"], sigma=init["sigma"], **kw)
 
 
-def _lockstep(w, init, pool, ids, steps, promote=True, check_readout=False, fp16=False, L=-1):
+def _lockstep(w, init, pool, ids, steps, promote=True, check_readout=False, fp16=False, L=-1, t0=0):
     """Run `steps` decode(+compaction) steps in lock-step on the states `ids`.  fp16: the pool
     stores fp16 factors; the oracle rounds the factors it writes the same way, and every exported
     factor must be exactly representable in fp16."""
@@ -35,7 +35,7 @@ def _lockstep(w, init, pool, ids, steps, promote=True, check_readout=False, fp16
     o = torch.empty(w.n_states, w.d_v, device="cuda")
     worst = {"o": 0.0, "S": 0.0, "S_c": 0.0, "sigma": 0.0, "proj": 0.0, "ro": 0.0}
     guard = 0
-    for t in range(1, steps + 1):
+    for t in range(t0 + 1, t0 + steps + 1):
         x = gen.generate(t)
         before = ss.state_export(pool, ids)
         if fp16:
@@ -511,3 +511,45 @@ def test_fp16_decode_bytes_accounting():
         for g in ss.schedule_due(pool, t):
             ss.compact(pool, g)
     pool.close()
+
+
+@pytest.mark.parametrize("name", ["gdn_delta", "mixed_dense"])
+def test_compact_ids_lockstep(name):
+    """ss_compact_ids on a ragged subset across groups (dense states included for mixed_dense), with
+    pads partly filled: the listed states match the oracle's compaction of the same states; every
+    other state is exported bit for bit as before; decoding and the schedule then continue in
+    lock-step with the oracle."""
+    w = W.get(name, n_requests=1)
+    init = W.initial_state(w)
+    pool = _pool_from_init(w, init)
+    gen = W.StepInputs(w, device="cuda")
+    o = torch.empty(w.n_states, w.d_v, device="cuda")
+    for t in range(1, 12):
+        x = gen.generate(t)
+        ss.decode_step(pool, x["q"], x["k"], x["v"], x["alpha"], x["beta"], o)
+        for g in ss.schedule_due(pool, t):
+            ss.compact(pool, g)
+    rng = np.random.default_rng(3)
+    sel = np.unique(rng.choice(w.n_states, size=w.n_states // 7, replace=False))
+    ids = np.arange(w.n_states)
+    before = ss.state_export(pool, ids)
+    ss.compact_ids(pool, sel)
+    torch.cuda.synchronize()
+    after = ss.state_export(pool, ids)
+    mask = np.zeros(w.n_states, bool)
+    mask[sel] = True
+    for j in np.nonzero(~mask)[0]:
+        b, a = before[j], after[j]
+        assert b["dense"] == a["dense"]
+        for key in (("S",) if b["dense"] else ("U", "V", "sigma", "c", "K", "W")):
+            assert np.array_equal(a[key], b[key]), (j, key)
+    eps = init["eps"][sel]
+    P = oracle_from_export([before[j] for j in sel], eps, w.d_k, w.d_v, w.K, w.r)
+    P.compact()
+    ws, wsig, gd, bad = compare_compacted([after[j] for j in sel], P, eps)
+    assert not bad and ws <= TOL and wsig <= TOL, (ws, wsig, bad[:5])
+    assert any(len(before[j].get("c", [])) for j in sel if not before[j]["dense"])  # pads were non-empty
+    worst, guard = _lockstep(w, init, pool, np.unique(np.concatenate([sel[::5], [0]])), 10, t0=11)
+    pool.close()
+    print(name, "compact_ids", ws, wsig, "then", worst)
+    _assert_worst(worst)
