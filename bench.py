@@ -229,6 +229,8 @@ def main():
     ap.add_argument("--consolidate-period", type=int, default=1, help="steps between consolidation calls")
     ap.add_argument("--consolidate-async", action="store_true",
                     help="consolidate on a second stream, one group at a time from the wait queue, beside the decode")
+    ap.add_argument("--stagger", default=None, choices=["none", "even4", "paper8", "state8"],
+                    help="override the workload's compaction stagger (the per-step latency comparison)")
     ap.add_argument("--factor-fp16", action="store_true",
                     help="store the factor vectors in fp16 (pad, sigma, dense region and arithmetic stay fp32)")
     ap.add_argument("--no-graph", action="store_true",
@@ -250,6 +252,9 @@ def main():
 
     torch.cuda.set_device(0)
     w = W.get(args.workload, n_requests=args.requests)
+    if args.stagger is not None:
+        import dataclasses
+        w = dataclasses.replace(w, stagger=args.stagger)
     K_steps = args.steps if args.steps is not None else w.steps
     log = lambda *a: print(*a, file=sys.stderr, flush=True)  # noqa: E731
     log(f"[bench] workload {w.name}: {w.n_states} states {w.d_k}x{w.d_v}, {K_steps} timed steps")
