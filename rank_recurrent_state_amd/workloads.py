@@ -29,7 +29,7 @@ BASE_SEED = 20261202
 @dataclass(frozen=True)
 class Workload:
     name: str
-    config_id: int
+    seed_id: int
     n_requests: int
     n_layers: int
     n_heads: int
@@ -65,7 +65,7 @@ class Workload:
         return replace(self, n_requests=int(n_requests))
 
 
-# The five workloads.  Readings of unstated details are listed in the design doc.
+# The workloads.  Where the pages leave a detail open, the comment on each states the reading taken.
 WORKLOADS = {
     # 64 fp32 states, d_k=16, d_v=32, one shared 4-dim subspace, sigma_noise 0.05,
     # unit keys, empty start, eps 1e-3, compaction whenever the pad fills.
@@ -171,7 +171,7 @@ def _orthonormal(gen, batch, d, m):
 
 def head_bases(w: Workload, seed: int = BASE_SEED):
     """Per-head key-side and value-side subspace bases, float64 on the host."""
-    gen = _gen(seed * 7919 + w.config_id)
+    gen = _gen(seed * 7919 + w.seed_id)
     if w.inputs == "shared4":
         Pk = _orthonormal(gen, 1, w.d_k, 4).expand(w.heads_per_request, -1, -1).contiguous()
         Pv = _orthonormal(gen, 1, w.d_v, 4).expand(w.heads_per_request, -1, -1).contiguous()
@@ -196,7 +196,7 @@ def initial_state(w: Workload, seed: int = BASE_SEED):
     [N]), group_offset (int32 [G]).  Components of a state are sorted by sigma.
     """
     N, dk, dv = w.n_states, w.d_k, w.d_v
-    gen = _gen(seed * 104729 + w.config_id)
+    gen = _gen(seed * 104729 + w.seed_id)
     grp, offs = groups(w)
     base = {"rule": rules(w), "eps": eps_of(w), "group_of_state": grp, "group_offset": offs}
     if w.init == "empty":
@@ -314,7 +314,7 @@ class StepInputs:
         w = self.w
         idx = None if states is None else torch.as_tensor(states, dtype=torch.int64, device=self.device)
         n = w.n_states if idx is None else int(idx.shape[0])
-        gen = _gen(self.seed * 1_000_003 + w.config_id * 65_537 + int(step), self.device)
+        gen = _gen(self.seed * 1_000_003 + w.seed_id * 65_537 + int(step), self.device)
         dev, f32 = self.device, torch.float32
         dk, dv = w.d_k, w.d_v
         ashape = (n, dk) if w.diag_decay else (n,)  # per-channel decay: one alpha per key channel

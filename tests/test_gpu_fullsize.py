@@ -36,7 +36,7 @@ def _fullsize(name, steps, n_sample, requests=None):
     pool = ss.state_pool_create(w.n_states, w.d_k, w.d_v, w.K, w.r, group_of_state=init["group_of_state"],
                                 group_offset=init["group_offset"], rule=init["rule"], eps=init["eps"],
                                 comp_off=init["comp_off"], u=init["u"], v=init["v"], sigma=init["sigma"])
-    ids = _sample(w, init, n_sample, seed=w.config_id)
+    ids = _sample(w, init, n_sample, seed=w.seed_id)
     idx = torch.as_tensor(ids, device="cuda")
     eps = init["eps"][ids]
     grp = init["group_of_state"][ids]
