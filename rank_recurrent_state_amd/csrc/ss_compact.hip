@@ -493,32 +493,51 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   }
 }
 
-// Materialize a dense state into a new slot of the dense region, stored as
-// H = S^T row-major [d_v][d_k]: H[j][i] = sum_c sigma_c v_c[j] u_c[i]
-// (256 threads per state; thread t owns float4 column t % (d_k/4) of rows
-// t / (d_k/4) + RG * jj; components are staged through LDS in chunks of CH,
-// rows are covered in chunks of kMatRows per thread).
+// Materialize dense states into new slots of the dense region, stored as
+// H = S^T row-major [d_v][d_k]: H[j][i] = sum_c sigma_c v_c[j] u_c[i].  Three launches:
+//   k_mat_reserve  one thread: the states of the list take consecutive slots from the
+//                  dense count (base + list index);
+//   k_mat_rows     one workgroup per (state, block of RPB rows), so a few promotions still
+//                  spread over many CUs: thread t owns float4 column t % (d_k/4) of rows
+//                  t / (d_k/4) + RG * jj (jj < kMatRows); components are staged through
+//                  LDS in chunks of kMatCH (u whole, v only the block's rows);
+//   k_mat_finish   one thread per state: the dense record, the slot record, the slot's
+//                  per-channel decays (set to 1), counters.
+// The state's record is rewritten only by the last launch, after every row block has read
+// where its components are.
 constexpr int kMatCH = 16;
-constexpr int kMatRows = 8;
+constexpr int kMatRows = 2;
+
+__device__ __forceinline__ uint32_t mat_count(const MaterializeArgs &a) {
+  return a.count ? *a.count : (uint32_t)a.fixed_count;
+}
+
+__global__ void k_mat_reserve(MaterializeArgs a) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  const uint32_t base = a.counters[C_DENSE_COUNT];
+  a.counters[C_MAT_BASE] = base;
+  a.counters[C_DENSE_COUNT] = base + mat_count(a);  // may pass cap_d: readers clamp, k_mat_finish reports it
+}
 
 template <typename F>
-__global__ __launch_bounds__(256) void k_materialize(MaterializeArgs a) {
+__global__ __launch_bounds__(256) void k_mat_rows(MaterializeArgs a, int RB) {
   extern __shared__ float smem[];
-  __shared__ int s_slot;
   const int t = threadIdx.x;
   const int dk = a.dk, dv = a.dv;
-  const int C4 = dk >> 2, RG = 256 / C4;
+  const int C4 = dk >> 2, RG = 256 / C4, RPB = RG * kMatRows;
   const int c = t % C4, g = t / C4;
   const bool act = t < RG * C4;
-  float *su = smem;                 // [CH][dk]
-  float *sv = smem + kMatCH * dk;   // [CH][dv]
-  float *ss = sv + kMatCH * dv;     // [CH]
-  const uint32_t cnt = a.count ? *a.count : (uint32_t)a.fixed_count;
-  for (uint32_t li = blockIdx.x; li < cnt; li += gridDim.x) {
+  float *su = smem;                  // [CH][dk]
+  float *sv = smem + kMatCH * dk;    // [CH][RPB]
+  float *ss = sv + kMatCH * RPB;     // [CH]
+  const uint32_t cnt = mat_count(a);
+  const uint32_t base = a.counters[C_MAT_BASE];
+  for (int64_t idx = blockIdx.x; idx < (int64_t)cnt * RB; idx += gridDim.x) {  // uniform over the block
+    const int li = (int)(idx / RB), rb = (int)(idx - (int64_t)li * RB);
+    const int64_t slot = (int64_t)base + li;
+    if (slot >= a.cap_d) continue;  // k_mat_finish reports it
     const int s = a.list[li];
     const Meta m = a.meta[s];
-    const uint32_t flags = meta_flags(m.packed) & FLAG_DELTA;
-    // component comp: the CSR row (initial states) or the ring slot of the active / frozen part
     int n1, n2;
     int64_t o0 = 0;
     float scale = 1.0f;
@@ -531,7 +550,7 @@ __global__ __launch_bounds__(256) void k_materialize(MaterializeArgs a) {
       n2 = (int)meta_rf(m.packed);
       scale = m.gamma;
     }
-    // element i of u (or v) of component comp
+    // element i of u (or v) of component comp: the CSR row (initial states) or the ring slot
     auto comp_u = [&](int comp, int i) -> float {
       if (a.csr_off) return a.csr_u[(o0 + comp) * dk + i];
       return ldf(comp < n1 ? a.act.U<F>() + wrap(m.off_a + comp, a.act.cap) * dk + i
@@ -546,91 +565,83 @@ __global__ __launch_bounds__(256) void k_materialize(MaterializeArgs a) {
       if (a.csr_off) return a.csr_s[o0 + comp];
       return comp < n1 ? a.act.s[wrap(m.off_a + comp, a.act.cap)] : a.frz.s[wrap(m.off_f + comp - n1, a.frz.cap)];
     };
-    __syncthreads();
-    if (t == 0) {
-      const uint32_t slot =
-          __hip_atomic_fetch_add(&a.counters[C_DENSE_COUNT], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (slot < (uint32_t)a.cap_d) {
-        s_slot = (int)slot;
-      } else {
-        s_slot = -1;
-        __hip_atomic_fetch_add(&a.counters[C_ERR_DENSE_CAP], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        *a.hflag = 1u;
-      }
-    }
-    __syncthreads();
-    const int slot = s_slot;
-    if (slot < 0) continue;
-    if (a.dgam)  // per-channel decay: the new slot starts with no decay accumulated
-      for (int e = t; e < dk; e += 256) a.dgam[(int64_t)slot * dk + e] = 1.f;
     const int total = n1 + n2;
-    float *H = a.dense + (int64_t)slot * dk * dv;
+    const int j0 = rb * RPB, j1 = j0 + RPB < dv ? j0 + RPB : dv;
+    float *H = a.dense + slot * dk * dv;
     const int64_t di = a.dsrc_idx ? a.dsrc_idx[s] : -1;
-    if (di >= 0) {  // given dense: H = S^T
+    if (di >= 0) {  // given dense: rows j0..j1 of H = S^T
       const float *S = a.dsrc + di * dk * dv;
       if (act)
-        for (int j = g; j < dv; j += RG) {
+        for (int j = j0 + g; j < j1; j += RG) {
           const float *col = S + (int64_t)(4 * c) * dv + j;
           st4(H + (int64_t)j * dk + 4 * c, make_float4(col[0], col[dv], col[2 * dv], col[3 * dv]));
         }
+      continue;
     }
-    for (int r0 = 0; r0 < (di >= 0 ? 0 : dv); r0 += RG * kMatRows) {
-      float4 acc[kMatRows];
+    float4 acc[kMatRows];
 #pragma unroll
-      for (int jj = 0; jj < kMatRows; ++jj) acc[jj] = zero4();
-      for (int c0 = 0; c0 < total; c0 += kMatCH) {
-        __syncthreads();
-        for (int e = t; e < kMatCH * dk; e += 256) {
-          const int cc = e / dk, i = e - cc * dk, comp = c0 + cc;
-          su[e] = comp < total ? comp_u(comp, i) : 0.f;
-        }
-        for (int e = t; e < kMatCH * dv; e += 256) {
-          const int cc = e / dv, j = e - cc * dv, comp = c0 + cc;
-          sv[e] = comp < total ? comp_v(comp, j) : 0.f;
-        }
-        if (t < kMatCH) {
-          const int comp = c0 + t;
-          ss[t] = comp < total ? scale * comp_s(comp) : 0.f;
-        }
-        __syncthreads();
-        if (act) {
-          const int lim = (total - c0) < kMatCH ? (total - c0) : kMatCH;
-          for (int cc = 0; cc < lim; ++cc) {
-            const float4 u4 = *reinterpret_cast<const float4 *>(su + cc * dk + 4 * c);
-            const float sc = ss[cc];
-#pragma unroll
-            for (int jj = 0; jj < kMatRows; ++jj) {
-              const int j = r0 + g + RG * jj;
-              if (j < dv) acc[jj] = fma4(sc * sv[cc * dv + j], u4, acc[jj]);
-            }
-          }
-        }
+    for (int jj = 0; jj < kMatRows; ++jj) acc[jj] = zero4();
+    for (int c0 = 0; c0 < total; c0 += kMatCH) {
+      __syncthreads();
+      for (int e = t; e < kMatCH * dk; e += 256) {
+        const int cc = e / dk, i = e - cc * dk, comp = c0 + cc;
+        su[e] = comp < total ? comp_u(comp, i) : 0.f;
       }
+      for (int e = t; e < kMatCH * RPB; e += 256) {
+        const int cc = e / RPB, jr = e - cc * RPB, comp = c0 + cc, j = j0 + jr;
+        sv[e] = (comp < total && j < j1) ? comp_v(comp, j) : 0.f;
+      }
+      if (t < kMatCH) {
+        const int comp = c0 + t;
+        ss[t] = comp < total ? scale * comp_s(comp) : 0.f;
+      }
+      __syncthreads();
       if (act) {
+        const int lim = (total - c0) < kMatCH ? (total - c0) : kMatCH;
+        for (int cc = 0; cc < lim; ++cc) {
+          const float4 u4 = *reinterpret_cast<const float4 *>(su + cc * dk + 4 * c);
+          const float sc = ss[cc];
 #pragma unroll
-        for (int jj = 0; jj < kMatRows; ++jj) {
-          const int j = r0 + g + RG * jj;
-          if (j < dv) st4(H + (int64_t)j * dk + 4 * c, acc[jj]);
+          for (int jj = 0; jj < kMatRows; ++jj) acc[jj] = fma4(sc * sv[cc * RPB + g + RG * jj], u4, acc[jj]);
         }
       }
     }
-    if (t == 0) {
-      Meta nm;
-      nm.off_a = slot;
-      nm.off_f = 0;
-      nm.gamma = 1.0f;
-      nm.packed = meta_pack(0, 0, 0, flags | FLAG_DENSE);
-      a.meta[s] = nm;
-      DenseSlot ds;
-      ds.s = s;
-      ds.packed = meta_pack(0, 0, 0, flags | FLAG_DENSE);  // empty pad
-      ds.gamma = 1.0f;
-      ds.spare = 0u;
-      a.dslot[slot] = ds;
-      if (!a.csr_off)
-        __hip_atomic_fetch_add(&a.counters[C_PROMOTIONS], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (act) {
+#pragma unroll
+      for (int jj = 0; jj < kMatRows; ++jj) {
+        const int j = j0 + g + RG * jj;
+        if (j < j1) st4(H + (int64_t)j * dk + 4 * c, acc[jj]);
+      }
     }
   }
+}
+
+__global__ __launch_bounds__(256) void k_mat_finish(MaterializeArgs a) {
+  const uint32_t li = blockIdx.x * 256u + threadIdx.x;
+  if (li >= mat_count(a)) return;
+  const int64_t slot = (int64_t)a.counters[C_MAT_BASE] + li;
+  const int s = a.list[li];
+  if (slot >= a.cap_d) {
+    __hip_atomic_fetch_add(&a.counters[C_ERR_DENSE_CAP], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *a.hflag = 1u;
+    return;
+  }
+  const uint32_t flags = meta_flags(a.meta[s].packed) & FLAG_DELTA;
+  Meta nm;
+  nm.off_a = (int32_t)slot;
+  nm.off_f = 0;
+  nm.gamma = 1.0f;
+  nm.packed = meta_pack(0, 0, 0, flags | FLAG_DENSE);
+  a.meta[s] = nm;
+  DenseSlot ds;
+  ds.s = s;
+  ds.packed = meta_pack(0, 0, 0, flags | FLAG_DENSE);  // empty pad
+  ds.gamma = 1.0f;
+  ds.spare = 0u;
+  a.dslot[slot] = ds;
+  if (a.dgam)  // per-channel decay: the new slot starts with no decay accumulated
+    for (int e = 0; e < a.dk; ++e) a.dgam[slot * a.dk + e] = 1.f;
+  if (!a.csr_off) __hip_atomic_fetch_add(&a.counters[C_PROMOTIONS], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Pool creation: place the CSR components of every state into its slice of
@@ -859,10 +870,14 @@ hipError_t launch_compact(const CompactArgs &a, hipStream_t st) {
 
 hipError_t launch_materialize(const MaterializeArgs &a, int64_t grid_upper, hipStream_t st) {
   if (grid_upper <= 0) return hipSuccess;
-  const unsigned grid = (unsigned)(grid_upper < 2048 ? grid_upper : 2048);
-  const size_t sh = sizeof(float) * (size_t)kMatCH * (a.dk + a.dv + 1);
-  if (a.act.half) hipLaunchKernelGGL(k_materialize<_Float16>, dim3(grid), dim3(256), sh, st, a);
-  else hipLaunchKernelGGL(k_materialize<float>, dim3(grid), dim3(256), sh, st, a);
+  const int C4 = a.dk >> 2, RPB = (256 / C4) * kMatRows, RB = (a.dv + RPB - 1) / RPB;
+  const int64_t want = grid_upper * RB;
+  const unsigned grid = (unsigned)(want < 4096 ? want : 4096);
+  const size_t sh = sizeof(float) * ((size_t)kMatCH * (a.dk + RPB) + kMatCH);
+  hipLaunchKernelGGL(k_mat_reserve, dim3(1), dim3(64), 0, st, a);
+  if (a.act.half) hipLaunchKernelGGL(k_mat_rows<_Float16>, dim3(grid), dim3(256), sh, st, a, RB);
+  else hipLaunchKernelGGL(k_mat_rows<float>, dim3(grid), dim3(256), sh, st, a, RB);
+  hipLaunchKernelGGL(k_mat_finish, dim3((unsigned)((grid_upper + 255) / 256)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

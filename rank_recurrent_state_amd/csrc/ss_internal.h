@@ -63,7 +63,8 @@ enum Counter : int {
   C_PROMOTIONS = 5,    // total promotions
   C_FACT0 = 6,         // length of the factored-state list
   C_FACT1 = 7,         // length of its scratch copy while it is pruned
-  C_N = 8
+  C_MAT_BASE = 8,      // first dense slot of the states a materialization places
+  C_N = 9
 };
 
 // 16-byte record of a dense slot.  packed: n << 16 | flags << 24, as Meta.
