@@ -30,12 +30,13 @@ def _sample(w, init, n, seed):
     return np.unique(np.array(ids, dtype=np.int64))
 
 
-def _fullsize(name, steps, n_sample, requests=None):
+def _fullsize(name, steps, n_sample, requests=None, fp16=False):
     w = W.get(name, n_requests=requests)
     init = W.initial_state(w)
     pool = ss.state_pool_create(w.n_states, w.d_k, w.d_v, w.K, w.r, group_of_state=init["group_of_state"],
                                 group_offset=init["group_offset"], rule=init["rule"], eps=init["eps"],
-                                comp_off=init["comp_off"], u=init["u"], v=init["v"], sigma=init["sigma"])
+                                comp_off=init["comp_off"], u=init["u"], v=init["v"], sigma=init["sigma"],
+                                diag_decay=w.diag_decay, factor_fp16=fp16)
     ids = _sample(w, init, n_sample, seed=w.seed_id)
     idx = torch.as_tensor(ids, device="cuda")
     eps = init["eps"][ids]
@@ -47,7 +48,7 @@ def _fullsize(name, steps, n_sample, requests=None):
     for t in range(1, steps + 1):
         x = gen.generate(t)
         before = ss.state_export(pool, ids)
-        P = oracle_from_export(before, eps, w.d_k, w.d_v, w.K, w.r)
+        P = oracle_from_export(before, eps, w.d_k, w.d_v, w.K, w.r, factor_fp16=fp16, diag_decay=w.diag_decay)
         sub = {k: v[idx].cpu().numpy().astype(np.float64) for k, v in x.items()}
         ss.decode_step(pool, x["q"], x["k"], x["v"], x["alpha"], x["beta"], o)
         due = ss.schedule_due(pool, t)
@@ -62,7 +63,7 @@ def _fullsize(name, steps, n_sample, requests=None):
         if due:
             sel = np.nonzero(np.isin(grp, due))[0]
             P.compact(sel)
-            ws, wsig, gd, bad = compare_compacted(after, P, eps)
+            ws, wsig, gd, bad = compare_compacted(after, P, eps, fp16=fp16)
             assert not bad, f"{name} step {t}: rank/dense mismatches outside the guard band: {bad[:5]}"
             guard += gd
             worst["S_c"] = max(worst["S_c"], ws)
@@ -99,3 +100,13 @@ def test_fullsize_mixed_dense():
 def test_fullsize_mamba2_1m():
     """1,032,192 Mamba-2 states (512 requests), 4 steps with the compaction of the first due group."""
     _fullsize("mamba2_1m", steps=4, n_sample=128)
+
+
+def test_fullsize_kda_delta():
+    """40,960 Kimi Delta Attention states 128x128 (per-channel decay), 10 steps."""
+    _fullsize("kda_delta", steps=10, n_sample=256)
+
+
+def test_fullsize_gdn_delta_fp16():
+    """98,304 Gated-DeltaNet states with fp16 factors, 10 steps."""
+    _fullsize("gdn_delta", steps=10, n_sample=256, fp16=True)
