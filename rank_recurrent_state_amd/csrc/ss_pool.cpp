@@ -36,6 +36,7 @@ ss_status fail(ss_status st, const std::string &msg) {
 
 // host-mapped words: error flags raised by kernels, and the length of the factored-state list
 enum HostFlag { HF_PAD = 0, HF_DENSE_CAP = 1, HF_FACT = 2, HF_RING = 3, HF_N = 4 };
+constexpr int64_t kPruneEvery = 8;
 
 }  // namespace
 
@@ -93,6 +94,10 @@ struct ss_pool {
   std::vector<void *> dev_allocs;
   int64_t reserved = 0;
   int64_t decode_calls = 0, compact_calls = 0, readout_calls = 0;
+  // The factored-state list may hold states that have gone dense (the decode skips them), so the
+  // eager path prunes it on every kPruneEvery-th compaction call only; the list then shrinks a
+  // little later, for two launches fewer on the other calls.
+  int64_t prune_due = 0;
   // consolidation queue: groups compacted since their last consolidation, and when each group
   // was last consolidated (-1: never)
   std::vector<char> cons_wait;
@@ -944,7 +949,7 @@ ss_status ss_compact(ss_pool *p, int32_t group, hipStream_t stream) {
     after_compact_group(p, g, ab[0]);
   }
   refresh_fact_upper(p);
-  if (any && p->promote && p->fact_upper > 0) {
+  if (any && p->promote && p->fact_upper > 0 && p->prune_due++ % kPruneEvery == 0) {
     const hipError_t e = enqueue_prune(p, p->fact_upper, stream);
     if (e != hipSuccess) return hip_fail(e, "factored-list launch");
   }
@@ -988,7 +993,7 @@ ss_status ss_compact_ids(ss_pool *p, const int32_t *ids, int64_t n, hipStream_t 
     after_compact_group(p, g, ab[0]);
   }
   refresh_fact_upper(p);
-  if (any && p->promote && p->fact_upper > 0) {
+  if (any && p->promote && p->fact_upper > 0 && p->prune_due++ % kPruneEvery == 0) {
     e = enqueue_prune(p, p->fact_upper, stream);
     if (e != hipSuccess) return hip_fail(e, "factored-list launch");
   }
