@@ -96,3 +96,55 @@ def test_fp16_initial_factors_are_rounded_and_fp32_pools_are_not():
     P32.set_state(0, st)
     assert np.array_equal(P16.get_state(0).U, np.float16(U).astype(np.float64))
     assert np.array_equal(P32.get_state(0).U, U)
+
+
+def test_fp16_with_channel_decay_rounds_at_compaction_only():
+    """Per-channel decay with fp16 factors: between compactions the stored u carry the decays
+    applied since the last one (not fp16 values); right after a compaction every factor is an
+    fp16 value again, and the run stays within the rounding bound of the fp32 run."""
+    N, d_k, d_v, K, r = 5, 16, 12, 4, 3
+    P32 = OraclePool(N, d_k, d_v, K=K, r=r, promote=False, diag_decay=True)
+    P16 = OraclePool(N, d_k, d_v, K=K, r=r, promote=False, factor_fp16=True, diag_decay=True)
+    for P in (P32, P16):
+        for s in range(N):
+            P.set_state(s, OracleState(rule=1, eps=1e-3))
+    rng = np.random.default_rng(11)
+    mid_rounded = True
+    for t in range(1, 25):
+        q = rng.standard_normal((N, d_k))
+        k = rng.standard_normal((N, d_k))
+        k /= np.linalg.norm(k, axis=1, keepdims=True)
+        v = rng.standard_normal((N, d_v))
+        lam = rng.uniform(0.7, 1.0, (N, d_k))
+        b = 1 / (1 + np.exp(-rng.standard_normal(N)))
+        for P in (P32, P16):
+            P.decode(q, k, v, lam, b)
+        if t % K == 0:
+            for P in (P32, P16):
+                P.compact()
+            for s in range(N):
+                st = P16.get_state(s)
+                for A in (st.U, st.V):
+                    assert all(x == round_fp16(x) for x in A.ravel())
+        elif t > K:
+            st = P16.get_state(0)
+            mid_rounded = mid_rounded and all(x == round_fp16(x) for x in st.U.ravel())
+    assert not mid_rounded  # decayed u are not fp16 values until the next compaction
+    worst = 0.0
+    for s in range(N):
+        S32, S16 = P32.reconstruct(s), P16.reconstruct(s)
+        worst = max(worst, np.linalg.norm(S16 - S32) / (2.0 ** -10 * P32.get_state(s).sigma.sum()))
+    assert 0.0 < worst <= 8.0, worst
+
+
+def test_mid_run_load_keeps_values_as_given():
+    """A mid-run state (as_init=False) is loaded as given; only initial factors are rounded."""
+    rng = np.random.default_rng(12)
+    U = rng.standard_normal((2, 8)) * np.array([[0.3], [0.7]])
+    V = rng.standard_normal((2, 6))
+    st = OracleState(U, V, np.array([2.0, 1.0]), rule=0, eps=0.0)
+    P = OraclePool(1, 8, 6, K=4, r=2, promote=False, factor_fp16=True)
+    P.set_state(0, st, as_init=False)
+    assert np.array_equal(P.get_state(0).U, U)
+    P.set_state(0, st)
+    assert np.array_equal(P.get_state(0).U, np.float16(U).astype(np.float64))
