@@ -35,15 +35,17 @@ def _same_states(a, b, t):
             assert np.array_equal(x[key], y[key]), f"step {t} state {x['id']} field {key}"
 
 
-def _twin_run(name, steps, requests=1, arena=0, eager_extra=False, oracle_steps=()):
+def _twin_run(name, steps, requests=1, arena=0, eager_extra=False, oracle_steps=(), fp16=False):
     w = W.get(name, n_requests=requests if name != "tiny" else None)
     init = W.initial_state(w)
-    A = _pool(w, init, arena_components=arena)
-    B = _pool(w, init, arena_components=arena)
+    diag = w.diag_decay
+    A = _pool(w, init, arena_components=arena, factor_fp16=fp16, diag_decay=diag)
+    B = _pool(w, init, arena_components=arena, factor_fp16=fp16, diag_decay=diag)
     N, dk, dv = w.n_states, w.d_k, w.d_v
     delta = bool(np.any(init["rule"] == 1))
     buf = {"q": torch.zeros(N, dk, device="cuda"), "k": torch.zeros(N, dk, device="cuda"),
-           "v": torch.zeros(N, dv, device="cuda"), "alpha": torch.zeros(N, device="cuda"),
+           "v": torch.zeros(N, dv, device="cuda"),
+           "alpha": torch.zeros((N, dk) if diag else (N,), device="cuda"),
            "beta": torch.zeros(N, device="cuda") if delta else None}
     oA = torch.empty(N, dv, device="cuda")
     oB = torch.empty(N, dv, device="cuda")
@@ -61,7 +63,7 @@ def _twin_run(name, steps, requests=1, arena=0, eager_extra=False, oracle_steps=
         check = t in oracle_steps
         if check:
             before = ss.state_export(B, ids)
-            P = oracle_from_export(before, eps, dk, dv, w.K, w.r)
+            P = oracle_from_export(before, eps, dk, dv, w.K, w.r, factor_fp16=fp16, diag_decay=diag)
             sub = {k: v.cpu().numpy()[ids].astype(np.float64) for k, v in x.items()}
         graph.launch(t)
         ss.decode_step(A, x["q"], x["k"], x["v"], x["alpha"], x["beta"] if delta else None, oA)
@@ -77,7 +79,7 @@ def _twin_run(name, steps, requests=1, arena=0, eager_extra=False, oracle_steps=
             worst["o"] = max(worst["o"], float(e.max()))
             if due:
                 P.compact(np.nonzero(np.isin(grp, due))[0])
-                ws, wsig, gd, bad = compare_compacted(ss.state_export(B, ids), P, eps)
+                ws, wsig, gd, bad = compare_compacted(ss.state_export(B, ids), P, eps, fp16=fp16)
                 assert not bad, f"step {t}: rank/dense mismatches outside the guard band: {bad[:5]}"
                 worst["S_c"] = max(worst["S_c"], ws)
                 worst["sigma"] = max(worst["sigma"], wsig)
@@ -122,6 +124,19 @@ def test_graph_gdn_delta_with_eager_work_between_replays():
     """1,536 delta-rule states 128x128, with eager readouts and out-of-schedule compactions
     between the replays."""
     _twin_run("gdn_delta", 20, eager_extra=True, oracle_steps={3, 8})
+
+
+def test_graph_kda_per_channel_decay():
+    """640 Kimi-Delta-Attention states 128x128 with per-channel decay: the decay accumulated in the
+    pads (gamma) and its reset at compaction are captured like every other kernel argument."""
+    _twin_run("kda_delta", 20, eager_extra=True, oracle_steps={3, 8})
+
+
+@pytest.mark.parametrize("name", ["gdn_delta", "kda_delta"])
+def test_graph_fp16_factors(name):
+    """Factors stored in binary16: the graph pool stays bit-identical to the eager one and within
+    the fp16 rounding bound of the oracle."""
+    _twin_run(name, 20, arena=1, oracle_steps={3, 8}, fp16=True)
 
 
 def test_graph_on_dense_baseline_pool():
