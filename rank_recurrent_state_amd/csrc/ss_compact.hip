@@ -54,9 +54,31 @@ __device__ __forceinline__ void copy_comp(const float *su, const float *sv, F *d
   }
 }
 
+// streaming store into factor storage: the copied components are read again only by the next
+// decode step, after the rest of the compaction has gone through the caches
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void stf4nt(float *p, float4 v) {
+  const f32x4_t x = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(x, reinterpret_cast<f32x4_t *>(p));
+}
+__device__ __forceinline__ void stf4nt(_Float16 *p, float4 v) {
+  half4_t h;
+  h.x = (_Float16)v.x;
+  h.y = (_Float16)v.y;
+  h.z = (_Float16)v.z;
+  h.w = (_Float16)v.w;
+  __builtin_nontemporal_store(h, reinterpret_cast<half4_t *>(p));
+}
+
+__device__ __forceinline__ void stfnt(float *p, float v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void stfnt(_Float16 *p, float v) { __builtin_nontemporal_store((_Float16)v, p); }
+__device__ __forceinline__ float ldfnt(const float *p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ float ldfnt(const _Float16 *p) { return (float)__builtin_nontemporal_load(p); }
+
 // Copy `cnt` components (u, v) starting at ring position c0 of arena `src`
 // to the positions dst_of(f) (a component for which it returns false is dropped).
-// All lanes take float4 pieces of consecutive components, UNC pieces in flight.
+// All lanes take float4 pieces of consecutive components, UNC pieces in flight; the source is
+// read once and the destination written once, both with the nontemporal hint.
 template <typename F, typename DstOf>
 __device__ __forceinline__ void copy_comps(const Arena &src, int64_t c0, int cnt, int dk, int dv, int lane,
                                            DstOf dst_of) {
@@ -72,7 +94,7 @@ __device__ __forceinline__ void copy_comps(const Arena &src, int64_t c0, int cnt
       const int f = ec / tot4, c = ec - f * tot4;
       const int64_t cs = wrap(c0 + f, src.cap);
       const F *p = c < dk4 ? src.U<F>() + cs * dk + 4 * c : src.V<F>() + cs * dv + 4 * (c - dk4);
-      x[q] = ldf4(p);
+      x[q] = ldf4nt(p);
     }
 #pragma unroll
     for (int q = 0; q < UNC; ++q) {
@@ -81,8 +103,7 @@ __device__ __forceinline__ void copy_comps(const Arena &src, int64_t c0, int cnt
         const int f = e / tot4, c = e - f * tot4;
         F *du, *dvp;
         if (dst_of(f, du, dvp)) {
-          if (c < dk4) stf4(du + 4 * c, x[q]);
-          else stf4(dvp + 4 * (c - dk4), x[q]);
+          stf4nt(c < dk4 ? du + 4 * c : dvp + 4 * (c - dk4), x[q]);  // one 16-byte store
         }
       }
     }
@@ -212,8 +233,8 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
 #pragma unroll
         for (int t = 0; t < NS; ++t) {
           const int row = lane + 64 * t;
-          uc[jj][t] = self(valid && row < dk, su[row < dk ? row : dk - 1]);
-          vc[jj][t] = self(valid && row < dv, sv[row < dv ? row : dv - 1]);
+          uc[jj][t] = self(valid && row < dk, ldfnt(su + (row < dk ? row : dk - 1)));
+          vc[jj][t] = self(valid && row < dv, ldfnt(sv + (row < dv ? row : dv - 1)));
         }
       } else {  // fp16 factors (wave-uniform branch)
         const F *su = a.act.U<F>() + ca * dk;
@@ -221,8 +242,8 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
 #pragma unroll
         for (int t = 0; t < NS; ++t) {
           const int row = lane + 64 * t;
-          uc[jj][t] = self(valid && row < dk, ldf(su + (row < dk ? row : dk - 1)));
-          vc[jj][t] = self(valid && row < dv, ldf(sv + (row < dv ? row : dv - 1)));
+          uc[jj][t] = self(valid && row < dk, ldfnt(su + (row < dk ? row : dk - 1)));
+          vc[jj][t] = self(valid && row < dv, ldfnt(sv + (row < dv ? row : dv - 1)));
         }
       }
       if constexpr (DIAG) {  // active columns and pad keys carry the decays
@@ -411,8 +432,8 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
 #pragma unroll
     for (int t = 0; t < NS; ++t) {  // rounded to the storage type here (fp16 factors: at every compaction)
       const int row = lane + 64 * t;
-      if (row < dk) stf(du + row, ou[t]);
-      if (row < dv) stf(dvv + row, ov[t]);
+      if (row < dk) stfnt(du + row, ou[t]);
+      if (row < dv) stfnt(dvv + row, ov[t]);
     }
   }
   if (lane < kl && posL[lane] < total) *slot_s(posL[lane]) = sgs[lane];
@@ -432,8 +453,8 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
 #pragma unroll
         for (int t = 0; t < NS; ++t) {
           const int row = lane + 64 * t;
-          xu[c][t] = ldf(su + (row < dk ? row : dk - 1));
-          xv[c][t] = ldf(sv + (row < dv ? row : dv - 1));
+          xu[c][t] = ldfnt(su + (row < dk ? row : dk - 1));
+          xv[c][t] = ldfnt(sv + (row < dv ? row : dv - 1));
         }
       }
 #pragma unroll
@@ -448,8 +469,8 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
 #pragma unroll
         for (int t = 0; t < NS; ++t) {
           const int row = lane + 64 * t;
-          if (row < dk) stf(du + row, xu[c][t] * gr[t] * inv);
-          if (row < dv) stf(dvv + row, xv[c][t]);
+          if (row < dk) stfnt(du + row, xu[c][t] * gr[t] * inv);
+          if (row < dv) stfnt(dvv + row, xv[c][t]);
         }
       }
     }
