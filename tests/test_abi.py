@@ -187,3 +187,36 @@ def test_create_rejects_bad_dense_given_states(lib):
     init2 = ss.Init(off.ctypes.data_as(ss._c_i64p), u.ctypes.data_as(ss._c_f32p), u.ctypes.data_as(ss._c_f32p),
                     sig.ctypes.data_as(ss._c_f32p), mask2.ctypes.data_as(ss._c_u8p), None)
     assert lib.ss_state_pool_create(ctypes.byref(desc), ctypes.byref(init2), None, ctypes.byref(out)) == ss.SS_ERR_ARG
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built HIP library every entry point raises: there is no CPU path to fall back on."""
+    from rank_recurrent_state_amd import sinkstate
+    monkeypatch.setattr(sinkstate, "LIB_PATH", str(tmp_path / "libsinkstate.so"))
+    monkeypatch.setattr(sinkstate, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        sinkstate.load_library()
+    with pytest.raises(RuntimeError, match="missing"):
+        sinkstate.state_pool_create(4, 16, 32, 8, 2)
+
+
+def test_product_path_does_not_reach_the_oracle():
+    """The package and the binding import nothing from the oracle, and bench.py touches it only in
+    its CPU-baseline leg."""
+    pkg = os.path.join(ROOT, "rank_recurrent_state_amd")
+    pat = re.compile(r"^\s*(import|from)\s+\S*oracle", re.M)
+    for name in sorted(os.listdir(pkg)):
+        if name.endswith(".py"):
+            assert not pat.search(open(os.path.join(pkg, name)).read()), name
+    for src in ("ss_pool.cpp", "ss_decode.hip", "ss_compact.hip", "ss_consolidate.hip", "ss_init.hip"):
+        text = open(os.path.join(pkg, "csrc", src)).read()
+        assert "orc_" not in text and "oracle" not in text.lower(), src
+    bench = open(os.path.join(ROOT, "bench.py")).read()
+    uses = [m.start() for m in re.finditer(r"\boracle\b", bench)]
+    fn = re.search(r"def cpu_baseline\b.*?(?=\ndef |\Z)", bench, re.S)
+    assert fn is not None
+    for u in uses:
+        line = bench[bench.rfind("\n", 0, u) + 1:bench.find("\n", u)]
+        if line.lstrip().startswith("#") or "\"" in line or "'" in line:
+            continue  # comments and strings
+        assert fn.start() <= u < fn.end(), line
