@@ -526,3 +526,86 @@ def test_rsvd_blocks_cover_the_state_and_zero_state_is_empty():
     assert np.linalg.norm(S - Uo.T @ np.diag(so) @ Vo) <= 1e-12 * np.linalg.norm(S)
     Uz, Vz, sz = rsvd_init(np.zeros((10, 6)), om, 0.1, iters=2)
     assert len(sz) == 0
+
+
+# --------------------------------------------------------------------------
+# the bound's per-step decay is exact: after a compaction drops a known E, decode steps that
+# write nothing (k = 0, v = 0) only decay the state, so the factored state stays exactly
+# (prod alpha) E away from the untruncated one, and SEED Prop. 3's bound is attained
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("promote", [False, True])
+@pytest.mark.parametrize("rule,dense_ref", [(0, False), (1, False), (0, True), (1, True)])
+def test_bound_decays_exactly_and_is_attained(rule, dense_ref, promote):
+    """With promote, the compaction leaves 3 > L = 2 components and the state goes dense: its
+    bound must keep decaying on the dense path."""
+    g = json.load(open(os.path.join(GOLD, "sinkstate_fig6_worked_example.json")))
+    e = np.eye(6)
+    loc, fr = g["local_svd_sigma_printed"], g["frozen_sigma_printed"]
+    comps = dict(U=np.stack([e[0], e[3], e[4]]), V=np.stack([e[0], e[3], e[4]]),
+                 sigma=np.array([loc[0], fr[0], fr[1]]), PK=np.stack([e[1], e[2]]), PW=np.stack([e[1], e[2]]),
+                 pc=np.array([loc[1], loc[2]]))
+    P = OraclePool(1, 6, 6, 2, g["r"], 2 if promote else 99, promote)
+    P.set_state(0, OracleState(**comps, rule=rule, eps=g["eps"]), as_init=False)   # no fallback test at load
+    S0 = P.reconstruct(0)
+    R = OraclePool(1, 6, 6, 2, g["r"], 99, False)   # the same state, never truncated
+    R.set_state(0, OracleState(S=S0, rule=rule) if dense_ref else OracleState(**comps, rule=rule, eps=0.0),
+                as_init=False)
+    if not dense_ref:
+        R.compact([0])   # eps = 0: exact up to rounding, and R's pad is free again
+    P.compact([0])
+    E = 0.79 * np.outer(e[4], e[4]) + 0.04 * np.outer(e[2], e[2])   # what the Figure 6 example drops
+    assert abs(P.bound(0) - np.linalg.norm(E)) <= 1e-14
+    assert P.get_state(0).dense == promote
+    alphas = [0.9, 0.8, 0.95, 0.7, 0.99]   # fewer than K = 2 steps between compactions of R
+    prod = 1.0
+    z = np.zeros((1, 6))
+    for t, a in enumerate(alphas[:1]):
+        P.decode(z, z, z, np.array([a]), np.array([0.5]))
+        R.decode(z, z, z, np.array([a]), np.array([0.5]))
+        prod *= a
+        assert abs(P.bound(0) - prod * np.linalg.norm(E)) <= 1e-14, (t, P.bound(0))
+        err = np.linalg.norm(P.reconstruct(0) - R.reconstruct(0))
+        assert abs(err - P.bound(0)) <= 1e-14, (t, err, P.bound(0))
+    # a second compaction of the zero-weight pad drops nothing more; the bound keeps decaying
+    P.compact([0])
+    for a in alphas[1:]:
+        if not dense_ref:
+            R.compact([0])   # eps = 0: exact, keeps R's pad from filling
+        P.decode(z, z, z, np.array([a]), np.array([0.5]))
+        R.decode(z, z, z, np.array([a]), np.array([0.5]))
+        P.compact([0])
+        prod *= a
+        assert abs(P.bound(0) - prod * np.linalg.norm(E)) <= 1e-14, (a, P.bound(0))
+        err = np.linalg.norm(P.reconstruct(0) - R.reconstruct(0))
+        assert abs(err - P.bound(0)) <= 1e-14, (a, err, P.bound(0))
+
+
+@pytest.mark.parametrize("promote", [False, True])
+def test_bound_decays_with_the_largest_channel_decay(promote):
+    """Per-channel decay: the contraction factor is the largest channel decay; with every channel
+    decaying alike the bound is attained exactly."""
+    rng = np.random.default_rng(31)
+    d = 8
+    U, V = _orth(rng, d, 3), _orth(rng, d, 3)
+    P = OraclePool(1, d, d, 8, 2, 1 if promote else 99, promote, diag_decay=True)
+    # two components and one pad slot orthogonal to them, whose weight 0.01 falls below 0.05 * 4
+    P.set_state(0, OracleState(U[:, :2].T, V[:, :2].T, np.array([4.0, 1.0]), U[:, 2:].T, V[:, 2:].T,
+                               np.array([0.01]), eps=0.05), as_init=False)
+    S0 = P.reconstruct(0)   # before the truncation
+    P.compact([0])
+    assert P.get_state(0).dense == promote
+    assert abs(P.bound(0) - 0.01) <= 1e-15
+    prod = 1.0
+    z = np.zeros((1, d))
+    for lam in [0.9, 0.97, 0.8]:
+        P.decode(z, z, z, np.full((1, d), lam), np.array([0.3]))
+        prod *= lam
+        assert abs(P.bound(0) - 0.01 * prod) <= 1e-15
+        err = np.linalg.norm(P.reconstruct(0) - prod * S0)
+        assert abs(err - P.bound(0)) <= 1e-14
+    # unequal channel decays: the bound follows the largest one and still holds
+    lam = np.linspace(0.5, 0.9, d)[None]
+    P.decode(z, z, z, lam, np.array([0.3]))
+    assert abs(P.bound(0) - 0.01 * prod * 0.9) <= 1e-15
+    Sref = (lam[0][:, None] * prod) * S0
+    assert np.linalg.norm(P.reconstruct(0) - Sref) <= P.bound(0) + 1e-14
