@@ -23,8 +23,9 @@ if torch.cuda.is_available():
     from rank_recurrent_state_amd import workloads as W
 
 
-def _freerun(name, steps, stride, requests=None):
+def _freerun(name, steps, stride, requests=None, need_promotions=False):
     w = W.get(name, n_requests=requests)
+    L = ss.dense_rank_limit(w.d_k, w.d_v)
     init = W.initial_state(w)
     pool = ss.state_pool_create(w.n_states, w.d_k, w.d_v, w.K, w.r, group_of_state=init["group_of_state"],
                                 group_offset=init["group_offset"], rule=init["rule"], eps=init["eps"],
@@ -71,8 +72,21 @@ def _freerun(name, steps, stride, requests=None):
             Sg, So, Sd = reconstruct(gpu[j]), Pf.reconstruct(j), Pd.reconstruct(j)
             nd = max(np.linalg.norm(Sd), 1e-30)
             ost = Pf.get_state(j)
-            ranks_differ = gpu[j]["dense"] != ost.dense or (
-                not ost.dense and len(gpu[j]["sigma"]) != len(ost.sigma))
+            if gpu[j]["dense"] != ost.dense:
+                # one side promoted: accepted only when the factored side holds exactly L components
+                # and the states differ by no more than one component at the threshold, i.e. the
+                # other side kept an (L+1)-th component that fell in the guard band
+                fac = ost if not ost.dense else None
+                rk = len(fac.sigma) if fac is not None else len(gpu[j]["sigma"])
+                smax = float(fac.sigma[0]) if fac is not None else float(np.max(gpu[j]["sigma"]))
+                diff = np.linalg.norm(Sg - So)
+                assert rk == L and diff <= (eps[j] + GUARD) * smax + TOL * np.linalg.norm(So), \
+                    (name, t, j, rk, diff, smax)
+                Pf.set_state(j, to_oracle_state(gpu[j], eps[j]), as_init=False)
+                resync += 1
+                resynced.add(j)
+                continue
+            ranks_differ = not ost.dense and len(gpu[j]["sigma"]) != len(ost.sigma)
             if ranks_differ:
                 # accepted only for a guard-band decision: the components the two sides keep
                 # differently lie within GUARD sigma_max of the threshold
@@ -93,21 +107,39 @@ def _freerun(name, steps, stride, requests=None):
             b = Pf.bound(j)
             worst["bound_or"] = max(worst["bound_or"], (np.linalg.norm(So - Sd) - b) / nd)
             worst["bound_gpu"] = max(worst["bound_gpu"], (np.linalg.norm(Sg - Sd) - b) / nd)
+    n_dense_or = sum(Pf.get_state(j).dense for j in range(n))
+    n_dense_gpu = sum(st["dense"] for st in ss.state_export(pool, ids))
+    promotions = ss.pool_stats(pool)["promotions"]
     pool.close()
-    print(name, n, "states", steps, "steps", worst, "resyncs", resync)
+    print(name, n, "states", steps, "steps", worst, "resyncs", resync, "dense in the sample: oracle", n_dense_or,
+          "gpu", n_dense_gpu, "gpu promotions", promotions)
+    if need_promotions:
+        assert n_dense_or > 0 and n_dense_gpu > 0 and promotions > 0, (n_dense_or, n_dense_gpu, promotions)
     assert worst["o"] <= TOL and worst["S"] <= TOL, worst
     assert worst["bound_or"] <= 1e-12, worst
     assert worst["bound_gpu"] <= TOL, worst
 
 
 def test_freerun_tiny():
-    """All 64 states 16x32 from an empty start, 64 steps (8 compactions, promotions to dense)."""
-    _freerun("tiny", steps=64, stride=1)
+    """All 64 states 16x32 from an empty start over the workload's whole 256 steps (32 compactions,
+    promotions to dense), outputs checked every step."""
+    _freerun("tiny", steps=256, stride=1, need_promotions=True)
 
 
 def test_freerun_mamba2_one_request():
-    _freerun("mamba2_258k", steps=32, stride=41, requests=1)
+    """One request (2,016 states, every 41st sampled) over the workload's whole 1,024 steps: ranks
+    cross L = 49 near step 44 and the whole sample is dense by step 64; the remaining steps run the
+    dense region's buffered steps and pad folds."""
+    _freerun("mamba2_258k", steps=1024, stride=41, requests=1, need_promotions=True)
 
 
 def test_freerun_gdn_one_request():
-    _freerun("gdn_delta", steps=32, stride=31, requests=1)
+    """One request (1,536 delta-rule states, every 31st sampled) over the workload's whole 512
+    steps, past the sample's first promotions (near step 75)."""
+    _freerun("gdn_delta", steps=512, stride=31, requests=1, need_promotions=True)
+
+
+def test_freerun_mixed_one_request():
+    """One request of the mixed pool (1,024 states, half scalar-decay, half delta-rule, some dense
+    from the start, every 19th sampled) over the workload's whole 256 steps."""
+    _freerun("mixed_dense", steps=256, stride=19, requests=1, need_promotions=True)
