@@ -24,6 +24,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
+# plain (non-packed) fp32 VALU ceiling of the compaction: 256 CUs x 4 SIMDs x 16 lanes x 2 flops per
+# FMA x 2.4 GHz = 78.6 TFLOP/s (the published 157.3 counts packed fp32 instructions, which this
+# library does not use)
+FP32_VALU_PEAK_TFLOPS = 78.6
 METRIC = "state-steps/sec and achieved HBM GB/s (% peak) for decode_step, 258k states"
 
 
@@ -40,8 +44,9 @@ ASYNC_LOG = {}  # poll results (and launches) of the asynchronous consolidation,
 def _run_steps(ss, torch, pool, xs, t0, o, ev=None, cons=(0, 1), side=None):
     """Run len(xs) steps starting after step t0; optional per-step events.  cons = (groups, period):
     every `period` steps, consolidate up to `groups` groups from the wait queue after the compactions.
-    side: a second stream for the asynchronous consolidation: after each step's compactions the
-    finished result is installed (or dropped when stale) and the next group from the queue starts."""
+    side: a second stream for the asynchronous consolidation (or "host" for the host-core form):
+    after each step's compactions the finished result is installed (or dropped when stale) and the
+    next group from the queue starts."""
     for i, x in enumerate(xs):
         t = t0 + i + 1
         if ev is not None:
@@ -52,7 +57,8 @@ def _run_steps(ss, torch, pool, xs, t0, o, ev=None, cons=(0, 1), side=None):
         if side is not None:
             st = ss.consolidate_poll(pool)
             ASYNC_LOG[st] = ASYNC_LOG.get(st, 0) + 1
-            if st != ss.CONS_RUNNING and ss.consolidate_async(pool, side) >= 0:
+            if st != ss.CONS_RUNNING and (ss.consolidate_host(pool) if side == "host"
+                                          else ss.consolidate_async(pool, side)) >= 0:
                 ASYNC_LOG["launched"] = ASYNC_LOG.get("launched", 0) + 1
         elif cons[0] > 0 and t % cons[1] == 0:
             ss.consolidate_next(pool, cons[0])
@@ -188,7 +194,7 @@ def _traffic(kernel, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None when the decode
     kernel's source has changed since the counters were taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
@@ -227,6 +233,8 @@ def main():
     ap.add_argument("--consolidate", type=int, default=0,
                     help="groups consolidated from the wait queue after a step's compactions (0: off)")
     ap.add_argument("--consolidate-period", type=int, default=1, help="steps between consolidation calls")
+    ap.add_argument("--consolidate-host", action="store_true",
+                    help="consolidate frozen parts on host cores beside the decode (download, fp64 SVD, upload)")
     ap.add_argument("--consolidate-async", action="store_true",
                     help="consolidate on a second stream, one group at a time from the wait queue, beside the decode")
     ap.add_argument("--stagger", default=None, choices=["none", "even4", "paper8", "state8"],
@@ -265,7 +273,7 @@ def main():
     o = torch.empty(w.n_states, w.d_v, device="cuda")
 
     cons = (max(0, args.consolidate), max(1, args.consolidate_period))
-    side = torch.cuda.Stream() if args.consolidate_async else None  # default priority
+    side = "host" if args.consolidate_host else torch.cuda.Stream() if args.consolidate_async else None  # default priority
     # warmup on a scratch pool of the same workload
     fkw = {"factor_fp16": True} if args.factor_fp16 else {}
     if args.warmup > 0:
@@ -338,7 +346,8 @@ def main():
         xf = st1["consolidate_flops"] - st0["consolidate_flops"]
         alog = {"launched": ASYNC_LOG.get("launched", 0), "steps_running": ASYNC_LOG.get(ss.CONS_RUNNING, 0),
                 "installed": ASYNC_LOG.get(ss.CONS_INSTALLED, 0), "discarded": ASYNC_LOG.get(ss.CONS_DISCARDED, 0)}
-        consolidation = {"mode": "async (second stream)" if side is not None else "in the step",
+        consolidation = {"mode": "host cores (download, fp64 SVD, upload)" if side == "host" else
+                         "async (second stream)" if side is not None else "in the step",
                          "async_polls": alog if side is not None else None,
                          "groups_per_call": cons[0], "period": cons[1], "launches": kn["consolidate"],
                          "live_bytes_end": st1["live_bytes"], "n_dense_end": st1["n_dense"],
@@ -420,6 +429,13 @@ def main():
                         "achieved_GBs": decode_bytes / (decode_ms / 1e3) / 1e9 if decode_ms else None,
                         "kernels": per_kernel},
         "compaction": compaction,
+        "compaction_roofline": {"bound": "valu", "kernel": "compact",
+                                "achieved": compaction["algorithmic_TFLOPs"], "peak": FP32_VALU_PEAK_TFLOPS,
+                                "unit": "TFLOP/s",
+                                "frac": compaction["algorithmic_TFLOPs"] / FP32_VALU_PEAK_TFLOPS
+                                if compaction["algorithmic_TFLOPs"] else None,
+                                "flops_per_launch": cflops / kn["compact"] if kn["compact"] else None,
+                                "share_of_step": kms["compact"] / total_ms if total_ms else None},
         "consolidation": consolidation,
         "frozen_components_end": st1["frozen_components"],
         "phases": phases,

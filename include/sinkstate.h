@@ -161,6 +161,7 @@ typedef struct {
   uint64_t consolidate_states;   /* states whose frozen part was consolidated */
   uint64_t consolidate_flops;    /* algorithmic flops of those consolidations */
   uint64_t consolidate_removed;  /* frozen components they removed */
+  int64_t jacobi_limit_hits;     /* compactions whose small SVD still rotated in its last allowed sweep */
 } ss_stats;
 
 /* Create a pool ([SS] 4.4 "Memory layout"): per state a 16-byte metadata
@@ -172,6 +173,27 @@ typedef struct {
  * SS_ERR_HIP.  On success *out owns the pool; release it with
  * ss_state_pool_destroy. */
 ss_status ss_state_pool_create(const ss_pool_desc *desc, const ss_init *init, hipStream_t stream, ss_pool **out);
+
+/* Create a pool from dense states and their randomized block SVD ([SS] 4.2
+ * "Randomized SVD initialization after prefill"; 4.4 "Memory layout": the
+ * dense fallback is decided once a state has been factored).  S, u, v, sigma
+ * and rank are device memory as ss_rsvd_init with
+ * the same max_rank reads and writes them: S [n_states][d_k][d_v], u
+ * [n_states][max_rank][d_k], v [n_states][max_rank][d_v], sigma
+ * [n_states][max_rank], rank [n_states].  The library reads the factors and
+ * ranks back (the call synchronizes `stream`), keeps a state whose rank
+ * exceeds L (desc->dense_rank_limit, or floor(d_k d_v / (d_k + d_v))) dense
+ * as its exact S, read in place on the device, and gives every other state
+ * its rank[s] components in descending sigma (the blocks are each
+ * descending, not across blocks; equal values keep block order), first r
+ * active, the rest frozen.  Then as ss_state_pool_create, whose desc fields
+ * apply (force_dense is refused).  The caller keeps ownership of every
+ * pointer; S may be freed once the call returns.  Errors: SS_ERR_ARG (also
+ * for a rank outside [0, max_rank]), SS_ERR_SHAPE, SS_ERR_OOM, SS_ERR_CAPACITY,
+ * SS_ERR_HIP. */
+ss_status ss_state_pool_create_from_dense(const ss_pool_desc *desc, const float *S, const float *u, const float *v,
+                                          const float *sigma, const int32_t *rank, int32_t max_rank,
+                                          hipStream_t stream, ss_pool **out);
 
 /* Waits for the pool's streams and frees all of its memory.  NULL is a no-op. */
 ss_status ss_state_pool_destroy(ss_pool *pool);
@@ -256,9 +278,9 @@ ss_status ss_consolidate_next(ss_pool *pool, int32_t max_groups, int32_t *out, i
  * part).  Here the exact SVD runs on the GPU, on a second stream `side` given by the caller, while
  * the pool's stream goes on decoding.
  *  ss_consolidate_async: group >= 0 selects that group; group < 0 takes, among the groups waiting
- *    (compacted since their last consolidation), the one compacted most recently, whose result has
- *    the longest time to land before the group compacts again; then the least recently
- *    consolidated, then the lowest id (*launched = -1 when no group waits).  On
+ *    (compacted since their last consolidation), those whose last asynchronous result was dropped
+ *    as stale first, then the least recently consolidated (never consolidated first), then the
+ *    lowest id ([SS] Figure 7(b); *launched = -1 when no group waits).  On
  *    `stream` it copies the group's 16-byte records aside; `side` waits for that copy and runs the
  *    kernel, which reads the frozen parts and writes its results to staging only (the rings and
  *    records are not touched).  One consolidation may be in flight per pool (SS_ERR_STATE for a
@@ -275,6 +297,33 @@ ss_status ss_consolidate_next(ss_pool *pool, int32_t max_groups, int32_t *out, i
 enum { SS_CONS_IDLE = 0, SS_CONS_RUNNING = 1, SS_CONS_INSTALLED = 2, SS_CONS_DISCARDED = 3 };
 ss_status ss_consolidate_async(ss_pool *pool, int32_t group, hipStream_t stream, hipStream_t side, int32_t *launched);
 ss_status ss_consolidate_poll(ss_pool *pool, int32_t wait, hipStream_t stream, int32_t *state);
+
+/* Asynchronous consolidation on host cores, the pipeline of [SS] 4.3 "Asynchronous CPU
+ * Consolidation" and Figure 7(b): download the frozen parts, exact SVD on the host, upload, and
+ * install unless the group has compacted meanwhile.  Group selection, the snapshot of the records
+ * on `stream`, the one-in-flight rule, SS_CONS_* states and the install with its staleness check
+ * are those of ss_consolidate_async, and ss_consolidate_poll completes it; the frozen part a
+ * result replaces is the one the snapshot names.  The library's own second stream (created at the
+ * first call, default priority) gathers the group's frozen components into device staging (the
+ * group's segment of the frozen ring, packed per member as [group][f][d_k], [.][f][d_v], [.][f])
+ * and copies them, with each state's sigma_0, into pinned host memory.  A host thread then waits
+ * for the download and runs, on `threads` host threads (0: one per hardware thread), an exact
+ * fp64 SVD of every frozen part (thin QR of V_F, B = U_F Sigma_F R^T, thin QR of B, one-sided
+ * Jacobi on its R to 1e-15), drops values below eps * sigma_0, and enqueues the upload of the
+ * results on the same stream.  ss_consolidate_poll returns SS_CONS_RUNNING until that upload is
+ * enqueued (wait != 0 blocks), then installs on `stream` after it, or drops a stale result.  A
+ * ring re-pack waits only for the gather.  Pinned host memory of the staging's size is allocated
+ * at the first call.  Not available with diag_decay (SS_ERR_ARG).  Errors: SS_ERR_ARG,
+ * SS_ERR_STATE (one in flight), SS_ERR_OOM, SS_ERR_HIP. */
+ss_status ss_consolidate_host(ss_pool *pool, int32_t group, hipStream_t stream, int32_t threads, int32_t *launched);
+
+/* The host arithmetic of ss_consolidate_host for one state, on host memory (a test and
+ * measurement hook; touches no GPU): the f components u [f][d_k], v [f][d_v], sigma [f] (fp32,
+ * caller-owned) are replaced by the exact SVD of sum_k sigma_k u_k v_k^T with the values below
+ * eps * sigma0 dropped, in descending order; *kept receives their count (<= f) and rows past it
+ * are left as they were.  Errors: SS_ERR_ARG (null pointer, f < 0), SS_ERR_SHAPE (d_k, d_v < 1). */
+ss_status ss_host_consolidate_frozen(int32_t d_k, int32_t d_v, int32_t f, float *u, float *v, float *sigma,
+                                     float sigma0, float eps, int32_t *kept);
 
 /* Staggered schedule ([SS] 4.2 "Staggered compaction across layers"): the
  * groups due after decode step `step` (counted from 1) are those with
@@ -293,7 +342,8 @@ ss_status ss_schedule_due(const ss_pool *pool, int64_t step, int32_t *out, int32
  * block; if one is below, no further block is taken; otherwise the block is
  * subtracted from the residual and the next block starts.  At most n_blocks
  * blocks and max_rank components.  (The dense-fallback decision, rank > L,
- * is the caller's: see ss_init.dense_mask.)
+ * is taken when a pool is built from these results:
+ * ss_state_pool_create_from_dense.)
  * All pointers are device memory, row-major, caller-owned:
  *   S [n][d_k][d_v] (read), omega [n][n_blocks][d_k][block] (read),
  *   eps [n] (read), work [n][d_k][d_v] (scratch, overwritten),
@@ -306,6 +356,7 @@ ss_status ss_schedule_due(const ss_pool *pool, int64_t step, int32_t *out, int32
 ss_status ss_rsvd_init(const float *S, int64_t n, int32_t d_k, int32_t d_v, int32_t block, int32_t n_blocks,
                        int32_t iters, const float *omega, const float *eps, int32_t max_rank, float *work, float *u,
                        float *v, float *sigma, int32_t *rank, hipStream_t stream);
+
 
 /* Whole decode steps as HIP graphs ([SS] 4.4 "Kernel fusion, load balancing,
  * and support for CUDA graphs": the pages replay steps as graphs; here one

@@ -11,7 +11,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsinkstate.so")
-SOURCES = ["ss_pool.cpp", "ss_decode.hip", "ss_compact.hip", "ss_init.hip", "ss_consolidate.hip"]
+SOURCES = ["ss_pool.cpp", "ss_host_cons.cpp", "ss_decode.hip", "ss_compact.hip", "ss_init.hip",
+           "ss_consolidate.hip"]
 ARCH = os.environ.get("SINKSTATE_ARCH", "gfx950")
 
 FLAGS = [

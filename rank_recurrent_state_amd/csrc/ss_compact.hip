@@ -163,6 +163,7 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   const bool work = live && n > 0 && !keep;  // a Brand update; otherwise the components move unchanged
   const int mcol = ra + n;
   int kl = 0, kf = 0, total = 0, ra2 = ra, rf2 = rf, sweeps = 0;
+  bool jlimit = false;
   float uc[kMaxM][NS], vc[kMaxM][NS];
   float gr[NS];  // DIAG: the state's decays, row lane + 64 t (0 past d_k)
 #pragma unroll
@@ -269,7 +270,7 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
       Vh[j * 16 + i] = (i == j) ? 1.f : 0.f;
     }
     wave_sync();
-    sweeps = jacobi16(Cm, Vh, mcol, lane);
+    sweeps = jacobi16(Cm, Vh, mcol, lane, &jlimit);
     if (lane < 16) {
       float x = 0.f;
 #pragma unroll
@@ -505,6 +506,370 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
           __hip_atomic_fetch_add(&a.counters[C_PROMOTE_COUNT], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       a.promote_list[idx] = s;
     }
+    if (jlimit) __hip_atomic_fetch_add(&a.counters[C_JACOBI_LIMIT], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long D = (unsigned long long)(dk + dv), mm = (unsigned long long)mcol;
+    const unsigned long long flops = 4ull * D * mm * (mm - 1) + 2ull * mm * mm * mm +
+                                     9ull * mm * mm * (mm - 1) * (unsigned long long)sweeps +
+                                     2ull * D * mm * (unsigned long long)kl;
+    __hip_atomic_fetch_add(&a.acct_flops[s & (kAcctSlots - 1)], flops, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(&a.acct_states[s & (kAcctSlots - 1)], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Brand compaction with the two sides of a state split across the halves of its wavefront (one
+// wavefront per state, four per workgroup).  Lanes [0, 32) hold the d_k side of every column
+// ([U_a | K]), lanes [32, 64) the d_v side ([V_a | W]); a lane keeps NB float4 blocks of each
+// column (element 128 b + 4 l + c of its side's vector in lane l of the half, block b, component
+// c).  Both sides' CGS2 then run as one instruction stream, and each pair of dot products (one per
+// side) is one sum over 32 lanes, where k_compact needs two sums over 64 lanes; the columns take
+// the same registers.  The core, the Jacobi SVD (jacobi16), the merge and the writes are those of
+// k_compact, with the same arithmetic and decisions.
+// ---------------------------------------------------------------------------------------------
+template <int NB>
+__device__ __forceinline__ float dotb(const float4 (&x)[NB], const float4 (&y)[NB]) {
+  float acc = dot4(x[0], y[0]);
+#pragma unroll
+  for (int b = 1; b < NB; ++b) acc += dot4(x[b], y[b]);
+  return acc;
+}
+
+template <int NB, typename F>
+__global__ __launch_bounds__(256) void k_compact_h(CompactArgs a) {
+  __shared__ __align__(16) float lds[4][kLdsPerWave];
+  __shared__ int wg_cnt[4][2];
+  __shared__ unsigned long long wg_base[2];
+  __shared__ int wg_ok;
+  const int w = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int side = lane >> 5, r = lane & 31;
+  const int mi = blockIdx.x * 4 + w;
+  float *Rl = lds[w] + kOffRl;
+  float *Rr = lds[w] + kOffRr;
+  float *Cm = lds[w] + kOffCm;
+  float *Vh = lds[w] + kOffVh;
+  float *scw = lds[w] + kOffScw;
+  float *sgs = lds[w] + kOffSgs;
+  float *sraw = lds[w] + kOffSraw;
+  int *perm = reinterpret_cast<int *>(lds[w] + kOffPerm);
+  int *posL = reinterpret_cast<int *>(lds[w] + kOffPosL);
+  float *fsl = lds[w] + kOffFs;
+  int *posF = reinterpret_cast<int *>(lds[w] + kOffPosF);
+  const int dk = a.dk, dv = a.dv, K = a.K, rr_ = a.r;
+  const int dme = side ? dv : dk;  // length of this lane's side of a column
+  const int64_t capA = a.act.cap, capF = a.frz.cap;
+
+  // ---- phase A: what this wave's state becomes -------------------------------------------
+  bool live = mi < a.n_members;  // a member of the group held in factored form
+  int s = 0, ra = 0, rf = 0, n = 0, off_a = 0, off_f = 0;
+  uint32_t flags = 0;
+  float gamma = 1.0f;
+  if (live) {
+    s = uniform(a.members[mi]);
+    const Meta m = a.meta[s];
+    const uint32_t packed = (uint32_t)uniform((int)m.packed);
+    flags = meta_flags(packed);
+    if (flags & FLAG_DENSE) {
+      live = false;
+    } else {
+      ra = meta_ra(packed);
+      rf = meta_rf(packed);
+      n = meta_n(packed);
+      off_a = uniform(m.off_a);
+      off_f = uniform(m.off_f);
+      gamma = uniformf(m.gamma);
+    }
+  }
+  // an unselected member (compaction of listed states) keeps its pad and Gamma and only moves
+  const bool keep = live && a.sel != nullptr && a.sel[s] == 0;
+  const bool work = live && n > 0 && !keep;  // a Brand update; otherwise the components move unchanged
+  const int mcol = ra + n;
+  int kl = 0, kf = 0, total = 0, ra2 = ra, rf2 = rf, sweeps = 0;
+  bool jlimit = false;
+  float4 x[kMaxM][NB];
+  if (work) {
+    // frozen singular values (scaled by Gamma) to LDS: the merge searches them there
+    for (int f = lane; f < rf; f += 64) fsl[f] = a.frz.s[wrap(off_f + f, capF)] * gamma;
+    // columns: [U_a | K] on the d_k lanes, [V_a | W] on the d_v lanes
+#pragma unroll
+    for (int jj = 0; jj < kMaxM; ++jj) {
+      const bool valid = jj < mcol;
+      const int j = valid ? jj : mcol - 1;  // clamped: the loads stay in bounds (mcol >= 1 here)
+      const bool isact = j < ra;
+      const int64_t ca = wrap(off_a + (isact ? j : 0), capA);
+      const int64_t slot = isact ? 0 : (int64_t)s * K + (j - ra);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int e = 128 * b + 4 * r;
+        const bool ok = valid && e < dme;
+        const int eo = e < dme ? e : 0;
+        float4 v;
+        if (std::is_same<F, float>::value || !isact) {  // wave-uniform branch
+          const float *src = isact ? (side ? a.act.V<float>() + ca * dv : a.act.U<float>() + ca * dk)
+                                   : (side ? a.pw + slot * dv : a.pk + slot * dk);
+          v = ld4nt(src + eo);
+        } else {
+          v = ldf4nt((side ? a.act.V<F>() + ca * dv : a.act.U<F>() + ca * dk) + eo);
+        }
+        x[jj][b] = sel4(ok, v);
+      }
+    }
+    if (lane < kMaxM) {
+      float wgt = 0.f;
+      if (lane < ra) wgt = a.act.s[wrap(off_a + lane, capA)] * gamma;
+      else if (lane < mcol) wgt = a.pc[(int64_t)s * K + (lane - ra)] * gamma;
+      scw[lane] = wgt;
+    }
+    // CGS2 of both sides at once; R goes to LDS row-major, R[i * 16 + jj] = R(i, jj).  A column
+    // whose residual is at most 1e-5 of its input norm is dependent: it and its R row are zeroed.
+    float *Rs = side ? Rr : Rl;
+#pragma unroll
+    for (int jj = 0; jj < kMaxM; ++jj) {
+      if (jj < mcol) {
+        const float n0 = group_sum<32>(dotb<NB>(x[jj], x[jj]));
+        float myr = 0.f;  // R(r, jj) for r < jj
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+          float du[kMaxM];
+#pragma unroll
+          for (int i = 0; i < jj; ++i) du[i] = group_sum<32>(dotb<NB>(x[i], x[jj]));
+#pragma unroll
+          for (int i = 0; i < jj; ++i) {
+            myr += (r == i) ? du[i] : 0.f;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) x[jj][b] = fma4(-du[i], x[i][b], x[jj][b]);
+          }
+        }
+        const float nu = group_sum<32>(dotb<NB>(x[jj], x[jj]));
+        const bool kk = nu > 0.f && nu > kTau2 * n0;
+        const float su = sqrtf(nu);
+        const float iv = kk ? 1.0f / su : 0.f;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) x[jj][b] = scale4(iv, x[jj][b]);
+        if (r < kMaxM) Rs[r * 16 + jj] = r < jj ? myr : (r == jj ? (kk ? su : 0.f) : 0.f);
+      } else {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) x[jj][b] = zero4();
+        if (r < kMaxM) Rs[r * 16 + jj] = 0.f;
+      }
+    }
+    wave_sync();
+    // core C = R_L diag(w) R_R^T, column-major: lane l forms C(i, j) for i = l mod 16 and the four
+    // j = l / 16 + 4 q from row i of R_L and rows j of R_R (both upper triangular, so the sum over t
+    // runs over t >= max(i, j); the zero terms below it leave the sum unchanged)
+    {
+      const int i = lane & 15, j0 = lane >> 4;
+      float rl[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 a4 = *reinterpret_cast<const float4 *>(Rl + i * 16 + 4 * q);
+        const float4 w4 = *reinterpret_cast<const float4 *>(scw + 4 * q);
+        rl[4 * q] = a4.x * w4.x;
+        rl[4 * q + 1] = a4.y * w4.y;
+        rl[4 * q + 2] = a4.z * w4.z;
+        rl[4 * q + 3] = a4.w * w4.w;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = j0 + 4 * q;
+        float acc = 0.f;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const float4 b4 = *reinterpret_cast<const float4 *>(Rr + j * 16 + 4 * h);
+          acc = fmaf(rl[4 * h], b4.x, acc);
+          acc = fmaf(rl[4 * h + 1], b4.y, acc);
+          acc = fmaf(rl[4 * h + 2], b4.z, acc);
+          acc = fmaf(rl[4 * h + 3], b4.w, acc);
+        }
+        Cm[j * 16 + i] = acc;
+        Vh[j * 16 + i] = (i == j) ? 1.f : 0.f;
+      }
+    }
+    wave_sync();
+    sweeps = jacobi16(Cm, Vh, mcol, lane, &jlimit);
+    if (lane < 16) {
+      float xx = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) xx = fmaf(Cm[lane * 16 + i], Cm[lane * 16 + i], xx);
+      sraw[lane] = lane < mcol ? sqrtf(xx) : -1.f;
+    }
+    wave_sync();
+    if (lane < mcol) {
+      const float my = sraw[lane];
+      int rank = 0;
+      for (int i = 0; i < mcol; ++i) {
+        const float o = sraw[i];
+        rank += (o > my) || (o == my && i < lane);
+      }
+      perm[rank] = lane;
+      sgs[rank] = my;
+    }
+    wave_sync();
+
+    // merge with the frozen part and truncate: both lists are descending; on ties the local
+    // component comes first; drop sigma < eps * sigma_max and sigma = 0
+    const float smax = fmaxf(sgs[0], rf > 0 ? fsl[0] : 0.f);
+    const float thr = a.eps[s] * smax;
+    kl = __builtin_popcountll(__builtin_amdgcn_ballot_w64(lane < mcol && sgs[lane] >= thr && sgs[lane] > 0.f));
+    for (int f0 = 0; f0 < rf; f0 += 64) {
+      const int f = f0 + lane;
+      kf += __builtin_popcountll(__builtin_amdgcn_ballot_w64(f < rf && fsl[f] >= thr && fsl[f] > 0.f));
+    }
+    total = kl + kf;
+    const int cap_total = rr_ + a.fcap;
+    if (total > cap_total) {
+      if (lane == 0)
+        __hip_atomic_fetch_add(&a.counters[C_CAP_TRUNC], (uint32_t)(total - cap_total), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+      total = cap_total;
+    }
+    ra2 = total < rr_ ? total : rr_;
+    rf2 = total - ra2;
+    if (lane < kl) {  // local i goes after the frozen ones strictly greater than it
+      const float xv = sgs[lane];
+      int lo = 0, hi = kf;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (fsl[mid] > xv) lo = mid + 1;
+        else hi = mid;
+      }
+      posL[lane] = lane + lo;
+    }
+    for (int f = lane; f < kf; f += 64) {  // frozen f goes after the local ones >= it
+      const float xv = fsl[f];
+      int c = 0;
+      for (int i = 0; i < kl; ++i) c += sgs[i] >= xv ? 1 : 0;
+      posF[f] = f + c;
+    }
+    wave_sync();
+  }
+
+  // ---- allocation: the workgroup's new components, one atomic add per ring ----------------
+  if (lane == 0) {
+    wg_cnt[w][0] = live ? ra2 : 0;
+    wg_cnt[w][1] = live ? rf2 : 0;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int sa = 0, sf = 0;
+    for (int i = 0; i < 4; ++i) {
+      sa += wg_cnt[i][0];
+      sf += wg_cnt[i][1];
+    }
+    unsigned long long ba = 0, bf = 0;
+    bool ok = true;
+    if (sa) {
+      ba = __hip_atomic_fetch_add(&a.ring_a->head, (unsigned long long)sa, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ok = ok && ba + sa <= a.ring_a->limit;
+    }
+    if (sf) {
+      bf = __hip_atomic_fetch_add(&a.ring_f->head, (unsigned long long)sf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ok = ok && bf + sf <= a.ring_f->limit;
+    }
+    if (!ok) {  // the ring is full: the group's states keep their old form and the pool reports it
+      __hip_atomic_fetch_add(&a.ring_a->overflow, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *a.hflag = 1u;
+    }
+    wg_base[0] = ba;
+    wg_base[1] = bf;
+    wg_ok = ok ? 1 : 0;
+  }
+  __syncthreads();
+  if (!live || !wg_ok) return;
+  unsigned long long va = wg_base[0], vf = wg_base[1];
+  for (int i = 0; i < w; ++i) {
+    va += (unsigned long long)wg_cnt[i][0];
+    vf += (unsigned long long)wg_cnt[i][1];
+  }
+  const int64_t dst_a = (int64_t)(va % (unsigned long long)capA), dst_f = (int64_t)(vf % (unsigned long long)capF);
+
+  // ---- phase B: write the new components and the record ------------------------------------
+  if (!work) {  // nothing buffered (or not selected): the components move unchanged
+    copy_comps<F>(a.act, off_a, ra, dk, dv, lane, [&](int f, F *&du, F *&dvp) {
+      const int64_t c = wrap(dst_a + f, capA);
+      du = a.act.U<F>() + c * dk;
+      dvp = a.act.V<F>() + c * dv;
+      return true;
+    });
+    copy_comps<F>(a.frz, off_f, rf, dk, dv, lane, [&](int f, F *&du, F *&dvp) {
+      const int64_t c = wrap(dst_f + f, capF);
+      du = a.frz.U<F>() + c * dk;
+      dvp = a.frz.V<F>() + c * dv;
+      return true;
+    });
+    // an empty pad means Gamma = 1 (no step since the last compaction) and sigma takes it in;
+    // an unselected member keeps Gamma with its pad
+    const float gs = keep ? 1.0f : gamma;
+    for (int f = lane; f < ra; f += 64) a.act.s[wrap(dst_a + f, capA)] = a.act.s[wrap(off_a + f, capA)] * gs;
+    for (int f = lane; f < rf; f += 64) a.frz.s[wrap(dst_f + f, capF)] = a.frz.s[wrap(off_f + f, capF)] * gs;
+    if (lane == 0) {
+      Meta nm;
+      nm.off_a = (int32_t)dst_a;
+      nm.off_f = (int32_t)dst_f;
+      nm.gamma = keep ? gamma : 1.0f;
+      nm.packed = meta_pack(ra, rf, keep ? n : 0, flags);
+      a.meta[s] = nm;
+    }
+    return;
+  }
+  // merged position pos -> slot of the new active (pos < r) or frozen component
+  auto slot_u = [&](int pos) -> F * {
+    return pos < rr_ ? a.act.U<F>() + wrap(dst_a + pos, capA) * dk : a.frz.U<F>() + wrap(dst_f + pos - rr_, capF) * dk;
+  };
+  auto slot_v = [&](int pos) -> F * {
+    return pos < rr_ ? a.act.V<F>() + wrap(dst_a + pos, capA) * dv : a.frz.V<F>() + wrap(dst_f + pos - rr_, capF) * dv;
+  };
+  auto slot_s = [&](int pos) -> float * {
+    return pos < rr_ ? a.act.s + wrap(dst_a + pos, capA) : a.frz.s + wrap(dst_f + pos - rr_, capF);
+  };
+  // kept local components: U' = Q_L U_hat (d_k lanes), V' = Q_R V_hat (d_v lanes)
+  for (int i = 0; i < kl; ++i) {
+    const int pos = posL[i];
+    if (pos >= total) continue;
+    const int j = perm[i];
+    const float inv = side ? 1.f : 1.0f / sgs[i];
+    const float *cf = (side ? Vh : Cm) + j * 16;
+    float4 o[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) o[b] = zero4();
+#pragma unroll
+    for (int tt = 0; tt < kMaxM; ++tt) {
+      const float c = cf[tt] * inv;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) o[b] = fma4(c, x[tt][b], o[b]);
+    }
+    F *dst = side ? slot_v(pos) : slot_u(pos);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {  // rounded to the storage type here (fp16 factors: at every compaction)
+      const int e = 128 * b + 4 * r;
+      if (e < dme) stf4nt(dst + e, o[b]);
+    }
+  }
+  if (lane < kl && posL[lane] < total) *slot_s(posL[lane]) = sgs[lane];
+  // kept frozen components: copied, sigma scaled by Gamma
+  copy_comps<F>(a.frz, off_f, kf, dk, dv, lane, [&](int f, F *&du, F *&dvp) {
+    const int pos = posF[f];
+    if (pos >= total) return false;
+    du = slot_u(pos);
+    dvp = slot_v(pos);
+    return true;
+  });
+  for (int f = lane; f < kf; f += 64) {
+    const int pos = posF[f];
+    if (pos < total) *slot_s(pos) = fsl[f];
+  }
+  if (lane == 0) {
+    Meta nm;
+    nm.off_a = (int32_t)dst_a;
+    nm.off_f = (int32_t)dst_f;
+    nm.gamma = 1.0f;
+    nm.packed = meta_pack(ra2, rf2, 0, flags);
+    a.meta[s] = nm;
+    if (a.promote && total > a.L) {
+      const uint32_t idx =
+          __hip_atomic_fetch_add(&a.counters[C_PROMOTE_COUNT], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      a.promote_list[idx] = s;
+    }
+    if (jlimit) __hip_atomic_fetch_add(&a.counters[C_JACOBI_LIMIT], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const unsigned long long D = (unsigned long long)(dk + dv), mm = (unsigned long long)mcol;
     const unsigned long long flops = 4ull * D * mm * (mm - 1) + 2ull * mm * mm * mm +
                                      9ull * mm * mm * (mm - 1) * (unsigned long long)sweeps +
@@ -869,6 +1234,13 @@ __global__ void k_fill_f32(float *p, int64_t n, float x) {
   if (i < n) p[i] = x;
 }
 
+template <int NB, typename F>
+hipError_t compact_h(const CompactArgs &a, hipStream_t st) {
+  const dim3 grid((unsigned)((a.n_members + 3) / 4)), block(256);
+  hipLaunchKernelGGL((k_compact_h<NB, F>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
 template <typename F, bool DG>
 hipError_t compact_ns(const CompactArgs &a, int ns, hipStream_t st) {
   const dim3 grid((unsigned)((a.n_members + 3) / 4)), block(256);
@@ -886,7 +1258,9 @@ hipError_t launch_compact(const CompactArgs &a, hipStream_t st) {
   const int ns = d <= 64 ? 1 : d <= 128 ? 2 : d <= 256 ? 4 : 0;
   if (ns == 0) return hipErrorInvalidValue;
   if (a.gam) return a.act.half ? compact_ns<_Float16, true>(a, ns, st) : compact_ns<float, true>(a, ns, st);
-  return a.act.half ? compact_ns<_Float16, false>(a, ns, st) : compact_ns<float, false>(a, ns, st);
+  // the two sides of a state on the two halves of its wavefront
+  if (d <= 128) return a.act.half ? compact_h<1, _Float16>(a, st) : compact_h<1, float>(a, st);
+  return a.act.half ? compact_h<2, _Float16>(a, st) : compact_h<2, float>(a, st);
 }
 
 hipError_t launch_materialize(const MaterializeArgs &a, int64_t grid_upper, hipStream_t st) {

@@ -338,7 +338,46 @@ __global__ __launch_bounds__(256) void k_cons_install(InstallArgs a) {
   }
 }
 
+// Host-core form, download side: one wavefront per member copies the frozen part the snapshot
+// record names (u, v, sigma, as fp32) into the member's staging rows, and the state's sigma_0
+// (the larger of its first active and first frozen value); cnt is the frozen count, or 0 for a
+// state the consolidation leaves alone (dense, no frozen part, or more than fmax components).
+template <typename F>
+__global__ __launch_bounds__(256) void k_cons_gather(GatherArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 4 + uniform(threadIdx.x >> 6);
+  if (i >= a.n_members) return;
+  const Meta m = a.snap[i];
+  const uint32_t pk = (uint32_t)uniform((int)m.packed);
+  const int ra = meta_ra(pk), rf = meta_rf(pk);
+  const bool ok = !(meta_flags(pk) & FLAG_DENSE) && rf > 0 && rf <= a.fmax;
+  if (lane == 0) a.st_cnt[i] = ok ? rf : 0;
+  if (!ok) return;
+  const int64_t capF = a.frz.cap, off_f = uniform(m.off_f);
+  const size_t sbase = (size_t)i * a.fmax;
+  const int dk = a.dk, dv = a.dv;
+  for (int k = 0; k < rf; ++k) {
+    const int64_t c = wrap(off_f + k, capF);
+    for (int e = lane; e < dk; e += 64) a.st_u[(sbase + k) * dk + e] = ldf(a.frz.U<F>() + c * dk + e);
+    for (int e = lane; e < dv; e += 64) a.st_v[(sbase + k) * dv + e] = ldf(a.frz.V<F>() + c * dv + e);
+    if (lane == 0) a.st_s[sbase + k] = a.frz.s[c];
+  }
+  if (lane == 0) {
+    const float s_act = ra > 0 ? a.act.s[wrap((int64_t)m.off_a, a.act.cap)] : 0.f;
+    const float s_frz = a.frz.s[wrap(off_f, capF)];
+    a.st_s0[i] = s_act > s_frz ? s_act : s_frz;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_cons_gather(const GatherArgs &a, hipStream_t st) {
+  if (a.n_members <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((a.n_members + 3) / 4)), block(256);
+  if (a.frz.half) hipLaunchKernelGGL(k_cons_gather<_Float16>, grid, block, 0, st, a);
+  else hipLaunchKernelGGL(k_cons_gather<float>, grid, block, 0, st, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_cons_snapshot(const Meta *meta, const int32_t *members, int32_t n, Meta *snap, hipStream_t st) {
   if (n <= 0) return hipSuccess;

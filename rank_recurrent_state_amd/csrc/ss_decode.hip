@@ -58,11 +58,20 @@ __device__ __forceinline__ float4 one4() { return make_float4(1.f, 1.f, 1.f, 1.f
 // and a step with decays lambda reads the stored parts with q~ = gamma' q and k~ = gamma' k,
 // gamma' = gamma lambda:  p_q = stored^T q~,  w = beta (v - stored^T k~) (delta) or v,
 // o = p_q + <k, q> w;  the new slot is (k / gamma', w, 1).
+// A state's pairs lie in up to five contiguous runs: its active components (two runs when they
+// wrap around the ring's end), its frozen components (likewise) and its pad.  The stream walks
+// them in chunks of at most G * UN pairs that never cross a run, so a chunk is a wave-uniform
+// base address per vector plus a small per-lane offset (the pair's place in the run times d).
+#ifndef SS_FACT_WAVES
+#define SS_FACT_WAVES 4
+#endif
+constexpr int kFactWaves = SS_FACT_WAVES;  // wavefronts (states) per workgroup of the factored decode
+
 template <int P, int UN, bool RO, bool ANYDELTA, typename F, bool DIAG>
-__global__ __launch_bounds__(256) void k_decode_factored(DecodeArgs a) {
-  constexpr int G = 64 / P;
+__global__ __launch_bounds__(64 * kFactWaves) void k_decode_factored(DecodeArgs a) {
+  constexpr int G = 64 / P, C = G * UN;
   const int lane = threadIdx.x & 63;
-  const uint32_t li = blockIdx.x * 4u + (uint32_t)uniform(threadIdx.x >> 6);
+  const uint32_t li = blockIdx.x * (uint32_t)kFactWaves + (uint32_t)uniform(threadIdx.x >> 6);
   if (li >= *a.fact_count) return;
   const int64_t s = uniform(a.fact_ids[li]);
   const int grp = lane / P, col = lane % P;
@@ -83,9 +92,8 @@ __global__ __launch_bounds__(256) void k_decode_factored(DecodeArgs a) {
     }
     return;
   }
-  const int rr = ra + rf, T = rr + n;
-  const int64_t pad0 = s * (int64_t)K - rr;  // pad slot of list index i is pad0 + i
-  // the inputs are issued before the pair stream; pairs stream in chunks of G * UN
+  const int rr = ra + rf;
+  // the inputs are issued before the pair stream
   const float4 q4 = sel4(kin, ld4nt(a.q + s * dk + 4 * colk));
   const float4 k4 = RO ? zero4() : sel4(kin, ld4nt(a.k + s * dk + 4 * colk));
   const float4 v4 = RO ? zero4() : sel4(vin, ld4nt(a.v + s * dv + 4 * colv));
@@ -100,76 +108,100 @@ __global__ __launch_bounds__(256) void k_decode_factored(DecodeArgs a) {
   const float4 qs = DIAG ? mul4(gn4, q4) : q4;  // what the stored parts are read with
   const float4 ks = DIAG ? mul4(gn4, k4) : k4;
   float4 acc = zero4(), acck = zero4();
-  // pairs [ib, ie) of the list in chunks of G * UN, double-buffered: the next chunk's loads are in
-  // flight while the current one is reduced; ld(i, x, y, w) issues the loads of pair i
-  auto stream = [&](int ib, int ie, auto ld) {
-    float4 xA[UN], yA[UN], xB[UN], yB[UN];
-    float wA[UN], wB[UN];
-    auto load = [&](float4 (&x)[UN], float4 (&y)[UN], float (&wt)[UN], int i0) {
+
+  // the runs, in list order: active (up to the ring's end, then from its start), frozen (likewise),
+  // pad; each by its first component's position in its arena (the pad: its first slot)
+  const int64_t capA = a.act.cap, capF = a.frz.cap;
+  const int na0 = (int)((int64_t)off_a + ra <= capA ? ra : capA - off_a);
+  const int nf0 = (int)((int64_t)off_f + rf <= capF ? rf : capF - off_f);
+  const int rn0 = na0, rn1 = ra - na0, rn2 = nf0, rn3 = rf - nf0, rn4 = n;
+  const int64_t padc = s * (int64_t)K;
+  // chunk cursor (wave-uniform): run index and pairs of that run already taken
+  int ri = 0, rp = 0;
+  struct Chunk {
+    const F *xf, *yf;        // component runs
+    const float *xp, *yp;    // the pad run
+    const float *w;
+    int cnt, pad;
+    int sh;                  // lane group of the chunk's first pair: its index in the whole list, mod G
+  };
+  auto run_len = [&](int r) { return r == 0 ? rn0 : r == 1 ? rn1 : r == 2 ? rn2 : r == 3 ? rn3 : rn4; };
+  auto next = [&](Chunk &c) -> bool {
+    while (ri < 5 && rp >= run_len(ri)) {
+      ++ri;
+      rp = 0;
+    }
+    if (ri >= 5) return false;
+    const int len = run_len(ri);
+    const int cnt = len - rp < C ? len - rp : C;
+    const bool isa = ri < 2;
+    const int64_t c0 = (ri == 0 ? (int64_t)off_a : ri == 1 ? 0 : ri == 2 ? (int64_t)off_f : ri == 3 ? 0 : padc) + rp;
+    const Arena &ar = isa ? a.act : a.frz;
+    c.xf = ar.U<F>() + c0 * dk;
+    c.yf = ar.V<F>() + c0 * dv;
+    c.xp = a.pk + c0 * dk;
+    c.yp = a.pw + c0 * dv;
+    c.w = ri == 4 ? a.pc + c0 : ar.s + c0;
+    c.cnt = cnt;
+    c.pad = ri == 4;
+    const int gs = (ri == 0 ? 0 : ri == 1 ? na0 : ri == 2 ? ra : ri == 3 ? ra + nf0 : rr) + rp;
+    c.sh = gs & (G - 1);
+    rp += cnt;
+    return true;
+  };
+  // Pair i of the whole list is always reduced by lane group i mod G, in list order, whatever the
+  // runs: each group's sum, and so the result, does not depend on where the ring wraps.  In a
+  // chunk starting at list index gs, group g takes the chunk's pairs p = u * G + ((g - gs) mod G).
+  auto slot = [&](const Chunk &c, int u) -> uint32_t { return (uint32_t)(u * G + ((grp - c.sh) & (G - 1))); };
+  // the pair of unroll slot u, clamped into the chunk's run
+  auto load = [&](const Chunk &c, float4 (&x)[UN], float4 (&y)[UN], float (&wt)[UN]) {
 #pragma unroll
-      for (int u = 0; u < UN; ++u) {
-        const int iu = i0 + u * G + grp;
-        ld(iu < ie ? iu : ie - 1, x[u], y[u], wt[u]);  // clamped pair (ie > ib here); its weight is masked at use
+    for (int u = 0; u < UN; ++u) {
+      const uint32_t pc = min(slot(c, u), (uint32_t)(c.cnt - 1));
+      const uint32_t ox = pc * (uint32_t)dk + 4u * (uint32_t)colk, oy = pc * (uint32_t)dv + 4u * (uint32_t)colv;
+      if (std::is_same<F, float>::value) {
+        const float *xb = c.pad ? c.xp : reinterpret_cast<const float *>(c.xf);
+        const float *yb = c.pad ? c.yp : reinterpret_cast<const float *>(c.yf);
+        x[u] = ld4nt(xb + ox);
+        y[u] = ld4nt(yb + oy);
+      } else if (c.pad) {
+        x[u] = ld4nt(c.xp + ox);
+        y[u] = ld4nt(c.yp + oy);
+      } else {
+        x[u] = ldf4nt(c.xf + ox);
+        y[u] = ldf4nt(c.yf + oy);
       }
-    };
-    auto reduce = [&](const float4 (&x)[UN], const float4 (&y)[UN], const float (&wt)[UN], int i0) {
-#pragma unroll
-      for (int u = 0; u < UN; ++u) {
-        const float wu = (i0 + u * G + grp < ie) ? wt[u] : 0.f;
-        const float cq = group_sum<P>(dot4(x[u], qs)) * wu;
-        acc = fma4(cq, y[u], acc);
-        if (delta) {
-          const float ck = group_sum<P>(dot4(x[u], ks)) * wu;
-          acck = fma4(ck, y[u], acck);
-        }
-      }
-    };
-    constexpr int C = G * UN;
-    if (ib < ie) load(xA, yA, wA, ib);
-    for (int i0 = ib; i0 < ie; i0 += 2 * C) {
-      if (i0 + C < ie) load(xB, yB, wB, i0 + C);
-      reduce(xA, yA, wA, i0);
-      if (i0 + 2 * C < ie) load(xA, yA, wA, i0 + 2 * C);
-      if (i0 + C < ie) reduce(xB, yB, wB, i0 + C);
+      wt[u] = ldnt(c.w + pc);
     }
   };
-  // clamped lanes: q4, k4 are 0 off the key lanes and lanes off the value range are never stored
-  auto ld_pad = [&](int i, float4 &x, float4 &y, float &w) {
-    const int64_t c = pad0 + i;
-    x = ld4nt(a.pk + c * dk + 4 * colk);
-    y = ld4nt(a.pw + c * dv + 4 * colv);
-    w = ldnt(a.pc + c);
-  };
-  if constexpr (std::is_same<F, float>::value) {
-    // one list: active, frozen and pad pairs share the chunks
-    stream(0, T, [&](int i, float4 &x, float4 &y, float &w) {
-      const float *xp, *yp, *wp;
-      int64_t c;
-      if (i < ra) {
-        c = wrap(off_a + i, a.act.cap);
-        xp = a.act.U<float>(); yp = a.act.V<float>(); wp = a.act.s;
-      } else if (i < rr) {
-        c = wrap(off_f + (i - ra), a.frz.cap);
-        xp = a.frz.U<float>(); yp = a.frz.V<float>(); wp = a.frz.s;
-      } else {
-        c = pad0 + i;
-        xp = a.pk; yp = a.pw; wp = a.pc;
+  auto reduce = [&](const Chunk &c, const float4 (&x)[UN], const float4 (&y)[UN], const float (&wt)[UN]) {
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const float wu = (slot(c, u) < (uint32_t)c.cnt) ? wt[u] : 0.f;  // the clamped pairs weigh nothing
+      const float cq = group_sum<P>(dot4(x[u], qs)) * wu;
+      acc = fma4(cq, y[u], acc);
+      if (delta) {
+        const float ck = group_sum<P>(dot4(x[u], ks)) * wu;
+        acck = fma4(ck, y[u], acck);
       }
-      x = ld4nt(xp + c * dk + 4 * colk);
-      y = ld4nt(yp + c * dv + 4 * colv);
-      w = ldnt(wp + c);
-    });
-  } else {
-    // fp16 components, then the fp32 pad
-    stream(0, rr, [&](int i, float4 &x, float4 &y, float &w) {
-      const bool act = i < ra;
-      const int64_t c = act ? wrap(off_a + i, a.act.cap) : wrap(off_f + (i - ra), a.frz.cap);
-      const Arena &ar = act ? a.act : a.frz;
-      x = ldf4nt(ar.U<F>() + c * dk + 4 * colk);
-      y = ldf4nt(ar.V<F>() + c * dv + 4 * colv);
-      w = ldnt(ar.s + c);
-    });
-    stream(rr, T, ld_pad);
+    }
+  };
+  // double-buffered: the next chunk's loads are in flight while the current one is reduced
+  {
+    float4 xA[UN], yA[UN], xB[UN], yB[UN];
+    float wA[UN], wB[UN];
+    Chunk cA, cB;
+    bool hA = next(cA);
+    if (hA) load(cA, xA, yA, wA);
+    while (hA) {
+      const bool hB = next(cB);
+      if (hB) load(cB, xB, yB, wB);
+      reduce(cA, xA, yA, wA);
+      if (!hB) break;
+      hA = next(cA);
+      if (hA) load(cA, xA, yA, wA);
+      reduce(cB, xB, yB, wB);
+    }
   }
   acc = cross_group_sum4<P>(acc);
   const float4 pq = DIAG ? acc : scale4(gamma, acc);
@@ -737,7 +769,8 @@ __global__ __launch_bounds__(256) void k_dense_plain(DenseArgs a) {
 
 template <bool RO, bool AD, typename F, bool DG>
 hipError_t decode_factored_p(const DecodeArgs &a, int P, hipStream_t st) {
-  const dim3 grid((unsigned)((a.N + 3) / 4)), block(256);  // a.N: upper bound of the list length
+  // a.N: upper bound of the list length
+  const dim3 grid((unsigned)((a.N + kFactWaves - 1) / kFactWaves)), block(64 * kFactWaves);
   switch (P) {
     case 1: hipLaunchKernelGGL((k_decode_factored<1, 1, RO, AD, F, DG>), grid, block, 0, st, a); break;
     case 2: hipLaunchKernelGGL((k_decode_factored<2, 1, RO, AD, F, DG>), grid, block, 0, st, a); break;

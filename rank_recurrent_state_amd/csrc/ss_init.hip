@@ -246,13 +246,15 @@ __global__ __launch_bounds__(256) void k_rsvd(RsvdArgs a) {
 
 }  // namespace
 
+// the residual in LDS when it fits beside the kernel's 33 KB of static LDS
+bool rsvd_residual_in_lds(int dk, int dv) { return sizeof(float) * (size_t)dk * (dv + 1) <= 120 * 1024; }
+
 hipError_t launch_rsvd_init(const RsvdArgs &a, hipStream_t st) {
   if (a.n <= 0) return hipSuccess;
   const int nk = a.dk <= 64 ? 1 : a.dk <= 128 ? 2 : 4, nv = a.dv <= 64 ? 1 : a.dv <= 128 ? 2 : 4;
   const dim3 g((unsigned)a.n), b(256);
-  // the residual in LDS when it fits beside the kernel's 33 KB of static LDS
   const size_t sh = sizeof(float) * (size_t)a.dk * (a.dv + 1);
-  const bool lds = sh <= 120 * 1024;
+  const bool lds = rsvd_residual_in_lds(a.dk, a.dv);
 #define SS_RSVD(K, V)                                                                        \
   if (nk == K && nv == V) {                                                                  \
     if (lds) hipLaunchKernelGGL((k_rsvd<K, V, true>), g, b, sh, st, a);                      \

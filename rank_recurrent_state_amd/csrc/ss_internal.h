@@ -64,7 +64,8 @@ enum Counter : int {
   C_FACT0 = 6,         // length of the factored-state list
   C_FACT1 = 7,         // length of its scratch copy while it is pruned
   C_MAT_BASE = 8,      // first dense slot of the states a materialization places
-  C_N = 9
+  C_JACOBI_LIMIT = 9,  // compactions whose Jacobi SVD still rotated in its last allowed sweep
+  C_N = 10
 };
 
 // 16-byte record of a dense slot.  packed: n << 16 | flags << 24, as Meta.
@@ -252,6 +253,8 @@ struct RsvdArgs {
   int32_t *rank;       // [n]
 };
 hipError_t launch_rsvd_init(const RsvdArgs &a, hipStream_t st);
+// whether a d_k x d_v residual fits the initialization kernel's LDS (else it needs a workspace)
+bool rsvd_residual_in_lds(int dk, int dv);
 
 // consolidation of the frozen parts of a group's factored states (one workgroup each, in place)
 struct ConsolidateArgs {
@@ -288,6 +291,17 @@ struct InstallArgs {
   uint32_t *installed;         // states installed (device counter)
 };
 hipError_t launch_cons_install(const InstallArgs &a, hipStream_t st);
+// host-core consolidation: the frozen parts the snapshot names, copied into staging for download
+struct GatherArgs {
+  int dk, dv, fmax;
+  int32_t n_members;
+  const Meta *snap;
+  Arena act, frz;
+  float *st_u, *st_v, *st_s;   // [n_members][fmax][d_k], [.][fmax][d_v], [.][fmax]
+  int32_t *st_cnt;             // [n_members] frozen count copied (0: left alone)
+  float *st_s0;                // [n_members] sigma_0 of the state
+};
+hipError_t launch_cons_gather(const GatherArgs &a, hipStream_t st);
 
 // how a state is decoded
 enum DecodeKind : int { KIND_FACTORED = 0, KIND_DENSE_BUFFERED = 1, KIND_DENSE_PLAIN = 2 };

@@ -165,7 +165,9 @@ __device__ __forceinline__ void cgs2_pair(float (&u)[kMaxM][NS], float (&v)[kMax
 // rotation zeroes the pair's inner product: zeta = (|y|^2 - |x|^2) / (2 x.y),
 // t = sign(zeta) / (|zeta| + sqrt(1 + zeta^2)), c = 1 / sqrt(1 + t^2), s = c t,
 // with the hardware reciprocal and reciprocal square root (about 1 ulp).
-__device__ inline int jacobi16(float *Cm, float *Vh, int m, int lane) {
+// *limit (when given) is set if the last allowed sweep still rotated.
+__device__ inline int jacobi16(float *Cm, float *Vh, int m, int lane, bool *limit = nullptr) {
+  if (limit) *limit = false;
   const int M = (m + 1) & ~1;
   if (M < 2) return 0;
   const int np = M >> 1, rounds = M - 1;
@@ -213,6 +215,7 @@ __device__ inline int jacobi16(float *Cm, float *Vh, int m, int lane) {
       if (p != 0) cj = (cj + 1 == M - 1) ? 0 : cj + 1;
     }
     if (!any) break;
+    if (limit && sweep == kMaxSweeps) *limit = true;
   }
   return sweep;
 }

@@ -14,15 +14,19 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <deque>
 #include <cstdio>
 #include <cstring>
 #include <limits>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "../../include/sinkstate.h"
+#include "ss_host_cons.h"
 #include "ss_internal.h"
 
 namespace {
@@ -49,6 +53,7 @@ struct ss_pool {
   std::vector<int32_t> group_offset;
   std::vector<int64_t> group_start, group_size;
   std::vector<int32_t> members_host;  // state ids grouped by compaction group
+  std::vector<float> eps_host;        // per state epsilon (host copy)
   int64_t cap_d = 0;
   int64_t dense_upper = 0;
   // device memory
@@ -105,10 +110,25 @@ struct ss_pool {
   int64_t cons_seq = 0, consolidate_calls = 0;
   // asynchronous consolidation: one group at a time on a caller's second stream, results staged and
   // installed by ss_consolidate_poll on the pool's stream; stale once the group compacts meanwhile
+  std::vector<char> cons_dropped;  // per group: its last asynchronous result was dropped as stale
   struct ConsAsync {
     bool inflight = false, stale = false;
     int group = -1;
     hipEvent_t snap_ev = nullptr, done_ev = nullptr;
+    // the host-core form: the library's own stream for the gather, the download and the upload;
+    // read_ev: the rings have been read (a re-pack waits for it); dl_ev: the download is done;
+    // the host worker runs the SVDs, enqueues the upload and records done_ev
+    bool host = false;
+    hipStream_t own_side = nullptr;
+    hipEvent_t read_ev = nullptr, dl_ev = nullptr;
+    float *st_s0 = nullptr;
+    float *h_u = nullptr, *h_v = nullptr, *h_s = nullptr, *h_s0 = nullptr, *h_eps = nullptr;
+    int32_t *h_cnt = nullptr;
+    int64_t h_members = 0;
+    std::thread worker;
+    std::atomic<int> hstate{0};  // 0 idle, 1 running, 2 done, 3 failed
+    std::string herr;
+    double host_ms = 0.0;        // wall time of the host SVDs of the last job
     ss::Meta *snap = nullptr;
     float *st_u = nullptr, *st_v = nullptr, *st_s = nullptr;
     int32_t *st_cnt = nullptr;
@@ -362,7 +382,7 @@ ss_status ring_repack(ss_pool *p, int first, const int64_t (&newcap)[2], hipStre
                                     : hip_fail(e, "ring repack");
   }
   if (p->ca.inflight) {  // an asynchronous consolidation may still read the old rings
-    e = hipEventSynchronize(p->ca.done_ev);
+    e = hipEventSynchronize(p->ca.host ? p->ca.read_ev : p->ca.done_ev);
     if (e != hipSuccess) {
       for (int R = 0; R < 2; ++R) (void)hipFree(blk[R]);
       return hip_fail(e, "ring repack: waiting for the consolidation");
@@ -485,7 +505,10 @@ const char *ss_status_string(ss_status st) {
 
 const char *ss_last_error(void) { return g_last_error.c_str(); }
 
-ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipStream_t stream, ss_pool **out) {
+// dense_dev: device [N][d_k][d_v] holding the S of the states init->dense_mask marks (instead of
+// the host array init->dense); read in place, never copied to the host
+static ss_status pool_create(const ss_pool_desc *d, const ss_init *init, const float *dense_dev, hipStream_t stream,
+                             ss_pool **out) {
   if (!out) return fail(SS_ERR_ARG, "out is NULL");
   *out = nullptr;
   if (!d) return fail(SS_ERR_ARG, "desc is NULL");
@@ -558,7 +581,7 @@ ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipSt
       ++n_given;
       if (!d->force_dense) ++n_dense0;  // (force_dense already counts every state)
     }
-    if (n_given > 0 && !init->dense) return fail(SS_ERR_ARG, "dense is required when dense_mask marks states");
+    if (n_given > 0 && !init->dense && !dense_dev) return fail(SS_ERR_ARG, "dense is required when dense_mask marks states");
     if (!off && !d->force_dense) n_dense0 = n_given;
   }
   auto given = [&](int64_t s) { return dmask && dmask[s]; };
@@ -624,7 +647,8 @@ ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipSt
       if (cap_ring[R] >= (int64_t)INT32_MAX) return fail(SS_ERR_CAPACITY, "too many components for 32-bit offsets");
     }
   }
-  std::vector<float> epsv(N);
+  std::vector<float> &epsv = p->eps_host;
+  epsv.assign(N, 0.f);
   for (int64_t s = 0; s < N; ++s) epsv[s] = d->eps ? d->eps[s] : d->eps_default;
   std::vector<uint8_t> rulev(N, 0);
   if (d->rule) std::memcpy(rulev.data(), d->rule, N);
@@ -701,11 +725,17 @@ ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipSt
   if (n_given > 0) {
     talloc((void **)&d_mask, N);
     talloc((void **)&d_didx, N * sizeof(int64_t));
-    talloc((void **)&d_dsrc, (size_t)n_given * dk * dv * sizeof(float));
     didx.assign(N, -1);
-    int64_t k = 0;
-    for (int64_t s = 0; s < N; ++s)
-      if (dmask[s]) didx[s] = k++;
+    if (dense_dev) {  // read where it is: state s at row s
+      d_dsrc = const_cast<float *>(dense_dev);
+      for (int64_t s = 0; s < N; ++s)
+        if (dmask[s]) didx[s] = s;
+    } else {
+      talloc((void **)&d_dsrc, (size_t)n_given * dk * dv * sizeof(float));
+      int64_t k = 0;
+      for (int64_t s = 0; s < N; ++s)
+        if (dmask[s]) didx[s] = k++;
+    }
   }
   if (factored)
     for (int R = 0; R < 2; ++R) talloc((void **)&d_pos[R], N * sizeof(int64_t));
@@ -733,7 +763,9 @@ ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipSt
     up(d_mask, dmask, N);
     up(d_didx, didx.data(), N * sizeof(int64_t));
     const size_t per = (size_t)dk * dv;
-    if (n_given == N) {
+    if (dense_dev) {
+      // nothing to upload
+    } else if (n_given == N) {
       up(d_dsrc, init->dense, sizeof(float) * per * N);
     } else {  // the given states' S, packed in state order (the upload is synchronized below)
       dense_pack.resize(per * n_given);
@@ -795,11 +827,91 @@ ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipSt
   return SS_OK;
 }
 
+ss_status ss_state_pool_create(const ss_pool_desc *d, const ss_init *init, hipStream_t stream, ss_pool **out) {
+  return pool_create(d, init, nullptr, stream, out);
+}
+
+ss_status ss_state_pool_create_from_dense(const ss_pool_desc *d, const float *S, const float *u, const float *v,
+                                          const float *sigma, const int32_t *rank, int32_t max_rank,
+                                          hipStream_t stream, ss_pool **out) {
+  if (!out) return fail(SS_ERR_ARG, "out is NULL");
+  *out = nullptr;
+  if (!d) return fail(SS_ERR_ARG, "desc is NULL");
+  const int64_t N = d->n_states;
+  if (N < 1) return fail(SS_ERR_ARG, "n_states must be >= 1");
+  if (d->d_k < 4 || d->d_v < 4 || d->d_k > 256 || d->d_v > 256 || (d->d_k & 3) || (d->d_v & 3))
+    return fail(SS_ERR_SHAPE, "d_k and d_v must be multiples of 4 in [4, 256]");
+  const int dk = d->d_k, dv = d->d_v;
+  if (max_rank < 1 || max_rank > std::min(dk, dv)) return fail(SS_ERR_ARG, "max_rank must be in [1, min(d_k, d_v)]");
+  if (!S || !u || !v || !sigma || !rank) return fail(SS_ERR_ARG, "null pointer");
+  if (d->force_dense) return fail(SS_ERR_ARG, "a pool built from factors cannot be force_dense");
+  const int L = d->dense_rank_limit < 0 ? ss_dense_rank_limit(dk, dv) : d->dense_rank_limit;
+  const size_t M = (size_t)max_rank;
+  std::vector<int32_t> rk(N);
+  std::vector<float> hs((size_t)N * M), hu, hv;
+  try {
+    hu.resize((size_t)N * M * dk);
+    hv.resize((size_t)N * M * dv);
+  } catch (const std::bad_alloc &) {
+    return fail(SS_ERR_OOM, "host allocation failed");
+  }
+  hipError_t e = hipMemcpyAsync(rk.data(), rank, N * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(hs.data(), sigma, hs.size() * sizeof(float), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(hu.data(), u, hu.size() * sizeof(float), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(hv.data(), v, hv.size() * sizeof(float), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "reading the initialization results");
+  // the dense fallback ([SS] 4.4 "Memory layout": decided once the state is factored): rank > L
+  // keeps the state's exact S; the others keep their components in descending sigma (the blocks
+  // are each descending, not across blocks; ties keep block order)
+  std::vector<int64_t> off(N + 1, 0);
+  std::vector<uint8_t> dmask(N, 0);
+  int64_t n_dense = 0;
+  for (int64_t s = 0; s < N; ++s) {
+    if (rk[s] < 0 || rk[s] > max_rank) return fail(SS_ERR_ARG, "rank out of [0, max_rank]");
+    const bool dn = rk[s] > L;
+    dmask[s] = dn ? 1 : 0;
+    n_dense += dn ? 1 : 0;
+    off[s + 1] = off[s] + (dn ? 0 : rk[s]);
+  }
+  std::vector<float> cu((size_t)off[N] * dk), cv((size_t)off[N] * dv), cs((size_t)off[N]);
+  std::vector<int> ord;
+  for (int64_t s = 0; s < N; ++s) {
+    if (dmask[s]) continue;
+    const int R = rk[s];
+    const float *sg = hs.data() + (size_t)s * M;
+    ord.resize(R);
+    for (int i = 0; i < R; ++i) ord[i] = i;
+    std::stable_sort(ord.begin(), ord.end(), [&](int a, int b) { return sg[a] > sg[b]; });
+    for (int i = 0; i < R; ++i) {
+      const size_t src = (size_t)s * M + ord[i], dst = (size_t)off[s] + i;
+      std::memcpy(cu.data() + dst * dk, hu.data() + src * dk, dk * sizeof(float));
+      std::memcpy(cv.data() + dst * dv, hv.data() + src * dv, dv * sizeof(float));
+      cs[dst] = sg[ord[i]];
+    }
+  }
+  ss_init in{};
+  in.comp_off = off.data();
+  in.u = cu.data();
+  in.v = cv.data();
+  in.sigma = cs.data();
+  in.dense_mask = n_dense ? dmask.data() : nullptr;
+  in.dense = nullptr;
+  return pool_create(d, &in, S, stream, out);
+}
+
 ss_status ss_state_pool_destroy(ss_pool *p) {
   if (!p) return SS_OK;
+  if (p->ca.worker.joinable()) p->ca.worker.join();
   (void)hipDeviceSynchronize();
   if (p->ca.snap_ev) (void)hipEventDestroy(p->ca.snap_ev);
   if (p->ca.done_ev) (void)hipEventDestroy(p->ca.done_ev);
+  if (p->ca.read_ev) (void)hipEventDestroy(p->ca.read_ev);
+  if (p->ca.dl_ev) (void)hipEventDestroy(p->ca.dl_ev);
+  if (p->ca.own_side) (void)hipStreamDestroy(p->ca.own_side);
+  for (void *h : {(void *)p->ca.h_u, (void *)p->ca.h_v, (void *)p->ca.h_s, (void *)p->ca.h_s0, (void *)p->ca.h_eps,
+                  (void *)p->ca.h_cnt})
+    if (h) (void)hipHostFree(h);
   free_all(p);
   delete p;
   return SS_OK;
@@ -838,6 +950,13 @@ static hipError_t enqueue_decode(ss_pool *p, const float *q, const float *k, con
 // Enqueue the compaction of group g (the ring space must have been checked): fold the pads of its
 // dense members, compact its factored members into a new ring segment, promote.  with_dense:
 // whether dense members may exist.
+
+// Largest frozen count a factored state of the pool can hold: with promotion a state keeps at
+// most L components, r of them active; without, the per-state frozen capacity.
+static int frozen_max(const ss_pool *p) {
+  return p->promote ? std::max(0, std::min(p->fcap, p->L - p->r)) : p->fcap;
+}
+
 static hipError_t enqueue_compact_group(ss_pool *p, int g, bool with_dense, bool timing, hipStream_t stream,
                                         const uint8_t *sel = nullptr) {
   hipError_t e = ss::launch_ring_begin(p->ring, p->ring + 1, p->seg, p->seg + 2 * p->G, p->G, p->act.cap, p->frz.cap,
@@ -1001,9 +1120,10 @@ ss_status ss_compact_ids(ss_pool *p, const int32_t *ids, int64_t n, hipStream_t 
   return SS_OK;
 }
 
-ss_status ss_rsvd_init(const float *S, int64_t n, int32_t d_k, int32_t d_v, int32_t block, int32_t n_blocks,
-                       int32_t iters, const float *omega, const float *eps, int32_t max_rank, float *work, float *u,
-                       float *v, float *sigma, int32_t *rank, hipStream_t stream) {
+// host-side checks shared by both initialization entry points (before any HIP call)
+static ss_status rsvd_check(const float *S, int64_t n, int32_t d_k, int32_t d_v, int32_t block, int32_t n_blocks,
+                            int32_t iters, const float *omega, const float *eps, int32_t max_rank, const void *u,
+                            const void *v, const void *sigma, const void *rank) {
   if (n < 0) return fail(SS_ERR_ARG, "n must be >= 0");
   if (d_k < 4 || d_v < 4 || d_k > 256 || d_v > 256 || (d_k & 3) || (d_v & 3))
     return fail(SS_ERR_SHAPE, "d_k and d_v must be multiples of 4 in [4, 256]");
@@ -1013,8 +1133,14 @@ ss_status ss_rsvd_init(const float *S, int64_t n, int32_t d_k, int32_t d_v, int3
   if (max_rank < 1 || max_rank > std::min(d_k, d_v) || (int64_t)max_rank > (int64_t)n_blocks * block)
     return fail(SS_ERR_ARG, "max_rank must be in [1, min(d_k, d_v, n_blocks * block)]");
   if (n == 0) return SS_OK;
-  if (!S || !omega || !eps || !work || !u || !v || !sigma || !rank) return fail(SS_ERR_ARG, "null pointer");
+  if (!S || !omega || !eps || !u || !v || !sigma || !rank) return fail(SS_ERR_ARG, "null pointer");
   if (n > (int64_t)INT32_MAX) return fail(SS_ERR_ARG, "too many states for one launch");
+  return SS_OK;
+}
+
+static ss_status rsvd_launch(const float *S, int64_t n, int32_t d_k, int32_t d_v, int32_t block, int32_t n_blocks,
+                             int32_t iters, const float *omega, const float *eps, int32_t max_rank, float *work,
+                             float *u, float *v, float *sigma, int32_t *rank, hipStream_t stream) {
   ss::RsvdArgs a{};
   a.n = n; a.dk = d_k; a.dv = d_v; a.b = block; a.nb = n_blocks; a.iters = iters; a.max_rank = max_rank;
   a.S = S; a.omega = omega; a.eps = eps; a.work = work; a.u = u; a.v = v; a.sigma = sigma; a.rank = rank;
@@ -1022,10 +1148,13 @@ ss_status ss_rsvd_init(const float *S, int64_t n, int32_t d_k, int32_t d_v, int3
   return e == hipSuccess ? SS_OK : hip_fail(e, "randomized SVD launch");
 }
 
-// Largest frozen count a factored state of the pool can hold: with promotion a state keeps at
-// most L components, r of them active; without, the per-state frozen capacity.
-static int frozen_max(const ss_pool *p) {
-  return p->promote ? std::max(0, std::min(p->fcap, p->L - p->r)) : p->fcap;
+ss_status ss_rsvd_init(const float *S, int64_t n, int32_t d_k, int32_t d_v, int32_t block, int32_t n_blocks,
+                       int32_t iters, const float *omega, const float *eps, int32_t max_rank, float *work, float *u,
+                       float *v, float *sigma, int32_t *rank, hipStream_t stream) {
+  ss_status st = rsvd_check(S, n, d_k, d_v, block, n_blocks, iters, omega, eps, max_rank, u, v, sigma, rank);
+  if (st != SS_OK || n == 0) return st;
+  if (!work) return fail(SS_ERR_ARG, "null pointer");
+  return rsvd_launch(S, n, d_k, d_v, block, n_blocks, iters, omega, eps, max_rank, work, u, v, sigma, rank, stream);
 }
 
 static hipError_t enqueue_consolidate_group(ss_pool *p, int g, hipStream_t stream) {
@@ -1096,6 +1225,62 @@ ss_status ss_consolidate_next(ss_pool *p, int32_t max_groups, int32_t *out, int3
   return SS_OK;
 }
 
+// Queue head of the asynchronous forms ([SS] 4.3, Figure 7(b)): among the groups waiting (compacted
+// since their last consolidation), those whose last result was dropped as stale first, then the
+// least recently consolidated (never consolidated first), then the lowest id.  group >= 0 selects it.
+static int async_pick(ss_pool *p, int group) {
+  if ((int)p->cons_dropped.size() < p->G) p->cons_dropped.assign(p->G, 0);
+  if (group >= 0) return group;
+  int g = -1;
+  for (int h = 0; h < p->G; ++h) {
+    if (!p->cons_wait[h]) continue;
+    if (g < 0 || p->cons_dropped[h] > p->cons_dropped[g] ||
+        (p->cons_dropped[h] == p->cons_dropped[g] && p->cons_last[h] < p->cons_last[g]))
+      g = h;
+  }
+  return g;
+}
+
+// Staging of the asynchronous forms, for the largest group (allocated at the first call; the host
+// form adds pinned host buffers of the same shape, sigma_0 and epsilon per member, and its own
+// stream and events)
+static hipError_t async_staging(ss_pool *p, int fmax, bool host) {
+  hipError_t e = hipSuccess;
+  int64_t gmax = 0;
+  for (int h = 0; h < p->G; ++h) gmax = std::max<int64_t>(gmax, p->group_size[h]);
+  if (p->ca.cap_members < gmax || p->ca.fmax < fmax) {
+    if (p->ca.cap_members) return hipErrorInvalidValue;
+    e = dalloc(p, &p->ca.snap, (size_t)gmax);
+    if (e == hipSuccess) e = dalloc(p, &p->ca.st_u, (size_t)gmax * fmax * p->dk);
+    if (e == hipSuccess) e = dalloc(p, &p->ca.st_v, (size_t)gmax * fmax * p->dv);
+    if (e == hipSuccess) e = dalloc(p, &p->ca.st_s, (size_t)gmax * fmax);
+    if (e == hipSuccess) e = dalloc(p, &p->ca.st_cnt, (size_t)gmax);
+    if (e == hipSuccess) e = dalloc(p, &p->ca.installed, 1);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ca.snap_ev, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ca.done_ev, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+    p->ca.cap_members = gmax;
+    p->ca.fmax = fmax;
+  }
+  if (host && !p->ca.own_side) {
+    const size_t rows = (size_t)gmax * fmax;
+    auto pin = [&](void **q, size_t bytes) {
+      if (e == hipSuccess) e = hipHostMalloc(q, bytes, hipHostMallocDefault);
+    };
+    e = dalloc(p, &p->ca.st_s0, (size_t)gmax);
+    pin((void **)&p->ca.h_u, rows * p->dk * sizeof(float));
+    pin((void **)&p->ca.h_v, rows * p->dv * sizeof(float));
+    pin((void **)&p->ca.h_s, rows * sizeof(float));
+    pin((void **)&p->ca.h_cnt, (size_t)gmax * sizeof(int32_t));
+    pin((void **)&p->ca.h_s0, (size_t)gmax * sizeof(float));
+    pin((void **)&p->ca.h_eps, (size_t)gmax * sizeof(float));
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ca.read_ev, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ca.dl_ev, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&p->ca.own_side, hipStreamNonBlocking);
+  }
+  return e;
+}
+
 ss_status ss_consolidate_async(ss_pool *p, int32_t group, hipStream_t stream, hipStream_t side, int32_t *launched) {
   if (!p || !launched) return fail(SS_ERR_ARG, "bad arguments");
   *launched = -1;
@@ -1107,39 +1292,13 @@ ss_status ss_consolidate_async(ss_pool *p, int32_t group, hipStream_t stream, hi
   const int fmax = frozen_max(p);
   if (ss::consolidate_lds_bytes(p->dk, p->dv, fmax, false) > ss::kConsolidateLdsMax)
     return fail(SS_ERR_SHAPE, "the pool's largest frozen part does not fit the consolidation kernel's LDS");
-  int g = group;
-  if (g < 0) {
-    // among the waiting groups, the one compacted most recently: its result has the longest time
-    // to land before the group's next compaction makes it stale; then least recently
-    // consolidated, then lowest id
-    if ((int)p->ca.last_compact.size() < p->G) p->ca.last_compact.assign(p->G, -1);
-    const std::vector<int64_t> &lc = p->ca.last_compact;
-    for (int h = 0; h < p->G; ++h) {
-      if (!p->cons_wait[h]) continue;
-      if (g < 0 || lc[h] > lc[g] || (lc[h] == lc[g] && p->cons_last[h] < p->cons_last[g])) g = h;
-    }
-    if (g < 0) return SS_OK;
-  }
+  const int g = async_pick(p, group);
+  if (g < 0) return SS_OK;
   p->cons_wait[g] = 0;
   p->cons_last[g] = p->cons_seq++;
   if (p->group_size[g] == 0 || fmax == 0) return SS_OK;
-  hipError_t e = hipSuccess;
-  int64_t gmax = 0;
-  for (int h = 0; h < p->G; ++h) gmax = std::max<int64_t>(gmax, p->group_size[h]);
-  if (p->ca.cap_members < gmax || p->ca.fmax < fmax) {  // staging for the largest group (first call)
-    if (p->ca.cap_members) return fail(SS_ERR_STATE, "staging shape changed");
-    e = dalloc(p, &p->ca.snap, (size_t)gmax);
-    if (e == hipSuccess) e = dalloc(p, &p->ca.st_u, (size_t)gmax * fmax * p->dk);
-    if (e == hipSuccess) e = dalloc(p, &p->ca.st_v, (size_t)gmax * fmax * p->dv);
-    if (e == hipSuccess) e = dalloc(p, &p->ca.st_s, (size_t)gmax * fmax);
-    if (e == hipSuccess) e = dalloc(p, &p->ca.st_cnt, (size_t)gmax);
-    if (e == hipSuccess) e = dalloc(p, &p->ca.installed, 1);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ca.snap_ev, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ca.done_ev, hipEventDisableTiming);
-    if (e != hipSuccess) return e == hipErrorOutOfMemory ? fail(SS_ERR_OOM, "consolidation staging") : hip_fail(e, "consolidation staging");
-    p->ca.cap_members = gmax;
-    p->ca.fmax = fmax;
-  }
+  hipError_t e = async_staging(p, fmax, false);
+  if (e != hipSuccess) return e == hipErrorOutOfMemory ? fail(SS_ERR_OOM, "consolidation staging") : hip_fail(e, "consolidation staging");
   const int32_t n = (int32_t)p->group_size[g];
   const int32_t *members = p->members + p->group_start[g];
   e = ss::launch_cons_snapshot(p->meta, members, n, p->ca.snap, stream);
@@ -1158,6 +1317,96 @@ ss_status ss_consolidate_async(ss_pool *p, int32_t group, hipStream_t stream, hi
   if (e == hipSuccess) e = hipEventRecord(p->ca.done_ev, side);
   if (e != hipSuccess) return hip_fail(e, "asynchronous consolidation launch");
   p->ca.inflight = true;
+  p->ca.host = false;
+  p->ca.stale = false;
+  p->ca.group = g;
+  p->ca.launched++;
+  *launched = g;
+  return SS_OK;
+}
+
+ss_status ss_host_consolidate_frozen(int32_t d_k, int32_t d_v, int32_t f, float *u, float *v, float *sigma,
+                                     float sigma0, float eps, int32_t *kept) {
+  if (!kept || f < 0) return fail(SS_ERR_ARG, "bad arguments");
+  if (d_k < 1 || d_v < 1) return fail(SS_ERR_SHAPE, "d_k and d_v must be >= 1");
+  if (f > 0 && (!u || !v || !sigma)) return fail(SS_ERR_ARG, "null pointer");
+  *kept = ss::host_consolidate_one(d_k, d_v, f, u, v, sigma, sigma0, eps);
+  return SS_OK;
+}
+
+ss_status ss_consolidate_host(ss_pool *p, int32_t group, hipStream_t stream, int32_t threads, int32_t *launched) {
+  if (!p || !launched) return fail(SS_ERR_ARG, "bad arguments");
+  *launched = -1;
+  if (threads < 0) return fail(SS_ERR_ARG, "threads must be >= 0");
+  if (p->diag) return fail(SS_ERR_ARG, "consolidation is not available with per-channel decay");
+  ss_status st = poll(p);
+  if (st != SS_OK) return st;
+  if (group >= p->G) return fail(SS_ERR_ARG, "group out of range");
+  if (p->ca.inflight) return fail(SS_ERR_STATE, "an asynchronous consolidation is already in flight");
+  if (p->force_dense) return SS_OK;
+  const int fmax = frozen_max(p);
+  const int g = async_pick(p, group);
+  if (g < 0) return SS_OK;
+  p->cons_wait[g] = 0;
+  p->cons_last[g] = p->cons_seq++;
+  if (p->group_size[g] == 0 || fmax == 0) return SS_OK;
+  hipError_t e = async_staging(p, fmax, true);
+  if (e != hipSuccess) return e == hipErrorOutOfMemory ? fail(SS_ERR_OOM, "consolidation staging") : hip_fail(e, "consolidation staging");
+  const int32_t n = (int32_t)p->group_size[g];
+  const int32_t *members = p->members + p->group_start[g];
+  hipStream_t side = p->ca.own_side;
+  // snapshot of the records on the pool's stream; the side stream copies the frozen parts they
+  // name into staging and downloads them with the states' sigma_0 and epsilon
+  e = ss::launch_cons_snapshot(p->meta, members, n, p->ca.snap, stream);
+  if (e == hipSuccess) e = hipEventRecord(p->ca.snap_ev, stream);
+  if (e == hipSuccess) e = hipStreamWaitEvent(side, p->ca.snap_ev, 0);
+  if (e == hipSuccess) {
+    ss::GatherArgs ga{};
+    ga.dk = p->dk; ga.dv = p->dv; ga.fmax = fmax; ga.n_members = n; ga.snap = p->ca.snap;
+    ga.act = p->act; ga.frz = p->frz; ga.st_u = p->ca.st_u; ga.st_v = p->ca.st_v; ga.st_s = p->ca.st_s;
+    ga.st_cnt = p->ca.st_cnt; ga.st_s0 = p->ca.st_s0;
+    e = ss::launch_cons_gather(ga, side);
+  }
+  if (e == hipSuccess) e = hipEventRecord(p->ca.read_ev, side);
+  const size_t rows = (size_t)n * fmax;
+  auto d2h = [&](void *dst, const void *src, size_t bytes) {
+    if (e == hipSuccess) e = hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, side);
+  };
+  d2h(p->ca.h_u, p->ca.st_u, rows * p->dk * sizeof(float));
+  d2h(p->ca.h_v, p->ca.st_v, rows * p->dv * sizeof(float));
+  d2h(p->ca.h_s, p->ca.st_s, rows * sizeof(float));
+  d2h(p->ca.h_cnt, p->ca.st_cnt, (size_t)n * sizeof(int32_t));
+  d2h(p->ca.h_s0, p->ca.st_s0, (size_t)n * sizeof(float));
+  if (e == hipSuccess) e = hipEventRecord(p->ca.dl_ev, side);
+  if (e != hipSuccess) return hip_fail(e, "host consolidation download");
+  for (int32_t i = 0; i < n; ++i) p->ca.h_eps[i] = p->eps_host[p->members_host[p->group_start[g] + i]];
+  // the host worker: wait for the download, run the SVDs, enqueue the upload and its event
+  const int nt = threads > 0 ? threads : std::max(1, (int)std::thread::hardware_concurrency());
+  p->ca.hstate.store(1);
+  p->ca.herr.clear();
+  const int dk = p->dk, dv = p->dv;
+  p->ca.worker = std::thread([p, n, fmax, nt, dk, dv, side]() {
+    auto &c = p->ca;
+    hipError_t we = hipEventSynchronize(c.dl_ev);
+    if (we == hipSuccess) {
+      const auto t0 = std::chrono::steady_clock::now();
+      ss::host_consolidate_batch(n, dk, dv, fmax, c.h_u, c.h_v, c.h_s, c.h_cnt, c.h_s0, c.h_eps, nt);
+      c.host_ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+      const size_t rows = (size_t)n * fmax;
+      auto h2d = [&](void *dst, const void *src, size_t bytes) {
+        if (we == hipSuccess) we = hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, side);
+      };
+      h2d(c.st_u, c.h_u, rows * dk * sizeof(float));
+      h2d(c.st_v, c.h_v, rows * dv * sizeof(float));
+      h2d(c.st_s, c.h_s, rows * sizeof(float));
+      h2d(c.st_cnt, c.h_cnt, (size_t)n * sizeof(int32_t));
+      if (we == hipSuccess) we = hipEventRecord(c.done_ev, side);
+    }
+    if (we != hipSuccess) c.herr = hipGetErrorString(we);
+    c.hstate.store(we == hipSuccess ? 2 : 3);
+  });
+  p->ca.inflight = true;
+  p->ca.host = true;
   p->ca.stale = false;
   p->ca.group = g;
   p->ca.launched++;
@@ -1171,6 +1420,17 @@ ss_status ss_consolidate_poll(ss_pool *p, int32_t wait, hipStream_t stream, int3
   ss_status st = poll(p);
   if (st != SS_OK) return st;
   if (!p->ca.inflight) return SS_OK;
+  if (p->ca.host) {  // the host worker enqueues the upload and records done_ev when it is through
+    if (!wait && p->ca.hstate.load() == 1) {
+      *state = SS_CONS_RUNNING;
+      return SS_OK;
+    }
+    if (p->ca.worker.joinable()) p->ca.worker.join();
+    if (p->ca.hstate.load() == 3) {
+      p->ca.inflight = false;
+      return fail(SS_ERR_HIP, "host consolidation: " + p->ca.herr);
+    }
+  }
   hipError_t e = wait ? hipEventSynchronize(p->ca.done_ev) : hipEventQuery(p->ca.done_ev);
   if (e == hipErrorNotReady) {
     *state = SS_CONS_RUNNING;
@@ -1180,9 +1440,12 @@ ss_status ss_consolidate_poll(ss_pool *p, int32_t wait, hipStream_t stream, int3
   p->ca.inflight = false;
   if (p->ca.stale) {
     p->ca.discarded++;
+    p->cons_dropped[p->ca.group] = 1;  // retried first ([SS] Figure 7(b))
+    p->cons_wait[p->ca.group] = 1;
     *state = SS_CONS_DISCARDED;
     return SS_OK;
   }
+  p->cons_dropped[p->ca.group] = 0;
   ss::InstallArgs ia{};
   const int g = p->ca.group;
   ia.dk = p->dk; ia.dv = p->dv; ia.fmax = p->ca.fmax; ia.n_members = (int32_t)p->group_size[g];
@@ -1391,6 +1654,7 @@ ss_status ss_pool_stats(ss_pool *p, ss_stats *out, hipStream_t stream) {
   out->decode_bytes = out->decode_bytes_factored + out->decode_bytes_dense;
   out->promotions = ctr[ss::C_PROMOTIONS];
   out->cap_truncations = ctr[ss::C_CAP_TRUNC];
+  out->jacobi_limit_hits = ctr[ss::C_JACOBI_LIMIT];
   if (!p->force_dense) {  // exact ring figures (the stream is idle here)
     ss::Ring ring[2];
     std::vector<unsigned long long> seg(4 * (size_t)p->G);

@@ -61,6 +61,7 @@ class Stats(ctypes.Structure):
         ("kernel_ms", ctypes.c_double * 8), ("kernel_launches", ctypes.c_int64 * 8),
         ("consolidate_calls", ctypes.c_int64), ("consolidate_states", ctypes.c_uint64),
         ("consolidate_flops", ctypes.c_uint64), ("consolidate_removed", ctypes.c_uint64),
+        ("jacobi_limit_hits", ctypes.c_int64),
     ]
 
 
@@ -90,6 +91,9 @@ def load_library():
     lib.ss_consolidate_next.argtypes = [vp, ctypes.c_int32, _c_i32p, _c_i32p, vp]
     lib.ss_consolidate_async.argtypes = [vp, ctypes.c_int32, vp, vp, _c_i32p]
     lib.ss_consolidate_poll.argtypes = [vp, ctypes.c_int32, vp, _c_i32p]
+    lib.ss_consolidate_host.argtypes = [vp, ctypes.c_int32, vp, ctypes.c_int32, _c_i32p]
+    lib.ss_host_consolidate_frozen.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _c_f32p, _c_f32p,
+                                               _c_f32p, ctypes.c_float, ctypes.c_float, _c_i32p]
     lib.ss_schedule_due.argtypes = [vp, ctypes.c_int64, _c_i32p, ctypes.c_int32, _c_i32p]
     lib.ss_state_export.argtypes = [vp, _c_i64p, ctypes.c_int64, vp, ctypes.c_size_t,
                                     ctypes.POINTER(ctypes.c_size_t), vp]
@@ -105,6 +109,9 @@ def load_library():
     lib.ss_rsvd_init.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                  ctypes.c_int32, vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp]
     lib.ss_rsvd_init.restype = ctypes.c_int
+    lib.ss_state_pool_create_from_dense.argtypes = [ctypes.POINTER(PoolDesc)] + [vp] * 5 + [ctypes.c_int32, vp,
+                                                                                         ctypes.POINTER(vp)]
+    lib.ss_state_pool_create_from_dense.restype = ctypes.c_int
     lib.ss_status_string.argtypes = [ctypes.c_int]
     lib.ss_status_string.restype = ctypes.c_char_p
     lib.ss_last_error.restype = ctypes.c_char_p
@@ -184,23 +191,31 @@ class StatePool:
             pass
 
 
+def _desc(n_states, d_k, d_v, pad_slots, r_active, dense_rank_limit, promote_on_compact, max_frozen, force_dense,
+          group_of_state, group_offset, rule, eps, eps_default, dense_capacity, arena_components, factor_fp16,
+          diag_decay):
+    """ss_pool_desc and the host arrays it points to (kept alive by the caller)."""
+    n_groups = 1 if group_offset is None else len(group_offset)
+    g_a, g_p = _arr(group_of_state, np.int32, _c_i32p)
+    o_a, o_p = _arr(group_offset, np.int32, _c_i32p)
+    r_a, r_p = _arr(rule, np.uint8, _c_u8p)
+    e_a, e_p = _arr(eps, np.float32, _c_f32p)
+    desc = PoolDesc(int(n_states), int(d_k), int(d_v), int(pad_slots), int(r_active), int(dense_rank_limit),
+                    int(bool(promote_on_compact)), int(max_frozen), int(bool(force_dense)), int(n_groups),
+                    g_p, o_p, r_p, e_p, float(eps_default), int(dense_capacity),
+                    int(arena_components), int(factor_fp16), int(bool(diag_decay)))
+    return desc, [g_a, o_a, r_a, e_a], n_groups
+
+
 def state_pool_create(n_states, d_k, d_v, pad_slots=8, r_active=8, dense_rank_limit=-1, promote_on_compact=True,
                       max_frozen=0, force_dense=False, group_of_state=None, group_offset=None, rule=None, eps=None,
                       eps_default=0.0, dense_capacity=0, comp_off=None, u=None, v=None, sigma=None,
                       arena_components=0, dense_mask=None, dense=None, factor_fp16=False, diag_decay=False,
                       stream=None) -> StatePool:
     lib = load_library()
-    n_groups = 1 if group_offset is None else len(group_offset)
-    keep = []
-    g_a, g_p = _arr(group_of_state, np.int32, _c_i32p)
-    o_a, o_p = _arr(group_offset, np.int32, _c_i32p)
-    r_a, r_p = _arr(rule, np.uint8, _c_u8p)
-    e_a, e_p = _arr(eps, np.float32, _c_f32p)
-    keep += [g_a, o_a, r_a, e_a]
-    desc = PoolDesc(int(n_states), int(d_k), int(d_v), int(pad_slots), int(r_active), int(dense_rank_limit),
-                    int(bool(promote_on_compact)), int(max_frozen), int(bool(force_dense)), int(n_groups),
-                    g_p, o_p, r_p, e_p, float(eps_default), int(dense_capacity),
-                    int(arena_components), int(factor_fp16), int(bool(diag_decay)))
+    desc, keep, n_groups = _desc(n_states, d_k, d_v, pad_slots, r_active, dense_rank_limit, promote_on_compact,
+                                 max_frozen, force_dense, group_of_state, group_offset, rule, eps, eps_default,
+                                 dense_capacity, arena_components, factor_fp16, diag_decay)
     init = None
     if comp_off is not None or dense_mask is not None:
         c_a, c_p = _arr(comp_off, np.int64, _c_i64p)
@@ -283,36 +298,30 @@ def rsvd_init(S, omega, eps, iters=2, max_rank=None, stream=None):
 
 
 def state_pool_from_dense(S, omega, eps, d_k=None, d_v=None, pad_slots=8, r_active=8, iters=2, rule=None,
-                          **create_kw) -> StatePool:
-    """A pool initialized from dense states after prefill: randomized block SVD of each state on
-    the GPU (rsvd_init), then the dense fallback for states whose rank exceeds L, which are kept
-    as their exact S.  S: (N, d_k, d_v) float32 (host array or CUDA tensor); omega: (N, n_blocks,
-    d_k, block) Gaussian; eps: scalar or (N,).  create_kw go to state_pool_create."""
+                          dense_rank_limit=-1, promote_on_compact=True, max_frozen=0, group_of_state=None,
+                          group_offset=None, dense_capacity=0, arena_components=0, factor_fp16=False,
+                          diag_decay=False, stream=None) -> StatePool:
+    """A pool initialized from dense states after prefill: rsvd_init on the GPU, then
+    ss_state_pool_create_from_dense, where the library applies the dense fallback and orders each
+    state's components.  S: (N, d_k, d_v) float32 (host array or CUDA tensor); omega: (N, n_blocks,
+    d_k, block) Gaussian; eps: scalar or (N,)."""
     St = torch.as_tensor(S, dtype=torch.float32).cuda().contiguous()
     Om = torch.as_tensor(omega, dtype=torch.float32).cuda().contiguous()
     N, dk, dv = St.shape
-    L = create_kw.get("dense_rank_limit", -1)
-    L = dense_rank_limit(dk, dv) if L is None or L < 0 else L
     nb, b = Om.shape[1], Om.shape[3]
     max_rank = min(dk, dv, nb * b)
     eps_a = np.broadcast_to(np.asarray(eps, dtype=np.float32), (N,)).copy()
-    u, v, sg, rk = rsvd_init(St, Om, torch.from_numpy(eps_a).cuda(), iters=iters, max_rank=max_rank)
-    rk = rk.cpu().numpy().astype(np.int64)
-    dense_mask = (rk > L).astype(np.uint8)
-    R = np.where(dense_mask == 1, 0, rk)
-    comp_off = np.concatenate([[0], np.cumsum(R)]).astype(np.int64)
-    # components in descending sigma per state (blocks are each descending, not across blocks)
-    sgh = sg.cpu().numpy()
-    sel = np.concatenate([i * max_rank + np.argsort(-sgh[i, :r], kind="stable") for i, r in enumerate(R)]) \
-        .astype(np.int64) if R.sum() else np.zeros(0, dtype=np.int64)
-    idx = torch.from_numpy(sel).cuda()
-    uu = u.reshape(N * max_rank, dk).index_select(0, idx).cpu().numpy()
-    vv = v.reshape(N * max_rank, dv).index_select(0, idx).cpu().numpy()
-    ss_ = sg.reshape(N * max_rank).index_select(0, idx).cpu().numpy()
-    dense_host = St.cpu().numpy() if dense_mask.any() else None
-    return state_pool_create(N, dk, dv, pad_slots, r_active, rule=rule, eps=eps_a, comp_off=comp_off, u=uu, v=vv,
-                             sigma=ss_, dense_mask=dense_mask if dense_mask.any() else None, dense=dense_host,
-                             **create_kw)
+    u, v, sg, rk = rsvd_init(St, Om, torch.from_numpy(eps_a).cuda(), iters=iters, max_rank=max_rank, stream=stream)
+    desc, keep, n_groups = _desc(N, dk, dv, pad_slots, r_active, dense_rank_limit, promote_on_compact, max_frozen,
+                                 False, group_of_state, group_offset, rule, eps_a, 0.0, dense_capacity,
+                                 arena_components, factor_fp16, diag_decay)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    handle = ctypes.c_void_p()
+    _check(load_library().ss_state_pool_create_from_dense(ctypes.byref(desc), p(St), p(u), p(v), p(sg), p(rk),
+                                                          max_rank, _stream(stream), ctypes.byref(handle)))
+    any_delta = rule is not None and bool(np.any(np.asarray(rule) == 1))
+    return StatePool(handle, int(N), int(dk), int(dv), int(pad_slots), int(r_active), n_groups, any_delta,
+                     bool(diag_decay))
 
 
 def readout(pool: StatePool, q, o, stream=None):
@@ -346,6 +355,29 @@ def consolidate_async(pool: StatePool, side, group: int = -1, stream=None) -> in
     g = ctypes.c_int32()
     _check(load_library().ss_consolidate_async(pool.handle, int(group), _stream(stream), _stream(side), ctypes.byref(g)))
     return int(g.value)
+
+
+def host_consolidate_frozen(u, v, sigma, sigma0, eps):
+    """ss_host_consolidate_frozen on host arrays u (f, d_k), v (f, d_v), sigma (f,): returns the kept
+    (u, v, sigma) as new float32 arrays."""
+    u = np.ascontiguousarray(u, np.float32).copy()
+    v = np.ascontiguousarray(v, np.float32).copy()
+    sg = np.ascontiguousarray(sigma, np.float32).copy()
+    f, dk = u.shape
+    dv = v.shape[1]
+    kept = ctypes.c_int32(0)
+    _check(load_library().ss_host_consolidate_frozen(dk, dv, f, u.ctypes.data_as(_c_f32p), v.ctypes.data_as(_c_f32p),
+                                                     sg.ctypes.data_as(_c_f32p), float(sigma0), float(eps),
+                                                     ctypes.byref(kept)))
+    k = kept.value
+    return u[:k], v[:k], sg[:k]
+
+
+def consolidate_host(pool: StatePool, group: int = -1, threads: int = 0, stream=None) -> int:
+    """ss_consolidate_host: the group launched (-1: none waits)."""
+    out = ctypes.c_int32(-1)
+    _check(load_library().ss_consolidate_host(pool.handle, int(group), _stream(stream), int(threads), ctypes.byref(out)))
+    return out.value
 
 
 def consolidate_poll(pool: StatePool, wait: bool = False, stream=None) -> int:

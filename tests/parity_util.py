@@ -70,10 +70,37 @@ def rel_out_err(o_gpu, o_or, S_norm, q_norm):
     return np.linalg.norm(o_gpu - o_or, axis=1) / den
 
 
-def compare_compacted(gpu_states, P, eps, K=None, fp16=False):
+def nuclear_bound(st):
+    """An upper bound on the sum of the singular values a compaction of the exported factored state
+    `st` can keep: the local part sum_a sigma_a u_a v_a^T + sum_j c_j k_j w_j^T has nuclear norm at
+    most sum_a sigma_a + sum_j |c_j| |k_j| |w_j|, and the frozen values are kept or dropped as they
+    are."""
+    if isinstance(st, dict):  # a GPU export
+        if st["dense"]:
+            return 0.0
+        sig, c, Kp, Wp = st["sigma"], st["c"], st["K"], st["W"]
+    else:  # an oracle state
+        if st.dense:
+            return 0.0
+        sig, c, Kp, Wp = st.sigma, st.pc, st.PK, st.PW
+    sig, c = np.asarray(sig, np.float64), np.asarray(c, np.float64)
+    pad = np.sum(np.abs(c) * np.linalg.norm(np.asarray(Kp, np.float64), axis=1)
+                 * np.linalg.norm(np.asarray(Wp, np.float64), axis=1)) if len(c) else 0.0
+    return float(np.sum(np.abs(sig)) + pad)
+
+
+def states_of(P, n):
+    """The oracle pool's states 0..n-1 (e.g. just before a compaction, for compare_compacted's `before`)."""
+    return [P.get_state(j) for j in range(n)]
+
+
+def compare_compacted(gpu_states, P, eps, K=None, fp16=False, before=None):
     """Compare GPU states after a compaction with the oracle's.  Returns
     (max state rel err, max sigma rel err, guard-band count, rank mismatches outside the guard band).
-    fp16: the state error is reported as TOL * err / (TOL ||S|| + 2 rho), so that TOL stays the bar."""
+    fp16: the state error is reported as TOL * err / (TOL ||S|| + 2 rho), so that TOL stays the bar.
+    A state the compaction promoted (factored in `before`, the exports the compaction started from,
+    dense after it) is built on each side from the factors that side rounded to fp16 at this
+    compaction, so it gets the same allowance, with rho taken from nuclear_bound(before[j])."""
     worst_s, worst_sig, guard, bad = 0.0, 0.0, 0, []
     for j, st in enumerate(gpu_states):
         ost = P.get_state(j)
@@ -81,9 +108,12 @@ def compare_compacted(gpu_states, P, eps, K=None, fp16=False):
         So = P.reconstruct(j)
         nrm = np.linalg.norm(So)
         err = np.linalg.norm(Sg - So)
-        if fp16 and not ost.dense:
+        promoted = before is not None and ost.dense and st["dense"] and nuclear_bound(before[j]) > 0.0
+        if fp16 and (not ost.dense or promoted):
             d_k, d_v = So.shape
-            allowed = TOL * nrm + 2.0 * fp16_rounding_bound(ost.sigma, d_k, d_v)
+            rho = fp16_rounding_bound(ost.sigma, d_k, d_v) if not ost.dense else \
+                fp16_rounding_bound([nuclear_bound(before[j])], d_k, d_v)
+            allowed = TOL * nrm + 2.0 * rho
             worst_s = max(worst_s, TOL * err / max(allowed, 1e-30))
         else:
             worst_s = max(worst_s, err / max(nrm, 1e-30))

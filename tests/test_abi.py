@@ -170,6 +170,24 @@ def test_rsvd_init_rejects_bad_arguments_without_touching_the_gpu(lib):
     assert lib.ss_rsvd_init(None, 0, 16, 16, 4, 2, 2, None, None, 8, None, None, None, None, None, None) == ss.SS_OK
 
 
+def test_create_from_dense_rejects_bad_arguments_without_touching_the_gpu(lib):
+    from rank_recurrent_state_amd import sinkstate as ss
+    vp = ctypes.c_void_p(1)  # never dereferenced: every case fails the host-side checks first
+    out = ctypes.c_void_p()
+    desc, keep, _ = ss._desc(16, 16, 32, 8, 8, -1, True, 0, False, None, None, None, None, 1e-3, 0, 0, False, False)
+    f = lib.ss_state_pool_create_from_dense
+    assert f(None, vp, vp, vp, vp, vp, 8, None, ctypes.byref(out)) == ss.SS_ERR_ARG
+    assert f(ctypes.byref(desc), vp, vp, vp, vp, vp, 8, None, None) == ss.SS_ERR_ARG
+    assert f(ctypes.byref(desc), vp, vp, vp, vp, vp, 0, None, ctypes.byref(out)) == ss.SS_ERR_ARG
+    assert f(ctypes.byref(desc), vp, vp, vp, vp, vp, 17, None, ctypes.byref(out)) == ss.SS_ERR_ARG
+    assert f(ctypes.byref(desc), vp, None, vp, vp, vp, 8, None, ctypes.byref(out)) == ss.SS_ERR_ARG
+    bad, keep2, _ = ss._desc(16, 18, 32, 8, 8, -1, True, 0, False, None, None, None, None, 1e-3, 0, 0, False, False)
+    assert f(ctypes.byref(bad), vp, vp, vp, vp, vp, 8, None, ctypes.byref(out)) == ss.SS_ERR_SHAPE
+    fd, keep3, _ = ss._desc(16, 16, 32, 8, 8, -1, True, 0, True, None, None, None, None, 1e-3, 0, 0, False, False)
+    assert f(ctypes.byref(fd), vp, vp, vp, vp, vp, 8, None, ctypes.byref(out)) == ss.SS_ERR_ARG
+    assert not out.value
+
+
 def test_create_rejects_bad_dense_given_states(lib):
     import numpy as np
     from rank_recurrent_state_amd import sinkstate as ss

@@ -36,7 +36,14 @@ def _run(w, pool, t0, t1):
     torch.cuda.synchronize()
 
 
-def _consolidate_and_compare(w, init, pool, ids, group=-1, fp16=False):
+def _host_consolidate_all(pool, G, threads=0):
+    """Every group through the host-core pipeline, one at a time, each result installed."""
+    for g in range(G):
+        assert ss.consolidate_host(pool, g, threads=threads) == g
+        assert ss.consolidate_poll(pool, wait=True) == ss.CONS_INSTALLED
+
+
+def _consolidate_and_compare(w, init, pool, ids, group=-1, fp16=False, host=False):
     eps = init["eps"][ids]
     before = ss.state_export(pool, ids)
     P = oracle_from_export(before, eps, w.d_k, w.d_v, w.K, w.r, factor_fp16=fp16)
@@ -44,7 +51,15 @@ def _consolidate_and_compare(w, init, pool, ids, group=-1, fp16=False):
     # Gram matrix of unit vectors deviates from I by at most about 2 * 2^-11
     otol = 1.0e-3 + 1e-5 if fp16 else 1e-4
     st0 = ss.pool_stats(pool)
-    ss.consolidate(pool, group)
+    if host:
+        G = len(init["group_offset"])
+        if group < 0:
+            _host_consolidate_all(pool, G)
+        else:
+            assert ss.consolidate_host(pool, group) == group
+            assert ss.consolidate_poll(pool, wait=True) == ss.CONS_INSTALLED
+    else:
+        ss.consolidate(pool, group)
     torch.cuda.synchronize()
     after = ss.state_export(pool, ids)
     sel = np.arange(len(ids)) if group < 0 else np.nonzero(init["group_of_state"][ids] == group)[0]
@@ -363,3 +378,121 @@ def test_consolidate_async_queue_head_and_rejections():
     with pytest.raises(RuntimeError):
         ss.consolidate_async(kp, side, group=0)
     kp.close()
+
+
+# --------------------------------------------------------------------------------------------
+# host-core pipeline (SinkState 4.3, Figure 7(b)): download, exact fp64 SVD on host threads,
+# upload, install unless stale
+# --------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("name,steps,fp16", [("tiny", 64, False), ("gdn_delta", 48, False), ("gdn_delta", 48, True),
+                                             ("mamba2_258k", 48, False)])
+def test_consolidate_host_matches_oracle(name, steps, fp16):
+    """Every group consolidated on host cores: states, values and ranks as the oracle's exact
+    consolidation, active parts and pads untouched, new frozen factors orthonormal."""
+    w = W.get(name, n_requests=None if name == "tiny" else 1)
+    init = W.initial_state(w)
+    pool = _pool(w, init, **({"factor_fp16": True} if fp16 else {}))
+    _run(w, pool, 1, steps)
+    ids = np.arange(w.n_states) if name == "tiny" else \
+        np.unique(np.concatenate([np.arange(0, w.n_states, 7), [w.n_states - 1]]))
+    removed, guard = _consolidate_and_compare(w, init, pool, ids, fp16=fp16, host=True)
+    print(name, fp16, "removed", removed, "guard", guard)
+    if name == "gdn_delta":
+        assert removed > 0
+    pool.close()
+
+
+def test_consolidate_host_stale_is_dropped_and_retried_first():
+    """The group compacts while its host result is being computed: the result is dropped, the pool
+    equals a twin that never consolidated, and the next launch from the queue takes that group
+    before a group that was never consolidated (dropped first, then least recently consolidated)."""
+    w = W.get("gdn_delta", n_requests=1)
+    init = W.initial_state(w)
+    pa, pb = _pool(w, init), _pool(w, init)
+    gen = W.StepInputs(w, device="cuda")
+    o = torch.empty(w.n_states, w.d_v, device="cuda")
+    for p in (pa, pb):
+        _run_steps(w, p, 1, 40, o, gen)
+    g = ss.schedule_due(pa, 41)[0]
+    assert ss.consolidate_host(pa, g) == g
+    with pytest.raises(RuntimeError):  # one in flight per pool
+        ss.consolidate_host(pa, g)
+    for p in (pa, pb):
+        _run_steps(w, p, 41, 41, o, gen)  # compacts g
+    assert ss.consolidate_poll(pa, wait=True) == ss.CONS_DISCARDED
+    torch.cuda.synchronize()
+    ids = np.arange(w.n_states)
+    for x, y in zip(ss.state_export(pa, ids), ss.state_export(pb, ids)):
+        assert x["dense"] == y["dense"]
+        key = "S" if x["dense"] else "sigma"
+        assert np.array_equal(x[key], y[key])
+    # every other group waits too and was never consolidated; g goes first all the same
+    assert ss.consolidate_host(pa) == g
+    assert ss.consolidate_poll(pa, wait=True) == ss.CONS_INSTALLED
+    h = ss.consolidate_host(pa)
+    assert h != g and h >= 0
+    assert ss.consolidate_poll(pa, wait=True) == ss.CONS_INSTALLED
+    pa.close()
+    pb.close()
+
+
+def test_consolidate_async_retries_dropped_group_first():
+    """The GPU asynchronous form follows the same queue rule."""
+    w = W.get("gdn_delta", n_requests=1)
+    init = W.initial_state(w)
+    pool = _pool(w, init)
+    gen = W.StepInputs(w, device="cuda")
+    o = torch.empty(w.n_states, w.d_v, device="cuda")
+    _run_steps(w, pool, 1, 40, o, gen)
+    g = ss.schedule_due(pool, 41)[0]
+    side = torch.cuda.Stream()
+    assert ss.consolidate_async(pool, side, group=g) == g
+    _run_steps(w, pool, 41, 41, o, gen)
+    assert ss.consolidate_poll(pool, wait=True) == ss.CONS_DISCARDED
+    assert ss.consolidate_async(pool, side) == g
+    assert ss.consolidate_poll(pool, wait=True) == ss.CONS_INSTALLED
+    pool.close()
+
+
+def test_consolidate_host_across_ring_repacks():
+    """Rings created at the initial size: compactions of other groups re-pack them while the host
+    computes (the re-pack waits only for the gather); the install then lands at the moved
+    positions and agrees with a twin consolidated synchronously on the GPU, to the parity
+    tolerance (the host works in fp64)."""
+    w = W.get("gdn_delta", n_requests=1)
+    init = W.initial_state(w)
+    pa = _pool(w, init, arena_components=1)
+    pb = _pool(w, init, arena_components=1)
+    gen = W.StepInputs(w, device="cuda")
+    o = torch.empty(w.n_states, w.d_v, device="cuda")
+    for p in (pa, pb):
+        _run_steps(w, p, 1, 12, o, gen)
+    G = len(init["group_offset"])
+    g = _not_due(pa, 13, 16, G)[0]
+    r0 = ss.pool_stats(pa)["ring_repacks"]
+    assert ss.consolidate_host(pa, g) == g
+    ss.consolidate(pb, g)
+    for p in (pa, pb):
+        _run_steps(w, p, 13, 16, o, gen)
+    st = ss.consolidate_poll(pa, wait=True)
+    print("repacks during the consolidation", ss.pool_stats(pa)["ring_repacks"] - r0)
+    assert st == ss.CONS_INSTALLED
+    torch.cuda.synchronize()
+    ids = np.nonzero(init["group_of_state"] == g)[0]
+    for x, y in zip(ss.state_export(pa, ids), ss.state_export(pb, ids)):
+        assert x["dense"] == y["dense"]
+        if x["dense"]:
+            continue
+        ra = x["n_active"]
+        assert ra == y["n_active"] and len(x["sigma"]) == len(y["sigma"])
+        for key in ("U", "V", "sigma"):  # the active parts were never touched
+            assert np.array_equal(x[key][:ra], y[key][:ra]), key
+        # the frozen parts (the pads differ: delta-rule steps read the state before the install)
+        fx = (x["U"][ra:].T.astype(np.float64) * x["sigma"][ra:]) @ x["V"][ra:].astype(np.float64)
+        fy = (y["U"][ra:].T.astype(np.float64) * y["sigma"][ra:]) @ y["V"][ra:].astype(np.float64)
+        full = (y["U"].T.astype(np.float64) * y["sigma"]) @ y["V"].astype(np.float64)
+        assert np.linalg.norm(fx - fy) <= TOL * np.linalg.norm(full)
+        if len(y["sigma"]) > ra:
+            assert np.max(np.abs(x["sigma"][ra:] - y["sigma"][ra:]) / y["sigma"][ra:]) <= TOL
+    pa.close()
+    pb.close()

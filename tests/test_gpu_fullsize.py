@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from parity_util import TOL, compare_compacted, oracle_from_export, reconstruct, rel_out_err
+from parity_util import TOL, compare_compacted, states_of, oracle_from_export, reconstruct, rel_out_err
 
 pytestmark = pytest.mark.gpu
 
@@ -62,8 +62,9 @@ def _fullsize(name, steps, n_sample, requests=None, fp16=False):
         after = ss.state_export(pool, ids)
         if due:
             sel = np.nonzero(np.isin(grp, due))[0]
+            pre = states_of(P, len(ids))
             P.compact(sel)
-            ws, wsig, gd, bad = compare_compacted(after, P, eps, fp16=fp16)
+            ws, wsig, gd, bad = compare_compacted(after, P, eps, fp16=fp16, before=pre)
             assert not bad, f"{name} step {t}: rank/dense mismatches outside the guard band: {bad[:5]}"
             guard += gd
             worst["S_c"] = max(worst["S_c"], ws)

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from parity_util import TOL, compare_compacted, oracle_from_export, reconstruct, rel_out_err
+from parity_util import TOL, compare_compacted, states_of, oracle_from_export, reconstruct, rel_out_err
 
 pytestmark = pytest.mark.gpu
 
@@ -78,8 +78,9 @@ def _twin_run(name, steps, requests=1, arena=0, eager_extra=False, oracle_steps=
             e = rel_out_err(oB.cpu().numpy()[ids], oo, Sn, np.linalg.norm(sub["q"], axis=1))
             worst["o"] = max(worst["o"], float(e.max()))
             if due:
+                pre = states_of(P, len(ids))
                 P.compact(np.nonzero(np.isin(grp, due))[0])
-                ws, wsig, gd, bad = compare_compacted(ss.state_export(B, ids), P, eps, fp16=fp16)
+                ws, wsig, gd, bad = compare_compacted(ss.state_export(B, ids), P, eps, fp16=fp16, before=pre)
                 assert not bad, f"step {t}: rank/dense mismatches outside the guard band: {bad[:5]}"
                 worst["S_c"] = max(worst["S_c"], ws)
                 worst["sigma"] = max(worst["sigma"], wsig)

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from parity_util import TOL, compare_compacted, oracle_from_export, reconstruct, rel_out_err
+from parity_util import TOL, compare_compacted, states_of, oracle_from_export, reconstruct, rel_out_err
 
 pytestmark = pytest.mark.gpu
 
@@ -118,9 +118,10 @@ def test_kda_edge_shapes(rule, fp16):
             e = rel_out_err(o.cpu().numpy(), oo, Sn, np.linalg.norm(q.cpu().numpy(), axis=1))
             worst = max(worst, float(e.max()))
             if due:
+                pre = states_of(P, len(ids))
                 P.compact()
                 after = ss.state_export(pool, ids)
-                ws, wsig, gd, bad = compare_compacted(after, P, eps, fp16=fp16)
+                ws, wsig, gd, bad = compare_compacted(after, P, eps, fp16=fp16, before=pre)
                 assert not bad and ws <= TOL and wsig <= TOL, (dk, dv, K, r, ws, wsig, bad)
                 for st in after:  # the compaction folded the decays in: unit factors again
                     if not st["dense"] and len(st["sigma"]):

@@ -69,7 +69,7 @@ def _lockstep(w, init, pool, ids, steps, promote=True, check_readout=False, fp16
             sel = np.nonzero(np.isin(grp, due))[0]
             P2.compact(sel)
             comp = ss.state_export(pool, ids)
-            ws, wsig, gd, bad = compare_compacted(comp, P2, eps, fp16=fp16)
+            ws, wsig, gd, bad = compare_compacted(comp, P2, eps, fp16=fp16, before=after)
             assert not bad, f"step {t}: rank/dense mismatches outside the guard band: {bad[:5]}"
             guard += gd
             worst["S_c"] = max(worst["S_c"], ws)
