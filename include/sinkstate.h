@@ -177,7 +177,7 @@ ss_status ss_state_pool_create(const ss_pool_desc *desc, const ss_init *init, hi
 /* Create a pool from dense states and their randomized block SVD ([SS] 4.2
  * "Randomized SVD initialization after prefill"; 4.4 "Memory layout": the
  * dense fallback is decided once a state has been factored).  S, u, v, sigma
- * and rank are device memory as ss_rsvd_init with
+ * and rank are device memory as ss_rsvd_init (or ss_rsvd_init_noalloc) with
  * the same max_rank reads and writes them: S [n_states][d_k][d_v], u
  * [n_states][max_rank][d_k], v [n_states][max_rank][d_v], sigma
  * [n_states][max_rank], rank [n_states].  The library reads the factors and
@@ -357,6 +357,23 @@ ss_status ss_rsvd_init(const float *S, int64_t n, int32_t d_k, int32_t d_v, int3
                        int32_t iters, const float *omega, const float *eps, int32_t max_rank, float *work, float *u,
                        float *v, float *sigma, int32_t *rank, hipStream_t stream);
 
+/* ss_rsvd_init without the caller's workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It allocates nothing: a state whose
+ * d_k x d_v residual does not fit the kernel's LDS (d_k (d_v + 1) floats
+ * above 120 KB, e.g. 256 x 128) keeps it in a fixed 32 MiB device array that
+ * the library holds on each GPU it runs on until the process ends; smaller
+ * states use no workspace at all.  Arguments, layouts, results and errors are
+ * those of ss_rsvd_init (the same kernel runs), without `work`.  Limit: when
+ * the workspace is used, n * d_k * d_v must not exceed 8,388,608 floats, else
+ * SS_ERR_CAPACITY (checked on the host before any HIP call); split larger
+ * batches over several calls.  Every call on a GPU shares that GPU's array
+ * (its contents are overwritten, none needs to start at zero), so calls that
+ * overlap on one GPU, on different streams or threads, race; calls on one
+ * stream do not. */
+ss_status ss_rsvd_init_noalloc(const float *S, int64_t n, int32_t d_k, int32_t d_v, int32_t block, int32_t n_blocks,
+                               int32_t iters, const float *omega, const float *eps, int32_t max_rank, float *u,
+                               float *v, float *sigma, int32_t *rank, hipStream_t stream);
 
 /* Whole decode steps as HIP graphs ([SS] 4.4 "Kernel fusion, load balancing,
  * and support for CUDA graphs": the pages replay steps as graphs; here one

@@ -20,6 +20,9 @@
 // product and four of its block columns), with Omega and
 // Q in LDS; orth is the CGS2 thin QR and the block SVD is the thin QR of
 // Omega followed by one-sided Jacobi on its R, both on wavefront 0.
+#include <mutex>
+#include <unordered_map>
+
 #include "ss_internal.h"
 #include "ss_linalg.h"
 #include "ss_wave.h"
@@ -265,6 +268,33 @@ hipError_t launch_rsvd_init(const RsvdArgs &a, hipStream_t st) {
   SS_RSVD(4, 4)
 #undef SS_RSVD
   return hipErrorInvalidValue;
+}
+
+// Fixed workspace of the allocation-free initialization entry point: the residuals of a call
+// whose states do not fit the kernel's LDS live here instead of in a caller's buffer.  The array
+// is a file-scope device variable, so each GPU the library runs on holds its own copy for the
+// life of the process.  In host code its name stands for no device address: the address is
+// asked of the runtime once per device (with that device current) and kept.
+namespace {
+__device__ __align__(256) float scratch[kRsvdScratchFloats];
+std::mutex g_scratch_mu;
+std::unordered_map<int, float *> g_scratch_ptr;  // device -> address of its copy of `scratch`
+}  // namespace
+
+hipError_t rsvd_scratch(float **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it == g_scratch_ptr.end()) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    it = g_scratch_ptr.emplace(dev, static_cast<float *>(ptr)).first;
+  }
+  *out = it->second;
+  return hipSuccess;
 }
 
 }  // namespace ss

@@ -255,6 +255,10 @@ struct RsvdArgs {
 hipError_t launch_rsvd_init(const RsvdArgs &a, hipStream_t st);
 // whether a d_k x d_v residual fits the initialization kernel's LDS (else it needs a workspace)
 bool rsvd_residual_in_lds(int dk, int dv);
+// the fixed device workspace of ss_rsvd_init_noalloc: kRsvdScratchFloats floats (32 MiB) per GPU;
+// its address on the current device (looked up once per device)
+constexpr size_t kRsvdScratchFloats = size_t(8) << 20;
+hipError_t rsvd_scratch(float **out);
 
 // consolidation of the frozen parts of a group's factored states (one workgroup each, in place)
 struct ConsolidateArgs {

@@ -1157,6 +1157,25 @@ ss_status ss_rsvd_init(const float *S, int64_t n, int32_t d_k, int32_t d_v, int3
   return rsvd_launch(S, n, d_k, d_v, block, n_blocks, iters, omega, eps, max_rank, work, u, v, sigma, rank, stream);
 }
 
+ss_status ss_rsvd_init_noalloc(const float *S, int64_t n, int32_t d_k, int32_t d_v, int32_t block, int32_t n_blocks,
+                               int32_t iters, const float *omega, const float *eps, int32_t max_rank, float *u,
+                               float *v, float *sigma, int32_t *rank, hipStream_t stream) {
+  ss_status st = rsvd_check(S, n, d_k, d_v, block, n_blocks, iters, omega, eps, max_rank, u, v, sigma, rank);
+  if (st != SS_OK || n == 0) return st;
+  const bool need_ws = !ss::rsvd_residual_in_lds(d_k, d_v);
+  if (need_ws && n * (int64_t)d_k * d_v > (int64_t)ss::kRsvdScratchFloats)
+    return fail(SS_ERR_CAPACITY, "n * d_k * d_v exceeds the 8,388,608-float (32 MiB) fixed workspace of "
+                                 "ss_rsvd_init_noalloc; split the states over several calls");
+  float *ws = nullptr;
+  if (need_ws) {
+    const hipError_t e = ss::rsvd_scratch(&ws);
+    if (e != hipSuccess) return hip_fail(e, "workspace address");
+  }
+  // states whose residual fits the LDS read no workspace
+  return rsvd_launch(S, n, d_k, d_v, block, n_blocks, iters, omega, eps, max_rank, ws, u, v, sigma, rank, stream);
+}
+
+
 static hipError_t enqueue_consolidate_group(ss_pool *p, int g, hipStream_t stream) {
   ss::ConsolidateArgs a{};
   a.dk = p->dk; a.dv = p->dv; a.fmax = frozen_max(p);

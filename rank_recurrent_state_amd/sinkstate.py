@@ -109,6 +109,9 @@ def load_library():
     lib.ss_rsvd_init.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                  ctypes.c_int32, vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp]
     lib.ss_rsvd_init.restype = ctypes.c_int
+    lib.ss_rsvd_init_noalloc.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_int32, vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp]
+    lib.ss_rsvd_init_noalloc.restype = ctypes.c_int
     lib.ss_state_pool_create_from_dense.argtypes = [ctypes.POINTER(PoolDesc)] + [vp] * 5 + [ctypes.c_int32, vp,
                                                                                          ctypes.POINTER(vp)]
     lib.ss_state_pool_create_from_dense.restype = ctypes.c_int
@@ -295,6 +298,29 @@ def rsvd_init(S, omega, eps, iters=2, max_rank=None, stream=None):
     _check(load_library().ss_rsvd_init(p(S), n, dk, dv, b, nb, int(iters), p(omega), p(eps_t), max_rank, p(work),
                                        p(u), p(v), p(sigma), p(rank), _stream(stream)))
     return u, v, sigma, rank
+
+
+def rsvd_init_noalloc(S, omega, eps, u, v, sigma, rank, iters=2, stream=None):
+    """ss_rsvd_init_noalloc: the randomized block SVD with the library's fixed workspace.  The caller
+    passes the outputs, allocated beforehand: u (n, max_rank, d_k), v (n, max_rank, d_v),
+    sigma (n, max_rank) float32 and rank (n,) int32 CUDA tensors; eps is an (n,) float32 CUDA tensor."""
+    n, dk, dv = S.shape
+    n2, nb, dk2, b = omega.shape
+    if n2 != n or dk2 != dk:
+        raise ValueError("omega must be (n, n_blocks, d_k, block)")
+    max_rank = u.shape[1]
+    if u.shape != (n, max_rank, dk) or v.shape != (n, max_rank, dv) or sigma.shape != (n, max_rank) \
+            or rank.shape != (n,) or eps.shape != (n,):
+        raise ValueError("outputs must be u (n, max_rank, d_k), v (n, max_rank, d_v), sigma (n, max_rank), "
+                         "rank (n,); eps (n,)")
+    for t, name, dt in ((S, "S", torch.float32), (omega, "omega", torch.float32), (eps, "eps", torch.float32),
+                        (u, "u", torch.float32), (v, "v", torch.float32), (sigma, "sigma", torch.float32),
+                        (rank, "rank", torch.int32)):
+        if not (t.is_cuda and t.dtype == dt and t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous {dt} CUDA tensor")
+    p = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    _check(load_library().ss_rsvd_init_noalloc(p(S), n, dk, dv, b, nb, int(iters), p(omega), p(eps), max_rank,
+                                               p(u), p(v), p(sigma), p(rank), _stream(stream)))
 
 
 def state_pool_from_dense(S, omega, eps, d_k=None, d_v=None, pad_slots=8, r_active=8, iters=2, rule=None,

@@ -170,6 +170,25 @@ def test_rsvd_init_rejects_bad_arguments_without_touching_the_gpu(lib):
     assert lib.ss_rsvd_init(None, 0, 16, 16, 4, 2, 2, None, None, 8, None, None, None, None, None, None) == ss.SS_OK
 
 
+def test_rsvd_init_noalloc_checks_without_touching_the_gpu(lib):
+    """The allocation-free initialization checks its arguments like ss_rsvd_init and rejects a batch
+    larger than its fixed 32 MiB workspace before any HIP call; states whose residual fits the LDS
+    need no workspace, so their batch size is not limited by it."""
+    from rank_recurrent_state_amd import sinkstate as ss
+    vp = ctypes.c_void_p(1)  # never dereferenced: every case fails the host-side checks first
+    f = lib.ss_rsvd_init_noalloc
+    assert f(vp, -1, 16, 16, 4, 2, 2, vp, vp, 8, vp, vp, vp, vp, None) == ss.SS_ERR_ARG
+    assert f(vp, 4, 18, 16, 4, 2, 2, vp, vp, 8, vp, vp, vp, vp, None) == ss.SS_ERR_SHAPE
+    assert f(vp, 4, 16, 16, 4, 2, 2, vp, vp, 9, vp, vp, vp, vp, None) == ss.SS_ERR_ARG
+    assert f(None, 4, 16, 16, 4, 2, 2, None, None, 8, None, None, None, None, None) == ss.SS_ERR_ARG
+    assert f(None, 0, 16, 16, 4, 2, 2, None, None, 8, None, None, None, None, None) == ss.SS_OK
+    # 256 x 128 needs the workspace: 257 states are 8,421,376 floats, one more than fits
+    assert f(vp, 257, 256, 128, 8, 2, 2, vp, vp, 16, vp, vp, vp, vp, None) == ss.SS_ERR_CAPACITY
+    assert b"32 MiB" in lib.ss_last_error()
+    # 128 x 80 fits the LDS: a large batch passes the capacity check and stops at the null pointer
+    assert f(None, 10**6, 128, 80, 8, 2, 2, vp, vp, 16, vp, vp, vp, vp, None) == ss.SS_ERR_ARG
+
+
 def test_create_from_dense_rejects_bad_arguments_without_touching_the_gpu(lib):
     from rank_recurrent_state_amd import sinkstate as ss
     vp = ctypes.c_void_p(1)  # never dereferenced: every case fails the host-side checks first
