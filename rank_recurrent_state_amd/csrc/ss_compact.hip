@@ -685,7 +685,7 @@ __global__ __launch_bounds__(256) void k_compact_h(CompactArgs a) {
       }
     }
     wave_sync();
-    sweeps = jacobi16(Cm, Vh, mcol, lane, &jlimit);
+    sweeps = jacobi16n(Cm, Vh, sraw, mcol, lane, &jlimit);  // sraw holds the column norms meanwhile
     if (lane < 16) {
       float xx = 0.f;
 #pragma unroll

@@ -220,4 +220,68 @@ __device__ inline int jacobi16(float *Cm, float *Vh, int m, int lane, bool *limi
   return sweep;
 }
 
+// jacobi16 with the column norms carried: the same pairs, order, stopping rule and rotation, but
+// each round computes only the pair's inner product g; the squared norms a, b of the pair's columns
+// are read from `nrm` (16 floats of LDS) and, after a rotation by t = tan(theta), updated to
+// a - t g and b + t g (the rotation zeroes g).  The norms are recomputed from the columns at the
+// start of every sweep, so the rounding of the updates never accumulates past one sweep.  Each lane
+// of a pair holds two consecutive rows (one 8-byte LDS access per column), and the lanes read the
+// pair's Vh columns before the rotation is decided, so that their latency overlaps the arithmetic.
+__device__ inline int jacobi16n(float *Cm, float *Vh, float *nrm, int m, int lane, bool *limit = nullptr) {
+  if (limit) *limit = false;
+  const int M = (m + 1) & ~1;
+  if (M < 2) return 0;
+  const int np = M >> 1, rounds = M - 1;
+  const int p = lane >> 3, sub = lane & 7;
+  const bool act = p < np;
+  const float tol2 = kTolJ * kTolJ;
+  int sweep = 0;
+  while (sweep < kMaxSweeps) {
+    ++sweep;
+    if (lane < 16) {
+      const float2 *cc = reinterpret_cast<const float2 *>(Cm + lane * 16);
+      float xx = 0.f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) xx = fmaf(cc[q].x, cc[q].x, fmaf(cc[q].y, cc[q].y, xx));
+      nrm[lane] = xx;
+    }
+    wave_sync();
+    bool any = false;
+    int ci = p == 0 ? 0 : p % (M - 1);
+    int cj = p == 0 ? M - 1 : (M - 1 - p) % (M - 1);
+    for (int k = 0; k < rounds; ++k) {
+      const int ii = act ? ci : 0, jj = act ? cj : 0;  // clamped: in bounds
+      const float2 x = *reinterpret_cast<const float2 *>(Cm + ii * 16 + 2 * sub);
+      const float2 y = *reinterpret_cast<const float2 *>(Cm + jj * 16 + 2 * sub);
+      const float2 vx = *reinterpret_cast<const float2 *>(Vh + ii * 16 + 2 * sub);
+      const float2 vy = *reinterpret_cast<const float2 *>(Vh + jj * 16 + 2 * sub);
+      const float aa = nrm[ii], bb = nrm[jj];
+      const float gg = group_sum<8>(fmaf(x.x, y.x, x.y * y.y));
+      const bool rot = act && gg != 0.f && gg * gg > tol2 * (aa * bb);
+      if (rot) {
+        const float zeta = (bb - aa) * (0.5f * __builtin_amdgcn_rcpf(gg));
+        const float az = fabsf(zeta);
+        const float t = az > 1e10f ? 0.5f * __builtin_amdgcn_rcpf(zeta)
+                                   : copysignf(__builtin_amdgcn_rcpf(az + __builtin_amdgcn_sqrtf(fmaf(zeta, zeta, 1.f))), zeta);
+        const float c = __builtin_amdgcn_rsqf(fmaf(t, t, 1.f)), sn = c * t;
+        *reinterpret_cast<float2 *>(Cm + ii * 16 + 2 * sub) = make_float2(c * x.x - sn * y.x, c * x.y - sn * y.y);
+        *reinterpret_cast<float2 *>(Cm + jj * 16 + 2 * sub) = make_float2(sn * x.x + c * y.x, sn * x.y + c * y.y);
+        *reinterpret_cast<float2 *>(Vh + ii * 16 + 2 * sub) = make_float2(c * vx.x - sn * vy.x, c * vx.y - sn * vy.y);
+        *reinterpret_cast<float2 *>(Vh + jj * 16 + 2 * sub) = make_float2(sn * vx.x + c * vy.x, sn * vx.y + c * vy.y);
+        if (sub == 0) {
+          nrm[ii] = fmaf(-t, gg, aa);
+          nrm[jj] = fmaf(t, gg, bb);
+        }
+      }
+      any = any || (__builtin_amdgcn_ballot_w64(rot) != 0ull);
+      wave_sync();
+      ci = (ci + 1 == M - 1) ? 0 : ci + 1;
+      if (p != 0) cj = (cj + 1 == M - 1) ? 0 : cj + 1;
+    }
+    if (!any) break;
+    if (limit && sweep == kMaxSweeps) *limit = true;
+  }
+  return sweep;
+}
+
 }  // namespace ss
