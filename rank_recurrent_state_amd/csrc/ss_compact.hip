@@ -44,6 +44,20 @@ constexpr int kOffRl = 0, kOffRr = 256, kOffCm = 512, kOffVh = 768, kOffScw = 10
 constexpr int kOffFraw = kLdsPerWave, kOffForig = kOffFraw + kMaxFrozen, kOffFnorm = kOffForig + kMaxFrozen,
               kLdsPerWaveDiag = kOffFnorm + kMaxFrozen;
 
+// A member's slots in its group's new ring segments: upper bounds of its new active and frozen
+// counts that the stored record already fixes, so that every member's place in the segment is a
+// prefix sum taken before the compaction runs (no allocation inside it).  A merge keeps at most
+// ra + rf + n components and at most r + fcap, the first r of them active; a state moved unchanged
+// keeps ra and rf.  With the ring's invariant (frozen components only behind a full active part)
+// neither bound exceeds the old slot plus the pad size K, which bounds the ring usage on the host.
+__device__ __forceinline__ void slot_sizes(int ra, int rf, int n, int r, int fcap, int &sa, int &sf) {
+  int t = ra + rf + n;
+  if (t > r + fcap) t = r + fcap;
+  const int ta = t < r ? t : r;
+  sa = ta > ra ? ta : ra;
+  sf = t - ta > rf ? t - ta : rf;
+}
+
 // copy one fp32 component (u, v) into factor storage of type F, with float4 lanes
 template <typename F>
 __device__ __forceinline__ void copy_comp(const float *su, const float *sv, F *du, F *dv_, int dk, int dv, int lane) {
@@ -118,9 +132,6 @@ __device__ __forceinline__ void copy_comps(const Arena &src, int64_t c0, int cnt
 template <int NS, typename F, bool DIAG>
 __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   __shared__ float lds[4][DIAG ? kLdsPerWaveDiag : kLdsPerWave];
-  __shared__ int wg_cnt[4][2];
-  __shared__ unsigned long long wg_base[2];
-  __shared__ int wg_ok;
   const int w = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int mi = blockIdx.x * 4 + w;
   float *Rl = lds[w] + kOffRl;
@@ -328,43 +339,20 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
     wave_sync();
   }
 
-  // ---- allocation: the workgroup's new components, one atomic add per ring ----------------
-  if (lane == 0) {
-    wg_cnt[w][0] = live ? ra2 : 0;
-    wg_cnt[w][1] = live ? rf2 : 0;
+  // ---- placement: the member's slots in the group's new segments ---------------------------
+  if (!live) return;
+  {
+    int sa, sf;
+    slot_sizes(ra, rf, n, r, a.fcap, sa, sf);
+    if (ra2 > sa || rf2 > sf) {  // cannot happen (the slots bound the counts); never overwrite a neighbour
+      if (lane == 0) *a.hflag = 1u;
+      return;
+    }
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int sa = 0, sf = 0;
-    for (int i = 0; i < 4; ++i) {
-      sa += wg_cnt[i][0];
-      sf += wg_cnt[i][1];
-    }
-    unsigned long long ba = 0, bf = 0;
-    bool ok = true;
-    if (sa) {
-      ba = __hip_atomic_fetch_add(&a.ring_a->head, (unsigned long long)sa, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      ok = ok && ba + sa <= a.ring_a->limit;
-    }
-    if (sf) {
-      bf = __hip_atomic_fetch_add(&a.ring_f->head, (unsigned long long)sf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      ok = ok && bf + sf <= a.ring_f->limit;
-    }
-    if (!ok) {  // the ring is full: the group's states keep their old form and the pool reports it
-      __hip_atomic_fetch_add(&a.ring_a->overflow, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      *a.hflag = 1u;
-    }
-    wg_base[0] = ba;
-    wg_base[1] = bf;
-    wg_ok = ok ? 1 : 0;
-  }
-  __syncthreads();
-  if (!live || !wg_ok) return;
-  unsigned long long va = wg_base[0], vf = wg_base[1];
-  for (int i = 0; i < w; ++i) {
-    va += (unsigned long long)wg_cnt[i][0];
-    vf += (unsigned long long)wg_cnt[i][1];
-  }
+  const unsigned long long rel = a.slot_in[mi] + a.slot_blk[mi / kSlotBlock];
+  const unsigned long long va = a.ring_a->begin + (rel & 0xffffffffull), vf = a.ring_f->begin + (rel >> 32);
+  // the ring is full (the ring set-up has raised the pool's flag): the state keeps its old form
+  if (va + ra2 > a.ring_a->limit || vf + rf2 > a.ring_f->limit) return;
   const int64_t dst_a = (int64_t)(va % (unsigned long long)capA), dst_f = (int64_t)(vf % (unsigned long long)capF);
 
   // ---- phase B: write the new components and the record ------------------------------------
@@ -537,9 +525,6 @@ __device__ __forceinline__ float dotb(const float4 (&x)[NB], const float4 (&y)[N
 template <int NB, typename F>
 __global__ __launch_bounds__(256) void k_compact_h(CompactArgs a) {
   __shared__ __align__(16) float lds[4][kLdsPerWave];
-  __shared__ int wg_cnt[4][2];
-  __shared__ unsigned long long wg_base[2];
-  __shared__ int wg_ok;
   const int w = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int side = lane >> 5, r = lane & 31;
   const int mi = blockIdx.x * 4 + w;
@@ -743,43 +728,20 @@ __global__ __launch_bounds__(256) void k_compact_h(CompactArgs a) {
     wave_sync();
   }
 
-  // ---- allocation: the workgroup's new components, one atomic add per ring ----------------
-  if (lane == 0) {
-    wg_cnt[w][0] = live ? ra2 : 0;
-    wg_cnt[w][1] = live ? rf2 : 0;
+  // ---- placement: the member's slots in the group's new segments ---------------------------
+  if (!live) return;
+  {
+    int sa, sf;
+    slot_sizes(ra, rf, n, rr_, a.fcap, sa, sf);
+    if (ra2 > sa || rf2 > sf) {  // cannot happen (the slots bound the counts); never overwrite a neighbour
+      if (lane == 0) *a.hflag = 1u;
+      return;
+    }
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int sa = 0, sf = 0;
-    for (int i = 0; i < 4; ++i) {
-      sa += wg_cnt[i][0];
-      sf += wg_cnt[i][1];
-    }
-    unsigned long long ba = 0, bf = 0;
-    bool ok = true;
-    if (sa) {
-      ba = __hip_atomic_fetch_add(&a.ring_a->head, (unsigned long long)sa, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      ok = ok && ba + sa <= a.ring_a->limit;
-    }
-    if (sf) {
-      bf = __hip_atomic_fetch_add(&a.ring_f->head, (unsigned long long)sf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      ok = ok && bf + sf <= a.ring_f->limit;
-    }
-    if (!ok) {  // the ring is full: the group's states keep their old form and the pool reports it
-      __hip_atomic_fetch_add(&a.ring_a->overflow, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      *a.hflag = 1u;
-    }
-    wg_base[0] = ba;
-    wg_base[1] = bf;
-    wg_ok = ok ? 1 : 0;
-  }
-  __syncthreads();
-  if (!live || !wg_ok) return;
-  unsigned long long va = wg_base[0], vf = wg_base[1];
-  for (int i = 0; i < w; ++i) {
-    va += (unsigned long long)wg_cnt[i][0];
-    vf += (unsigned long long)wg_cnt[i][1];
-  }
+  const unsigned long long rel = a.slot_in[mi] + a.slot_blk[mi / kSlotBlock];
+  const unsigned long long va = a.ring_a->begin + (rel & 0xffffffffull), vf = a.ring_f->begin + (rel >> 32);
+  // the ring is full (the ring set-up has raised the pool's flag): the state keeps its old form
+  if (va + ra2 > a.ring_a->limit || vf + rf2 > a.ring_f->limit) return;
   const int64_t dst_a = (int64_t)(va % (unsigned long long)capA), dst_f = (int64_t)(vf % (unsigned long long)capF);
 
   // ---- phase B: write the new components and the record ------------------------------------
@@ -1095,10 +1057,49 @@ __global__ __launch_bounds__(256) void k_prune_factored(const int32_t *src, cons
   if (keep) dst[base + __builtin_popcountll(mask & ((1ull << lane) - 1ull))] = s;
 }
 
-// ring bookkeeping around a compaction: seg_x[2 g] / seg_x[2 g + 1] are the virtual start / end of
-// group g's segment (start == end: no live segment)
-__global__ void k_ring_begin(Ring *ra, Ring *rf, const unsigned long long *seg_a, const unsigned long long *seg_f,
-                             int n_groups, int64_t cap_a, int64_t cap_f, uint32_t *counters) {
+// A group's ring slots, first pass: per member its slot sizes packed as (active | frozen << 32),
+// scanned (exclusive) within blocks of kSlotBlock members; each block's total goes to blk.
+__global__ __launch_bounds__(kSlotBlock) void k_slot_scan(const int32_t *members, int n_members, const Meta *meta,
+                                                          int r, int fcap, unsigned long long *in_blk,
+                                                          unsigned long long *blk) {
+  using Scan = hipcub::BlockScan<unsigned long long, kSlotBlock>;
+  __shared__ typename Scan::TempStorage tmp;
+  const int mi = blockIdx.x * kSlotBlock + threadIdx.x;
+  unsigned long long v = 0;
+  if (mi < n_members) {
+    const uint32_t packed = meta[members[mi]].packed;
+    if (!(meta_flags(packed) & FLAG_DENSE)) {
+      int sa, sf;
+      slot_sizes((int)meta_ra(packed), (int)meta_rf(packed), (int)meta_n(packed), r, fcap, sa, sf);
+      v = (unsigned long long)sa | ((unsigned long long)sf << 32);
+    }
+  }
+  unsigned long long ex, tot;
+  Scan(tmp).ExclusiveSum(v, ex, tot);
+  if (mi < n_members) in_blk[mi] = ex;
+  if (threadIdx.x == 0) blk[blockIdx.x] = tot;
+}
+
+// Ring set-up of a compaction, after k_slot_scan: the block totals become block offsets, each
+// ring's new segment is [begin, begin + its slots) from the old head, and the limit is the oldest
+// live segment's start plus the capacity (seg_x[2 g] / seg_x[2 g + 1]: virtual start / end of
+// group g's segment, start == end: none).  A segment past its limit raises the pool's flag.
+__global__ __launch_bounds__(kSlotBlock) void k_ring_begin(Ring *ra, Ring *rf, const unsigned long long *seg_a,
+                                                           const unsigned long long *seg_f, int n_groups,
+                                                           int64_t cap_a, int64_t cap_f, uint32_t *counters,
+                                                           unsigned long long *blk, int n_blk, uint32_t *hflag) {
+  using Scan = hipcub::BlockScan<unsigned long long, kSlotBlock>;
+  __shared__ typename Scan::TempStorage tmp;
+  unsigned long long carry = 0;
+  for (int b0 = 0; b0 < n_blk; b0 += kSlotBlock) {
+    const int b = b0 + (int)threadIdx.x;
+    const unsigned long long v = b < n_blk ? blk[b] : 0ull;
+    unsigned long long ex, tot;
+    Scan(tmp).ExclusiveSum(v, ex, tot);
+    __syncthreads();  // tmp is used again
+    if (b < n_blk) blk[b] = carry + ex;
+    carry += tot;
+  }
   if (threadIdx.x != 0) return;
   counters[C_PROMOTE_COUNT] = 0u;  // the compaction's promotion list starts empty
   counters[C_FACT1] = 0u;          // scratch length for a pruning of the factored-state list
@@ -1111,6 +1112,12 @@ __global__ void k_ring_begin(Ring *ra, Ring *rf, const unsigned long long *seg_a
   rf->limit = tf + (unsigned long long)cap_f;
   ra->begin = ra->head;
   rf->begin = rf->head;
+  ra->head = ra->begin + (carry & 0xffffffffull);
+  rf->head = rf->begin + (carry >> 32);
+  if (ra->head > ra->limit || rf->head > rf->limit) {  // the members whose slots pass it keep their old form
+    ra->overflow += 1ull;
+    *hflag = 1u;
+  }
 }
 
 __global__ void k_ring_end(Ring *ra, Ring *rf, unsigned long long *seg_a, unsigned long long *seg_f, int g) {
@@ -1293,9 +1300,13 @@ hipError_t launch_prune_factored(int32_t *list, uint32_t *count, int32_t *tmp, u
   return hipGetLastError();
 }
 
-hipError_t launch_ring_begin(Ring *ra, Ring *rf, const unsigned long long *seg_a, const unsigned long long *seg_f,
-                             int n_groups, int64_t cap_a, int64_t cap_f, uint32_t *counters, hipStream_t st) {
-  hipLaunchKernelGGL(k_ring_begin, dim3(1), dim3(64), 0, st, ra, rf, seg_a, seg_f, n_groups, cap_a, cap_f, counters);
+hipError_t launch_ring_begin(const RingBeginArgs &b, hipStream_t st) {
+  const int n_blk = (b.n_members + kSlotBlock - 1) / kSlotBlock;
+  if (n_blk > 0)
+    hipLaunchKernelGGL(k_slot_scan, dim3((unsigned)n_blk), dim3(kSlotBlock), 0, st, b.members, b.n_members, b.meta, b.r,
+                       b.fcap, b.slot_in, b.slot_blk);
+  hipLaunchKernelGGL(k_ring_begin, dim3(1), dim3(kSlotBlock), 0, st, b.ring_a, b.ring_f, b.seg_a, b.seg_f, b.n_groups,
+                     b.cap_a, b.cap_f, b.counters, b.slot_blk, n_blk, b.hflag);
   return hipGetLastError();
 }
 

@@ -16,11 +16,14 @@
 // The active and frozen arenas are rings of `cap` components.  Positions are
 // virtual (64-bit, only growing); component c lives at c mod cap, and a
 // state's components are consecutive in that sense, so the record holds the
-// physical start and a reader wraps once (wrap()).  A compaction allocates
-// the new components of its group from the ring head, one atomic add per
-// workgroup, so a group's components form one exactly packed segment; the
-// group's previous segment is released when the compaction completes, and
-// the ring tail is the oldest segment still live.
+// physical start and a reader wraps once (wrap()).  A compaction places the
+// new components of its group from the ring head: each member gets a slot of
+// the largest counts its record allows (at most r active, at most its pad size
+// more than before), at a prefix sum taken before the compaction, so the
+// kernel allocates nothing and a group's components form one segment whose
+// slack is bounded by the pads; the group's previous segment is released
+// when the compaction completes, and the ring tail is the oldest segment
+// still live.  A re-pack lays the segments out exactly again.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -145,7 +148,8 @@ struct CompactArgs {
   const float *eps;
   Meta *meta;
   Arena act, frz;
-  Ring *ring_a, *ring_f;       // the new components are allocated from these
+  Ring *ring_a, *ring_f;       // the new components go to [begin, head) of these
+  const unsigned long long *slot_in, *slot_blk;  // member slots (launch_ring_begin)
   uint32_t *hflag;             // host-mapped flag raised when a ring is full
   float *pk, *pw, *pc;
   int32_t *promote_list;
@@ -201,10 +205,27 @@ hipError_t launch_materialize(const MaterializeArgs &a, int64_t grid_upper, hipS
 hipError_t launch_scatter(const ScatterArgs &a, hipStream_t st);
 hipError_t launch_zero_u32(uint32_t *p, int n, hipStream_t st);
 hipError_t launch_fill_f32(float *p, int64_t n, float x, hipStream_t st);
-// before a compaction of group g: limit = (oldest live segment start) + cap, begin = head, per ring,
-// and the promotion list and the pruning scratch emptied; after it: the group's segment becomes [begin, head)
-hipError_t launch_ring_begin(Ring *ra, Ring *rf, const unsigned long long *seg_a, const unsigned long long *seg_f,
-                             int n_groups, int64_t cap_a, int64_t cap_f, uint32_t *counters, hipStream_t st);
+// Before a compaction of a group: each member's slots in the new segments (slot_in, per member
+// relative to the block of kSlotBlock members it falls in; slot_blk, per block; both packed as
+// active | frozen << 32), and per ring limit = (oldest live segment start) + cap, begin = head,
+// head = begin + the slots; the promotion list and the pruning scratch emptied.  After it: the
+// group's segment becomes [begin, head).
+constexpr int kSlotBlock = 1024;
+struct RingBeginArgs {
+  Ring *ring_a, *ring_f;
+  const unsigned long long *seg_a, *seg_f;
+  int n_groups;
+  int64_t cap_a, cap_f;
+  uint32_t *counters;
+  const int32_t *members;             // the group's members
+  int n_members;
+  const Meta *meta;
+  int r, fcap;
+  unsigned long long *slot_in;        // [n_members]
+  unsigned long long *slot_blk;       // [ceil(n_members / kSlotBlock)]
+  uint32_t *hflag;                    // host-mapped flag raised when a ring is full
+};
+hipError_t launch_ring_begin(const RingBeginArgs &b, hipStream_t st);
 hipError_t launch_ring_end(Ring *ra, Ring *rf, unsigned long long *seg_a, unsigned long long *seg_f, int g,
                            hipStream_t st);
 // copy every factored state's components into new rings at the given positions (arena growth)

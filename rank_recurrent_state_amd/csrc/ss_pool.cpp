@@ -4,11 +4,12 @@
 // Pool layout (SinkState 4.4 "Memory layout": active and frozen factors in
 // their own contiguous regions, offsets per state).  Each region is a ring of
 // components; the states are listed by compaction group, and each group's
-// components form one exactly packed segment of the ring.  A compaction of
-// group g allocates the group's new segment at the ring head (never writing
-// what may still be read) and releases the old one, so with the groups laid
-// out in the order in which they fall due the ring holds the live components
-// plus one group's growth.  The host bounds the ring usage without waiting
+// components form one segment of the ring (exactly packed when laid out or
+// re-packed; after a compaction each member's slot may hold up to its pad
+// size of slack).  A compaction of group g places the group's new segment at
+// the ring head (never writing what may still be read) and releases the old
+// one, so with the groups laid out in the order in which they fall due the
+// ring holds the live components plus one group's growth.  The host bounds the ring usage without waiting
 // for the device (see ensure_ring_space) and re-packs, growing the ring,
 // only when the bound says the next compaction might not fit.
 #include <hip/hip_runtime.h>
@@ -67,6 +68,7 @@ struct ss_pool {
   size_t ring_bytes[2] = {0, 0};
   ss::Ring *ring = nullptr;            // [2]
   unsigned long long *seg = nullptr;   // [2][2 G]: virtual start, end of each group's segment
+  unsigned long long *slot_in = nullptr, *slot_blk = nullptr;  // a compaction's member slots (largest group)
   // Segments of each ring in allocation order (group -1: a released gap), each with an upper
   // bound of its size; the latest record of a group is its live segment.
   struct RingRec { int64_t seq; int g; int64_t n; };
@@ -630,7 +632,7 @@ static ss_status pool_create(const ss_pool_desc *d, const ss_init *init, const f
     // device allocation, and large ones are slow (tens of ms per GB here), so when that maximum
     // fits in a quarter of the free device memory it is reserved at once; otherwise the active
     // ring starts at its maximum and the frozen ring at twice its contents plus one group's
-    // growth, and they grow when needed.  Segments stay exactly packed either way.
+    // growth, and they grow when needed.  Either way a state's slot never exceeds its cap.
     int64_t nf = 0, ngmax = 0;
     for (int g = 0; g < G; ++g) ngmax = std::max(ngmax, p->group_size[g]);
     for (int64_t s = 0; s < N; ++s) nf += cnt[0][s] >= 0 ? 1 : 0;
@@ -646,6 +648,9 @@ static ss_status pool_create(const ss_pool_desc *d, const ss_init *init, const f
       cap_ring[R] = std::max<int64_t>({1, tot[R], d->arena_components ? d->arena_components : autocap});
       if (cap_ring[R] >= (int64_t)INT32_MAX) return fail(SS_ERR_CAPACITY, "too many components for 32-bit offsets");
     }
+    // a compaction sums its members' slots in 32 bits per ring
+    if (ngmax * (int64_t)std::max(r, fcap) >= (int64_t)INT32_MAX)
+      return fail(SS_ERR_CAPACITY, "a compaction group holds too many components for 32-bit slot sums");
   }
   std::vector<float> &epsv = p->eps_host;
   epsv.assign(N, 0.f);
@@ -663,6 +668,10 @@ static ss_status pool_create(const ss_pool_desc *d, const ss_init *init, const f
     for (int R = 0; R < 2; ++R) chk(ring_alloc(p, cap_ring[R], &p->ring_blk[R], &p->ring_bytes[R], &p->arena(R)));
     chk(dalloc(p, &p->ring, 2));
     chk(dalloc(p, &p->seg, 4 * (size_t)G));
+    int64_t gmax = 0;
+    for (int g = 0; g < G; ++g) gmax = std::max(gmax, p->group_size[g]);
+    chk(dalloc(p, &p->slot_in, (size_t)gmax + 1));
+    chk(dalloc(p, &p->slot_blk, (size_t)(gmax + ss::kSlotBlock - 1) / ss::kSlotBlock + 1));
     chk(dalloc(p, &p->pk, (size_t)N * K * dk));
     chk(dalloc(p, &p->pw, (size_t)N * K * dv));
     chk(dalloc(p, &p->pc, (size_t)N * K));
@@ -959,8 +968,13 @@ static int frozen_max(const ss_pool *p) {
 
 static hipError_t enqueue_compact_group(ss_pool *p, int g, bool with_dense, bool timing, hipStream_t stream,
                                         const uint8_t *sel = nullptr) {
-  hipError_t e = ss::launch_ring_begin(p->ring, p->ring + 1, p->seg, p->seg + 2 * p->G, p->G, p->act.cap, p->frz.cap,
-                                       p->counters, stream);
+  ss::RingBeginArgs rb{};
+  rb.ring_a = p->ring; rb.ring_f = p->ring + 1; rb.seg_a = p->seg; rb.seg_f = p->seg + 2 * p->G; rb.n_groups = p->G;
+  rb.cap_a = p->act.cap; rb.cap_f = p->frz.cap; rb.counters = p->counters;
+  rb.members = p->members + p->group_start[g]; rb.n_members = (int)p->group_size[g]; rb.meta = p->meta;
+  rb.r = p->r; rb.fcap = p->fcap; rb.slot_in = p->slot_in; rb.slot_blk = p->slot_blk;
+  rb.hflag = p->hflags_dev + HF_RING;
+  hipError_t e = ss::launch_ring_begin(rb, stream);
   if (e != hipSuccess) return e;
   if (with_dense) {
     ss::DenseArgs da{};
@@ -978,6 +992,7 @@ static hipError_t enqueue_compact_group(ss_pool *p, int g, bool with_dense, bool
   a.members = p->members + p->group_start[g];
   a.eps = p->eps; a.meta = p->meta; a.act = p->act; a.frz = p->frz;
   a.ring_a = p->ring; a.ring_f = p->ring + 1; a.hflag = p->hflags_dev + HF_RING;
+  a.slot_in = p->slot_in; a.slot_blk = p->slot_blk;
   a.pk = p->pk; a.pw = p->pw; a.pc = p->pc; a.promote_list = p->promote_list; a.counters = p->counters;
   a.acct_flops = p->acct + ss::A_COMPACT_FLOPS * ss::kAcctSlots;
   a.acct_states = p->acct + ss::A_COMPACT_STATES * ss::kAcctSlots;
