@@ -153,8 +153,9 @@ __global__ __launch_bounds__(64 * kFactWaves) void k_decode_factored(DecodeArgs 
   // runs: each group's sum, and so the result, does not depend on where the ring wraps.  In a
   // chunk starting at list index gs, group g takes the chunk's pairs p = u * G + ((g - gs) mod G).
   auto slot = [&](const Chunk &c, int u) -> uint32_t { return (uint32_t)(u * G + ((grp - c.sh) & (G - 1))); };
-  // the pair of unroll slot u, clamped into the chunk's run
-  auto load = [&](const Chunk &c, float4 (&x)[UN], float4 (&y)[UN], float (&wt)[UN]) {
+  // the pair of unroll slot u, clamped into the chunk's run; the chunk's weights in one load (lane l
+  // holds the weight of pair l mod C), handed to the lane groups by a cross-lane permute
+  auto load = [&](const Chunk &c, float4 (&x)[UN], float4 (&y)[UN], float &wl) {
 #pragma unroll
     for (int u = 0; u < UN; ++u) {
       const uint32_t pc = min(slot(c, u), (uint32_t)(c.cnt - 1));
@@ -171,13 +172,14 @@ __global__ __launch_bounds__(64 * kFactWaves) void k_decode_factored(DecodeArgs 
         x[u] = ldf4nt(c.xf + ox);
         y[u] = ldf4nt(c.yf + oy);
       }
-      wt[u] = ldnt(c.w + pc);
     }
+    wl = ldnt(c.w + min((uint32_t)(lane % C), (uint32_t)(c.cnt - 1)));
   };
-  auto reduce = [&](const Chunk &c, const float4 (&x)[UN], const float4 (&y)[UN], const float (&wt)[UN]) {
+  auto reduce = [&](const Chunk &c, const float4 (&x)[UN], const float4 (&y)[UN], float wl) {
 #pragma unroll
     for (int u = 0; u < UN; ++u) {
-      const float wu = (slot(c, u) < (uint32_t)c.cnt) ? wt[u] : 0.f;  // the clamped pairs weigh nothing
+      const float wp = __shfl(wl, (int)slot(c, u));
+      const float wu = (slot(c, u) < (uint32_t)c.cnt) ? wp : 0.f;  // the clamped pairs weigh nothing
       const float cq = group_sum<P>(dot4(x[u], qs)) * wu;
       acc = fma4(cq, y[u], acc);
       if (delta) {
@@ -189,7 +191,7 @@ __global__ __launch_bounds__(64 * kFactWaves) void k_decode_factored(DecodeArgs 
   // double-buffered: the next chunk's loads are in flight while the current one is reduced
   {
     float4 xA[UN], yA[UN], xB[UN], yB[UN];
-    float wA[UN], wB[UN];
+    float wA, wB;
     Chunk cA, cB;
     bool hA = next(cA);
     if (hA) load(cA, xA, yA, wA);
@@ -778,7 +780,7 @@ hipError_t decode_factored_p(const DecodeArgs &a, int P, hipStream_t st) {
     case 8: hipLaunchKernelGGL((k_decode_factored<8, 2, RO, AD, F, DG>), grid, block, 0, st, a); break;
     case 16: hipLaunchKernelGGL((k_decode_factored<16, 2, RO, AD, F, DG>), grid, block, 0, st, a); break;
 #ifndef SS_FACT_UN32
-#define SS_FACT_UN32 4
+#define SS_FACT_UN32 2
 #endif
     case 32: hipLaunchKernelGGL((k_decode_factored<32, SS_FACT_UN32, RO, AD, F, DG>), grid, block, 0, st, a); break;
     case 64: hipLaunchKernelGGL((k_decode_factored<64, 8, RO, AD, F, DG>), grid, block, 0, st, a); break;
