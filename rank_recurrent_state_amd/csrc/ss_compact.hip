@@ -604,27 +604,36 @@ __global__ __launch_bounds__(256) void k_compact_h(CompactArgs a) {
       else if (lane < mcol) wgt = a.pc[(int64_t)s * K + (lane - ra)] * gamma;
       scw[lane] = wgt;
     }
-    // CGS2 of both sides at once; R goes to LDS row-major, R[i * 16 + jj] = R(i, jj).  A column
-    // whose residual is at most 1e-5 of its input norm is dependent: it and its R row are zeroed.
+    // Gram-Schmidt of both sides at once, reorthogonalized by the criterion of Daniel, Gragg,
+    // Kaufman and Stewart (1976): a second projection pass runs only when the first one removed more
+    // than half of the column's squared norm (for both sides at once, so the wave stays uniform);
+    // otherwise one pass already leaves the column orthogonal to working precision.  R goes to LDS
+    // row-major, R[i * 16 + jj] = R(i, jj).  A column whose residual is at most 1e-5 of its input
+    // norm is dependent: it and its R row are zeroed.
     float *Rs = side ? Rr : Rl;
 #pragma unroll
     for (int jj = 0; jj < kMaxM; ++jj) {
       if (jj < mcol) {
         const float n0 = group_sum<32>(dotb<NB>(x[jj], x[jj]));
         float myr = 0.f;  // R(r, jj) for r < jj
+        float nu = n0;
+        bool again = true;  // the second pass (wave-uniform)
 #pragma unroll
         for (int pass = 0; pass < 2; ++pass) {
-          float du[kMaxM];
+          if (jj > 0 && (pass == 0 || again)) {
+            float du[kMaxM];
 #pragma unroll
-          for (int i = 0; i < jj; ++i) du[i] = group_sum<32>(dotb<NB>(x[i], x[jj]));
+            for (int i = 0; i < jj; ++i) du[i] = group_sum<32>(dotb<NB>(x[i], x[jj]));
 #pragma unroll
-          for (int i = 0; i < jj; ++i) {
-            myr += (r == i) ? du[i] : 0.f;
+            for (int i = 0; i < jj; ++i) {
+              myr += (r == i) ? du[i] : 0.f;
 #pragma unroll
-            for (int b = 0; b < NB; ++b) x[jj][b] = fma4(-du[i], x[i][b], x[jj][b]);
+              for (int b = 0; b < NB; ++b) x[jj][b] = fma4(-du[i], x[i][b], x[jj][b]);
+            }
+            nu = group_sum<32>(dotb<NB>(x[jj], x[jj]));
+            if (pass == 0) again = __builtin_amdgcn_ballot_w64(nu < 0.5f * n0) != 0ull;
           }
         }
-        const float nu = group_sum<32>(dotb<NB>(x[jj], x[jj]));
         const bool kk = nu > 0.f && nu > kTau2 * n0;
         const float su = sqrtf(nu);
         const float iv = kk ? 1.0f / su : 0.f;

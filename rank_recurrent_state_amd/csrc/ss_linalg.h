@@ -259,10 +259,11 @@ __device__ inline int jacobi16n(float *Cm, float *Vh, float *nrm, int m, int lan
       const float gg = group_sum<8>(fmaf(x.x, y.x, x.y * y.y));
       const bool rot = act && gg != 0.f && gg * gg > tol2 * (aa * bb);
       if (rot) {
-        const float zeta = (bb - aa) * (0.5f * __builtin_amdgcn_rcpf(gg));
-        const float az = fabsf(zeta);
-        const float t = az > 1e10f ? 0.5f * __builtin_amdgcn_rcpf(zeta)
-                                   : copysignf(__builtin_amdgcn_rcpf(az + __builtin_amdgcn_sqrtf(fmaf(zeta, zeta, 1.f))), zeta);
+        // t = tan of the rotation angle, the root of smaller magnitude of t^2 + 2 zeta t - 1 = 0 with
+        // zeta = (b - a) / (2 g), written without zeta: t = sign(d) 2 g / (|d| + sqrt(d^2 + 4 g^2)),
+        // d = b - a (Rutishauser's form; no division by g and no large-zeta branch)
+        const float d = bb - aa, g2 = gg + gg;
+        const float t = (d < 0.f ? -g2 : g2) * __builtin_amdgcn_rcpf(fabsf(d) + __builtin_amdgcn_sqrtf(fmaf(d, d, g2 * g2)));
         const float c = __builtin_amdgcn_rsqf(fmaf(t, t, 1.f)), sn = c * t;
         *reinterpret_cast<float2 *>(Cm + ii * 16 + 2 * sub) = make_float2(c * x.x - sn * y.x, c * x.y - sn * y.y);
         *reinterpret_cast<float2 *>(Cm + jj * 16 + 2 * sub) = make_float2(sn * x.x + c * y.x, sn * x.y + c * y.y);
