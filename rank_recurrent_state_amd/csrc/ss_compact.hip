@@ -569,6 +569,7 @@ __global__ __launch_bounds__(256) void k_compact_h(CompactArgs a) {
   const bool work = live && n > 0 && !keep;  // a Brand update; otherwise the components move unchanged
   const int mcol = ra + n;
   int kl = 0, kf = 0, total = 0, ra2 = ra, rf2 = rf, sweeps = 0;
+  int proj = 0;  // column projections made by the Gram-Schmidt passes
   bool jlimit = false;
   float4 x[kMaxM][NB];
   if (work) {
@@ -632,6 +633,7 @@ __global__ __launch_bounds__(256) void k_compact_h(CompactArgs a) {
             }
             nu = group_sum<32>(dotb<NB>(x[jj], x[jj]));
             if (pass == 0) again = __builtin_amdgcn_ballot_w64(nu < 0.5f * n0) != 0ull;
+            proj += jj;
           }
         }
         const bool kk = nu > 0.f && nu > kTau2 * n0;
@@ -675,16 +677,50 @@ __global__ __launch_bounds__(256) void k_compact_h(CompactArgs a) {
           acc = fmaf(rl[4 * h + 3], b4.w, acc);
         }
         Cm[j * 16 + i] = acc;
-        Vh[j * 16 + i] = (i == j) ? 1.f : 0.f;
+        Vh[j * 16 + i] = acc;  // C kept: the rotations are recovered from it below
       }
     }
     wave_sync();
-    sweeps = jacobi16n(Cm, Vh, sraw, mcol, lane, &jlimit);  // sraw holds the column norms meanwhile
+    sweeps = jacobi16c(Cm, sraw, mcol, lane, &jlimit);  // sraw holds the column norms meanwhile
     if (lane < 16) {
       float xx = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) xx = fmaf(Cm[lane * 16 + i], Cm[lane * 16 + i], xx);
       sraw[lane] = lane < mcol ? sqrtf(xx) : -1.f;
+    }
+    wave_sync();
+    // right singular vectors of C: V(:, j) = C^T b_j / s_j^2 (see jacobi16c), lane l forming rows
+    // l mod 16 of the four columns l / 16 + 4 q; C is read whole before V overwrites it
+    {
+      const int row = lane & 15, j0 = lane >> 4;
+      float c0[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 a4 = *reinterpret_cast<const float4 *>(Vh + row * 16 + 4 * q);
+        c0[4 * q] = a4.x;
+        c0[4 * q + 1] = a4.y;
+        c0[4 * q + 2] = a4.z;
+        c0[4 * q + 3] = a4.w;
+      }
+      float vq[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = j0 + 4 * q;
+        float acc = 0.f;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const float4 b4 = *reinterpret_cast<const float4 *>(Cm + j * 16 + 4 * h);
+          acc = fmaf(c0[4 * h], b4.x, acc);
+          acc = fmaf(c0[4 * h + 1], b4.y, acc);
+          acc = fmaf(c0[4 * h + 2], b4.z, acc);
+          acc = fmaf(c0[4 * h + 3], b4.w, acc);
+        }
+        const float sj = sraw[j];
+        vq[q] = sj > 0.f ? acc / (sj * sj) : 0.f;
+      }
+      wave_sync();
+#pragma unroll
+      for (int q = 0; q < 4; ++q) Vh[(j0 + 4 * q) * 16 + row] = vq[q];
     }
     wave_sync();
     if (lane < mcol) {
@@ -842,8 +878,8 @@ __global__ __launch_bounds__(256) void k_compact_h(CompactArgs a) {
     }
     if (jlimit) __hip_atomic_fetch_add(&a.counters[C_JACOBI_LIMIT], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const unsigned long long D = (unsigned long long)(dk + dv), mm = (unsigned long long)mcol;
-    const unsigned long long flops = 4ull * D * mm * (mm - 1) + 2ull * mm * mm * mm +
-                                     9ull * mm * mm * (mm - 1) * (unsigned long long)sweeps +
+    const unsigned long long flops = 4ull * D * (unsigned long long)proj + 4ull * mm * mm * mm +
+                                     6ull * mm * mm * (mm - 1) * (unsigned long long)sweeps +
                                      2ull * D * mm * (unsigned long long)kl;
     __hip_atomic_fetch_add(&a.acct_flops[s & (kAcctSlots - 1)], flops, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_fetch_add(&a.acct_states[s & (kAcctSlots - 1)], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

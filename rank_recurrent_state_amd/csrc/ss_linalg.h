@@ -285,4 +285,62 @@ __device__ inline int jacobi16n(float *Cm, float *Vh, float *nrm, int m, int lan
   return sweep;
 }
 
+// jacobi16n without the accumulated rotations: only the columns of Cm turn (B = C J); the caller
+// recovers J from B.  At convergence B^T B = diag(s^2) and C^T C = J diag(s^2) J^T, so
+// C^T B = J diag(s^2): column j of J is C^T b_j / s_j^2 for s_j > 0 (the columns with s_j = 0 carry
+// no component).  This halves the work per rotation.
+__device__ inline int jacobi16c(float *Cm, float *nrm, int m, int lane, bool *limit = nullptr) {
+  if (limit) *limit = false;
+  const int M = (m + 1) & ~1;
+  if (M < 2) return 0;
+  const int np = M >> 1, rounds = M - 1;
+  const int p = lane >> 3, sub = lane & 7;
+  const bool act = p < np;
+  const float tol2 = kTolJ * kTolJ;
+  int sweep = 0;
+  while (sweep < kMaxSweeps) {
+    ++sweep;
+    if (lane < 16) {
+      const float2 *cc = reinterpret_cast<const float2 *>(Cm + lane * 16);
+      float xx = 0.f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) xx = fmaf(cc[q].x, cc[q].x, fmaf(cc[q].y, cc[q].y, xx));
+      nrm[lane] = xx;
+    }
+    wave_sync();
+    bool any = false;
+    int ci = p == 0 ? 0 : p % (M - 1);
+    int cj = p == 0 ? M - 1 : (M - 1 - p) % (M - 1);
+    for (int k = 0; k < rounds; ++k) {
+      const int ii = act ? ci : 0, jj = act ? cj : 0;  // clamped: in bounds
+      const float2 x = *reinterpret_cast<const float2 *>(Cm + ii * 16 + 2 * sub);
+      const float2 y = *reinterpret_cast<const float2 *>(Cm + jj * 16 + 2 * sub);
+      const float aa = nrm[ii], bb = nrm[jj];
+      const float gg = group_sum<8>(fmaf(x.x, y.x, x.y * y.y));
+      const bool rot = act && gg != 0.f && gg * gg > tol2 * (aa * bb);
+      if (rot) {
+        // t = tan of the rotation angle, the root of smaller magnitude of t^2 + 2 zeta t - 1 = 0 with
+        // zeta = (b - a) / (2 g), written without zeta: t = sign(d) 2 g / (|d| + sqrt(d^2 + 4 g^2)),
+        // d = b - a (Rutishauser's form; no division by g and no large-zeta branch)
+        const float d = bb - aa, g2 = gg + gg;
+        const float t = (d < 0.f ? -g2 : g2) * __builtin_amdgcn_rcpf(fabsf(d) + __builtin_amdgcn_sqrtf(fmaf(d, d, g2 * g2)));
+        const float c = __builtin_amdgcn_rsqf(fmaf(t, t, 1.f)), sn = c * t;
+        *reinterpret_cast<float2 *>(Cm + ii * 16 + 2 * sub) = make_float2(c * x.x - sn * y.x, c * x.y - sn * y.y);
+        *reinterpret_cast<float2 *>(Cm + jj * 16 + 2 * sub) = make_float2(sn * x.x + c * y.x, sn * x.y + c * y.y);
+        if (sub == 0) {
+          nrm[ii] = fmaf(-t, gg, aa);
+          nrm[jj] = fmaf(t, gg, bb);
+        }
+      }
+      any = any || (__builtin_amdgcn_ballot_w64(rot) != 0ull);
+      wave_sync();
+      ci = (ci + 1 == M - 1) ? 0 : ci + 1;
+      if (p != 0) cj = (cj + 1 == M - 1) ? 0 : cj + 1;
+    }
+    if (!any) break;
+    if (limit && sweep == kMaxSweeps) *limit = true;
+  }
+  return sweep;
+}
+
 }  // namespace ss
