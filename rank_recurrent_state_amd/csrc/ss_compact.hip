@@ -1129,21 +1129,42 @@ __global__ __launch_bounds__(kSlotBlock) void k_slot_scan(const int32_t *members
 // ring's new segment is [begin, begin + its slots) from the old head, and the limit is the oldest
 // live segment's start plus the capacity (seg_x[2 g] / seg_x[2 g + 1]: virtual start / end of
 // group g's segment, start == end: none).  A segment past its limit raises the pool's flag.
+// A group of at most kSlotBlock members (small != 0) is scanned here whole, without k_slot_scan.
 __global__ __launch_bounds__(kSlotBlock) void k_ring_begin(Ring *ra, Ring *rf, const unsigned long long *seg_a,
                                                            const unsigned long long *seg_f, int n_groups,
                                                            int64_t cap_a, int64_t cap_f, uint32_t *counters,
-                                                           unsigned long long *blk, int n_blk, uint32_t *hflag) {
+                                                           unsigned long long *blk, int n_blk, uint32_t *hflag,
+                                                           int small, const int32_t *members, int n_members,
+                                                           const Meta *meta, int r, int fcap,
+                                                           unsigned long long *in_blk) {
   using Scan = hipcub::BlockScan<unsigned long long, kSlotBlock>;
   __shared__ typename Scan::TempStorage tmp;
   unsigned long long carry = 0;
-  for (int b0 = 0; b0 < n_blk; b0 += kSlotBlock) {
-    const int b = b0 + (int)threadIdx.x;
-    const unsigned long long v = b < n_blk ? blk[b] : 0ull;
-    unsigned long long ex, tot;
-    Scan(tmp).ExclusiveSum(v, ex, tot);
-    __syncthreads();  // tmp is used again
-    if (b < n_blk) blk[b] = carry + ex;
-    carry += tot;
+  if (small) {
+    const int mi = (int)threadIdx.x;
+    unsigned long long v = 0;
+    if (mi < n_members) {
+      const uint32_t packed = meta[members[mi]].packed;
+      if (!(meta_flags(packed) & FLAG_DENSE)) {
+        int sa, sf;
+        slot_sizes((int)meta_ra(packed), (int)meta_rf(packed), (int)meta_n(packed), r, fcap, sa, sf);
+        v = (unsigned long long)sa | ((unsigned long long)sf << 32);
+      }
+    }
+    unsigned long long ex;
+    Scan(tmp).ExclusiveSum(v, ex, carry);
+    if (mi < n_members) in_blk[mi] = ex;
+    if (threadIdx.x == 0) blk[0] = 0ull;
+  } else {
+    for (int b0 = 0; b0 < n_blk; b0 += kSlotBlock) {
+      const int b = b0 + (int)threadIdx.x;
+      const unsigned long long v = b < n_blk ? blk[b] : 0ull;
+      unsigned long long ex, tot;
+      Scan(tmp).ExclusiveSum(v, ex, tot);
+      __syncthreads();  // tmp is used again
+      if (b < n_blk) blk[b] = carry + ex;
+      carry += tot;
+    }
   }
   if (threadIdx.x != 0) return;
   counters[C_PROMOTE_COUNT] = 0u;  // the compaction's promotion list starts empty
@@ -1347,11 +1368,13 @@ hipError_t launch_prune_factored(int32_t *list, uint32_t *count, int32_t *tmp, u
 
 hipError_t launch_ring_begin(const RingBeginArgs &b, hipStream_t st) {
   const int n_blk = (b.n_members + kSlotBlock - 1) / kSlotBlock;
-  if (n_blk > 0)
+  const int small = n_blk <= 1 ? 1 : 0;  // one block: scanned by k_ring_begin itself
+  if (!small)
     hipLaunchKernelGGL(k_slot_scan, dim3((unsigned)n_blk), dim3(kSlotBlock), 0, st, b.members, b.n_members, b.meta, b.r,
                        b.fcap, b.slot_in, b.slot_blk);
   hipLaunchKernelGGL(k_ring_begin, dim3(1), dim3(kSlotBlock), 0, st, b.ring_a, b.ring_f, b.seg_a, b.seg_f, b.n_groups,
-                     b.cap_a, b.cap_f, b.counters, b.slot_blk, n_blk, b.hflag);
+                     b.cap_a, b.cap_f, b.counters, b.slot_blk, n_blk, b.hflag, small, b.members, b.n_members, b.meta,
+                     b.r, b.fcap, b.slot_in);
   return hipGetLastError();
 }
 

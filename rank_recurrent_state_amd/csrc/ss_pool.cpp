@@ -966,8 +966,20 @@ static int frozen_max(const ss_pool *p) {
   return p->promote ? std::max(0, std::min(p->fcap, p->L - p->r)) : p->fcap;
 }
 
-static hipError_t enqueue_compact_group(ss_pool *p, int g, bool with_dense, bool timing, hipStream_t stream,
-                                        const uint8_t *sel = nullptr) {
+// with_factored: whether factored members may exist; without them only the dense fold runs (the
+// pool's factored states are all gone dense, and states never return to factored form).
+static hipError_t enqueue_compact_group(ss_pool *p, int g, bool with_dense, bool with_factored, bool timing,
+                                        hipStream_t stream, const uint8_t *sel = nullptr) {
+  if (!with_factored) {
+    if (!with_dense) return hipSuccess;
+    ss::DenseArgs da{};
+    da.dk = p->dk; da.dv = p->dv; da.K = p->K; da.cap_d = (uint32_t)p->cap_d; da.meta = p->meta;
+    da.dense = p->dense; da.dslot = p->dslot; da.pk = p->dpk; da.pw = p->dpw; da.pc = p->dpc;
+    da.members = p->members + p->group_start[g]; da.n_members = (int32_t)p->group_size[g];
+    da.counters = p->counters; da.acct = p->acct; da.diag = p->diag; da.dgam = p->dgam; da.sel = sel;
+    auto fn = [&] { return ss::launch_dense_fold(da, stream); };
+    return timing ? timed(p, SS_KERNEL_DENSE_FOLD, stream, fn) : fn();
+  }
   ss::RingBeginArgs rb{};
   rb.ring_a = p->ring; rb.ring_f = p->ring + 1; rb.seg_a = p->seg; rb.seg_f = p->seg + 2 * p->G; rb.n_groups = p->G;
   rb.cap_a = p->act.cap; rb.cap_f = p->frz.cap; rb.counters = p->counters;
@@ -1017,16 +1029,18 @@ static hipError_t enqueue_prune(ss_pool *p, int64_t fact_grid, hipStream_t strea
                                    p->counters + ss::C_FACT1, fact_grid, p->meta, p->hflags_dev + HF_FACT, stream);
 }
 
-// host bookkeeping after the compaction of group g was enqueued with segment bounds ab
-static void after_compact_group(ss_pool *p, int g, const int64_t (&ab)[2]) {
+// host bookkeeping after the compaction of group g was enqueued with segment bounds ab (ab == nullptr:
+// only the dense fold ran, the rings and the factored states are untouched)
+static void after_compact_group(ss_pool *p, int g, const int64_t (*ab)[2]) {
   p->cons_wait[g] = 1;
   if (p->ca.inflight && p->ca.group == g) p->ca.stale = true;  // its snapshot no longer describes the group
   if ((int)p->ca.last_compact.size() < p->G) p->ca.last_compact.assign(p->G, -1);
   p->ca.last_compact[g] = p->ca.compact_seq++;
+  if (!ab) return;
   for (int R = 0; R < 2; ++R) {  // the group's new segment, by its bound
     p->last_seq[R][g] = p->seq;
-    p->seg_bound[R][g] = ab[R];
-    p->recs[R].push_back({p->seq++, g, ab[R]});
+    p->seg_bound[R][g] = (*ab)[R];
+    p->recs[R].push_back({p->seq++, g, (*ab)[R]});
   }
   if (p->promote) p->dense_upper = std::min<int64_t>(p->cap_d, p->dense_upper + p->group_size[g]);
 }
@@ -1072,15 +1086,19 @@ ss_status ss_compact(ss_pool *p, int32_t group, hipStream_t stream) {
   if (p->force_dense) return SS_OK;  // dense states have no pad to compact
   const int g0 = group < 0 ? 0 : group, g1 = group < 0 ? p->G : group + 1;
   bool any = false;
+  refresh_fact_upper(p);
+  const bool fact = p->fact_upper > 0;  // otherwise every state is dense: only the folds run
   for (int g = g0; g < g1; ++g) {
     if (p->group_size[g] == 0) continue;
     any = true;
     int64_t ab[1][2];
-    st = ensure_ring_space(p, &g, 1, stream, ab);
-    if (st != SS_OK) return st;
-    const hipError_t e = enqueue_compact_group(p, g, p->dense_upper > 0, true, stream);
+    if (fact) {
+      st = ensure_ring_space(p, &g, 1, stream, ab);
+      if (st != SS_OK) return st;
+    }
+    const hipError_t e = enqueue_compact_group(p, g, p->dense_upper > 0, fact, true, stream);
     if (e != hipSuccess) return hip_fail(e, "compact launch");
-    after_compact_group(p, g, ab[0]);
+    after_compact_group(p, g, fact ? ab : nullptr);
   }
   refresh_fact_upper(p);
   if (any && p->promote && p->fact_upper > 0 && p->prune_due++ % kPruneEvery == 0) {
@@ -1122,9 +1140,9 @@ ss_status ss_compact_ids(ss_pool *p, const int32_t *ids, int64_t n, hipStream_t 
     int64_t ab[1][2];
     st = ensure_ring_space(p, &g, 1, stream, ab);
     if (st != SS_OK) return st;
-    e = enqueue_compact_group(p, g, p->dense_upper > 0, true, stream, p->sel);
+    e = enqueue_compact_group(p, g, p->dense_upper > 0, true, true, stream, p->sel);
     if (e != hipSuccess) return hip_fail(e, "compact launch");
-    after_compact_group(p, g, ab[0]);
+    after_compact_group(p, g, &ab[0]);
   }
   refresh_fact_upper(p);
   if (any && p->promote && p->fact_upper > 0 && p->prune_due++ % kPruneEvery == 0) {
@@ -1770,7 +1788,7 @@ ss_status capture_all(ss_step_graph *sg) {
     e = enqueue_decode(p, sg->q, sg->k, sg->v, sg->alpha, sg->beta, sg->o, false, sg->fact_grid, sg->dense_grid,
                        false, sg->cs);
     for (size_t i = 0; e == hipSuccess && i < sg->due[ph].size(); ++i)
-      e = enqueue_compact_group(p, sg->due[ph][i], sg->dense_grid > 0, false, sg->cs);
+      e = enqueue_compact_group(p, sg->due[ph][i], sg->dense_grid > 0, sg->fact_grid > 0, false, sg->cs);
     if (e == hipSuccess && !sg->due[ph].empty() && p->promote && sg->fact_grid > 0)
       e = enqueue_prune(p, sg->fact_grid, sg->cs);
     hipGraph_t graph = nullptr;
@@ -1832,7 +1850,11 @@ ss_status ss_step_graph_launch(ss_step_graph *sg, int64_t step, hipStream_t stre
   const std::vector<int> &due = sg->due[ph];
   std::vector<int64_t> ab(2 * due.size() + 2, 0);
   auto abp = reinterpret_cast<int64_t(*)[2]>(ab.data());
-  if (!due.empty()) {
+  // whether the graph launched below places components in the rings: it does while factored states
+  // remain (fact_upper <= the captured grid, and a pool left with none is captured again below)
+  refresh_fact_upper(p);
+  const bool fact = !p->force_dense && p->fact_upper > 0;
+  if (!due.empty() && fact) {
     st = ensure_ring_space(p, due.data(), (int)due.size(), stream, abp);
     if (st != SS_OK) return st;
   }
@@ -1845,7 +1867,7 @@ ss_status ss_step_graph_launch(ss_step_graph *sg, int64_t step, hipStream_t stre
   }
   const hipError_t e = hipGraphLaunch(sg->exec[ph], stream);
   if (e != hipSuccess) return hip_fail(e, "graph launch");
-  for (size_t i = 0; i < due.size(); ++i) after_compact_group(p, due[i], abp[i]);
+  for (size_t i = 0; i < due.size(); ++i) after_compact_group(p, due[i], fact ? &abp[i] : nullptr);
   p->decode_calls++;
   if (!due.empty()) p->compact_calls++;
   return SS_OK;
