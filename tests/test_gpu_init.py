@@ -2,9 +2,10 @@
 
 Both sides get the same fp32 states and the same Gaussian blocks (drawn on the host from a
 seeded generator).  Compared per state: the number of components (equal, except when a
-singular value lies within 1e-5 sigma_0 of the threshold), each singular value to 1e-4 sigma_0
-(the normwise form used for compaction), and the reconstruction to 1e-4 in relative Frobenius
-norm.
+singular value lies within 1e-5 sigma_0 of the threshold: then the values that differ must all lie
+there, the shared ones are still compared, and the reconstructions may differ by those values only),
+each singular value to 1e-4 sigma_0 (the normwise form used for compaction) and, at or above
+1e-2 sigma_0, to 1e-4 of itself, and the reconstruction to 1e-4 in relative Frobenius norm.
 """
 import numpy as np
 import pytest
@@ -46,25 +47,36 @@ def _check(d_k, d_v, b, nb, iters, eps, kind, n=24, seed=0):
                                 max_rank=max_rank)
     torch.cuda.synchronize()
     u, v, sg, rk = u.cpu().numpy(), v.cpu().numpy(), sg.cpu().numpy(), rk.cpu().numpy()
-    worst = {"sigma": 0.0, "S": 0.0}
+    worst = {"sigma": 0.0, "sigma_rel": 0.0, "S": 0.0}
     guard = 0
     for i in range(n):
         Uo, Vo, so = oracle_rsvd(S[i].astype(np.float64), om[i].astype(np.float64), eps, iters=iters,
                                  max_rank=max_rank)
         R = int(rk[i])
         s0 = so[0] if len(so) else 1.0
+        Rc = min(R, len(so))
+        extra = 0.0
         if R != len(so):
-            # a decision at the threshold or at max_rank may differ only inside the guard band
-            edge = np.abs(so - eps * s0) <= 1e-5 * s0
-            assert edge.any() or abs(R - len(so)) == 0, (i, R, len(so), so)
+            # a decision at the threshold may differ only inside the guard band: every value one
+            # side keeps and the other drops lies within 1e-5 sigma_0 of eps sigma_0
+            xo, xg = so[Rc:], sg[i, Rc:R].astype(np.float64)
+            assert np.all(np.abs(xo - eps * s0) <= 1e-5 * s0) and np.all(np.abs(xg - eps * s0) <= 1e-5 * s0), \
+                (i, R, len(so), so, sg[i, :R])
             guard += 1
+            extra = float(np.sqrt(np.sum(xo ** 2) + np.sum(xg ** 2)))
+        if Rc == 0:
             continue
-        if R == 0:
-            continue
-        worst["sigma"] = max(worst["sigma"], float(np.max(np.abs(sg[i, :R] - so)) / s0))
+        d = np.abs(sg[i, :Rc].astype(np.float64) - so[:Rc])
+        worst["sigma"] = max(worst["sigma"], float(np.max(d) / s0))
+        # per value, where an fp32 factorization can resolve it (Weyl: |d sigma| <= ||d S||, about
+        # 1e-7 sigma_0 here): relative error of every value at or above 1e-2 sigma_0
+        big = so[:Rc] >= 1e-2 * s0
+        if big.any():
+            worst["sigma_rel"] = max(worst["sigma_rel"], float(np.max(d[big] / so[:Rc][big])))
         Sg = (u[i, :R].T.astype(np.float64) * sg[i, :R]) @ v[i, :R].astype(np.float64)
         So = (Uo.T * so) @ Vo
-        worst["S"] = max(worst["S"], np.linalg.norm(Sg - So) / max(np.linalg.norm(So), 1e-30))
+        nS = max(np.linalg.norm(So), 1e-30)
+        worst["S"] = max(worst["S"], max(0.0, np.linalg.norm(Sg - So) - extra) / nS)
     print(kind, (d_k, d_v, b, nb, iters), worst, "guard", guard)
     for k, x in worst.items():
         assert x <= TOL, f"{k}: {x:.3e} > {TOL} ({worst})"
