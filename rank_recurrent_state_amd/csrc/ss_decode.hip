@@ -72,8 +72,10 @@ __global__ __launch_bounds__(64 * kFactWaves) void k_decode_factored(DecodeArgs 
   constexpr int G = 64 / P, C = G * UN;
   const int lane = threadIdx.x & 63;
   const uint32_t li = blockIdx.x * (uint32_t)kFactWaves + (uint32_t)uniform(threadIdx.x >> 6);
-  if (li >= *a.fact_count) return;
-  const int64_t s = uniform(a.fact_ids[li]);
+  const uint32_t cnt = *a.fact_count;
+  if (li >= cnt) return;
+  // a list of every state is a permutation of them: wave li takes state li, one dependent load less
+  const int64_t s = cnt == (uint32_t)a.n_states ? (int64_t)li : uniform(a.fact_ids[li]);
   const int grp = lane / P, col = lane % P;
   const int dk = a.dk, dv = a.dv, K = a.K;
   const bool kin = col < (dk >> 2), vin = col < (dv >> 2);
@@ -288,8 +290,10 @@ __global__ __launch_bounds__(256) void k_decode_factored_h8(DecodeArgs a) {
   constexpr int G = 64 / P;
   const int lane = threadIdx.x & 63;
   const uint32_t li = blockIdx.x * 4u + (uint32_t)uniform(threadIdx.x >> 6);
-  if (li >= *a.fact_count) return;
-  const int64_t s = uniform(a.fact_ids[li]);
+  const uint32_t cnt = *a.fact_count;
+  if (li >= cnt) return;
+  // a list of every state is a permutation of them: wave li takes state li, one dependent load less
+  const int64_t s = cnt == (uint32_t)a.n_states ? (int64_t)li : uniform(a.fact_ids[li]);
   const int grp = lane / P, col = lane % P;
   const int dk = a.dk, dv = a.dv, K = a.K;
   const bool kin = col < (dk >> 3), vin = col < (dv >> 3);

@@ -111,6 +111,7 @@ struct DecodeArgs {
   int dk, dv, K;
   const int32_t *fact_ids;     // ids of the factored states (dense ones are served by the dense kernel)
   const uint32_t *fact_count;  // its length (device)
+  int64_t n_states;            // states in the pool: a list of that length holds every state once
   Meta *meta;
   Arena act, frz;
   float *pk, *pw, *pc;

@@ -935,7 +935,7 @@ static hipError_t enqueue_decode(ss_pool *p, const float *q, const float *k, con
   if (!p->force_dense && fact_grid > 0) {
     ss::DecodeArgs a{};
     a.N = fact_grid; a.dk = p->dk; a.dv = p->dv; a.K = p->K; a.meta = p->meta; a.act = p->act; a.frz = p->frz;
-    a.fact_ids = p->fact_ids[0]; a.fact_count = p->counters + ss::C_FACT0;
+    a.fact_ids = p->fact_ids[0]; a.fact_count = p->counters + ss::C_FACT0; a.n_states = p->N;
     a.pk = p->pk; a.pw = p->pw; a.pc = p->pc; a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.o = o;
     a.counters = p->counters; a.acct = p->acct + ss::A_DECODE_FACTORED * ss::kAcctSlots;
     a.hflag = p->hflags_dev + HF_PAD; a.gam = p->gam;
