@@ -297,7 +297,51 @@ __device__ inline int jacobi16c(float *Cm, float *nrm, int m, int lane, bool *li
   const int p = lane >> 3, sub = lane & 7;
   const bool act = p < np;
   const float tol2 = kTolJ * kTolJ;
+  // the round-robin schedule, the same every sweep: this lane's pair's column indices, 4 bits per
+  // round (rounds 0-7 in lo, 8-14 in hi); inactive pairs read column 0 and never rotate
+  uint32_t ilo = 0, ihi = 0, jlo = 0, jhi = 0;
+  {
+    int ci = p == 0 ? 0 : p % (M - 1);
+    int cj = p == 0 ? M - 1 : (M - 1 - p) % (M - 1);
+    for (int k = 0; k < rounds; ++k) {
+      const uint32_t ii = act ? (uint32_t)ci : 0u, jj = act ? (uint32_t)cj : 0u;
+      if (k < 8) {
+        ilo |= ii << (4 * k);
+        jlo |= jj << (4 * k);
+      } else {
+        ihi |= ii << (4 * (k - 8));
+        jhi |= jj << (4 * (k - 8));
+      }
+      ci = (ci + 1 == M - 1) ? 0 : ci + 1;
+      if (p != 0) cj = (cj + 1 == M - 1) ? 0 : cj + 1;
+    }
+  }
   int sweep = 0;
+  bool any = false;
+  auto round = [&](uint32_t iw, uint32_t jw, int sh) {
+    const uint32_t ii = (iw >> sh) & 15u, jj = (jw >> sh) & 15u;
+    const float2 x = *reinterpret_cast<const float2 *>(Cm + ii * 16 + 2 * sub);
+    const float2 y = *reinterpret_cast<const float2 *>(Cm + jj * 16 + 2 * sub);
+    const float aa = nrm[ii], bb = nrm[jj];
+    const float gg = group_sum<8>(fmaf(x.x, y.x, x.y * y.y));
+    const bool rot = act && gg != 0.f && gg * gg > tol2 * (aa * bb);
+    if (rot) {
+      // t = tan of the rotation angle, the root of smaller magnitude of t^2 + 2 zeta t - 1 = 0 with
+      // zeta = (b - a) / (2 g), written without zeta: t = sign(d) 2 g / (|d| + sqrt(d^2 + 4 g^2)),
+      // d = b - a (Rutishauser's form; no division by g and no large-zeta branch)
+      const float d = bb - aa, g2 = gg + gg;
+      const float t = (d < 0.f ? -g2 : g2) * __builtin_amdgcn_rcpf(fabsf(d) + __builtin_amdgcn_sqrtf(fmaf(d, d, g2 * g2)));
+      const float c = __builtin_amdgcn_rsqf(fmaf(t, t, 1.f)), sn = c * t;
+      *reinterpret_cast<float2 *>(Cm + ii * 16 + 2 * sub) = make_float2(c * x.x - sn * y.x, c * x.y - sn * y.y);
+      *reinterpret_cast<float2 *>(Cm + jj * 16 + 2 * sub) = make_float2(sn * x.x + c * y.x, sn * x.y + c * y.y);
+      if (sub == 0) {
+        nrm[ii] = fmaf(-t, gg, aa);
+        nrm[jj] = fmaf(t, gg, bb);
+      }
+    }
+    any = any || (__builtin_amdgcn_ballot_w64(rot) != 0ull);
+    wave_sync();
+  };
   while (sweep < kMaxSweeps) {
     ++sweep;
     if (lane < 16) {
@@ -308,35 +352,10 @@ __device__ inline int jacobi16c(float *Cm, float *nrm, int m, int lane, bool *li
       nrm[lane] = xx;
     }
     wave_sync();
-    bool any = false;
-    int ci = p == 0 ? 0 : p % (M - 1);
-    int cj = p == 0 ? M - 1 : (M - 1 - p) % (M - 1);
-    for (int k = 0; k < rounds; ++k) {
-      const int ii = act ? ci : 0, jj = act ? cj : 0;  // clamped: in bounds
-      const float2 x = *reinterpret_cast<const float2 *>(Cm + ii * 16 + 2 * sub);
-      const float2 y = *reinterpret_cast<const float2 *>(Cm + jj * 16 + 2 * sub);
-      const float aa = nrm[ii], bb = nrm[jj];
-      const float gg = group_sum<8>(fmaf(x.x, y.x, x.y * y.y));
-      const bool rot = act && gg != 0.f && gg * gg > tol2 * (aa * bb);
-      if (rot) {
-        // t = tan of the rotation angle, the root of smaller magnitude of t^2 + 2 zeta t - 1 = 0 with
-        // zeta = (b - a) / (2 g), written without zeta: t = sign(d) 2 g / (|d| + sqrt(d^2 + 4 g^2)),
-        // d = b - a (Rutishauser's form; no division by g and no large-zeta branch)
-        const float d = bb - aa, g2 = gg + gg;
-        const float t = (d < 0.f ? -g2 : g2) * __builtin_amdgcn_rcpf(fabsf(d) + __builtin_amdgcn_sqrtf(fmaf(d, d, g2 * g2)));
-        const float c = __builtin_amdgcn_rsqf(fmaf(t, t, 1.f)), sn = c * t;
-        *reinterpret_cast<float2 *>(Cm + ii * 16 + 2 * sub) = make_float2(c * x.x - sn * y.x, c * x.y - sn * y.y);
-        *reinterpret_cast<float2 *>(Cm + jj * 16 + 2 * sub) = make_float2(sn * x.x + c * y.x, sn * x.y + c * y.y);
-        if (sub == 0) {
-          nrm[ii] = fmaf(-t, gg, aa);
-          nrm[jj] = fmaf(t, gg, bb);
-        }
-      }
-      any = any || (__builtin_amdgcn_ballot_w64(rot) != 0ull);
-      wave_sync();
-      ci = (ci + 1 == M - 1) ? 0 : ci + 1;
-      if (p != 0) cj = (cj + 1 == M - 1) ? 0 : cj + 1;
-    }
+    any = false;
+    const int r0 = rounds < 8 ? rounds : 8;
+    for (int k = 0; k < r0; ++k) round(ilo, jlo, 4 * k);
+    for (int k = 8; k < rounds; ++k) round(ihi, jhi, 4 * (k - 8));
     if (!any) break;
     if (limit && sweep == kMaxSweeps) *limit = true;
   }
