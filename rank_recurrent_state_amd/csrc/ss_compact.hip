@@ -605,12 +605,15 @@ __global__ __launch_bounds__(256) void k_compact_h(CompactArgs a) {
       else if (lane < mcol) wgt = a.pc[(int64_t)s * K + (lane - ra)] * gamma;
       scw[lane] = wgt;
     }
-    // Gram-Schmidt of both sides at once, reorthogonalized by the criterion of Daniel, Gragg,
-    // Kaufman and Stewart (1976): a second projection pass runs only when the first one removed more
-    // than half of the column's squared norm (for both sides at once, so the wave stays uniform);
-    // otherwise one pass already leaves the column orthogonal to working precision.  R goes to LDS
-    // row-major, R[i * 16 + jj] = R(i, jj).  A column whose residual is at most 1e-5 of its input
-    // norm is dependent: it and its R row are zeroed.
+    // Gram-Schmidt of both sides at once with selective reorthogonalization (the test of Daniel,
+    // Gragg, Kaufman and Stewart, 1976, with a lower threshold): one classical pass leaves along the
+    // earlier columns a rounding residue of a few unit roundoffs times the column's input norm, so
+    // relative to what remains it is that residue times sqrt(n0 / nu).  A second pass runs only when
+    // the first one kept less than kReorth2 of the squared norm, i.e. when that factor exceeds
+    // sqrt(10) (for both sides at once, so the wave stays uniform); above it one pass is orthogonal
+    // to a few unit roundoffs already.  R goes to LDS row-major, R[i * 16 + jj] = R(i, jj).  A
+    // column whose residual is at most 1e-5 of its input norm is dependent: it and its R row are
+    // zeroed.
     float *Rs = side ? Rr : Rl;
 #pragma unroll
     for (int jj = 0; jj < kMaxM; ++jj) {
@@ -632,7 +635,7 @@ __global__ __launch_bounds__(256) void k_compact_h(CompactArgs a) {
               for (int b = 0; b < NB; ++b) x[jj][b] = fma4(-du[i], x[i][b], x[jj][b]);
             }
             nu = group_sum<32>(dotb<NB>(x[jj], x[jj]));
-            if (pass == 0) again = __builtin_amdgcn_ballot_w64(nu < 0.5f * n0) != 0ull;
+            if (pass == 0) again = __builtin_amdgcn_ballot_w64(nu < kReorth2 * n0) != 0ull;
             proj += jj;
           }
         }

@@ -9,6 +9,7 @@
 namespace ss {
 
 constexpr float kTau2 = 1e-10f;  // (1e-5)^2: CGS2 dependent-column test on squared norms
+constexpr float kReorth2 = 0.1f;  // selective Gram-Schmidt: second pass below this share of the squared norm
 constexpr float kTolJ = 1e-6f;   // Jacobi: rotate while |a_i.a_j| > tol |a_i| |a_j|
 constexpr int kMaxSweeps = 16;
 
