@@ -652,11 +652,15 @@ __global__ __launch_bounds__(256) void k_compact_h(CompactArgs a) {
       }
     }
     wave_sync();
-    // core C = R_L diag(w) R_R^T, column-major: lane l forms C(i, j) for i = l mod 16 and the four
-    // j = l / 16 + 4 q from row i of R_L and rows j of R_R (both upper triangular, so the sum over t
-    // runs over t >= max(i, j); the zero terms below it leave the sum unchanged)
+    // core C = R_L diag(w) R_R^T: lane l forms C(i, j) for i = l mod 16 and the four j = l / 16 + 4 q
+    // from row i of R_L and rows j of R_R (both upper triangular, so the sum over t runs over
+    // t >= max(i, j); the zero terms below it leave the sum unchanged).  C goes to Vh column-major
+    // (kept: the rotations are recovered from it below) and, in jacobi16c's layout, over R_L and R_R
+    // once every lane has read them.
+    float *Bj = Rl;  // Rl and Rr: 512 floats
     {
       const int i = lane & 15, j0 = lane >> 4;
+      float cv[4];
       float rl[16];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -679,12 +683,24 @@ __global__ __launch_bounds__(256) void k_compact_h(CompactArgs a) {
           acc = fmaf(rl[4 * h + 2], b4.z, acc);
           acc = fmaf(rl[4 * h + 3], b4.w, acc);
         }
-        Cm[j * 16 + i] = acc;
-        Vh[j * 16 + i] = acc;  // C kept: the rotations are recovered from it below
+        cv[q] = acc;
+      }
+      wave_sync();
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = j0 + 4 * q;
+        Vh[j * 16 + i] = cv[q];
+        Bj[j * 32 + 4 * (i >> 1) + (i & 1)] = cv[q];
       }
     }
     wave_sync();
-    sweeps = jacobi16c(Cm, sraw, mcol, lane, &jlimit);  // sraw holds the column norms meanwhile
+    sweeps = jacobi16c(Bj, mcol, lane, &jlimit);
+    {  // B to Cm, column-major: lane l moves rows 4 (l & 3) to 4 (l & 3) + 3 of column l / 4
+      const float4 *q = reinterpret_cast<const float4 *>(Bj) + 8 * (lane >> 2) + 2 * (lane & 3);
+      const float4 u0 = q[0], u1 = q[1];
+      *reinterpret_cast<float4 *>(Cm + 16 * (lane >> 2) + 4 * (lane & 3)) = make_float4(u0.x, u0.y, u1.x, u1.y);
+    }
+    wave_sync();
     if (lane < 16) {
       float xx = 0.f;
 #pragma unroll

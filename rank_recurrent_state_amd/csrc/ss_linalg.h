@@ -221,76 +221,33 @@ __device__ inline int jacobi16(float *Cm, float *Vh, int m, int lane, bool *limi
   return sweep;
 }
 
-// jacobi16 with the column norms carried: the same pairs, order, stopping rule and rotation, but
-// each round computes only the pair's inner product g; the squared norms a, b of the pair's columns
-// are read from `nrm` (16 floats of LDS) and, after a rotation by t = tan(theta), updated to
-// a - t g and b + t g (the rotation zeroes g).  The norms are recomputed from the columns at the
-// start of every sweep, so the rounding of the updates never accumulates past one sweep.  Each lane
-// of a pair holds two consecutive rows (one 8-byte LDS access per column), and the lanes read the
-// pair's Vh columns before the rotation is decided, so that their latency overlaps the arithmetic.
-__device__ inline int jacobi16n(float *Cm, float *Vh, float *nrm, int m, int lane, bool *limit = nullptr) {
-  if (limit) *limit = false;
-  const int M = (m + 1) & ~1;
-  if (M < 2) return 0;
-  const int np = M >> 1, rounds = M - 1;
-  const int p = lane >> 3, sub = lane & 7;
-  const bool act = p < np;
-  const float tol2 = kTolJ * kTolJ;
-  int sweep = 0;
-  while (sweep < kMaxSweeps) {
-    ++sweep;
-    if (lane < 16) {
-      const float2 *cc = reinterpret_cast<const float2 *>(Cm + lane * 16);
-      float xx = 0.f;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) xx = fmaf(cc[q].x, cc[q].x, fmaf(cc[q].y, cc[q].y, xx));
-      nrm[lane] = xx;
-    }
-    wave_sync();
-    bool any = false;
-    int ci = p == 0 ? 0 : p % (M - 1);
-    int cj = p == 0 ? M - 1 : (M - 1 - p) % (M - 1);
-    for (int k = 0; k < rounds; ++k) {
-      const int ii = act ? ci : 0, jj = act ? cj : 0;  // clamped: in bounds
-      const float2 x = *reinterpret_cast<const float2 *>(Cm + ii * 16 + 2 * sub);
-      const float2 y = *reinterpret_cast<const float2 *>(Cm + jj * 16 + 2 * sub);
-      const float2 vx = *reinterpret_cast<const float2 *>(Vh + ii * 16 + 2 * sub);
-      const float2 vy = *reinterpret_cast<const float2 *>(Vh + jj * 16 + 2 * sub);
-      const float aa = nrm[ii], bb = nrm[jj];
-      const float gg = group_sum<8>(fmaf(x.x, y.x, x.y * y.y));
-      const bool rot = act && gg != 0.f && gg * gg > tol2 * (aa * bb);
-      if (rot) {
-        // t = tan of the rotation angle, the root of smaller magnitude of t^2 + 2 zeta t - 1 = 0 with
-        // zeta = (b - a) / (2 g), written without zeta: t = sign(d) 2 g / (|d| + sqrt(d^2 + 4 g^2)),
-        // d = b - a (Rutishauser's form; no division by g and no large-zeta branch)
-        const float d = bb - aa, g2 = gg + gg;
-        const float t = (d < 0.f ? -g2 : g2) * __builtin_amdgcn_rcpf(fabsf(d) + __builtin_amdgcn_sqrtf(fmaf(d, d, g2 * g2)));
-        const float c = __builtin_amdgcn_rsqf(fmaf(t, t, 1.f)), sn = c * t;
-        *reinterpret_cast<float2 *>(Cm + ii * 16 + 2 * sub) = make_float2(c * x.x - sn * y.x, c * x.y - sn * y.y);
-        *reinterpret_cast<float2 *>(Cm + jj * 16 + 2 * sub) = make_float2(sn * x.x + c * y.x, sn * x.y + c * y.y);
-        *reinterpret_cast<float2 *>(Vh + ii * 16 + 2 * sub) = make_float2(c * vx.x - sn * vy.x, c * vx.y - sn * vy.y);
-        *reinterpret_cast<float2 *>(Vh + jj * 16 + 2 * sub) = make_float2(sn * vx.x + c * vy.x, sn * vx.y + c * vy.y);
-        if (sub == 0) {
-          nrm[ii] = fmaf(-t, gg, aa);
-          nrm[jj] = fmaf(t, gg, bb);
-        }
-      }
-      any = any || (__builtin_amdgcn_ballot_w64(rot) != 0ull);
-      wave_sync();
-      ci = (ci + 1 == M - 1) ? 0 : ci + 1;
-      if (p != 0) cj = (cj + 1 == M - 1) ? 0 : cj + 1;
-    }
-    if (!any) break;
-    if (limit && sweep == kMaxSweeps) *limit = true;
-  }
-  return sweep;
+// (a << 7) + b in one instruction (the compiler emits a shift and an add for it)
+__device__ __forceinline__ uint32_t lshl7_add(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_lshl_add_u32 %0, %1, 7, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
 
-// jacobi16n without the accumulated rotations: only the columns of Cm turn (B = C J); the caller
-// recovers J from B.  At convergence B^T B = diag(s^2) and C^T C = J diag(s^2) J^T, so
-// C^T B = J diag(s^2): column j of J is C^T b_j / s_j^2 for s_j > 0 (the columns with s_j = 0 carry
-// no component).  This halves the work per rotation.
-__device__ inline int jacobi16c(float *Cm, float *nrm, int m, int lane, bool *limit = nullptr) {
+// One-sided Jacobi on the columns of a 16 x 16 matrix B (columns >= m zero) with the same pairs,
+// order, stopping rule and rotation as jacobi16, but without accumulating the rotations: only B
+// turns (B = C J), and the caller recovers J from C.  At convergence B^T B = diag(s^2) and
+// C^T C = J diag(s^2) J^T, so C^T B = J diag(s^2): column j of J is C^T b_j / s_j^2 for s_j > 0
+// (the columns with s_j = 0 carry no component).
+//
+// Each round computes only the pair's inner product g; the squared norms a, b of the pair's columns
+// are carried and, after a rotation by t = tan(theta), updated to a - t g and b + t g (the rotation
+// zeroes g).  They are recomputed from the columns at the start of every sweep, so the rounding of
+// the updates never accumulates past one sweep.  Layout of Bj (512 floats of LDS): column j is 8
+// chunks of 4 floats, chunk c = {B(2c, j), B(2c + 1, j), |b_j|^2, unused}.  The lane holding rows
+// 2c, 2c + 1 of a pair's column reads them and the column's norm with one 16-byte access, and every
+// lane keeps its chunk's copy of the norm current, so no lane waits on another for a norm.
+//
+// t is the root of smaller magnitude of t^2 + 2 zeta t - 1 = 0 with zeta = (b - a) / (2 g), written
+// without zeta: t = sign(d) 2 g / (|d| + sqrt(d^2 + 4 g^2)), d = b - a (Rutishauser's form; no
+// division by g and no large-zeta branch); c = 1 / sqrt(1 + t^2), s = c t.  The round-robin
+// schedule is the same every sweep and is packed once: 4 bits per round of this lane's pair's
+// column indices.
+__device__ inline int jacobi16c(float *Bj, int m, int lane, bool *limit = nullptr) {
   if (limit) *limit = false;
   const int M = (m + 1) & ~1;
   if (M < 2) return 0;
@@ -298,8 +255,7 @@ __device__ inline int jacobi16c(float *Cm, float *nrm, int m, int lane, bool *li
   const int p = lane >> 3, sub = lane & 7;
   const bool act = p < np;
   const float tol2 = kTolJ * kTolJ;
-  // the round-robin schedule, the same every sweep: this lane's pair's column indices, 4 bits per
-  // round (rounds 0-7 in lo, 8-14 in hi); inactive pairs read column 0 and never rotate
+  // rounds 0-7 in lo, 8-14 in hi; inactive pairs read column 0 and never rotate
   uint32_t ilo = 0, ihi = 0, jlo = 0, jhi = 0;
   {
     int ci = p == 0 ? 0 : p % (M - 1);
@@ -317,40 +273,37 @@ __device__ inline int jacobi16c(float *Cm, float *nrm, int m, int lane, bool *li
       if (p != 0) cj = (cj + 1 == M - 1) ? 0 : cj + 1;
     }
   }
+  // LDS byte address of this lane's chunk of column 0; column i's is 128 i past it
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4f lds_v4f;
+  const uint32_t base = (uint32_t)(size_t)(lds_v4f *)(reinterpret_cast<v4f *>(Bj) + sub);
   int sweep = 0;
   bool any = false;
   auto round = [&](uint32_t iw, uint32_t jw, int sh) {
-    const uint32_t ii = (iw >> sh) & 15u, jj = (jw >> sh) & 15u;
-    const float2 x = *reinterpret_cast<const float2 *>(Cm + ii * 16 + 2 * sub);
-    const float2 y = *reinterpret_cast<const float2 *>(Cm + jj * 16 + 2 * sub);
-    const float aa = nrm[ii], bb = nrm[jj];
+    lds_v4f *px = (lds_v4f *)(size_t)lshl7_add(__builtin_amdgcn_ubfe(iw, sh, 4), base);
+    lds_v4f *py = (lds_v4f *)(size_t)lshl7_add(__builtin_amdgcn_ubfe(jw, sh, 4), base);
+    const v4f x = *px, y = *py;
     const float gg = group_sum<8>(fmaf(x.x, y.x, x.y * y.y));
-    const bool rot = act && gg != 0.f && gg * gg > tol2 * (aa * bb);
+    // |a b|: a carried norm may round below zero; then g = 0 must still not rotate
+    const bool rot = act && gg * gg > tol2 * fabsf(x.z * y.z);
     if (rot) {
-      // t = tan of the rotation angle, the root of smaller magnitude of t^2 + 2 zeta t - 1 = 0 with
-      // zeta = (b - a) / (2 g), written without zeta: t = sign(d) 2 g / (|d| + sqrt(d^2 + 4 g^2)),
-      // d = b - a (Rutishauser's form; no division by g and no large-zeta branch)
-      const float d = bb - aa, g2 = gg + gg;
+      const float d = y.z - x.z, g2 = gg + gg;
       const float t = (d < 0.f ? -g2 : g2) * __builtin_amdgcn_rcpf(fabsf(d) + __builtin_amdgcn_sqrtf(fmaf(d, d, g2 * g2)));
       const float c = __builtin_amdgcn_rsqf(fmaf(t, t, 1.f)), sn = c * t;
-      *reinterpret_cast<float2 *>(Cm + ii * 16 + 2 * sub) = make_float2(c * x.x - sn * y.x, c * x.y - sn * y.y);
-      *reinterpret_cast<float2 *>(Cm + jj * 16 + 2 * sub) = make_float2(sn * x.x + c * y.x, sn * x.y + c * y.y);
-      if (sub == 0) {
-        nrm[ii] = fmaf(-t, gg, aa);
-        nrm[jj] = fmaf(t, gg, bb);
-      }
+      *px = v4f{c * x.x - sn * y.x, c * x.y - sn * y.y, fmaf(-t, gg, x.z), 0.f};
+      *py = v4f{sn * x.x + c * y.x, sn * x.y + c * y.y, fmaf(t, gg, y.z), 0.f};
     }
     any = any || (__builtin_amdgcn_ballot_w64(rot) != 0ull);
     wave_sync();
   };
   while (sweep < kMaxSweeps) {
     ++sweep;
-    if (lane < 16) {
-      const float2 *cc = reinterpret_cast<const float2 *>(Cm + lane * 16);
-      float xx = 0.f;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) xx = fmaf(cc[q].x, cc[q].x, fmaf(cc[q].y, cc[q].y, xx));
-      nrm[lane] = xx;
+    {  // norms: lane l sums chunks 2 (l & 3) and 2 (l & 3) + 1 of column l / 4, four lanes per column
+      float4 *q = reinterpret_cast<float4 *>(Bj) + 8 * (lane >> 2) + 2 * (lane & 3);
+      const float4 u0 = q[0], u1 = q[1];
+      const float xx = group_sum<4>(fmaf(u0.x, u0.x, fmaf(u0.y, u0.y, fmaf(u1.x, u1.x, u1.y * u1.y))));
+      reinterpret_cast<float *>(q)[2] = xx;
+      reinterpret_cast<float *>(q)[6] = xx;
     }
     wave_sync();
     any = false;
