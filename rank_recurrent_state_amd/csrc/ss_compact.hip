@@ -619,24 +619,32 @@ __global__ __launch_bounds__(256) void k_compact_h(CompactArgs a) {
     for (int jj = 0; jj < kMaxM; ++jj) {
       if (jj < mcol) {
         const float n0 = group_sum<32>(dotb<NB>(x[jj], x[jj]));
-        float myr = 0.f;  // R(r, jj) for r < jj
         float nu = n0;
-        bool again = true;  // the second pass (wave-uniform)
+        if (jj > 0) {
+          float du[kMaxM];  // R(i, jj), i < jj: the same value in every lane of the side
 #pragma unroll
-        for (int pass = 0; pass < 2; ++pass) {
-          if (jj > 0 && (pass == 0 || again)) {
-            float du[kMaxM];
+          for (int i = 0; i < jj; ++i) du[i] = group_sum<32>(dotb<NB>(x[i], x[jj]));
 #pragma unroll
-            for (int i = 0; i < jj; ++i) du[i] = group_sum<32>(dotb<NB>(x[i], x[jj]));
+          for (int i = 0; i < jj; ++i) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) x[jj][b] = fma4(-du[i], x[i][b], x[jj][b]);
+          }
+          nu = group_sum<32>(dotb<NB>(x[jj], x[jj]));
+          proj += jj;
+          if (__builtin_amdgcn_ballot_w64(nu < kReorth2 * n0) != 0ull) {  // the second pass (wave-uniform)
 #pragma unroll
             for (int i = 0; i < jj; ++i) {
-              myr += (r == i) ? du[i] : 0.f;
+              const float e = group_sum<32>(dotb<NB>(x[i], x[jj]));
 #pragma unroll
-              for (int b = 0; b < NB; ++b) x[jj][b] = fma4(-du[i], x[i][b], x[jj][b]);
+              for (int b = 0; b < NB; ++b) x[jj][b] = fma4(-e, x[i][b], x[jj][b]);
+              du[i] += e;
             }
             nu = group_sum<32>(dotb<NB>(x[jj], x[jj]));
-            if (pass == 0) again = __builtin_amdgcn_ballot_w64(nu < kReorth2 * n0) != 0ull;
             proj += jj;
+          }
+          if (r == 0) {  // one lane per side writes the column's entries above the diagonal
+#pragma unroll
+            for (int i = 0; i < jj; ++i) Rs[i * 16 + jj] = du[i];
           }
         }
         const bool kk = nu > 0.f && nu > kTau2 * n0;
@@ -644,7 +652,7 @@ __global__ __launch_bounds__(256) void k_compact_h(CompactArgs a) {
         const float iv = kk ? 1.0f / su : 0.f;
 #pragma unroll
         for (int b = 0; b < NB; ++b) x[jj][b] = scale4(iv, x[jj][b]);
-        if (r < kMaxM) Rs[r * 16 + jj] = r < jj ? myr : (r == jj ? (kk ? su : 0.f) : 0.f);
+        if (r < kMaxM && r >= jj) Rs[r * 16 + jj] = r == jj ? (kk ? su : 0.f) : 0.f;
       } else {
 #pragma unroll
         for (int b = 0; b < NB; ++b) x[jj][b] = zero4();
@@ -695,21 +703,28 @@ __global__ __launch_bounds__(256) void k_compact_h(CompactArgs a) {
     }
     wave_sync();
     sweeps = jacobi16c(Bj, mcol, lane, &jlimit);
-    {  // B to Cm, column-major: lane l moves rows 4 (l & 3) to 4 (l & 3) + 3 of column l / 4
-      const float4 *q = reinterpret_cast<const float4 *>(Bj) + 8 * (lane >> 2) + 2 * (lane & 3);
+    // the singular values s_j = |b_j| and the left singular vectors u_j = b_j / s_j of C, to Cm
+    // column-major: lane l takes rows 4 (l & 3) to 4 (l & 3) + 3 of column l / 4 (a column with
+    // s_j = 0 stays zero); 1 / s_j goes to sinv (over R_R, once every lane has read B)
+    float *sinv = Rr;
+    {
+      const int col = lane >> 2;
+      const float4 *q = reinterpret_cast<const float4 *>(Bj) + 8 * col + 2 * (lane & 3);
       const float4 u0 = q[0], u1 = q[1];
-      *reinterpret_cast<float4 *>(Cm + 16 * (lane >> 2) + 4 * (lane & 3)) = make_float4(u0.x, u0.y, u1.x, u1.y);
+      const float sj = __builtin_amdgcn_sqrtf(
+          group_sum<4>(fmaf(u0.x, u0.x, fmaf(u0.y, u0.y, fmaf(u1.x, u1.x, u1.y * u1.y)))));
+      const float is = sj > 0.f ? __builtin_amdgcn_rcpf(sj) : 0.f;
+      *reinterpret_cast<float4 *>(Cm + 16 * col + 4 * (lane & 3)) =
+          make_float4(u0.x * is, u0.y * is, u1.x * is, u1.y * is);
+      wave_sync();
+      if ((lane & 3) == 0) {
+        sraw[col] = col < mcol ? sj : -1.f;
+        sinv[col] = is;
+      }
     }
     wave_sync();
-    if (lane < 16) {
-      float xx = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) xx = fmaf(Cm[lane * 16 + i], Cm[lane * 16 + i], xx);
-      sraw[lane] = lane < mcol ? sqrtf(xx) : -1.f;
-    }
-    wave_sync();
-    // right singular vectors of C: V(:, j) = C^T b_j / s_j^2 (see jacobi16c), lane l forming rows
-    // l mod 16 of the four columns l / 16 + 4 q; C is read whole before V overwrites it
+    // right singular vectors of C: V(:, j) = C^T b_j / s_j^2 = C^T u_j / s_j (see jacobi16c), lane l
+    // forming rows l mod 16 of the four columns l / 16 + 4 q; C is read whole before V overwrites it
     {
       const int row = lane & 15, j0 = lane >> 4;
       float c0[16];
@@ -734,8 +749,7 @@ __global__ __launch_bounds__(256) void k_compact_h(CompactArgs a) {
           acc = fmaf(c0[4 * h + 2], b4.z, acc);
           acc = fmaf(c0[4 * h + 3], b4.w, acc);
         }
-        const float sj = sraw[j];
-        vq[q] = sj > 0.f ? acc / (sj * sj) : 0.f;
+        vq[q] = acc * sinv[j];
       }
       wave_sync();
 #pragma unroll
@@ -852,14 +866,13 @@ __global__ __launch_bounds__(256) void k_compact_h(CompactArgs a) {
     const int pos = posL[i];
     if (pos >= total) continue;
     const int j = perm[i];
-    const float inv = side ? 1.f : 1.0f / sgs[i];
-    const float *cf = (side ? Vh : Cm) + j * 16;
+    const float *cf = (side ? Vh : Cm) + j * 16;  // u_j or v_j of C
     float4 o[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) o[b] = zero4();
 #pragma unroll
     for (int tt = 0; tt < kMaxM; ++tt) {
-      const float c = cf[tt] * inv;
+      const float c = cf[tt];
 #pragma unroll
       for (int b = 0; b < NB; ++b) o[b] = fma4(c, x[tt][b], o[b]);
     }
