@@ -91,33 +91,34 @@ __device__ __forceinline__ float ldfnt(const _Float16 *p) { return (float)__buil
 
 // Copy `cnt` components (u, v) starting at ring position c0 of arena `src`
 // to the positions dst_of(f) (a component for which it returns false is dropped).
-// All lanes take float4 pieces of consecutive components, UNC pieces in flight; the source is
-// read once and the destination written once, both with the nontemporal hint.
+// A component is d_k / 4 + d_v / 4 float4 chunks (u's, then v's); lane l moves chunks l, l + 64, ...
+// of every component, so its offsets inside a component are fixed and only the component's slots
+// (wave-uniform) change from one to the next.  UNC components per round keep their loads in flight
+// together; the source is read once and the destination written once, both with the nontemporal
+// hint.  dst_of is called with a wave-uniform f by every lane.
 template <typename F, typename DstOf>
 __device__ __forceinline__ void copy_comps(const Arena &src, int64_t c0, int cnt, int dk, int dv, int lane,
                                            DstOf dst_of) {
-  constexpr int UNC = 8;
+  constexpr int UNC = 4;
   const int dk4 = dk >> 2, tot4 = dk4 + (dv >> 2);
-  const int n = cnt * tot4;
-  for (int e0 = 0; e0 < n; e0 += 64 * UNC) {
-    float4 x[UNC];
+  for (int cb = 0; cb < tot4; cb += 64) {
+    const int c = cb + lane;
+    const bool on = c < tot4;
+    const bool isu = c < dk4;
+    const int off = !on ? 0 : (isu ? 4 * c : 4 * (c - dk4));  // element offset inside u or v (0 when off)
+    for (int f0 = 0; f0 < cnt; f0 += UNC) {
+      float4 x[UNC];
 #pragma unroll
-    for (int q = 0; q < UNC; ++q) {
-      const int e = e0 + q * 64 + lane;
-      const int ec = e < n ? e : n - 1;  // clamped (n >= 1 inside the loop)
-      const int f = ec / tot4, c = ec - f * tot4;
-      const int64_t cs = wrap(c0 + f, src.cap);
-      const F *p = c < dk4 ? src.U<F>() + cs * dk + 4 * c : src.V<F>() + cs * dv + 4 * (c - dk4);
-      x[q] = ldf4nt(p);
-    }
+      for (int q = 0; q < UNC; ++q) {
+        const int f = f0 + q < cnt ? f0 + q : cnt - 1;  // clamped (cnt >= 1 inside the loop)
+        const int64_t cs = wrap(c0 + f, src.cap);
+        x[q] = ldf4nt(isu ? src.U<F>() + cs * dk + off : src.V<F>() + cs * dv + off);
+      }
 #pragma unroll
-    for (int q = 0; q < UNC; ++q) {
-      const int e = e0 + q * 64 + lane;
-      if (e < n) {
-        const int f = e / tot4, c = e - f * tot4;
-        F *du, *dvp;
-        if (dst_of(f, du, dvp)) {
-          stf4nt(c < dk4 ? du + 4 * c : dvp + 4 * (c - dk4), x[q]);  // one 16-byte store
+      for (int q = 0; q < UNC; ++q) {
+        if (f0 + q < cnt) {
+          F *du, *dvp;
+          if (dst_of(f0 + q, du, dvp) && on) stf4nt(isu ? du + off : dvp + off, x[q]);  // one 16-byte store
         }
       }
     }
@@ -471,7 +472,7 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   } else {
     // kept frozen components: copied, sigma scaled by Gamma
     copy_comps<F>(a.frz, off_f, kf, dk, dv, lane, [&](int f, F *&du, F *&dvp) {
-      const int pos = posF[f];
+      const int pos = uniform(posF[f]);  // f is wave-uniform
       if (pos >= total) return false;
       du = slot_u(pos);
       dvp = slot_v(pos);
@@ -886,7 +887,7 @@ __global__ __launch_bounds__(256) void k_compact_h(CompactArgs a) {
   if (lane < kl && posL[lane] < total) *slot_s(posL[lane]) = sgs[lane];
   // kept frozen components: copied, sigma scaled by Gamma
   copy_comps<F>(a.frz, off_f, kf, dk, dv, lane, [&](int f, F *&du, F *&dvp) {
-    const int pos = posF[f];
+    const int pos = uniform(posF[f]);  // f is wave-uniform
     if (pos >= total) return false;
     du = slot_u(pos);
     dvp = slot_v(pos);
