@@ -576,28 +576,30 @@ __global__ __launch_bounds__(256) void k_compact_h(CompactArgs a) {
   if (work) {
     // frozen singular values (scaled by Gamma) to LDS: the merge searches them there
     for (int f = lane; f < rf; f += 64) fsl[f] = a.frz.s[wrap(off_f + f, capF)] * gamma;
-    // columns: [U_a | K] on the d_k lanes, [V_a | W] on the d_v lanes
+    // columns: [U_a | K] on the d_k lanes, [V_a | W] on the d_v lanes; this lane's side's arena and
+    // pad bases and row length are taken once, so a column costs one multiply-add per address
+    {
+      const F *act_b = side ? a.act.V<F>() : a.act.U<F>();
+      const float *pad_b = (side ? a.pw : a.pk) + (int64_t)s * K * dme;
 #pragma unroll
-    for (int jj = 0; jj < kMaxM; ++jj) {
-      const bool valid = jj < mcol;
-      const int j = valid ? jj : mcol - 1;  // clamped: the loads stay in bounds (mcol >= 1 here)
-      const bool isact = j < ra;
-      const int64_t ca = wrap(off_a + (isact ? j : 0), capA);
-      const int64_t slot = isact ? 0 : (int64_t)s * K + (j - ra);
+      for (int jj = 0; jj < kMaxM; ++jj) {
+        const bool valid = jj < mcol;
+        const int j = valid ? jj : mcol - 1;  // clamped: the loads stay in bounds (mcol >= 1 here)
+        const bool isact = j < ra;
+        const int64_t ca = wrap(off_a + (isact ? j : 0), capA);
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const int e = 128 * b + 4 * r;
-        const bool ok = valid && e < dme;
-        const int eo = e < dme ? e : 0;
-        float4 v;
-        if (std::is_same<F, float>::value || !isact) {  // wave-uniform branch
-          const float *src = isact ? (side ? a.act.V<float>() + ca * dv : a.act.U<float>() + ca * dk)
-                                   : (side ? a.pw + slot * dv : a.pk + slot * dk);
-          v = ld4nt(src + eo);
-        } else {
-          v = ldf4nt((side ? a.act.V<F>() + ca * dv : a.act.U<F>() + ca * dk) + eo);
+        for (int b = 0; b < NB; ++b) {
+          const int e = 128 * b + 4 * r;
+          const bool ok = valid && e < dme;
+          const int eo = e < dme ? e : 0;
+          float4 v;
+          if (isact) {  // wave-uniform branch
+            v = ldf4nt(act_b + ca * dme + eo);
+          } else {
+            v = ld4nt(pad_b + (j - ra) * dme + eo);
+          }
+          x[jj][b] = sel4(ok, v);
         }
-        x[jj][b] = sel4(ok, v);
       }
     }
     if (lane < kMaxM) {
