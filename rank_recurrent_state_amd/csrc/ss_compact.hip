@@ -5,14 +5,16 @@
 //   1. U_C = [U_active | pad keys] (d_k x m), V_C = [V_active | pad w]
 //      (d_v x m), weights Gamma * (sigma_active, c); m = r_a + n <= 16.
 //      Element e of a column lives in lane e % 64, register e / 64.
-//   2. Thin QR of both sides by classical Gram-Schmidt with one
-//      re-orthogonalization pass (CGS2); a column whose residual is at most
-//      1e-5 of its own norm is taken as dependent and zeroed (its R row is
-//      then zero too, so it cannot create a spurious component).
+//   2. Thin QR of both sides by classical Gram-Schmidt, a second projection
+//      pass only for a column whose first pass kept less than a tenth of its
+//      squared norm; a column whose residual is at most 1e-5 of its own norm
+//      is taken as dependent and zeroed (its R row is then zero too, so it
+//      cannot create a spurious component).
 //   3. Core C = R_L diag(w) R_R^T (m x m) in LDS.
-//   4. One-sided (Hestenes) Jacobi SVD of C: 8 lanes per column pair, pairs
-//      in round-robin (circle) order so that m/2 disjoint pairs rotate at
-//      once; sweeps until no pair is off-orthogonal by more than 1e-6.
+//   4. One-sided (Hestenes) Jacobi SVD of C on its columns only: 8 lanes per
+//      column pair, pairs in round-robin (circle) order so that m/2 disjoint
+//      pairs rotate at once; sweeps until no pair is off-orthogonal by more
+//      than 1e-6.  The right singular vectors follow from C afterwards.
 //   5. Sort the local singular values; merge them with the frozen ones
 //      (scaled by Gamma) in descending order, local first on ties; drop
 //      sigma < eps * sigma_max and sigma = 0 (SinkState 4.1, 4.2 example).
@@ -175,6 +177,7 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   const bool work = live && n > 0 && !keep;  // a Brand update; otherwise the components move unchanged
   const int mcol = ra + n;
   int kl = 0, kf = 0, total = 0, ra2 = ra, rf2 = rf, sweeps = 0;
+  int proj = 0;  // column projections made by the Gram-Schmidt passes
   bool jlimit = false;
   float uc[kMaxM][NS], vc[kMaxM][NS];
   float gr[NS];  // DIAG: the state's decays, row lane + 64 t (0 past d_k)
@@ -270,24 +273,81 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
       else if (lane < mcol) wgt = a.pc[(int64_t)s * K + (lane - ra)] * gamma;
       scw[lane] = wgt;
     }
-    cgs2_pair<NS>(uc, vc, mcol, lane, Rl, Rr);
+    cgs_pair<NS>(uc, vc, mcol, lane, Rl, Rr, proj);
     wave_sync();
-    for (int e = lane; e < 256; e += 64) {
-      const int i = e & 15, j = e >> 4;
-      float acc = 0.f;
-      if (i < mcol && j < mcol) {
-        for (int t = (i > j ? i : j); t < mcol; ++t) acc = fmaf(Rl[t * 16 + i] * scw[t], Rr[t * 16 + j], acc);
+    // core C = R_L diag(w) R_R^T (R column-major here): to Vh column-major (kept: the rotations are
+    // recovered from it below) and, in jacobi16c's layout, over R_L and R_R once every lane has
+    // read them
+    float *Bj = Rl;  // Rl and Rr: 512 floats
+    {
+      float cv[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = lane + 64 * q, i = e & 15, j = e >> 4;
+        float acc = 0.f;
+        if (i < mcol && j < mcol) {
+          for (int t = (i > j ? i : j); t < mcol; ++t) acc = fmaf(Rl[t * 16 + i] * scw[t], Rr[t * 16 + j], acc);
+        }
+        cv[q] = acc;
       }
-      Cm[j * 16 + i] = acc;
-      Vh[j * 16 + i] = (i == j) ? 1.f : 0.f;
+      wave_sync();
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = lane + 64 * q, i = e & 15, j = e >> 4;
+        Vh[j * 16 + i] = cv[q];
+        Bj[j * 32 + 4 * (i >> 1) + (i & 1)] = cv[q];
+      }
     }
     wave_sync();
-    sweeps = jacobi16(Cm, Vh, mcol, lane, &jlimit);
-    if (lane < 16) {
-      float x = 0.f;
+    sweeps = jacobi16c(Bj, mcol, lane, &jlimit);
+    // s_j = |b_j| and u_j = b_j / s_j to Cm column-major, 1 / s_j to sinv (over R_R once every lane
+    // has read B); then V(:, j) = C^T u_j / s_j, as in k_compact_h
+    float *sinv = Rr;
+    {
+      const int col = lane >> 2;
+      const float4 *q = reinterpret_cast<const float4 *>(Bj) + 8 * col + 2 * (lane & 3);
+      const float4 u0 = q[0], u1 = q[1];
+      const float sj = __builtin_amdgcn_sqrtf(
+          group_sum<4>(fmaf(u0.x, u0.x, fmaf(u0.y, u0.y, fmaf(u1.x, u1.x, u1.y * u1.y)))));
+      const float is = sj > 0.f ? __builtin_amdgcn_rcpf(sj) : 0.f;
+      *reinterpret_cast<float4 *>(Cm + 16 * col + 4 * (lane & 3)) =
+          make_float4(u0.x * is, u0.y * is, u1.x * is, u1.y * is);
+      wave_sync();
+      if ((lane & 3) == 0) {
+        sraw[col] = col < mcol ? sj : -1.f;
+        sinv[col] = is;
+      }
+    }
+    wave_sync();
+    {
+      const int row = lane & 15, j0 = lane >> 4;
+      float c0[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) x = fmaf(Cm[lane * 16 + i], Cm[lane * 16 + i], x);
-      sraw[lane] = lane < mcol ? sqrtf(x) : -1.f;
+      for (int q = 0; q < 4; ++q) {
+        const float4 a4 = *reinterpret_cast<const float4 *>(Vh + row * 16 + 4 * q);
+        c0[4 * q] = a4.x;
+        c0[4 * q + 1] = a4.y;
+        c0[4 * q + 2] = a4.z;
+        c0[4 * q + 3] = a4.w;
+      }
+      float vq[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = j0 + 4 * q;
+        float acc = 0.f;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const float4 b4 = *reinterpret_cast<const float4 *>(Cm + j * 16 + 4 * h);
+          acc = fmaf(c0[4 * h], b4.x, acc);
+          acc = fmaf(c0[4 * h + 1], b4.y, acc);
+          acc = fmaf(c0[4 * h + 2], b4.z, acc);
+          acc = fmaf(c0[4 * h + 3], b4.w, acc);
+        }
+        vq[q] = acc * sinv[j];
+      }
+      wave_sync();
+#pragma unroll
+      for (int q = 0; q < 4; ++q) Vh[(j0 + 4 * q) * 16 + row] = vq[q];
     }
     wave_sync();
     if (lane < mcol) {
@@ -400,7 +460,6 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
     const int pos = posL[i];
     if (pos >= total) continue;
     const int j = perm[i];
-    const float inv = 1.0f / sgs[i];
     float ou[NS], ov[NS];
 #pragma unroll
     for (int t = 0; t < NS; ++t) {
@@ -409,8 +468,8 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
     }
 #pragma unroll
     for (int tt = 0; tt < kMaxM; ++tt) {
-      const float cu = Cm[j * 16 + tt] * inv;
-      const float cv = Vh[j * 16 + tt];
+      const float cu = Cm[j * 16 + tt];  // u_j of C
+      const float cv = Vh[j * 16 + tt];  // v_j of C
 #pragma unroll
       for (int t = 0; t < NS; ++t) {
         ou[t] = fmaf(uc[tt][t], cu, ou[t]);
@@ -497,8 +556,8 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
     }
     if (jlimit) __hip_atomic_fetch_add(&a.counters[C_JACOBI_LIMIT], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const unsigned long long D = (unsigned long long)(dk + dv), mm = (unsigned long long)mcol;
-    const unsigned long long flops = 4ull * D * mm * (mm - 1) + 2ull * mm * mm * mm +
-                                     9ull * mm * mm * (mm - 1) * (unsigned long long)sweeps +
+    const unsigned long long flops = 4ull * D * (unsigned long long)proj + 4ull * mm * mm * mm +
+                                     6ull * mm * mm * (mm - 1) * (unsigned long long)sweeps +
                                      2ull * D * mm * (unsigned long long)kl;
     __hip_atomic_fetch_add(&a.acct_flops[s & (kAcctSlots - 1)], flops, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_fetch_add(&a.acct_states[s & (kAcctSlots - 1)], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -510,10 +569,10 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
 // wavefront per state, four per workgroup).  Lanes [0, 32) hold the d_k side of every column
 // ([U_a | K]), lanes [32, 64) the d_v side ([V_a | W]); a lane keeps NB float4 blocks of each
 // column (element 128 b + 4 l + c of its side's vector in lane l of the half, block b, component
-// c).  Both sides' CGS2 then run as one instruction stream, and each pair of dot products (one per
-// side) is one sum over 32 lanes, where k_compact needs two sums over 64 lanes; the columns take
-// the same registers.  The core, the Jacobi SVD (jacobi16), the merge and the writes are those of
-// k_compact, with the same arithmetic and decisions.
+// c).  Both sides' Gram-Schmidt then runs as one instruction stream, and each pair of dot products
+// (one per side) is one sum over 32 lanes, where k_compact needs two sums over 64 lanes; the
+// columns take the same registers.  The second-pass test, the core, the Jacobi SVD (jacobi16c), the
+// merge and the writes are those of k_compact, with the same decisions.
 // ---------------------------------------------------------------------------------------------
 template <int NB>
 __device__ __forceinline__ float dotb(const float4 (&x)[NB], const float4 (&y)[NB]) {
