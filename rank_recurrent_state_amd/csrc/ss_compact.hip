@@ -108,13 +108,15 @@ __device__ __forceinline__ void copy_comps(const Arena &src, int64_t c0, int cnt
     const bool on = c < tot4;
     const bool isu = c < dk4;
     const int off = !on ? 0 : (isu ? 4 * c : 4 * (c - dk4));  // element offset inside u or v (0 when off)
+    const F *sbase = (isu ? src.U<F>() : src.V<F>()) + off;     // this lane's side, taken once
+    const uint32_t sd = isu ? (uint32_t)dk : (uint32_t)dv;
     for (int f0 = 0; f0 < cnt; f0 += UNC) {
       float4 x[UNC];
 #pragma unroll
       for (int q = 0; q < UNC; ++q) {
         const int f = f0 + q < cnt ? f0 + q : cnt - 1;  // clamped (cnt >= 1 inside the loop)
         const int64_t cs = wrap(c0 + f, src.cap);
-        x[q] = ldf4nt(isu ? src.U<F>() + cs * dk + off : src.V<F>() + cs * dv + off);
+        x[q] = ldf4nt(sbase + cs * (int64_t)sd);
       }
 #pragma unroll
       for (int q = 0; q < UNC; ++q) {
@@ -457,9 +459,9 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
   };
   // kept local components: U' = Q_L U_hat, V' = Q_R V_hat
   for (int i = 0; i < kl; ++i) {
-    const int pos = posL[i];
+    const int pos = uniform(posL[i]);  // i is wave-uniform
     if (pos >= total) continue;
-    const int j = perm[i];
+    const int j = uniform(perm[i]);
     float ou[NS], ov[NS];
 #pragma unroll
     for (int t = 0; t < NS; ++t) {
@@ -925,9 +927,9 @@ __global__ __launch_bounds__(256) void k_compact_h(CompactArgs a) {
   };
   // kept local components: U' = Q_L U_hat (d_k lanes), V' = Q_R V_hat (d_v lanes)
   for (int i = 0; i < kl; ++i) {
-    const int pos = posL[i];
+    const int pos = uniform(posL[i]);  // i is wave-uniform
     if (pos >= total) continue;
-    const int j = perm[i];
+    const int j = uniform(perm[i]);
     const float *cf = (side ? Vh : Cm) + j * 16;  // u_j or v_j of C
     float4 o[NB];
 #pragma unroll
