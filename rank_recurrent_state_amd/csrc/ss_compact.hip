@@ -498,7 +498,7 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
 #pragma unroll
       for (int c = 0; c < FC; ++c) {
         const int f = f0 + c < kf ? f0 + c : kf - 1;  // clamped (kf >= 1 inside the loop)
-        const int64_t cs = wrap(off_f + forig[f], capF);
+        const int64_t cs = wrap(off_f + uniform(forig[f]), capF);  // f is wave-uniform
         const F *su = a.frz.U<F>() + cs * dk;
         const F *sv = a.frz.V<F>() + cs * dv;
 #pragma unroll
@@ -512,9 +512,9 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
       for (int c = 0; c < FC; ++c) {
         const int f = f0 + c;
         if (f >= kf) break;
-        const int pos = posF[f];
+        const int pos = uniform(posF[f]);  // f is wave-uniform
         if (pos >= total) continue;
-        const float inv = 1.0f / fnrm[forig[f]];
+        const float inv = __builtin_amdgcn_rcpf(uniformf(fnrm[uniform(forig[f])]));
         F *du = slot_u(pos);
         F *dvv = slot_v(pos);
 #pragma unroll
