@@ -4,7 +4,8 @@
 // 64-lane wavefront per state of the group, four states per workgroup.
 //   1. U_C = [U_active | pad keys] (d_k x m), V_C = [V_active | pad w]
 //      (d_v x m), weights Gamma * (sigma_active, c); m = r_a + n <= 16.
-//      Element e of a column lives in lane e % 64, register e / 64.
+//      The d_k side of every column lives on lanes 0-31, the d_v side on
+//      lanes 32-63, four consecutive elements per lane and float4 block.
 //   2. Thin QR of both sides by classical Gram-Schmidt, a second projection
 //      pass only for a column whose first pass kept less than a tenth of its
 //      squared norm; a column whose residual is at most 1e-5 of its own norm
@@ -16,7 +17,8 @@
 //      pairs rotate at once; sweeps until no pair is off-orthogonal by more
 //      than 1e-6.  The right singular vectors follow from C afterwards.
 //   5. Sort the local singular values; merge them with the frozen ones
-//      (scaled by Gamma) in descending order, local first on ties; drop
+//      (scaled by Gamma; with per-channel decay by |gamma u_f|, and sorted
+//      again) in descending order, local first on ties; drop
 //      sigma < eps * sigma_max and sigma = 0 (SinkState 4.1, 4.2 example).
 //   6. U' = Q_L U_hat, V' = Q_R V_hat for the kept local components; kept
 //      frozen components are copied.  The first r of the merged list go to
@@ -129,452 +131,19 @@ __device__ __forceinline__ void copy_comps(const Arena &src, int64_t c0, int cnt
   }
 }
 
-// DIAG (per-channel decay): the state is diag(gamma) times its stored parts, gamma holding the
-// decays accumulated per key channel since the last compaction.  The active columns and the pad
-// keys enter the QR scaled by gamma; each frozen u_f is scaled by gamma and given unit norm again
-// (sigma_f takes the norm), and the frozen list is re-sorted by the new sigma (stored order on
-// ties) before the merge; gamma is reset to 1.
-template <int NS, typename F, bool DIAG>
-__global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
-  __shared__ float lds[4][DIAG ? kLdsPerWaveDiag : kLdsPerWave];
-  const int w = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int mi = blockIdx.x * 4 + w;
-  float *Rl = lds[w] + kOffRl;
-  float *Rr = lds[w] + kOffRr;
-  float *Cm = lds[w] + kOffCm;
-  float *Vh = lds[w] + kOffVh;
-  float *scw = lds[w] + kOffScw;
-  float *sgs = lds[w] + kOffSgs;
-  float *sraw = lds[w] + kOffSraw;
-  int *perm = reinterpret_cast<int *>(lds[w] + kOffPerm);
-  int *posL = reinterpret_cast<int *>(lds[w] + kOffPosL);
-  float *fsl = lds[w] + kOffFs;
-  int *posF = reinterpret_cast<int *>(lds[w] + kOffPosF);
-  const int dk = a.dk, dv = a.dv, K = a.K, r = a.r;
-  const int64_t capA = a.act.cap, capF = a.frz.cap;
-
-  // ---- phase A: what this wave's state becomes -------------------------------------------
-  bool live = mi < a.n_members;  // a member of the group held in factored form
-  int s = 0, ra = 0, rf = 0, n = 0, off_a = 0, off_f = 0;
-  uint32_t flags = 0;
-  float gamma = 1.0f;
-  if (live) {
-    s = uniform(a.members[mi]);
-    const Meta m = a.meta[s];
-    const uint32_t packed = (uint32_t)uniform((int)m.packed);
-    flags = meta_flags(packed);
-    if (flags & FLAG_DENSE) {
-      live = false;
-    } else {
-      ra = meta_ra(packed);
-      rf = meta_rf(packed);
-      n = meta_n(packed);
-      off_a = uniform(m.off_a);
-      off_f = uniform(m.off_f);
-      gamma = uniformf(m.gamma);
-    }
-  }
-  // an unselected member (compaction of listed states) keeps its pad and Gamma and only moves
-  const bool keep = live && a.sel != nullptr && a.sel[s] == 0;
-  const bool work = live && n > 0 && !keep;  // a Brand update; otherwise the components move unchanged
-  const int mcol = ra + n;
-  int kl = 0, kf = 0, total = 0, ra2 = ra, rf2 = rf, sweeps = 0;
-  int proj = 0;  // column projections made by the Gram-Schmidt passes
-  bool jlimit = false;
-  float uc[kMaxM][NS], vc[kMaxM][NS];
-  float gr[NS];  // DIAG: the state's decays, row lane + 64 t (0 past d_k)
-#pragma unroll
-  for (int t = 0; t < NS; ++t) gr[t] = 1.f;
-  if (DIAG && work) {
-#pragma unroll
-    for (int t = 0; t < NS; ++t) {
-      const int row = lane + 64 * t;
-      gr[t] = self(row < dk, a.gam[(int64_t)s * dk + (row < dk ? row : dk - 1)]);
-    }
-  }
-  if (work) {
-    if constexpr (DIAG) {
-      float *fraw = lds[w] + kOffFraw, *fnrm = lds[w] + kOffFnorm;
-      int *forig = reinterpret_cast<int *>(lds[w] + kOffForig);
-      // norms |gamma u_f|, four components in flight
-      for (int f0 = 0; f0 < rf; f0 += 4) {
-        float x[4][NS];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int f = f0 + c < rf ? f0 + c : rf - 1;  // clamped (rf >= 1 inside the loop)
-          const F *fu = a.frz.U<F>() + wrap(off_f + f, capF) * dk;
-#pragma unroll
-          for (int t = 0; t < NS; ++t) {
-            const int row = lane + 64 * t;
-            x[c][t] = ldf(fu + (row < dk ? row : dk - 1));
-          }
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          float acc = 0.f;
-#pragma unroll
-          for (int t = 0; t < NS; ++t) {
-            const float y = x[c][t] * gr[t];
-            acc = fmaf(y, y, acc);
-          }
-          acc = wave_sum(acc);
-          if (lane == 0 && f0 + c < rf) fnrm[f0 + c] = sqrtf(acc);
-        }
-      }
-      wave_sync();
-      for (int f = lane; f < rf; f += 64) fraw[f] = a.frz.s[wrap(off_f + f, capF)] * fnrm[f];
-      wave_sync();
-      for (int f = lane; f < rf; f += 64) {  // descending, stored order on ties
-        const float x = fraw[f];
-        int rk = 0;
-        for (int g = 0; g < rf; ++g) {
-          const float y = fraw[g];
-          rk += (y > x) || (y == x && g < f);
-        }
-        fsl[rk] = x;
-        forig[rk] = f;
-      }
-      wave_sync();
-    } else {
-      // frozen singular values (scaled by Gamma) to LDS: the merge searches them there
-      for (int f = lane; f < rf; f += 64) fsl[f] = a.frz.s[wrap(off_f + f, capF)] * gamma;
-    }
-#pragma unroll
-    for (int jj = 0; jj < kMaxM; ++jj) {
-      const bool valid = jj < mcol;
-      const int j = valid ? jj : mcol - 1;  // clamped: the loads stay in bounds (mcol >= 1 here)
-      const bool isact = j < ra;
-      const int64_t ca = wrap(off_a + j, capA);
-      if (std::is_same<F, float>::value || !isact) {
-        const float *su = isact ? a.act.U<float>() + ca * dk : a.pk + ((int64_t)s * K + (j - ra)) * dk;
-        const float *sv = isact ? a.act.V<float>() + ca * dv : a.pw + ((int64_t)s * K + (j - ra)) * dv;
-#pragma unroll
-        for (int t = 0; t < NS; ++t) {
-          const int row = lane + 64 * t;
-          uc[jj][t] = self(valid && row < dk, ldfnt(su + (row < dk ? row : dk - 1)));
-          vc[jj][t] = self(valid && row < dv, ldfnt(sv + (row < dv ? row : dv - 1)));
-        }
-      } else {  // fp16 factors (wave-uniform branch)
-        const F *su = a.act.U<F>() + ca * dk;
-        const F *sv = a.act.V<F>() + ca * dv;
-#pragma unroll
-        for (int t = 0; t < NS; ++t) {
-          const int row = lane + 64 * t;
-          uc[jj][t] = self(valid && row < dk, ldfnt(su + (row < dk ? row : dk - 1)));
-          vc[jj][t] = self(valid && row < dv, ldfnt(sv + (row < dv ? row : dv - 1)));
-        }
-      }
-      if constexpr (DIAG) {  // active columns and pad keys carry the decays
-#pragma unroll
-        for (int t = 0; t < NS; ++t) uc[jj][t] *= gr[t];
-      }
-    }
-    if (lane < kMaxM) {
-      float wgt = 0.f;
-      if (lane < ra) wgt = a.act.s[wrap(off_a + lane, capA)] * gamma;
-      else if (lane < mcol) wgt = a.pc[(int64_t)s * K + (lane - ra)] * gamma;
-      scw[lane] = wgt;
-    }
-    cgs_pair<NS>(uc, vc, mcol, lane, Rl, Rr, proj);
-    wave_sync();
-    // core C = R_L diag(w) R_R^T (R column-major here): to Vh column-major (kept: the rotations are
-    // recovered from it below) and, in jacobi16c's layout, over R_L and R_R once every lane has
-    // read them
-    float *Bj = Rl;  // Rl and Rr: 512 floats
-    {
-      float cv[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = lane + 64 * q, i = e & 15, j = e >> 4;
-        float acc = 0.f;
-        if (i < mcol && j < mcol) {
-          for (int t = (i > j ? i : j); t < mcol; ++t) acc = fmaf(Rl[t * 16 + i] * scw[t], Rr[t * 16 + j], acc);
-        }
-        cv[q] = acc;
-      }
-      wave_sync();
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = lane + 64 * q, i = e & 15, j = e >> 4;
-        Vh[j * 16 + i] = cv[q];
-        Bj[j * 32 + 4 * (i >> 1) + (i & 1)] = cv[q];
-      }
-    }
-    wave_sync();
-    sweeps = jacobi16c(Bj, mcol, lane, &jlimit);
-    // s_j = |b_j| and u_j = b_j / s_j to Cm column-major, 1 / s_j to sinv (over R_R once every lane
-    // has read B); then V(:, j) = C^T u_j / s_j, as in k_compact_h
-    float *sinv = Rr;
-    {
-      const int col = lane >> 2;
-      const float4 *q = reinterpret_cast<const float4 *>(Bj) + 8 * col + 2 * (lane & 3);
-      const float4 u0 = q[0], u1 = q[1];
-      const float sj = __builtin_amdgcn_sqrtf(
-          group_sum<4>(fmaf(u0.x, u0.x, fmaf(u0.y, u0.y, fmaf(u1.x, u1.x, u1.y * u1.y)))));
-      const float is = sj > 0.f ? __builtin_amdgcn_rcpf(sj) : 0.f;
-      *reinterpret_cast<float4 *>(Cm + 16 * col + 4 * (lane & 3)) =
-          make_float4(u0.x * is, u0.y * is, u1.x * is, u1.y * is);
-      wave_sync();
-      if ((lane & 3) == 0) {
-        sraw[col] = col < mcol ? sj : -1.f;
-        sinv[col] = is;
-      }
-    }
-    wave_sync();
-    {
-      const int row = lane & 15, j0 = lane >> 4;
-      float c0[16];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 a4 = *reinterpret_cast<const float4 *>(Vh + row * 16 + 4 * q);
-        c0[4 * q] = a4.x;
-        c0[4 * q + 1] = a4.y;
-        c0[4 * q + 2] = a4.z;
-        c0[4 * q + 3] = a4.w;
-      }
-      float vq[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int j = j0 + 4 * q;
-        float acc = 0.f;
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const float4 b4 = *reinterpret_cast<const float4 *>(Cm + j * 16 + 4 * h);
-          acc = fmaf(c0[4 * h], b4.x, acc);
-          acc = fmaf(c0[4 * h + 1], b4.y, acc);
-          acc = fmaf(c0[4 * h + 2], b4.z, acc);
-          acc = fmaf(c0[4 * h + 3], b4.w, acc);
-        }
-        vq[q] = acc * sinv[j];
-      }
-      wave_sync();
-#pragma unroll
-      for (int q = 0; q < 4; ++q) Vh[(j0 + 4 * q) * 16 + row] = vq[q];
-    }
-    wave_sync();
-    if (lane < mcol) {
-      const float my = sraw[lane];
-      int rank = 0;
-      for (int i = 0; i < mcol; ++i) {
-        const float o = sraw[i];
-        rank += (o > my) || (o == my && i < lane);
-      }
-      perm[rank] = lane;
-      sgs[rank] = my;
-    }
-    wave_sync();
-
-    // merge with the frozen part and truncate: both lists are descending; on ties the local
-    // component comes first; drop sigma < eps * sigma_max and sigma = 0
-    const float smax = fmaxf(sgs[0], rf > 0 ? fsl[0] : 0.f);
-    const float thr = a.eps[s] * smax;
-    kl = __builtin_popcountll(__builtin_amdgcn_ballot_w64(lane < mcol && sgs[lane] >= thr && sgs[lane] > 0.f));
-    for (int f0 = 0; f0 < rf; f0 += 64) {
-      const int f = f0 + lane;
-      kf += __builtin_popcountll(__builtin_amdgcn_ballot_w64(f < rf && fsl[f] >= thr && fsl[f] > 0.f));
-    }
-    total = kl + kf;
-    const int cap_total = r + a.fcap;
-    if (total > cap_total) {
-      if (lane == 0)
-        __hip_atomic_fetch_add(&a.counters[C_CAP_TRUNC], (uint32_t)(total - cap_total), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-      total = cap_total;
-    }
-    ra2 = total < r ? total : r;
-    rf2 = total - ra2;
-    if (lane < kl) {  // local i goes after the frozen ones strictly greater than it
-      const float x = sgs[lane];
-      int lo = 0, hi = kf;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (fsl[mid] > x) lo = mid + 1;
-        else hi = mid;
-      }
-      posL[lane] = lane + lo;
-    }
-    for (int f = lane; f < kf; f += 64) {  // frozen f goes after the local ones >= it
-      const float x = fsl[f];
-      int c = 0;
-      for (int i = 0; i < kl; ++i) c += sgs[i] >= x ? 1 : 0;
-      posF[f] = f + c;
-    }
-    wave_sync();
-  }
-
-  // ---- placement: the member's slots in the group's new segments ---------------------------
-  if (!live) return;
-  {
-    int sa, sf;
-    slot_sizes(ra, rf, n, r, a.fcap, sa, sf);
-    if (ra2 > sa || rf2 > sf) {  // cannot happen (the slots bound the counts); never overwrite a neighbour
-      if (lane == 0) *a.hflag = 1u;
-      return;
-    }
-  }
-  const unsigned long long rel = a.slot_in[mi] + a.slot_blk[mi / kSlotBlock];
-  const unsigned long long va = a.ring_a->begin + (rel & 0xffffffffull), vf = a.ring_f->begin + (rel >> 32);
-  // the ring is full (the ring set-up has raised the pool's flag): the state keeps its old form
-  if (va + ra2 > a.ring_a->limit || vf + rf2 > a.ring_f->limit) return;
-  const int64_t dst_a = (int64_t)(va % (unsigned long long)capA), dst_f = (int64_t)(vf % (unsigned long long)capF);
-
-  // ---- phase B: write the new components and the record ------------------------------------
-  if (!work) {  // nothing buffered (or not selected): the components move unchanged
-    copy_comps<F>(a.act, off_a, ra, dk, dv, lane, [&](int f, F *&du, F *&dvp) {
-      const int64_t c = wrap(dst_a + f, capA);
-      du = a.act.U<F>() + c * dk;
-      dvp = a.act.V<F>() + c * dv;
-      return true;
-    });
-    copy_comps<F>(a.frz, off_f, rf, dk, dv, lane, [&](int f, F *&du, F *&dvp) {
-      const int64_t c = wrap(dst_f + f, capF);
-      du = a.frz.U<F>() + c * dk;
-      dvp = a.frz.V<F>() + c * dv;
-      return true;
-    });
-    // an empty pad means Gamma = 1 (no step since the last compaction) and sigma takes it in;
-    // an unselected member keeps Gamma with its pad
-    const float gs = keep ? 1.0f : gamma;
-    for (int f = lane; f < ra; f += 64) a.act.s[wrap(dst_a + f, capA)] = a.act.s[wrap(off_a + f, capA)] * gs;
-    for (int f = lane; f < rf; f += 64) a.frz.s[wrap(dst_f + f, capF)] = a.frz.s[wrap(off_f + f, capF)] * gs;
-    if (lane == 0) {
-      Meta nm;
-      nm.off_a = (int32_t)dst_a;
-      nm.off_f = (int32_t)dst_f;
-      nm.gamma = keep ? gamma : 1.0f;
-      nm.packed = meta_pack(ra, rf, keep ? n : 0, flags);
-      a.meta[s] = nm;
-    }
-    return;
-  }
-  // merged position pos -> slot of the new active (pos < r) or frozen component
-  auto slot_u = [&](int pos) -> F * {
-    return pos < r ? a.act.U<F>() + wrap(dst_a + pos, capA) * dk : a.frz.U<F>() + wrap(dst_f + pos - r, capF) * dk;
-  };
-  auto slot_v = [&](int pos) -> F * {
-    return pos < r ? a.act.V<F>() + wrap(dst_a + pos, capA) * dv : a.frz.V<F>() + wrap(dst_f + pos - r, capF) * dv;
-  };
-  auto slot_s = [&](int pos) -> float * {
-    return pos < r ? a.act.s + wrap(dst_a + pos, capA) : a.frz.s + wrap(dst_f + pos - r, capF);
-  };
-  // kept local components: U' = Q_L U_hat, V' = Q_R V_hat
-  for (int i = 0; i < kl; ++i) {
-    const int pos = uniform(posL[i]);  // i is wave-uniform
-    if (pos >= total) continue;
-    const int j = uniform(perm[i]);
-    float ou[NS], ov[NS];
-#pragma unroll
-    for (int t = 0; t < NS; ++t) {
-      ou[t] = 0.f;
-      ov[t] = 0.f;
-    }
-#pragma unroll
-    for (int tt = 0; tt < kMaxM; ++tt) {
-      const float cu = Cm[j * 16 + tt];  // u_j of C
-      const float cv = Vh[j * 16 + tt];  // v_j of C
-#pragma unroll
-      for (int t = 0; t < NS; ++t) {
-        ou[t] = fmaf(uc[tt][t], cu, ou[t]);
-        ov[t] = fmaf(vc[tt][t], cv, ov[t]);
-      }
-    }
-    F *du = slot_u(pos);
-    F *dvv = slot_v(pos);
-#pragma unroll
-    for (int t = 0; t < NS; ++t) {  // rounded to the storage type here (fp16 factors: at every compaction)
-      const int row = lane + 64 * t;
-      if (row < dk) stfnt(du + row, ou[t]);
-      if (row < dv) stfnt(dvv + row, ov[t]);
-    }
-  }
-  if (lane < kl && posL[lane] < total) *slot_s(posL[lane]) = sgs[lane];
-  if constexpr (DIAG) {
-    // kept frozen components in sorted order: u <- gamma u / |gamma u|, v copied; gamma <- 1
-    const float *fnrm = lds[w] + kOffFnorm;
-    const int *forig = reinterpret_cast<const int *>(lds[w] + kOffForig);
-    constexpr int FC = 4;  // components in flight: all loads of a batch are issued before its stores
-    for (int f0 = 0; f0 < kf; f0 += FC) {
-      float xu[FC][NS], xv[FC][NS];
-#pragma unroll
-      for (int c = 0; c < FC; ++c) {
-        const int f = f0 + c < kf ? f0 + c : kf - 1;  // clamped (kf >= 1 inside the loop)
-        const int64_t cs = wrap(off_f + uniform(forig[f]), capF);  // f is wave-uniform
-        const F *su = a.frz.U<F>() + cs * dk;
-        const F *sv = a.frz.V<F>() + cs * dv;
-#pragma unroll
-        for (int t = 0; t < NS; ++t) {
-          const int row = lane + 64 * t;
-          xu[c][t] = ldfnt(su + (row < dk ? row : dk - 1));
-          xv[c][t] = ldfnt(sv + (row < dv ? row : dv - 1));
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < FC; ++c) {
-        const int f = f0 + c;
-        if (f >= kf) break;
-        const int pos = uniform(posF[f]);  // f is wave-uniform
-        if (pos >= total) continue;
-        const float inv = __builtin_amdgcn_rcpf(uniformf(fnrm[uniform(forig[f])]));
-        F *du = slot_u(pos);
-        F *dvv = slot_v(pos);
-#pragma unroll
-        for (int t = 0; t < NS; ++t) {
-          const int row = lane + 64 * t;
-          if (row < dk) stfnt(du + row, xu[c][t] * gr[t] * inv);
-          if (row < dv) stfnt(dvv + row, xv[c][t]);
-        }
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < NS; ++t) {
-      const int row = lane + 64 * t;
-      if (row < dk) a.gam[(int64_t)s * dk + row] = 1.f;
-    }
-  } else {
-    // kept frozen components: copied, sigma scaled by Gamma
-    copy_comps<F>(a.frz, off_f, kf, dk, dv, lane, [&](int f, F *&du, F *&dvp) {
-      const int pos = uniform(posF[f]);  // f is wave-uniform
-      if (pos >= total) return false;
-      du = slot_u(pos);
-      dvp = slot_v(pos);
-      return true;
-    });
-  }
-  for (int f = lane; f < kf; f += 64) {
-    const int pos = posF[f];
-    if (pos < total) *slot_s(pos) = fsl[f];
-  }
-  if (lane == 0) {
-    Meta nm;
-    nm.off_a = (int32_t)dst_a;
-    nm.off_f = (int32_t)dst_f;
-    nm.gamma = 1.0f;
-    nm.packed = meta_pack(ra2, rf2, 0, flags);
-    a.meta[s] = nm;
-    if (a.promote && total > a.L) {
-      const uint32_t idx =
-          __hip_atomic_fetch_add(&a.counters[C_PROMOTE_COUNT], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      a.promote_list[idx] = s;
-    }
-    if (jlimit) __hip_atomic_fetch_add(&a.counters[C_JACOBI_LIMIT], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned long long D = (unsigned long long)(dk + dv), mm = (unsigned long long)mcol;
-    const unsigned long long flops = 4ull * D * (unsigned long long)proj + 4ull * mm * mm * mm +
-                                     6ull * mm * mm * (mm - 1) * (unsigned long long)sweeps +
-                                     2ull * D * mm * (unsigned long long)kl;
-    __hip_atomic_fetch_add(&a.acct_flops[s & (kAcctSlots - 1)], flops, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_fetch_add(&a.acct_states[s & (kAcctSlots - 1)], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
-
 // ---------------------------------------------------------------------------------------------
 // Brand compaction with the two sides of a state split across the halves of its wavefront (one
 // wavefront per state, four per workgroup).  Lanes [0, 32) hold the d_k side of every column
 // ([U_a | K]), lanes [32, 64) the d_v side ([V_a | W]); a lane keeps NB float4 blocks of each
 // column (element 128 b + 4 l + c of its side's vector in lane l of the half, block b, component
 // c).  Both sides' Gram-Schmidt then runs as one instruction stream, and each pair of dot products
-// (one per side) is one sum over 32 lanes, where k_compact needs two sums over 64 lanes; the
-// columns take the same registers.  The second-pass test, the core, the Jacobi SVD (jacobi16c), the
-// merge and the writes are those of k_compact, with the same decisions.
+// (one per side) is one sum over 32 lanes.
+//
+// DIAG (per-channel decay): the state is diag(gamma) times its stored parts, gamma holding the
+// decays accumulated per key channel since the last compaction.  The active columns and the pad
+// keys enter the QR scaled by gamma; each frozen u_f is scaled by gamma and given unit norm again
+// (sigma_f takes the norm), and the frozen list is sorted again by the new sigma (stored order on
+// ties) before the merge; gamma is reset to 1.
 // ---------------------------------------------------------------------------------------------
 template <int NB>
 __device__ __forceinline__ float dotb(const float4 (&x)[NB], const float4 (&y)[NB]) {
@@ -584,9 +153,9 @@ __device__ __forceinline__ float dotb(const float4 (&x)[NB], const float4 (&y)[N
   return acc;
 }
 
-template <int NB, typename F>
+template <int NB, typename F, bool DIAG>
 __global__ __launch_bounds__(256) void k_compact_h(CompactArgs a) {
-  __shared__ __align__(16) float lds[4][kLdsPerWave];
+  __shared__ __align__(16) float lds[4][DIAG ? kLdsPerWaveDiag : kLdsPerWave];
   const int w = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int side = lane >> 5, r = lane & 31;
   const int mi = blockIdx.x * 4 + w;
@@ -634,9 +203,63 @@ __global__ __launch_bounds__(256) void k_compact_h(CompactArgs a) {
   int proj = 0;  // column projections made by the Gram-Schmidt passes
   bool jlimit = false;
   float4 x[kMaxM][NB];
+  // DIAG: the state's decays on this lane's rows of the d_k side, 1 on the d_v side and past d_k
+  float4 g4[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) g4[b] = make_float4(1.f, 1.f, 1.f, 1.f);
+  if (DIAG && work && side == 0) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int e = 128 * b + 4 * r;
+      if (e < dk) g4[b] = ld4(a.gam + (int64_t)s * dk + e);
+    }
+  }
   if (work) {
-    // frozen singular values (scaled by Gamma) to LDS: the merge searches them there
-    for (int f = lane; f < rf; f += 64) fsl[f] = a.frz.s[wrap(off_f + f, capF)] * gamma;
+    if constexpr (DIAG) {
+      // the frozen singular values become sigma_f |gamma u_f| and their order is taken again
+      // (descending, stored order on ties); the norms on the d_k half, four components in flight
+      float *fraw = lds[w] + kOffFraw, *fnrm = lds[w] + kOffFnorm;
+      int *forig = reinterpret_cast<int *>(lds[w] + kOffForig);
+      for (int f0 = 0; f0 < rf; f0 += 4) {
+        float4 y[4][NB];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int f = f0 + c < rf ? f0 + c : rf - 1;  // clamped (rf >= 1 inside the loop)
+          const F *fu = a.frz.U<F>() + wrap(off_f + f, capF) * dk;
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            const int e = 128 * b + 4 * r;
+            y[c][b] = zero4();
+            if (side == 0 && e < dk) {
+              const float4 t = ldf4nt(fu + e);
+              y[c][b] = make_float4(t.x * g4[b].x, t.y * g4[b].y, t.z * g4[b].z, t.w * g4[b].w);
+            }
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float nn = group_sum<32>(dotb<NB>(y[c], y[c]));  // lanes of the d_k half
+          if (lane == 0 && f0 + c < rf) fnrm[f0 + c] = sqrtf(nn);
+        }
+      }
+      wave_sync();
+      for (int f = lane; f < rf; f += 64) fraw[f] = a.frz.s[wrap(off_f + f, capF)] * fnrm[f];
+      wave_sync();
+      for (int f = lane; f < rf; f += 64) {
+        const float xv = fraw[f];
+        int rk = 0;
+        for (int g = 0; g < rf; ++g) {
+          const float yv = fraw[g];
+          rk += (yv > xv) || (yv == xv && g < f);
+        }
+        fsl[rk] = xv;
+        forig[rk] = f;
+      }
+      wave_sync();
+    } else {
+      // frozen singular values (scaled by Gamma) to LDS: the merge searches them there
+      for (int f = lane; f < rf; f += 64) fsl[f] = a.frz.s[wrap(off_f + f, capF)] * gamma;
+    }
     // columns: [U_a | K] on the d_k lanes, [V_a | W] on the d_v lanes; this lane's side's arena and
     // pad bases and row length are taken once, so a column costs one multiply-add per address
     {
@@ -659,7 +282,8 @@ __global__ __launch_bounds__(256) void k_compact_h(CompactArgs a) {
           } else {
             v = ld4nt(pad_b + (j - ra) * dme + eo);
           }
-          x[jj][b] = sel4(ok, v);
+          if constexpr (DIAG) v = make_float4(v.x * g4[b].x, v.y * g4[b].y, v.z * g4[b].z, v.w * g4[b].w);
+          x[jj][b] = sel4(ok, v);  // DIAG: active columns and pad keys carry the decays
         }
       }
     }
@@ -948,14 +572,59 @@ __global__ __launch_bounds__(256) void k_compact_h(CompactArgs a) {
     }
   }
   if (lane < kl && posL[lane] < total) *slot_s(posL[lane]) = sgs[lane];
-  // kept frozen components: copied, sigma scaled by Gamma
-  copy_comps<F>(a.frz, off_f, kf, dk, dv, lane, [&](int f, F *&du, F *&dvp) {
-    const int pos = uniform(posF[f]);  // f is wave-uniform
-    if (pos >= total) return false;
-    du = slot_u(pos);
-    dvp = slot_v(pos);
-    return true;
-  });
+  if constexpr (DIAG) {
+    // kept frozen components in sorted order: u <- gamma u / |gamma u|, v copied; gamma <- 1
+    const float *fnrm = lds[w] + kOffFnorm;
+    const int *forig = reinterpret_cast<const int *>(lds[w] + kOffForig);
+    constexpr int FC = 4;  // components in flight: all loads of a batch are issued before its stores
+    for (int f0 = 0; f0 < kf; f0 += FC) {
+      float4 y[FC][NB];
+#pragma unroll
+      for (int c = 0; c < FC; ++c) {
+        const int f = f0 + c < kf ? f0 + c : kf - 1;  // clamped (kf >= 1 inside the loop)
+        const int64_t cs = wrap(off_f + uniform(forig[f]), capF);  // f is wave-uniform
+        const F *src = side ? a.frz.V<F>() + cs * dv : a.frz.U<F>() + cs * dk;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const int e = 128 * b + 4 * r;
+          y[c][b] = ldf4nt(src + (e < dme ? e : 0));
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < FC; ++c) {
+        const int f = f0 + c;
+        if (f >= kf) break;
+        const int pos = uniform(posF[f]);  // f is wave-uniform
+        if (pos >= total) continue;
+        const float inv = side ? 1.f : __builtin_amdgcn_rcpf(uniformf(fnrm[uniform(forig[f])]));
+        F *dst = side ? slot_v(pos) : slot_u(pos);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const int e = 128 * b + 4 * r;
+          const float4 t = y[c][b];
+          if (e < dme)
+            stf4nt(dst + e, make_float4(t.x * g4[b].x * inv, t.y * g4[b].y * inv, t.z * g4[b].z * inv,
+                                        t.w * g4[b].w * inv));
+        }
+      }
+    }
+    if (side == 0) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int e = 128 * b + 4 * r;
+        if (e < dk) st4(a.gam + (int64_t)s * dk + e, make_float4(1.f, 1.f, 1.f, 1.f));
+      }
+    }
+  } else {
+    // kept frozen components: copied, sigma scaled by Gamma
+    copy_comps<F>(a.frz, off_f, kf, dk, dv, lane, [&](int f, F *&du, F *&dvp) {
+      const int pos = uniform(posF[f]);  // f is wave-uniform
+      if (pos >= total) return false;
+      du = slot_u(pos);
+      dvp = slot_v(pos);
+      return true;
+    });
+  }
   for (int f = lane; f < kf; f += 64) {
     const int pos = posF[f];
     if (pos < total) *slot_s(pos) = fsl[f];
@@ -1403,33 +1072,27 @@ __global__ void k_fill_f32(float *p, int64_t n, float x) {
   if (i < n) p[i] = x;
 }
 
-template <int NB, typename F>
+template <int NB, typename F, bool DG>
 hipError_t compact_h(const CompactArgs &a, hipStream_t st) {
   const dim3 grid((unsigned)((a.n_members + 3) / 4)), block(256);
-  hipLaunchKernelGGL((k_compact_h<NB, F>), grid, block, 0, st, a);
+  hipLaunchKernelGGL((k_compact_h<NB, F, DG>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
-template <typename F, bool DG>
-hipError_t compact_ns(const CompactArgs &a, int ns, hipStream_t st) {
-  const dim3 grid((unsigned)((a.n_members + 3) / 4)), block(256);
-  if (ns == 1) hipLaunchKernelGGL((k_compact<1, F, DG>), grid, block, 0, st, a);
-  else if (ns == 2) hipLaunchKernelGGL((k_compact<2, F, DG>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((k_compact<4, F, DG>), grid, block, 0, st, a);
-  return hipGetLastError();
-}
 
 }  // namespace
 
 hipError_t launch_compact(const CompactArgs &a, hipStream_t st) {
   if (a.n_members <= 0) return hipSuccess;
   const int d = a.dk > a.dv ? a.dk : a.dv;
-  const int ns = d <= 64 ? 1 : d <= 128 ? 2 : d <= 256 ? 4 : 0;
-  if (ns == 0) return hipErrorInvalidValue;
-  if (a.gam) return a.act.half ? compact_ns<_Float16, true>(a, ns, st) : compact_ns<float, true>(a, ns, st);
-  // the two sides of a state on the two halves of its wavefront
-  if (d <= 128) return a.act.half ? compact_h<1, _Float16>(a, st) : compact_h<1, float>(a, st);
-  return a.act.half ? compact_h<2, _Float16>(a, st) : compact_h<2, float>(a, st);
+  if (d > 256) return hipErrorInvalidValue;
+  // the two sides of a state on the two halves of its wavefront; a.gam: per-channel decay
+  if (a.gam) {
+    if (d <= 128) return a.act.half ? compact_h<1, _Float16, true>(a, st) : compact_h<1, float, true>(a, st);
+    return a.act.half ? compact_h<2, _Float16, true>(a, st) : compact_h<2, float, true>(a, st);
+  }
+  if (d <= 128) return a.act.half ? compact_h<1, _Float16, false>(a, st) : compact_h<1, float, false>(a, st);
+  return a.act.half ? compact_h<2, _Float16, false>(a, st) : compact_h<2, float, false>(a, st);
 }
 
 hipError_t launch_materialize(const MaterializeArgs &a, int64_t grid_upper, hipStream_t st) {

@@ -71,99 +71,6 @@ __device__ __forceinline__ void cgs2_one(float (&u)[kMaxM][NS], int m, int lane,
   }
 }
 
-// In-place classical Gram-Schmidt thin QR of the register-resident columns u[0..m) and v[0..m),
-// both sides interleaved (they are independent, so their reductions overlap), with selective
-// reorthogonalization: a column gets a second projection pass only when the first one kept less
-// than kReorth2 of its squared norm on either side (one pass leaves along the earlier columns a
-// rounding residue of a few unit roundoffs times the input norm, that is at most sqrt(1 / kReorth2)
-// times as much relative to what remains).  R goes to LDS column-major 16 x 16:
-// R[j * 16 + i] = R(i, j).  A column whose residual is at most 1e-5 of its input norm is dependent:
-// it and its R row are zeroed.  proj counts the column projections made.
-template <int NS>
-__device__ __forceinline__ void cgs_pair(float (&u)[kMaxM][NS], float (&v)[kMaxM][NS], int m, int lane, float *Ru,
-                                         float *Rv, int &proj) {
-#pragma unroll
-  for (int j = 0; j < kMaxM; ++j) {
-    if (j < m) {
-      float n0u = 0.f, n0v = 0.f;
-#pragma unroll
-      for (int t = 0; t < NS; ++t) {
-        n0u = fmaf(u[j][t], u[j][t], n0u);
-        n0v = fmaf(v[j][t], v[j][t], n0v);
-      }
-      n0u = wave_sum_u(n0u);
-      n0v = wave_sum_u(n0v);
-      float ru[kMaxM], rv[kMaxM];
-#pragma unroll
-      for (int i = 0; i < kMaxM; ++i) ru[i] = rv[i] = 0.f;
-      float nu = n0u, nv = n0v;
-#pragma unroll
-      for (int pass = 0; pass < 2; ++pass) {
-        if (j == 0 || (pass == 1 && nu >= kReorth2 * n0u && nv >= kReorth2 * n0v)) break;  // wave-uniform
-        float du[kMaxM], dv[kMaxM];
-#pragma unroll
-        for (int i = 0; i < j; ++i) {
-          float x = 0.f, y = 0.f;
-#pragma unroll
-          for (int t = 0; t < NS; ++t) {
-            x = fmaf(u[i][t], u[j][t], x);
-            y = fmaf(v[i][t], v[j][t], y);
-          }
-          du[i] = wave_sum_u(x);
-          dv[i] = wave_sum_u(y);
-        }
-#pragma unroll
-        for (int i = 0; i < j; ++i) {
-          ru[i] += du[i];
-          rv[i] += dv[i];
-#pragma unroll
-          for (int t = 0; t < NS; ++t) {
-            u[j][t] = fmaf(-du[i], u[i][t], u[j][t]);
-            v[j][t] = fmaf(-dv[i], v[i][t], v[j][t]);
-          }
-        }
-        proj += j;
-        nu = nv = 0.f;
-#pragma unroll
-        for (int t = 0; t < NS; ++t) {
-          nu = fmaf(u[j][t], u[j][t], nu);
-          nv = fmaf(v[j][t], v[j][t], nv);
-        }
-        nu = wave_sum_u(nu);
-        nv = wave_sum_u(nv);
-      }
-      const bool ku = nu > 0.f && nu > kTau2 * n0u, kv = nv > 0.f && nv > kTau2 * n0v;
-      const float su = sqrtf(nu), sv = sqrtf(nv);
-      const float iu = ku ? 1.0f / su : 0.f, iv = kv ? 1.0f / sv : 0.f;
-#pragma unroll
-      for (int t = 0; t < NS; ++t) {
-        u[j][t] *= iu;
-        v[j][t] *= iv;
-      }
-      if (lane < kMaxM) {  // R column j: lane i writes row i
-        float xu = 0.f, xv = 0.f;
-#pragma unroll
-        for (int i = 0; i < kMaxM; ++i) {
-          if (i == lane && i < j) {
-            xu = ru[i];
-            xv = rv[i];
-          }
-        }
-        if (lane == j) {
-          xu = ku ? su : 0.f;
-          xv = kv ? sv : 0.f;
-        }
-        Ru[j * 16 + lane] = xu;
-        Rv[j * 16 + lane] = xv;
-      }
-    } else {
-#pragma unroll
-      for (int t = 0; t < NS; ++t) u[j][t] = v[j][t] = 0.f;
-      if (lane < kMaxM) Ru[j * 16 + lane] = Rv[j * 16 + lane] = 0.f;
-    }
-  }
-}
-
 // One-sided Jacobi on the 16 x 16 column-major C (columns >= m are zero),
 // accumulating the rotations into Vh.  Returns the number of sweeps run.
 // Pairs follow the round-robin (circle) order on M = m rounded up to even:
