@@ -1,7 +1,9 @@
-// ss_linalg.h -- wavefront-level small dense linear algebra shared by the
-// compaction and the initialization kernels: thin QR by classical
-// Gram-Schmidt with one re-orthogonalization pass (CGS2) on register-resident
-// columns, and one-sided (Hestenes) Jacobi SVD of a 16 x 16 matrix in LDS.
+// ss_linalg.h -- wavefront-level small dense linear algebra for the compaction
+// and the initialization kernels: thin QR by classical Gram-Schmidt with one
+// re-orthogonalization pass (CGS2) on register-resident columns (the
+// initialization; the compaction's selective Gram-Schmidt uses the thresholds
+// below), and one-sided (Hestenes) Jacobi SVDs of a 16 x 16 matrix in LDS, with
+// the rotations accumulated (jacobi16) or the columns only (jacobi16c).
 #pragma once
 #include "ss_internal.h"
 #include "ss_wave.h"
