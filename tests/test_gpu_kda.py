@@ -80,9 +80,11 @@ def test_kda_dense_baseline():
 @pytest.mark.parametrize("rule,fp16", [(0, False), (1, False), (1, True)])
 def test_kda_edge_shapes(rule, fp16):
     """Ragged counts, small and odd shapes, K = 1 and 3, both rules, decays down to 0.5; with fp16
-    factors both fp16 decode kernels (eight elements per lane when d_k, d_v are multiples of 8)."""
+    factors both fp16 decode kernels (eight elements per lane when d_k, d_v are multiples of 8).
+    d = 256 takes the compaction's two float4 blocks per lane."""
     rng = np.random.default_rng(7 + rule)
-    for (dk, dv, K, r, N) in [(4, 8, 1, 1, 37), (12, 20, 3, 2, 37), (64, 44, 8, 8, 9), (16, 32, 2, 3, 21)]:
+    for (dk, dv, K, r, N) in [(4, 8, 1, 1, 37), (12, 20, 3, 2, 37), (64, 44, 8, 8, 9), (16, 32, 2, 3, 21),
+                              (256, 16, 8, 8, 13), (40, 256, 2, 3, 9)]:
         R = rng.integers(0, 6, N)
         R[0] = 0
         off = np.concatenate([[0], np.cumsum(R)]).astype(np.int64)
