@@ -21,8 +21,11 @@
 //      part is B Q^T with Q orthonormal.
 //   4. One-sided (Hestenes) Jacobi on the columns of B: 8 lanes per column
 //      pair, up to 32 pairs per round in round-robin (circle) order, one
-//      barrier per round; the rotations are accumulated in Y (f x f).  At
-//      convergence B = X diag(s), and the frozen part is X diag(s) (Q Y)^T.
+//      barrier per round; the rotations are accumulated in Y (f x f).  The
+//      columns' squared norms are taken at the start of each sweep and then
+//      carried (a - t g, b + t g after a rotation by t = tan theta), so a pair
+//      computes only its inner product.  At convergence B = X diag(s), and the
+//      frozen part is X diag(s) (Q Y)^T.
 //   5. Sort s; keep s >= eps sigma_0 (and s > 0); write u = B_j / s_j and
 //      s_j over the state's frozen slots, bring Q back into A, and write
 //      v = Q Y_j.  The result never has more components than the old frozen
@@ -166,9 +169,19 @@ __global__ __launch_bounds__(256) void k_consolidate(ConsolidateArgs a) {
   int sweeps = 0;
   if (M >= 2) {
     const int np = M >> 1, rounds = M - 1, grp = tid >> 3, sub = tid & 7;
+    float *nrm = dt;  // the carried squared column norms (dt is free after the QR)
+    const float tol2 = kTolJ * kTolJ;
     for (int sw = 0; sw < kConsSweeps; ++sw) {
       ++sweeps;
       int *fl = flag + (sw & 1);
+      for (int j = w; j < M; j += 4) {
+        const float *bj = A + (size_t)j * bs;
+        float x = 0.f;
+        for (int e = lane; e < dk; e += 64) x = fmaf(bj[e], bj[e], x);
+        x = wave_sum_u(x);
+        if (lane == 0) nrm[j] = x;
+      }
+      __syncthreads();
       for (int k = 0; k < rounds; ++k) {
         for (int p = grp; p < np; p += kCT / 8) {
           const int ci = p == 0 ? k : (k + p) % (M - 1);
@@ -181,23 +194,18 @@ __global__ __launch_bounds__(256) void k_consolidate(ConsolidateArgs a) {
             xr[t] = self(e < dk, x[ec]);
             yr[t] = self(e < dk, y[ec]);
           }
-          float aa = 0.f, bb = 0.f, gg = 0.f;
+          float gg = 0.f;
 #pragma unroll
-          for (int t = 0; t < KE; ++t) {
-            aa = fmaf(xr[t], xr[t], aa);
-            bb = fmaf(yr[t], yr[t], bb);
-            gg = fmaf(xr[t], yr[t], gg);
-          }
-          aa = group_sum<8>(aa);
-          bb = group_sum<8>(bb);
+          for (int t = 0; t < KE; ++t) gg = fmaf(xr[t], yr[t], gg);
           gg = group_sum<8>(gg);
-          const bool rot = gg != 0.f && fabsf(gg) > kTolJ * __builtin_amdgcn_sqrtf(aa * bb);
+          const float aa = nrm[ci], bb = nrm[cj];
+          // |a b|: a carried norm may round below zero; then g = 0 must still not rotate
+          const bool rot = gg * gg > tol2 * fabsf(aa * bb);
           if (rot) {
-            // zeta = (|y|^2 - |x|^2) / (2 x.y); t = sign(zeta) / (|zeta| + sqrt(1 + zeta^2)) zeroes x'.y'
-            const float zeta = (bb - aa) * (0.5f * __builtin_amdgcn_rcpf(gg));
-            const float az = fabsf(zeta);
-            const float t = az > 1e10f ? 0.5f * __builtin_amdgcn_rcpf(zeta)
-                                       : copysignf(__builtin_amdgcn_rcpf(az + __builtin_amdgcn_sqrtf(fmaf(zeta, zeta, 1.f))), zeta);
+            // t = tan of the rotation angle that zeroes x'.y', the root of smaller magnitude, in
+            // Rutishauser's form: t = sign(d) 2 g / (|d| + sqrt(d^2 + 4 g^2)), d = b - a
+            const float d = bb - aa, g2 = gg + gg;
+            const float t = (d < 0.f ? -g2 : g2) * __builtin_amdgcn_rcpf(fabsf(d) + __builtin_amdgcn_sqrtf(fmaf(d, d, g2 * g2)));
             const float c = __builtin_amdgcn_rsqf(fmaf(t, t, 1.f)), sn = c * t;
             float *yx = Y + (size_t)ci * ys, *yy = Y + (size_t)cj * ys;
             float ux[KE], uy[KE];
@@ -219,7 +227,11 @@ __global__ __launch_bounds__(256) void k_consolidate(ConsolidateArgs a) {
                 yy[e] = sn * ux[q] + c * uy[q];
               }
             }
-            if (sub == 0) *fl = 1;
+            if (sub == 0) {
+              nrm[ci] = fmaf(-t, gg, aa);
+              nrm[cj] = fmaf(t, gg, bb);
+              *fl = 1;
+            }
           }
         }
         __syncthreads();
