@@ -327,9 +327,21 @@ __global__ __launch_bounds__(256) void k_decode_factored_h8(DecodeArgs a) {
   }
   const f8 qs = DIAG ? mul8(gn8, q8) : q8;
   const f8 ks = DIAG ? mul8(gn8, k8) : k8;
+  // per-channel decay: q, k and the decays are held apart from the scaled qs and ks, so k.q, the
+  // new pad key (slot n, which the stream does not read) and the decays are taken before the
+  // stream, which frees their registers (four waves per SIMD instead of three on the delta rule)
+  float kq = 0.f;
+  if constexpr (!RO && DIAG) {
+    kq = group_sum<P>(dot8(k8, q8));
+    if (grp == 0 && kin) {
+      st8nt(a.pk + (s * (int64_t)K + n) * dk + 8 * col, div8(k8, gn8));
+      st8(a.gam + s * dk + 8 * col, gn8);
+    }
+  }
   f8 acc = zero8(), acck = zero8();
-  // pairs in chunks of G * UN (single-buffered: with eight elements per lane a second buffer
-  // costs more occupancy than it hides latency)
+  // pairs in chunks of G * UN, single-buffered: with eight elements per lane a second buffer
+  // costs more occupancy than it hides latency, and so do larger chunks (at 16 lanes per pair,
+  // two pairs per group leave room for five waves per SIMD on the delta rule, four pairs three)
   auto stream = [&](int ib, int ie, auto ld) {
     for (int i0 = ib; i0 < ie; i0 += G * UN) {
       f8 x[UN], y[UN];
@@ -376,14 +388,11 @@ __global__ __launch_bounds__(256) void k_decode_factored_h8(DecodeArgs a) {
       acck = cross_group_sum8<P>(acck);
       w8 = scale8(be, sub8(v8, DIAG ? acck : scale8(al * gamma, acck)));
     }
-    const float kq = group_sum<P>(dot8(k8, q8));
+    if constexpr (!DIAG) kq = group_sum<P>(dot8(k8, q8));
     const f8 o8 = add8(scale8(al, pq), scale8(kq, w8));
     const float gnew = al * gamma;
     if (grp == 0) {
-      if (kin) {
-        st8nt(a.pk + (s * (int64_t)K + n) * dk + 8 * col, DIAG ? div8(k8, gn8) : k8);
-        if constexpr (DIAG) st8(a.gam + s * dk + 8 * col, gn8);
-      }
+      if (!DIAG && kin) st8nt(a.pk + (s * (int64_t)K + n) * dk + 8 * col, k8);
       if (vin) {
         st8nt(a.pw + (s * (int64_t)K + n) * dv + 8 * col, w8);
         st8(a.o + s * dv + 8 * col, o8);
@@ -794,7 +803,7 @@ hipError_t decode_factored_p(const DecodeArgs &a, int P, hipStream_t st) {
 }
 
 #ifndef SS_FACT_H8_UN
-#define SS_FACT_H8_UN 4
+#define SS_FACT_H8_UN 2
 #endif
 template <bool RO, bool AD, bool DG>
 hipError_t decode_factored_h8_p(const DecodeArgs &a, int P, hipStream_t st) {
