@@ -77,7 +77,7 @@ def test_kda_dense_baseline():
     _assert_worst(worst)
 
 
-@pytest.mark.parametrize("rule,fp16", [(0, False), (1, False), (1, True)])
+@pytest.mark.parametrize("rule,fp16", [(0, False), (1, False), (0, True), (1, True)])
 def test_kda_edge_shapes(rule, fp16):
     """Ragged counts, small and odd shapes, K = 1 and 3, both rules, decays down to 0.5; with fp16
     factors both fp16 decode kernels (eight elements per lane when d_k, d_v are multiples of 8).
