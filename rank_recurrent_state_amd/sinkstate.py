@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import weakref
 
 import numpy as np
 import torch  # loaded first so that the library binds to the same HIP runtime
@@ -181,9 +182,12 @@ class StatePool:
         self.any_delta = any_delta
         self.diag_decay = diag_decay
         self.n_alpha = n_states * d_k if diag_decay else n_states  # per-channel decay: alpha is [N][d_k]
+        self._graphs = weakref.WeakSet()  # step graphs over this pool: destroyed before it
 
     def close(self):
         if self.handle:
+            for g in list(self._graphs):
+                g.close()
             load_library().ss_state_pool_destroy(self.handle)
             self.handle = None
 
@@ -256,10 +260,14 @@ class StepGraph:
         args = [_ptr(q, N * dk, "q"), _ptr(k, N * dk, "k"), _ptr(v, N * dv, "v"), _ptr(alpha, pool.n_alpha, "alpha"),
                 _ptr(beta, N, "beta") if beta is not None else None, _ptr(o, N * dv, "o")]
         h = ctypes.c_void_p()
+        self.handle = None
         _check(load_library().ss_step_graph_create(pool.handle, *args, ctypes.byref(h)))
         self.handle = h
+        pool._graphs.add(self)
 
     def launch(self, step: int, stream=None):
+        if not self.handle:
+            raise SinkStateError(SS_ERR_STATE, "the step graph is closed (or its pool was)")
         _check(load_library().ss_step_graph_launch(self.handle, int(step), _stream(stream)))
 
     def close(self):

@@ -257,3 +257,43 @@ def test_product_path_does_not_reach_the_oracle():
         if line.lstrip().startswith("#") or "\"" in line or "'" in line:
             continue  # comments and strings
         assert fn.start() <= u < fn.end(), line
+
+
+def test_pool_close_destroys_its_step_graphs_first(monkeypatch):
+    """A step graph must be destroyed before its pool: closing the pool closes its live graphs
+    first, and a closed graph refuses to launch instead of handing the library a dangling handle
+    (a stand-in library records the calls; no GPU involved)."""
+    import types
+    from rank_recurrent_state_amd import sinkstate as ss
+    calls = []
+
+    class Lib:
+        def ss_step_graph_create(self, pool, *args):
+            args[-1]._obj.value = 0x20
+            calls.append(("create", pool))
+            return 0
+
+        def ss_step_graph_launch(self, h, step, stream):
+            calls.append(("launch", h.value, step))
+            return 0
+
+        def ss_step_graph_destroy(self, h):
+            calls.append(("graph_destroy", h.value))
+            return 0
+
+        def ss_state_pool_destroy(self, h):
+            calls.append(("pool_destroy", h))
+            return 0
+
+    monkeypatch.setattr(ss, "_lib", Lib())
+    stream = types.SimpleNamespace(cuda_stream=0)
+    pool = ss.StatePool(0x10, 4, 16, 32, 8, 2, 1, False)
+    g = ss.StepGraph(pool, None, None, None, None, None, None)
+    g.launch(3, stream=stream)
+    pool.close()
+    assert calls == [("create", 0x10), ("launch", 0x20, 3), ("graph_destroy", 0x20), ("pool_destroy", 0x10)]
+    with pytest.raises(ss.SinkStateError):
+        g.launch(4, stream=stream)
+    g.close()
+    pool.close()
+    assert len(calls) == 4
